@@ -1,0 +1,16 @@
+"""Weight-only quantized linear layers (ternary 2-bit and W4A16) for AMD MI355X.
+
+The compute lives in libtq.so (hand-written HIP kernels for gfx950 behind a C
+ABI, include/tq.h); this package is its Python binding plus the packed
+layout descriptions.  Build the library with
+``python -m bit_weight_only_tq_amd.build``.
+"""
+
+from ._lib import (TQError, load, tq_abi_version, tq_gemm, tq_pack, tq_select_path,  # noqa: F401
+                   tq_unpack, w4a16_gemm, w4a16_pack, w4a16_unpack)
+from .layout import TernaryLayout, W4Layout  # noqa: F401
+
+__all__ = [
+    "TQError", "load", "tq_abi_version", "tq_gemm", "tq_pack", "tq_select_path", "tq_unpack",
+    "w4a16_gemm", "w4a16_pack", "w4a16_unpack", "TernaryLayout", "W4Layout",
+]

@@ -1,0 +1,188 @@
+"""ctypes binding of libtq.so: argument marshalling only.
+
+Every function here forwards to the C ABI declared in include/tq.h with the
+same name; tensors are torch tensors on the current HIP device (torch is used
+for device memory and the current stream, nothing else).  There is no CPU
+fallback: if libtq.so is missing or cannot be loaded, every call raises.
+"""
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libtq.so")
+
+# tq_status
+STATUS_NAMES = {
+    0: "TQ_OK", 1: "TQ_ERR_NULL", 2: "TQ_ERR_SHAPE", 3: "TQ_ERR_ALIGN", 4: "TQ_ERR_DTYPE",
+    5: "TQ_ERR_GROUP", 6: "TQ_ERR_NONFINITE", 7: "TQ_ERR_RANGE", 8: "TQ_ERR_BAD_CODE",
+    9: "TQ_ERR_HIP", 10: "TQ_ERR_PATH",
+}
+# tq_dtype
+TQ_F16, TQ_BF16 = 0, 1
+# tq_path
+PATHS = {"auto": 0, "gemv": 1, "stream_mfma": 2, "gemm": 3}
+PATH_NAMES = {v: k for k, v in PATHS.items()}
+
+# every symbol include/tq.h declares, with (restype, argtypes)
+_i64, _vp, _i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+SIGNATURES = {
+    "tq_pack": (_i32, [_vp, _i64, _i64, _vp, _vp, _vp]),
+    "tq_unpack": (_i32, [_vp, _vp, _i64, _i64, _vp, _vp, _vp]),
+    "w4a16_pack": (_i32, [_vp, _i64, _i64, _i64, _vp, _vp, _vp]),
+    "w4a16_unpack": (_i32, [_vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp]),
+    "tq_gemm": (_i32, [_vp, _i32, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp]),
+    "tq_gemm_ex": (_i32, [_vp, _i32, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _i32]),
+    "w4a16_gemm": (_i32, [_vp, _i32, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _vp]),
+    "w4a16_gemm_ex": (_i32, [_vp, _i32, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _vp, _i32]),
+    "tq_select_path": (_i32, [_i32, _i64, _i64, _i64, _i32]),
+    "tq_status_str": (ctypes.c_char_p, [_i32]),
+    "tq_abi_version": (_i32, []),
+}
+
+
+class TQError(RuntimeError):
+    """A libtq call returned a status other than TQ_OK."""
+
+    def __init__(self, fn: str, status: int, msg: str):
+        self.status = status
+        self.name = STATUS_NAMES.get(status, str(status))
+        super().__init__(f"{fn}: {self.name} ({msg})")
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load libtq.so once and declare its prototypes; raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"libtq.so not built: {path} is missing "
+                           "(run `python -m bit_weight_only_tq_amd.build`)")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        msg = load().tq_status_str(status).decode()
+        raise TQError(fn, status, msg)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device=None):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dtype_enum(t):
+    import torch
+    if t.dtype == torch.float16:
+        return TQ_F16
+    if t.dtype == torch.bfloat16:
+        return TQ_BF16
+    raise TypeError(f"activations must be float16 or bfloat16, got {t.dtype}")
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("tensors must be contiguous device tensors")
+
+
+# ------------------------------------------------------------------ prepare
+
+def tq_pack(W):
+    """fp32 [N, K] -> (codes uint8 [N, ceil(K/4)], scale fp16 [N])."""
+    import torch
+    _need_cuda(W)
+    if W.dtype != torch.float32 or W.dim() != 2:
+        raise TypeError("W must be a 2-D float32 tensor")
+    N, K = W.shape
+    codes = torch.empty((N, (K + 3) // 4), dtype=torch.uint8, device=W.device)
+    scale = torch.empty((N,), dtype=torch.float16, device=W.device)
+    _check("tq_pack", load().tq_pack(_ptr(W), N, K, _ptr(codes), _ptr(scale), _stream(W.device)))
+    return codes, scale
+
+
+def tq_unpack(codes, scale, K: int, want_t: bool = True, want_wdq: bool = True):
+    """-> (t int8 [N, K] or None, wdq fp16 [N, K] or None)."""
+    import torch
+    _need_cuda(codes, scale)
+    N = codes.shape[0]
+    t = torch.empty((N, K), dtype=torch.int8, device=codes.device) if want_t else None
+    w = torch.empty((N, K), dtype=torch.float16, device=codes.device) if want_wdq else None
+    _check("tq_unpack", load().tq_unpack(_ptr(codes), _ptr(scale), N, K, _ptr(t), _ptr(w), _stream(codes.device)))
+    return t, w
+
+
+def w4a16_pack(W, group_size: int = 128):
+    """fp32 [N, K] -> (qweight int32 [N, K/8], scales fp16 [N, K/group])."""
+    import torch
+    _need_cuda(W)
+    if W.dtype != torch.float32 or W.dim() != 2:
+        raise TypeError("W must be a 2-D float32 tensor")
+    N, K = W.shape
+    q = torch.empty((N, K // 8), dtype=torch.int32, device=W.device)
+    s = torch.empty((N, max(K // max(group_size, 1), 1)), dtype=torch.float16, device=W.device)
+    _check("w4a16_pack", load().w4a16_pack(_ptr(W), N, K, group_size, _ptr(q), _ptr(s), _stream(W.device)))
+    return q, s
+
+
+def w4a16_unpack(qweight, scales, K: int, group_size: int = 128, want_q: bool = True, want_wdq: bool = True):
+    """-> (q uint8 [N, K] or None, wdq fp16 [N, K] or None)."""
+    import torch
+    _need_cuda(qweight, scales)
+    N = qweight.shape[0]
+    q = torch.empty((N, K), dtype=torch.uint8, device=qweight.device) if want_q else None
+    w = torch.empty((N, K), dtype=torch.float16, device=qweight.device) if want_wdq else None
+    _check("w4a16_unpack", load().w4a16_unpack(_ptr(qweight), _ptr(scales), N, K, group_size,
+                                               _ptr(q), _ptr(w), _stream(qweight.device)))
+    return q, w
+
+
+# -------------------------------------------------------------------- apply
+
+def tq_gemm(A, codes, scale, bias=None, out=None, path: str = "auto"):
+    """C = A @ dequant(codes, scale)^T (+ bias); A [M, K] fp16/bf16."""
+    import torch
+    _need_cuda(A, codes, scale, bias)
+    M, K = A.shape
+    N = codes.shape[0]
+    C = out if out is not None else torch.empty((M, N), dtype=A.dtype, device=A.device)
+    _check("tq_gemm", load().tq_gemm_ex(_ptr(A), _dtype_enum(A), M, N, K, _ptr(codes), _ptr(scale),
+                                         _ptr(bias), _ptr(C), _stream(A.device), PATHS[path]))
+    return C
+
+
+def w4a16_gemm(A, qweight, scales, bias=None, out=None, group_size: int = 128, path: str = "auto"):
+    """C = A @ dequant(qweight, scales)^T (+ bias); A [M, K] fp16/bf16."""
+    import torch
+    _need_cuda(A, qweight, scales, bias)
+    M, K = A.shape
+    N = qweight.shape[0]
+    C = out if out is not None else torch.empty((M, N), dtype=A.dtype, device=A.device)
+    _check("w4a16_gemm", load().w4a16_gemm_ex(_ptr(A), _dtype_enum(A), M, N, K, _ptr(qweight), _ptr(scales),
+                                               group_size, _ptr(bias), _ptr(C), _stream(A.device), PATHS[path]))
+    return C
+
+
+def tq_select_path(fmt: str, M: int, N: int, K: int, dtype: str = "f16") -> str:
+    """The dispatcher's kernel choice for a shape ("gemv", "stream_mfma", "gemm")."""
+    f = {"ternary": 0, "w4a16": 1}[fmt]
+    d = {"f16": TQ_F16, "bf16": TQ_BF16}[dtype]
+    return PATH_NAMES[load().tq_select_path(f, M, N, K, d)]
+
+
+def tq_abi_version() -> int:
+    return load().tq_abi_version()

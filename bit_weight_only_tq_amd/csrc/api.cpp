@@ -1,0 +1,205 @@
+// extern "C" entry points of libtq: argument checks, the M-based dispatcher,
+// and the synchronous prepare calls.  See include/tq.h for the contract.
+//
+// The library never calls hipSetDevice and keeps no state between calls: it
+// works on the caller's current device and stream (page "Ternary quantized
+// models in vLLM ...", section 5.1: a kernel bound to the wrong device
+// ordinal is the first deployment failure it lists).
+
+#include "tq.h"
+
+#include <hip/hip_runtime.h>
+
+#include "tq_internal.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Dispatcher thresholds on M (activation rows).  Decode-sized M is bound by
+// streaming the packed weights; large M is a dense contraction for the matrix
+// cores.
+constexpr int64_t kGemvMaxM = tq::kGemvMaxM;
+
+// Device status word for the synchronous prepare calls.
+struct StatusWord {
+    int* dev = nullptr;
+    tq_status init(hipStream_t s) {
+        if (hipMalloc(&dev, 4 * sizeof(int)) != hipSuccess) { dev = nullptr; return TQ_ERR_HIP; }
+        if (hipMemsetAsync(dev, 0, 4 * sizeof(int), s) != hipSuccess) return TQ_ERR_HIP;
+        return TQ_OK;
+    }
+    tq_status read(hipStream_t s, int out[4]) {
+        if (hipMemcpyAsync(out, dev, 4 * sizeof(int), hipMemcpyDeviceToHost, s) != hipSuccess) return TQ_ERR_HIP;
+        if (hipStreamSynchronize(s) != hipSuccess) return TQ_ERR_HIP;
+        return TQ_OK;
+    }
+    ~StatusWord() {
+        if (dev) (void)hipFree(dev);
+    }
+};
+
+tq_status check_gemm_common(const void* A, tq_dtype dt, int64_t M, int64_t N, int64_t K, const void* wq,
+                            const uint16_t* scale, void* C) {
+    if (!A || !wq || !scale || !C) return TQ_ERR_NULL;
+    if (dt != TQ_F16 && dt != TQ_BF16) return TQ_ERR_DTYPE;
+    if (M <= 0 || N <= 0 || K <= 0) return TQ_ERR_SHAPE;
+    if (!aligned16(A) || !aligned16(wq)) return TQ_ERR_ALIGN;
+    if ((reinterpret_cast<uintptr_t>(C) & 1u) || (reinterpret_cast<uintptr_t>(scale) & 1u)) return TQ_ERR_ALIGN;
+    return TQ_OK;
+}
+
+tq_status from_hip(hipError_t e) { return e == hipSuccess ? TQ_OK : TQ_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int tq_abi_version(void) { return TQ_ABI_VERSION; }
+
+const char* tq_status_str(tq_status s) {
+    switch (s) {
+        case TQ_OK: return "ok";
+        case TQ_ERR_NULL: return "a required pointer is NULL";
+        case TQ_ERR_SHAPE: return "invalid shape (sizes must be positive; see K constraints)";
+        case TQ_ERR_ALIGN: return "pointer not 16-byte aligned";
+        case TQ_ERR_DTYPE: return "unknown activation dtype";
+        case TQ_ERR_GROUP: return "W4A16 group size must be 128";
+        case TQ_ERR_NONFINITE: return "a weight is NaN or infinite";
+        case TQ_ERR_RANGE: return "a scale overflows fp16";
+        case TQ_ERR_BAD_CODE: return "packed code field 0b11 (unused) found";
+        case TQ_ERR_HIP: return "HIP runtime error or kernel launch failure";
+        case TQ_ERR_PATH: return "forced kernel path cannot run this shape";
+    }
+    return "unknown status";
+}
+
+tq_path tq_select_path(int format, int64_t M, int64_t N, int64_t K, tq_dtype dt) {
+    (void)N; (void)K; (void)dt;
+    if (M <= kGemvMaxM) return TQ_PATH_GEMV;
+    if (format == 1) return TQ_PATH_GEMV;  // W4A16: small-M kernel over blocks of rows
+    return TQ_PATH_GEMM;
+}
+
+// ---------------------------------------------------------------- prepare
+
+tq_status tq_pack(const float* W, int64_t N, int64_t K, uint8_t* codes, uint16_t* scale_f16, hipStream_t stream) {
+    if (!W || !codes || !scale_f16) return TQ_ERR_NULL;
+    if (N <= 0 || K <= 0) return TQ_ERR_SHAPE;
+    if ((reinterpret_cast<uintptr_t>(W) & 3u) || (reinterpret_cast<uintptr_t>(scale_f16) & 1u)) return TQ_ERR_ALIGN;
+    if ((K % 64) == 0 && !aligned16(codes)) return TQ_ERR_ALIGN;
+    StatusWord st;
+    tq_status r = st.init(stream);
+    if (r != TQ_OK) return r;
+    int flags[4];
+    if (tq::launch_finite_scan(W, N * K, st.dev, stream) != hipSuccess) return TQ_ERR_HIP;
+    if ((r = st.read(stream, flags)) != TQ_OK) return r;
+    if (flags[0]) return TQ_ERR_NONFINITE;
+    if (tq::launch_ternary_pack(W, N, K, codes, scale_f16, st.dev, stream) != hipSuccess) return TQ_ERR_HIP;
+    if ((r = st.read(stream, flags)) != TQ_OK) return r;
+    if (flags[1]) return TQ_ERR_RANGE;
+    return TQ_OK;
+}
+
+tq_status tq_unpack(const uint8_t* codes, const uint16_t* scale_f16, int64_t N, int64_t K, int8_t* t_out,
+                    uint16_t* wdq_f16_out, hipStream_t stream) {
+    if (!codes || !scale_f16) return TQ_ERR_NULL;
+    if (N <= 0 || K <= 0) return TQ_ERR_SHAPE;
+    if ((reinterpret_cast<uintptr_t>(scale_f16) & 1u) || (reinterpret_cast<uintptr_t>(wdq_f16_out) & 1u))
+        return TQ_ERR_ALIGN;
+    StatusWord st;
+    tq_status r = st.init(stream);
+    if (r != TQ_OK) return r;
+    int flags[4];
+    if (tq::launch_ternary_unpack(codes, scale_f16, N, K, t_out, wdq_f16_out, st.dev, stream) != hipSuccess)
+        return TQ_ERR_HIP;
+    if ((r = st.read(stream, flags)) != TQ_OK) return r;
+    if (flags[2]) return TQ_ERR_BAD_CODE;
+    return TQ_OK;
+}
+
+tq_status w4a16_pack(const float* W, int64_t N, int64_t K, int64_t group_size, int32_t* qweight,
+                     uint16_t* scales_f16, hipStream_t stream) {
+    if (!W || !qweight || !scales_f16) return TQ_ERR_NULL;
+    if (group_size != 128) return TQ_ERR_GROUP;
+    if (N <= 0 || K <= 0 || (K % 128) != 0) return TQ_ERR_SHAPE;
+    if (!aligned16(W) || (reinterpret_cast<uintptr_t>(qweight) & 3u) || (reinterpret_cast<uintptr_t>(scales_f16) & 1u))
+        return TQ_ERR_ALIGN;
+    StatusWord st;
+    tq_status r = st.init(stream);
+    if (r != TQ_OK) return r;
+    int flags[4];
+    if (tq::launch_finite_scan(W, N * K, st.dev, stream) != hipSuccess) return TQ_ERR_HIP;
+    if ((r = st.read(stream, flags)) != TQ_OK) return r;
+    if (flags[0]) return TQ_ERR_NONFINITE;
+    if (tq::launch_w4_pack(W, N, K, qweight, scales_f16, st.dev, stream) != hipSuccess) return TQ_ERR_HIP;
+    if ((r = st.read(stream, flags)) != TQ_OK) return r;
+    if (flags[1]) return TQ_ERR_RANGE;
+    return TQ_OK;
+}
+
+tq_status w4a16_unpack(const int32_t* qweight, const uint16_t* scales_f16, int64_t N, int64_t K,
+                       int64_t group_size, uint8_t* q_out, uint16_t* wdq_f16_out, hipStream_t stream) {
+    if (!qweight || !scales_f16) return TQ_ERR_NULL;
+    if (group_size != 128) return TQ_ERR_GROUP;
+    if (N <= 0 || K <= 0 || (K % 128) != 0) return TQ_ERR_SHAPE;
+    if ((reinterpret_cast<uintptr_t>(qweight) & 3u) || (reinterpret_cast<uintptr_t>(scales_f16) & 1u) ||
+        (reinterpret_cast<uintptr_t>(wdq_f16_out) & 1u))
+        return TQ_ERR_ALIGN;
+    if (tq::launch_w4_unpack(qweight, scales_f16, N, K, q_out, wdq_f16_out, stream) != hipSuccess) return TQ_ERR_HIP;
+    return from_hip(hipStreamSynchronize(stream));
+}
+
+// ------------------------------------------------------------------ apply
+
+tq_status tq_gemm_ex(const void* A, tq_dtype dt, int64_t M, int64_t N, int64_t K, const uint8_t* codes,
+                     const uint16_t* scale_f16, const void* bias, void* C, hipStream_t stream, tq_path path) {
+    tq_status r = check_gemm_common(A, dt, M, N, K, codes, scale_f16, C);
+    if (r != TQ_OK) return r;
+    if (K % 64 != 0) return TQ_ERR_SHAPE;
+    if (bias && (reinterpret_cast<uintptr_t>(bias) & 1u)) return TQ_ERR_ALIGN;
+    if (path == TQ_PATH_AUTO) path = tq_select_path(0, M, N, K, dt);
+    tq::GemmArgs a{static_cast<const uint16_t*>(A), dt == TQ_BF16 ? 1 : 0, M, N, K, codes, scale_f16,
+                   static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(C)};
+    switch (path) {
+        case TQ_PATH_GEMV:
+            if (M > kGemvMaxM) return TQ_ERR_PATH;
+            return from_hip(tq::launch_ternary_gemv(a, stream));
+        case TQ_PATH_GEMM:
+            return from_hip(tq::launch_ternary_gemm(a, stream));
+        default:
+            return TQ_ERR_PATH;
+    }
+}
+
+tq_status tq_gemm(const void* A, tq_dtype dt, int64_t M, int64_t N, int64_t K, const uint8_t* codes,
+                  const uint16_t* scale_f16, const void* bias, void* C, hipStream_t stream) {
+    return tq_gemm_ex(A, dt, M, N, K, codes, scale_f16, bias, C, stream, TQ_PATH_AUTO);
+}
+
+tq_status w4a16_gemm_ex(const void* A, tq_dtype dt, int64_t M, int64_t N, int64_t K, const int32_t* qweight,
+                        const uint16_t* scales_f16, int64_t group_size, const void* bias, void* C,
+                        hipStream_t stream, tq_path path) {
+    tq_status r = check_gemm_common(A, dt, M, N, K, qweight, scales_f16, C);
+    if (r != TQ_OK) return r;
+    if (group_size != 128) return TQ_ERR_GROUP;
+    if (K % 128 != 0) return TQ_ERR_SHAPE;
+    if (bias && (reinterpret_cast<uintptr_t>(bias) & 1u)) return TQ_ERR_ALIGN;
+    if (path == TQ_PATH_AUTO) path = tq_select_path(1, M, N, K, dt);
+    tq::GemmArgs a{static_cast<const uint16_t*>(A), dt == TQ_BF16 ? 1 : 0, M, N, K, qweight, scales_f16,
+                   static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(C)};
+    switch (path) {
+        case TQ_PATH_GEMV:
+            if (M > kGemvMaxM) return from_hip(tq::launch_w4_gemm(a, stream));
+            return from_hip(tq::launch_w4_gemv(a, stream));
+        default:
+            return TQ_ERR_PATH;
+    }
+}
+
+tq_status w4a16_gemm(const void* A, tq_dtype dt, int64_t M, int64_t N, int64_t K, const int32_t* qweight,
+                     const uint16_t* scales_f16, int64_t group_size, const void* bias, void* C, hipStream_t stream) {
+    return w4a16_gemm_ex(A, dt, M, N, K, qweight, scales_f16, group_size, bias, C, stream, TQ_PATH_AUTO);
+}
+
+}  // extern "C"

@@ -1,0 +1,108 @@
+// Device helpers shared by the HIP kernels of libtq (gfx950, wave64).
+//
+// Conversions are written from the IEEE-754 format definitions on integer
+// bit patterns, so their rounding never depends on the hardware mode
+// register: binary16 = 1 sign, 5 exponent (bias 15), 10 fraction bits;
+// bfloat16 = the top half of binary32.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tq {
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kWave = 64;
+
+// fp64 -> binary16 bit pattern, rounded once to nearest, ties to even.
+// Magnitudes that round past 65504 give infinity; NaN gives 0x7E00.
+__device__ __forceinline__ uint16_t f64_to_f16_rne(double x) {
+    const uint64_t u = (uint64_t)__double_as_longlong(x);
+    const uint32_t sign = (uint32_t)(u >> 48) & 0x8000u;
+    const uint64_t a = u & 0x7FFFFFFFFFFFFFFFull;
+    if (a >= 0x7FF0000000000000ull)  // inf or NaN
+        return (uint16_t)(a > 0x7FF0000000000000ull ? 0x7E00u : (sign | 0x7C00u));
+    const int e = (int)(a >> 52) - 1023;  // exponent of a normal double
+    if (e < -25) return (uint16_t)sign;   // below half the smallest subnormal (2^-25)
+    const uint64_t m = (a & 0x000FFFFFFFFFFFFFull) | 0x0010000000000000ull;  // 53-bit significand
+    int E = e < -14 ? -14 : e;            // binade of the result (subnormals share -14)
+    const int shift = 42 + E - e;         // 52 - 10 + (E - e): to units of 2^(E-10)
+    uint64_t r = m >> shift;
+    const uint64_t rem = m & ((1ull << shift) - 1);
+    const uint64_t half = 1ull << (shift - 1);
+    if (rem > half || (rem == half && (r & 1))) ++r;
+    if (r == 2048) { ++E; r = 1024; }     // carried into the next binade
+    if (E + 15 >= 31) return (uint16_t)(sign | 0x7C00u);
+    const uint32_t bits = (E == -14) ? (uint32_t)r : ((uint32_t)(E + 15) << 10) + (uint32_t)(r - 1024);
+    return (uint16_t)(sign | bits);
+}
+
+// binary32 -> binary16 bit pattern, round to nearest even (same construction).
+__device__ __forceinline__ uint16_t f32_to_f16_rne(float x) {
+    const uint32_t u = __float_as_uint(x);
+    const uint32_t sign = (u >> 16) & 0x8000u;
+    const uint32_t a = u & 0x7FFFFFFFu;
+    if (a >= 0x7F800000u) return (uint16_t)(a > 0x7F800000u ? 0x7E00u : (sign | 0x7C00u));
+    const int e = (int)(a >> 23) - 127;
+    if (e < -25) return (uint16_t)sign;
+    const uint32_t m = (a & 0x007FFFFFu) | 0x00800000u;  // 24-bit significand
+    int E = e < -14 ? -14 : e;
+    const int shift = 13 + E - e;  // 23 - 10 + (E - e), in [13, 24]
+    uint32_t r = m >> shift;
+    const uint32_t rem = m & ((1u << shift) - 1);
+    const uint32_t half = 1u << (shift - 1);
+    if (rem > half || (rem == half && (r & 1))) ++r;
+    if (r == 2048) { ++E; r = 1024; }
+    if (E + 15 >= 31) return (uint16_t)(sign | 0x7C00u);
+    const uint32_t bits = (E == -14) ? r : ((uint32_t)(E + 15) << 10) + (r - 1024);
+    return (uint16_t)(sign | bits);
+}
+
+// binary32 -> bfloat16 bit pattern, round to nearest even; NaN stays NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
+    const uint32_t u = __float_as_uint(x);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)(((u >> 16) & 0x8000u) | 0x7FC0u);
+    return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+// Exact value of a binary16 bit pattern.
+__device__ __forceinline__ float f16_bits_to_f32(uint16_t h) {
+    return (float)__builtin_bit_cast(_Float16, h);
+}
+__device__ __forceinline__ double f16_bits_to_f64(uint16_t h) {
+    return (double)__builtin_bit_cast(_Float16, h);
+}
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) {
+    return __uint_as_float((uint32_t)h << 16);
+}
+
+// Activation element type tags.
+struct F16 {
+    static __device__ __forceinline__ float to_f32(uint16_t h) { return f16_bits_to_f32(h); }
+    static __device__ __forceinline__ uint16_t from_f32(float x) { return f32_to_f16_rne(x); }
+};
+struct BF16 {
+    static __device__ __forceinline__ float to_f32(uint16_t h) { return bf16_bits_to_f32(h); }
+    static __device__ __forceinline__ uint16_t from_f32(float x) { return f32_to_bf16_rne(x); }
+};
+
+// Sum over the 64 lanes of a wave; every lane receives the total.  The first
+// four steps stay inside a 16-lane row (DPP: swap neighbours, swap pairs,
+// mirror half-rows, mirror rows); the last two cross rows.
+__device__ __forceinline__ float wave_sum(float v) {
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));  // row_half_mirror
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));  // row_mirror
+    v += __shfl_xor(v, 16, kWave);
+    v += __shfl_xor(v, 32, kWave);
+    return v;
+}
+
+}  // namespace tq

@@ -1,0 +1,40 @@
+// Internal launcher declarations shared by the libtq translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tq {
+
+// pack.hip
+hipError_t launch_finite_scan(const float* W, int64_t total, int* flags, hipStream_t s);
+hipError_t launch_ternary_pack(const float* W, int64_t N, int64_t K, uint8_t* codes, uint16_t* scale,
+                               int* flags, hipStream_t s);
+hipError_t launch_ternary_unpack(const uint8_t* codes, const uint16_t* scale, int64_t N, int64_t K,
+                                 int8_t* t_out, uint16_t* wdq_out, int* flags, hipStream_t s);
+hipError_t launch_w4_pack(const float* W, int64_t N, int64_t K, int32_t* qweight, uint16_t* scales,
+                          int* flags, hipStream_t s);
+hipError_t launch_w4_unpack(const int32_t* qweight, const uint16_t* scales, int64_t N, int64_t K,
+                            uint8_t* q_out, uint16_t* wdq_out, hipStream_t s);
+
+// Arguments of one quantized linear-layer call (apply stage).
+struct GemmArgs {
+    const uint16_t* A;      // [M, K] fp16 / bf16 bit patterns
+    int bf16;               // 0: fp16 activations and output, 1: bf16
+    int64_t M, N, K;
+    const void* wq;         // ternary codes [N, K/4] or W4 words [N, K/8]
+    const uint16_t* scale;  // ternary [N]; W4 [N, K/128]
+    const uint16_t* bias;   // [N] or nullptr
+    uint16_t* C;            // [M, N]
+};
+
+// gemv.hip: small M (<= kGemvMaxM), weights streamed once per call.
+constexpr int kGemvMaxM = 16;
+hipError_t launch_ternary_gemv(const GemmArgs& a, hipStream_t s);
+hipError_t launch_w4_gemv(const GemmArgs& a, hipStream_t s);
+
+// gemm.hip: LDS-tiled matrix-core GEMM, any M.
+hipError_t launch_ternary_gemm(const GemmArgs& a, hipStream_t s);
+hipError_t launch_w4_gemm(const GemmArgs& a, hipStream_t s);
+
+}  // namespace tq

@@ -1,0 +1,207 @@
+/*
+ * tq.h - weight-only quantized linear layers for AMD Instinct MI355X (gfx950).
+ *
+ * Two packed weight formats, each multiplied against fp16 or bf16 activations
+ * with fp32 accumulation:
+ *
+ *  - Ternary: every weight is one of {-1, 0, +1} times a per-output-row fp16
+ *    scale; four 2-bit codes per byte.  Sources: page "Ternary quantized
+ *    models in vLLM: reverse engineering, reconciliation and kernel
+ *    optimization" (wzjinhao.cn/news/47283) - section 1 (tip: scaled sign
+ *    function with a threshold), section 2.3 (the layer receives the packed
+ *    uint8 weight, its fp16 scale and an optional bias, and never holds fp16
+ *    weights), section 3.1 (threshold 0.7 * mean|w|, code table, bit order,
+ *    fp16 scale), section 3.2 (row length ceil(K/4) bytes), section 4 (the
+ *    layer's arithmetic: value = code - 1, dot product per output).
+ *
+ *  - W4A16: symmetric int4 with a fixed zero point of 8, eight codes per
+ *    int32 along K, one fp16 scale per output row and group of 128 columns.
+ *    Source: page "Model quantization - vLLM runtime quantization
+ *    architecture" (notes.devxops.cn, 2026-05-14), section 5 steps (1) and
+ *    (3): bits 4, group_size 128, sym, packed factor 8, weight [d_out, d_in/8],
+ *    scales [d_out, d_in/128]; section 4.4: the prepare (create + load +
+ *    post-process) then apply lifecycle this API follows.
+ *
+ * Conventions for every call:
+ *  - Tensor pointers are DEVICE pointers on the current HIP device (the
+ *    library never calls hipSetDevice).  Tensors are row-major and contiguous.
+ *  - fp16 and bf16 values are passed as 16-bit patterns (uint16_t / void*).
+ *  - The caller owns every buffer; the library keeps no pointer after a call
+ *    returns.  Buffers must stay alive until the work on `stream` completes.
+ *  - Shapes: M = activation rows, N = output features (weight rows),
+ *    K = input features.  A is [M, K], C is [M, N].
+ *  - Errors the host can see return at once with nothing launched:
+ *    TQ_ERR_NULL, TQ_ERR_SHAPE, TQ_ERR_ALIGN, TQ_ERR_DTYPE, TQ_ERR_GROUP,
+ *    TQ_ERR_PATH.  A failed launch or HIP call returns TQ_ERR_HIP.
+ *  - Prepare calls (pack / unpack) are SYNCHRONOUS: they wait for `stream`
+ *    and report data errors (TQ_ERR_NONFINITE, TQ_ERR_RANGE,
+ *    TQ_ERR_BAD_CODE).  They allocate a small device status word for the
+ *    duration of the call.
+ *  - Apply calls (tq_gemm, w4a16_gemm) are ASYNCHRONOUS on `stream`,
+ *    allocate nothing, never synchronize and are safe to capture in a HIP
+ *    graph.  Faults during execution surface at the caller's next sync.
+ *  - All results are deterministic: no atomics, no split-K races; the same
+ *    inputs and path give bit-identical outputs.
+ */
+#ifndef TQ_H
+#define TQ_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TQ_ABI_VERSION 1
+
+typedef enum tq_status {
+    TQ_OK = 0,
+    TQ_ERR_NULL = 1,       /* a required pointer is NULL */
+    TQ_ERR_SHAPE = 2,      /* a size is <= 0 or violates a K constraint */
+    TQ_ERR_ALIGN = 3,      /* a pointer is not 16-byte aligned */
+    TQ_ERR_DTYPE = 4,      /* unknown activation dtype enum */
+    TQ_ERR_GROUP = 5,      /* W4A16 group size other than 128 */
+    TQ_ERR_NONFINITE = 6,  /* pack: a weight is NaN or infinite */
+    TQ_ERR_RANGE = 7,      /* pack: a scale rounds to infinity in fp16 */
+    TQ_ERR_BAD_CODE = 8,   /* unpack: a 2-bit field holds the unused 0b11 */
+    TQ_ERR_HIP = 9,        /* a HIP runtime call or kernel launch failed */
+    TQ_ERR_PATH = 10       /* a forced kernel path cannot run this shape */
+} tq_status;
+
+typedef enum tq_dtype {
+    TQ_F16 = 0,            /* IEEE binary16 activations and outputs */
+    TQ_BF16 = 1            /* bfloat16 activations and outputs */
+} tq_dtype;
+
+/* Kernel families the dispatcher chooses between (by M; see tq_select_path). */
+typedef enum tq_path {
+    TQ_PATH_AUTO = 0,        /* let the dispatcher choose */
+    TQ_PATH_GEMV = 1,        /* small M: weight-streaming kernel, codes read once per call */
+    TQ_PATH_STREAM_MFMA = 2, /* medium M: weight-streaming kernel with matrix-core MACs */
+    TQ_PATH_GEMM = 3         /* large M: LDS-tiled matrix-core GEMM (prefill) */
+} tq_path;
+
+/* ---------------------------------------------------------------- prepare */
+
+/*
+ * tq_pack - ternarize and pack fp32 weights.
+ *   W          [N, K] fp32 (device).
+ *   codes      [N, ceil(K/4)] uint8 (device, written).  Code of column 4j+k
+ *              sits in bits 2k..2k+1 of byte j of its row; 00 = -1, 01 = 0,
+ *              10 = +1; 11 is never written; tail fields of a row whose K is
+ *              not a multiple of 4 are 01.
+ *   scale_f16  [N] fp16 bit patterns (device, written).
+ * Per row n (sums in fp64, sequential in ascending column order):
+ *   S = sum |w|;  thr = 0.7 * (S / K);  kept = |w| > thr;  t = sign(w) if kept
+ *   else 0;  scale = (sum of kept |w|) / (number kept), rounded once to fp16
+ *   (round to nearest even), +0 for a row with nothing kept (an all-zero row).
+ * Any N >= 1, K >= 1.  Errors: TQ_ERR_NONFINITE if any weight is NaN/Inf
+ * (checked before anything is written), TQ_ERR_RANGE if a scale overflows
+ * fp16 (outputs then hold partial results).  Synchronous.
+ */
+tq_status tq_pack(const float* W, int64_t N, int64_t K,
+                  uint8_t* codes, uint16_t* scale_f16, hipStream_t stream);
+
+/*
+ * tq_unpack - decode packed ternary weights.
+ *   t_out        [N, K] int8 in {-1, 0, +1} (device, written; may be NULL).
+ *   wdq_f16_out  [N, K] fp16 bit patterns of t * scale (device, written; may
+ *                be NULL).  The product is exact in fp16 with IEEE signs
+ *                (-1 * +0 = -0, 0 * s = +0).
+ * Errors: TQ_ERR_BAD_CODE if any field of columns 0..K-1 is 0b11 (outputs
+ * then hold partial results; padding fields are not examined).  Synchronous.
+ */
+tq_status tq_unpack(const uint8_t* codes, const uint16_t* scale_f16, int64_t N, int64_t K,
+                    int8_t* t_out, uint16_t* wdq_f16_out, hipStream_t stream);
+
+/*
+ * w4a16_pack - symmetric int4 quantization, group of 128 along K.
+ *   W           [N, K] fp32 (device), K % group_size == 0.
+ *   qweight     [N, K/8] int32 (device, written); nibble i (bits 4i..4i+3)
+ *               of word j holds column 8j+i, as q = r + 8 in 0..15.
+ *   scales_f16  [N, K/group_size] fp16 bit patterns (device, written).
+ * Per (row, group): s = fp16(max|w| / 7) (fp64 divide, one rounding);
+ * r = round-half-even(w / s) in fp64, clamped to [-8, 7]; r = 0 if s == 0.
+ * Errors: TQ_ERR_GROUP unless group_size == 128; TQ_ERR_NONFINITE,
+ * TQ_ERR_RANGE as for tq_pack.  Synchronous.
+ */
+tq_status w4a16_pack(const float* W, int64_t N, int64_t K, int64_t group_size,
+                     int32_t* qweight, uint16_t* scales_f16, hipStream_t stream);
+
+/*
+ * w4a16_unpack - decode int4 weights.
+ *   q_out        [N, K] uint8 codes 0..15 (device, written; may be NULL).
+ *   wdq_f16_out  [N, K] fp16 bit patterns of (q - 8) * s rounded once to
+ *                nearest even (device, written; may be NULL).
+ * Synchronous.
+ */
+tq_status w4a16_unpack(const int32_t* qweight, const uint16_t* scales_f16,
+                       int64_t N, int64_t K, int64_t group_size,
+                       uint8_t* q_out, uint16_t* wdq_f16_out, hipStream_t stream);
+
+/* ------------------------------------------------------------------ apply */
+
+/*
+ * tq_gemm - C = A * dequant(codes, scale)^T (+ bias), fp32 accumulation.
+ *   A      [M, K] activations in `dt` (device, 16-byte aligned).
+ *   codes  [N, K/4] packed ternary codes as written by tq_pack (16-byte aligned).
+ *   scale_f16 [N] fp16 row scales.
+ *   bias   [N] in `dt`, added in fp32 after scaling (may be NULL).
+ *   C      [M, N] in `dt` (device, written), rounded once from fp32 to
+ *          nearest even; overflow gives +-inf.
+ * C[m, n] = scale[n] * sum_k A[m, k] * t[n, k] + bias[n]: the scale is
+ * applied after accumulation (ternary page, section 4.2).  Requires
+ * K % 64 == 0 (rows are whole 16-byte chunks).  A row of codes containing the
+ * unused field 0b11 gives an unspecified result.  Asynchronous; allocates
+ * nothing; graph-capturable.
+ */
+tq_status tq_gemm(const void* A, tq_dtype dt, int64_t M, int64_t N, int64_t K,
+                  const uint8_t* codes, const uint16_t* scale_f16, const void* bias,
+                  void* C, hipStream_t stream);
+
+/* tq_gemm with a forced kernel path (tests and benchmarks). */
+tq_status tq_gemm_ex(const void* A, tq_dtype dt, int64_t M, int64_t N, int64_t K,
+                     const uint8_t* codes, const uint16_t* scale_f16, const void* bias,
+                     void* C, hipStream_t stream, tq_path path);
+
+/*
+ * w4a16_gemm - C = A * dequant(qweight, scales)^T (+ bias), fp32 accumulation.
+ *   qweight [N, K/8] int32 and scales_f16 [N, K/128] as written by
+ *   w4a16_pack; group_size must be 128; K % 128 == 0.
+ * C[m, n] = sum_g s[n, g] * sum_{k in g} A[m, k] * (q[n, k] - 8) + bias[n]:
+ * the group scale multiplies each group's fp32 partial sum.  Other arguments
+ * as tq_gemm.  Asynchronous; allocates nothing; graph-capturable.
+ */
+tq_status w4a16_gemm(const void* A, tq_dtype dt, int64_t M, int64_t N, int64_t K,
+                     const int32_t* qweight, const uint16_t* scales_f16, int64_t group_size,
+                     const void* bias, void* C, hipStream_t stream);
+
+/* w4a16_gemm with a forced kernel path (tests and benchmarks). */
+tq_status w4a16_gemm_ex(const void* A, tq_dtype dt, int64_t M, int64_t N, int64_t K,
+                        const int32_t* qweight, const uint16_t* scales_f16, int64_t group_size,
+                        const void* bias, void* C, hipStream_t stream, tq_path path);
+
+/* ------------------------------------------------------------------ misc */
+
+/*
+ * tq_select_path - the dispatcher's choice for a shape (never TQ_PATH_AUTO).
+ *   format: 0 = ternary, 1 = W4A16.  Decode-sized M streams the weights
+ *   (they dominate the bytes moved); prefill-sized M is a dense contraction
+ *   for the matrix cores (the decode / prefill split of the quantization
+ *   decision tree on page "10.6 Quantization choice and vLLM in practice",
+ *   section 10.6.1).
+ */
+tq_path tq_select_path(int format, int64_t M, int64_t N, int64_t K, tq_dtype dt);
+
+/* Static string for a status code (never NULL). */
+const char* tq_status_str(tq_status s);
+
+/* TQ_ABI_VERSION of the loaded library. */
+int tq_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQ_H */

@@ -505,6 +505,17 @@ def pin_tolerance_check(o):
     assert not ok
     ok, st = o.check.tolerance_ok(np.array([[np.nan, -2.0]]), ref, mag)
     assert not ok and not st["finite"]
+    # bf16 outputs: the exact value 2 + 2^-7 (mag 2 + 2^-7) is a tie between the
+    # bf16 neighbours 2 and 2 + 2^-6; either is a correct rounding, off by 2^-7,
+    # which exceeds 2e-3 * mag + 1e-3 = 0.00504 but not the added 2^-8 * |out|.
+    x = 2 + 2.0 ** -7
+    ok, _ = o.check.tolerance_ok(np.array([[2.0]]), np.array([[x]]), np.array([[x]]))
+    assert not ok
+    for c in (2.0, 2 + 2.0 ** -6):
+        ok, st = o.check.tolerance_ok(np.array([[c]]), np.array([[x]]), np.array([[x]]), out_dtype="bf16")
+        assert ok, st
+    ok, _ = o.check.tolerance_ok(np.array([[2.0 - 2.0 ** -6]]), np.array([[x]]), np.array([[x]]), out_dtype="bf16")
+    assert not ok
     qc = o.check.quant_check(np.array([1.0, 2.0]), np.array([1.0, 2.5]), atol=0.1, rtol=0.1)
     assert qc == {"ok": False, "max_abs": 0.5, "mean_abs": 0.25, "finite": True}
 

@@ -1,0 +1,116 @@
+"""The C-ABI library loads and exports every symbol include/tq.h declares.
+
+CPU only: these calls either need no device (version, strings, dispatcher)
+or are rejected by host-side argument checks before any HIP call is made.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from bit_weight_only_tq_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tq.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for required in ("tq_pack", "tq_gemm", "w4a16_gemm", "tq_unpack", "w4a16_pack", "w4a16_unpack"):
+        assert required in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+        assert name in _lib.SIGNATURES, f"binding lacks a prototype for {name}"
+
+
+def test_binding_declares_nothing_extra():
+    assert set(_lib.SIGNATURES) == set(_declared_functions())
+
+
+def test_version_and_status_strings(lib):
+    assert lib.tq_abi_version() == 1
+    src = open(HEADER).read()
+    assert "#define TQ_ABI_VERSION 1" in src
+    for code, name in _lib.STATUS_NAMES.items():
+        assert re.search(rf"\b{name}\s*=\s*{code}\b", src), name
+        s = lib.tq_status_str(code)
+        assert isinstance(s, bytes) and len(s) > 0
+    assert lib.tq_status_str(99) == b"unknown status"
+
+
+def test_dispatcher_by_m():
+    sel = _lib.tq_select_path
+    for M in (1, 4, 16):
+        assert sel("ternary", M, 4096, 4096) == "gemv"
+        assert sel("w4a16", M, 4096, 4096) == "gemv"
+    for M in (2048, 4096, 8192):
+        assert sel("ternary", M, 14336, 4096, "bf16") == "gemm"
+
+
+V = ctypes.c_void_p
+FAKE = V(0x10000)          # never dereferenced: every call below fails a host check first
+MIS = V(0x10002)           # 2-byte aligned only
+
+
+@pytest.mark.parametrize("args, want", [
+    ((None, 0, 1, 64, 64, FAKE, FAKE, None, FAKE, None), "TQ_ERR_NULL"),
+    ((FAKE, 0, 1, 64, 64, None, FAKE, None, FAKE, None), "TQ_ERR_NULL"),
+    ((FAKE, 0, 1, 64, 64, FAKE, None, None, FAKE, None), "TQ_ERR_NULL"),
+    ((FAKE, 0, 1, 64, 64, FAKE, FAKE, None, None, None), "TQ_ERR_NULL"),
+    ((FAKE, 7, 1, 64, 64, FAKE, FAKE, None, FAKE, None), "TQ_ERR_DTYPE"),
+    ((FAKE, 0, 0, 64, 64, FAKE, FAKE, None, FAKE, None), "TQ_ERR_SHAPE"),
+    ((FAKE, 0, 1, -5, 64, FAKE, FAKE, None, FAKE, None), "TQ_ERR_SHAPE"),
+    ((FAKE, 0, 1, 64, 0, FAKE, FAKE, None, FAKE, None), "TQ_ERR_SHAPE"),
+    ((FAKE, 0, 1, 64, 96, FAKE, FAKE, None, FAKE, None), "TQ_ERR_SHAPE"),   # K % 64 != 0
+    ((MIS, 0, 1, 64, 64, FAKE, FAKE, None, FAKE, None), "TQ_ERR_ALIGN"),
+    ((FAKE, 0, 1, 64, 64, MIS, FAKE, None, FAKE, None), "TQ_ERR_ALIGN"),
+    ((FAKE, 0, 1, 64, 64, FAKE, FAKE, None, V(0x10001), None), "TQ_ERR_ALIGN"),
+])
+def test_tq_gemm_host_checks(lib, args, want):
+    assert _lib.STATUS_NAMES[lib.tq_gemm(*args)] == want
+
+
+def test_tq_gemm_ex_bad_path(lib):
+    st = lib.tq_gemm_ex(FAKE, 0, 32, 64, 64, FAKE, FAKE, None, FAKE, None, 1)  # gemv cannot take M=32
+    assert _lib.STATUS_NAMES[st] == "TQ_ERR_PATH"
+    st = lib.tq_gemm_ex(FAKE, 0, 1, 64, 64, FAKE, FAKE, None, FAKE, None, 9)
+    assert _lib.STATUS_NAMES[st] == "TQ_ERR_PATH"
+
+
+@pytest.mark.parametrize("args, want", [
+    ((FAKE, 0, 1, 64, 128, FAKE, FAKE, 64, None, FAKE, None), "TQ_ERR_GROUP"),
+    ((FAKE, 0, 1, 64, 192, FAKE, FAKE, 128, None, FAKE, None), "TQ_ERR_SHAPE"),
+    ((None, 0, 1, 64, 128, FAKE, FAKE, 128, None, FAKE, None), "TQ_ERR_NULL"),
+    ((FAKE, 2, 1, 64, 128, FAKE, FAKE, 128, None, FAKE, None), "TQ_ERR_DTYPE"),
+])
+def test_w4a16_gemm_host_checks(lib, args, want):
+    assert _lib.STATUS_NAMES[lib.w4a16_gemm(*args)] == want
+
+
+def test_prepare_host_checks(lib):
+    name = _lib.STATUS_NAMES
+    assert name[lib.tq_pack(None, 4, 4, FAKE, FAKE, None)] == "TQ_ERR_NULL"
+    assert name[lib.tq_pack(FAKE, 0, 4, FAKE, FAKE, None)] == "TQ_ERR_SHAPE"
+    assert name[lib.tq_pack(FAKE, 4, 64, MIS, FAKE, None)] == "TQ_ERR_ALIGN"
+    assert name[lib.tq_unpack(None, FAKE, 4, 4, None, None, None)] == "TQ_ERR_NULL"
+    assert name[lib.tq_unpack(FAKE, FAKE, 4, -1, None, None, None)] == "TQ_ERR_SHAPE"
+    assert name[lib.w4a16_pack(FAKE, 4, 128, 32, FAKE, FAKE, None)] == "TQ_ERR_GROUP"
+    assert name[lib.w4a16_pack(FAKE, 4, 100, 128, FAKE, FAKE, None)] == "TQ_ERR_SHAPE"
+    assert name[lib.w4a16_pack(MIS, 4, 128, 128, FAKE, FAKE, None)] == "TQ_ERR_ALIGN"
+    assert name[lib.w4a16_unpack(FAKE, FAKE, 4, 128, 64, None, None, None)] == "TQ_ERR_GROUP"

@@ -1,0 +1,197 @@
+"""GPU parity: quantized GEMV / GEMM outputs against the fp64 oracle.
+
+Each output element must be finite and within 2e-3 * sum_k |a_k w_k| + 1e-3
+of the oracle's fp64 product with the dequantized weights.  One-hot
+activations must reproduce single dequantized weights bit for bit.
+"""
+import numpy as np
+import pytest
+
+import oracle.rne as OR
+import oracle.ternary as OT
+import oracle.w4 as OW
+import synth
+from gpu_common import bits16, check_close, log, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+_CACHE = {}
+
+
+def _ternary(N, K, dev):
+    """(W, codes, scale on device, oracle codes, oracle scale bits, wdq64) for a shape."""
+    key = ("t", N, K)
+    if key not in _CACHE:
+        import torch
+        import bit_weight_only_tq_amd as tq
+        W = synth.smallest_case()[0] if (N, K) == (256, 256) else synth.weights(N, K, synth.seed_for("w", N, K))
+        codes, scale = tq.tq_pack(torch.from_numpy(W).to(dev))
+        rc, rs = OT.ternary_pack(W)
+        np.testing.assert_array_equal(codes.cpu().numpy(), rc)
+        np.testing.assert_array_equal(bits16(scale), rs)
+        _CACHE.clear()
+        _CACHE[key] = (codes, scale, rc, rs, OT.ternary_dequant(rc, rs, K))
+    return _CACHE[key]
+
+
+def _w4(N, K, dev):
+    key = ("w4", N, K)
+    if key not in _CACHE:
+        import torch
+        import bit_weight_only_tq_amd as tq
+        W = synth.weights(N, K, synth.seed_for("w4", N, K))
+        q, s = tq.w4a16_pack(torch.from_numpy(W).to(dev))
+        rq, rs = OW.w4_pack(W)
+        np.testing.assert_array_equal(q.cpu().numpy(), rq)
+        _CACHE.clear()
+        _CACHE[key] = (q, s, rq, rs, OW.w4_dequant(rq, rs, K))
+    return _CACHE[key]
+
+
+def test_smallest_case():
+    """256 x 256 ternary layer, M = 1, fp16, seed 0."""
+    import bit_weight_only_tq_amd as tq
+    dev = require_gpu()
+    log("smallest case 256x256 M=1")
+    W, A = synth.smallest_case()
+    codes, scale, rc, rs, wdq = _ternary(256, 256, dev)
+    C = tq.tq_gemm(A.to(dev), codes, scale)
+    check_close(C, A, wdq, label="smallest")
+
+
+DECODE_SHAPES = [(4096, 4096), (1024, 4096), (14336, 4096), (4096, 14336)]
+
+
+@pytest.mark.parametrize("N,K", DECODE_SHAPES)
+@pytest.mark.parametrize("M", [1, 4, 16])
+def test_ternary_decode(N, K, M):
+    import bit_weight_only_tq_amd as tq
+    dev = require_gpu()
+    log(f"tq_gemm decode N={N} K={K} M={M}")
+    codes, scale, rc, rs, wdq = _ternary(N, K, dev)
+    A = synth.activations(M, K, synth.seed_for("a", N, K, M), "f16")
+    assert tq.tq_select_path("ternary", M, N, K) == "gemv"
+    C = tq.tq_gemm(A.to(dev), codes, scale)
+    check_close(C, A, wdq, label=f"decode {N}x{K} M={M}")
+
+
+@pytest.mark.parametrize("N,K", DECODE_SHAPES)
+@pytest.mark.parametrize("M", [1, 4, 16])
+def test_w4_decode(N, K, M):
+    import bit_weight_only_tq_amd as tq
+    dev = require_gpu()
+    log(f"w4a16_gemm decode N={N} K={K} M={M}")
+    q, s, rq, rs, wdq = _w4(N, K, dev)
+    A = synth.activations(M, K, synth.seed_for("a4", N, K, M), "f16")
+    C = tq.w4a16_gemm(A.to(dev), q, s)
+    check_close(C, A, wdq, label=f"w4 {N}x{K} M={M}")
+
+
+@pytest.mark.parametrize("N,K", [(14336, 4096), (4096, 14336)])
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_ternary_prefill_full(N, K, dt):
+    """M = 2048, every output element checked."""
+    import bit_weight_only_tq_amd as tq
+    dev = require_gpu()
+    M = 2048
+    log(f"tq_gemm prefill N={N} K={K} M={M} {dt}")
+    codes, scale, rc, rs, wdq = _ternary(N, K, dev)
+    A = synth.activations(M, K, synth.seed_for("p", N, K, M, dt), dt)
+    assert tq.tq_select_path("ternary", M, N, K, dt) == "gemm"
+    C = tq.tq_gemm(A.to(dev), codes, scale)
+    check_close(C, A, wdq, label=f"prefill {N}x{K} M={M} {dt}")
+
+
+@pytest.mark.parametrize("N,K", [(14336, 4096), (4096, 14336)])
+@pytest.mark.parametrize("M,dt", [(4096, "bf16"), (4096, "f16"), (8192, "bf16")])
+def test_ternary_prefill_sampled(N, K, M, dt):
+    """Large M: all columns of 256 sampled rows (fixed seed) checked."""
+    import torch
+    import bit_weight_only_tq_amd as tq
+    dev = require_gpu()
+    log(f"tq_gemm prefill sampled N={N} K={K} M={M} {dt}")
+    codes, scale, rc, rs, wdq = _ternary(N, K, dev)
+    A = synth.activations(M, K, synth.seed_for("p", N, K, M, dt), dt)
+    C = tq.tq_gemm(A.to(dev), codes, scale)
+    rows = np.sort(np.random.default_rng(M + N).choice(M, 256, replace=False))
+    idx = torch.from_numpy(rows)
+    check_close(C.cpu()[idx], A[idx], wdq, label=f"prefill {N}x{K} M={M} {dt} sampled")
+
+
+@pytest.mark.parametrize("M,N,K", [
+    (1, 64, 64), (3, 100, 128), (17, 130, 192), (33, 257, 256), (130, 300, 64), (129, 513, 320),
+    (5, 1000, 448), (2, 7, 64),
+])
+@pytest.mark.parametrize("path", ["gemv", "gemm"])
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_ternary_ragged(M, N, K, path, dt):
+    """Tiles with ragged edges in M and N, several K steps, both kernel families."""
+    import torch
+    import bit_weight_only_tq_amd as tq
+    dev = require_gpu()
+    if path == "gemv" and M > 16:
+        pytest.skip("gemv handles M <= 16")
+    log(f"tq_gemm ragged M={M} N={N} K={K} {path} {dt}")
+    codes, scale, rc, rs, wdq = _ternary(N, K, dev)
+    A = synth.activations(M, K, synth.seed_for("r", M, N, K, dt), dt)
+    bias = synth.activations(1, N, synth.seed_for("b", N, dt), dt)[0]
+    C = tq.tq_gemm(A.to(dev), codes, scale, bias=bias.to(dev), path=path)
+    check_close(C, A, wdq, bias=bias, label=f"ragged {M}x{N}x{K} {path} {dt}")
+
+
+@pytest.mark.parametrize("path", ["gemv", "gemm"])
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_one_hot_bit_exact(path, dt):
+    """A = rows of the identity: C[m, n] = wdq[n, k_m] exactly (one rounding of
+    +-scale or 0 to the output dtype); pins indexing and bit order."""
+    import torch
+    import bit_weight_only_tq_amd as tq
+    dev = require_gpu()
+    N, K = 300, 256
+    log(f"one-hot {path} {dt}")
+    codes, scale, rc, rs, wdq = _ternary(N, K, dev)
+    ks = [0, 1, 2, 3, 4, 7, 8, 15, 16, 63, 64, 127, 200, 255] if path == "gemm" else [0, 5, 9, 255]
+    M = len(ks)
+    A = torch.zeros((M, K), dtype=torch.float16 if dt == "f16" else torch.bfloat16)
+    for m, k in enumerate(ks):
+        A[m, k] = 1.0
+    C = tq.tq_gemm(A.to(dev), codes, scale, path=path)
+    want = wdq[:, ks].T
+    want_bits = OR.f16_bits(want) if dt == "f16" else OR.bf16_bits(want)
+    np.testing.assert_array_equal(bits16(C), want_bits)
+
+
+@pytest.mark.parametrize("path,M", [("gemv", 1), ("gemv", 16), ("gemm", 300)])
+def test_deterministic_and_canary(path, M):
+    """Two runs give bit-identical outputs; the bytes after C stay untouched."""
+    import torch
+    import bit_weight_only_tq_amd as tq
+    dev = require_gpu()
+    N, K = 1024, 4096
+    log(f"determinism {path} M={M}")
+    codes, scale, rc, rs, wdq = _ternary(N, K, dev)
+    A = synth.activations(M, K, synth.seed_for("d", M), "f16").to(dev)
+    buf = torch.full((M * N + 4096,), -12345.0, dtype=torch.float16, device=dev)
+    C1 = buf[:M * N].view(M, N)
+    tq.tq_gemm(A, codes, scale, out=C1, path=path)
+    C2 = tq.tq_gemm(A, codes, scale, path=path)
+    torch.cuda.synchronize()
+    assert torch.equal(C1.view(torch.int16), C2.view(torch.int16))
+    assert bool((buf[M * N:] == -12345.0).all())
+
+
+@pytest.mark.parametrize("M", [1, 40])
+def test_w4_ragged_and_blocked(M):
+    import torch
+    import bit_weight_only_tq_amd as tq
+    dev = require_gpu()
+    N, K = 200, 384
+    log(f"w4 ragged M={M}")
+    q, s, rq, rs, wdq = _w4(N, K, dev)
+    A = synth.activations(M, K, synth.seed_for("w4r", M), "f16")
+    bias = synth.activations(1, N, synth.seed_for("w4b"), "f16")[0]
+    C = tq.w4a16_gemm(A.to(dev), q, s, bias=bias.to(dev))
+    check_close(C, A, wdq, bias=bias, label=f"w4 ragged M={M}")
+    Ab = synth.activations(M, K, synth.seed_for("w4rb", M), "bf16")
+    C = tq.w4a16_gemm(Ab.to(dev), q, s)
+    check_close(C, Ab, wdq, label=f"w4 ragged bf16 M={M}")

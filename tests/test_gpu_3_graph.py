@@ -1,0 +1,46 @@
+"""The apply calls allocate nothing and never synchronize, so they can be
+captured in a HIP graph; every replay must equal the eager result."""
+import pytest
+
+import synth
+from gpu_common import log, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("fmt,M,N,K", [
+    ("ternary", 1, 4096, 4096), ("ternary", 16, 1024, 4096), ("ternary", 512, 1024, 4096),
+    ("w4a16", 4, 1024, 4096),
+])
+def test_graph_replay_matches_eager(fmt, M, N, K):
+    import torch
+    import bit_weight_only_tq_amd as tq
+    dev = require_gpu()
+    log(f"graph {fmt} M={M} N={N} K={K}")
+    W = torch.from_numpy(synth.weights(N, K, synth.seed_for("g", fmt, N, K))).to(dev)
+    if fmt == "ternary":
+        wq, sc = tq.tq_pack(W)
+        fn = lambda a, out: tq.tq_gemm(a, wq, sc, out=out)  # noqa: E731
+    else:
+        wq, sc = tq.w4a16_pack(W)
+        fn = lambda a, out: tq.w4a16_gemm(a, wq, sc, out=out)  # noqa: E731
+    A = synth.activations(M, K, synth.seed_for("ga", M), "f16").to(dev)
+    eager = fn(A, None)
+    torch.cuda.synchronize()
+    out = torch.empty_like(eager)
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn(A, out)  # warm-up outside the graph
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        fn(A, out)
+    for i in range(4):
+        out.fill_(0)
+        junk = torch.randn(1000, device=dev).sum()  # unrelated eager work between replays
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {i}"
+        del junk
