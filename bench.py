@@ -41,6 +41,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--layers", type=int, default=32)
     ap.add_argument("--graph", action="store_true", help="replay each step from a captured HIP graph")
+    ap.add_argument("--fused", action="store_true", help="q,k,v and gate,up as one call each (N stacked)")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default="", help="profiling helper: 'decode' or 'prefill'")
@@ -52,14 +53,25 @@ def ternary_bytes(M, N, K):
     return N * ((K + 3) // 4) + 2 * N + 2 * M * K + 2 * M * N
 
 
-def build_decode(layers, dev):
+def layer_shapes(fused):
+    """Projections of one Llama-3-8B layer; fused = q,k,v and gate,up stacked along N
+    (one call each, as a serving stack lays them out)."""
+    import synth
+    if not fused:
+        return list(synth.LLAMA3_8B.items())
+    s = synth.LLAMA3_8B
+    return [("qkv", (s["q"][0] + s["k"][0] + s["v"][0], 4096)), ("o", s["o"]),
+            ("gate_up", (2 * s["gate"][0], 4096)), ("down", s["down"])]
+
+
+def build_decode(layers, dev, fused=False):
     import torch
     import bit_weight_only_tq_amd as tq
     import synth
     mats = []
     t0 = time.time()
     for layer in range(layers):
-        for name, (N, K) in synth.LLAMA3_8B.items():
+        for name, (N, K) in layer_shapes(fused):
             W = synth.weights_device(N, K, synth.seed_for("bench8b", layer, name), dev)
             codes, scale = tq.tq_pack(W)
             del W
@@ -196,7 +208,7 @@ def main():
     out = {}
     if args.only in ("", "decode"):
         import synth
-        mats = build_decode(args.layers, dev)
+        mats = build_decode(args.layers, dev, args.fused)
         xs = {K: synth.activations_device(1, K, synth.seed_for("benchx", K), "f16", dev)
               for K in {m[2] for m in mats}}
         outs = [torch.empty((1, m[1]), dtype=torch.float16, device=dev) for m in mats]
@@ -242,12 +254,13 @@ def main():
                 "workload": "Llama-3-8B decode, M=1: 32 layers x {q,k,v,o,gate,up,down} ternary GEMV",
                 "layers": args.layers, "M": 1, "launches_per_step": len(mats),
                 "packed_bytes_per_step": packed, "algorithmic_bytes_per_step": alg,
-                "graph": bool(args.graph), "hbm_frac": round(value / HBM_PEAK_GBS, 4),
+                "graph": bool(args.graph), "fused_qkv_gate_up": bool(args.fused),
+                "hbm_frac": round(value / HBM_PEAK_GBS, 4),
             },
             "roofline": {
                 "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": "ternary_gemv_kernel<1,F16>", "avg_launch_us": round(avg_dur * 1e6, 3),
+                "kernel": "ternary_gemv_mfma_kernel", "avg_launch_us": round(avg_dur * 1e6, 3),
                 "avg_alg_bytes_per_launch": round(avg_bytes), "launches_timed": nl,
             },
         })

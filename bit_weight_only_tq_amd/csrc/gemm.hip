@@ -122,6 +122,8 @@ __global__ __launch_bounds__(kThreads) void ternary_gemm_kernel(GemmArgs p) {
                             : make_uint4(0x55555555u, 0x55555555u, 0x55555555u, 0x55555555u);
     };
 
+    const uint32_t magic_v = vgpr_const<Mfma<T>::kMagicPair>();
+    const uint32_t mask3 = sgpr_const<0x00030003u>();
     auto store_lds = [&]() {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
@@ -136,7 +138,7 @@ __global__ __launch_bounds__(kThreads) void ternary_gemm_kernel(GemmArgs p) {
         for (int d = 0; d < 4; ++d) {  // code dword d = columns 16d .. 16d+15
             uint32_t o[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) o[i] = ((bw[d] >> (2 * i)) & 0x00030003u) | Mfma<T>::kMagicPair;
+            for (int i = 0; i < 8; ++i) o[i] = ((bw[d] >> (2 * i)) & mask3) | magic_v;
             uint4* dst = reinterpret_cast<uint4*>(Bs + tid * LDSK + 16 * d);
             dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
             dst[1] = make_uint4(o[4], o[5], o[6], o[7]);

@@ -119,9 +119,417 @@ __global__ __launch_bounds__(kGemvWaves * kWave) void w4_gemv_kernel(GemmArgs p)
     }
 }
 
+// ------------------------------------------------ ternary, matrix cores
+//
+// fp16 activations, M <= 16, K % 256 == 0.  The multiply-accumulates run on
+// v_mfma_f32_16x16x32_f16 with M padded to 16 rows, so every M up to 16
+// costs the same; the VALU only unpacks codes, at about one op per code.
+//
+// Unpack: a code dword x holds fields f_0..f_15 (f_j at bits 2j, column j of
+// its 16).  Masking one field of each 16-bit half into the mantissa of the
+// fp16 constant 1024 (0x6400, unit in the last place 1) gives, in one
+// v_and_or_b32, the pair P_i = (1024 + 4^s f_i, 1024 + 4^s f_{i+8}) with
+// s = i for fields in bits 0..9 (i = 0..4); fields in bits 10..15 are shifted
+// down by 10 first (s = i - 5).  The activations are pre-scaled once per
+// 256 columns to a'_k = a_k / 4^s(k) and paired the same way, so
+//   sum_k a'_k (1024 + 4^s c_k) = sum_k a_k c_k + sum_k a'_k 1024,
+// and since t = c - 1, sum_k a_k t_k = that minus sum_k a'_k (1024 + 4^s).
+// The subtracted term does not depend on the weight row: one extra MFMA of
+// the same a' against the constant pattern -(1024 + 4^s) per eight MFMAs
+// accumulates it for all rows at once.
+//
+// Work split: a block owns 16R weight rows (R blocks of 16, one per MFMA
+// column tile) and all of K; its W waves take every W-th 256-column
+// chunk-set.  Lane l = 16g + i loads 16 bytes (64 codes) of row i of each
+// row block, chunk 4cs + g, and the 64 activations of row m = i of that
+// chunk; MFMA j of a chunk-set contracts code dword j/2, fields
+// 4(j%2)..4(j%2)+3 and their partners.  Wave partials meet in LDS and are
+// summed in a fixed order: deterministic, no atomics.
+
+constexpr uint32_t kMagic2 = 0x64006400u;  // (1024.0, 1024.0) as fp16
+
+template <int I>
+__device__ __forceinline__ uint32_t field_pair(uint32_t x, uint32_t y, uint32_t magic_v) {
+    if constexpr (I < 5) return (x & sgpr_const<(0x00030003u << (2 * I))>()) | magic_v;
+    else return (y & sgpr_const<(0x00030003u << (2 * (I - 5)))>()) | magic_v;
+}
+
+// 1 / 4^s for field I, as an fp16 pair.
+template <int I>
+__device__ __forceinline__ f16x2 inv_mult() {
+    constexpr int s = I < 5 ? I : I - 5;
+    const _Float16 v = (_Float16)(1.0f / (float)(1 << (2 * s)));
+    return f16x2{v, v};
+}
+
+// -(1024 + 4^s) for field I in both halves (the code-01 pattern, negated).
+template <int I>
+__device__ __forceinline__ constexpr uint32_t neg_one_pattern() {
+    constexpr int s = I < 5 ? I : I - 5;
+    return 0xE400E400u | (0x00010001u << (2 * s));
+}
+
+// a' pair for field I of code dword D: (a[16D+I], a[16D+I+8]) / 4^s(I).
+template <int D, int I>
+__device__ __forceinline__ uint32_t a_pair(const uint4 av[8]) {
+    const uint4& lo4 = av[2 * D];
+    const uint4& hi4 = av[2 * D + 1];
+    constexpr int c = I / 2;
+    const uint32_t lo = c == 0 ? lo4.x : c == 1 ? lo4.y : c == 2 ? lo4.z : lo4.w;
+    const uint32_t hi = c == 0 ? hi4.x : c == 1 ? hi4.y : c == 2 ? hi4.z : hi4.w;
+    const uint32_t pr = __builtin_amdgcn_perm(hi, lo, (I & 1) ? 0x07060302u : 0x05040100u);
+    const f16x2 v = __builtin_bit_cast(f16x2, pr) * inv_mult<I>();
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ uint32_t dword_of(const uint4& q, int d) {
+    return d == 0 ? q.x : d == 1 ? q.y : d == 2 ? q.z : q.w;
+}
+
+template <int R, int W>
+__global__ __launch_bounds__(W * kWave) void ternary_gemv_mfma_kernel(GemmArgs p) {
+    __shared__ f32x4 red[W][R][kWave];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x >> 6;
+    const int g = lane >> 4;
+    const int i16 = lane & 15;
+    const int64_t N = p.N, K = p.K;
+    const int M = (int)p.M;
+    const int64_t rb = K / 4;
+    const int CS = (int)(K / 256);
+    const int64_t n_base = (int64_t)blockIdx.x * (16 * R);
+    const uint8_t* codes = static_cast<const uint8_t*>(p.wq);
+    const bool a_live = i16 < M;
+    const uint16_t* a_row = p.A + (int64_t)(a_live ? i16 : 0) * K;
+
+    const uint8_t* crow[R];
+    bool rlive[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int64_t n = n_base + 16 * r + i16;
+        rlive[r] = n < N;
+        crow[r] = codes + (rlive[r] ? n : 0) * rb;
+    }
+
+    f32x4 acc[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 dacc = f32x4{0.f, 0.f, 0.f, 0.f};
+    const uint32_t magic_v = vgpr_const<kMagic2>();
+
+    uint4 q[R], qn[R];
+    int cs = wave;
+    if (cs < CS) {
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            q[r] = rlive[r] ? *reinterpret_cast<const uint4*>(crow[r] + (int64_t)(4 * cs + g) * 16)
+                            : make_uint4(0x55555555u, 0x55555555u, 0x55555555u, 0x55555555u);
+    }
+    for (; cs < CS; cs += W) {
+        const int chunk = 4 * cs + g;
+        // prefetch the next chunk-set's codes
+        const int csn = cs + W;
+        if (csn < CS) {
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+                qn[r] = rlive[r] ? *reinterpret_cast<const uint4*>(crow[r] + (int64_t)(4 * csn + g) * 16)
+                                 : make_uint4(0x55555555u, 0x55555555u, 0x55555555u, 0x55555555u);
+        }
+        uint4 av[8];
+        if (a_live) {
+            const uint4* ap = reinterpret_cast<const uint4*>(a_row + (int64_t)chunk * 64);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) av[e] = ap[e];
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) av[e] = make_uint4(0u, 0u, 0u, 0u);
+        }
+#define TQ_MFMA_J(D, I0)                                                                              \
+    {                                                                                                 \
+        const uint4 aw = make_uint4(a_pair<D, I0>(av), a_pair<D, I0 + 1>(av), a_pair<D, I0 + 2>(av),  \
+                                    a_pair<D, I0 + 3>(av));                                           \
+        const f16x8 aop = __builtin_bit_cast(f16x8, aw);                                              \
+        const uint4 nw = make_uint4(neg_one_pattern<I0>(), neg_one_pattern<I0 + 1>(),                 \
+                                    neg_one_pattern<I0 + 2>(), neg_one_pattern<I0 + 3>());            \
+        dacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, __builtin_bit_cast(f16x8, nw), dacc, 0, 0, 0); \
+        _Pragma("unroll") for (int r = 0; r < R; ++r) {                                               \
+            const uint32_t x = dword_of(q[r], D);                                                     \
+            const uint32_t y = x >> 10;                                                               \
+            const uint4 bw = make_uint4(field_pair<I0>(x, y, magic_v), field_pair<I0 + 1>(x, y, magic_v), \
+                                        field_pair<I0 + 2>(x, y, magic_v), field_pair<I0 + 3>(x, y, magic_v)); \
+            acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, __builtin_bit_cast(f16x8, bw), acc[r], 0, 0, 0); \
+        }                                                                                             \
+    }
+        TQ_MFMA_J(0, 0)
+        TQ_MFMA_J(0, 4)
+        TQ_MFMA_J(1, 0)
+        TQ_MFMA_J(1, 4)
+        TQ_MFMA_J(2, 0)
+        TQ_MFMA_J(2, 4)
+        TQ_MFMA_J(3, 0)
+        TQ_MFMA_J(3, 4)
+#undef TQ_MFMA_J
+        if (csn < CS) {
+#pragma unroll
+            for (int r = 0; r < R; ++r) q[r] = qn[r];
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) red[wave][r][lane] = acc[r] + dacc;
+    __syncthreads();
+    for (int e = threadIdx.x; e < R * kWave; e += W * kWave) {
+        const int r = e / kWave;
+        const int l = e % kWave;
+        f32x4 s = red[0][r][l];
+#pragma unroll
+        for (int w = 1; w < W; ++w) s += red[w][r][l];
+        const int64_t n = n_base + 16 * r + (l & 15);
+        if (n >= N) continue;
+        const float sc = f16_bits_to_f32(p.scale[n]);
+        const float b = p.bias ? F16::to_f32(p.bias[n]) : 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int m = 4 * (l >> 4) + i;
+            if (m < M) p.C[(int64_t)m * N + n] = F16::from_f32(s[i] * sc + b);
+        }
+    }
+}
+
+// Same arithmetic, latency-first schedule (fp16, M <= 4, M * K <= 32768).
+//
+// 1. The block loads the activations it needs first (few KB, mostly from the
+//    L2), then every wave issues the code loads of ALL its chunk-sets (at most
+//    CSW, fully unrolled), so the kernel waits for HBM once and the in-order
+//    completion counter lets the activation work start before codes arrive.
+// 2. While the codes are in flight the block writes the scaled, paired a'
+//    values to LDS in the order the MFMA operands read them - dword
+//    ((m * K/64 + chunk) * 32 + 8 d + i) = pair (d, i) of row m - and sums the
+//    row-independent term D[m] = sum_k a'_k (1024 + 4^s(k)) with dot2 (one
+//    partial per 16 columns, reduced in a fixed order).
+// 3. Each wave contracts its chunk-sets as their codes land; partials of the
+//    W waves meet in LDS, D[m] is subtracted once, the row scale applied.
+// Block = W waves (W = ceil(K/256 / CSW) <= 16) over 16R rows and all of K.
+template <int I>
+__device__ __forceinline__ constexpr uint32_t one_pattern() {  // (1024 + 4^s) in both halves
+    constexpr int s = I < 5 ? I : I - 5;
+    return 0x64006400u | (0x00010001u << (2 * s));
+}
+
+template <int R, int CSW, int UPT>
+__global__ __launch_bounds__(1024) void ternary_gemv_lds_kernel(GemmArgs p) {
+    extern __shared__ uint4 smem[];
+    uint32_t* aps = reinterpret_cast<uint32_t*>(smem);
+    const int W = blockDim.x >> 6;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x >> 6;
+    const int g = lane >> 4;
+    const int i16 = lane & 15;
+    const int64_t N = p.N, K = p.K;
+    const int M = (int)p.M;
+    const int64_t rb = K / 4;
+    const int nch = (int)(K / 64);
+    const int CS = (int)(K / 256);
+    const int64_t n_base = (int64_t)blockIdx.x * (16 * R);
+    const uint8_t* codes = static_cast<const uint8_t*>(p.wq);
+    const int cs0 = wave * CSW;
+    const int cnt = CS - cs0 < CSW ? CS - cs0 : CSW;  // may be <= 0 for a trailing wave
+    const int units = M * nch * 4;                     // (row, chunk, dword) = 16 columns
+    uint32_t* zero_blk = aps + (int64_t)M * nch * 32;  // 32 zero dwords: a' of rows m >= M
+    float* dpart = reinterpret_cast<float*>(zero_blk + 32);  // [units] D partials
+    // Memory operations below are branch-free (addresses clamped into the
+    // tensors, surplus results discarded) so the hardware's in-order load
+    // counters let each use wait only for the loads it needs.
+
+    // 1a. activation loads of this thread's prep units (issued before the codes)
+    uint4 av[UPT][8];
+#pragma unroll
+    for (int j = 0; j < UPT; ++j) {
+        const int u = (int)threadIdx.x + j * (int)blockDim.x;
+        const int uc = u < units ? u : units - 1;
+        const int m = uc / (nch * 4);
+        const int rem = uc - m * nch * 4;
+        const uint4* src = reinterpret_cast<const uint4*>(p.A + (int64_t)m * K + (int64_t)(rem >> 2) * 64 + 16 * (rem & 3));
+        av[j][0] = src[0];
+        av[j][1] = src[1];
+    }
+    // 1b. all code loads of this wave (rows past N re-read row N-1, chunk-sets
+    //     past the wave's share re-read its first one; both are ignored)
+    uint4 q[CSW][R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int64_t n = n_base + 16 * r + i16;
+        const uint8_t* crow = codes + (n < N ? n : N - 1) * rb;
+#pragma unroll
+        for (int s = 0; s < CSW; ++s) {
+            const int cs = (s < cnt) ? cs0 + s : (cs0 < CS ? cs0 : 0);
+            q[s][r] = *reinterpret_cast<const uint4*>(crow + (int64_t)(4 * cs + g) * 16);
+        }
+    }
+    // 2. a' and D partials to LDS
+    if (threadIdx.x < 8) reinterpret_cast<uint4*>(zero_blk)[threadIdx.x] = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int j = 0; j < UPT; ++j) {
+        const int u = (int)threadIdx.x + j * (int)blockDim.x;
+        if (u >= units) break;
+        const int m = u / (nch * 4);
+        const int rem = u - m * nch * 4;
+        const uint4 w0 = make_uint4(a_pair<0, 0>(av[j]), a_pair<0, 1>(av[j]), a_pair<0, 2>(av[j]), a_pair<0, 3>(av[j]));
+        const uint4 w1 = make_uint4(a_pair<0, 4>(av[j]), a_pair<0, 5>(av[j]), a_pair<0, 6>(av[j]), a_pair<0, 7>(av[j]));
+        float dp = 0.0f;
+        dp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w0.x), __builtin_bit_cast(f16x2, one_pattern<0>()), dp, false);
+        dp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w0.y), __builtin_bit_cast(f16x2, one_pattern<1>()), dp, false);
+        dp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w0.z), __builtin_bit_cast(f16x2, one_pattern<2>()), dp, false);
+        dp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w0.w), __builtin_bit_cast(f16x2, one_pattern<3>()), dp, false);
+        dp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w1.x), __builtin_bit_cast(f16x2, one_pattern<4>()), dp, false);
+        dp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w1.y), __builtin_bit_cast(f16x2, one_pattern<5>()), dp, false);
+        dp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w1.z), __builtin_bit_cast(f16x2, one_pattern<6>()), dp, false);
+        dp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w1.w), __builtin_bit_cast(f16x2, one_pattern<7>()), dp, false);
+        uint4* dst = reinterpret_cast<uint4*>(aps + ((int64_t)(m * nch + (rem >> 2)) * 32 + 8 * (rem & 3)));
+        dst[0] = w0;
+        dst[1] = w1;
+        dpart[u] = dp;
+    }
+    __syncthreads();
+
+    // 3. contract
+    f32x4 acc[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const bool a_live = i16 < M;
+    const uint32_t magic_v = vgpr_const<kMagic2>();
+#pragma unroll
+    for (int s = 0; s < CSW; ++s) {
+        if (s < cnt) {
+            const int chunk = 4 * (cs0 + s) + g;
+            const uint4* arow = reinterpret_cast<const uint4*>(a_live ? aps + (int64_t)(i16 * nch + chunk) * 32 : zero_blk);
+            uint4 aw[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) aw[e] = arow[e];
+#define TQ_MFMA_L(D, I0)                                                                              \
+    {                                                                                                 \
+        const f16x8 aop = __builtin_bit_cast(f16x8, aw[2 * (D) + (I0) / 4]);                          \
+        _Pragma("unroll") for (int r = 0; r < R; ++r) {                                               \
+            const uint32_t x = dword_of(q[s][r], D);                                                  \
+            const uint32_t y = x >> 10;                                                               \
+            const uint4 bw = make_uint4(field_pair<I0>(x, y, magic_v), field_pair<I0 + 1>(x, y, magic_v), \
+                                        field_pair<I0 + 2>(x, y, magic_v), field_pair<I0 + 3>(x, y, magic_v)); \
+            acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, __builtin_bit_cast(f16x8, bw), acc[r], 0, 0, 0); \
+        }                                                                                             \
+    }
+            TQ_MFMA_L(0, 0)
+            TQ_MFMA_L(0, 4)
+            TQ_MFMA_L(1, 0)
+            TQ_MFMA_L(1, 4)
+            TQ_MFMA_L(2, 0)
+            TQ_MFMA_L(2, 4)
+            TQ_MFMA_L(3, 0)
+            TQ_MFMA_L(3, 4)
+#undef TQ_MFMA_L
+        }
+    }
+
+    // 4. D[m] (wave 0, fixed order), wave partials -> LDS, fixed-order sum
+    __syncthreads();  // a' no longer needed; dpart still live
+    __shared__ float dsum[4];
+    f32x4* red = reinterpret_cast<f32x4*>(smem);
+    if (wave == 0) {
+        const int per = nch * 4;
+        for (int m = 0; m < M; ++m) {
+            float t = 0.0f;
+            for (int k = lane; k < per; k += kWave) t += dpart[m * per + k];
+            t = wave_sum(t);
+            if (lane == 0) dsum[m] = t;
+        }
+    }
+    __syncthreads();  // dpart consumed before red overwrites it
+#pragma unroll
+    for (int r = 0; r < R; ++r) red[(wave * R + r) * kWave + lane] = acc[r];
+    __syncthreads();
+    for (int e = threadIdx.x; e < R * kWave; e += blockDim.x) {
+        const int r = e / kWave;
+        const int l = e % kWave;
+        f32x4 sum = red[r * kWave + l];
+        for (int w = 1; w < W; ++w) sum += red[(w * R + r) * kWave + l];
+        const int64_t n = n_base + 16 * r + (l & 15);
+        if (n >= N) continue;
+        const float sc = f16_bits_to_f32(p.scale[n]);
+        const float b = p.bias ? F16::to_f32(p.bias[n]) : 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int m = 4 * (l >> 4) + i;
+            if (m < M) p.C[(int64_t)m * N + n] = F16::from_f32((sum[i] - dsum[m]) * sc + b);
+        }
+    }
+}
+
 // ------------------------------------------------------------- launchers
 
+template <int R, int W>
+static void launch_gemv_mfma(const GemmArgs& a, hipStream_t s) {
+    const dim3 grid((unsigned)((a.N + 16 * R - 1) / (16 * R)));
+    ternary_gemv_mfma_kernel<R, W><<<grid, W * kWave, 0, s>>>(a);
+}
+
+template <int R>
+static void launch_gemv_mfma_w(const GemmArgs& a, hipStream_t s) {
+    const int64_t cs = a.K / 256;
+    if (cs >= 16) launch_gemv_mfma<R, 8>(a, s);
+    else if (cs >= 8) launch_gemv_mfma<R, 4>(a, s);
+    else if (cs >= 4) launch_gemv_mfma<R, 2>(a, s);
+    else launch_gemv_mfma<R, 1>(a, s);
+}
+
+bool ternary_gemv_mfma_ok(const GemmArgs& a) { return !a.bf16 && a.M <= kGemvMaxM && a.K % 256 == 0; }
+
+#ifndef TQ_GEMV_LDS_R
+#define TQ_GEMV_LDS_R 1
+#endif
+constexpr int kGemvLdsR = TQ_GEMV_LDS_R;  // 16-row blocks per workgroup
+constexpr int64_t kGemvLdsMaxMK = 28672;  // LDS: a' (M*K*2 B) + zero block + D partials (M*K/4 B) <= 64 KB
+
+// Shape rule for the LDS kernel: chunk-sets per wave CSW in {4, 8}, W waves.
+static bool gemv_lds_plan(const GemmArgs& a, int* csw, int* waves) {
+    if (a.bf16 || a.M > 4 || a.K % 256 != 0 || a.M * a.K > kGemvLdsMaxMK) return false;
+    const int64_t cs = a.K / 256;
+    if ((cs + 3) / 4 <= 8) *csw = 4;
+    else if ((cs + 7) / 8 <= 16) *csw = 8;
+    else return false;
+    *waves = (int)((cs + *csw - 1) / *csw);
+    return a.M * (a.K / 16) <= (int64_t)4 * *waves * kWave;  // at most 4 prep units per thread
+}
+
 hipError_t launch_ternary_gemv(const GemmArgs& a, hipStream_t s) {
+    int csw = 0, waves = 0;
+    if (gemv_lds_plan(a, &csw, &waves)) {
+        const int64_t aprime = a.M * a.K * 2 + 128 + a.M * (a.K / 16) * 4;
+        const int64_t red = (int64_t)waves * kGemvLdsR * kWave * 16;
+        const size_t lds = (size_t)(aprime > red ? aprime : red);
+        const dim3 grid((unsigned)((a.N + 16 * kGemvLdsR - 1) / (16 * kGemvLdsR)));
+        const int64_t units = a.M * (a.K / 16);
+        const int64_t upt = (units + waves * kWave - 1) / (waves * kWave);
+        const dim3 block(waves * kWave);
+#define TQ_LDS_LAUNCH(CSW, UPT) ternary_gemv_lds_kernel<kGemvLdsR, CSW, UPT><<<grid, block, lds, s>>>(a)
+        if (csw == 4) {
+            if (upt <= 1) TQ_LDS_LAUNCH(4, 1);
+            else if (upt <= 2) TQ_LDS_LAUNCH(4, 2);
+            else TQ_LDS_LAUNCH(4, 4);
+        } else {
+            if (upt <= 1) TQ_LDS_LAUNCH(8, 1);
+            else if (upt <= 2) TQ_LDS_LAUNCH(8, 2);
+            else TQ_LDS_LAUNCH(8, 4);
+        }
+#undef TQ_LDS_LAUNCH
+        return hipGetLastError();
+    }
+    if (ternary_gemv_mfma_ok(a)) {
+        if (a.M <= 4) launch_gemv_mfma_w<2>(a, s);
+        else launch_gemv_mfma_w<4>(a, s);
+        return hipGetLastError();
+    }
+    return launch_ternary_gemv_simple(a, s);
+}
+
+hipError_t launch_ternary_gemv_simple(const GemmArgs& a, hipStream_t s) {
     const dim3 grid((unsigned)((a.N + kGemvWaves - 1) / kGemvWaves));
     const dim3 block(kGemvWaves * kWave);
     if (a.M <= 1) {

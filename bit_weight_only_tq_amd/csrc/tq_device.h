@@ -82,6 +82,26 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) {
     return __uint_as_float((uint32_t)h << 16);
 }
 
+// Constants the compiler cannot fold back into literals.  A VOP3 instruction
+// on this target reads at most one scalar value and no literal, so with both
+// operands of (x & mask) | magic as literals the compiler splits the pattern
+// into v_and_b32 + v_or_b32; with the mask in an SGPR and the magic in a VGPR
+// it selects a single v_and_or_b32.  Only the constants are opaque: the
+// arithmetic stays visible to the compiler, which therefore still inserts
+// the wait states a matrix instruction needs after a VALU write.
+template <uint32_t C>
+__device__ __forceinline__ uint32_t sgpr_const() {
+    uint32_t r;
+    asm("s_mov_b32 %0, %1" : "=s"(r) : "i"(C));
+    return r;
+}
+template <uint32_t C>
+__device__ __forceinline__ uint32_t vgpr_const() {
+    uint32_t r;
+    asm("v_mov_b32 %0, %1" : "=v"(r) : "i"(C));
+    return r;
+}
+
 // Activation element type tags.
 struct F16 {
     static __device__ __forceinline__ float to_f32(uint16_t h) { return f16_bits_to_f32(h); }

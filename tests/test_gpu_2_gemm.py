@@ -121,6 +121,8 @@ def test_ternary_prefill_sampled(N, K, M, dt):
 @pytest.mark.parametrize("M,N,K", [
     (1, 64, 64), (3, 100, 128), (17, 130, 192), (33, 257, 256), (130, 300, 64), (129, 513, 320),
     (5, 1000, 448), (2, 7, 64),
+    (1, 300, 256), (4, 33, 512), (2, 70, 1280), (3, 31, 2304), (1, 5, 28672),
+    (9, 45, 768), (16, 100, 2048), (12, 20, 4096), (2, 40, 512), (4, 9, 7168),
 ])
 @pytest.mark.parametrize("path", ["gemv", "gemm"])
 @pytest.mark.parametrize("dt", ["f16", "bf16"])
