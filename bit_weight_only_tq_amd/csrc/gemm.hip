@@ -7,22 +7,14 @@
 // asynchronous weight staging through shared memory).  Tiles here are sized
 // for gfx950 (64-wide waves, 160 KB LDS), not for the page's 32x32 blocks.
 //
-// Block tile BM x BN = 128 x 256 outputs, K step BK = 64, four waves in a
-// 2 x 2 arrangement, each wave owning 64 x 128 outputs = 4 x 8 tiles of
-// v_mfma_f32_16x16x32_{f16,bf16}.
-//
-// Unpacking codes into matrix-core operands costs one VALU op per code: a
-// pair of 2-bit fields is masked straight into the low mantissa bits of the
-// constant MAGIC (1024.0 in fp16, 128.0 in bf16, whose unit in the last
-// place is 1), giving the exact values MAGIC + c for c in {0, 1, 2}.  Since
-// t = c - 1,  sum_k a_k t_k = sum_k a_k (MAGIC + c_k) - (MAGIC + 1) sum_k a_k,
-// and the row sums of A are accumulated alongside (dot2 on the A fragments
-// the wave already holds), so the correction is one FMA per output.
-//
-// A field pair extracted from bits 2i and 16+2i of a code dword covers
-// columns i and i+8 of that dword's 16 columns, so K positions inside each
-// 16-column group are stored in the order (0, 8, 1, 9, ..., 7, 15) for both
-// operands in LDS; the contraction is invariant under that common reordering.
+// Unpacking codes into matrix-core operands costs about one VALU op per
+// code: a pair of 2-bit fields is masked straight into the low mantissa bits
+// of the constant MAGIC (1024.0 in fp16, 128.0 in bf16, whose unit in the
+// last place is 1), giving the exact values MAGIC + c for c in {0, 1, 2}.
+// Since t = c - 1,
+//   sum_k a_k t_k = sum_k a_k (MAGIC + c_k) - (MAGIC + 1) sum_k a_k,
+// and the row sums of A are accumulated alongside with dot2, so the
+// correction is one FMA per output.
 
 #include "tq_device.h"
 #include "tq_internal.h"
@@ -67,82 +59,111 @@ template <> struct Mfma<BF16> {
     static constexpr uint32_t kOnePair = 0x3F803F80u;
 };
 
-// Interleave two groups of 8 activation columns (lo = columns 0..7,
-// hi = columns 8..15 of a 16-column group) into the LDS order
-// (0, 8, 1, 9, ..., 7, 15): out dword i = (lo[i], hi[i]).
-__device__ __forceinline__ void interleave16(const uint4& lo, const uint4& hi, uint32_t out[8]) {
-    const uint32_t l[4] = {lo.x, lo.y, lo.z, lo.w};
-    const uint32_t h[4] = {hi.x, hi.y, hi.z, hi.w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        // v_perm_b32(s0, s1, sel): bytes 0-3 of s1 are selectors 0-3, of s0 are 4-7
-        out[2 * j] = __builtin_amdgcn_perm(h[j], l[j], 0x05040100u);      // (lo.low16, hi.low16)
-        out[2 * j + 1] = __builtin_amdgcn_perm(h[j], l[j], 0x07060302u);  // (lo.high16, hi.high16)
-    }
+// ------------------------------------------------------------------------
+// v3 (K % 64 == 0): all global traffic is DMA (global_load_lds_dwordx4, no
+// registers) into a 3-stage LDS ring issued two K-steps ahead:
+//  - activations: 256 rows x 64 columns per stage, natural column order,
+//    16-byte chunks XOR-swizzled (chunk c of row r at position c ^ (r % 8));
+//  - codes: 256 weight rows x 16 bytes (64 columns) per stage.
+// Codes are unpacked in registers into natural-order fp16 / bf16 pairs
+// (f_2j, f_2j+1):  E = x & 0x33333333 (even fields), O = (x >> 2) & 0x33333333
+// (odd fields), Y = byte-merge(E, O) per half dword, pair j = ((Y >> 4j) &
+// 0x00030003) | MAGIC.  Block tile 256 x 256, K-step 64, eight waves (2 x 4)
+// of 128 x 64 outputs; MFMA s of a K-step (s = 0, 1) takes 8-column chunk
+// 2g + s for lane group g.  Row sums of A for the bias correction are split
+// over the four waves sharing a row block (m-tiles wn and wn + 4).  The
+// epilogue stages each wave's outputs through LDS so that every lane stores
+// 16 contiguous bytes.
+namespace v3 {
+
+constexpr int BM = 256;
+constexpr int BN = 256;
+constexpr int BK = 64;
+constexpr int kThreads = 512;
+constexpr int WM = 128, WN = 64;
+constexpr int TM = WM / 16, TN = WN / 16;
+constexpr int kStages = 3;
+constexpr int kABytes = BM * BK * 2;                // 32 KB, unpadded (swizzled)
+constexpr int kBBytes = BN * BK / 4;                // 4 KB of codes
+constexpr int kStageBytes = kABytes + kBBytes;
+constexpr int kEpiLd = WN + 8;                      // epilogue staging row (halves)
+constexpr int kEpiRows = 32;
+constexpr int kEpiBytesPerWave = kEpiRows * kEpiLd * 2;
+constexpr size_t kLdsBytes = (size_t)kStages * kStageBytes;
+static_assert(8 * kEpiBytesPerWave + BM * 4 <= (int)kLdsBytes, "epilogue staging must fit in the ring");
+
+// 16 bytes per lane, global -> LDS at M0 + 16 * lane (M0 must be wave-uniform).
+// Issued through asm so that the compiler does not model the LDS write: its
+// conservative tracking would otherwise wait for every DMA in flight before
+// any LDS read, defeating the prefetch.  The kernel orders the DMA itself:
+// explicit vmcnt waits before the barrier that publishes a stage, and the
+// "memory" clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_addr) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :: "v"(gptr), "s"(lds_addr) : "memory", "m0");
+}
+
+// Bare workgroup barrier: __syncthreads() would add a release fence that
+// waits for every outstanding DMA, including the stage issued ahead.
+__device__ __forceinline__ void stage_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 }
 
 template <class T>
-__global__ __launch_bounds__(kThreads) void ternary_gemm_kernel(GemmArgs p) {
+__global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
     typedef typename Mfma<T>::vec vec;
-    __shared__ __attribute__((aligned(16))) uint16_t As[BM * LDSK];
-    __shared__ __attribute__((aligned(16))) uint16_t Bs[BN * LDSK];
+    extern __shared__ uint4 smem_v3[];
+    uint8_t* lds = reinterpret_cast<uint8_t*>(smem_v3);
+    const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)smem_v3;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: lives in an SGPR
+    const int wm = wave >> 2, wn = wave & 3;
+    const int g = lane >> 4;
+    const int i16 = lane & 15;
     const int64_t m0 = (int64_t)blockIdx.y * BM;
     const int64_t n0 = (int64_t)blockIdx.x * BN;
     const int64_t M = p.M, N = p.N, K = p.K;
-    const int64_t rb = K / 4;  // code bytes per weight row
-    const uint8_t* codes = static_cast<const uint8_t*>(p.wq);
-
-    // global -> register staging: A = two (row, 16-column group) pieces of
-    // 32 bytes per thread; B = one 16-byte chunk (64 codes) of row n0 + tid.
-    const int a_grp = tid & 3;         // 16-column group within BK
-    const int a_row0 = tid >> 2;       // rows a_row0 and a_row0 + 64
-    uint4 a_reg[2][2];
-    uint4 b_reg;
-    const int64_t b_row = n0 + tid;
-
-    auto load_global = [&](int64_t k0) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int64_t r = m0 + a_row0 + 64 * j;
-            if (r < M) {
-                const uint4* src = reinterpret_cast<const uint4*>(p.A + r * K + k0 + 16 * a_grp);
-                a_reg[j][0] = src[0];
-                a_reg[j][1] = src[1];
-            } else {
-                a_reg[j][0] = make_uint4(0, 0, 0, 0);
-                a_reg[j][1] = make_uint4(0, 0, 0, 0);
-            }
-        }
-        b_reg = (b_row < N) ? *reinterpret_cast<const uint4*>(codes + b_row * rb + k0 / 4)
-                            : make_uint4(0x55555555u, 0x55555555u, 0x55555555u, 0x55555555u);
-    };
-
+    const int64_t rb = K / 4;
     const uint32_t magic_v = vgpr_const<Mfma<T>::kMagicPair>();
     const uint32_t mask3 = sgpr_const<0x00030003u>();
-    auto store_lds = [&]() {
+    const uint32_t mask33 = sgpr_const<0x33333333u>();
+
+    // Activation DMA: wave w fills 1-KB blocks 4w .. 4w+3 of a stage (8 rows
+    // each); lane l lands at chunk l % 8 of row l / 8, so it fetches global
+    // chunk (l % 8) ^ (l / 8) of that row.  Rows past M re-read row M-1.
+    const uint16_t* a_blk = p.A + m0 * K;
+    uint32_t a_off[4];
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            uint32_t o[8];
-            interleave16(a_reg[j][0], a_reg[j][1], o);
-            uint4* dst = reinterpret_cast<uint4*>(As + (a_row0 + 64 * j) * LDSK + 16 * a_grp);
-            dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
-            dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
-        }
-        const uint32_t bw[4] = {b_reg.x, b_reg.y, b_reg.z, b_reg.w};
+    for (int u = 0; u < 4; ++u) {
+        int64_t r = 8 * (4 * wave + u) + (lane >> 3);
+        if (m0 + r >= M) r = M - 1 - m0;
+        a_off[u] = (uint32_t)(r * K + 8 * ((lane & 7) ^ (lane >> 3)));
+    }
+    // Code DMA (waves 0..3): lane l of wave w fetches the 16 bytes of weight
+    // row n0 + 64w + l for the K-step.  Rows past N re-read row N-1.
+    const uint8_t* b_blk = static_cast<const uint8_t*>(p.wq) + n0 * rb;
+    uint32_t b_off;
+    {
+        int64_t n = 64 * (wave & 3) + lane;
+        if (n0 + n >= N) n = N - 1 - n0;
+        b_off = (uint32_t)(n * rb);
+    }
+    const bool b_issuer = wave < 4;
+    auto issue = [&](int kstep, int stage) {
+        const int64_t k0 = (int64_t)kstep * BK;
+        const uint32_t dst = lds_base + (uint32_t)(stage * kStageBytes + 4096 * wave);
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {  // code dword d = columns 16d .. 16d+15
-            uint32_t o[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) o[i] = ((bw[d] >> (2 * i)) & mask3) | magic_v;
-            uint4* dst = reinterpret_cast<uint4*>(Bs + tid * LDSK + 16 * d);
-            dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
-            dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
-        }
+        for (int u = 0; u < 4; ++u) dma16(a_blk + k0 + a_off[u], dst + 1024u * u);
+        if (b_issuer) dma16(b_blk + k0 / 4 + b_off, lds_base + (uint32_t)(stage * kStageBytes + kABytes + 1024 * wave));
+    };
+    // the stage issued before the last one has landed (per-wave DMA counts)
+    auto wait_prev_stage = [&]() {
+        if (b_issuer) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
     };
 
     f32x4 acc[TM][TN];
@@ -150,80 +171,149 @@ __global__ __launch_bounds__(kThreads) void ternary_gemm_kernel(GemmArgs p) {
     for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float rsum[TM] = {0.f, 0.f, 0.f, 0.f};  // partial row sums of A (row lane%16 of tile i)
+    float rsum[2] = {0.f, 0.f};  // row sums for m-tiles wn and wn + 4
 
-    const int frag_row = lane & 15;
-    const int frag_k = 8 * (lane >> 4);
+    // fragment row R = wm*128 + 16i + i16 (R % 8 == i16 % 8): chunk c at
+    // byte R*128 + 16*(c ^ (i16 & 7)) of a stage
+    const int frag_base = (wm * WM + i16) * (BK * 2);
+    const int swz = i16 & 7;
+    // code dword of tile j: row wn*64 + 16j + i16, bytes 4g .. 4g+3
+    const int b_frag = kABytes + (wn * WN + i16) * 16 + 4 * g;
 
-    load_global(0);
-    for (int64_t k0 = 0; k0 < K; k0 += BK) {
-        __syncthreads();
-        store_lds();
-        __syncthreads();
-        if (k0 + BK < K) load_global(k0 + BK);
+    const int nk = (int)(K / BK);
+    issue(0, 0);
+    issue(nk > 1 ? 1 : 0, 1);
+    wait_prev_stage();
+    stage_barrier();
+    for (int kt = 0; kt < nk; ++kt) {
+        const int stage = kt % kStages;
+        // Unconditional so the per-wave counts stay exact: past the end the DMA
+        // re-reads the last K-step into the stage nobody reads any more.
+        issue(kt + 2 < nk ? kt + 2 : nk - 1, (kt + 2) % kStages);
+        const uint8_t* sbase = lds + stage * kStageBytes;
+        uint32_t E[TN], O[TN];
 #pragma unroll
-        for (int ks = 0; ks < BK; ks += 32) {
+        for (int j = 0; j < TN; ++j) {
+            const uint32_t x = *reinterpret_cast<const uint32_t*>(sbase + b_frag + 16 * 16 * j);
+            E[j] = x & mask33;
+            O[j] = (x >> 2) & mask33;
+        }
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const int chunk = (2 * g + s) ^ swz;
             vec af[TM];
 #pragma unroll
-            for (int i = 0; i < TM; ++i) {
-                const uint4 v = *reinterpret_cast<const uint4*>(As + (wm * WM + 16 * i + frag_row) * LDSK + ks + frag_k);
-                af[i] = __builtin_bit_cast(vec, v);
-                float r = rsum[i];
+            for (int i = 0; i < TM; ++i)
+                af[i] = __builtin_bit_cast(vec, *reinterpret_cast<const uint4*>(sbase + frag_base + i * 16 * (BK * 2) + 16 * chunk));
+            uint4 bop[TN];
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const uint32_t y = __builtin_amdgcn_perm(O[j], E[j], s ? 0x07060302u : 0x05040100u);
+                bop[j] = make_uint4((y & mask3) | magic_v, ((y >> 4) & mask3) | magic_v,
+                                    ((y >> 8) & mask3) | magic_v, ((y >> 12) & mask3) | magic_v);
+            }
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {  // this wave's share of the row sums: m-tiles wn, wn + 4
+                const uint4 v = *reinterpret_cast<const uint4*>(sbase + frag_base + (wn + 4 * t) * 16 * (BK * 2) + 16 * chunk);
+                float r = rsum[t];
                 r = Mfma<T>::dot2(v.x, Mfma<T>::kOnePair, r);
                 r = Mfma<T>::dot2(v.y, Mfma<T>::kOnePair, r);
                 r = Mfma<T>::dot2(v.z, Mfma<T>::kOnePair, r);
                 r = Mfma<T>::dot2(v.w, Mfma<T>::kOnePair, r);
-                rsum[i] = r;
+                rsum[t] = r;
             }
 #pragma unroll
             for (int j = 0; j < TN; ++j) {
-                const uint4 v = *reinterpret_cast<const uint4*>(Bs + (wn * WN + 16 * j + frag_row) * LDSK + ks + frag_k);
-                const vec bf = __builtin_bit_cast(vec, v);
+                const vec bf = __builtin_bit_cast(vec, bop[j]);
 #pragma unroll
                 for (int i = 0; i < TM; ++i) acc[i][j] = Mfma<T>::mma(af[i], bf, acc[i][j]);
             }
         }
+        wait_prev_stage();  // stage kt + 1 (issued last iteration) has landed
+        stage_barrier();    // ... for every wave, and nobody reads stage kt any more
     }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();        // the ring is idle from here on
 
-    // full row sums: lanes l, l^16, l^32, l^48 hold the four K subsets of row l%16
+    // row sums -> LDS
+    float* rs_lds = reinterpret_cast<float*>(lds + 8 * kEpiBytesPerWave);
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-        rsum[i] += __shfl_xor(rsum[i], 16, kWave);
-        rsum[i] += __shfl_xor(rsum[i], 32, kWave);
+    for (int t = 0; t < 2; ++t) {
+        float r = rsum[t];
+        r += __shfl_xor(r, 16, kWave);
+        r += __shfl_xor(r, 32, kWave);
+        if (g == 0) rs_lds[wm * WM + 16 * (wn + 4 * t) + i16] = r;
     }
-    // epilogue: lane holds rows 4*(lane/16) + r (r = 0..3), column lane%16 of each tile
-    const int out_col = lane & 15;
-    const int out_row = 4 * (lane >> 4);
+    __syncthreads();
+
+    // epilogue: per wave, 4 slabs of 32 rows x 64 columns through a private LDS area
+    uint16_t* stg = reinterpret_cast<uint16_t*>(lds + wave * kEpiBytesPerWave);
+    float sc[TN], bi[TN];
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-        float rs[4];
+    for (int j = 0; j < TN; ++j) {
+        const int64_t n = n0 + wn * WN + 16 * j + i16;
+        const int64_t nc = n < N ? n : N - 1;
+        sc[j] = f16_bits_to_f32(p.scale[nc]);
+        bi[j] = p.bias ? T::to_f32(p.bias[nc]) : 0.0f;
+    }
+    const bool vec_ok = (N % 8) == 0;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) rs[r] = __shfl(rsum[i], out_row + r, kWave);
+    for (int slab = 0; slab < TM / 2; ++slab) {
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const int64_t n = n0 + wn * WN + 16 * j + out_col;
-            if (n >= N) continue;
-            const float s = f16_bits_to_f32(p.scale[n]);
-            const float b = p.bias ? T::to_f32(p.bias[n]) : 0.0f;
+        for (int ii = 0; ii < 2; ++ii) {
+            const int i = 2 * slab + ii;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int64_t m = m0 + wm * WM + 16 * i + out_row + r;
-                if (m < M) {
-                    const float v = acc[i][j][r] - Mfma<T>::kBias * rs[r];
-                    p.C[m * N + n] = T::from_f32(v * s + b);
-                }
+                const int row = 16 * ii + 4 * g + r;
+                const float rs = rs_lds[wm * WM + 16 * i + 4 * g + r];
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+                    stg[row * kEpiLd + 16 * j + i16] = T::from_f32_fast((acc[i][j][r] - Mfma<T>::kBias * rs) * sc[j] + bi[j]);
+            }
+        }
+        // each lane stores 16 contiguous bytes: row lane/8 + 8q, columns 8*(lane%8) .. +7
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int row = (lane >> 3) + 8 * q;
+            const int col = 8 * (lane & 7);
+            const int64_t m = m0 + wm * WM + 32 * slab + row;
+            const int64_t n = n0 + wn * WN + col;
+            if (m >= M) continue;
+            const uint4 v = *reinterpret_cast<const uint4*>(stg + row * kEpiLd + col);
+            if (vec_ok && n + 8 <= N) {
+                *reinterpret_cast<uint4*>(p.C + m * N + n) = v;
+            } else {
+                const uint16_t h[8] = {(uint16_t)v.x, (uint16_t)(v.x >> 16), (uint16_t)v.y, (uint16_t)(v.y >> 16),
+                                       (uint16_t)v.z, (uint16_t)(v.z >> 16), (uint16_t)v.w, (uint16_t)(v.w >> 16)};
+                for (int e = 0; e < 8; ++e)
+                    if (n + e < N) p.C[m * N + n + e] = h[e];
             }
         }
     }
 }
 
+}  // namespace v3
+
+
 }  // namespace
 
-hipError_t launch_ternary_gemm(const GemmArgs& a, hipStream_t s) {
-    const dim3 grid((unsigned)((a.N + BN - 1) / BN), (unsigned)((a.M + BM - 1) / BM));
-    if (a.bf16) ternary_gemm_kernel<BF16><<<grid, kThreads, 0, s>>>(a);
-    else ternary_gemm_kernel<F16><<<grid, kThreads, 0, s>>>(a);
+template <class T>
+static hipError_t launch_v3(const GemmArgs& a, hipStream_t s) {
+    static bool attr_set = false;  // per-function LDS limit; setting it is idempotent
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&v3::gemm_kernel<T>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)v3::kLdsBytes);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    const dim3 grid((unsigned)((a.N + v3::BN - 1) / v3::BN), (unsigned)((a.M + v3::BM - 1) / v3::BM));
+    v3::gemm_kernel<T><<<grid, v3::kThreads, v3::kLdsBytes, s>>>(a);
     return hipGetLastError();
+}
+
+hipError_t launch_ternary_gemm(const GemmArgs& a, hipStream_t s) {
+    // the C ABI guarantees K % 64 == 0 (whole 16-byte code chunks per row)
+    return a.bf16 ? launch_v3<BF16>(a, s) : launch_v3<F16>(a, s);
 }
 
 // W4A16 at large M: run the small-M kernel on successive blocks of 16

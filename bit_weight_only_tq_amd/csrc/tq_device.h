@@ -103,13 +103,19 @@ __device__ __forceinline__ uint32_t vgpr_const() {
 }
 
 // Activation element type tags.
+// from_f32 rounds in software (mode-independent); from_f32_fast uses the
+// hardware conversion, which rounds to nearest even under the default mode
+// register and keeps fp16 subnormals - used where a result only has to meet
+// a tolerance.
 struct F16 {
     static __device__ __forceinline__ float to_f32(uint16_t h) { return f16_bits_to_f32(h); }
     static __device__ __forceinline__ uint16_t from_f32(float x) { return f32_to_f16_rne(x); }
+    static __device__ __forceinline__ uint16_t from_f32_fast(float x) { return __builtin_bit_cast(uint16_t, (_Float16)x); }
 };
 struct BF16 {
     static __device__ __forceinline__ float to_f32(uint16_t h) { return bf16_bits_to_f32(h); }
     static __device__ __forceinline__ uint16_t from_f32(float x) { return f32_to_bf16_rne(x); }
+    static __device__ __forceinline__ uint16_t from_f32_fast(float x) { return f32_to_bf16_rne(x); }
 };
 
 // Sum over the 64 lanes of a wave; every lane receives the total.  The first
