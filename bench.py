@@ -1,20 +1,30 @@
 """Benchmark of the ternary weight-only linear layer on one MI355X.
 
-Default workload (the headline metric): a Llama-3-8B decode pass at M = 1 -
-32 layers x 7 ternary projections (q, k, v, o, gate, up, down), 1.66 GB of
-packed codes resident in HBM, distinct seeded weights per layer, so every
-step streams all weights from HBM (the set is 6.5x the 256 MB MALL).  One
-step = one such pass (224 GEMV launches).  ``value`` is packed-weight bytes
-per second over the timed steps.
+Headline workload (``value``): Llama-3-8B decode at M = 1.  One step is one
+pass over the linear layers of all 32 decoder layers, laid out as a serving
+stack lays them out - q, k, v stacked along N into one call (6144 x 4096),
+o (4096 x 4096), gate and up stacked into one call (28672 x 4096), down
+(4096 x 14336) - 128 ternary GEMV launches, replayed from a HIP graph.  The
+1.74 GB of packed codes (distinct seeded weights per layer) are resident in
+HBM, 6.8x the 256 MB last-level cache, so every step streams them from HBM.
+``value`` = packed-weight bytes per second over the timed steps.
 
-Secondary (reported in the same line): the prefill GEMM at M = 4096 on the
-Llama-3-8B MLP shapes (14336 x 4096 and 4096 x 14336) in fp16 and bf16,
-TFLOP/s = 2MNK / time.
+Also reported in the same JSON line:
+  * ``roofline``: algorithmic bytes (codes + scales + activations + outputs)
+    per GEMV launch over the average launch time, both measured with HIP
+    events around the timed region on the launch stream; HBM peak 8 TB/s.
+    ``traffic`` is filled from rocprofv3 FETCH_SIZE / WRITE_SIZE runs (see
+    profiles/) when given with --traffic-json.
+  * ``decode_unfused``: the same pass with q, k, v, gate, up as separate
+    calls (224 launches).
+  * ``secondary``: the prefill GEMM at M = 4096 on the MLP shapes
+    (14336 x 4096, 4096 x 14336), fp16 and bf16, TFLOP/s = 2MNK / time.
+  * ``cpu_baseline``: the CPU oracle (fp64 dequant + fp64 product), untuned,
+    timed on the host on a bounded sample of the same workload.
 
-The ``cpu_baseline`` leg times the oracle (fp64 dequant + fp64 matmul) on
-the host on a bounded sample of the same workload.
-
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--graph]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--mode MODE]
+  --mode full (default) | decode | prefill | calib (plain copy of known size,
+  for scaling hardware byte counters)
 """
 
 import argparse
@@ -28,6 +38,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 MFMA_PEAK_TFLOPS = 2500.0    # MI355X dense fp16 / bf16 matrix peak, published
+METRIC = "HBM GB/s (% peak) ternary GEMV at M=1; fp16-MFMA TFLOP/s at M=4096"
 
 
 def log(msg):
@@ -40,11 +51,12 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--layers", type=int, default=32)
-    ap.add_argument("--graph", action="store_true", help="replay each step from a captured HIP graph")
-    ap.add_argument("--fused", action="store_true", help="q,k,v and gate,up as one call each (N stacked)")
-    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--mode", default="full", choices=["full", "decode", "prefill", "calib"])
+    ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
+    ap.add_argument("--unfused", action="store_true", help="decode mode: q,k,v,gate,up as separate calls")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", default="", help="profiling helper: 'decode' or 'prefill'")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="lower bound on the CPU sample's run time")
+    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "ternary_gemv_traffic.json"))
     return ap.parse_args()
 
 
@@ -54,17 +66,16 @@ def ternary_bytes(M, N, K):
 
 
 def layer_shapes(fused):
-    """Projections of one Llama-3-8B layer; fused = q,k,v and gate,up stacked along N
-    (one call each, as a serving stack lays them out)."""
+    """Projections of one Llama-3-8B layer (name, (N, K)); fused stacks q,k,v and gate,up along N."""
     import synth
-    if not fused:
-        return list(synth.LLAMA3_8B.items())
     s = synth.LLAMA3_8B
+    if not fused:
+        return list(s.items())
     return [("qkv", (s["q"][0] + s["k"][0] + s["v"][0], 4096)), ("o", s["o"]),
-            ("gate_up", (2 * s["gate"][0], 4096)), ("down", s["down"])]
+            ("gate_up", (s["gate"][0] + s["up"][0], 4096)), ("down", s["down"])]
 
 
-def build_decode(layers, dev, fused=False):
+def build_decode(layers, dev, fused):
     import torch
     import bit_weight_only_tq_amd as tq
     import synth
@@ -81,16 +92,8 @@ def build_decode(layers, dev, fused=False):
     return mats
 
 
-def decode_step_fn(mats, xs, outs):
-    import bit_weight_only_tq_amd as tq
-
-    def step():
-        for i, (name, N, K, codes, scale) in enumerate(mats):
-            tq.tq_gemm(xs[K], codes, scale, out=outs[i])
-    return step
-
-
 def time_region(fn, steps, stream):
+    """Seconds for `steps` calls of fn, from HIP events on `stream`."""
     import torch
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
@@ -100,39 +103,59 @@ def time_region(fn, steps, stream):
         fn()
     end.record(stream)
     end.synchronize()
-    return start.elapsed_time(end) / 1e3  # seconds
+    return start.elapsed_time(end) / 1e3
 
 
-def per_launch_durations(mats, xs, outs, stream, reps=3):
-    """Average device time of each GEMV launch, from HIP events recorded on
-    the launch stream around every launch of `reps` full steps."""
+def run_decode(args, dev, fused, graph):
     import torch
     import bit_weight_only_tq_amd as tq
-    tot_t, tot_b, n = 0.0, 0, 0
-    pairs = []
-    for _ in range(reps):
+    import synth
+    stream = torch.cuda.current_stream()
+    mats = build_decode(args.layers, dev, fused)
+    xs = {K: synth.activations_device(1, K, synth.seed_for("benchx", K), "f16", dev) for K in {m[2] for m in mats}}
+    outs = [torch.empty((1, m[1]), dtype=torch.float16, device=dev) for m in mats]
+
+    def step():
         for i, (name, N, K, codes, scale) in enumerate(mats):
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
             tq.tq_gemm(xs[K], codes, scale, out=outs[i])
-            e1.record(stream)
-            pairs.append((e0, e1, ternary_bytes(1, N, K)))
+
+    run = step
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            step()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            step()
+        run = g.replay
+    for _ in range(args.warmup):
+        run()
     torch.cuda.synchronize()
-    for e0, e1, b in pairs:
-        tot_t += e0.elapsed_time(e1) / 1e3
-        tot_b += b
-        n += 1
-    return tot_t / n, tot_b / n, n
+    t = time_region(run, args.steps, stream)
+    packed = sum(m[3].numel() for m in mats)
+    alg = sum(ternary_bytes(1, m[1], m[2]) for m in mats)
+    res = {
+        "launches": len(mats), "seconds": t, "packed_bytes": packed, "alg_bytes": alg,
+        "ms_per_step": t / args.steps * 1e3, "packed_gbs": packed * args.steps / t / 1e9,
+        "alg_gbs": alg * args.steps / t / 1e9,
+        "avg_launch_us": t / args.steps / len(mats) * 1e6, "alg_bytes_per_launch": alg / len(mats),
+    }
+    del mats, xs, outs
+    torch.cuda.empty_cache()
+    return res
 
 
-def bench_prefill(dev, iters=5):
+def run_prefill(dev, iters=10):
     import torch
     import bit_weight_only_tq_amd as tq
     import synth
     res = {}
     M = 4096
-    flops_tot, t_tot = 0.0, 0.0
+    flops_f16, t_f16 = 0.0, 0.0
+    stream = torch.cuda.current_stream()
     for (N, K) in [(14336, 4096), (4096, 14336)]:
         W = synth.weights_device(N, K, synth.seed_for("benchpf", N, K), dev)
         codes, scale = tq.tq_pack(W)
@@ -140,139 +163,148 @@ def bench_prefill(dev, iters=5):
         for dt in ("f16", "bf16"):
             A = synth.activations_device(M, K, synth.seed_for("benchpfa", N, K, dt), dt, dev)
             C = torch.empty((M, N), dtype=A.dtype, device=dev)
-            for _ in range(2):
+            for _ in range(3):
                 tq.tq_gemm(A, codes, scale, out=C)
-            s = torch.cuda.current_stream()
-            t = time_region(lambda: tq.tq_gemm(A, codes, scale, out=C), iters, s) / iters
-            tf = 2.0 * M * N * K / t / 1e12
-            res[f"{N}x{K}_{dt}"] = {"ms": round(t * 1e3, 4), "tflops": round(tf, 1)}
+            t = time_region(lambda: tq.tq_gemm(A, codes, scale, out=C), iters, stream) / iters
+            res[f"{N}x{K}_{dt}"] = {"ms": round(t * 1e3, 4), "tflops": round(2.0 * M * N * K / t / 1e12, 1)}
             if dt == "f16":
-                flops_tot += 2.0 * M * N * K
-                t_tot += t
+                flops_f16 += 2.0 * M * N * K
+                t_f16 += t
             del A, C
-    res["fp16_tflops_M4096"] = round(flops_tot / t_tot / 1e12, 1)
-    res["frac_of_peak"] = round(flops_tot / t_tot / 1e12 / MFMA_PEAK_TFLOPS, 4)
-    return res
+    tf = flops_f16 / t_f16 / 1e12
+    return {"metric": "fp16-MFMA TFLOP/s at M=4096 (ternary prefill GEMM, Llama-3-8B MLP shapes)",
+            "value": round(tf, 1), "unit": "TFLOP/s", "peak": MFMA_PEAK_TFLOPS,
+            "frac_of_peak": round(tf / MFMA_PEAK_TFLOPS, 4), "kernel": "v3::gemm_kernel", **res}
 
 
-def cpu_baseline():
-    """The oracle, untuned, on one Llama-3-8B layer (7 projections) at M = 1:
-    fp64 unpack + dequant of the packed codes, then the fp64 product."""
+def run_calib(dev, nbytes=1 << 30, iters=5):
+    """A plain device copy of known size, for scaling FETCH_SIZE / WRITE_SIZE."""
+    import torch
+    src = torch.empty(nbytes // 2, dtype=torch.float16, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    stream = torch.cuda.current_stream()
+    dst.copy_(src)
+    t = time_region(lambda: dst.copy_(src), iters, stream) / iters
+    return {"calib_copy_bytes": nbytes, "copy_ms": round(t * 1e3, 4), "copy_read_gbs": round(nbytes / t / 1e9, 1)}
+
+
+def cpu_baseline(min_seconds):
+    """The oracle, untuned, on Llama-3-8B layers at M = 1: fp64 unpack and
+    dequant of the packed codes, then the fp64 product (numpy BLAS)."""
     import numpy as np
     import oracle.gemm as OG
     import oracle.ternary as OT
     import synth
-    rng_seed = 7
-    total_bytes, total_t = 0, 0.0
-    for name, (N, K) in synth.LLAMA3_8B.items():
+    layer = []
+    for name, (N, K) in layer_shapes(False):
         W = synth.weights(N, K, synth.seed_for("cpu", name))
         codes, sb = OT.ternary_pack(W)
-        a = synth.activations(1, K, rng_seed).double().numpy()
-        t0 = time.perf_counter()
-        wdq = OT.ternary_dequant(codes, sb, K)
-        out, mag = OG.gemm_ref64(a, wdq)
-        total_t += time.perf_counter() - t0
-        total_bytes += codes.nbytes
-        del W, wdq
-    threads = None
+        layer.append((K, codes, sb, synth.activations(1, K, synth.seed_for("cpux", K)).double().numpy()))
+        del W
+    total_bytes, total_t, reps = 0, 0.0, 0
+    while total_t < min_seconds:
+        for K, codes, sb, a in layer:
+            t0 = time.perf_counter()
+            wdq = OT.ternary_dequant(codes, sb, K)
+            OG.gemm_ref64(a, wdq)
+            total_t += time.perf_counter() - t0
+            total_bytes += codes.nbytes
+            del wdq
+        reps += 1
+    threads = 1
     try:
         import threadpoolctl
-        info = threadpoolctl.threadpool_info()
-        threads = max((i.get("num_threads", 1) for i in info), default=1)
+        threads = max((i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()), default=1)
     except Exception:
         pass
     return {
-        "value": round(total_bytes / total_t / 1e9, 3),
-        "unit": "GB/s",
-        "cores": threads or 1,
-        "kind": "oracle",
-        "sample": "one Llama-3-8B layer (q,k,v,o,gate,up,down; 52 MiB packed) at M=1, "
-                  f"fp64 dequant + fp64 matmul, {total_t:.1f} s; host has {os.cpu_count()} CPUs",
+        "value": round(total_bytes / total_t / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+        "sample": f"{reps} passes over one Llama-3-8B layer's 7 projections (52 MiB packed) at M=1: "
+                  f"fp64 dequant + fp64 matmul, {total_t:.1f} s of CPU work; host reports {os.cpu_count()} CPUs",
     }
+
+
+def load_traffic(path):
+    """HBM bytes per GEMV launch from the committed counter summary, or None
+    when it is missing or was measured on a different kernel source."""
+    import hashlib
+    try:
+        with open(path) as f:
+            tj = json.load(f)
+        with open(os.path.join(ROOT, tj["kernel_source"]), "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest() != tj["kernel_sha256"]:
+                return None
+        return tj["hbm_bytes_per_launch"]
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1"}))
+        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1"}), flush=True)
         sys.exit(2)
     import torch
     import bit_weight_only_tq_amd as tq
     tq.load()
     if not torch.cuda.is_available():
-        print(json.dumps({"error": "no GPU visible"}))
+        print(json.dumps({"error": "no GPU visible"}), flush=True)
         sys.exit(1)
     dev = torch.device("cuda", 0)
-    stream = torch.cuda.current_stream()
 
-    out = {}
-    if args.only in ("", "decode"):
-        import synth
-        mats = build_decode(args.layers, dev, args.fused)
-        xs = {K: synth.activations_device(1, K, synth.seed_for("benchx", K), "f16", dev)
-              for K in {m[2] for m in mats}}
-        outs = [torch.empty((1, m[1]), dtype=torch.float16, device=dev) for m in mats]
-        step = decode_step_fn(mats, xs, outs)
-        packed = sum(m[3].numel() for m in mats)
-        alg = sum(ternary_bytes(1, m[1], m[2]) for m in mats)
-        if args.graph:
-            g = torch.cuda.CUDAGraph()
-            s2 = torch.cuda.Stream()
-            s2.wait_stream(stream)
-            with torch.cuda.stream(s2):
-                step()
-            stream.wait_stream(s2)
-            torch.cuda.synchronize()
-            with torch.cuda.graph(g):
-                step()
-            run = g.replay
-        else:
-            run = step
-        for _ in range(args.warmup):
-            run()
-        torch.cuda.synchronize()
-        log(f"timing {args.steps} steps")
-        t = time_region(run, args.steps, stream)
-        ms = t / args.steps * 1e3
-        value = packed * args.steps / t / 1e9
-        avg_dur, avg_bytes, nl = per_launch_durations(mats, xs, outs, stream)
-        achieved = avg_bytes / avg_dur / 1e9
-        out.update({
-            "metric": "HBM GB/s (% peak) ternary GEMV at M=1; fp16-MFMA TFLOP/s at M=4096",
-            "value": round(value, 1),
-            "unit": "GB/s",
-            "n_gpus": 1,
-            "steps": args.steps,
-            "warmup": args.warmup,
-            "ms_per_step": round(ms, 4),
-            "higher_is_better": True,
-            "scaling": "weak",
-            "vs_baseline": None,
-            "dtype": "f16",
-            "data": "synthetic (seeded N(0,0.02) weights ternarized on device, N(0,1) activations)",
-            "config": {
-                "workload": "Llama-3-8B decode, M=1: 32 layers x {q,k,v,o,gate,up,down} ternary GEMV",
-                "layers": args.layers, "M": 1, "launches_per_step": len(mats),
-                "packed_bytes_per_step": packed, "algorithmic_bytes_per_step": alg,
-                "graph": bool(args.graph), "fused_qkv_gate_up": bool(args.fused),
-                "hbm_frac": round(value / HBM_PEAK_GBS, 4),
-            },
-            "roofline": {
-                "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": "ternary_gemv_mfma_kernel", "avg_launch_us": round(avg_dur * 1e6, 3),
-                "avg_alg_bytes_per_launch": round(avg_bytes), "launches_timed": nl,
-            },
-        })
-        del mats, xs, outs
-        torch.cuda.empty_cache()
-    if args.only in ("", "prefill") and not args.no_prefill:
+    if args.mode == "calib":
+        print(json.dumps(run_calib(dev)), flush=True)
+        return
+    if args.mode == "prefill":
+        print(json.dumps({"secondary": run_prefill(dev)}), flush=True)
+        return
+
+    graph = not args.no_graph
+    fused = not args.unfused
+    log(f"decode: {args.layers} layers, fused={fused}, graph={graph}")
+    d = run_decode(args, dev, fused, graph)
+    traffic = load_traffic(args.traffic_json)
+    achieved = d["alg_bytes_per_launch"] / (d["avg_launch_us"] * 1e-6) / 1e9
+    out = {
+        "metric": METRIC,
+        "value": round(d["packed_gbs"], 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(d["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic: seeded N(0,0.02) fp32 weights ternarized on device, N(0,1) fp16 activations",
+        "config": {
+            "workload": "Llama-3-8B decode, M=1: 32 layers x {qkv (6144x4096), o (4096x4096), "
+                        "gate_up (28672x4096), down (4096x14336)} ternary GEMV",
+            "M": 1, "layers": args.layers, "launches_per_step": d["launches"],
+            "packed_bytes_per_step": d["packed_bytes"], "algorithmic_bytes_per_step": d["alg_bytes"],
+            "graph_replay": graph, "fused_qkv_gate_up": fused,
+            "hbm_frac_packed": round(d["packed_gbs"] / HBM_PEAK_GBS, 4),
+        },
+        "roofline": {
+            "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "kernel": "ternary_gemv_lds_kernel", "avg_launch_us": round(d["avg_launch_us"], 3),
+            "alg_bytes_per_launch": round(d["alg_bytes_per_launch"]),
+        },
+    }
+    if args.mode == "full":
+        if fused:
+            log("decode, unfused projections")
+            u = run_decode(args, dev, False, graph)
+            out["decode_unfused"] = {"value": round(u["packed_gbs"], 1), "unit": "GB/s",
+                                     "ms_per_step": round(u["ms_per_step"], 4), "launches_per_step": u["launches"],
+                                     "avg_launch_us": round(u["avg_launch_us"], 3)}
         log("prefill GEMM M=4096")
-        out["secondary"] = {"metric": "fp16-MFMA TFLOP/s at M=4096 (ternary prefill GEMM)",
-                            **bench_prefill(dev)}
-    if not args.no_cpu_baseline and args.only == "":
-        log("cpu baseline (oracle)")
-        out["cpu_baseline"] = cpu_baseline()
+        out["secondary"] = run_prefill(dev)
+        if not args.no_cpu_baseline:
+            log("cpu baseline (oracle)")
+            out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 

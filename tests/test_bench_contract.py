@@ -1,0 +1,35 @@
+"""bench.py contract checks that need no GPU."""
+import json
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    msg = json.loads(r.stdout.strip().splitlines()[-1])
+    assert "one GPU" in msg["error"]
+
+
+def test_traffic_summary_matches_kernel_or_is_dropped(tmp_path):
+    sys.path.insert(0, ROOT)
+    import bench
+    tj = os.path.join(ROOT, "profiles", "ternary_gemv_traffic.json")
+    v = bench.load_traffic(tj)
+    assert v is None or v > 0
+    bad = json.load(open(tj))
+    bad["kernel_sha256"] = "0" * 64
+    p = tmp_path / "t.json"
+    p.write_text(json.dumps(bad))
+    assert bench.load_traffic(str(p)) is None
+
+
+def test_algorithmic_bytes():
+    sys.path.insert(0, ROOT)
+    import bench
+    # codes N*K/4 + fp16 scales + fp16 activations + fp16 outputs
+    assert bench.ternary_bytes(1, 4096, 4096) == 4096 * 1024 + 2 * 4096 + 2 * 4096 + 2 * 4096
