@@ -23,16 +23,6 @@ namespace tq {
 
 namespace {
 
-constexpr int BM = 128;
-constexpr int BN = 256;
-constexpr int BK = 64;
-constexpr int LDSK = BK + 8;     // padded LDS row (halves): 144 bytes, conflict-free 16-byte reads
-constexpr int kThreads = 256;
-constexpr int WM = 64;           // wave tile rows
-constexpr int WN = 128;          // wave tile cols
-constexpr int TM = WM / 16;      // 4 mfma tiles down
-constexpr int TN = WN / 16;      // 8 mfma tiles across
-
 template <class T> struct Mfma;
 template <> struct Mfma<F16> {
     typedef f16x8 vec;
