@@ -289,13 +289,9 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
 
 template <class T>
 static hipError_t launch_v3(const GemmArgs& a, hipStream_t s) {
-    static bool attr_set = false;  // per-function LDS limit; setting it is idempotent
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&v3::gemm_kernel<T>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)v3::kLdsBytes);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    static DeviceFlags lds_limit_set;
+    hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(&v3::gemm_kernel<T>), (int)v3::kLdsBytes, lds_limit_set);
+    if (e != hipSuccess) return e;
     const dim3 grid((unsigned)((a.N + v3::BN - 1) / v3::BN), (unsigned)((a.M + v3::BM - 1) / v3::BM));
     v3::gemm_kernel<T><<<grid, v3::kThreads, v3::kLdsBytes, s>>>(a);
     return hipGetLastError();

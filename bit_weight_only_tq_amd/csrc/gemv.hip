@@ -295,19 +295,27 @@ __global__ __launch_bounds__(W * kWave) void ternary_gemv_mfma_kernel(GemmArgs p
     }
 }
 
-// Same arithmetic, latency-first schedule (fp16, M <= 4, M * K <= 32768).
+// Same arithmetic, latency-first schedule (fp16, M <= 4, M * K <= 28672).
 //
-// 1. The block loads the activations it needs first (few KB, mostly from the
-//    L2), then every wave issues the code loads of ALL its chunk-sets (at most
-//    CSW, fully unrolled), so the kernel waits for HBM once and the in-order
-//    completion counter lets the activation work start before codes arrive.
+// 1. Each thread loads the activations of its prep units first (a few KB per
+//    block, mostly L2 hits); then every wave issues the code loads of ALL its
+//    chunk-sets.  Every load is unconditional (addresses clamped, surplus
+//    results discarded): the compiler then keeps this issue order, and the
+//    in-order completion counter lets each use wait only for the loads it
+//    needs - in particular the prep waits for the activations only.
 // 2. While the codes are in flight the block writes the scaled, paired a'
 //    values to LDS in the order the MFMA operands read them - dword
-//    ((m * K/64 + chunk) * 32 + 8 d + i) = pair (d, i) of row m - and sums the
-//    row-independent term D[m] = sum_k a'_k (1024 + 4^s(k)) with dot2 (one
-//    partial per 16 columns, reduced in a fixed order).
-// 3. Each wave contracts its chunk-sets as their codes land; partials of the
-//    W waves meet in LDS, D[m] is subtracted once, the row scale applied.
+//    ((m * K/64 + chunk) * 32 + 8 d + i) = pair (d, i) of row m - and the
+//    row-independent term D[m] = sum_k a'_k (1024 + 4^s(k)): one dot2 partial
+//    per 16 columns, summed over each 16-lane row (16 consecutive units of
+//    one activation row) and stored once per 256 columns.  A bare barrier
+//    (LDS writes complete; no wait on the code loads, which a __syncthreads()
+//    fence would add) publishes them.
+// 3. The trailing wave sums D[m] over its K/256 partials in a fixed order;
+//    every wave contracts its chunk-sets in issue order as their codes land.
+//    Lanes of activation rows m >= M take zero operands without reading LDS.
+// 4. Wave partials meet in their own LDS area; after one barrier a fixed-order
+//    sum, D[m] subtracted once, the row scale and bias applied.
 // Block = W waves (W = ceil(K/256 / CSW) <= 16) over 16R rows and all of K.
 template <int I>
 __device__ __forceinline__ constexpr uint32_t one_pattern() {  // (1024 + 4^s) in both halves
@@ -315,9 +323,25 @@ __device__ __forceinline__ constexpr uint32_t one_pattern() {  // (1024 + 4^s) i
     return 0x64006400u | (0x00010001u << (2 * s));
 }
 
+// LDS layout of the kernel below (byte offsets): a' [M*K*2], D partials
+// [M*K/256 floats, padded to 16 B], D sums [4 floats], wave partials
+// [W*R*64 lanes*16 B], a 32-byte sink for the stores of surplus prep lanes.
+struct GemvLds {
+    int64_t dpart, dsum, red, sink, total;
+    __host__ __device__ GemvLds(int64_t M, int64_t K, int W, int R) {
+        dpart = M * K * 2;
+        dsum = dpart + ((M * (K / 256) * 4 + 15) / 16) * 16;
+        red = dsum + 16;
+        sink = red + (int64_t)W * R * 64 * 16;
+        total = sink + 32;
+    }
+};
+static inline size_t gemv_lds_bytes(int64_t M, int64_t K, int W, int R) { return (size_t)GemvLds(M, K, W, R).total; }
+
 template <int R, int CSW, int UPT>
 __global__ __launch_bounds__(1024) void ternary_gemv_lds_kernel(GemmArgs p) {
     extern __shared__ uint4 smem[];
+    uint8_t* lds = reinterpret_cast<uint8_t*>(smem);
     uint32_t* aps = reinterpret_cast<uint32_t*>(smem);
     const int W = blockDim.x >> 6;
     const int lane = threadIdx.x & (kWave - 1);
@@ -332,47 +356,64 @@ __global__ __launch_bounds__(1024) void ternary_gemv_lds_kernel(GemmArgs p) {
     const int64_t n_base = (int64_t)blockIdx.x * (16 * R);
     const uint8_t* codes = static_cast<const uint8_t*>(p.wq);
     const int cs0 = wave * CSW;
-    const int cnt = CS - cs0 < CSW ? CS - cs0 : CSW;  // may be <= 0 for a trailing wave
-    const int units = M * nch * 4;                     // (row, chunk, dword) = 16 columns
-    uint32_t* zero_blk = aps + (int64_t)M * nch * 32;  // 32 zero dwords: a' of rows m >= M
-    float* dpart = reinterpret_cast<float*>(zero_blk + 32);  // [units] D partials
-    // Memory operations below are branch-free (addresses clamped into the
-    // tensors, surplus results discarded) so the hardware's in-order load
-    // counters let each use wait only for the loads it needs.
+    const int cnt = CS - cs0 < CSW ? CS - cs0 : CSW;  // >= 1 for every wave of the launch
+    const int units = M * nch * 4;                     // (row, chunk, dword) = 16 columns; units % 16 == 0
+    const GemvLds L(M, K, W, R);
+    float* dpart = reinterpret_cast<float*>(lds + L.dpart);  // [M][CS]
+    float* dsum = reinterpret_cast<float*>(lds + L.dsum);    // [4]
+    f32x4* red = reinterpret_cast<f32x4*>(lds + L.red);      // [W][R][64]
+    uint4* sink = reinterpret_cast<uint4*>(lds + L.sink);
 
-    // 1a. activation loads of this thread's prep units (issued before the codes)
+    // 1a. activation loads of this thread's prep units (issued before the codes);
+    //     unit u covers columns 16 (u % per) .. +15 of activation row u / per
+    const int per = nch * 4;
     uint4 av[UPT][8];
 #pragma unroll
     for (int j = 0; j < UPT; ++j) {
         const int u = (int)threadIdx.x + j * (int)blockDim.x;
         const int uc = u < units ? u : units - 1;
-        const int m = uc / (nch * 4);
-        const int rem = uc - m * nch * 4;
-        const uint4* src = reinterpret_cast<const uint4*>(p.A + (int64_t)m * K + (int64_t)(rem >> 2) * 64 + 16 * (rem & 3));
+        const int m = (uc >= per) + (uc >= 2 * per) + (uc >= 3 * per);  // M <= 4
+        const int rem = uc - m * per;
+        const uint4* src = reinterpret_cast<const uint4*>(p.A + (int64_t)m * K + 16 * rem);
         av[j][0] = src[0];
         av[j][1] = src[1];
     }
-    // 1b. all code loads of this wave (rows past N re-read row N-1, chunk-sets
-    //     past the wave's share re-read its first one; both are ignored)
-    uint4 q[CSW][R];
+    // 1b. all code loads of this wave, in the order step 3 consumes them (rows
+    //     past N re-read row N-1, chunk-sets past the wave's share re-read its
+    //     first one; both are ignored)
+    const uint8_t* crow[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const int64_t n = n_base + 16 * r + i16;
-        const uint8_t* crow = codes + (n < N ? n : N - 1) * rb;
-#pragma unroll
-        for (int s = 0; s < CSW; ++s) {
-            const int cs = (s < cnt) ? cs0 + s : (cs0 < CS ? cs0 : 0);
-            q[s][r] = *reinterpret_cast<const uint4*>(crow + (int64_t)(4 * cs + g) * 16);
-        }
+        crow[r] = codes + (n < N ? n : N - 1) * rb;
     }
-    // 2. a' and D partials to LDS
-    if (threadIdx.x < 8) reinterpret_cast<uint4*>(zero_blk)[threadIdx.x] = make_uint4(0u, 0u, 0u, 0u);
+    uint4 q[CSW][R];
+#pragma unroll
+    for (int s = 0; s < CSW; ++s) {
+        const int cs = (s < cnt) ? cs0 + s : cs0;
+#pragma unroll
+        for (int r = 0; r < R; ++r) q[s][r] = *reinterpret_cast<const uint4*>(crow[r] + (int64_t)(4 * cs + g) * 16);
+    }
+    // 1c. row scale and bias of the output this thread finishes in step 4
+    //     (thread e < 64R: row n_base + 16 (e / 64) + e % 16), loaded now so
+    //     that the epilogue does not wait for memory
+    float sc_e, bi_e;
+    {
+        const int e = (int)threadIdx.x % (R * kWave);
+        const int64_t n = n_base + 16 * (e / kWave) + (e & 15);
+        const int64_t nc = n < N ? n : N - 1;
+        sc_e = f16_bits_to_f32(p.scale[nc]);
+        bi_e = p.bias ? F16::to_f32(p.bias[nc]) : 0.0f;
+    }
+    // 2. a' and D partials to LDS; surplus units (u >= units, whole 16-lane
+    //    rows since units and blockDim are multiples of 16) store to the sink
 #pragma unroll
     for (int j = 0; j < UPT; ++j) {
         const int u = (int)threadIdx.x + j * (int)blockDim.x;
-        if (u >= units) break;
-        const int m = u / (nch * 4);
-        const int rem = u - m * nch * 4;
+        const bool live = u < units;
+        const int uc = live ? u : units - 1;
+        const int m = (uc >= per) + (uc >= 2 * per) + (uc >= 3 * per);
+        const int rem = uc - m * per;
         const uint4 w0 = make_uint4(a_pair<0, 0>(av[j]), a_pair<0, 1>(av[j]), a_pair<0, 2>(av[j]), a_pair<0, 3>(av[j]));
         const uint4 w1 = make_uint4(a_pair<0, 4>(av[j]), a_pair<0, 5>(av[j]), a_pair<0, 6>(av[j]), a_pair<0, 7>(av[j]));
         float dp = 0.0f;
@@ -384,14 +425,25 @@ __global__ __launch_bounds__(1024) void ternary_gemv_lds_kernel(GemmArgs p) {
         dp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w1.y), __builtin_bit_cast(f16x2, one_pattern<5>()), dp, false);
         dp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w1.z), __builtin_bit_cast(f16x2, one_pattern<6>()), dp, false);
         dp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w1.w), __builtin_bit_cast(f16x2, one_pattern<7>()), dp, false);
-        uint4* dst = reinterpret_cast<uint4*>(aps + ((int64_t)(m * nch + (rem >> 2)) * 32 + 8 * (rem & 3)));
+        dp = row16_sum(dp);  // the 16 units of this row: 256 columns of activation row m
+        uint4* dst = live ? reinterpret_cast<uint4*>(aps + ((int64_t)(m * nch + (rem >> 2)) * 32 + 8 * (rem & 3))) : sink;
         dst[0] = w0;
         dst[1] = w1;
-        dpart[u] = dp;
+        if (live && (lane & 15) == 0) dpart[u >> 4] = dp;
     }
-    __syncthreads();
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 
-    // 3. contract
+    // 3. D[m] (trailing wave, fixed order), then contract
+    if (wave == W - 1) {
+        for (int m = 0; m < M; ++m) {
+            float t = 0.0f;
+            for (int c = lane; c < CS; c += kWave) t += dpart[m * CS + c];
+            t = wave_sum(t);
+            if (lane == 0) dsum[m] = t;
+        }
+    }
     f32x4 acc[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -401,10 +453,17 @@ __global__ __launch_bounds__(1024) void ternary_gemv_lds_kernel(GemmArgs p) {
     for (int s = 0; s < CSW; ++s) {
         if (s < cnt) {
             const int chunk = 4 * (cs0 + s) + g;
-            const uint4* arow = reinterpret_cast<const uint4*>(a_live ? aps + (int64_t)(i16 * nch + chunk) * 32 : zero_blk);
+            // Lanes of rows m >= M only feed output rows that are never
+            // stored (row m of the product depends on row m of A alone), so
+            // they skip the LDS read and keep an arbitrary register value.
             uint4 aw[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) aw[e] = arow[e];
+            for (int e = 0; e < 8; ++e) aw[e] = opaque_uint4();
+            if (a_live) {
+                const uint4* arow = reinterpret_cast<const uint4*>(aps + (int64_t)(i16 * nch + chunk) * 32);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) aw[e] = arow[e];
+            }
 #define TQ_MFMA_L(D, I0)                                                                              \
     {                                                                                                 \
         const f16x8 aop = __builtin_bit_cast(f16x8, aw[2 * (D) + (I0) / 4]);                          \
@@ -428,36 +487,23 @@ __global__ __launch_bounds__(1024) void ternary_gemv_lds_kernel(GemmArgs p) {
         }
     }
 
-    // 4. D[m] (wave 0, fixed order), wave partials -> LDS, fixed-order sum
-    __syncthreads();  // a' no longer needed; dpart still live
-    __shared__ float dsum[4];
-    f32x4* red = reinterpret_cast<f32x4*>(smem);
-    if (wave == 0) {
-        const int per = nch * 4;
-        for (int m = 0; m < M; ++m) {
-            float t = 0.0f;
-            for (int k = lane; k < per; k += kWave) t += dpart[m * per + k];
-            t = wave_sum(t);
-            if (lane == 0) dsum[m] = t;
-        }
-    }
-    __syncthreads();  // dpart consumed before red overwrites it
+    // 4. wave partials -> LDS, fixed-order sum
 #pragma unroll
     for (int r = 0; r < R; ++r) red[(wave * R + r) * kWave + lane] = acc[r];
     __syncthreads();
-    for (int e = threadIdx.x; e < R * kWave; e += blockDim.x) {
+    if ((int)threadIdx.x < R * kWave) {  // R <= W
+        const int e = (int)threadIdx.x;
         const int r = e / kWave;
         const int l = e % kWave;
         f32x4 sum = red[r * kWave + l];
         for (int w = 1; w < W; ++w) sum += red[(w * R + r) * kWave + l];
         const int64_t n = n_base + 16 * r + (l & 15);
-        if (n >= N) continue;
-        const float sc = f16_bits_to_f32(p.scale[n]);
-        const float b = p.bias ? F16::to_f32(p.bias[n]) : 0.0f;
+        if (n < N) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int m = 4 * (l >> 4) + i;
-            if (m < M) p.C[(int64_t)m * N + n] = F16::from_f32((sum[i] - dsum[m]) * sc + b);
+            for (int i = 0; i < 4; ++i) {
+                const int m = 4 * (l >> 4) + i;
+                if (m < M) p.C[(int64_t)m * N + n] = F16::from_f32((sum[i] - dsum[m]) * sc_e + bi_e);
+            }
         }
     }
 }
@@ -484,42 +530,58 @@ bool ternary_gemv_mfma_ok(const GemmArgs& a) { return !a.bf16 && a.M <= kGemvMax
 #ifndef TQ_GEMV_LDS_R
 #define TQ_GEMV_LDS_R 1
 #endif
-constexpr int kGemvLdsR = TQ_GEMV_LDS_R;  // 16-row blocks per workgroup
-constexpr int64_t kGemvLdsMaxMK = 28672;  // LDS: a' (M*K*2 B) + zero block + D partials (M*K/4 B) <= 64 KB
+#ifndef TQ_GEMV_MIN_CSW
+#define TQ_GEMV_MIN_CSW 4
+#endif
+constexpr int kGemvLdsR = TQ_GEMV_LDS_R;      // 16-row blocks per workgroup
+constexpr int kGemvMinCsw = TQ_GEMV_MIN_CSW;  // fewest chunk-sets per wave
+constexpr int64_t kGemvLdsMaxMK = 28672;      // a' (M*K*2 bytes) within 56 KB
+constexpr int kGemvLdsMaxBytes = 96 * 1024;   // >= gemv_lds_bytes() of every eligible shape
 
-// Shape rule for the LDS kernel: chunk-sets per wave CSW in {4, 8}, W waves.
+// Shape rule for the LDS kernel: the fewest chunk-sets per wave CSW in
+// {1, 2, 4, 8} (at least kGemvMinCsw) that keeps the block within 16 waves.
 static bool gemv_lds_plan(const GemmArgs& a, int* csw, int* waves) {
     if (a.bf16 || a.M > 4 || a.K % 256 != 0 || a.M * a.K > kGemvLdsMaxMK) return false;
     const int64_t cs = a.K / 256;
-    if ((cs + 3) / 4 <= 8) *csw = 4;
-    else if ((cs + 7) / 8 <= 16) *csw = 8;
-    else return false;
-    *waves = (int)((cs + *csw - 1) / *csw);
+    int c = kGemvMinCsw;
+    while (c <= 8 && (cs + c - 1) / c > 16) c *= 2;
+    if (c > 8) return false;
+    *csw = c;
+    *waves = (int)((cs + c - 1) / c);
+    if (*waves < kGemvLdsR) return false;                      // the epilogue uses 64R threads
     return a.M * (a.K / 16) <= (int64_t)4 * *waves * kWave;  // at most 4 prep units per thread
+}
+
+template <int CSW, int UPT>
+static hipError_t launch_gemv_lds(const GemmArgs& a, int waves, hipStream_t s) {
+    static DeviceFlags lds_limit_set;
+    hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(&ternary_gemv_lds_kernel<kGemvLdsR, CSW, UPT>),
+                                   kGemvLdsMaxBytes, lds_limit_set);
+    if (e != hipSuccess) return e;
+    const size_t lds = gemv_lds_bytes(a.M, a.K, waves, kGemvLdsR);
+    const dim3 grid((unsigned)((a.N + 16 * kGemvLdsR - 1) / (16 * kGemvLdsR)));
+    ternary_gemv_lds_kernel<kGemvLdsR, CSW, UPT><<<grid, dim3(waves * kWave), lds, s>>>(a);
+    return hipGetLastError();
+}
+
+template <int CSW>
+static hipError_t launch_gemv_lds_upt(const GemmArgs& a, int waves, hipStream_t s) {
+    const int64_t units = a.M * (a.K / 16);
+    const int64_t upt = (units + waves * kWave - 1) / (waves * kWave);
+    if (upt <= 1) return launch_gemv_lds<CSW, 1>(a, waves, s);
+    if (upt <= 2) return launch_gemv_lds<CSW, 2>(a, waves, s);
+    return launch_gemv_lds<CSW, 4>(a, waves, s);
 }
 
 hipError_t launch_ternary_gemv(const GemmArgs& a, hipStream_t s) {
     int csw = 0, waves = 0;
     if (gemv_lds_plan(a, &csw, &waves)) {
-        const int64_t aprime = a.M * a.K * 2 + 128 + a.M * (a.K / 16) * 4;
-        const int64_t red = (int64_t)waves * kGemvLdsR * kWave * 16;
-        const size_t lds = (size_t)(aprime > red ? aprime : red);
-        const dim3 grid((unsigned)((a.N + 16 * kGemvLdsR - 1) / (16 * kGemvLdsR)));
-        const int64_t units = a.M * (a.K / 16);
-        const int64_t upt = (units + waves * kWave - 1) / (waves * kWave);
-        const dim3 block(waves * kWave);
-#define TQ_LDS_LAUNCH(CSW, UPT) ternary_gemv_lds_kernel<kGemvLdsR, CSW, UPT><<<grid, block, lds, s>>>(a)
-        if (csw == 4) {
-            if (upt <= 1) TQ_LDS_LAUNCH(4, 1);
-            else if (upt <= 2) TQ_LDS_LAUNCH(4, 2);
-            else TQ_LDS_LAUNCH(4, 4);
-        } else {
-            if (upt <= 1) TQ_LDS_LAUNCH(8, 1);
-            else if (upt <= 2) TQ_LDS_LAUNCH(8, 2);
-            else TQ_LDS_LAUNCH(8, 4);
+        switch (csw) {
+            case 1: return launch_gemv_lds_upt<1>(a, waves, s);
+            case 2: return launch_gemv_lds_upt<2>(a, waves, s);
+            case 4: return launch_gemv_lds_upt<4>(a, waves, s);
+            default: return launch_gemv_lds_upt<8>(a, waves, s);
         }
-#undef TQ_LDS_LAUNCH
-        return hipGetLastError();
     }
     if (ternary_gemv_mfma_ok(a)) {
         if (a.M <= 4) launch_gemv_mfma_w<2>(a, s);

@@ -102,6 +102,15 @@ __device__ __forceinline__ uint32_t vgpr_const() {
     return r;
 }
 
+// A register value the compiler treats as defined but whose contents are
+// whatever the registers hold: no instruction is emitted.  For operands whose
+// results are discarded.
+__device__ __forceinline__ uint4 opaque_uint4() {
+    uint4 v;
+    asm volatile("" : "=v"(v.x), "=v"(v.y), "=v"(v.z), "=v"(v.w));
+    return v;
+}
+
 // Activation element type tags.
 // from_f32 rounds in software (mode-independent); from_f32_fast uses the
 // hardware conversion, which rounds to nearest even under the default mode
@@ -118,14 +127,21 @@ struct BF16 {
     static __device__ __forceinline__ uint16_t from_f32_fast(float x) { return f32_to_bf16_rne(x); }
 };
 
-// Sum over the 64 lanes of a wave; every lane receives the total.  The first
-// four steps stay inside a 16-lane row (DPP: swap neighbours, swap pairs,
-// mirror half-rows, mirror rows); the last two cross rows.
-__device__ __forceinline__ float wave_sum(float v) {
+// Sum over the 16 lanes of each DPP row (lanes 16r .. 16r+15); every lane of
+// the row receives its row's total.  Steps: swap neighbours, swap pairs,
+// mirror half-rows, mirror rows.  All 64 lanes must be active.
+__device__ __forceinline__ float row16_sum(float v) {
     v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
     v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
     v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));  // row_half_mirror
     v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));  // row_mirror
+    return v;
+}
+
+// Sum over the 64 lanes of a wave; every lane receives the total: the row
+// sums, then two exchanges across rows.
+__device__ __forceinline__ float wave_sum(float v) {
+    v = row16_sum(v);
     v += __shfl_xor(v, 16, kWave);
     v += __shfl_xor(v, 32, kWave);
     return v;

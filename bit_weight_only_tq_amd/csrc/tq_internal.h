@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace tq {
 
 // pack.hip
@@ -16,6 +18,26 @@ hipError_t launch_w4_pack(const float* W, int64_t N, int64_t K, int32_t* qweight
                           int* flags, hipStream_t s);
 hipError_t launch_w4_unpack(const int32_t* qweight, const uint16_t* scales, int64_t N, int64_t K,
                             uint8_t* q_out, uint16_t* wdq_out, hipStream_t s);
+
+// One bit per device ordinal (0..63): whether a per-function setting has been
+// applied on that device.
+struct DeviceFlags {
+    std::atomic<uint64_t> bits{0};
+};
+
+// Allow `fn` up to `bytes` of dynamic LDS on the current device (once per
+// device; repeating the call is harmless, so a race between threads is too).
+inline hipError_t raise_lds_limit(const void* fn, int bytes, DeviceFlags& done) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const uint64_t bit = dev < 64 ? (1ull << dev) : 0ull;
+    if (bit && (done.bits.load(std::memory_order_relaxed) & bit)) return hipSuccess;
+    e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e != hipSuccess) return e;
+    done.bits.fetch_or(bit, std::memory_order_relaxed);
+    return hipSuccess;
+}
 
 // Arguments of one quantized linear-layer call (apply stage).
 struct GemmArgs {
