@@ -297,52 +297,54 @@ __global__ __launch_bounds__(W * kWave) void ternary_gemv_mfma_kernel(GemmArgs p
 
 // Same arithmetic, latency-first schedule (fp16, M <= 4, M * K <= 28672).
 //
-// 1. Each thread loads the activations of its prep units first (a few KB per
-//    block, mostly L2 hits); then every wave issues the code loads of ALL its
-//    chunk-sets.  Every load is unconditional (addresses clamped, surplus
-//    results discarded): the compiler then keeps this issue order, and the
-//    in-order completion counter lets each use wait only for the loads it
-//    needs - in particular the prep waits for the activations only.
-// 2. While the codes are in flight the block writes the scaled, paired a'
-//    values to LDS in the order the MFMA operands read them - dword
-//    ((m * K/64 + chunk) * 32 + 8 d + i) = pair (d, i) of row m - and the
-//    row-independent term D[m] = sum_k a'_k (1024 + 4^s(k)): one dot2 partial
-//    per 16 columns, summed over each 16-lane row (16 consecutive units of
-//    one activation row) and stored once per 256 columns.  A bare barrier
-//    (LDS writes complete; no wait on the code loads, which a __syncthreads()
-//    fence would add) publishes them.
-// 3. The trailing wave sums D[m] over its K/256 partials in a fixed order;
-//    every wave contracts its chunk-sets in issue order as their codes land.
-//    Lanes of activation rows m >= M take zero operands without reading LDS.
-// 4. Wave partials meet in their own LDS area; after one barrier a fixed-order
-//    sum, D[m] subtracted once, the row scale and bias applied.
-// Block = W waves (W = ceil(K/256 / CSW) <= 16) over 16R rows and all of K.
+// Block = W waves over 16R weight rows and all of K; wave w owns chunk-sets
+// w*CSW .. w*CSW + CSW-1 (256 columns each) of every row.  Waves are
+// independent until the final reduction: each preps the activations of its
+// own columns in a private LDS area, so no barrier sits between the code
+// loads and the contraction.
+// 1. Each lane loads the activations of its prep units first (16 columns of
+//    one activation row per unit, M*CSW/4 units per lane), then the wave
+//    issues all its code loads in the order step 3 consumes them.  Every
+//    load is unconditional (addresses clamped, surplus results discarded):
+//    the compiler keeps this issue order, and the in-order completion
+//    counter lets each use wait only for the loads it needs - the prep waits
+//    for the activations only.  The epilogue's row scale and bias are loaded
+//    here too.
+// 2. While the codes are in flight the wave writes its scaled, paired a'
+//    values to its LDS area in MFMA operand order - dword
+//    ((m * 4 CSW + chunk) * 32 + 8 d + i) = pair (d, i) of row m - and sums
+//    its share of D[m] = sum_k a'_k (1024 + 4^s(k)): dot2 partials per 16
+//    columns, reduced over each 16-lane row (256 columns of one activation
+//    row) and over the wave's chunk-sets in a fixed order.
+// 3. The wave contracts its chunk-sets as their codes land.  Lanes of
+//    activation rows m >= M skip the LDS read (their output rows are never
+//    stored).  Its D share is subtracted from its partials.
+// 4. Wave partials meet in LDS; after one barrier a fixed-order sum, then the
+//    row scale and bias.
 template <int I>
 __device__ __forceinline__ constexpr uint32_t one_pattern() {  // (1024 + 4^s) in both halves
     constexpr int s = I < 5 ? I : I - 5;
     return 0x64006400u | (0x00010001u << (2 * s));
 }
 
-// LDS layout of the kernel below (byte offsets): a' [M*K*2], D partials
-// [M*K/256 floats, padded to 16 B], D sums [4 floats], wave partials
-// [W*R*64 lanes*16 B], a 32-byte sink for the stores of surplus prep lanes.
+// LDS layout of the kernel below (byte offsets): per wave, a' [M][4 CSW
+// chunks][128 bytes] then D partials [M][CSW floats, padded to 16 bytes];
+// after the W wave areas, the wave partials [W][R][64 lanes][16 bytes].
 struct GemvLds {
-    int64_t dpart, dsum, red, sink, total;
-    __host__ __device__ GemvLds(int64_t M, int64_t K, int W, int R) {
-        dpart = M * K * 2;
-        dsum = dpart + ((M * (K / 256) * 4 + 15) / 16) * 16;
-        red = dsum + 16;
-        sink = red + (int64_t)W * R * 64 * 16;
-        total = sink + 32;
+    int64_t wave_bytes, dpart, red, total;
+    __host__ __device__ GemvLds(int64_t M, int csw, int W, int R) {
+        dpart = M * csw * 512;
+        wave_bytes = dpart + ((M * csw * 4 + 15) / 16) * 16;
+        red = W * wave_bytes;
+        total = red + (int64_t)W * R * 64 * 16;
     }
 };
-static inline size_t gemv_lds_bytes(int64_t M, int64_t K, int W, int R) { return (size_t)GemvLds(M, K, W, R).total; }
+static inline size_t gemv_lds_bytes(int64_t M, int csw, int W, int R) { return (size_t)GemvLds(M, csw, W, R).total; }
 
 template <int R, int CSW, int UPT>
 __global__ __launch_bounds__(1024) void ternary_gemv_lds_kernel(GemmArgs p) {
     extern __shared__ uint4 smem[];
     uint8_t* lds = reinterpret_cast<uint8_t*>(smem);
-    uint32_t* aps = reinterpret_cast<uint32_t*>(smem);
     const int W = blockDim.x >> 6;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x >> 6;
@@ -351,30 +353,28 @@ __global__ __launch_bounds__(1024) void ternary_gemv_lds_kernel(GemmArgs p) {
     const int64_t N = p.N, K = p.K;
     const int M = (int)p.M;
     const int64_t rb = K / 4;
-    const int nch = (int)(K / 64);
     const int CS = (int)(K / 256);
     const int64_t n_base = (int64_t)blockIdx.x * (16 * R);
     const uint8_t* codes = static_cast<const uint8_t*>(p.wq);
     const int cs0 = wave * CSW;
     const int cnt = CS - cs0 < CSW ? CS - cs0 : CSW;  // >= 1 for every wave of the launch
-    const int units = M * nch * 4;                     // (row, chunk, dword) = 16 columns; units % 16 == 0
-    const GemvLds L(M, K, W, R);
-    float* dpart = reinterpret_cast<float*>(lds + L.dpart);  // [M][CS]
-    float* dsum = reinterpret_cast<float*>(lds + L.dsum);    // [4]
-    f32x4* red = reinterpret_cast<f32x4*>(lds + L.red);      // [W][R][64]
-    uint4* sink = reinterpret_cast<uint4*>(lds + L.sink);
+    const GemvLds L(M, CSW, W, R);
+    uint32_t* aps = reinterpret_cast<uint32_t*>(lds + wave * L.wave_bytes);   // this wave's a'
+    float* dpart = reinterpret_cast<float*>(lds + wave * L.wave_bytes + L.dpart);
+    f32x4* red = reinterpret_cast<f32x4*>(lds + L.red);                      // [W][R][64]
 
-    // 1a. activation loads of this thread's prep units (issued before the codes);
-    //     unit u covers columns 16 (u % per) .. +15 of activation row u / per
-    const int per = nch * 4;
+    // 1a. activation loads: unit u = lane + 64 j covers columns
+    //     256 cs0 + 16 c .. +15 of activation row m, where u = m * per + c
+    const int per = cnt * 16;
+    const int units = M * per;  // a multiple of 16
     uint4 av[UPT][8];
 #pragma unroll
     for (int j = 0; j < UPT; ++j) {
-        const int u = (int)threadIdx.x + j * (int)blockDim.x;
+        const int u = lane + j * kWave;
         const int uc = u < units ? u : units - 1;
         const int m = (uc >= per) + (uc >= 2 * per) + (uc >= 3 * per);  // M <= 4
-        const int rem = uc - m * per;
-        const uint4* src = reinterpret_cast<const uint4*>(p.A + (int64_t)m * K + 16 * rem);
+        const int c = uc - m * per;
+        const uint4* src = reinterpret_cast<const uint4*>(p.A + (int64_t)m * K + (int64_t)cs0 * 256 + 16 * c);
         av[j][0] = src[0];
         av[j][1] = src[1];
     }
@@ -395,8 +395,7 @@ __global__ __launch_bounds__(1024) void ternary_gemv_lds_kernel(GemmArgs p) {
         for (int r = 0; r < R; ++r) q[s][r] = *reinterpret_cast<const uint4*>(crow[r] + (int64_t)(4 * cs + g) * 16);
     }
     // 1c. row scale and bias of the output this thread finishes in step 4
-    //     (thread e < 64R: row n_base + 16 (e / 64) + e % 16), loaded now so
-    //     that the epilogue does not wait for memory
+    //     (thread e < 64R: row n_base + 16 (e / 64) + e % 16)
     float sc_e, bi_e;
     {
         const int e = (int)threadIdx.x % (R * kWave);
@@ -405,15 +404,14 @@ __global__ __launch_bounds__(1024) void ternary_gemv_lds_kernel(GemmArgs p) {
         sc_e = f16_bits_to_f32(p.scale[nc]);
         bi_e = p.bias ? F16::to_f32(p.bias[nc]) : 0.0f;
     }
-    // 2. a' and D partials to LDS; surplus units (u >= units, whole 16-lane
-    //    rows since units and blockDim are multiples of 16) store to the sink
+    // 2. a' and D partials of this wave's columns to its LDS area
 #pragma unroll
     for (int j = 0; j < UPT; ++j) {
-        const int u = (int)threadIdx.x + j * (int)blockDim.x;
+        const int u = lane + j * kWave;
         const bool live = u < units;
         const int uc = live ? u : units - 1;
         const int m = (uc >= per) + (uc >= 2 * per) + (uc >= 3 * per);
-        const int rem = uc - m * per;
+        const int c = uc - m * per;
         const uint4 w0 = make_uint4(a_pair<0, 0>(av[j]), a_pair<0, 1>(av[j]), a_pair<0, 2>(av[j]), a_pair<0, 3>(av[j]));
         const uint4 w1 = make_uint4(a_pair<0, 4>(av[j]), a_pair<0, 5>(av[j]), a_pair<0, 6>(av[j]), a_pair<0, 7>(av[j]));
         float dp = 0.0f;
@@ -425,25 +423,29 @@ __global__ __launch_bounds__(1024) void ternary_gemv_lds_kernel(GemmArgs p) {
         dp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w1.y), __builtin_bit_cast(f16x2, one_pattern<5>()), dp, false);
         dp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w1.z), __builtin_bit_cast(f16x2, one_pattern<6>()), dp, false);
         dp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w1.w), __builtin_bit_cast(f16x2, one_pattern<7>()), dp, false);
-        dp = row16_sum(dp);  // the 16 units of this row: 256 columns of activation row m
-        uint4* dst = live ? reinterpret_cast<uint4*>(aps + ((int64_t)(m * nch + (rem >> 2)) * 32 + 8 * (rem & 3))) : sink;
-        dst[0] = w0;
-        dst[1] = w1;
-        if (live && (lane & 15) == 0) dpart[u >> 4] = dp;
-    }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-
-    // 3. D[m] (trailing wave, fixed order), then contract
-    if (wave == W - 1) {
-        for (int m = 0; m < M; ++m) {
-            float t = 0.0f;
-            for (int c = lane; c < CS; c += kWave) t += dpart[m * CS + c];
-            t = wave_sum(t);
-            if (lane == 0) dsum[m] = t;
+        dp = row16_sum(dp);  // 16 units of one row: 256 columns (one chunk-set) of activation row m
+        if (live) {
+            uint4* dst = reinterpret_cast<uint4*>(aps + ((int64_t)(m * 4 * CSW + (c >> 2)) * 32 + 8 * (c & 3)));
+            dst[0] = w0;
+            dst[1] = w1;
+            if ((c & 15) == 0) dpart[m * CSW + (c >> 4)] = dp;
         }
     }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's LDS writes are complete
+
+    // this lane's share of D for its output rows m = 4 (lane / 16) + i
+    float dsub[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int m = 4 * g + i;
+        float t = 0.0f;
+        if (m < M) {
+            for (int q2 = 0; q2 < cnt; ++q2) t += dpart[m * CSW + q2];
+        }
+        dsub[i] = t;
+    }
+
+    // 3. contract
     f32x4 acc[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -452,7 +454,6 @@ __global__ __launch_bounds__(1024) void ternary_gemv_lds_kernel(GemmArgs p) {
 #pragma unroll
     for (int s = 0; s < CSW; ++s) {
         if (s < cnt) {
-            const int chunk = 4 * (cs0 + s) + g;
             // Lanes of rows m >= M only feed output rows that are never
             // stored (row m of the product depends on row m of A alone), so
             // they skip the LDS read and keep an arbitrary register value.
@@ -460,7 +461,7 @@ __global__ __launch_bounds__(1024) void ternary_gemv_lds_kernel(GemmArgs p) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) aw[e] = opaque_uint4();
             if (a_live) {
-                const uint4* arow = reinterpret_cast<const uint4*>(aps + (int64_t)(i16 * nch + chunk) * 32);
+                const uint4* arow = reinterpret_cast<const uint4*>(aps + (int64_t)(i16 * 4 * CSW + 4 * s + g) * 32);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) aw[e] = arow[e];
             }
@@ -487,9 +488,14 @@ __global__ __launch_bounds__(1024) void ternary_gemv_lds_kernel(GemmArgs p) {
         }
     }
 
-    // 4. wave partials -> LDS, fixed-order sum
+    // 4. wave partials (D share removed) -> LDS, fixed-order sum
 #pragma unroll
-    for (int r = 0; r < R; ++r) red[(wave * R + r) * kWave + lane] = acc[r];
+    for (int r = 0; r < R; ++r) {
+        f32x4 v = acc[r];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] -= dsub[i];
+        red[(wave * R + r) * kWave + lane] = v;
+    }
     __syncthreads();
     if ((int)threadIdx.x < R * kWave) {  // R <= W
         const int e = (int)threadIdx.x;
@@ -502,7 +508,174 @@ __global__ __launch_bounds__(1024) void ternary_gemv_lds_kernel(GemmArgs p) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int m = 4 * (l >> 4) + i;
-                if (m < M) p.C[(int64_t)m * N + n] = F16::from_f32((sum[i] - dsum[m]) * sc_e + bi_e);
+                if (m < M) p.C[(int64_t)m * N + n] = F16::from_f32(sum[i] * sc_e + bi_e);
+            }
+        }
+    }
+}
+
+// Same arithmetic, streaming schedule (fp16, M <= 16, K / 256 <= 16 CSW).
+//
+// One workgroup per compute unit walks T consecutive 16-row blocks.  Wave w
+// owns chunk-sets w*CSW .. w*CSW + CSW-1 (256 columns each) of all of them,
+// so the activation operand of its MFMAs never changes: it is built once, in
+// registers, from the activations of its columns (lane 16g + i: row i,
+// chunk 4cs + g), together with the wave's share of D[m].  The wave issues
+// its activation loads, then the code loads of all T row-blocks, then builds
+// the operand while the codes are in flight, and contracts each row-block as
+// its codes land (in-order completion), one accumulator per row-block.  Wave
+// partials meet in LDS once, at the end, and are summed in a fixed order.
+template <int CSW, int T>
+__global__ __launch_bounds__(1024) void ternary_gemv_stream_kernel(GemmArgs p) {
+    extern __shared__ uint4 smem[];
+    f32x4* red = reinterpret_cast<f32x4*>(smem);  // [W][T][64]
+    const int W = blockDim.x >> 6;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x >> 6;
+    const int g = lane >> 4;
+    const int i16 = lane & 15;
+    const int64_t N = p.N, K = p.K;
+    const int M = (int)p.M;
+    const int64_t rb = K / 4;
+    const int CS = (int)(K / 256);
+    const int64_t n_base = (int64_t)blockIdx.x * (16 * T);
+    const uint8_t* codes = static_cast<const uint8_t*>(p.wq);
+    const int cs0 = wave * CSW;
+    const int cnt = CS - cs0 < CSW ? CS - cs0 : CSW;  // >= 1 for every wave of the launch
+
+    // 1. activations of this lane's operand row (rows m >= M only feed output
+    //    rows that are never stored: they skip the load and keep an arbitrary
+    //    register value)
+    const bool a_live = i16 < M;
+    uint4 av[CSW][8];
+#pragma unroll
+    for (int s = 0; s < CSW; ++s)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) av[s][e] = opaque_uint4();
+    if (a_live) {
+        const uint16_t* arow = p.A + (int64_t)i16 * K;
+#pragma unroll
+        for (int s = 0; s < CSW; ++s) {
+            const int cs = (s < cnt) ? cs0 + s : cs0;
+            const uint4* src = reinterpret_cast<const uint4*>(arow + (int64_t)(4 * cs + g) * 64);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) av[s][e] = src[e];
+        }
+    }
+    // 2. code loads of all row-blocks, in the order step 4 consumes them (rows
+    //    past N re-read row N-1, chunk-sets past the wave's share re-read its
+    //    first one; both are ignored)
+    uint4 q[T][CSW];
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        const int64_t n = n_base + 16 * t + i16;
+        const uint8_t* crow = codes + (n < N ? n : N - 1) * rb;
+#pragma unroll
+        for (int s = 0; s < CSW; ++s) {
+            const int cs = (s < cnt) ? cs0 + s : cs0;
+            q[t][s] = *reinterpret_cast<const uint4*>(crow + (int64_t)(4 * cs + g) * 16);
+        }
+    }
+    // row scale and bias of the output this thread finishes in step 5
+    // (thread e < 64T: row n_base + 16 (e / 64) + e % 16)
+    float sc_e, bi_e;
+    {
+        const int e = (int)threadIdx.x % (T * kWave);
+        const int64_t n = n_base + 16 * (e / kWave) + (e & 15);
+        const int64_t nc = n < N ? n : N - 1;
+        sc_e = f16_bits_to_f32(p.scale[nc]);
+        bi_e = p.bias ? F16::to_f32(p.bias[nc]) : 0.0f;
+    }
+
+    // 3. operands a' (pair (d, i) of a chunk in dword 8 d + i) and the D share
+    uint4 aw[CSW][8];
+    float dl = 0.0f;
+#pragma unroll
+    for (int s = 0; s < CSW; ++s) {
+#define TQ_APREP(D)                                                                                  \
+        aw[s][2 * (D)] = make_uint4(a_pair<D, 0>(av[s]), a_pair<D, 1>(av[s]), a_pair<D, 2>(av[s]), a_pair<D, 3>(av[s])); \
+        aw[s][2 * (D) + 1] = make_uint4(a_pair<D, 4>(av[s]), a_pair<D, 5>(av[s]), a_pair<D, 6>(av[s]), a_pair<D, 7>(av[s]));
+        TQ_APREP(0)
+        TQ_APREP(1)
+        TQ_APREP(2)
+        TQ_APREP(3)
+#undef TQ_APREP
+        if (s < cnt) {
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const uint4 lo = aw[s][2 * d], hi = aw[s][2 * d + 1];
+                dl = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, lo.x), __builtin_bit_cast(f16x2, one_pattern<0>()), dl, false);
+                dl = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, lo.y), __builtin_bit_cast(f16x2, one_pattern<1>()), dl, false);
+                dl = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, lo.z), __builtin_bit_cast(f16x2, one_pattern<2>()), dl, false);
+                dl = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, lo.w), __builtin_bit_cast(f16x2, one_pattern<3>()), dl, false);
+                dl = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, hi.x), __builtin_bit_cast(f16x2, one_pattern<4>()), dl, false);
+                dl = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, hi.y), __builtin_bit_cast(f16x2, one_pattern<5>()), dl, false);
+                dl = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, hi.z), __builtin_bit_cast(f16x2, one_pattern<6>()), dl, false);
+                dl = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, hi.w), __builtin_bit_cast(f16x2, one_pattern<7>()), dl, false);
+            }
+        }
+    }
+    // D share of operand row i16, summed over the four lane groups; output
+    // element i of this lane belongs to row 4g + i
+    dl += __shfl_xor(dl, 16, kWave);
+    dl += __shfl_xor(dl, 32, kWave);
+    float dsub[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dsub[i] = __shfl(dl, 4 * g + i, kWave);
+
+    // 4. contract each row-block as its codes land
+    const uint32_t magic_v = vgpr_const<kMagic2>();
+    f32x4 acc[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        f32x4 a4 = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < CSW; ++s) {
+            if (s < cnt) {
+#define TQ_MFMA_S(D, I0)                                                                              \
+    {                                                                                                 \
+        const uint32_t x = dword_of(q[t][s], D);                                                      \
+        const uint32_t y = x >> 10;                                                                   \
+        const uint4 bw = make_uint4(field_pair<I0>(x, y, magic_v), field_pair<I0 + 1>(x, y, magic_v), \
+                                    field_pair<I0 + 2>(x, y, magic_v), field_pair<I0 + 3>(x, y, magic_v)); \
+        a4 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, aw[s][2 * (D) + (I0) / 4]), \
+                                                    __builtin_bit_cast(f16x8, bw), a4, 0, 0, 0);      \
+    }
+                TQ_MFMA_S(0, 0)
+                TQ_MFMA_S(0, 4)
+                TQ_MFMA_S(1, 0)
+                TQ_MFMA_S(1, 4)
+                TQ_MFMA_S(2, 0)
+                TQ_MFMA_S(2, 4)
+                TQ_MFMA_S(3, 0)
+                TQ_MFMA_S(3, 4)
+#undef TQ_MFMA_S
+            }
+        }
+        acc[t] = a4;
+    }
+
+    // 5. wave partials (D share removed) -> LDS, fixed-order sum
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        f32x4 v = acc[t];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] -= dsub[i];
+        red[(wave * T + t) * kWave + lane] = v;
+    }
+    __syncthreads();
+    if ((int)threadIdx.x < T * kWave) {  // T <= W
+        const int e = (int)threadIdx.x;
+        const int t = e / kWave;
+        const int l = e % kWave;
+        f32x4 sum = red[t * kWave + l];
+        for (int w = 1; w < W; ++w) sum += red[(w * T + t) * kWave + l];
+        const int64_t n = n_base + 16 * t + (l & 15);
+        if (n < N) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int m = 4 * (l >> 4) + i;
+                if (m < M) p.C[(int64_t)m * N + n] = F16::from_f32(sum[i] * sc_e + bi_e);
             }
         }
     }
@@ -527,60 +700,138 @@ static void launch_gemv_mfma_w(const GemmArgs& a, hipStream_t s) {
 
 bool ternary_gemv_mfma_ok(const GemmArgs& a) { return !a.bf16 && a.M <= kGemvMaxM && a.K % 256 == 0; }
 
-#ifndef TQ_GEMV_LDS_R
-#define TQ_GEMV_LDS_R 1
-#endif
 #ifndef TQ_GEMV_MIN_CSW
 #define TQ_GEMV_MIN_CSW 4
 #endif
-constexpr int kGemvLdsR = TQ_GEMV_LDS_R;      // 16-row blocks per workgroup
 constexpr int kGemvMinCsw = TQ_GEMV_MIN_CSW;  // fewest chunk-sets per wave
 constexpr int64_t kGemvLdsMaxMK = 28672;      // a' (M*K*2 bytes) within 56 KB
-constexpr int kGemvLdsMaxBytes = 96 * 1024;   // >= gemv_lds_bytes() of every eligible shape
+constexpr int kGemvLdsMaxBytes = 160 * 1024;  // the CU's LDS
+
+struct GemvPlan {
+    int csw, waves, rows16, upt;
+    size_t lds;
+};
 
 // Shape rule for the LDS kernel: the fewest chunk-sets per wave CSW in
-// {1, 2, 4, 8} (at least kGemvMinCsw) that keeps the block within 16 waves.
-static bool gemv_lds_plan(const GemmArgs& a, int* csw, int* waves) {
+// {1, 2, 4, 8} (at least kGemvMinCsw) that keeps the block within 16 waves;
+// R 16-row blocks per workgroup, more for larger M (the activation prep is
+// shared by R times more rows) while at least 256 workgroups remain.
+static bool gemv_lds_plan(const GemmArgs& a, GemvPlan* pl) {
     if (a.bf16 || a.M > 4 || a.K % 256 != 0 || a.M * a.K > kGemvLdsMaxMK) return false;
     const int64_t cs = a.K / 256;
     int c = kGemvMinCsw;
+    while (c > 1 && (cs + c / 2 - 1) / (c / 2) <= 4) c /= 2;  // keep at least 4 waves when K is short
     while (c <= 8 && (cs + c - 1) / c > 16) c *= 2;
     if (c > 8) return false;
-    *csw = c;
-    *waves = (int)((cs + c - 1) / c);
-    if (*waves < kGemvLdsR) return false;                      // the epilogue uses 64R threads
-    return a.M * (a.K / 16) <= (int64_t)4 * *waves * kWave;  // at most 4 prep units per thread
+    pl->csw = c;
+    pl->waves = (int)((cs + c - 1) / c);
+    const int64_t nrb = (a.N + 15) / 16;
+    pl->rows16 = (a.M > 1 && c <= 4 && pl->waves >= 2 && nrb >= 512) ? 2 : 1;
+    pl->upt = (int)((a.M * c + 3) / 4);  // <= 4: CSW = 8 only for K > 4096 * 4, where M * K <= 28672 keeps M = 1
+    pl->lds = gemv_lds_bytes(a.M, c, pl->waves, pl->rows16);
+    return pl->lds <= (size_t)kGemvLdsMaxBytes;
 }
 
-template <int CSW, int UPT>
-static hipError_t launch_gemv_lds(const GemmArgs& a, int waves, hipStream_t s) {
+template <int R, int CSW, int UPT>
+static hipError_t launch_gemv_lds(const GemmArgs& a, const GemvPlan& pl, hipStream_t s) {
     static DeviceFlags lds_limit_set;
-    hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(&ternary_gemv_lds_kernel<kGemvLdsR, CSW, UPT>),
+    hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(&ternary_gemv_lds_kernel<R, CSW, UPT>),
                                    kGemvLdsMaxBytes, lds_limit_set);
     if (e != hipSuccess) return e;
-    const size_t lds = gemv_lds_bytes(a.M, a.K, waves, kGemvLdsR);
-    const dim3 grid((unsigned)((a.N + 16 * kGemvLdsR - 1) / (16 * kGemvLdsR)));
-    ternary_gemv_lds_kernel<kGemvLdsR, CSW, UPT><<<grid, dim3(waves * kWave), lds, s>>>(a);
+    const dim3 grid((unsigned)((a.N + 16 * R - 1) / (16 * R)));
+    ternary_gemv_lds_kernel<R, CSW, UPT><<<grid, dim3(pl.waves * kWave), pl.lds, s>>>(a);
     return hipGetLastError();
 }
 
-template <int CSW>
-static hipError_t launch_gemv_lds_upt(const GemmArgs& a, int waves, hipStream_t s) {
-    const int64_t units = a.M * (a.K / 16);
-    const int64_t upt = (units + waves * kWave - 1) / (waves * kWave);
-    if (upt <= 1) return launch_gemv_lds<CSW, 1>(a, waves, s);
-    if (upt <= 2) return launch_gemv_lds<CSW, 2>(a, waves, s);
-    return launch_gemv_lds<CSW, 4>(a, waves, s);
+template <int R, int CSW>
+static hipError_t launch_gemv_lds_upt(const GemmArgs& a, const GemvPlan& pl, hipStream_t s) {
+    switch (pl.upt) {
+        case 1: return launch_gemv_lds<R, CSW, 1>(a, pl, s);
+        case 2: return launch_gemv_lds<R, CSW, 2>(a, pl, s);
+        case 3: return launch_gemv_lds<R, CSW, 3>(a, pl, s);
+        default: return launch_gemv_lds<R, CSW, 4>(a, pl, s);
+    }
+}
+
+// Streaming kernel: fp16, 3 <= M <= 16, K <= 8192 (one or two chunk-sets per
+// wave, at most 16 waves); for M <= 2 the LDS kernel is faster, its per-wave
+// activation prep being cheaper than building the operand in every wave.  T row-blocks per workgroup: the fewest that keep
+// the grid within one workgroup per compute unit (at most 8; at most 4 with
+// two chunk-sets per wave, for registers).
+struct StreamPlan {
+    int csw, waves, t;
+    size_t lds;
+};
+
+static int compute_units() {
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int v = cached[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    cached[dev].store(v, std::memory_order_relaxed);
+    return v;
+}
+
+static bool gemv_stream_plan(const GemmArgs& a, StreamPlan* pl) {
+    if (a.bf16 || a.M < 3 || a.M > kGemvMaxM || a.K % 256 != 0) return false;
+    const int64_t cs = a.K / 256;
+    if (cs > 32) return false;
+    pl->csw = cs <= 16 ? 1 : 2;
+    pl->waves = (int)((cs + pl->csw - 1) / pl->csw);
+    const int64_t nrb = (a.N + 15) / 16;
+    const int64_t cus = compute_units();
+    const int tmax = pl->csw == 1 ? 8 : 4;
+    int t = 1;
+    while (t < tmax && t < pl->waves && (nrb + t - 1) / t > cus) t *= 2;
+    pl->t = t;
+    pl->lds = (size_t)pl->waves * t * kWave * 16;
+    return true;
+}
+
+template <int CSW, int T>
+static hipError_t launch_gemv_stream(const GemmArgs& a, const StreamPlan& pl, hipStream_t s) {
+    static DeviceFlags lds_limit_set;
+    hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(&ternary_gemv_stream_kernel<CSW, T>),
+                                   kGemvLdsMaxBytes, lds_limit_set);
+    if (e != hipSuccess) return e;
+    const dim3 grid((unsigned)((a.N + 16 * T - 1) / (16 * T)));
+    ternary_gemv_stream_kernel<CSW, T><<<grid, dim3(pl.waves * kWave), pl.lds, s>>>(a);
+    return hipGetLastError();
 }
 
 hipError_t launch_ternary_gemv(const GemmArgs& a, hipStream_t s) {
-    int csw = 0, waves = 0;
-    if (gemv_lds_plan(a, &csw, &waves)) {
-        switch (csw) {
-            case 1: return launch_gemv_lds_upt<1>(a, waves, s);
-            case 2: return launch_gemv_lds_upt<2>(a, waves, s);
-            case 4: return launch_gemv_lds_upt<4>(a, waves, s);
-            default: return launch_gemv_lds_upt<8>(a, waves, s);
+    StreamPlan sp;
+    if (gemv_stream_plan(a, &sp)) {
+        if (sp.csw == 1) {
+            switch (sp.t) {
+                case 1: return launch_gemv_stream<1, 1>(a, sp, s);
+                case 2: return launch_gemv_stream<1, 2>(a, sp, s);
+                case 4: return launch_gemv_stream<1, 4>(a, sp, s);
+                default: return launch_gemv_stream<1, 8>(a, sp, s);
+            }
+        }
+        switch (sp.t) {
+            case 1: return launch_gemv_stream<2, 1>(a, sp, s);
+            case 2: return launch_gemv_stream<2, 2>(a, sp, s);
+            default: return launch_gemv_stream<2, 4>(a, sp, s);
+        }
+    }
+    GemvPlan pl;
+    if (gemv_lds_plan(a, &pl)) {
+        if (pl.rows16 == 2) {
+            switch (pl.csw) {
+                case 1: return launch_gemv_lds_upt<2, 1>(a, pl, s);
+                case 2: return launch_gemv_lds_upt<2, 2>(a, pl, s);
+                default: return launch_gemv_lds_upt<2, 4>(a, pl, s);
+            }
+        }
+        switch (pl.csw) {
+            case 1: return launch_gemv_lds_upt<1, 1>(a, pl, s);
+            case 2: return launch_gemv_lds_upt<1, 2>(a, pl, s);
+            case 4: return launch_gemv_lds_upt<1, 4>(a, pl, s);
+            default: return launch_gemv_lds_upt<1, 8>(a, pl, s);
         }
     }
     if (ternary_gemv_mfma_ok(a)) {

@@ -123,6 +123,9 @@ def test_ternary_prefill_sampled(N, K, M, dt):
     (5, 1000, 448), (2, 7, 64),
     (1, 300, 256), (4, 33, 512), (2, 70, 1280), (3, 31, 2304), (1, 5, 28672),
     (9, 45, 768), (16, 100, 2048), (12, 20, 4096), (2, 40, 512), (4, 9, 7168),
+    # decode kernels with several 16-row blocks per workgroup and a partial
+    # last workgroup, and a last wave with fewer chunk-sets than the others
+    (3, 4200, 1024), (5, 16400, 2048), (4, 50, 4352), (6, 8300, 4352), (2, 8300, 4352),
 ])
 @pytest.mark.parametrize("path", ["gemv", "gemm"])
 @pytest.mark.parametrize("dt", ["f16", "bf16"])
