@@ -17,14 +17,18 @@ Also reported in the same JSON line:
     profiles/) when given with --traffic-json.
   * ``decode_unfused``: the same pass with q, k, v, gate, up as separate
     calls (224 launches).
+  * ``decode_70b``: Llama-3-70B decode at M = 1 - 80 layers x {qkv
+    (10240 x 8192), o (8192 x 8192), gate_up (57344 x 8192), down
+    (8192 x 28672)}, 320 launches per step over 17.1 GB of resident packed
+    codes (one seeded layer packed on the device, copied to 80 layers).
   * ``secondary``: the prefill GEMM at M = 4096 on the MLP shapes
     (14336 x 4096, 4096 x 14336), fp16 and bf16, TFLOP/s = 2MNK / time.
   * ``cpu_baseline``: the CPU oracle (fp64 dequant + fp64 product), untuned,
     timed on the host on a bounded sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--mode MODE]
-  --mode full (default) | decode | prefill | calib (plain copy of known size,
-  for scaling hardware byte counters)
+  --mode full (default) | decode | decode70b | prefill | calib (plain copy of
+  known size, for scaling hardware byte counters)
 """
 
 import argparse
@@ -51,7 +55,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--layers", type=int, default=32)
-    ap.add_argument("--mode", default="full", choices=["full", "decode", "prefill", "calib"])
+    ap.add_argument("--mode", default="full", choices=["full", "decode", "decode70b", "prefill", "calib"])
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
     ap.add_argument("--unfused", action="store_true", help="decode mode: q,k,v,gate,up as separate calls")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -65,27 +69,36 @@ def ternary_bytes(M, N, K):
     return N * ((K + 3) // 4) + 2 * N + 2 * M * K + 2 * M * N
 
 
-def layer_shapes(fused):
-    """Projections of one Llama-3-8B layer (name, (N, K)); fused stacks q,k,v and gate,up along N."""
+def layer_shapes(fused, model="8b"):
+    """Projections of one decoder layer (name, (N, K)); fused stacks q,k,v and gate,up along N."""
     import synth
-    s = synth.LLAMA3_8B
+    s = synth.LLAMA3_8B if model == "8b" else synth.LLAMA3_70B
     if not fused:
         return list(s.items())
-    return [("qkv", (s["q"][0] + s["k"][0] + s["v"][0], 4096)), ("o", s["o"]),
-            ("gate_up", (s["gate"][0] + s["up"][0], 4096)), ("down", s["down"])]
+    hidden = s["q"][1]
+    return [("qkv", (s["q"][0] + s["k"][0] + s["v"][0], hidden)), ("o", s["o"]),
+            ("gate_up", (s["gate"][0] + s["up"][0], hidden)), ("down", s["down"])]
 
 
-def build_decode(layers, dev, fused):
+def build_decode(layers, dev, fused, model="8b"):
+    """Packed matrices of `layers` decoder layers.  8B: distinct seeded weights
+    per layer.  70B: one seeded layer packed, its codes copied to every layer
+    (17 GB of distinct device buffers; the bytes streamed are the same)."""
     import torch
     import bit_weight_only_tq_amd as tq
     import synth
     mats = []
     t0 = time.time()
+    first = {}
     for layer in range(layers):
-        for name, (N, K) in layer_shapes(fused):
-            W = synth.weights_device(N, K, synth.seed_for("bench8b", layer, name), dev)
-            codes, scale = tq.tq_pack(W)
-            del W
+        for name, (N, K) in layer_shapes(fused, model):
+            if model == "8b" or layer == 0:
+                W = synth.weights_device(N, K, synth.seed_for("bench" + model, layer, name), dev)
+                codes, scale = tq.tq_pack(W)
+                del W
+                first[name] = (codes, scale)
+            else:
+                codes, scale = (t.clone() for t in first[name])
             mats.append((name, N, K, codes, scale))
     torch.cuda.synchronize()
     log(f"packed {len(mats)} matrices in {time.time() - t0:.1f} s")
@@ -106,12 +119,14 @@ def time_region(fn, steps, stream):
     return start.elapsed_time(end) / 1e3
 
 
-def run_decode(args, dev, fused, graph):
+def run_decode(args, dev, fused, graph, model="8b", layers=None, steps=None):
     import torch
     import bit_weight_only_tq_amd as tq
     import synth
     stream = torch.cuda.current_stream()
-    mats = build_decode(args.layers, dev, fused)
+    layers = args.layers if layers is None else layers
+    steps = args.steps if steps is None else steps
+    mats = build_decode(layers, dev, fused, model)
     xs = {K: synth.activations_device(1, K, synth.seed_for("benchx", K), "f16", dev) for K in {m[2] for m in mats}}
     outs = [torch.empty((1, m[1]), dtype=torch.float16, device=dev) for m in mats]
 
@@ -134,18 +149,33 @@ def run_decode(args, dev, fused, graph):
     for _ in range(args.warmup):
         run()
     torch.cuda.synchronize()
-    t = time_region(run, args.steps, stream)
+    t = time_region(run, steps, stream)
     packed = sum(m[3].numel() for m in mats)
     alg = sum(ternary_bytes(1, m[1], m[2]) for m in mats)
     res = {
         "launches": len(mats), "seconds": t, "packed_bytes": packed, "alg_bytes": alg,
-        "ms_per_step": t / args.steps * 1e3, "packed_gbs": packed * args.steps / t / 1e9,
-        "alg_gbs": alg * args.steps / t / 1e9,
-        "avg_launch_us": t / args.steps / len(mats) * 1e6, "alg_bytes_per_launch": alg / len(mats),
+        "ms_per_step": t / steps * 1e3, "packed_gbs": packed * steps / t / 1e9,
+        "alg_gbs": alg * steps / t / 1e9,
+        "avg_launch_us": t / steps / len(mats) * 1e6, "alg_bytes_per_launch": alg / len(mats),
     }
     del mats, xs, outs
+    if graph:
+        del g
     torch.cuda.empty_cache()
     return res
+
+
+def run_decode_70b(args, dev):
+    """Llama-3-70B decode at M = 1 over 80 resident layers (secondary)."""
+    import synth
+    d = run_decode(args, dev, True, not args.no_graph, model="70b", layers=synth.LLAMA3_70B_LAYERS,
+                   steps=max(2, args.steps // 2))
+    return {"metric": "HBM GB/s ternary GEMV at M=1, Llama-3-70B decode (80 layers resident)",
+            "value": round(d["packed_gbs"], 1), "unit": "GB/s", "frac_of_peak": round(d["packed_gbs"] / HBM_PEAK_GBS, 4),
+            "ms_per_step": round(d["ms_per_step"], 4), "launches_per_step": d["launches"],
+            "packed_bytes_per_step": d["packed_bytes"], "avg_launch_us": round(d["avg_launch_us"], 3),
+            "workload": "80 layers x {qkv (10240x8192), o (8192x8192), gate_up (57344x8192), down (8192x28672)}, "
+                        "one seeded layer packed on the device and copied to every layer"}
 
 
 def run_prefill(dev, iters=10):
@@ -258,6 +288,9 @@ def main():
     if args.mode == "prefill":
         print(json.dumps({"secondary": run_prefill(dev)}), flush=True)
         return
+    if args.mode == "decode70b":
+        print(json.dumps({"decode_70b": run_decode_70b(args, dev)}), flush=True)
+        return
 
     graph = not args.no_graph
     fused = not args.unfused
@@ -300,6 +333,8 @@ def main():
             out["decode_unfused"] = {"value": round(u["packed_gbs"], 1), "unit": "GB/s",
                                      "ms_per_step": round(u["ms_per_step"], 4), "launches_per_step": u["launches"],
                                      "avg_launch_us": round(u["avg_launch_us"], 3)}
+        log("decode, Llama-3-70B, 80 layers")
+        out["decode_70b"] = run_decode_70b(args, dev)
         log("prefill GEMM M=4096")
         out["secondary"] = run_prefill(dev)
         if not args.no_cpu_baseline:
