@@ -6,11 +6,12 @@ layout descriptions.  Build the library with
 ``python -m bit_weight_only_tq_amd.build``.
 """
 
-from ._lib import (TQError, load, tq_abi_version, tq_gemm, tq_pack, tq_select_path,  # noqa: F401
-                   tq_unpack, w4a16_gemm, w4a16_pack, w4a16_unpack)
+from ._lib import (TQError, load, tq_abi_version, tq_gemm, tq_gemm_workspace_bytes, tq_pack,  # noqa: F401
+                   tq_select_path, tq_unpack, w4a16_gemm, w4a16_pack, w4a16_unpack)
 from .layout import TernaryLayout, W4Layout  # noqa: F401
 
 __all__ = [
-    "TQError", "load", "tq_abi_version", "tq_gemm", "tq_pack", "tq_select_path", "tq_unpack",
+    "TQError", "load", "tq_abi_version", "tq_gemm", "tq_gemm_workspace_bytes", "tq_pack", "tq_select_path",
+    "tq_unpack",
     "w4a16_gemm", "w4a16_pack", "w4a16_unpack", "TernaryLayout", "W4Layout",
 ]

@@ -25,7 +25,7 @@ PATHS = {"auto": 0, "gemv": 1, "stream_mfma": 2, "gemm": 3}
 PATH_NAMES = {v: k for k, v in PATHS.items()}
 
 # every symbol include/tq.h declares, with (restype, argtypes)
-_i64, _vp, _i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+_i64, _vp, _i32, _sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
 SIGNATURES = {
     "tq_pack": (_i32, [_vp, _i64, _i64, _vp, _vp, _vp]),
     "tq_unpack": (_i32, [_vp, _vp, _i64, _i64, _vp, _vp, _vp]),
@@ -33,6 +33,8 @@ SIGNATURES = {
     "w4a16_unpack": (_i32, [_vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp]),
     "tq_gemm": (_i32, [_vp, _i32, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp]),
     "tq_gemm_ex": (_i32, [_vp, _i32, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _i32]),
+    "tq_gemm_ws": (_i32, [_vp, _i32, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _sz, _vp, _i32]),
+    "tq_gemm_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32, _i32]),
     "w4a16_gemm": (_i32, [_vp, _i32, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _vp]),
     "w4a16_gemm_ex": (_i32, [_vp, _i32, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _vp, _i32]),
     "tq_select_path": (_i32, [_i32, _i64, _i64, _i64, _i32]),
@@ -153,15 +155,33 @@ def w4a16_unpack(qweight, scales, K: int, group_size: int = 128, want_q: bool = 
 
 # -------------------------------------------------------------------- apply
 
-def tq_gemm(A, codes, scale, bias=None, out=None, path: str = "auto"):
-    """C = A @ dequant(codes, scale)^T (+ bias); A [M, K] fp16/bf16."""
+def tq_gemm_workspace_bytes(M: int, N: int, K: int, dtype: str = "f16", path: str = "auto") -> int:
+    """Bytes of workspace tq_gemm_ws uses for its fastest schedule (0: none)."""
+    d = {"f16": TQ_F16, "bf16": TQ_BF16}[dtype]
+    return int(load().tq_gemm_workspace_bytes(M, N, K, d, PATHS[path]))
+
+
+def tq_gemm(A, codes, scale, bias=None, out=None, path: str = "auto", workspace="auto"):
+    """C = A @ dequant(codes, scale)^T (+ bias); A [M, K] fp16/bf16.
+
+    workspace: "auto" takes the bytes tq_gemm_workspace_bytes asks for from
+    torch's allocator (stream-ordered, so overlapping calls never share it);
+    None runs without one; or a contiguous device tensor."""
     import torch
     _need_cuda(A, codes, scale, bias)
     M, K = A.shape
     N = codes.shape[0]
+    dt = _dtype_enum(A)
     C = out if out is not None else torch.empty((M, N), dtype=A.dtype, device=A.device)
-    _check("tq_gemm", load().tq_gemm_ex(_ptr(A), _dtype_enum(A), M, N, K, _ptr(codes), _ptr(scale),
-                                         _ptr(bias), _ptr(C), _stream(A.device), PATHS[path]))
+    if isinstance(workspace, str):
+        nbytes = int(load().tq_gemm_workspace_bytes(M, N, K, dt, PATHS[path]))
+        workspace = torch.empty((nbytes,), dtype=torch.uint8, device=A.device) if nbytes else None
+    ws_bytes = 0
+    if workspace is not None:
+        _need_cuda(workspace)
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _check("tq_gemm", load().tq_gemm_ws(_ptr(A), dt, M, N, K, _ptr(codes), _ptr(scale), _ptr(bias), _ptr(C),
+                                         _ptr(workspace), ws_bytes, _stream(A.device), PATHS[path]))
     return C
 
 

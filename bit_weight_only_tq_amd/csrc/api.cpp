@@ -18,8 +18,9 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 // Dispatcher thresholds on M (activation rows).  Decode-sized M is bound by
 // streaming the packed weights; large M is a dense contraction for the matrix
-// cores.
+// cores; in between, 64-row tiles with K split across workgroups.
 constexpr int64_t kGemvMaxM = tq::kGemvMaxM;
+constexpr int64_t kMediumMaxM = 256;  // M < 256: medium path
 
 // Device status word for the synchronous prepare calls.
 struct StatusWord {
@@ -78,7 +79,15 @@ tq_path tq_select_path(int format, int64_t M, int64_t N, int64_t K, tq_dtype dt)
     (void)N; (void)K; (void)dt;
     if (M <= kGemvMaxM) return TQ_PATH_GEMV;
     if (format == 1) return TQ_PATH_GEMV;  // W4A16: small-M kernel over blocks of rows
+    if (M < kMediumMaxM) return TQ_PATH_STREAM_MFMA;
     return TQ_PATH_GEMM;
+}
+
+size_t tq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, tq_dtype dt, tq_path path) {
+    if (M <= 0 || N <= 0 || K <= 0 || K % 64 != 0) return 0;
+    if (path == TQ_PATH_AUTO) path = tq_select_path(0, M, N, K, dt);
+    if (path != TQ_PATH_STREAM_MFMA) return 0;
+    return tq::medium_m_workspace_bytes(M, N, K, tq::compute_units());
 }
 
 // ---------------------------------------------------------------- prepare
@@ -152,12 +161,14 @@ tq_status w4a16_unpack(const int32_t* qweight, const uint16_t* scales_f16, int64
 
 // ------------------------------------------------------------------ apply
 
-tq_status tq_gemm_ex(const void* A, tq_dtype dt, int64_t M, int64_t N, int64_t K, const uint8_t* codes,
-                     const uint16_t* scale_f16, const void* bias, void* C, hipStream_t stream, tq_path path) {
+tq_status tq_gemm_ws(const void* A, tq_dtype dt, int64_t M, int64_t N, int64_t K, const uint8_t* codes,
+                     const uint16_t* scale_f16, const void* bias, void* C, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream, tq_path path) {
     tq_status r = check_gemm_common(A, dt, M, N, K, codes, scale_f16, C);
     if (r != TQ_OK) return r;
     if (K % 64 != 0) return TQ_ERR_SHAPE;
     if (bias && (reinterpret_cast<uintptr_t>(bias) & 1u)) return TQ_ERR_ALIGN;
+    if (workspace && !aligned16(workspace)) return TQ_ERR_ALIGN;
     if (path == TQ_PATH_AUTO) path = tq_select_path(0, M, N, K, dt);
     tq::GemmArgs a{static_cast<const uint16_t*>(A), dt == TQ_BF16 ? 1 : 0, M, N, K, codes, scale_f16,
                    static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(C)};
@@ -165,6 +176,9 @@ tq_status tq_gemm_ex(const void* A, tq_dtype dt, int64_t M, int64_t N, int64_t K
         case TQ_PATH_GEMV:
             if (M > kGemvMaxM) return TQ_ERR_PATH;
             return from_hip(tq::launch_ternary_gemv(a, stream));
+        case TQ_PATH_STREAM_MFMA:
+            return from_hip(tq::launch_ternary_medium(a, workspace, workspace ? workspace_bytes : 0,
+                                                      tq::compute_units(), stream));
         case TQ_PATH_GEMM:
             return from_hip(tq::launch_ternary_gemm(a, stream));
         default:
@@ -172,9 +186,14 @@ tq_status tq_gemm_ex(const void* A, tq_dtype dt, int64_t M, int64_t N, int64_t K
     }
 }
 
+tq_status tq_gemm_ex(const void* A, tq_dtype dt, int64_t M, int64_t N, int64_t K, const uint8_t* codes,
+                     const uint16_t* scale_f16, const void* bias, void* C, hipStream_t stream, tq_path path) {
+    return tq_gemm_ws(A, dt, M, N, K, codes, scale_f16, bias, C, nullptr, 0, stream, path);
+}
+
 tq_status tq_gemm(const void* A, tq_dtype dt, int64_t M, int64_t N, int64_t K, const uint8_t* codes,
                   const uint16_t* scale_f16, const void* bias, void* C, hipStream_t stream) {
-    return tq_gemm_ex(A, dt, M, N, K, codes, scale_f16, bias, C, stream, TQ_PATH_AUTO);
+    return tq_gemm_ws(A, dt, M, N, K, codes, scale_f16, bias, C, nullptr, 0, stream, TQ_PATH_AUTO);
 }
 
 tq_status w4a16_gemm_ex(const void* A, tq_dtype dt, int64_t M, int64_t N, int64_t K, const int32_t* qweight,

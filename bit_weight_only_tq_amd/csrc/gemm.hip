@@ -49,6 +49,25 @@ template <> struct Mfma<BF16> {
     static constexpr uint32_t kOnePair = 0x3F803F80u;
 };
 
+// 16 bytes per lane, global -> LDS at M0 + 16 * lane (M0 must be wave-uniform).
+// Issued through asm so that the compiler does not model the LDS write: its
+// conservative tracking would otherwise wait for every DMA in flight before
+// any LDS read, defeating the prefetch.  The kernel orders the DMA itself:
+// explicit vmcnt waits before the barrier that publishes a stage, and the
+// "memory" clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_addr) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :: "v"(gptr), "s"(lds_addr) : "memory", "m0");
+}
+
+// Bare workgroup barrier: __syncthreads() would add a release fence that
+// waits for every outstanding DMA, including the stage issued ahead.
+__device__ __forceinline__ void stage_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // ------------------------------------------------------------------------
 // v3 (K % 64 == 0): all global traffic is DMA (global_load_lds_dwordx4, no
 // registers) into a 3-stage LDS ring issued two K-steps ahead:
@@ -81,25 +100,6 @@ constexpr int kEpiRows = 32;
 constexpr int kEpiBytesPerWave = kEpiRows * kEpiLd * 2;
 constexpr size_t kLdsBytes = (size_t)kStages * kStageBytes;
 static_assert(8 * kEpiBytesPerWave + BM * 4 <= (int)kLdsBytes, "epilogue staging must fit in the ring");
-
-// 16 bytes per lane, global -> LDS at M0 + 16 * lane (M0 must be wave-uniform).
-// Issued through asm so that the compiler does not model the LDS write: its
-// conservative tracking would otherwise wait for every DMA in flight before
-// any LDS read, defeating the prefetch.  The kernel orders the DMA itself:
-// explicit vmcnt waits before the barrier that publishes a stage, and the
-// "memory" clobber keeps the compiler from moving LDS accesses across it.
-__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_addr) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                 :: "v"(gptr), "s"(lds_addr) : "memory", "m0");
-}
-
-// Bare workgroup barrier: __syncthreads() would add a release fence that
-// waits for every outstanding DMA, including the stage issued ahead.
-__device__ __forceinline__ void stage_barrier() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
 
 template <class T>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
@@ -284,6 +284,220 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
 
 }  // namespace v3
 
+// ------------------------------------------------------------------------
+// Medium M (17 .. 255 activation rows): 16TM x 256 tiles (TM m-tiles of 16
+// rows, 256 weight rows) fed by the same DMA ring and register unpack as v3,
+// but six stages deep (five K-steps in flight), so that a single workgroup
+// per compute unit keeps enough loads outstanding.  Wave w computes all
+// 16TM rows x columns 32w .. 32w+31.  With few row tiles the grid is also
+// split along K: split z of S covers K-steps [z*nk/S, (z+1)*nk/S) and
+// writes its fp32 partial (row-sum correction applied, no scale) to a
+// workspace [S][M][N]; splitk_reduce_kernel then sums the S partials of each
+// output in order z = 0 .. S-1 and applies the row scale and bias.  With
+// S = 1 the tile kernel finishes its outputs itself.
+namespace mm {
+
+constexpr int BN = 256;
+constexpr int BK = 64;
+constexpr int kThreads = 512;
+constexpr int TN = 2;
+constexpr int kStages = 6;
+constexpr int kAhead = kStages - 1;
+constexpr int kBBytes = BN * BK / 4;  // 4 KB of codes per stage
+template <int TM> constexpr int a_bytes() { return 16 * TM * BK * 2; }
+template <int TM> constexpr int stage_bytes() { return a_bytes<TM>() + kBBytes; }
+template <int TM> constexpr size_t lds_bytes() { return (size_t)kStages * stage_bytes<TM>() + 16 * TM * 4; }
+
+struct SplitArgs {
+    GemmArgs g;
+    float* ws;  // [S][M][N] fp32 partials, unused when S == 1
+    int S;
+};
+
+template <class T, int TM>
+__global__ __launch_bounds__(kThreads) void tile_kernel(SplitArgs sa) {
+    typedef typename Mfma<T>::vec vec;
+    constexpr int BM = 16 * TM;
+    constexpr int kABytes = a_bytes<TM>();
+    constexpr int kStageBytes = stage_bytes<TM>();
+    const GemmArgs& p = sa.g;
+    extern __shared__ uint4 smem_mm[];
+    uint8_t* lds = reinterpret_cast<uint8_t*>(smem_mm);
+    const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)smem_mm;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4;
+    const int i16 = lane & 15;
+    const int64_t n0 = (int64_t)blockIdx.x * BN;
+    const int64_t m0 = (int64_t)blockIdx.y * BM;
+    const int z = blockIdx.z;
+    const int64_t M = p.M, N = p.N, K = p.K;
+    const int64_t rb = K / 4;
+    const int nk = (int)(K / BK);
+    const int ks0 = (int)((int64_t)nk * z / sa.S);
+    const int ks1 = (int)((int64_t)nk * (z + 1) / sa.S);  // > ks0: S <= nk
+    const uint32_t magic_v = vgpr_const<Mfma<T>::kMagicPair>();
+    const uint32_t mask3 = sgpr_const<0x00030003u>();
+    const uint32_t mask33 = sgpr_const<0x33333333u>();
+
+    // Activation DMA: waves 0 .. 2TM-1 fill the 1-KB blocks of a stage (8 rows
+    // each); lane l lands at chunk l % 8 of row 8w + l / 8 and fetches global
+    // chunk (l % 8) ^ (l / 8) of it.  Rows past M re-read row M-1.
+    const bool a_issuer = wave < 2 * TM;
+    uint32_t a_off;
+    {
+        int64_t r = 8 * (wave % (2 * TM)) + (lane >> 3);
+        if (m0 + r >= M) r = M - 1 - m0;
+        a_off = (uint32_t)(r * K + 8 * ((lane & 7) ^ (lane >> 3)));
+    }
+    const uint16_t* a_blk = p.A + m0 * K;
+    // Code DMA (waves 0..3): lane l of wave w fetches 16 bytes of weight row
+    // n0 + 64w + l.  Rows past N re-read row N-1.
+    const bool b_issuer = wave < 4;
+    const uint8_t* b_blk = static_cast<const uint8_t*>(p.wq) + n0 * rb;
+    uint32_t b_off;
+    {
+        int64_t n = 64 * (wave & 3) + lane;
+        if (n0 + n >= N) n = N - 1 - n0;
+        b_off = (uint32_t)(n * rb);
+    }
+    auto issue = [&](int kstep, int stage) {
+        const int64_t k0 = (int64_t)kstep * BK;
+        if (a_issuer) dma16(a_blk + k0 + a_off, lds_base + (uint32_t)(stage * kStageBytes + 1024 * wave));
+        if (b_issuer) dma16(b_blk + k0 / 4 + b_off, lds_base + (uint32_t)(stage * kStageBytes + kABytes + 1024 * wave));
+    };
+    // the oldest stage in flight has landed: at most kAhead - 1 stages of
+    // this wave's DMAs remain outstanding
+    const int per_stage = (a_issuer ? 1 : 0) + (b_issuer ? 1 : 0);
+    auto wait_oldest = [&]() {
+        if (per_stage == 2) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+        else if (per_stage == 1) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    };
+    static_assert(kAhead == 5, "wait counts above assume five K-steps in flight");
+
+    f32x4 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float rsum = 0.0f;  // row sums of m-tile (wave % TM), kept by waves 0 .. TM-1
+    const int rs_tile = wave % TM;
+    const int swz = i16 & 7;
+    const int frag_base = i16 * (BK * 2);
+    const int b_frag = kABytes + (32 * wave + i16) * 16 + 4 * g;
+
+#pragma unroll
+    for (int u = 0; u < kAhead; ++u) issue(ks0 + u < ks1 ? ks0 + u : ks1 - 1, u);
+    wait_oldest();
+    stage_barrier();
+    for (int kt = ks0; kt < ks1; ++kt) {
+        const int it = kt - ks0;
+        const int stage = it % kStages;
+        issue(kt + kAhead < ks1 ? kt + kAhead : ks1 - 1, (it + kAhead) % kStages);
+        const uint8_t* sbase = lds + stage * kStageBytes;
+        uint32_t E[TN], O[TN];
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const uint32_t x = *reinterpret_cast<const uint32_t*>(sbase + b_frag + 16 * 16 * j);
+            E[j] = x & mask33;
+            O[j] = (x >> 2) & mask33;
+        }
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const int chunk = (2 * g + s) ^ swz;
+            vec af[TM];
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+                af[i] = __builtin_bit_cast(vec, *reinterpret_cast<const uint4*>(sbase + frag_base + i * 16 * (BK * 2) + 16 * chunk));
+            uint4 bop[TN];
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const uint32_t y = __builtin_amdgcn_perm(O[j], E[j], s ? 0x07060302u : 0x05040100u);
+                bop[j] = make_uint4((y & mask3) | magic_v, ((y >> 4) & mask3) | magic_v,
+                                    ((y >> 8) & mask3) | magic_v, ((y >> 12) & mask3) | magic_v);
+            }
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                if (i == rs_tile) {  // wave-uniform
+                    const uint4 v = __builtin_bit_cast(uint4, af[i]);
+                    rsum = Mfma<T>::dot2(v.x, Mfma<T>::kOnePair, rsum);
+                    rsum = Mfma<T>::dot2(v.y, Mfma<T>::kOnePair, rsum);
+                    rsum = Mfma<T>::dot2(v.z, Mfma<T>::kOnePair, rsum);
+                    rsum = Mfma<T>::dot2(v.w, Mfma<T>::kOnePair, rsum);
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const vec bf = __builtin_bit_cast(vec, bop[j]);
+#pragma unroll
+                for (int i = 0; i < TM; ++i) acc[i][j] = Mfma<T>::mma(af[i], bf, acc[i][j]);
+            }
+        }
+        wait_oldest();      // stage of K-step kt + 1 has landed
+        stage_barrier();    // ... for every wave, and nobody reads stage kt any more
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+
+    float* rs_lds = reinterpret_cast<float*>(lds + kStages * kStageBytes);
+    {
+        float r = rsum;
+        r += __shfl_xor(r, 16, kWave);
+        r += __shfl_xor(r, 32, kWave);
+        if (wave < TM && g == 0) rs_lds[16 * wave + i16] = r;
+    }
+    __syncthreads();
+
+    const bool final_out = sa.S == 1;
+    float sc[TN], bi[TN];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+        const int64_t n = n0 + 32 * wave + 16 * j + i16;
+        const int64_t nc = n < N ? n : N - 1;
+        sc[j] = f16_bits_to_f32(p.scale[nc]);
+        bi[j] = p.bias ? T::to_f32(p.bias[nc]) : 0.0f;
+    }
+    float* wsz = final_out ? nullptr : sa.ws + (int64_t)z * M * N;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = 16 * i + 4 * g + r;
+            const int64_t m = m0 + row;
+            if (m >= M) continue;
+            const float corr = Mfma<T>::kBias * rs_lds[row];
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const int64_t n = n0 + 32 * wave + 16 * j + i16;
+                if (n >= N) continue;
+                const float v = acc[i][j][r] - corr;
+                if (final_out) p.C[m * N + n] = T::from_f32_fast(v * sc[j] + bi[j]);
+                else wsz[m * N + n] = v;
+            }
+        }
+    }
+}
+
+// C[m, n] = (sum over z of ws[z][m][n]) * scale[n] + bias[n]; grid (ceil(N/256), M).
+template <class T>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(SplitArgs sa) {
+    const GemmArgs& p = sa.g;
+    const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t m = blockIdx.y;
+    if (n >= p.N) return;
+    const int64_t MN = p.M * p.N;
+    const float* src = sa.ws + m * p.N + n;
+    float s = 0.0f;
+    for (int z = 0; z < sa.S; ++z) s += src[z * MN];
+    const float sc = f16_bits_to_f32(p.scale[n]);
+    const float b = p.bias ? T::to_f32(p.bias[n]) : 0.0f;
+    p.C[m * p.N + n] = T::from_f32_fast(s * sc + b);
+}
+
+}  // namespace mm
+
 
 }  // namespace
 
@@ -300,6 +514,52 @@ static hipError_t launch_v3(const GemmArgs& a, hipStream_t s) {
 hipError_t launch_ternary_gemm(const GemmArgs& a, hipStream_t s) {
     // the C ABI guarantees K % 64 == 0 (whole 16-byte code chunks per row)
     return a.bf16 ? launch_v3<BF16>(a, s) : launch_v3<F16>(a, s);
+}
+
+// Split count of the medium-M kernel: none when the row x column tiles
+// already cover three quarters of the compute units, else enough splits to
+// give every compute unit a workgroup, each split keeping >= 8 K-steps.
+int medium_m_splits(int64_t M, int64_t N, int64_t K, int compute_units) {
+    const int64_t tm = M <= 32 ? 2 : 4;
+    const int64_t tiles = ((N + mm::BN - 1) / mm::BN) * ((M + 16 * tm - 1) / (16 * tm));
+    if (4 * tiles >= 3 * (int64_t)compute_units) return 1;
+    int64_t S = ((int64_t)compute_units + tiles - 1) / tiles;
+    const int64_t smax = (K / mm::BK) / 8;
+    if (S > smax) S = smax;
+    return S < 1 ? 1 : (int)S;
+}
+
+size_t medium_m_workspace_bytes(int64_t M, int64_t N, int64_t K, int compute_units) {
+    const int S = medium_m_splits(M, N, K, compute_units);
+    return S > 1 ? (size_t)S * (size_t)M * (size_t)N * sizeof(float) : 0;
+}
+
+template <class T, int TM>
+static hipError_t launch_mm(const mm::SplitArgs& sa, hipStream_t s) {
+    static DeviceFlags lds_limit_set;
+    hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(&mm::tile_kernel<T, TM>), (int)mm::lds_bytes<TM>(),
+                                   lds_limit_set);
+    if (e != hipSuccess) return e;
+    const GemmArgs& a = sa.g;
+    const dim3 grid((unsigned)((a.N + mm::BN - 1) / mm::BN), (unsigned)((a.M + 16 * TM - 1) / (16 * TM)), (unsigned)sa.S);
+    mm::tile_kernel<T, TM><<<grid, mm::kThreads, mm::lds_bytes<TM>(), s>>>(sa);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (sa.S > 1) {
+        mm::splitk_reduce_kernel<T><<<dim3((unsigned)((a.N + 255) / 256), (unsigned)a.M), 256, 0, s>>>(sa);
+        e = hipGetLastError();
+    }
+    return e;
+}
+
+// Medium M with an optional workspace: S splits when `workspace` holds
+// medium_m_workspace_bytes(), a single pass over K otherwise.
+hipError_t launch_ternary_medium(const GemmArgs& a, void* workspace, size_t workspace_bytes, int compute_units,
+                                 hipStream_t s) {
+    mm::SplitArgs sa{a, static_cast<float*>(workspace), medium_m_splits(a.M, a.N, a.K, compute_units)};
+    if (sa.S > 1 && (!workspace || workspace_bytes < medium_m_workspace_bytes(a.M, a.N, a.K, compute_units))) sa.S = 1;
+    const bool small = a.M <= 32;
+    if (a.bf16) return small ? launch_mm<BF16, 2>(sa, s) : launch_mm<BF16, 4>(sa, s);
+    return small ? launch_mm<F16, 2>(sa, s) : launch_mm<F16, 4>(sa, s);
 }
 
 // W4A16 at large M: run the small-M kernel on successive blocks of 16

@@ -763,7 +763,7 @@ struct StreamPlan {
     size_t lds;
 };
 
-static int compute_units() {
+int compute_units() {
     static std::atomic<int> cached[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;

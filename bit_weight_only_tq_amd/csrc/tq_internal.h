@@ -59,6 +59,14 @@ hipError_t launch_w4_gemv(const GemmArgs& a, hipStream_t s);
 
 // gemm.hip: LDS-tiled matrix-core GEMM, any M.
 hipError_t launch_ternary_gemm(const GemmArgs& a, hipStream_t s);
+// gemm.hip: medium M (64-row tiles, K split across workgroups when the
+// workspace allows; see medium_m_workspace_bytes).
+int medium_m_splits(int64_t M, int64_t N, int64_t K, int compute_units);
+size_t medium_m_workspace_bytes(int64_t M, int64_t N, int64_t K, int compute_units);
+hipError_t launch_ternary_medium(const GemmArgs& a, void* workspace, size_t workspace_bytes, int compute_units,
+                                 hipStream_t s);
+// Compute units of the current device (cached per device ordinal).
+int compute_units();
 hipError_t launch_w4_gemm(const GemmArgs& a, hipStream_t s);
 
 }  // namespace tq

@@ -37,11 +37,12 @@
  *    and report data errors (TQ_ERR_NONFINITE, TQ_ERR_RANGE,
  *    TQ_ERR_BAD_CODE).  They allocate a small device status word for the
  *    duration of the call.
- *  - Apply calls (tq_gemm, w4a16_gemm) are ASYNCHRONOUS on `stream`,
- *    allocate nothing, never synchronize and are safe to capture in a HIP
- *    graph.  Faults during execution surface at the caller's next sync.
- *  - All results are deterministic: no atomics, no split-K races; the same
- *    inputs and path give bit-identical outputs.
+ *  - Apply calls (tq_gemm, tq_gemm_ws, w4a16_gemm) are ASYNCHRONOUS on
+ *    `stream`, allocate nothing, never synchronize and are safe to capture in
+ *    a HIP graph.  Faults during execution surface at the caller's next sync.
+ *  - All results are deterministic: no atomics; where K is split across
+ *    workgroups the partial sums are added in a fixed order.  The same
+ *    inputs, path and workspace size give bit-identical outputs.
  */
 #ifndef TQ_H
 #define TQ_H
@@ -53,7 +54,7 @@
 extern "C" {
 #endif
 
-#define TQ_ABI_VERSION 1
+#define TQ_ABI_VERSION 2
 
 typedef enum tq_status {
     TQ_OK = 0,
@@ -78,7 +79,7 @@ typedef enum tq_dtype {
 typedef enum tq_path {
     TQ_PATH_AUTO = 0,        /* let the dispatcher choose */
     TQ_PATH_GEMV = 1,        /* small M: weight-streaming kernel, codes read once per call */
-    TQ_PATH_STREAM_MFMA = 2, /* medium M: weight-streaming kernel with matrix-core MACs */
+    TQ_PATH_STREAM_MFMA = 2, /* medium M: 64-row tiles, K split across workgroups */
     TQ_PATH_GEMM = 3         /* large M: LDS-tiled matrix-core GEMM (prefill) */
 } tq_path;
 
@@ -166,6 +167,37 @@ tq_status tq_gemm_ex(const void* A, tq_dtype dt, int64_t M, int64_t N, int64_t K
                      void* C, hipStream_t stream, tq_path path);
 
 /*
+ * tq_gemm_ws - tq_gemm with a caller-owned workspace and a path choice.
+ *   workspace        device buffer (16-byte aligned) of workspace_bytes
+ *                    bytes, or NULL; the call may overwrite all of it and
+ *                    the caller must not touch it until the work on
+ *                    `stream` is done.  Calls that may overlap must use
+ *                    different workspaces.
+ *   workspace_bytes  at least tq_gemm_workspace_bytes(M, N, K, dt, path)
+ *                    for the split-K schedule of TQ_PATH_STREAM_MFMA; with
+ *                    less (or NULL) that path runs one workgroup per output
+ *                    tile over all of K - correct, slower.
+ *   path             TQ_PATH_AUTO or a forced kernel family (TQ_ERR_PATH if
+ *                    it cannot run the shape: TQ_PATH_GEMV needs M <= 16).
+ * With S > 1 splits the medium path writes S fp32 partials [S][M][N] into the
+ * workspace and a second kernel sums them in order z = 0 .. S-1.  Other
+ * arguments, results and errors as tq_gemm; TQ_ERR_ALIGN for a misaligned
+ * workspace.  Asynchronous; allocates nothing; graph-capturable.
+ */
+tq_status tq_gemm_ws(const void* A, tq_dtype dt, int64_t M, int64_t N, int64_t K,
+                     const uint8_t* codes, const uint16_t* scale_f16, const void* bias,
+                     void* C, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream, tq_path path);
+
+/*
+ * tq_gemm_workspace_bytes - workspace tq_gemm_ws needs for its fastest
+ * schedule of this shape on the current device (0 when none is used).
+ * Depends on the device's compute-unit count; query on the device that will
+ * run the call.
+ */
+size_t tq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, tq_dtype dt, tq_path path);
+
+/*
  * w4a16_gemm - C = A * dequant(qweight, scales)^T (+ bias), fp32 accumulation.
  *   qweight [N, K/8] int32 and scales_f16 [N, K/128] as written by
  *   w4a16_pack; group_size must be 128; K % 128 == 0.
@@ -186,11 +218,12 @@ tq_status w4a16_gemm_ex(const void* A, tq_dtype dt, int64_t M, int64_t N, int64_
 
 /*
  * tq_select_path - the dispatcher's choice for a shape (never TQ_PATH_AUTO).
- *   format: 0 = ternary, 1 = W4A16.  Decode-sized M streams the weights
- *   (they dominate the bytes moved); prefill-sized M is a dense contraction
- *   for the matrix cores (the decode / prefill split of the quantization
- *   decision tree on page "10.6 Quantization choice and vLLM in practice",
- *   section 10.6.1).
+ *   format: 0 = ternary, 1 = W4A16.  Decode-sized M (<= 16) streams the
+ *   weights (they dominate the bytes moved); prefill-sized M (>= 256) is a
+ *   dense contraction for the matrix cores (the decode / prefill split of
+ *   the quantization decision tree on page "10.6 Quantization choice and vLLM
+ *   in practice", section 10.6.1); ternary M in 17 .. 255 takes the medium
+ *   path, 64-row tiles with K split across workgroups.
  */
 tq_path tq_select_path(int format, int64_t M, int64_t N, int64_t K, tq_dtype dt);
 

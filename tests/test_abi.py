@@ -44,9 +44,9 @@ def test_binding_declares_nothing_extra():
 
 
 def test_version_and_status_strings(lib):
-    assert lib.tq_abi_version() == 1
+    assert lib.tq_abi_version() == 2
     src = open(HEADER).read()
-    assert "#define TQ_ABI_VERSION 1" in src
+    assert "#define TQ_ABI_VERSION 2" in src
     for code, name in _lib.STATUS_NAMES.items():
         assert re.search(rf"\b{name}\s*=\s*{code}\b", src), name
         s = lib.tq_status_str(code)
@@ -59,8 +59,24 @@ def test_dispatcher_by_m():
     for M in (1, 4, 16):
         assert sel("ternary", M, 4096, 4096) == "gemv"
         assert sel("w4a16", M, 4096, 4096) == "gemv"
-    for M in (2048, 4096, 8192):
+    for M in (17, 32, 64, 255):
+        assert sel("ternary", M, 8192, 8192) == "stream_mfma"
+        assert sel("w4a16", M, 8192, 8192) == "gemv"
+    for M in (256, 2048, 4096, 8192):
         assert sel("ternary", M, 14336, 4096, "bf16") == "gemm"
+
+
+def test_workspace_query():
+    """Split-K workspace of the medium path: S fp32 partials of [M, N], none
+    for the other paths or when the row x column tiles fill the device.  Off
+    the GPU the compute-unit count defaults to 256."""
+    wb = _lib.tq_gemm_workspace_bytes
+    assert wb(1, 4096, 4096) == 0 and wb(4096, 4096, 4096) == 0
+    assert wb(64, 8192, 8192) == 8 * 64 * 8192 * 4      # 32 tiles -> 8 splits
+    assert wb(32, 1024, 8192) == 16 * 32 * 1024 * 4     # capped at 8 K-steps per split
+    assert wb(64, 57344, 8192) == 0                     # 224 tiles: no split
+    assert wb(64, 8192, 8192, path="gemm") == 0
+    assert wb(64, 8192, 96) == 0                        # K % 64 != 0
 
 
 V = ctypes.c_void_p
@@ -84,6 +100,16 @@ MIS = V(0x10002)           # 2-byte aligned only
 ])
 def test_tq_gemm_host_checks(lib, args, want):
     assert _lib.STATUS_NAMES[lib.tq_gemm(*args)] == want
+
+
+def test_tq_gemm_ws_host_checks(lib):
+    name = _lib.STATUS_NAMES
+    st = lib.tq_gemm_ws(FAKE, 0, 32, 64, 64, FAKE, FAKE, None, FAKE, MIS, 1024, None, 0)
+    assert name[st] == "TQ_ERR_ALIGN"
+    st = lib.tq_gemm_ws(FAKE, 0, 32, 64, 64, FAKE, FAKE, None, FAKE, None, 0, None, 1)
+    assert name[st] == "TQ_ERR_PATH"
+    st = lib.tq_gemm_ws(None, 0, 32, 64, 64, FAKE, FAKE, None, FAKE, None, 0, None, 0)
+    assert name[st] == "TQ_ERR_NULL"
 
 
 def test_tq_gemm_ex_bad_path(lib):

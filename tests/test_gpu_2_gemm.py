@@ -127,10 +127,10 @@ def test_ternary_prefill_sampled(N, K, M, dt):
     # last workgroup, and a last wave with fewer chunk-sets than the others
     (3, 4200, 1024), (5, 16400, 2048), (4, 50, 4352), (6, 8300, 4352), (2, 8300, 4352),
 ])
-@pytest.mark.parametrize("path", ["gemv", "gemm"])
+@pytest.mark.parametrize("path", ["gemv", "stream_mfma", "gemm"])
 @pytest.mark.parametrize("dt", ["f16", "bf16"])
 def test_ternary_ragged(M, N, K, path, dt):
-    """Tiles with ragged edges in M and N, several K steps, both kernel families."""
+    """Tiles with ragged edges in M and N, several K steps, every kernel family."""
     import torch
     import bit_weight_only_tq_amd as tq
     dev = require_gpu()
@@ -144,7 +144,7 @@ def test_ternary_ragged(M, N, K, path, dt):
     check_close(C, A, wdq, bias=bias, label=f"ragged {M}x{N}x{K} {path} {dt}")
 
 
-@pytest.mark.parametrize("path", ["gemv", "gemm"])
+@pytest.mark.parametrize("path", ["gemv", "stream_mfma", "gemm"])
 @pytest.mark.parametrize("dt", ["f16", "bf16"])
 def test_one_hot_bit_exact(path, dt):
     """A = rows of the identity: C[m, n] = wdq[n, k_m] exactly (one rounding of
@@ -155,7 +155,7 @@ def test_one_hot_bit_exact(path, dt):
     N, K = 300, 256
     log(f"one-hot {path} {dt}")
     codes, scale, rc, rs, wdq = _ternary(N, K, dev)
-    ks = [0, 1, 2, 3, 4, 7, 8, 15, 16, 63, 64, 127, 200, 255] if path == "gemm" else [0, 5, 9, 255]
+    ks = [0, 5, 9, 255] if path == "gemv" else [0, 1, 2, 3, 4, 7, 8, 15, 16, 63, 64, 127, 200, 255]
     M = len(ks)
     A = torch.zeros((M, K), dtype=torch.float16 if dt == "f16" else torch.bfloat16)
     for m, k in enumerate(ks):
@@ -166,7 +166,8 @@ def test_one_hot_bit_exact(path, dt):
     np.testing.assert_array_equal(bits16(C), want_bits)
 
 
-@pytest.mark.parametrize("path,M", [("gemv", 1), ("gemv", 16), ("gemm", 300)])
+@pytest.mark.parametrize("path,M", [("gemv", 1), ("gemv", 16), ("stream_mfma", 40), ("stream_mfma", 100),
+                                    ("gemm", 300)])
 def test_deterministic_and_canary(path, M):
     """Two runs give bit-identical outputs; the bytes after C stay untouched."""
     import torch
@@ -183,6 +184,31 @@ def test_deterministic_and_canary(path, M):
     torch.cuda.synchronize()
     assert torch.equal(C1.view(torch.int16), C2.view(torch.int16))
     assert bool((buf[M * N:] == -12345.0).all())
+
+
+@pytest.mark.parametrize("M,N,K", [(17, 8192, 8192), (64, 1024, 8192), (32, 8192, 28672), (100, 2000, 4096)])
+def test_medium_split_k(M, N, K):
+    """Medium M with K split across workgroups (workspace from torch) and
+    without a workspace (one pass over K): both within the tolerance, on
+    sampled output columns at full 70B-like sizes."""
+    import torch
+    import bit_weight_only_tq_amd as tq
+    dev = require_gpu()
+    nbytes = tq.tq_gemm_workspace_bytes(M, N, K, path="stream_mfma")
+    log(f"medium split-K M={M} N={N} K={K} workspace={nbytes}")
+    W = synth.weights_device(N, K, synth.seed_for("msk", N, K), dev)
+    codes, scale = tq.tq_pack(W)
+    cols = np.sort(np.random.default_rng(N + K).choice(N, min(N, 192), replace=False))
+    idx = torch.from_numpy(cols).to(dev)
+    rc, rs = OT.ternary_pack(W.index_select(0, idx).cpu().numpy())
+    del W
+    wdq = OT.ternary_dequant(rc, rs, K)
+    A = synth.activations(M, K, synth.seed_for("mska", M, K), "f16")
+    bias = synth.activations(1, N, synth.seed_for("mskb", N), "f16")[0]
+    for ws in ("auto", None):
+        C = tq.tq_gemm(A.to(dev), codes, scale, bias=bias.to(dev), path="stream_mfma", workspace=ws)
+        check_close(C.index_select(1, idx), A, wdq, bias=bias[torch.from_numpy(cols)],
+                    label=f"medium {M}x{N}x{K} ws={ws}")
 
 
 @pytest.mark.parametrize("M", [1, 40])

@@ -50,6 +50,6 @@ def test_ternary_70b(N, K, M):
     log(f"tq_gemm 70b N={N} K={K} M={M}")
     codes, scale, rows, wdq = _packed(N, K, dev)
     A = synth.activations(M, K, synth.seed_for("a70b", N, K, M), "f16")
-    assert tq.tq_select_path("ternary", M, N, K) == ("gemv" if M <= 16 else "gemm")
+    assert tq.tq_select_path("ternary", M, N, K) == ("gemv" if M <= 16 else "stream_mfma")
     C = tq.tq_gemm(A.to(dev), codes, scale)
     check_close(C.index_select(1, torch.from_numpy(rows).to(dev)), A, wdq, label=f"70b {N}x{K} M={M}")
