@@ -681,6 +681,142 @@ __global__ __launch_bounds__(1024) void ternary_gemv_stream_kernel(GemmArgs p) {
     }
 }
 
+// ------------------------------------------------------ W4A16, matrix cores
+//
+// fp16 activations, M <= 16, K % 128 == 0.  A code word x (int32) holds
+// nibbles q_0 .. q_7 (q_i at bits 4i: column 8j + i of word j).  Masking one
+// nibble of each 16-bit half into the mantissa of the fp16 constant 1024
+// (0x6400, unit in the last place 1) gives a pair of exact values in one
+// v_and_or_b32:
+//   (x & 0x000F000F) | magic = (1024 + q_0, 1024 + q_4),
+//   (x & 0x00F000F0) | magic = (1024 + 16 q_1, 1024 + 16 q_5),
+// and with y = x >> 8 the pairs (q_2, q_6) and (16 q_3, 16 q_7) the same way.
+// The activations are paired to match - (a_0, a_4), (a_1, a_5) / 16, (a_2,
+// a_6), (a_3, a_7) / 16 - so one MFMA contracts one word of each of 16 rows:
+//   sum a' (1024 + 16^s q) = sum a q + sum a' 1024.
+// The weight value is q - 8 (zero point 8), so a group's sum is that minus
+// sum a' (1024 + 8 * 16^s), which is the same for every weight row: MFMAs of
+// the group's activation operand against that constant pattern, negated,
+// give every group accumulator its starting value.  The group scale
+// s[n, g] then multiplies the group's fp32 sum (page "Model quantization -
+// vLLM runtime quantization architecture", section 5: group_size 128).
+//
+// Work split: a block owns 16R weight rows and all of K; its W waves take
+// every W-th 128-column group.  Lane l = 16h + i loads 16 bytes (32 codes,
+// group columns 32h .. 32h+31) of row i of each row block, the row scales,
+// and the 32 activations of row m = i at those columns; MFMA d contracts
+// code word d of every lane.  The next group's loads are issued before the
+// current group is contracted.  Wave partials meet in LDS and are summed in
+// a fixed order.
+constexpr uint32_t kW4Neg0 = 0xE408E408u;  // -(1024 + 8), both halves
+constexpr uint32_t kW4Neg1 = 0xE480E480u;  // -(1024 + 128), both halves
+
+template <int R, int W>
+__global__ __launch_bounds__(W * kWave) void w4_gemv_mfma_kernel(GemmArgs p) {
+    __shared__ f32x4 red[W][R][kWave];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x >> 6;
+    const int h = lane >> 4;
+    const int i16 = lane & 15;
+    const int64_t N = p.N, K = p.K;
+    const int M = (int)p.M;
+    const int G = (int)(K / 128);
+    const int64_t rowb = K / 2;         // code bytes per row
+    const int64_t n_base = (int64_t)blockIdx.x * (16 * R);
+    const uint8_t* codes = static_cast<const uint8_t*>(p.wq);
+    const bool a_live = i16 < M;
+    const uint16_t* arow = p.A + (int64_t)(a_live ? i16 : 0) * K;
+
+    const uint8_t* crow[R];
+    const uint16_t* srow[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        int64_t n = n_base + 16 * r + i16;
+        n = n < N ? n : N - 1;  // rows past N re-read row N-1; ignored
+        crow[r] = codes + n * rowb + 16 * h;
+        srow[r] = p.scale + n * G;
+    }
+    auto load = [&](int gi, uint4 (&q)[R], uint16_t (&sc)[R], uint4 (&av)[4]) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) q[r] = *reinterpret_cast<const uint4*>(crow[r] + (int64_t)gi * 64);
+#pragma unroll
+        for (int r = 0; r < R; ++r) sc[r] = srow[r][gi];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) av[e] = opaque_uint4();
+        if (a_live) {
+            const uint4* ap = reinterpret_cast<const uint4*>(arow + (int64_t)gi * 128 + 32 * h);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) av[e] = ap[e];
+        }
+    };
+
+    f32x4 acc[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const uint32_t magic_v = vgpr_const<kMagic2>();
+    const f16x2 sixteenth = f16x2{(_Float16)0.0625f, (_Float16)0.0625f};
+    const uint4 negp = make_uint4(kW4Neg0, kW4Neg1, kW4Neg0, kW4Neg1);
+
+    uint4 q[R], qn[R], av[4], avn[4];
+    uint16_t sc[R], scn[R];
+    int gi = wave;
+    if (gi < G) load(gi, q, sc, av);
+    for (; gi < G; gi += W) {
+        const int gn = gi + W < G ? gi + W : gi;  // past the end: re-read, unused
+        load(gn, qn, scn, avn);
+        // activation operands of the four code words, and the group's start
+        uint4 aop[4];
+        f32x4 dacc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            const uint4 v = av[d];  // columns 8d .. 8d+7 of this lane's 32
+            const uint32_t p0 = __builtin_amdgcn_perm(v.z, v.x, 0x05040100u);
+            const uint32_t p1 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(v.z, v.x, 0x07060302u)) * sixteenth);
+            const uint32_t p2 = __builtin_amdgcn_perm(v.w, v.y, 0x05040100u);
+            const uint32_t p3 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(v.w, v.y, 0x07060302u)) * sixteenth);
+            aop[d] = make_uint4(p0, p1, p2, p3);
+            dacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, aop[d]), __builtin_bit_cast(f16x8, negp), dacc, 0, 0, 0);
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            f32x4 ag = dacc;
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const uint32_t x = dword_of(q[r], d);
+                const uint32_t y = x >> 8;
+                const uint4 bw = make_uint4((x & sgpr_const<0x000F000Fu>()) | magic_v, (x & sgpr_const<0x00F000F0u>()) | magic_v,
+                                            (y & sgpr_const<0x000F000Fu>()) | magic_v, (y & sgpr_const<0x00F000F0u>()) | magic_v);
+                ag = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, aop[d]), __builtin_bit_cast(f16x8, bw), ag, 0, 0, 0);
+            }
+            const float s = f16_bits_to_f32(sc[r]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[r][i] = fmaf(s, ag[i], acc[r][i]);
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) { q[r] = qn[r]; sc[r] = scn[r]; }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) av[e] = avn[e];
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) red[wave][r][lane] = acc[r];
+    __syncthreads();
+    for (int e = threadIdx.x; e < R * kWave; e += W * kWave) {
+        const int r = e / kWave;
+        const int l = e % kWave;
+        f32x4 sum = red[0][r][l];
+#pragma unroll
+        for (int w = 1; w < W; ++w) sum += red[w][r][l];
+        const int64_t n = n_base + 16 * r + (l & 15);
+        if (n >= N) continue;
+        const float b = p.bias ? F16::to_f32(p.bias[n]) : 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int m = 4 * (l >> 4) + i;
+            if (m < M) p.C[(int64_t)m * N + n] = F16::from_f32(sum[i] + b);
+        }
+    }
+}
+
 // ------------------------------------------------------------- launchers
 
 template <int R, int W>
@@ -858,7 +994,36 @@ hipError_t launch_ternary_gemv_simple(const GemmArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
+template <int R, int W>
+static hipError_t launch_w4_mfma(const GemmArgs& a, hipStream_t s) {
+    const dim3 grid((unsigned)((a.N + 16 * R - 1) / (16 * R)));
+    w4_gemv_mfma_kernel<R, W><<<grid, W * kWave, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+// fp16, 3 <= M <= 16 (for M <= 2 the FMA kernel is faster: its loads are
+// all in flight at once, while this kernel prefetches one group ahead): W
+// waves over the K/128 groups (at most 16), two 16-row blocks per workgroup
+// while at least 512 workgroups remain.
+template <int R>
+static hipError_t launch_w4_mfma_w(const GemmArgs& a, hipStream_t s) {
+    const int64_t G = a.K / 128;
+    if (G >= 16) return launch_w4_mfma<R, 16>(a, s);
+    if (G >= 8) return launch_w4_mfma<R, 8>(a, s);
+    if (G >= 4) return launch_w4_mfma<R, 4>(a, s);
+    if (G >= 2) return launch_w4_mfma<R, 2>(a, s);
+    return launch_w4_mfma<R, 1>(a, s);
+}
+
 hipError_t launch_w4_gemv(const GemmArgs& a, hipStream_t s) {
+    if (!a.bf16 && a.M >= 3 && a.M <= kGemvMaxM) {
+        const int64_t nrb = (a.N + 15) / 16;
+        return nrb >= 1024 ? launch_w4_mfma_w<2>(a, s) : launch_w4_mfma_w<1>(a, s);
+    }
+    return launch_w4_gemv_simple(a, s);
+}
+
+hipError_t launch_w4_gemv_simple(const GemmArgs& a, hipStream_t s) {
     const dim3 grid((unsigned)((a.N + kGemvWaves - 1) / kGemvWaves));
     const dim3 block(kGemvWaves * kWave);
     if (a.M <= 1) {

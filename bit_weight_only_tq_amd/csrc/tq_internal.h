@@ -55,7 +55,8 @@ constexpr int kGemvMaxM = 16;
 hipError_t launch_ternary_gemv(const GemmArgs& a, hipStream_t s);         // picks the fastest eligible kernel
 hipError_t launch_ternary_gemv_simple(const GemmArgs& a, hipStream_t s);  // any dtype, any K % 64 == 0
 bool ternary_gemv_mfma_ok(const GemmArgs& a);                             // fp16, K % 256 == 0
-hipError_t launch_w4_gemv(const GemmArgs& a, hipStream_t s);
+hipError_t launch_w4_gemv(const GemmArgs& a, hipStream_t s);         // picks the fastest eligible kernel
+hipError_t launch_w4_gemv_simple(const GemmArgs& a, hipStream_t s);  // any dtype
 
 // gemm.hip: LDS-tiled matrix-core GEMM, any M.
 hipError_t launch_ternary_gemm(const GemmArgs& a, hipStream_t s);

@@ -211,6 +211,38 @@ def test_medium_split_k(M, N, K):
                     label=f"medium {M}x{N}x{K} ws={ws}")
 
 
+@pytest.mark.parametrize("M,N,K", [(1, 20, 128), (3, 37, 384), (16, 300, 1024), (5, 16400, 256),
+                                   (2, 64, 2048), (16, 17, 4096), (7, 1000, 14336)])
+def test_w4_ragged_shapes(M, N, K):
+    """W4A16 matrix-core kernel: one group per row (K = 128) up to 112, ragged
+    N, two 16-row blocks per workgroup (N > 16384), M up to 16, with bias."""
+    import bit_weight_only_tq_amd as tq
+    dev = require_gpu()
+    log(f"w4 ragged M={M} N={N} K={K}")
+    q, s, rq, rs, wdq = _w4(N, K, dev)
+    A = synth.activations(M, K, synth.seed_for("w4rs", M, N, K), "f16")
+    bias = synth.activations(1, N, synth.seed_for("w4rsb", N), "f16")[0]
+    C = tq.w4a16_gemm(A.to(dev), q, s, bias=bias.to(dev))
+    check_close(C, A, wdq, bias=bias, label=f"w4 ragged {M}x{N}x{K}")
+
+
+def test_w4_one_hot_bit_exact():
+    """A = rows of the identity: C[m, n] = wdq[n, k_m] exactly (the group's
+    value (q - 8) * s rounded once to fp16); pins nibble order and pairing."""
+    import torch
+    import bit_weight_only_tq_amd as tq
+    dev = require_gpu()
+    N, K = 300, 256
+    log("w4 one-hot")
+    q, s, rq, rs, wdq = _w4(N, K, dev)
+    ks = [0, 1, 2, 3, 4, 5, 6, 7, 8, 31, 32, 100, 127, 128, 200, 255]
+    A = torch.zeros((len(ks), K), dtype=torch.float16)
+    for m, k in enumerate(ks):
+        A[m, k] = 1.0
+    C = tq.w4a16_gemm(A.to(dev), q, s)
+    np.testing.assert_array_equal(bits16(C), OR.f16_bits(wdq[:, ks].T))
+
+
 @pytest.mark.parametrize("M", [1, 40])
 def test_w4_ragged_and_blocked(M):
     import torch
