@@ -23,12 +23,18 @@ Also reported in the same JSON line:
     codes (one seeded layer packed on the device, copied to 80 layers).
   * ``secondary``: the prefill GEMM at M = 4096 on the MLP shapes
     (14336 x 4096, 4096 x 14336), fp16 and bf16, TFLOP/s = 2MNK / time.
+  * ``w4a16_decode``: the Llama-3-8B decode step of the headline with
+    W4A16 weights (group 128) at M = 1, 4 and 16, GB/s of packed codes +
+    group scales.
+  * ``medium_m``: the medium-M path (K split across workgroups) on one
+    Llama-3-70B layer's four shapes at M = 32 and 64, eight resident copies
+    rotated so that every call streams its codes from HBM.
   * ``cpu_baseline``: the CPU oracle (fp64 dequant + fp64 product), untuned,
     timed on the host on a bounded sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--mode MODE]
-  --mode full (default) | decode | decode70b | prefill | calib (plain copy of
-  known size, for scaling hardware byte counters)
+  --mode full (default) | decode | decode70b | w4 | medium | prefill | calib
+  (plain copy of known size, for scaling hardware byte counters)
 """
 
 import argparse
@@ -55,7 +61,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--layers", type=int, default=32)
-    ap.add_argument("--mode", default="full", choices=["full", "decode", "decode70b", "prefill", "calib"])
+    ap.add_argument("--mode", default="full",
+                    choices=["full", "decode", "decode70b", "w4", "medium", "prefill", "calib"])
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
     ap.add_argument("--unfused", action="store_true", help="decode mode: q,k,v,gate,up as separate calls")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -161,6 +168,89 @@ def run_decode(args, dev, fused, graph, model="8b", layers=None, steps=None):
     del mats, xs, outs
     if graph:
         del g
+    torch.cuda.empty_cache()
+    return res
+
+
+def w4_bytes(M, N, K):
+    """Algorithmic bytes of one W4A16 call: codes + group scales + A + C."""
+    return N * K // 2 + 2 * N * (K // 128) + 2 * M * K + 2 * M * N
+
+
+def run_w4_decode(args, dev, Ms=(1, 4, 16)):
+    """Llama-3-8B decode step with W4A16 weights, fused layout, graph replay."""
+    import torch
+    import bit_weight_only_tq_amd as tq
+    import synth
+    stream = torch.cuda.current_stream()
+    mats = []
+    for layer in range(args.layers):
+        for name, (N, K) in layer_shapes(True):
+            W = synth.weights_device(N, K, synth.seed_for("benchw4", layer, name), dev)
+            q, sc = tq.w4a16_pack(W)
+            del W
+            mats.append((N, K, q, sc))
+    torch.cuda.synchronize()
+    packed = sum(m[2].numel() * 4 + m[3].numel() * 2 for m in mats)
+    res = {"metric": "HBM GB/s W4A16 GEMV, Llama-3-8B decode (32 layers, fused qkv / gate_up)",
+           "unit": "GB/s", "packed_bytes_per_step": packed, "launches_per_step": len(mats)}
+    for M in Ms:
+        xs = {K: synth.activations_device(M, K, synth.seed_for("benchw4x", K, M), "f16", dev) for K in {m[1] for m in mats}}
+        outs = [torch.empty((M, m[0]), dtype=torch.float16, device=dev) for m in mats]
+
+        def step():
+            for i, (N, K, q, sc) in enumerate(mats):
+                tq.w4a16_gemm(xs[K], q, sc, out=outs[i])
+
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            step()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            step()
+        for _ in range(args.warmup):
+            g.replay()
+        t = time_region(g.replay, args.steps, stream)
+        alg = sum(w4_bytes(M, m[0], m[1]) for m in mats)
+        res[f"M{M}"] = {"value": round(packed * args.steps / t / 1e9, 1), "ms_per_step": round(t / args.steps * 1e3, 4),
+                        "avg_launch_us": round(t / args.steps / len(mats) * 1e6, 3),
+                        "alg_gbs": round(alg * args.steps / t / 1e9, 1)}
+        del g, xs, outs
+    del mats
+    torch.cuda.empty_cache()
+    return res
+
+
+def run_medium(dev, copies=8, iters=16):
+    """Medium-M path on one Llama-3-70B layer at M = 32, 64 (split K)."""
+    import torch
+    import bit_weight_only_tq_amd as tq
+    import synth
+    stream = torch.cuda.current_stream()
+    res = {"metric": "ternary medium-M path (K split across workgroups), one Llama-3-70B layer",
+           "kernel": "mm::tile_kernel + mm::splitk_reduce_kernel"}
+    for name, (N, K) in layer_shapes(True, "70b"):
+        W = synth.weights_device(N, K, synth.seed_for("benchmm", name), dev)
+        codes, scale = tq.tq_pack(W)
+        del W
+        reps = [(codes, scale)] + [(codes.clone(), scale.clone()) for _ in range(copies - 1)]
+        for M in (32, 64):
+            A = synth.activations_device(M, K, synth.seed_for("benchmma", N, K, M), "f16", dev)
+            C = torch.empty((M, N), dtype=torch.float16, device=dev)
+            nbytes = tq.tq_gemm_workspace_bytes(M, N, K)
+            ws = torch.empty((max(nbytes, 16),), dtype=torch.uint8, device=dev)
+            calls = [lambda c=c, s_=s_: tq.tq_gemm(A, c, s_, out=C, workspace=ws) for c, s_ in reps]
+            for c in calls:
+                c()
+            t = time_region(lambda: [c() for c in calls], iters, stream) / (iters * copies)
+            res[f"{name}_{N}x{K}_M{M}"] = {"us": round(t * 1e6, 2), "tflops": round(2.0 * M * N * K / t / 1e12, 1),
+                                           "packed_gbs": round(codes.numel() / t / 1e9, 1),
+                                           "splits": nbytes // (4 * M * N) if nbytes else 1}
+            del A, C, ws
+        del reps, codes, scale
     torch.cuda.empty_cache()
     return res
 
@@ -291,6 +381,12 @@ def main():
     if args.mode == "decode70b":
         print(json.dumps({"decode_70b": run_decode_70b(args, dev)}), flush=True)
         return
+    if args.mode == "w4":
+        print(json.dumps({"w4a16_decode": run_w4_decode(args, dev)}), flush=True)
+        return
+    if args.mode == "medium":
+        print(json.dumps({"medium_m": run_medium(dev)}), flush=True)
+        return
 
     graph = not args.no_graph
     fused = not args.unfused
@@ -335,6 +431,10 @@ def main():
                                      "avg_launch_us": round(u["avg_launch_us"], 3)}
         log("decode, Llama-3-70B, 80 layers")
         out["decode_70b"] = run_decode_70b(args, dev)
+        log("W4A16 decode")
+        out["w4a16_decode"] = run_w4_decode(args, dev)
+        log("medium M")
+        out["medium_m"] = run_medium(dev)
         log("prefill GEMM M=4096")
         out["secondary"] = run_prefill(dev)
         if not args.no_cpu_baseline:
