@@ -850,8 +850,8 @@ struct GemvPlan {
 
 // Shape rule for the LDS kernel: the fewest chunk-sets per wave CSW in
 // {1, 2, 4, 8} (at least kGemvMinCsw) that keeps the block within 16 waves;
-// R 16-row blocks per workgroup, more for larger M (the activation prep is
-// shared by R times more rows) while at least 256 workgroups remain.
+// R 16-row blocks per workgroup (the activation prep is shared by R times
+// more rows).
 static bool gemv_lds_plan(const GemmArgs& a, GemvPlan* pl) {
     if (a.bf16 || a.M > 4 || a.K % 256 != 0 || a.M * a.K > kGemvLdsMaxMK) return false;
     const int64_t cs = a.K / 256;
@@ -862,7 +862,10 @@ static bool gemv_lds_plan(const GemmArgs& a, GemvPlan* pl) {
     pl->csw = c;
     pl->waves = (int)((cs + c - 1) / c);
     const int64_t nrb = (a.N + 15) / 16;
-    pl->rows16 = (a.M > 1 && c <= 4 && pl->waves >= 2 && nrb >= 512) ? 2 : 1;
+    // two 16-row blocks per workgroup: for M = 2 once 256 workgroups remain;
+    // for M = 1 only on very tall matrices (measured: slower at 1792
+    // row-blocks, faster at 3584)
+    pl->rows16 = (c <= 4 && pl->waves >= 2 && (a.M > 1 ? nrb >= 512 : nrb >= 3072)) ? 2 : 1;
     pl->upt = (int)((a.M * c + 3) / 4);  // <= 4: CSW = 8 only for K > 4096 * 4, where M * K <= 28672 keeps M = 1
     pl->lds = gemv_lds_bytes(a.M, c, pl->waves, pl->rows16);
     return pl->lds <= (size_t)kGemvLdsMaxBytes;

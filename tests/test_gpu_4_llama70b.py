@@ -16,6 +16,8 @@ from gpu_common import bits16, check_close, log, require_gpu
 pytestmark = pytest.mark.gpu
 
 SHAPES_70B = [(8192, 8192), (1024, 8192), (28672, 8192), (8192, 28672)]
+# the stacked layouts the decode benchmark runs: q,k,v and gate,up along N
+FUSED_70B = [(10240, 8192), (57344, 8192)]
 SAMPLE_ROWS = 256
 _CACHE = {}
 
@@ -53,3 +55,16 @@ def test_ternary_70b(N, K, M):
     assert tq.tq_select_path("ternary", M, N, K) == ("gemv" if M <= 16 else "stream_mfma")
     C = tq.tq_gemm(A.to(dev), codes, scale)
     check_close(C.index_select(1, torch.from_numpy(rows).to(dev)), A, wdq, label=f"70b {N}x{K} M={M}")
+
+
+@pytest.mark.parametrize("N,K", FUSED_70B)
+@pytest.mark.parametrize("M", [1, 2, 16])
+def test_ternary_70b_fused(N, K, M):
+    import torch
+    import bit_weight_only_tq_amd as tq
+    dev = require_gpu()
+    log(f"tq_gemm 70b fused N={N} K={K} M={M}")
+    codes, scale, rows, wdq = _packed(N, K, dev)
+    A = synth.activations(M, K, synth.seed_for("a70bf", N, K, M), "f16")
+    C = tq.tq_gemm(A.to(dev), codes, scale)
+    check_close(C.index_select(1, torch.from_numpy(rows).to(dev)), A, wdq, label=f"70b fused {N}x{K} M={M}")
