@@ -215,7 +215,9 @@ def run_w4_decode(args, dev, Ms=(1, 4, 16)):
             g.replay()
         t = time_region(g.replay, args.steps, stream)
         alg = sum(w4_bytes(M, m[0], m[1]) for m in mats)
-        res[f"M{M}"] = {"value": round(packed * args.steps / t / 1e9, 1), "ms_per_step": round(t / args.steps * 1e3, 4),
+        res[f"M{M}"] = {"value": round(packed * args.steps / t / 1e9, 1),
+                        "frac_of_peak": round(packed * args.steps / t / 1e9 / HBM_PEAK_GBS, 4),
+                        "ms_per_step": round(t / args.steps * 1e3, 4),
                         "avg_launch_us": round(t / args.steps / len(mats) * 1e6, 3),
                         "alg_gbs": round(alg * args.steps / t / 1e9, 1)}
         del g, xs, outs
@@ -246,8 +248,12 @@ def run_medium(dev, copies=8, iters=16):
             for c in calls:
                 c()
             t = time_region(lambda: [c() for c in calls], iters, stream) / (iters * copies)
-            res[f"{name}_{N}x{K}_M{M}"] = {"us": round(t * 1e6, 2), "tflops": round(2.0 * M * N * K / t / 1e12, 1),
+            flops = 2.0 * M * N * K
+            alg = ternary_bytes(M, N, K)
+            roof_s = max(alg / (HBM_PEAK_GBS * 1e9), flops / (MFMA_PEAK_TFLOPS * 1e12))  # min(BW * I, peak)
+            res[f"{name}_{N}x{K}_M{M}"] = {"us": round(t * 1e6, 2), "tflops": round(flops / t / 1e12, 1),
                                            "packed_gbs": round(codes.numel() / t / 1e9, 1),
+                                           "roof_us": round(roof_s * 1e6, 2), "frac_of_roof": round(roof_s / t, 4),
                                            "splits": nbytes // (4 * M * N) if nbytes else 1}
             del A, C, ws
         del reps, codes, scale
@@ -269,32 +275,49 @@ def run_decode_70b(args, dev):
 
 
 def run_prefill(dev, iters=10):
+    """Ternary prefill GEMM on the Llama-3-8B MLP shapes: M = 4096 in fp16 (the
+    metric) and bf16, and bf16 at M = 2048 and 8192.  Beside it, as context only,
+    the same products with dense fp16/bf16 weights through torch's F.linear
+    (the vendor GEMM library), timed in the same process on the same inputs."""
     import torch
     import bit_weight_only_tq_amd as tq
     import synth
     res = {}
-    M = 4096
     flops_f16, t_f16 = 0.0, 0.0
     stream = torch.cuda.current_stream()
+    points = [(4096, "f16"), (4096, "bf16"), (2048, "bf16"), (8192, "bf16")]
     for (N, K) in [(14336, 4096), (4096, 14336)]:
         W = synth.weights_device(N, K, synth.seed_for("benchpf", N, K), dev)
         codes, scale = tq.tq_pack(W)
-        del W
-        for dt in ("f16", "bf16"):
+        for M, dt in points:
             A = synth.activations_device(M, K, synth.seed_for("benchpfa", N, K, dt), dt, dev)
             C = torch.empty((M, N), dtype=A.dtype, device=dev)
+            nbytes = tq.tq_gemm_workspace_bytes(M, N, K, dt)
+            ws = torch.empty((nbytes,), dtype=torch.uint8, device=dev) if nbytes else None
             for _ in range(3):
-                tq.tq_gemm(A, codes, scale, out=C)
-            t = time_region(lambda: tq.tq_gemm(A, codes, scale, out=C), iters, stream) / iters
-            res[f"{N}x{K}_{dt}"] = {"ms": round(t * 1e3, 4), "tflops": round(2.0 * M * N * K / t / 1e12, 1)}
-            if dt == "f16":
+                tq.tq_gemm(A, codes, scale, out=C, workspace=ws)
+            t = time_region(lambda: tq.tq_gemm(A, codes, scale, out=C, workspace=ws), iters, stream) / iters
+            entry = {"ms": round(t * 1e3, 4), "tflops": round(2.0 * M * N * K / t / 1e12, 1),
+                     "splits": nbytes // (4 * M * N) if nbytes else 1}
+            if M == 4096:
+                Wd = W.to(A.dtype)
+                for _ in range(3):
+                    torch.nn.functional.linear(A, Wd)
+                td = time_region(lambda: torch.nn.functional.linear(A, Wd), iters, stream) / iters
+                entry["dense_ref_tflops"] = round(2.0 * M * N * K / td / 1e12, 1)
+                del Wd
+            res[f"{N}x{K}_M{M}_{dt}"] = entry
+            if M == 4096 and dt == "f16":
                 flops_f16 += 2.0 * M * N * K
                 t_f16 += t
-            del A, C
+            del A, C, ws
+        del W, codes, scale
     tf = flops_f16 / t_f16 / 1e12
     return {"metric": "fp16-MFMA TFLOP/s at M=4096 (ternary prefill GEMM, Llama-3-8B MLP shapes)",
             "value": round(tf, 1), "unit": "TFLOP/s", "peak": MFMA_PEAK_TFLOPS,
-            "frac_of_peak": round(tf / MFMA_PEAK_TFLOPS, 4), "kernel": "v3::gemm_kernel", **res}
+            "frac_of_peak": round(tf / MFMA_PEAK_TFLOPS, 4), "kernel": "v3::gemm_kernel",
+            "dense_ref": "torch.nn.functional.linear with dense weights of the same shape and dtype (context only)",
+            **res}
 
 
 def run_calib(dev, nbytes=1 << 30, iters=5):

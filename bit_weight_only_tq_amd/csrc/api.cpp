@@ -86,8 +86,9 @@ tq_path tq_select_path(int format, int64_t M, int64_t N, int64_t K, tq_dtype dt)
 size_t tq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, tq_dtype dt, tq_path path) {
     if (M <= 0 || N <= 0 || K <= 0 || K % 64 != 0) return 0;
     if (path == TQ_PATH_AUTO) path = tq_select_path(0, M, N, K, dt);
-    if (path != TQ_PATH_STREAM_MFMA) return 0;
-    return tq::medium_m_workspace_bytes(M, N, K, tq::compute_units());
+    if (path == TQ_PATH_STREAM_MFMA) return tq::medium_m_workspace_bytes(M, N, K, tq::compute_units());
+    if (path == TQ_PATH_GEMM) return tq::gemm_workspace_bytes(M, N, K, tq::compute_units());
+    return 0;
 }
 
 // ---------------------------------------------------------------- prepare
@@ -180,7 +181,8 @@ tq_status tq_gemm_ws(const void* A, tq_dtype dt, int64_t M, int64_t N, int64_t K
             return from_hip(tq::launch_ternary_medium(a, workspace, workspace ? workspace_bytes : 0,
                                                       tq::compute_units(), stream));
         case TQ_PATH_GEMM:
-            return from_hip(tq::launch_ternary_gemm(a, stream));
+            return from_hip(tq::launch_ternary_gemm(a, workspace, workspace ? workspace_bytes : 0,
+                                                    tq::compute_units(), stream));
         default:
             return TQ_ERR_PATH;
     }

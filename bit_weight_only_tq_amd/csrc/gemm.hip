@@ -68,6 +68,17 @@ __device__ __forceinline__ void stage_barrier() {
     asm volatile("" ::: "memory");
 }
 
+// A GEMM whose K range is split S ways: split z of S covers K-steps
+// [z*nk/S, (z+1)*nk/S) and writes its fp32 partial (row-sum correction
+// applied, no scale) to ws[z][M][N]; a second kernel sums the S partials of
+// each output in order z = 0 .. S-1 and applies the row scale and bias, so
+// the result does not depend on scheduling.
+struct SplitArgs {
+    GemmArgs g;
+    float* ws;  // [S][M][N] fp32 partials, unused when S == 1
+    int S;
+};
+
 // ------------------------------------------------------------------------
 // v3 (K % 64 == 0): all global traffic is DMA (global_load_lds_dwordx4, no
 // registers) into a 3-stage LDS ring issued two K-steps ahead:
@@ -82,7 +93,8 @@ __device__ __forceinline__ void stage_barrier() {
 // 2g + s for lane group g.  Row sums of A for the bias correction are split
 // over the four waves sharing a row block (m-tiles wn and wn + 4).  The
 // epilogue stages each wave's outputs through LDS so that every lane stores
-// 16 contiguous bytes.
+// 16 contiguous bytes.  With a K split (blockIdx.z = split) the fp32
+// partials are stored straight from the accumulators instead.
 namespace v3 {
 
 constexpr int BM = 256;
@@ -102,8 +114,9 @@ constexpr size_t kLdsBytes = (size_t)kStages * kStageBytes;
 static_assert(8 * kEpiBytesPerWave + BM * 4 <= (int)kLdsBytes, "epilogue staging must fit in the ring");
 
 template <class T>
-__global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
+__global__ __launch_bounds__(kThreads) void gemm_kernel(SplitArgs sa) {
     typedef typename Mfma<T>::vec vec;
+    const GemmArgs& p = sa.g;
     extern __shared__ uint4 smem_v3[];
     uint8_t* lds = reinterpret_cast<uint8_t*>(smem_v3);
     const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)smem_v3;
@@ -170,16 +183,19 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
     // code dword of tile j: row wn*64 + 16j + i16, bytes 4g .. 4g+3
     const int b_frag = kABytes + (wn * WN + i16) * 16 + 4 * g;
 
-    const int nk = (int)(K / BK);
-    issue(0, 0);
-    issue(nk > 1 ? 1 : 0, 1);
+    // this split's K-steps [kb, kb + nk); the host keeps S <= K / BK
+    const int nk_all = (int)(K / BK);
+    const int kb = (int)((int64_t)blockIdx.z * nk_all / sa.S);
+    const int nk = (int)((int64_t)(blockIdx.z + 1) * nk_all / sa.S) - kb;
+    issue(kb, 0);
+    issue(kb + (nk > 1 ? 1 : 0), 1);
     wait_prev_stage();
     stage_barrier();
     for (int kt = 0; kt < nk; ++kt) {
         const int stage = kt % kStages;
         // Unconditional so the per-wave counts stay exact: past the end the DMA
         // re-reads the last K-step into the stage nobody reads any more.
-        issue(kt + 2 < nk ? kt + 2 : nk - 1, (kt + 2) % kStages);
+        issue(kb + (kt + 2 < nk ? kt + 2 : nk - 1), (kt + 2) % kStages);
         const uint8_t* sbase = lds + stage * kStageBytes;
         uint32_t E[TN], O[TN];
 #pragma unroll
@@ -236,6 +252,25 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
     }
     __syncthreads();
 
+    if (sa.S > 1) {  // fp32 partial of this split: 16 lanes store 64 contiguous bytes per row
+        float* ws = sa.ws + (int64_t)blockIdx.z * M * N;
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = wm * WM + 16 * i + 4 * g + r;
+                const int64_t m = m0 + row;
+                if (m >= M) continue;
+                const float rs = Mfma<T>::kBias * rs_lds[row];
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    const int64_t n = n0 + wn * WN + 16 * j + i16;
+                    if (n < N) ws[m * N + n] = acc[i][j][r] - rs;
+                }
+            }
+        return;
+    }
+
     // epilogue: per wave, 4 slabs of 32 rows x 64 columns through a private LDS area
     uint16_t* stg = reinterpret_cast<uint16_t*>(lds + wave * kEpiBytesPerWave);
     float sc[TN], bi[TN];
@@ -290,11 +325,8 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
 // but six stages deep (five K-steps in flight), so that a single workgroup
 // per compute unit keeps enough loads outstanding.  Wave w computes all
 // 16TM rows x columns 32w .. 32w+31.  With few row tiles the grid is also
-// split along K: split z of S covers K-steps [z*nk/S, (z+1)*nk/S) and
-// writes its fp32 partial (row-sum correction applied, no scale) to a
-// workspace [S][M][N]; splitk_reduce_kernel then sums the S partials of each
-// output in order z = 0 .. S-1 and applies the row scale and bias.  With
-// S = 1 the tile kernel finishes its outputs itself.
+// split along K as described at SplitArgs; with S = 1 the tile kernel
+// finishes its outputs itself.
 namespace mm {
 
 constexpr int BN = 256;
@@ -307,12 +339,6 @@ constexpr int kBBytes = BN * BK / 4;  // 4 KB of codes per stage
 template <int TM> constexpr int a_bytes() { return 16 * TM * BK * 2; }
 template <int TM> constexpr int stage_bytes() { return a_bytes<TM>() + kBBytes; }
 template <int TM> constexpr size_t lds_bytes() { return (size_t)kStages * stage_bytes<TM>() + 16 * TM * 4; }
-
-struct SplitArgs {
-    GemmArgs g;
-    float* ws;  // [S][M][N] fp32 partials, unused when S == 1
-    int S;
-};
 
 template <class T, int TM>
 __global__ __launch_bounds__(kThreads) void tile_kernel(SplitArgs sa) {
@@ -480,20 +506,24 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(SplitArgs sa) {
     }
 }
 
-// C[m, n] = (sum over z of ws[z][m][n]) * scale[n] + bias[n]; grid (ceil(N/256), M).
+// C[m, n] = (sum over z of ws[z][m][n]) * scale[n] + bias[n]; grid
+// (ceil(N/256), reduce_rows(M)), each workgroup row striding over m.
+constexpr int64_t kReduceMaxRows = 65535;
+inline unsigned reduce_rows(int64_t M) { return (unsigned)(M < kReduceMaxRows ? M : kReduceMaxRows); }
 template <class T>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(SplitArgs sa) {
     const GemmArgs& p = sa.g;
     const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t m = blockIdx.y;
     if (n >= p.N) return;
     const int64_t MN = p.M * p.N;
-    const float* src = sa.ws + m * p.N + n;
-    float s = 0.0f;
-    for (int z = 0; z < sa.S; ++z) s += src[z * MN];
     const float sc = f16_bits_to_f32(p.scale[n]);
     const float b = p.bias ? T::to_f32(p.bias[n]) : 0.0f;
-    p.C[m * p.N + n] = T::from_f32_fast(s * sc + b);
+    for (int64_t m = blockIdx.y; m < p.M; m += gridDim.y) {
+        const float* src = sa.ws + m * p.N + n;
+        float s = 0.0f;
+        for (int z = 0; z < sa.S; ++z) s += src[z * MN];
+        p.C[m * p.N + n] = T::from_f32_fast(s * sc + b);
+    }
 }
 
 }  // namespace mm
@@ -502,18 +532,57 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(SplitArgs sa) {
 }  // namespace
 
 template <class T>
-static hipError_t launch_v3(const GemmArgs& a, hipStream_t s) {
+static hipError_t launch_v3(const SplitArgs& sa, hipStream_t s) {
     static DeviceFlags lds_limit_set;
     hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(&v3::gemm_kernel<T>), (int)v3::kLdsBytes, lds_limit_set);
     if (e != hipSuccess) return e;
-    const dim3 grid((unsigned)((a.N + v3::BN - 1) / v3::BN), (unsigned)((a.M + v3::BM - 1) / v3::BM));
-    v3::gemm_kernel<T><<<grid, v3::kThreads, v3::kLdsBytes, s>>>(a);
-    return hipGetLastError();
+    const GemmArgs& a = sa.g;
+    const dim3 grid((unsigned)((a.N + v3::BN - 1) / v3::BN), (unsigned)((a.M + v3::BM - 1) / v3::BM), (unsigned)sa.S);
+    v3::gemm_kernel<T><<<grid, v3::kThreads, v3::kLdsBytes, s>>>(sa);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (sa.S > 1) {
+        mm::splitk_reduce_kernel<T><<<dim3((unsigned)((a.N + 255) / 256), mm::reduce_rows(a.M)), 256, 0, s>>>(sa);
+        e = hipGetLastError();
+    }
+    return e;
 }
 
-hipError_t launch_ternary_gemm(const GemmArgs& a, hipStream_t s) {
+// K split of the large-M kernel.  One 256 x 256 workgroup fills a compute
+// unit (the LDS ring takes 108 KB), so a grid of T tiles runs in
+// ceil(T / CUs) rounds of nk K-steps each.  When T leaves compute units idle,
+// S splits shorten each round to ceil(nk / S) K-steps at the price of
+// writing and re-reading S * M * N fp32 partials plus a second launch.  The
+// split count minimises that estimate, with one K-step taken as 1.5 us (a
+// 256 x 256 x 64 step at about 1 PFLOP/s over the whole chip) and the
+// partials moving at 4 TB/s; each split keeps at least 16 K-steps.
+int gemm_splits(int64_t M, int64_t N, int64_t K, int compute_units) {
+    const int64_t tiles = ((N + v3::BN - 1) / v3::BN) * ((M + v3::BM - 1) / v3::BM);
+    const int64_t nk = K / v3::BK;
+    const int64_t cus = compute_units > 0 ? compute_units : 1;
+    const double step_us = 1.5, partial_bytes_per_us = 4.0e6, launch_us = 3.0;
+    int best = 1;
+    double best_us = (double)((tiles + cus - 1) / cus) * (double)nk * step_us;
+    for (int S = 2; S <= 8 && nk / S >= 16; ++S) {
+        const double us = (double)((tiles * S + cus - 1) / cus) * (double)((nk + S - 1) / S) * step_us +
+                          2.0 * S * (double)M * (double)N * 4.0 / partial_bytes_per_us + launch_us;
+        if (us < best_us) { best_us = us; best = S; }
+    }
+    return best;
+}
+
+size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int compute_units) {
+    const int S = gemm_splits(M, N, K, compute_units);
+    return S > 1 ? (size_t)S * (size_t)M * (size_t)N * sizeof(float) : 0;
+}
+
+// Large M with an optional workspace: the split count of gemm_splits when
+// `workspace` holds gemm_workspace_bytes(), a single pass over K otherwise.
+hipError_t launch_ternary_gemm(const GemmArgs& a, void* workspace, size_t workspace_bytes, int compute_units,
+                               hipStream_t s) {
     // the C ABI guarantees K % 64 == 0 (whole 16-byte code chunks per row)
-    return a.bf16 ? launch_v3<BF16>(a, s) : launch_v3<F16>(a, s);
+    SplitArgs sa{a, static_cast<float*>(workspace), gemm_splits(a.M, a.N, a.K, compute_units)};
+    if (sa.S > 1 && (!workspace || workspace_bytes < gemm_workspace_bytes(a.M, a.N, a.K, compute_units))) sa.S = 1;
+    return a.bf16 ? launch_v3<BF16>(sa, s) : launch_v3<F16>(sa, s);
 }
 
 // Split count of the medium-M kernel: none when the row x column tiles
@@ -535,7 +604,7 @@ size_t medium_m_workspace_bytes(int64_t M, int64_t N, int64_t K, int compute_uni
 }
 
 template <class T, int TM>
-static hipError_t launch_mm(const mm::SplitArgs& sa, hipStream_t s) {
+static hipError_t launch_mm(const SplitArgs& sa, hipStream_t s) {
     static DeviceFlags lds_limit_set;
     hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(&mm::tile_kernel<T, TM>), (int)mm::lds_bytes<TM>(),
                                    lds_limit_set);
@@ -545,7 +614,7 @@ static hipError_t launch_mm(const mm::SplitArgs& sa, hipStream_t s) {
     mm::tile_kernel<T, TM><<<grid, mm::kThreads, mm::lds_bytes<TM>(), s>>>(sa);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (sa.S > 1) {
-        mm::splitk_reduce_kernel<T><<<dim3((unsigned)((a.N + 255) / 256), (unsigned)a.M), 256, 0, s>>>(sa);
+        mm::splitk_reduce_kernel<T><<<dim3((unsigned)((a.N + 255) / 256), mm::reduce_rows(a.M)), 256, 0, s>>>(sa);
         e = hipGetLastError();
     }
     return e;
@@ -555,7 +624,7 @@ static hipError_t launch_mm(const mm::SplitArgs& sa, hipStream_t s) {
 // medium_m_workspace_bytes(), a single pass over K otherwise.
 hipError_t launch_ternary_medium(const GemmArgs& a, void* workspace, size_t workspace_bytes, int compute_units,
                                  hipStream_t s) {
-    mm::SplitArgs sa{a, static_cast<float*>(workspace), medium_m_splits(a.M, a.N, a.K, compute_units)};
+    SplitArgs sa{a, static_cast<float*>(workspace), medium_m_splits(a.M, a.N, a.K, compute_units)};
     if (sa.S > 1 && (!workspace || workspace_bytes < medium_m_workspace_bytes(a.M, a.N, a.K, compute_units))) sa.S = 1;
     const bool small = a.M <= 32;
     if (a.bf16) return small ? launch_mm<BF16, 2>(sa, s) : launch_mm<BF16, 4>(sa, s);

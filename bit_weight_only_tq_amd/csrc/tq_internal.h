@@ -59,7 +59,12 @@ hipError_t launch_w4_gemv(const GemmArgs& a, hipStream_t s);         // picks th
 hipError_t launch_w4_gemv_simple(const GemmArgs& a, hipStream_t s);  // any dtype
 
 // gemm.hip: LDS-tiled matrix-core GEMM, any M.
-hipError_t launch_ternary_gemm(const GemmArgs& a, hipStream_t s);
+// Large M: K split S ways (gemm_splits) when `workspace` holds
+// gemm_workspace_bytes(), else one pass over K.
+hipError_t launch_ternary_gemm(const GemmArgs& a, void* workspace, size_t workspace_bytes, int compute_units,
+                               hipStream_t s);
+int gemm_splits(int64_t M, int64_t N, int64_t K, int compute_units);
+size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int compute_units);
 // gemm.hip: medium M (64-row tiles, K split across workgroups when the
 // workspace allows; see medium_m_workspace_bytes).
 int medium_m_splits(int64_t M, int64_t N, int64_t K, int compute_units);

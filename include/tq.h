@@ -174,12 +174,13 @@ tq_status tq_gemm_ex(const void* A, tq_dtype dt, int64_t M, int64_t N, int64_t K
  *                    `stream` is done.  Calls that may overlap must use
  *                    different workspaces.
  *   workspace_bytes  at least tq_gemm_workspace_bytes(M, N, K, dt, path)
- *                    for the split-K schedule of TQ_PATH_STREAM_MFMA; with
- *                    less (or NULL) that path runs one workgroup per output
- *                    tile over all of K - correct, slower.
+ *                    for the split-K schedule of TQ_PATH_STREAM_MFMA and
+ *                    TQ_PATH_GEMM; with less (or NULL) those paths run one
+ *                    workgroup per output tile over all of K - correct,
+ *                    slower when the output tiles leave compute units idle.
  *   path             TQ_PATH_AUTO or a forced kernel family (TQ_ERR_PATH if
  *                    it cannot run the shape: TQ_PATH_GEMV needs M <= 16).
- * With S > 1 splits the medium path writes S fp32 partials [S][M][N] into the
+ * With S > 1 splits the kernel writes S fp32 partials [S][M][N] into the
  * workspace and a second kernel sums them in order z = 0 .. S-1.  Other
  * arguments, results and errors as tq_gemm; TQ_ERR_ALIGN for a misaligned
  * workspace.  Asynchronous; allocates nothing; graph-capturable.

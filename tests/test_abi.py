@@ -67,16 +67,23 @@ def test_dispatcher_by_m():
 
 
 def test_workspace_query():
-    """Split-K workspace of the medium path: S fp32 partials of [M, N], none
-    for the other paths or when the row x column tiles fill the device.  Off
-    the GPU the compute-unit count defaults to 256."""
+    """Split-K workspace: S fp32 partials of [M, N] for the medium and large-M
+    paths, none for the GEMV path or when the output tiles fill the device.
+    Off the GPU the compute-unit count defaults to 256."""
     wb = _lib.tq_gemm_workspace_bytes
     assert wb(1, 4096, 4096) == 0 and wb(4096, 4096, 4096) == 0
     assert wb(64, 8192, 8192) == 8 * 64 * 8192 * 4      # 32 tiles -> 8 splits
     assert wb(32, 1024, 8192) == 16 * 32 * 1024 * 4     # capped at 8 K-steps per split
     assert wb(64, 57344, 8192) == 0                     # 224 tiles: no split
-    assert wb(64, 8192, 8192, path="gemm") == 0
     assert wb(64, 8192, 96) == 0                        # K % 64 != 0
+    # large M: 256 x 256 tiles, one per compute unit, >= 16 K-steps per split
+    assert wb(2048, 4096, 14336) == 2 * 2048 * 4096 * 4  # 128 tiles: two splits fill the device
+    assert wb(2048, 14336, 4096) == 0                   # 448 tiles: partials cost more than they save
+    assert wb(4096, 4096, 14336) == 0 and wb(8192, 4096, 14336) == 0
+    assert wb(300, 1000, 4096) == 4 * 300 * 1000 * 4    # 8 tiles, 64 K-steps -> 4 splits
+    assert wb(300, 1000, 1024) == 0                     # 16 K-steps: nothing to split
+    assert wb(64, 8192, 8192, path="gemm") == 8 * 64 * 8192 * 4
+    assert wb(4, 8192, 8192, path="gemv") == 0
 
 
 V = ctypes.c_void_p

@@ -211,6 +211,38 @@ def test_medium_split_k(M, N, K):
                     label=f"medium {M}x{N}x{K} ws={ws}")
 
 
+@pytest.mark.parametrize("M,N,K", [(2048, 4096, 14336), (300, 1000, 4096), (257, 300, 2048), (256, 4096, 4096)])
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_gemm_split_k(M, N, K, dt):
+    """Large-M kernel with K split across workgroups (workspace from torch)
+    and without a workspace (one pass over K): both within the tolerance on
+    sampled output columns, ragged M and N included, with bias."""
+    import torch
+    import bit_weight_only_tq_amd as tq
+    dev = require_gpu()
+    nbytes = tq.tq_gemm_workspace_bytes(M, N, K, dt, path="gemm")
+    log(f"gemm split-K M={M} N={N} K={K} {dt} workspace={nbytes}")
+    assert nbytes > 0
+    W = synth.weights_device(N, K, synth.seed_for("gsk", N, K), dev)
+    codes, scale = tq.tq_pack(W)
+    cols = np.sort(np.random.default_rng(N + K).choice(N, min(N, 192), replace=False))
+    idx = torch.from_numpy(cols).to(dev)
+    rc, rs = OT.ternary_pack(W.index_select(0, idx).cpu().numpy())
+    del W
+    wdq = OT.ternary_dequant(rc, rs, K)
+    A = synth.activations(M, K, synth.seed_for("gska", M, K, dt), dt)
+    bias = synth.activations(1, N, synth.seed_for("gskb", N, dt), dt)[0]
+    outs = []
+    for ws in ("auto", None):
+        C = tq.tq_gemm(A.to(dev), codes, scale, bias=bias.to(dev), path="gemm", workspace=ws)
+        check_close(C.index_select(1, idx), A, wdq, bias=bias[torch.from_numpy(cols)],
+                    label=f"gemm split {M}x{N}x{K} {dt} ws={ws}")
+        outs.append(C)
+    # a repeated split call is bit-identical (partials summed in a fixed order)
+    C2 = tq.tq_gemm(A.to(dev), codes, scale, bias=bias.to(dev), path="gemm")
+    assert torch.equal(outs[0].view(torch.int16), C2.view(torch.int16))
+
+
 @pytest.mark.parametrize("M,N,K", [(1, 20, 128), (3, 37, 384), (16, 300, 1024), (5, 16400, 256),
                                    (2, 64, 2048), (16, 17, 4096), (7, 1000, 14336)])
 def test_w4_ragged_shapes(M, N, K):

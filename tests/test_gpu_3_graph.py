@@ -9,7 +9,8 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("fmt,M,N,K", [
-    ("ternary", 1, 4096, 4096), ("ternary", 16, 1024, 4096), ("ternary", 512, 1024, 4096),
+    ("ternary", 1, 4096, 4096), ("ternary", 16, 1024, 4096),
+    ("ternary", 512, 1024, 4096), ("ternary", 2048, 14336, 4096),  # large M: split K (two kernels), one pass
     ("ternary", 40, 1024, 4096), ("ternary", 200, 2048, 1024),  # medium path: split K, two kernels
     ("w4a16", 4, 1024, 4096),
 ])
