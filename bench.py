@@ -33,7 +33,7 @@ Also reported in the same JSON line:
     timed on the host on a bounded sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--mode MODE]
-  --mode full (default) | decode | decode70b | w4 | medium | prefill | calib
+  --mode full (default) | decode | decodem | decode70b | w4 | medium | prefill | calib
   (plain copy of known size, for scaling hardware byte counters)
 """
 
@@ -62,7 +62,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--layers", type=int, default=32)
     ap.add_argument("--mode", default="full",
-                    choices=["full", "decode", "decode70b", "w4", "medium", "prefill", "calib"])
+                    choices=["full", "decode", "decodem", "decode70b", "w4", "medium", "prefill", "calib"])
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
     ap.add_argument("--unfused", action="store_true", help="decode mode: q,k,v,gate,up as separate calls")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -126,7 +126,7 @@ def time_region(fn, steps, stream):
     return start.elapsed_time(end) / 1e3
 
 
-def run_decode(args, dev, fused, graph, model="8b", layers=None, steps=None):
+def run_decode(args, dev, fused, graph, model="8b", layers=None, steps=None, M=1):
     import torch
     import bit_weight_only_tq_amd as tq
     import synth
@@ -134,8 +134,8 @@ def run_decode(args, dev, fused, graph, model="8b", layers=None, steps=None):
     layers = args.layers if layers is None else layers
     steps = args.steps if steps is None else steps
     mats = build_decode(layers, dev, fused, model)
-    xs = {K: synth.activations_device(1, K, synth.seed_for("benchx", K), "f16", dev) for K in {m[2] for m in mats}}
-    outs = [torch.empty((1, m[1]), dtype=torch.float16, device=dev) for m in mats]
+    xs = {K: synth.activations_device(M, K, synth.seed_for("benchx", K, M), "f16", dev) for K in {m[2] for m in mats}}
+    outs = [torch.empty((M, m[1]), dtype=torch.float16, device=dev) for m in mats]
 
     def step():
         for i, (name, N, K, codes, scale) in enumerate(mats):
@@ -158,7 +158,7 @@ def run_decode(args, dev, fused, graph, model="8b", layers=None, steps=None):
     torch.cuda.synchronize()
     t = time_region(run, steps, stream)
     packed = sum(m[3].numel() for m in mats)
-    alg = sum(ternary_bytes(1, m[1], m[2]) for m in mats)
+    alg = sum(ternary_bytes(M, m[1], m[2]) for m in mats)
     res = {
         "launches": len(mats), "seconds": t, "packed_bytes": packed, "alg_bytes": alg,
         "ms_per_step": t / steps * 1e3, "packed_gbs": packed * steps / t / 1e9,
@@ -258,6 +258,18 @@ def run_medium(dev, copies=8, iters=16):
             del A, C, ws
         del reps, codes, scale
     torch.cuda.empty_cache()
+    return res
+
+
+def run_decode_m(args, dev, graph, Ms=(4, 16)):
+    """Llama-3-8B ternary decode step (32 layers, fused qkv / gate_up) at
+    several activation rows M."""
+    res = {"metric": "HBM GB/s ternary GEMV, Llama-3-8B decode (32 layers, fused qkv / gate_up)", "unit": "GB/s"}
+    for M in Ms:
+        d = run_decode(args, dev, True, graph, M=M)
+        res[f"M{M}"] = {"value": round(d["packed_gbs"], 1), "frac_of_peak": round(d["packed_gbs"] / HBM_PEAK_GBS, 4),
+                        "ms_per_step": round(d["ms_per_step"], 4), "avg_launch_us": round(d["avg_launch_us"], 3),
+                        "alg_gbs": round(d["alg_gbs"], 1)}
     return res
 
 
@@ -385,7 +397,7 @@ def load_traffic(path):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1"}), flush=True)
+        print(json.dumps({"error": "the benchmark runs on exactly one GPU (no multi-GPU path); --gpus must be 1"}), flush=True)
         sys.exit(2)
     import torch
     import bit_weight_only_tq_amd as tq
@@ -400,6 +412,9 @@ def main():
         return
     if args.mode == "prefill":
         print(json.dumps({"secondary": run_prefill(dev)}), flush=True)
+        return
+    if args.mode == "decodem":
+        print(json.dumps({"decode_m": run_decode_m(args, dev, not args.no_graph)}), flush=True)
         return
     if args.mode == "decode70b":
         print(json.dumps({"decode_70b": run_decode_70b(args, dev)}), flush=True)
@@ -452,6 +467,8 @@ def main():
             out["decode_unfused"] = {"value": round(u["packed_gbs"], 1), "unit": "GB/s",
                                      "ms_per_step": round(u["ms_per_step"], 4), "launches_per_step": u["launches"],
                                      "avg_launch_us": round(u["avg_launch_us"], 3)}
+        log("decode, M = 4 and 16")
+        out["decode_m"] = run_decode_m(args, dev, graph)
         log("decode, Llama-3-70B, 80 layers")
         out["decode_70b"] = run_decode_70b(args, dev)
         log("W4A16 decode")

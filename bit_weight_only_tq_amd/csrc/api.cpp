@@ -88,6 +88,10 @@ size_t tq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, tq_dtype dt, tq_
     if (path == TQ_PATH_AUTO) path = tq_select_path(0, M, N, K, dt);
     if (path == TQ_PATH_STREAM_MFMA) return tq::medium_m_workspace_bytes(M, N, K, tq::compute_units());
     if (path == TQ_PATH_GEMM) return tq::gemm_workspace_bytes(M, N, K, tq::compute_units());
+    if (path == TQ_PATH_GEMV && M <= kGemvMaxM) {
+        const tq::GemmArgs a{nullptr, dt == TQ_BF16 ? 1 : 0, M, N, K, nullptr, nullptr, nullptr, nullptr};
+        return tq::gemv_workspace_bytes(a);
+    }
     return 0;
 }
 
@@ -176,7 +180,7 @@ tq_status tq_gemm_ws(const void* A, tq_dtype dt, int64_t M, int64_t N, int64_t K
     switch (path) {
         case TQ_PATH_GEMV:
             if (M > kGemvMaxM) return TQ_ERR_PATH;
-            return from_hip(tq::launch_ternary_gemv(a, stream));
+            return from_hip(tq::launch_ternary_gemv(a, workspace, workspace ? workspace_bytes : 0, stream));
         case TQ_PATH_STREAM_MFMA:
             return from_hip(tq::launch_ternary_medium(a, workspace, workspace ? workspace_bytes : 0,
                                                       tq::compute_units(), stream));

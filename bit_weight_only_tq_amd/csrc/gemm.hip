@@ -49,17 +49,6 @@ template <> struct Mfma<BF16> {
     static constexpr uint32_t kOnePair = 0x3F803F80u;
 };
 
-// 16 bytes per lane, global -> LDS at M0 + 16 * lane (M0 must be wave-uniform).
-// Issued through asm so that the compiler does not model the LDS write: its
-// conservative tracking would otherwise wait for every DMA in flight before
-// any LDS read, defeating the prefetch.  The kernel orders the DMA itself:
-// explicit vmcnt waits before the barrier that publishes a stage, and the
-// "memory" clobber keeps the compiler from moving LDS accesses across it.
-__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_addr) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                 :: "v"(gptr), "s"(lds_addr) : "memory", "m0");
-}
-
 // Bare workgroup barrier: __syncthreads() would add a release fence that
 // waits for every outstanding DMA, including the stage issued ahead.
 __device__ __forceinline__ void stage_barrier() {
@@ -67,17 +56,6 @@ __device__ __forceinline__ void stage_barrier() {
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
 }
-
-// A GEMM whose K range is split S ways: split z of S covers K-steps
-// [z*nk/S, (z+1)*nk/S) and writes its fp32 partial (row-sum correction
-// applied, no scale) to ws[z][M][N]; a second kernel sums the S partials of
-// each output in order z = 0 .. S-1 and applies the row scale and bias, so
-// the result does not depend on scheduling.
-struct SplitArgs {
-    GemmArgs g;
-    float* ws;  // [S][M][N] fp32 partials, unused when S == 1
-    int S;
-};
 
 // ------------------------------------------------------------------------
 // v3 (K % 64 == 0): all global traffic is DMA (global_load_lds_dwordx4, no
@@ -93,8 +71,9 @@ struct SplitArgs {
 // 2g + s for lane group g.  Row sums of A for the bias correction are split
 // over the four waves sharing a row block (m-tiles wn and wn + 4).  The
 // epilogue stages each wave's outputs through LDS so that every lane stores
-// 16 contiguous bytes.  With a K split (blockIdx.z = split) the fp32
-// partials are stored straight from the accumulators instead.
+// 16 contiguous bytes.  With a K split (blockIdx.z = split z of S, K-steps
+// [z*nk/S, (z+1)*nk/S)) the fp32 partials (row-sum correction applied) are
+// stored straight from the accumulators instead.
 namespace v3 {
 
 constexpr int BM = 256;
@@ -325,8 +304,8 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(SplitArgs sa) {
 // but six stages deep (five K-steps in flight), so that a single workgroup
 // per compute unit keeps enough loads outstanding.  Wave w computes all
 // 16TM rows x columns 32w .. 32w+31.  With few row tiles the grid is also
-// split along K as described at SplitArgs; with S = 1 the tile kernel
-// finishes its outputs itself.
+// split along K (SplitArgs); with S = 1 the tile kernel finishes its outputs
+// itself.
 namespace mm {
 
 constexpr int BN = 256;
@@ -531,6 +510,14 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(SplitArgs sa) {
 
 }  // namespace
 
+hipError_t launch_splitk_reduce(const SplitArgs& sa, hipStream_t s) {
+    const GemmArgs& a = sa.g;
+    const dim3 grid((unsigned)((a.N + 255) / 256), mm::reduce_rows(a.M));
+    if (a.bf16) mm::splitk_reduce_kernel<BF16><<<grid, 256, 0, s>>>(sa);
+    else mm::splitk_reduce_kernel<F16><<<grid, 256, 0, s>>>(sa);
+    return hipGetLastError();
+}
+
 template <class T>
 static hipError_t launch_v3(const SplitArgs& sa, hipStream_t s) {
     static DeviceFlags lds_limit_set;
@@ -540,10 +527,7 @@ static hipError_t launch_v3(const SplitArgs& sa, hipStream_t s) {
     const dim3 grid((unsigned)((a.N + v3::BN - 1) / v3::BN), (unsigned)((a.M + v3::BM - 1) / v3::BM), (unsigned)sa.S);
     v3::gemm_kernel<T><<<grid, v3::kThreads, v3::kLdsBytes, s>>>(sa);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    if (sa.S > 1) {
-        mm::splitk_reduce_kernel<T><<<dim3((unsigned)((a.N + 255) / 256), mm::reduce_rows(a.M)), 256, 0, s>>>(sa);
-        e = hipGetLastError();
-    }
+    if (sa.S > 1) e = launch_splitk_reduce(sa, s);
     return e;
 }
 
@@ -613,10 +597,7 @@ static hipError_t launch_mm(const SplitArgs& sa, hipStream_t s) {
     const dim3 grid((unsigned)((a.N + mm::BN - 1) / mm::BN), (unsigned)((a.M + 16 * TM - 1) / (16 * TM)), (unsigned)sa.S);
     mm::tile_kernel<T, TM><<<grid, mm::kThreads, mm::lds_bytes<TM>(), s>>>(sa);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    if (sa.S > 1) {
-        mm::splitk_reduce_kernel<T><<<dim3((unsigned)((a.N + 255) / 256), mm::reduce_rows(a.M)), 256, 0, s>>>(sa);
-        e = hipGetLastError();
-    }
+    if (sa.S > 1) e = launch_splitk_reduce(sa, s);
     return e;
 }
 

@@ -525,13 +525,34 @@ __global__ __launch_bounds__(1024) void ternary_gemv_lds_kernel(GemmArgs p) {
 // the operand while the codes are in flight, and contracts each row-block as
 // its codes land (in-order completion), one accumulator per row-block.  Wave
 // partials meet in LDS once, at the end, and are summed in a fixed order.
-template <int CSW, int T>
-__global__ __launch_bounds__(1024) void ternary_gemv_stream_kernel(GemmArgs p) {
+//
+// The operand layout puts 16 activation rows on neighbouring lanes, so
+// loading it directly would touch a different 128-byte line with every lane.
+// Instead each chunk-set's 512-byte row slices are copied global -> LDS by
+// DMA, two rows per instruction (lane l: row 2e + l/32, bytes 16 (l % 32)
+// ..), MR/2 instructions for the MR >= M rows (4, 8 or 16; rows past M
+// re-read row M-1), into the wave's own LDS area, and read back in operand
+// order.  The area holds CSW x MR rows x 32 slots of 16 bytes, slot q of row
+// r at q ^ (r % 16), which keeps the operand reads free of bank conflicts;
+// the same area later takes the wave's partial sums.
+//
+// Every workgroup reads the activations of its whole K range (M * K * 2
+// bytes), so for short, wide matrices the grid may also split K: workgroup
+// (x, z) covers chunk-sets z*CS/S .. (z+1)*CS/S - 1 of its row-blocks and
+// stores fp32 partials for launch_splitk_reduce (S = gridDim.y divides CS).
+__host__ __device__ constexpr int stream_wave_lds(int csw, int mr, int t) {  // bytes of one wave's LDS area
+    return t * 1024 > csw * mr * 512 ? t * 1024 : csw * mr * 512;
+}
+
+template <int CSW, int T, int MR>
+__global__ __launch_bounds__(1024) void ternary_gemv_stream_kernel(SplitArgs sa) {
+    const GemmArgs& p = sa.g;
     extern __shared__ uint4 smem[];
-    f32x4* red = reinterpret_cast<f32x4*>(smem);  // [W][T][64]
+    constexpr int kArea = stream_wave_lds(CSW, MR, T);
+    f32x4* red = reinterpret_cast<f32x4*>(smem);  // wave w, row-block t: red[w * kArea / 16 + 64 t + lane]
     const int W = blockDim.x >> 6;
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = lane >> 4;
     const int i16 = lane & 15;
     const int64_t N = p.N, K = p.K;
@@ -540,26 +561,37 @@ __global__ __launch_bounds__(1024) void ternary_gemv_stream_kernel(GemmArgs p) {
     const int CS = (int)(K / 256);
     const int64_t n_base = (int64_t)blockIdx.x * (16 * T);
     const uint8_t* codes = static_cast<const uint8_t*>(p.wq);
-    const int cs0 = wave * CSW;
-    const int cnt = CS - cs0 < CSW ? CS - cs0 : CSW;  // >= 1 for every wave of the launch
+    uint8_t* area = reinterpret_cast<uint8_t*>(smem) + wave * kArea;
+    const uint32_t area_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)smem + wave * kArea;
+    const int csz = CS / sa.S;                       // chunk-sets of this split
+    const int cs_end = ((int)blockIdx.y + 1) * csz;
+    const int cs0 = (int)blockIdx.y * csz + wave * CSW;
+    const int cnt = cs_end - cs0 < CSW ? cs_end - cs0 : CSW;  // >= 1 for every wave of the launch
 
-    // 1. activations of this lane's operand row (rows m >= M only feed output
-    //    rows that are never stored: they skip the load and keep an arbitrary
-    //    register value)
-    const bool a_live = i16 < M;
-    uint4 av[CSW][8];
+    // row scale and bias bits of the output this thread finishes in step 5
+    // (thread e < 64T: row n_base + 16 (e / 64) + e % 16); without a bias the
+    // scale is read twice, so that no branch splits the load phase
+    uint16_t sc_bits, bi_bits;
+    {
+        const int e = (int)threadIdx.x % (T * kWave);
+        const int64_t n = n_base + 16 * (e / kWave) + (e & 15);
+        const int64_t nc = n < N ? n : N - 1;
+        sc_bits = p.scale[nc];
+        bi_bits = (p.bias ? p.bias : p.scale)[nc];
+    }
+    // 1. activation slices -> the wave's LDS area by DMA, two rows per
+    //    instruction (rows past M re-read row M-1; operand rows m >= M only
+    //    feed outputs that are never stored)
 #pragma unroll
-    for (int s = 0; s < CSW; ++s)
+    for (int s = 0; s < CSW; ++s) {
+        const int cs = (s < cnt) ? cs0 + s : cs0;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) av[s][e] = opaque_uint4();
-    if (a_live) {
-        const uint16_t* arow = p.A + (int64_t)i16 * K;
-#pragma unroll
-        for (int s = 0; s < CSW; ++s) {
-            const int cs = (s < cnt) ? cs0 + s : cs0;
-            const uint4* src = reinterpret_cast<const uint4*>(arow + (int64_t)(4 * cs + g) * 64);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) av[s][e] = src[e];
+        for (int e = 0; e < MR / 2; ++e) {
+            const int r0 = 2 * e + (lane >> 5);
+            const int r = r0 < M ? r0 : M - 1;
+            const int piece = (lane & 31) ^ (r0 & 15);
+            dma16(p.A + (int64_t)r * K + (int64_t)cs * 256 + 8 * piece,
+                  area_lds + (uint32_t)(s * MR * 512 + e * 1024));
         }
     }
     // 2. code loads of all row-blocks, in the order step 4 consumes them (rows
@@ -576,18 +608,21 @@ __global__ __launch_bounds__(1024) void ternary_gemv_stream_kernel(GemmArgs p) {
             q[t][s] = *reinterpret_cast<const uint4*>(crow + (int64_t)(4 * cs + g) * 16);
         }
     }
-    // row scale and bias of the output this thread finishes in step 5
-    // (thread e < 64T: row n_base + 16 (e / 64) + e % 16)
-    float sc_e, bi_e;
-    {
-        const int e = (int)threadIdx.x % (T * kWave);
-        const int64_t n = n_base + 16 * (e / kWave) + (e & 15);
-        const int64_t nc = n < N ? n : N - 1;
-        sc_e = f16_bits_to_f32(p.scale[nc]);
-        bi_e = p.bias ? F16::to_f32(p.bias[nc]) : 0.0f;
-    }
 
-    // 3. operands a' (pair (d, i) of a chunk in dword 8 d + i) and the D share
+    // 3. wait for the activation DMA only (the T * CSW code loads issued after
+    //    it may still be in flight: completion is in order), read the operand
+    //    rows, then operands a' (pair (d, i) of a chunk in dword 8 d + i) and
+    //    the D share
+    static_assert(T * CSW <= 63, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(T * CSW) : "memory");
+    const int rd_row = i16 & (MR - 1);
+    uint4 av[CSW][8];
+#pragma unroll
+    for (int s = 0; s < CSW; ++s)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            av[s][e] = *reinterpret_cast<const uint4*>(area + s * MR * 512 + rd_row * 512 +
+                                                       16 * ((8 * g + e) ^ (rd_row & 15)));
     uint4 aw[CSW][8];
     float dl = 0.0f;
 #pragma unroll
@@ -661,7 +696,7 @@ __global__ __launch_bounds__(1024) void ternary_gemv_stream_kernel(GemmArgs p) {
         f32x4 v = acc[t];
 #pragma unroll
         for (int i = 0; i < 4; ++i) v[i] -= dsub[i];
-        red[(wave * T + t) * kWave + lane] = v;
+        red[wave * (kArea / 16) + t * kWave + lane] = v;
     }
     __syncthreads();
     if ((int)threadIdx.x < T * kWave) {  // T <= W
@@ -669,9 +704,18 @@ __global__ __launch_bounds__(1024) void ternary_gemv_stream_kernel(GemmArgs p) {
         const int t = e / kWave;
         const int l = e % kWave;
         f32x4 sum = red[t * kWave + l];
-        for (int w = 1; w < W; ++w) sum += red[(w * T + t) * kWave + l];
+        for (int w = 1; w < W; ++w) sum += red[w * (kArea / 16) + t * kWave + l];
         const int64_t n = n_base + 16 * t + (l & 15);
-        if (n < N) {
+        if (n < N && sa.S > 1) {
+            float* part = sa.ws + (int64_t)blockIdx.y * M * N;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int m = 4 * (l >> 4) + i;
+                if (m < M) part[(int64_t)m * N + n] = sum[i];
+            }
+        } else if (n < N) {
+            const float sc_e = f16_bits_to_f32(sc_bits);
+            const float bi_e = p.bias ? F16::to_f32(bi_bits) : 0.0f;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int m = 4 * (l >> 4) + i;
@@ -892,13 +936,17 @@ static hipError_t launch_gemv_lds_upt(const GemmArgs& a, const GemvPlan& pl, hip
     }
 }
 
-// Streaming kernel: fp16, 3 <= M <= 16, K <= 8192 (one or two chunk-sets per
-// wave, at most 16 waves); for M <= 2 the LDS kernel is faster, its per-wave
-// activation prep being cheaper than building the operand in every wave.  T row-blocks per workgroup: the fewest that keep
-// the grid within one workgroup per compute unit (at most 8; at most 4 with
-// two chunk-sets per wave, for registers).
+// Streaming kernel: fp16, 3 <= M <= 16, at most 32 chunk-sets (8192
+// columns) per workgroup (one or two per wave, at most 16 waves); for M <= 2
+// the LDS kernel is faster, its per-wave activation prep being cheaper than
+// building the operand in every wave.  T row-blocks per workgroup: the fewest
+// that keep the grid within one workgroup per compute unit (at most 8; at most
+// 4 with two chunk-sets per wave, for registers; at most the wave count, which
+// the final reduction needs).  The waves' LDS areas must fit the compute
+// unit's LDS, which rules out two chunk-sets per wave for M > 8.  S splits of
+// K when a workspace allows.
 struct StreamPlan {
-    int csw, waves, t;
+    int csw, waves, t, S, mr;
     size_t lds;
 };
 
@@ -913,50 +961,113 @@ int compute_units() {
     return v;
 }
 
-static bool gemv_stream_plan(const GemmArgs& a, StreamPlan* pl) {
-    if (a.bf16 || a.M < 3 || a.M > kGemvMaxM || a.K % 256 != 0) return false;
-    const int64_t cs = a.K / 256;
-    if (cs > 32) return false;
+// Geometry of the streaming kernel with K split S ways (false if it does not
+// fit: S must divide the chunk-sets, a split keeps at least four).
+static bool stream_geometry(const GemmArgs& a, int S, int64_t cus, StreamPlan* pl) {
+    const int64_t cs_all = a.K / 256;
+    if (S < 1 || cs_all % S != 0) return false;
+    const int64_t cs = cs_all / S;
+    if (cs > 32 || (S > 1 && cs < 4)) return false;
+    pl->S = S;
     pl->csw = cs <= 16 ? 1 : 2;
     pl->waves = (int)((cs + pl->csw - 1) / pl->csw);
     const int64_t nrb = (a.N + 15) / 16;
-    const int64_t cus = compute_units();
+    pl->mr = a.M <= 4 ? 4 : a.M <= 8 ? 8 : 16;
     const int tmax = pl->csw == 1 ? 8 : 4;
     int t = 1;
-    while (t < tmax && t < pl->waves && (nrb + t - 1) / t > cus) t *= 2;
+    while (t < tmax && 2 * t <= pl->waves && (nrb + t - 1) / t * S > cus) t *= 2;
     pl->t = t;
-    pl->lds = (size_t)pl->waves * t * kWave * 16;
-    return true;
+    pl->lds = (size_t)pl->waves * stream_wave_lds(pl->csw, pl->mr, t);
+    return pl->lds <= (size_t)kGemvLdsMaxBytes;
 }
 
-template <int CSW, int T>
-static hipError_t launch_gemv_stream(const GemmArgs& a, const StreamPlan& pl, hipStream_t s) {
-    static DeviceFlags lds_limit_set;
-    hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(&ternary_gemv_stream_kernel<CSW, T>),
-                                   kGemvLdsMaxBytes, lds_limit_set);
-    if (e != hipSuccess) return e;
-    const dim3 grid((unsigned)((a.N + 16 * T - 1) / (16 * T)));
-    ternary_gemv_stream_kernel<CSW, T><<<grid, dim3(pl.waves * kWave), pl.lds, s>>>(a);
-    return hipGetLastError();
+// Bytes one compute unit moves, as a cost: per workgroup the activations of
+// its K range (M * K/S * 2), its codes and, with a split, its fp32 partials
+// (written, then read back by the reduction), times the workgroups queued per
+// compute unit; a split also adds the reduction launch, counted as 160 KB
+// (what a compute unit takes in over the ~2.4 us a launch costs at the
+// measured ~65 KB/us per compute unit).
+static int64_t stream_cost(const GemmArgs& a, const StreamPlan& pl, int64_t cus) {
+    const int64_t kr = a.K / pl.S;
+    const int64_t per_wg = 2 * a.M * kr + (int64_t)pl.t * 16 * (kr / 4) +
+                           (pl.S > 1 ? (int64_t)pl.t * 16 * a.M * 8 : 0);
+    const int64_t nrb = (a.N + 15) / 16;
+    const int64_t wgs = (nrb + pl.t - 1) / pl.t * pl.S;
+    return (wgs + cus - 1) / cus * per_wg + (pl.S > 1 ? 160 * 1024 : 0);
 }
 
-hipError_t launch_ternary_gemv(const GemmArgs& a, hipStream_t s) {
-    StreamPlan sp;
-    if (gemv_stream_plan(a, &sp)) {
-        if (sp.csw == 1) {
-            switch (sp.t) {
-                case 1: return launch_gemv_stream<1, 1>(a, sp, s);
-                case 2: return launch_gemv_stream<1, 2>(a, sp, s);
-                case 4: return launch_gemv_stream<1, 4>(a, sp, s);
-                default: return launch_gemv_stream<1, 8>(a, sp, s);
-            }
-        }
-        switch (sp.t) {
-            case 1: return launch_gemv_stream<2, 1>(a, sp, s);
-            case 2: return launch_gemv_stream<2, 2>(a, sp, s);
-            default: return launch_gemv_stream<2, 4>(a, sp, s);
+// Cheapest streaming plan whose split fits `ws_bytes` of workspace.
+static bool gemv_stream_plan(const GemmArgs& a, size_t ws_bytes, StreamPlan* pl) {
+    if (a.bf16 || a.M < 3 || a.M > kGemvMaxM || a.K % 256 != 0) return false;
+    const int64_t cus = compute_units();
+    bool found = false;
+    int64_t best = 0;
+    for (int S = 1; S <= 16; ++S) {
+        StreamPlan c;
+        if (!stream_geometry(a, S, cus, &c)) continue;
+        if (S > 1 && ws_bytes < (size_t)S * (size_t)a.M * (size_t)a.N * sizeof(float)) continue;
+        const int64_t cost = stream_cost(a, c, cus);
+        if (!found || cost < best) {
+            *pl = c;
+            best = cost;
+            found = true;
         }
     }
+    return found;
+}
+
+size_t gemv_workspace_bytes(const GemmArgs& a) {
+    StreamPlan pl;
+    if (!gemv_stream_plan(a, SIZE_MAX, &pl) || pl.S == 1) return 0;
+    return (size_t)pl.S * (size_t)a.M * (size_t)a.N * sizeof(float);
+}
+
+template <int CSW, int T, int MR>
+static hipError_t launch_gemv_stream(const SplitArgs& sa, const StreamPlan& pl, hipStream_t s) {
+    static DeviceFlags lds_limit_set;
+    hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(&ternary_gemv_stream_kernel<CSW, T, MR>),
+                                   kGemvLdsMaxBytes, lds_limit_set);
+    if (e != hipSuccess) return e;
+    if (pl.lds != (size_t)pl.waves * stream_wave_lds(CSW, MR, T)) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)((sa.g.N + 16 * T - 1) / (16 * T)), (unsigned)sa.S);
+    ternary_gemv_stream_kernel<CSW, T, MR><<<grid, dim3(pl.waves * kWave), pl.lds, s>>>(sa);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    return sa.S > 1 ? launch_splitk_reduce(sa, s) : hipSuccess;
+}
+
+template <int MR>
+static hipError_t launch_gemv_stream_mr(const SplitArgs& sa, const StreamPlan& sp, hipStream_t s) {
+    if (sp.csw == 1) {
+        switch (sp.t) {
+            case 1: return launch_gemv_stream<1, 1, MR>(sa, sp, s);
+            case 2: return launch_gemv_stream<1, 2, MR>(sa, sp, s);
+            case 4: return launch_gemv_stream<1, 4, MR>(sa, sp, s);
+            default: return launch_gemv_stream<1, 8, MR>(sa, sp, s);
+        }
+    }
+    if constexpr (MR == 16) {
+        return hipErrorInvalidValue;  // 16 waves x 16 KB of activations exceed the LDS: the plan never asks for it
+    } else {
+        switch (sp.t) {
+            case 1: return launch_gemv_stream<2, 1, MR>(sa, sp, s);
+            case 2: return launch_gemv_stream<2, 2, MR>(sa, sp, s);
+            default: return launch_gemv_stream<2, 4, MR>(sa, sp, s);
+        }
+    }
+}
+
+static hipError_t launch_gemv_stream_t(const SplitArgs& sa, const StreamPlan& sp, hipStream_t s) {
+    if (sp.mr == 4) return launch_gemv_stream_mr<4>(sa, sp, s);
+    if (sp.mr == 8) return launch_gemv_stream_mr<8>(sa, sp, s);
+    return launch_gemv_stream_mr<16>(sa, sp, s);
+}
+
+hipError_t launch_ternary_gemv(const GemmArgs& a, hipStream_t s) { return launch_ternary_gemv(a, nullptr, 0, s); }
+
+hipError_t launch_ternary_gemv(const GemmArgs& a, void* workspace, size_t workspace_bytes, hipStream_t s) {
+    StreamPlan sp;
+    if (gemv_stream_plan(a, workspace ? workspace_bytes : 0, &sp))
+        return launch_gemv_stream_t(SplitArgs{a, static_cast<float*>(workspace), sp.S}, sp, s);
     GemvPlan pl;
     if (gemv_lds_plan(a, &pl)) {
         if (pl.rows16 == 2) {

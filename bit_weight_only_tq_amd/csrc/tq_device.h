@@ -127,6 +127,17 @@ struct BF16 {
     static __device__ __forceinline__ uint16_t from_f32_fast(float x) { return f32_to_bf16_rne(x); }
 };
 
+// 16 bytes per lane, global -> LDS at M0 + 16 * lane (M0 must be wave-uniform).
+// Issued through asm so that the compiler does not model the LDS write: its
+// conservative tracking would otherwise wait for every DMA in flight before
+// any LDS read, defeating the prefetch.  The kernel orders the DMA itself:
+// explicit vmcnt waits before the barrier that publishes a stage, and the
+// "memory" clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_addr) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :: "v"(gptr), "s"(lds_addr) : "memory", "m0");
+}
+
 // Sum over the 16 lanes of each DPP row (lanes 16r .. 16r+15); every lane of
 // the row receives its row's total.  Steps: swap neighbours, swap pairs,
 // mirror half-rows, mirror rows.  All 64 lanes must be active.

@@ -50,8 +50,23 @@ struct GemmArgs {
     uint16_t* C;            // [M, N]
 };
 
+// A call whose K range is split S ways: split z writes its fp32 partial sums
+// (no row scale, no bias) to ws[z][M][N]; launch_splitk_reduce then sums
+// the S partials of each output in order z = 0 .. S-1 and applies the row
+// scale and bias, so the result does not depend on scheduling.
+struct SplitArgs {
+    GemmArgs g;
+    float* ws;  // [S][M][N] fp32 partials, unused when S == 1
+    int S;
+};
+hipError_t launch_splitk_reduce(const SplitArgs& sa, hipStream_t s);  // gemm.hip
+
 // gemv.hip: small M (<= kGemvMaxM), weights streamed once per call.
 constexpr int kGemvMaxM = 16;
+// With a workspace of gemv_workspace_bytes() the streaming kernel may split
+// K (long-K, short-N shapes); without one it never does.
+size_t gemv_workspace_bytes(const GemmArgs& a);
+hipError_t launch_ternary_gemv(const GemmArgs& a, void* workspace, size_t workspace_bytes, hipStream_t s);
 hipError_t launch_ternary_gemv(const GemmArgs& a, hipStream_t s);         // picks the fastest eligible kernel
 hipError_t launch_ternary_gemv_simple(const GemmArgs& a, hipStream_t s);  // any dtype, any K % 64 == 0
 bool ternary_gemv_mfma_ok(const GemmArgs& a);                             // fp16, K % 256 == 0

@@ -243,6 +243,37 @@ def test_gemm_split_k(M, N, K, dt):
     assert torch.equal(outs[0].view(torch.int16), C2.view(torch.int16))
 
 
+@pytest.mark.parametrize("M,N,K", [(16, 4096, 14336), (3, 4100, 14336), (9, 8192, 28672), (5, 1000, 16384),
+                                   (16, 57344, 8192), (12, 8200, 8192)])
+def test_gemv_split_k(M, N, K):
+    """Small-M streaming kernel with K split across workgroups (workspace from
+    torch) and without a workspace (other kernels for K > 8192): both within
+    the tolerance on sampled output columns, ragged N, with bias; a repeated
+    split call is bit-identical."""
+    import torch
+    import bit_weight_only_tq_amd as tq
+    dev = require_gpu()
+    nbytes = tq.tq_gemm_workspace_bytes(M, N, K, path="gemv")
+    log(f"gemv split-K M={M} N={N} K={K} workspace={nbytes}")
+    W = synth.weights_device(N, K, synth.seed_for("vsk", N, K), dev)
+    codes, scale = tq.tq_pack(W)
+    cols = np.sort(np.random.default_rng(N + K + 1).choice(N, min(N, 192), replace=False))
+    idx = torch.from_numpy(cols).to(dev)
+    rc, rs = OT.ternary_pack(W.index_select(0, idx).cpu().numpy())
+    del W
+    wdq = OT.ternary_dequant(rc, rs, K)
+    A = synth.activations(M, K, synth.seed_for("vska", M, K), "f16")
+    bias = synth.activations(1, N, synth.seed_for("vskb", N), "f16")[0]
+    outs = []
+    for ws in ("auto", None):
+        C = tq.tq_gemm(A.to(dev), codes, scale, bias=bias.to(dev), path="gemv", workspace=ws)
+        check_close(C.index_select(1, idx), A, wdq, bias=bias[torch.from_numpy(cols)],
+                    label=f"gemv split {M}x{N}x{K} ws={ws}")
+        outs.append(C)
+    C2 = tq.tq_gemm(A.to(dev), codes, scale, bias=bias.to(dev), path="gemv")
+    assert torch.equal(outs[0].view(torch.int16), C2.view(torch.int16))
+
+
 @pytest.mark.parametrize("M,N,K", [(1, 20, 128), (3, 37, 384), (16, 300, 1024), (5, 16400, 256),
                                    (2, 64, 2048), (16, 17, 4096), (7, 1000, 14336)])
 def test_w4_ragged_shapes(M, N, K):
