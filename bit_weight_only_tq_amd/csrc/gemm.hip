@@ -507,6 +507,207 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(SplitArgs sa) {
 
 }  // namespace mm
 
+// ------------------------------------------------------------------------
+// Medium M, K % 256 == 0: the tile of the kernel above (16TM activation rows
+// x 256 weight rows, eight waves of 32 weight rows each, optional K split)
+// with 256-column K-steps in a 3-slot LDS ring filled two steps ahead, so
+// that each barrier covers 8TM MFMAs per wave and every DMA instruction
+// reads whole row segments:
+//  - codes: 256 rows x 64 bytes per step, 16 rows per instruction (lane l:
+//    row l/4, 16-byte chunk l%4); chunk c of row r sits at c ^ ((r/4) % 4)
+//    so that the 64 lanes' dword reads of a fragment hit 64 different banks;
+//  - activations: 16TM rows x 512 bytes per step, 2 rows per instruction
+//    (lane l: row l/32, chunk l%32); chunk c of row r at c ^ (r % 16).
+// Within a step, sub-step u (0..3) covers columns 64u .. 64u+63 exactly as
+// one K-step of the kernel above: MFMA s of lane group g takes the 8 columns
+// 64u + 16g + 8s .., codes dword u of the row segment, unpacked the same way.
+namespace mm2 {
+
+constexpr int BN = 256;
+constexpr int BK = 256;
+constexpr int kThreads = 512;
+constexpr int TN = 2;
+constexpr int kStages = 3;
+constexpr int kBBytes = BN * (BK / 4);  // 16 KB of codes per step
+template <int TM> constexpr int a_bytes() { return 16 * TM * BK * 2; }
+template <int TM> constexpr int stage_bytes() { return a_bytes<TM>() + kBBytes; }
+template <int TM> constexpr size_t lds_bytes() { return (size_t)kStages * stage_bytes<TM>() + 16 * TM * 4; }
+
+template <class T, int TM>
+__global__ __launch_bounds__(kThreads) void tile_kernel(SplitArgs sa) {
+    typedef typename Mfma<T>::vec vec;
+    constexpr int BM = 16 * TM;
+    constexpr int kABytes = a_bytes<TM>();
+    constexpr int kStageBytes = stage_bytes<TM>();
+    const GemmArgs& p = sa.g;
+    extern __shared__ uint4 smem_mm2[];
+    uint8_t* lds = reinterpret_cast<uint8_t*>(smem_mm2);
+    const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)smem_mm2;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4;
+    const int i16 = lane & 15;
+    const int64_t n0 = (int64_t)blockIdx.x * BN;
+    const int64_t m0 = (int64_t)blockIdx.y * BM;
+    const int z = blockIdx.z;
+    const int64_t M = p.M, N = p.N, K = p.K;
+    const int64_t rb = K / 4;
+    const int nk = (int)(K / BK);
+    const int ks0 = (int)((int64_t)nk * z / sa.S);
+    const int ks1 = (int)((int64_t)nk * (z + 1) / sa.S);  // > ks0: S <= nk
+    const uint32_t magic_v = vgpr_const<Mfma<T>::kMagicPair>();
+    const uint32_t mask3 = sgpr_const<0x00030003u>();
+    const uint32_t mask33 = sgpr_const<0x33333333u>();
+
+    // DMA sources.  Activations: wave w issues instructions w*TM .. w*TM+TM-1
+    // (rows 2i, 2i+1 of the tile; rows past M re-read row M-1).  Codes: wave w
+    // issues instructions 2w, 2w+1 (rows 16j .. 16j+15; rows past N re-read
+    // row N-1).  Offsets are relative to the K-step's first column.
+    const uint16_t* a_src[TM];
+#pragma unroll
+    for (int u = 0; u < TM; ++u) {
+        const int r = 2 * (wave * TM + u) + (lane >> 5);
+        const int64_t m = m0 + r < M ? m0 + r : M - 1;
+        a_src[u] = p.A + m * K + 8 * ((lane & 31) ^ (r & 15));
+    }
+    const uint8_t* b_src[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int r = 16 * (2 * wave + u) + (lane >> 2);
+        const int64_t n = n0 + r < N ? n0 + r : N - 1;
+        b_src[u] = static_cast<const uint8_t*>(p.wq) + n * rb + 16 * ((lane & 3) ^ ((r >> 2) & 3));
+    }
+    auto issue = [&](int kstep, int stage) {
+        const uint32_t st = lds_base + (uint32_t)(stage * kStageBytes);
+#pragma unroll
+        for (int u = 0; u < TM; ++u) dma16(a_src[u] + (int64_t)kstep * BK, st + 1024u * (wave * TM + u));
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+            dma16(b_src[u] + (int64_t)kstep * (BK / 4), st + kABytes + 1024u * (2 * wave + u));
+    };
+    // the older of the two K-steps in flight has landed (in-order completion:
+    // only the newer step's TM + 2 DMAs of this wave may remain)
+    auto wait_older = [&]() {
+        if constexpr (TM == 2) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+    };
+    static_assert(TM == 2 || TM == 4, "wait counts above assume TM + 2 DMAs per step");
+
+    f32x4 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float rsum = 0.0f;  // row sums of m-tile `wave`, kept by waves 0 .. TM-1
+    int b_row[TN], b_swz[TN];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+        b_row[j] = 32 * wave + 16 * j + i16;
+        b_swz[j] = (b_row[j] >> 2) & 3;
+    }
+
+    issue(ks0, 0);
+    issue(ks0 + 1 < ks1 ? ks0 + 1 : ks1 - 1, 1);
+    wait_older();
+    stage_barrier();
+    for (int kt = ks0; kt < ks1; ++kt) {
+        const int it = kt - ks0;
+        // Unconditional so the per-wave counts stay exact: past the end the DMA
+        // re-reads the last K-step into the slot nobody reads any more.
+        issue(kt + 2 < ks1 ? kt + 2 : ks1 - 1, (it + 2) % kStages);
+        const uint8_t* sbase = lds + (it % kStages) * kStageBytes;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            uint32_t E[TN], O[TN];
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const uint32_t x = *reinterpret_cast<const uint32_t*>(sbase + kABytes + b_row[j] * 64 +
+                                                                      16 * (u ^ b_swz[j]) + 4 * g);
+                E[j] = x & mask33;
+                O[j] = (x >> 2) & mask33;
+            }
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const int c = 8 * u + 2 * g + s;
+                vec af[TM];
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+                    af[i] = __builtin_bit_cast(vec, *reinterpret_cast<const uint4*>(sbase + (16 * i + i16) * 512 +
+                                                                                   16 * (c ^ i16)));
+                uint4 bop[TN];
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    const uint32_t y = __builtin_amdgcn_perm(O[j], E[j], s ? 0x07060302u : 0x05040100u);
+                    bop[j] = make_uint4((y & mask3) | magic_v, ((y >> 4) & mask3) | magic_v,
+                                        ((y >> 8) & mask3) | magic_v, ((y >> 12) & mask3) | magic_v);
+                }
+#pragma unroll
+                for (int i = 0; i < TM; ++i) {
+                    if (i == wave) {  // wave-uniform
+                        const uint4 v = __builtin_bit_cast(uint4, af[i]);
+                        rsum = Mfma<T>::dot2(v.x, Mfma<T>::kOnePair, rsum);
+                        rsum = Mfma<T>::dot2(v.y, Mfma<T>::kOnePair, rsum);
+                        rsum = Mfma<T>::dot2(v.z, Mfma<T>::kOnePair, rsum);
+                        rsum = Mfma<T>::dot2(v.w, Mfma<T>::kOnePair, rsum);
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    const vec bf = __builtin_bit_cast(vec, bop[j]);
+#pragma unroll
+                    for (int i = 0; i < TM; ++i) acc[i][j] = Mfma<T>::mma(af[i], bf, acc[i][j]);
+                }
+            }
+        }
+        wait_older();       // K-step kt + 1 has landed
+        stage_barrier();    // ... for every wave, and nobody reads step kt any more
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+
+    float* rs_lds = reinterpret_cast<float*>(lds + kStages * kStageBytes);
+    {
+        float r = rsum;
+        r += __shfl_xor(r, 16, kWave);
+        r += __shfl_xor(r, 32, kWave);
+        if (wave < TM && g == 0) rs_lds[16 * wave + i16] = r;
+    }
+    __syncthreads();
+
+    const bool final_out = sa.S == 1;
+    float sc[TN], bi[TN];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+        const int64_t n = n0 + 32 * wave + 16 * j + i16;
+        const int64_t nc = n < N ? n : N - 1;
+        sc[j] = f16_bits_to_f32(p.scale[nc]);
+        bi[j] = p.bias ? T::to_f32(p.bias[nc]) : 0.0f;
+    }
+    float* wsz = final_out ? nullptr : sa.ws + (int64_t)z * M * N;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = 16 * i + 4 * g + r;
+            const int64_t m = m0 + row;
+            if (m >= M) continue;
+            const float corr = Mfma<T>::kBias * rs_lds[row];
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const int64_t n = n0 + 32 * wave + 16 * j + i16;
+                if (n >= N) continue;
+                const float v = acc[i][j][r] - corr;
+                if (final_out) p.C[m * N + n] = T::from_f32_fast(v * sc[j] + bi[j]);
+                else wsz[m * N + n] = v;
+            }
+        }
+    }
+}
+
+}  // namespace mm2
+
 
 }  // namespace
 
@@ -569,14 +770,29 @@ hipError_t launch_ternary_gemm(const GemmArgs& a, void* workspace, size_t worksp
     return a.bf16 ? launch_v3<BF16>(sa, s) : launch_v3<F16>(sa, s);
 }
 
-// Split count of the medium-M kernel: none when the row x column tiles
-// already cover three quarters of the compute units, else enough splits to
-// give every compute unit a workgroup, each split keeping >= 8 K-steps.
+// Split count of the medium-M kernels.
+//  K % 256 == 0 (mm2): one workgroup fills a compute unit (the ring takes
+//  96 or 144 KB of LDS), so the split count is the largest that keeps the
+//  T tiles x S splits within one round on the compute units (at most 16,
+//  each split keeping two K-steps); measured on the Llama-3-70B shapes at
+//  M = 17 .. 64 this beat both fewer splits (longer K loops) and more (a
+//  second round), the fp32 partials costing little in comparison.
+//  Otherwise (mm): none when the row x column tiles already cover three
+//  quarters of the compute units, else enough splits to give every compute
+//  unit a workgroup, each split keeping >= 8 K-steps.
 int medium_m_splits(int64_t M, int64_t N, int64_t K, int compute_units) {
     const int64_t tm = M <= 32 ? 2 : 4;
     const int64_t tiles = ((N + mm::BN - 1) / mm::BN) * ((M + 16 * tm - 1) / (16 * tm));
-    if (4 * tiles >= 3 * (int64_t)compute_units) return 1;
-    int64_t S = ((int64_t)compute_units + tiles - 1) / tiles;
+    const int64_t cus = compute_units > 0 ? compute_units : 1;
+    if (K % mm2::BK == 0) {
+        int64_t S = cus / tiles;
+        const int64_t nk = K / mm2::BK;
+        if (S > 16) S = 16;
+        if (S > nk / 2) S = nk / 2;
+        return S < 1 ? 1 : (int)S;
+    }
+    if (4 * tiles >= 3 * cus) return 1;
+    int64_t S = (cus + tiles - 1) / tiles;
     const int64_t smax = (K / mm::BK) / 8;
     if (S > smax) S = smax;
     return S < 1 ? 1 : (int)S;
@@ -601,13 +817,37 @@ static hipError_t launch_mm(const SplitArgs& sa, hipStream_t s) {
     return e;
 }
 
+template <class T, int TM>
+static hipError_t launch_mm2(const SplitArgs& sa, hipStream_t s) {
+    static DeviceFlags lds_limit_set;
+    hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(&mm2::tile_kernel<T, TM>), (int)mm2::lds_bytes<TM>(),
+                                   lds_limit_set);
+    if (e != hipSuccess) return e;
+    const GemmArgs& a = sa.g;
+    if (sa.S < 1 || sa.S > a.K / mm2::BK) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)((a.N + mm2::BN - 1) / mm2::BN), (unsigned)((a.M + 16 * TM - 1) / (16 * TM)), (unsigned)sa.S);
+    mm2::tile_kernel<T, TM><<<grid, mm2::kThreads, mm2::lds_bytes<TM>(), s>>>(sa);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (sa.S > 1) e = launch_splitk_reduce(sa, s);
+    return e;
+}
+
 // Medium M with an optional workspace: S splits when `workspace` holds
 // medium_m_workspace_bytes(), a single pass over K otherwise.
 hipError_t launch_ternary_medium(const GemmArgs& a, void* workspace, size_t workspace_bytes, int compute_units,
                                  hipStream_t s) {
     SplitArgs sa{a, static_cast<float*>(workspace), medium_m_splits(a.M, a.N, a.K, compute_units)};
     if (sa.S > 1 && (!workspace || workspace_bytes < medium_m_workspace_bytes(a.M, a.N, a.K, compute_units))) sa.S = 1;
+    return launch_ternary_medium_split(sa, s);
+}
+
+hipError_t launch_ternary_medium_split(const SplitArgs& sa, hipStream_t s) {
+    const GemmArgs& a = sa.g;
     const bool small = a.M <= 32;
+    if (a.K % mm2::BK == 0) {
+        if (a.bf16) return small ? launch_mm2<BF16, 2>(sa, s) : launch_mm2<BF16, 4>(sa, s);
+        return small ? launch_mm2<F16, 2>(sa, s) : launch_mm2<F16, 4>(sa, s);
+    }
     if (a.bf16) return small ? launch_mm<BF16, 2>(sa, s) : launch_mm<BF16, 4>(sa, s);
     return small ? launch_mm<F16, 2>(sa, s) : launch_mm<F16, 4>(sa, s);
 }

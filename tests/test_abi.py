@@ -73,7 +73,10 @@ def test_workspace_query():
     wb = _lib.tq_gemm_workspace_bytes
     assert wb(1, 4096, 4096) == 0 and wb(4096, 4096, 4096) == 0
     assert wb(64, 8192, 8192) == 8 * 64 * 8192 * 4      # 32 tiles -> 8 splits
-    assert wb(32, 1024, 8192) == 16 * 32 * 1024 * 4     # capped at 8 K-steps per split
+    assert wb(32, 1024, 8192) == 16 * 32 * 1024 * 4     # 4 tiles: capped at 16 splits
+    assert wb(40, 10240, 8192) == 6 * 40 * 10240 * 4    # 40 tiles: 6 splits keep one round on 256 CUs
+    assert wb(100, 2000, 1024) == 2 * 100 * 2000 * 4    # 4 K-steps of 256: two per split
+    assert wb(100, 2000, 4160) == 8 * 100 * 2000 * 4    # K % 256 != 0: 64-column kernel, >= 8 K-steps per split
     assert wb(64, 57344, 8192) == 0                     # 224 tiles: no split
     assert wb(64, 8192, 96) == 0                        # K % 64 != 0
     # large M: 256 x 256 tiles, one per compute unit, >= 16 K-steps per split

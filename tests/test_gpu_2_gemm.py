@@ -186,16 +186,19 @@ def test_deterministic_and_canary(path, M):
     assert bool((buf[M * N:] == -12345.0).all())
 
 
-@pytest.mark.parametrize("M,N,K", [(17, 8192, 8192), (64, 1024, 8192), (32, 8192, 28672), (100, 2000, 4096)])
-def test_medium_split_k(M, N, K):
+@pytest.mark.parametrize("M,N,K,dt", [(17, 8192, 8192, "f16"), (64, 1024, 8192, "f16"), (32, 8192, 28672, "f16"),
+                                      (100, 2000, 4096, "f16"), (48, 10240, 8192, "bf16"), (64, 8192, 28672, "bf16"),
+                                      (40, 3000, 4160, "f16"), (200, 700, 4160, "bf16")])
+def test_medium_split_k(M, N, K, dt):
     """Medium M with K split across workgroups (workspace from torch) and
     without a workspace (one pass over K): both within the tolerance, on
-    sampled output columns at full 70B-like sizes."""
+    sampled output columns at full 70B-like sizes; K % 256 != 0 takes the
+    64-column-step kernel."""
     import torch
     import bit_weight_only_tq_amd as tq
     dev = require_gpu()
-    nbytes = tq.tq_gemm_workspace_bytes(M, N, K, path="stream_mfma")
-    log(f"medium split-K M={M} N={N} K={K} workspace={nbytes}")
+    nbytes = tq.tq_gemm_workspace_bytes(M, N, K, dt, path="stream_mfma")
+    log(f"medium split-K M={M} N={N} K={K} {dt} workspace={nbytes}")
     W = synth.weights_device(N, K, synth.seed_for("msk", N, K), dev)
     codes, scale = tq.tq_pack(W)
     cols = np.sort(np.random.default_rng(N + K).choice(N, min(N, 192), replace=False))
@@ -203,12 +206,12 @@ def test_medium_split_k(M, N, K):
     rc, rs = OT.ternary_pack(W.index_select(0, idx).cpu().numpy())
     del W
     wdq = OT.ternary_dequant(rc, rs, K)
-    A = synth.activations(M, K, synth.seed_for("mska", M, K), "f16")
-    bias = synth.activations(1, N, synth.seed_for("mskb", N), "f16")[0]
+    A = synth.activations(M, K, synth.seed_for("mska", M, K), dt)
+    bias = synth.activations(1, N, synth.seed_for("mskb", N), dt)[0]
     for ws in ("auto", None):
         C = tq.tq_gemm(A.to(dev), codes, scale, bias=bias.to(dev), path="stream_mfma", workspace=ws)
         check_close(C.index_select(1, idx), A, wdq, bias=bias[torch.from_numpy(cols)],
-                    label=f"medium {M}x{N}x{K} ws={ws}")
+                    label=f"medium {M}x{N}x{K} {dt} ws={ws}")
 
 
 @pytest.mark.parametrize("M,N,K", [(2048, 4096, 14336), (300, 1000, 4096), (257, 300, 2048), (256, 4096, 4096)])
