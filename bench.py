@@ -233,7 +233,7 @@ def run_medium(dev, copies=8, iters=16):
     import synth
     stream = torch.cuda.current_stream()
     res = {"metric": "ternary medium-M path (K split across workgroups), one Llama-3-70B layer",
-           "kernel": "mm::tile_kernel + mm::splitk_reduce_kernel"}
+           "kernel": "mm3::tile_kernel (fp16, K % 256 == 0) + mm::splitk_reduce_kernel"}
     for name, (N, K) in layer_shapes(True, "70b"):
         W = synth.weights_device(N, K, synth.seed_for("benchmm", name), dev)
         codes, scale = tq.tq_pack(W)

@@ -708,6 +708,228 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(SplitArgs sa) {
 
 }  // namespace mm2
 
+// ------------------------------------------------------------------------
+// Medium M, fp16, K % 256 == 0: the tiles, DMA layouts and split of mm2, but
+// the codes are unpacked with the fp16 a' scheme (one v_and_or_b32 per
+// operand register instead of about two and a half).  That needs the
+// activations paired and pre-scaled by 1/4^s, which is done once per K-step
+// for the whole workgroup, in place in the ring slot: thread t owns the
+// 16-column groups (row t/16 + 32p, group t%16) and rewrites each group's two
+// 16-byte chunks (columns 16G..16G+7 and 16G+8..) as its a' pairs for fields
+// 0..3 and 4..7, keeping the chunk positions (c ^ (r % 16)); it also sums
+// its share of D[m] = sum_k a'_k (1024 + 4^s(k)), the term the accumulators
+// carry on top of sum_k a_k t_k.  The prep of step k+1 shares a phase with
+// the MFMAs of step k, so one barrier per step still suffices:
+//   issue DMA of step k + R - 1; prep step k + 1; contract step k;
+//   wait for the DMA of step k + 2; barrier,
+// with R = 4 ring slots for 32 activation rows and 3 for 64 (LDS).
+// Sub-step u, half h of a K-step: lane group g contracts 16-column group
+// G = 4u + g, fields 4h..4h+3, against code dword g of row chunk u.
+namespace mm3 {
+
+constexpr int BN = 256;
+constexpr int BK = 256;
+constexpr int kThreads = 512;
+constexpr int TN = 2;
+constexpr int kBBytes = BN * (BK / 4);  // 16 KB of codes per step
+template <int TM> constexpr int a_bytes() { return 16 * TM * BK * 2; }
+template <int TM> constexpr int stage_bytes() { return a_bytes<TM>() + kBBytes; }
+template <int TM> constexpr int slots() { return TM == 2 ? 4 : 3; }
+template <int TM> constexpr size_t lds_bytes() { return (size_t)slots<TM>() * stage_bytes<TM>() + 16 * TM * 4; }
+
+// In-place a' prep of one 16-column group of one activation row; returns
+// its share of D.
+__device__ __forceinline__ float prep_group(uint8_t* row, int G, int swz) {
+    uint4* p0 = reinterpret_cast<uint4*>(row + 16 * ((2 * G) ^ swz));
+    uint4* p1 = reinterpret_cast<uint4*>(row + 16 * ((2 * G + 1) ^ swz));
+    uint4 av[2] = {*p0, *p1};  // columns 16G .. 16G+7, 16G+8 .. 16G+15
+    const uint4 f03 = make_uint4(a_pair<0, 0>(av), a_pair<0, 1>(av), a_pair<0, 2>(av), a_pair<0, 3>(av));
+    const uint4 f47 = make_uint4(a_pair<0, 4>(av), a_pair<0, 5>(av), a_pair<0, 6>(av), a_pair<0, 7>(av));
+    *p0 = f03;
+    *p1 = f47;
+    float d = 0.0f;
+    d = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, f03.x), __builtin_bit_cast(f16x2, one_pattern<0>()), d, false);
+    d = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, f03.y), __builtin_bit_cast(f16x2, one_pattern<1>()), d, false);
+    d = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, f03.z), __builtin_bit_cast(f16x2, one_pattern<2>()), d, false);
+    d = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, f03.w), __builtin_bit_cast(f16x2, one_pattern<3>()), d, false);
+    d = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, f47.x), __builtin_bit_cast(f16x2, one_pattern<4>()), d, false);
+    d = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, f47.y), __builtin_bit_cast(f16x2, one_pattern<5>()), d, false);
+    d = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, f47.z), __builtin_bit_cast(f16x2, one_pattern<6>()), d, false);
+    d = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, f47.w), __builtin_bit_cast(f16x2, one_pattern<7>()), d, false);
+    return d;
+}
+
+template <int TM>
+__global__ __launch_bounds__(kThreads) void tile_kernel(SplitArgs sa) {
+    constexpr int BM = 16 * TM;
+    constexpr int kABytes = a_bytes<TM>();
+    constexpr int kStageBytes = stage_bytes<TM>();
+    constexpr int R = slots<TM>();
+    constexpr int P = TM + 2;  // DMAs per wave per K-step
+    const GemmArgs& p = sa.g;
+    extern __shared__ uint4 smem_mm3[];
+    uint8_t* lds = reinterpret_cast<uint8_t*>(smem_mm3);
+    const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)smem_mm3;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4;
+    const int i16 = lane & 15;
+    const int64_t n0 = (int64_t)blockIdx.x * BN;
+    const int64_t m0 = (int64_t)blockIdx.y * BM;
+    const int z = blockIdx.z;
+    const int64_t M = p.M, N = p.N, K = p.K;
+    const int64_t rb = K / 4;
+    const int nk = (int)(K / BK);
+    const int ks0 = (int)((int64_t)nk * z / sa.S);
+    const int ks1 = (int)((int64_t)nk * (z + 1) / sa.S);  // > ks0: S <= nk
+    const uint32_t magic_v = vgpr_const<kMagic2>();
+
+    const uint16_t* a_src[TM];
+#pragma unroll
+    for (int u = 0; u < TM; ++u) {
+        const int r = 2 * (wave * TM + u) + (lane >> 5);
+        const int64_t m = m0 + r < M ? m0 + r : M - 1;
+        a_src[u] = p.A + m * K + 8 * ((lane & 31) ^ (r & 15));
+    }
+    const uint8_t* b_src[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int r = 16 * (2 * wave + u) + (lane >> 2);
+        const int64_t n = n0 + r < N ? n0 + r : N - 1;
+        b_src[u] = static_cast<const uint8_t*>(p.wq) + n * rb + 16 * ((lane & 3) ^ ((r >> 2) & 3));
+    }
+    auto issue = [&](int kstep, int slot) {
+        const uint32_t st = lds_base + (uint32_t)(slot * kStageBytes);
+#pragma unroll
+        for (int u = 0; u < TM; ++u) dma16(a_src[u] + (int64_t)kstep * BK, st + 1024u * (wave * TM + u));
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+            dma16(b_src[u] + (int64_t)kstep * (BK / 4), st + kABytes + 1024u * (2 * wave + u));
+    };
+    auto clamp_step = [&](int k) { return k < ks1 ? k : ks1 - 1; };
+
+    // prep units of this thread: row tid/16 + 32q, group tid%16
+    float dsum[TM / 2];
+#pragma unroll
+    for (int q = 0; q < TM / 2; ++q) dsum[q] = 0.0f;
+    auto prep = [&](int slot) {
+#pragma unroll
+        for (int q = 0; q < TM / 2; ++q) {
+            const int r = (tid >> 4) + 32 * q;
+            dsum[q] += prep_group(lds + slot * kStageBytes + r * 512, tid & 15, r & 15);
+        }
+    };
+
+    f32x4 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    int b_off[TN], b_swz[TN];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+        const int row = 32 * wave + 16 * j + i16;
+        b_off[j] = kABytes + row * 64 + 4 * g;
+        b_swz[j] = (row >> 2) & 3;
+    }
+
+    // prologue: steps 0 .. R-2 in flight, step 0 prepped, step 1 landed
+#pragma unroll
+    for (int u = 0; u < R - 1; ++u) issue(clamp_step(ks0 + u), u);
+    if constexpr (R == 4) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * P) : "memory");
+    else asm volatile("s_waitcnt vmcnt(%0)" :: "n"(P) : "memory");
+    stage_barrier();
+    prep(0);
+    if constexpr (R == 4) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(P) : "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    stage_barrier();
+    for (int kt = ks0; kt < ks1; ++kt) {
+        const int it = kt - ks0;
+        // Unconditional so the per-wave counts stay exact: past the end the DMA
+        // re-reads the last K-step into a slot nobody reads any more.
+        issue(clamp_step(kt + R - 1), (it + R - 1) % R);
+        if (kt + 1 < ks1) prep((it + 1) % R);
+        const uint8_t* sbase = lds + (it % R) * kStageBytes;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            uint32_t x[TN], y[TN];
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                x[j] = *reinterpret_cast<const uint32_t*>(sbase + b_off[j] + 16 * (u ^ b_swz[j]));
+                y[j] = x[j] >> 10;
+            }
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int q = 2 * (4 * u + g) + h;
+                f16x8 af[TM];
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+                    af[i] = __builtin_bit_cast(f16x8, *reinterpret_cast<const uint4*>(sbase + (16 * i + i16) * 512 +
+                                                                                     16 * (q ^ i16)));
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    const uint4 bw = h == 0 ? make_uint4(field_pair<0>(x[j], y[j], magic_v), field_pair<1>(x[j], y[j], magic_v),
+                                                         field_pair<2>(x[j], y[j], magic_v), field_pair<3>(x[j], y[j], magic_v))
+                                            : make_uint4(field_pair<4>(x[j], y[j], magic_v), field_pair<5>(x[j], y[j], magic_v),
+                                                         field_pair<6>(x[j], y[j], magic_v), field_pair<7>(x[j], y[j], magic_v));
+                    const f16x8 bf = __builtin_bit_cast(f16x8, bw);
+#pragma unroll
+                    for (int i = 0; i < TM; ++i)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf, acc[i][j], 0, 0, 0);
+                }
+            }
+        }
+        // the DMA of step kt + 2 has landed (only steps kt + 3 .. may remain)
+        if constexpr (R == 4) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(P) : "memory");
+        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        stage_barrier();
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+
+    // D[m]: the 16 groups of a row sit on 16 neighbouring lanes, summed in a fixed order
+    float* d_lds = reinterpret_cast<float*>(lds + R * kStageBytes);
+#pragma unroll
+    for (int q = 0; q < TM / 2; ++q) {
+        const float d = row16_sum(dsum[q]);
+        if ((tid & 15) == 0) d_lds[(tid >> 4) + 32 * q] = d;
+    }
+    __syncthreads();
+
+    const bool final_out = sa.S == 1;
+    float sc[TN], bi[TN];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+        const int64_t n = n0 + 32 * wave + 16 * j + i16;
+        const int64_t nc = n < N ? n : N - 1;
+        sc[j] = f16_bits_to_f32(p.scale[nc]);
+        bi[j] = p.bias ? F16::to_f32(p.bias[nc]) : 0.0f;
+    }
+    float* wsz = final_out ? nullptr : sa.ws + (int64_t)z * M * N;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = 16 * i + 4 * g + r;
+            const int64_t m = m0 + row;
+            if (m >= M) continue;
+            const float corr = d_lds[row];
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const int64_t n = n0 + 32 * wave + 16 * j + i16;
+                if (n >= N) continue;
+                const float v = acc[i][j][r] - corr;
+                if (final_out) p.C[m * N + n] = F16::from_f32_fast(v * sc[j] + bi[j]);
+                else wsz[m * N + n] = v;
+            }
+        }
+    }
+}
+
+}  // namespace mm3
+
 
 }  // namespace
 
@@ -832,6 +1054,21 @@ static hipError_t launch_mm2(const SplitArgs& sa, hipStream_t s) {
     return e;
 }
 
+template <int TM>
+static hipError_t launch_mm3(const SplitArgs& sa, hipStream_t s) {
+    static DeviceFlags lds_limit_set;
+    hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(&mm3::tile_kernel<TM>), (int)mm3::lds_bytes<TM>(),
+                                   lds_limit_set);
+    if (e != hipSuccess) return e;
+    const GemmArgs& a = sa.g;
+    if (sa.S < 1 || sa.S > a.K / mm3::BK) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)((a.N + mm3::BN - 1) / mm3::BN), (unsigned)((a.M + 16 * TM - 1) / (16 * TM)), (unsigned)sa.S);
+    mm3::tile_kernel<TM><<<grid, mm3::kThreads, mm3::lds_bytes<TM>(), s>>>(sa);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (sa.S > 1) e = launch_splitk_reduce(sa, s);
+    return e;
+}
+
 // Medium M with an optional workspace: S splits when `workspace` holds
 // medium_m_workspace_bytes(), a single pass over K otherwise.
 hipError_t launch_ternary_medium(const GemmArgs& a, void* workspace, size_t workspace_bytes, int compute_units,
@@ -846,7 +1083,7 @@ hipError_t launch_ternary_medium_split(const SplitArgs& sa, hipStream_t s) {
     const bool small = a.M <= 32;
     if (a.K % mm2::BK == 0) {
         if (a.bf16) return small ? launch_mm2<BF16, 2>(sa, s) : launch_mm2<BF16, 4>(sa, s);
-        return small ? launch_mm2<F16, 2>(sa, s) : launch_mm2<F16, 4>(sa, s);
+        return small ? launch_mm3<2>(sa, s) : launch_mm3<4>(sa, s);
     }
     if (a.bf16) return small ? launch_mm<BF16, 2>(sa, s) : launch_mm<BF16, 4>(sa, s);
     return small ? launch_mm<F16, 2>(sa, s) : launch_mm<F16, 4>(sa, s);

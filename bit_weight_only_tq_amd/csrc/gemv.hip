@@ -146,46 +146,6 @@ __global__ __launch_bounds__(kGemvWaves * kWave) void w4_gemv_kernel(GemmArgs p)
 // 4(j%2)..4(j%2)+3 and their partners.  Wave partials meet in LDS and are
 // summed in a fixed order: deterministic, no atomics.
 
-constexpr uint32_t kMagic2 = 0x64006400u;  // (1024.0, 1024.0) as fp16
-
-template <int I>
-__device__ __forceinline__ uint32_t field_pair(uint32_t x, uint32_t y, uint32_t magic_v) {
-    if constexpr (I < 5) return (x & sgpr_const<(0x00030003u << (2 * I))>()) | magic_v;
-    else return (y & sgpr_const<(0x00030003u << (2 * (I - 5)))>()) | magic_v;
-}
-
-// 1 / 4^s for field I, as an fp16 pair.
-template <int I>
-__device__ __forceinline__ f16x2 inv_mult() {
-    constexpr int s = I < 5 ? I : I - 5;
-    const _Float16 v = (_Float16)(1.0f / (float)(1 << (2 * s)));
-    return f16x2{v, v};
-}
-
-// -(1024 + 4^s) for field I in both halves (the code-01 pattern, negated).
-template <int I>
-__device__ __forceinline__ constexpr uint32_t neg_one_pattern() {
-    constexpr int s = I < 5 ? I : I - 5;
-    return 0xE400E400u | (0x00010001u << (2 * s));
-}
-
-// a' pair for field I of code dword D: (a[16D+I], a[16D+I+8]) / 4^s(I).
-template <int D, int I>
-__device__ __forceinline__ uint32_t a_pair(const uint4 av[8]) {
-    const uint4& lo4 = av[2 * D];
-    const uint4& hi4 = av[2 * D + 1];
-    constexpr int c = I / 2;
-    const uint32_t lo = c == 0 ? lo4.x : c == 1 ? lo4.y : c == 2 ? lo4.z : lo4.w;
-    const uint32_t hi = c == 0 ? hi4.x : c == 1 ? hi4.y : c == 2 ? hi4.z : hi4.w;
-    const uint32_t pr = __builtin_amdgcn_perm(hi, lo, (I & 1) ? 0x07060302u : 0x05040100u);
-    const f16x2 v = __builtin_bit_cast(f16x2, pr) * inv_mult<I>();
-    return __builtin_bit_cast(uint32_t, v);
-}
-
-__device__ __forceinline__ uint32_t dword_of(const uint4& q, int d) {
-    return d == 0 ? q.x : d == 1 ? q.y : d == 2 ? q.z : q.w;
-}
-
 template <int R, int W>
 __global__ __launch_bounds__(W * kWave) void ternary_gemv_mfma_kernel(GemmArgs p) {
     __shared__ f32x4 red[W][R][kWave];
@@ -321,11 +281,6 @@ __global__ __launch_bounds__(W * kWave) void ternary_gemv_mfma_kernel(GemmArgs p
 //    stored).  Its D share is subtracted from its partials.
 // 4. Wave partials meet in LDS; after one barrier a fixed-order sum, then the
 //    row scale and bias.
-template <int I>
-__device__ __forceinline__ constexpr uint32_t one_pattern() {  // (1024 + 4^s) in both halves
-    constexpr int s = I < 5 ? I : I - 5;
-    return 0x64006400u | (0x00010001u << (2 * s));
-}
 
 // LDS layout of the kernel below (byte offsets): per wave, a' [M][4 CSW
 // chunks][128 bytes] then D partials [M][CSW floats, padded to 16 bytes];
