@@ -37,6 +37,8 @@ SIGNATURES = {
     "tq_gemm_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32, _i32]),
     "w4a16_gemm": (_i32, [_vp, _i32, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _vp]),
     "w4a16_gemm_ex": (_i32, [_vp, _i32, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _vp, _i32]),
+    "w4a16_gemm_ws": (_i32, [_vp, _i32, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp, _i32]),
+    "w4a16_gemm_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32, _i64]),
     "tq_select_path": (_i32, [_i32, _i64, _i64, _i64, _i32]),
     "tq_status_str": (ctypes.c_char_p, [_i32]),
     "tq_abi_version": (_i32, []),
@@ -185,15 +187,33 @@ def tq_gemm(A, codes, scale, bias=None, out=None, path: str = "auto", workspace=
     return C
 
 
-def w4a16_gemm(A, qweight, scales, bias=None, out=None, group_size: int = 128, path: str = "auto"):
-    """C = A @ dequant(qweight, scales)^T (+ bias); A [M, K] fp16/bf16."""
+def w4a16_gemm_workspace_bytes(M: int, N: int, K: int, dtype: str = "f16", group_size: int = 128) -> int:
+    """Bytes of workspace w4a16_gemm_ws uses for its fastest schedule (0: none)."""
+    d = {"f16": TQ_F16, "bf16": TQ_BF16}[dtype]
+    return int(load().w4a16_gemm_workspace_bytes(M, N, K, d, group_size))
+
+
+def w4a16_gemm(A, qweight, scales, bias=None, out=None, group_size: int = 128, path: str = "auto",
+               workspace="auto"):
+    """C = A @ dequant(qweight, scales)^T (+ bias); A [M, K] fp16/bf16.
+
+    workspace: as for tq_gemm ("auto", None or a contiguous device tensor)."""
     import torch
     _need_cuda(A, qweight, scales, bias)
     M, K = A.shape
     N = qweight.shape[0]
+    dt = _dtype_enum(A)
     C = out if out is not None else torch.empty((M, N), dtype=A.dtype, device=A.device)
-    _check("w4a16_gemm", load().w4a16_gemm_ex(_ptr(A), _dtype_enum(A), M, N, K, _ptr(qweight), _ptr(scales),
-                                               group_size, _ptr(bias), _ptr(C), _stream(A.device), PATHS[path]))
+    if isinstance(workspace, str):
+        nbytes = int(load().w4a16_gemm_workspace_bytes(M, N, K, dt, group_size))
+        workspace = torch.empty((nbytes,), dtype=torch.uint8, device=A.device) if nbytes else None
+    ws_bytes = 0
+    if workspace is not None:
+        _need_cuda(workspace)
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _check("w4a16_gemm", load().w4a16_gemm_ws(_ptr(A), dt, M, N, K, _ptr(qweight), _ptr(scales), group_size,
+                                               _ptr(bias), _ptr(C), _ptr(workspace), ws_bytes, _stream(A.device),
+                                               PATHS[path]))
     return C
 
 

@@ -202,24 +202,46 @@ tq_status tq_gemm(const void* A, tq_dtype dt, int64_t M, int64_t N, int64_t K, c
     return tq_gemm_ws(A, dt, M, N, K, codes, scale_f16, bias, C, nullptr, 0, stream, TQ_PATH_AUTO);
 }
 
-tq_status w4a16_gemm_ex(const void* A, tq_dtype dt, int64_t M, int64_t N, int64_t K, const int32_t* qweight,
-                        const uint16_t* scales_f16, int64_t group_size, const void* bias, void* C,
-                        hipStream_t stream, tq_path path) {
+tq_status w4a16_gemm_ws(const void* A, tq_dtype dt, int64_t M, int64_t N, int64_t K, const int32_t* qweight,
+                        const uint16_t* scales_f16, int64_t group_size, const void* bias, void* C, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream, tq_path path) {
     tq_status r = check_gemm_common(A, dt, M, N, K, qweight, scales_f16, C);
     if (r != TQ_OK) return r;
     if (group_size != 128) return TQ_ERR_GROUP;
     if (K % 128 != 0) return TQ_ERR_SHAPE;
     if (bias && (reinterpret_cast<uintptr_t>(bias) & 1u)) return TQ_ERR_ALIGN;
+    if (workspace && !aligned16(workspace)) return TQ_ERR_ALIGN;
     if (path == TQ_PATH_AUTO) path = tq_select_path(1, M, N, K, dt);
     tq::GemmArgs a{static_cast<const uint16_t*>(A), dt == TQ_BF16 ? 1 : 0, M, N, K, qweight, scales_f16,
                    static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(C)};
+    const size_t wsb = workspace ? workspace_bytes : 0;
     switch (path) {
         case TQ_PATH_GEMV:
-            if (M > kGemvMaxM) return from_hip(tq::launch_w4_gemm(a, stream));
-            return from_hip(tq::launch_w4_gemv(a, stream));
+            if (M > kGemvMaxM) return from_hip(tq::launch_w4_gemm(a, workspace, wsb, stream));
+            return from_hip(tq::launch_w4_gemv(a, workspace, wsb, stream));
         default:
             return TQ_ERR_PATH;
     }
+}
+
+size_t w4a16_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, tq_dtype dt, int64_t group_size) {
+    if (M <= 0 || N <= 0 || K <= 0 || K % 128 != 0 || group_size != 128) return 0;
+    const tq::GemmArgs a{nullptr, dt == TQ_BF16 ? 1 : 0, M < kGemvMaxM ? M : kGemvMaxM, N, K,
+                         nullptr, nullptr, nullptr, nullptr};
+    size_t b = tq::w4_gemv_workspace_bytes(a);
+    if (M > kGemvMaxM && M % kGemvMaxM != 0) {  // the last block of M % 16 rows may split differently
+        tq::GemmArgs t = a;
+        t.M = M % kGemvMaxM;
+        const size_t bt = tq::w4_gemv_workspace_bytes(t);
+        if (bt > b) b = bt;
+    }
+    return b;
+}
+
+tq_status w4a16_gemm_ex(const void* A, tq_dtype dt, int64_t M, int64_t N, int64_t K, const int32_t* qweight,
+                        const uint16_t* scales_f16, int64_t group_size, const void* bias, void* C,
+                        hipStream_t stream, tq_path path) {
+    return w4a16_gemm_ws(A, dt, M, N, K, qweight, scales_f16, group_size, bias, C, nullptr, 0, stream, path);
 }
 
 tq_status w4a16_gemm(const void* A, tq_dtype dt, int64_t M, int64_t N, int64_t K, const int32_t* qweight,

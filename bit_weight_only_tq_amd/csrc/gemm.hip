@@ -485,7 +485,8 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(SplitArgs sa) {
     }
 }
 
-// C[m, n] = (sum over z of ws[z][m][n]) * scale[n] + bias[n]; grid
+// C[m, n] = (sum over z of ws[z][m][n]) * scale[n] + bias[n] (no scale when
+// the partials carry it already); grid
 // (ceil(N/256), reduce_rows(M)), each workgroup row striding over m.
 constexpr int64_t kReduceMaxRows = 65535;
 inline unsigned reduce_rows(int64_t M) { return (unsigned)(M < kReduceMaxRows ? M : kReduceMaxRows); }
@@ -495,7 +496,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(SplitArgs sa) {
     const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (n >= p.N) return;
     const int64_t MN = p.M * p.N;
-    const float sc = f16_bits_to_f32(p.scale[n]);
+    const float sc = sa.scaled ? 1.0f : f16_bits_to_f32(p.scale[n]);
     const float b = p.bias ? T::to_f32(p.bias[n]) : 0.0f;
     for (int64_t m = blockIdx.y; m < p.M; m += gridDim.y) {
         const float* src = sa.ws + m * p.N + n;
@@ -1089,15 +1090,16 @@ hipError_t launch_ternary_medium_split(const SplitArgs& sa, hipStream_t s) {
     return small ? launch_mm<F16, 2>(sa, s) : launch_mm<F16, 4>(sa, s);
 }
 
-// W4A16 at large M: run the small-M kernel on successive blocks of 16
+// W4A16 at large M: run the small-M kernels on successive blocks of 16
 // activation rows (weights are re-read once per block).
-hipError_t launch_w4_gemm(const GemmArgs& a, hipStream_t s) {
+hipError_t launch_w4_gemm(const GemmArgs& a, void* workspace, size_t workspace_bytes, hipStream_t s) {
     for (int64_t m = 0; m < a.M; m += kGemvMaxM) {
         GemmArgs b = a;
         b.A = a.A + m * a.K;
         b.C = a.C + m * a.N;
         b.M = (a.M - m) < kGemvMaxM ? (a.M - m) : kGemvMaxM;
-        hipError_t e = launch_w4_gemv(b, s);
+        // the blocks run in stream order, so they may share one workspace
+        hipError_t e = launch_w4_gemv(b, workspace, workspace_bytes, s);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;

@@ -816,6 +816,174 @@ __global__ __launch_bounds__(W * kWave) void w4_gemv_mfma_kernel(GemmArgs p) {
     }
 }
 
+// W4A16, streaming schedule (fp16, 3 <= M <= 16): the arithmetic above with
+// the work split of the ternary streaming kernel.  One workgroup walks T
+// consecutive 16-row blocks; wave w owns groups w*GSW .. w*GSW + GSW-1 (128
+// columns each) of its K range, so it builds the activation operands and the
+// groups' constant terms once and contracts every row-block against them.
+// Activations reach the wave's LDS area by DMA, four 256-byte row slices per
+// instruction (lane l: row 4e + l/16, 16-byte slot l%16, slot q of row r at
+// q ^ (r % 16)), MR/4 instructions for the MR >= M rows; each lane then reads
+// its four operand chunks (row i, slots 4h .. 4h+3).  Issue order: bias bits
+// and group scales, activation DMA, the code words of all row-blocks, then
+// one vmcnt wait for the DMA only.  With S = gridDim.y > 1 splits of the groups
+// the workgroup stores fp32 partials (group scales applied) for
+// launch_splitk_reduce.
+__host__ __device__ constexpr int w4_stream_wave_lds(int gsw, int mr, int t) {  // bytes of one wave's LDS area
+    return t * 1024 > gsw * mr * 256 ? t * 1024 : gsw * mr * 256;
+}
+
+template <int GSW, int T, int MR>
+__global__ __launch_bounds__(1024) void w4_gemv_stream_kernel(SplitArgs sa) {
+    const GemmArgs& p = sa.g;
+    extern __shared__ uint4 smem[];
+    constexpr int kArea = w4_stream_wave_lds(GSW, MR, T);
+    f32x4* red = reinterpret_cast<f32x4*>(smem);  // wave w, row-block t: red[w * kArea / 16 + 64 t + lane]
+    const int W = blockDim.x >> 6;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int h = lane >> 4;
+    const int i16 = lane & 15;
+    const int64_t N = p.N, K = p.K;
+    const int M = (int)p.M;
+    const int G = (int)(K / 128);
+    const int64_t rowb = K / 2;  // code bytes per row
+    const int64_t n_base = (int64_t)blockIdx.x * (16 * T);
+    const uint8_t* codes = static_cast<const uint8_t*>(p.wq);
+    uint8_t* area = reinterpret_cast<uint8_t*>(smem) + wave * kArea;
+    const uint32_t area_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)smem + wave * kArea;
+    const int gsz = G / sa.S;  // groups of this split
+    const int g_end = ((int)blockIdx.y + 1) * gsz;
+    const int g0 = (int)blockIdx.y * gsz + wave * GSW;
+    const int cnt = g_end - g0 < GSW ? g_end - g0 : GSW;  // >= 1 for every wave of the launch
+
+    // bias bits of the output this thread finishes (thread e < 64T: row
+    // n_base + 16 (e / 64) + e % 16); read from the scales when absent, so
+    // that no branch splits the load phase
+    uint16_t bi_bits;
+    {
+        const int e = (int)threadIdx.x % (T * kWave);
+        const int64_t n = n_base + 16 * (e / kWave) + (e & 15);
+        const int64_t nc = n < N ? n : N - 1;
+        bi_bits = (p.bias ? p.bias : p.scale)[nc];
+    }
+    // group scales of all row-blocks, first: the codes are waited for in
+    // order, so scales issued after them would hold up row-block 0
+    uint16_t sc[T][GSW];
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        const int64_t n = n_base + 16 * t + i16;
+        const uint16_t* srow = p.scale + (n < N ? n : N - 1) * G;
+#pragma unroll
+        for (int s = 0; s < GSW; ++s) sc[t][s] = srow[(s < cnt) ? g0 + s : g0];
+    }
+    // 1. activation slices -> LDS by DMA (rows past M re-read row M-1)
+#pragma unroll
+    for (int s = 0; s < GSW; ++s) {
+        const int gi = (s < cnt) ? g0 + s : g0;
+#pragma unroll
+        for (int e = 0; e < MR / 4; ++e) {
+            const int r0 = 4 * e + (lane >> 4);
+            const int r = r0 < M ? r0 : M - 1;
+            const int piece = (lane & 15) ^ (r0 & 15);
+            dma16(p.A + (int64_t)r * K + (int64_t)gi * 128 + 8 * piece,
+                  area_lds + (uint32_t)(s * MR * 256 + e * 1024));
+        }
+    }
+    // 2. code words of all row-blocks (rows past N re-read row N-1, groups
+    //    past the wave's share re-read its first; both ignored)
+    uint4 q[T][GSW];
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        const int64_t n = n_base + 16 * t + i16;
+        const uint8_t* crow = codes + (n < N ? n : N - 1) * rowb + 16 * h;
+#pragma unroll
+        for (int s = 0; s < GSW; ++s) {
+            const int gi = (s < cnt) ? g0 + s : g0;
+            q[t][s] = *reinterpret_cast<const uint4*>(crow + (int64_t)gi * 64);
+        }
+    }
+
+    // 3. wait for the DMA only (completion is in order), build the operands
+    //    and each group's constant term
+    static_assert(T * GSW <= 63, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(T * GSW) : "memory");
+    const int rd_row = i16 & (MR - 1);
+    const f16x2 sixteenth = f16x2{(_Float16)0.0625f, (_Float16)0.0625f};
+    const uint4 negp = make_uint4(kW4Neg0, kW4Neg1, kW4Neg0, kW4Neg1);
+    uint4 aop[GSW][4];
+    f32x4 dacc[GSW];
+#pragma unroll
+    for (int s = 0; s < GSW; ++s) {
+        dacc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            const uint4 v = *reinterpret_cast<const uint4*>(area + s * MR * 256 + rd_row * 256 +
+                                                            16 * ((4 * h + d) ^ (rd_row & 15)));
+            const uint32_t p0 = __builtin_amdgcn_perm(v.z, v.x, 0x05040100u);
+            const uint32_t p1 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(v.z, v.x, 0x07060302u)) * sixteenth);
+            const uint32_t p2 = __builtin_amdgcn_perm(v.w, v.y, 0x05040100u);
+            const uint32_t p3 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(v.w, v.y, 0x07060302u)) * sixteenth);
+            aop[s][d] = make_uint4(p0, p1, p2, p3);
+            dacc[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, aop[s][d]), __builtin_bit_cast(f16x8, negp), dacc[s], 0, 0, 0);
+        }
+    }
+
+    // 4. contract each row-block as its codes land
+    const uint32_t magic_v = vgpr_const<kMagic2>();
+    f32x4 acc[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        f32x4 a4 = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < GSW; ++s) {
+            if (s < cnt) {
+                f32x4 ag = dacc[s];
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    const uint32_t x = dword_of(q[t][s], d);
+                    const uint32_t y = x >> 8;
+                    const uint4 bw = make_uint4((x & sgpr_const<0x000F000Fu>()) | magic_v, (x & sgpr_const<0x00F000F0u>()) | magic_v,
+                                                (y & sgpr_const<0x000F000Fu>()) | magic_v, (y & sgpr_const<0x00F000F0u>()) | magic_v);
+                    ag = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, aop[s][d]), __builtin_bit_cast(f16x8, bw), ag, 0, 0, 0);
+                }
+                const float sv = f16_bits_to_f32(sc[t][s]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) a4[i] = fmaf(sv, ag[i], a4[i]);
+            }
+        }
+        acc[t] = a4;
+    }
+
+    // 5. wave partials -> LDS (each wave's own area), fixed-order sum
+#pragma unroll
+    for (int t = 0; t < T; ++t) red[wave * (kArea / 16) + t * kWave + lane] = acc[t];
+    __syncthreads();
+    if ((int)threadIdx.x < T * kWave) {  // T <= W
+        const int e = (int)threadIdx.x;
+        const int t = e / kWave;
+        const int l = e % kWave;
+        f32x4 sum = red[t * kWave + l];
+        for (int w = 1; w < W; ++w) sum += red[w * (kArea / 16) + t * kWave + l];
+        const int64_t n = n_base + 16 * t + (l & 15);
+        if (n < N && sa.S > 1) {
+            float* part = sa.ws + (int64_t)blockIdx.y * M * N;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int m = 4 * (l >> 4) + i;
+                if (m < M) part[(int64_t)m * N + n] = sum[i];
+            }
+        } else if (n < N) {
+            const float b = p.bias ? F16::to_f32(bi_bits) : 0.0f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int m = 4 * (l >> 4) + i;
+                if (m < M) p.C[(int64_t)m * N + n] = F16::from_f32(sum[i] + b);
+            }
+        }
+    }
+}
+
 // ------------------------------------------------------------- launchers
 
 template <int R, int W>
@@ -1084,7 +1252,111 @@ static hipError_t launch_w4_mfma_w(const GemmArgs& a, hipStream_t s) {
     return launch_w4_mfma<R, 1>(a, s);
 }
 
-hipError_t launch_w4_gemv(const GemmArgs& a, hipStream_t s) {
+// W4A16 streaming plan: as the ternary one, over 128-column groups.  S
+// divides the groups, a workgroup takes at most 32 (one or two per wave, at
+// most 16 waves), a split keeps at least four; T row-blocks per workgroup
+// (at most 8 with one group per wave, 4 with two; at most the wave count);
+// the waves' LDS areas must fit.  The cost is the same estimate of bytes per
+// compute unit: activations (M * K/S * 2), codes, split partials, plus
+// 160 KB for the reduction launch.
+struct W4StreamPlan {
+    int gsw, waves, t, S, mr;
+    size_t lds;
+};
+
+static bool w4_stream_geometry(const GemmArgs& a, int S, int64_t cus, W4StreamPlan* pl) {
+    const int64_t g_all = a.K / 128;
+    if (S < 1 || g_all % S != 0) return false;
+    const int64_t gs = g_all / S;
+    if (gs > 32 || (S > 1 && gs < 4)) return false;
+    pl->S = S;
+    pl->gsw = gs <= 16 ? 1 : 2;
+    pl->waves = (int)((gs + pl->gsw - 1) / pl->gsw);
+    pl->mr = a.M <= 4 ? 4 : a.M <= 8 ? 8 : 16;
+    const int64_t nrb = (a.N + 15) / 16;
+    const int tmax = pl->gsw == 1 ? 8 : 4;
+    int t = 1;
+    while (t < tmax && 2 * t <= pl->waves && (nrb + t - 1) / t * S > cus) t *= 2;
+    pl->t = t;
+    pl->lds = (size_t)pl->waves * w4_stream_wave_lds(pl->gsw, pl->mr, t);
+    return pl->lds <= (size_t)kGemvLdsMaxBytes;
+}
+
+static int64_t w4_stream_cost(const GemmArgs& a, const W4StreamPlan& pl, int64_t cus) {
+    const int64_t kr = a.K / pl.S;
+    const int64_t per_wg = 2 * a.M * kr + (int64_t)pl.t * 16 * (kr / 2) + (pl.S > 1 ? (int64_t)pl.t * 16 * a.M * 8 : 0);
+    const int64_t nrb = (a.N + 15) / 16;
+    const int64_t wgs = (nrb + pl.t - 1) / pl.t * pl.S;
+    return (wgs + cus - 1) / cus * per_wg + (pl.S > 1 ? 160 * 1024 : 0);
+}
+
+static bool w4_stream_plan(const GemmArgs& a, size_t ws_bytes, W4StreamPlan* pl) {
+    if (a.bf16 || a.M < 3 || a.M > kGemvMaxM || a.K % 128 != 0) return false;
+    const int64_t cus = compute_units();
+    bool found = false;
+    int64_t best = 0;
+    for (int S = 1; S <= 16; ++S) {
+        W4StreamPlan c;
+        if (!w4_stream_geometry(a, S, cus, &c)) continue;
+        if (S > 1 && ws_bytes < (size_t)S * (size_t)a.M * (size_t)a.N * sizeof(float)) continue;
+        const int64_t cost = w4_stream_cost(a, c, cus);
+        if (!found || cost < best) {
+            *pl = c;
+            best = cost;
+            found = true;
+        }
+    }
+    return found;
+}
+
+size_t w4_gemv_workspace_bytes(const GemmArgs& a) {
+    W4StreamPlan pl;
+    if (!w4_stream_plan(a, SIZE_MAX, &pl) || pl.S == 1) return 0;
+    return (size_t)pl.S * (size_t)a.M * (size_t)a.N * sizeof(float);
+}
+
+template <int GSW, int T, int MR>
+static hipError_t launch_w4_stream(const SplitArgs& sa, const W4StreamPlan& pl, hipStream_t s) {
+    static DeviceFlags lds_limit_set;
+    hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(&w4_gemv_stream_kernel<GSW, T, MR>),
+                                   kGemvLdsMaxBytes, lds_limit_set);
+    if (e != hipSuccess) return e;
+    if (pl.lds != (size_t)pl.waves * w4_stream_wave_lds(GSW, MR, T)) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)((sa.g.N + 16 * T - 1) / (16 * T)), (unsigned)sa.S);
+    w4_gemv_stream_kernel<GSW, T, MR><<<grid, dim3(pl.waves * kWave), pl.lds, s>>>(sa);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    return sa.S > 1 ? launch_splitk_reduce(sa, s) : hipSuccess;
+}
+
+template <int MR>
+static hipError_t launch_w4_stream_mr(const SplitArgs& sa, const W4StreamPlan& pl, hipStream_t s) {
+    if (pl.gsw == 1) {
+        switch (pl.t) {
+            case 1: return launch_w4_stream<1, 1, MR>(sa, pl, s);
+            case 2: return launch_w4_stream<1, 2, MR>(sa, pl, s);
+            case 4: return launch_w4_stream<1, 4, MR>(sa, pl, s);
+            default: return launch_w4_stream<1, 8, MR>(sa, pl, s);
+        }
+    }
+    switch (pl.t) {
+        case 1: return launch_w4_stream<2, 1, MR>(sa, pl, s);
+        case 2: return launch_w4_stream<2, 2, MR>(sa, pl, s);
+        default: return launch_w4_stream<2, 4, MR>(sa, pl, s);
+    }
+}
+
+static hipError_t launch_w4_stream_t(const SplitArgs& sa, const W4StreamPlan& pl, hipStream_t s) {
+    if (pl.mr == 4) return launch_w4_stream_mr<4>(sa, pl, s);
+    if (pl.mr == 8) return launch_w4_stream_mr<8>(sa, pl, s);
+    return launch_w4_stream_mr<16>(sa, pl, s);
+}
+
+hipError_t launch_w4_gemv(const GemmArgs& a, hipStream_t s) { return launch_w4_gemv(a, nullptr, 0, s); }
+
+hipError_t launch_w4_gemv(const GemmArgs& a, void* workspace, size_t workspace_bytes, hipStream_t s) {
+    W4StreamPlan sp;
+    if (w4_stream_plan(a, workspace ? workspace_bytes : 0, &sp))
+        return launch_w4_stream_t(SplitArgs{a, static_cast<float*>(workspace), sp.S, 1}, sp, s);
     if (!a.bf16 && a.M >= 3 && a.M <= kGemvMaxM) {
         const int64_t nrb = (a.N + 15) / 16;
         return nrb >= 1024 ? launch_w4_mfma_w<2>(a, s) : launch_w4_mfma_w<1>(a, s);

@@ -58,6 +58,7 @@ struct SplitArgs {
     GemmArgs g;
     float* ws;  // [S][M][N] fp32 partials, unused when S == 1
     int S;
+    int scaled;  // 1: the partials already carry the weight scales (W4A16), the reduction adds only the bias
 };
 hipError_t launch_splitk_reduce(const SplitArgs& sa, hipStream_t s);  // gemm.hip
 
@@ -70,6 +71,10 @@ hipError_t launch_ternary_gemv(const GemmArgs& a, void* workspace, size_t worksp
 hipError_t launch_ternary_gemv(const GemmArgs& a, hipStream_t s);         // picks the fastest eligible kernel
 hipError_t launch_ternary_gemv_simple(const GemmArgs& a, hipStream_t s);  // any dtype, any K % 64 == 0
 bool ternary_gemv_mfma_ok(const GemmArgs& a);                             // fp16, K % 256 == 0
+// W4A16 small M: with a workspace of w4_gemv_workspace_bytes() the streaming
+// kernel may split K; without one it never does.
+size_t w4_gemv_workspace_bytes(const GemmArgs& a);
+hipError_t launch_w4_gemv(const GemmArgs& a, void* workspace, size_t workspace_bytes, hipStream_t s);
 hipError_t launch_w4_gemv(const GemmArgs& a, hipStream_t s);         // picks the fastest eligible kernel
 hipError_t launch_w4_gemv_simple(const GemmArgs& a, hipStream_t s);  // any dtype
 
@@ -89,6 +94,6 @@ hipError_t launch_ternary_medium(const GemmArgs& a, void* workspace, size_t work
 hipError_t launch_ternary_medium_split(const SplitArgs& sa, hipStream_t s);  // a given split count
 // Compute units of the current device (cached per device ordinal).
 int compute_units();
-hipError_t launch_w4_gemm(const GemmArgs& a, hipStream_t s);
+hipError_t launch_w4_gemm(const GemmArgs& a, void* workspace, size_t workspace_bytes, hipStream_t s);
 
 }  // namespace tq

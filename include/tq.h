@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define TQ_ABI_VERSION 2
+#define TQ_ABI_VERSION 3
 
 typedef enum tq_status {
     TQ_OK = 0,
@@ -214,6 +214,30 @@ tq_status w4a16_gemm(const void* A, tq_dtype dt, int64_t M, int64_t N, int64_t K
 tq_status w4a16_gemm_ex(const void* A, tq_dtype dt, int64_t M, int64_t N, int64_t K,
                         const int32_t* qweight, const uint16_t* scales_f16, int64_t group_size,
                         const void* bias, void* C, hipStream_t stream, tq_path path);
+
+/*
+ * w4a16_gemm_ws - w4a16_gemm with a caller-owned workspace and a path
+ * choice (ABI 3).  The workspace rules are those of tq_gemm_ws: 16-byte
+ * aligned device memory of workspace_bytes bytes or NULL, overwritten by
+ * the call, not shared by calls that may overlap.  With at least
+ * w4a16_gemm_workspace_bytes() bytes the fp16 small-M kernel may split the
+ * K groups across workgroups (fp32 partials with the group scales applied,
+ * summed in order by a second kernel, bias added there); with less it makes
+ * one pass over K.  M > 16 runs as successive blocks of 16 rows that reuse
+ * the workspace in stream order.  Other arguments, results and errors as
+ * w4a16_gemm; TQ_ERR_ALIGN for a misaligned workspace.
+ */
+tq_status w4a16_gemm_ws(const void* A, tq_dtype dt, int64_t M, int64_t N, int64_t K,
+                        const int32_t* qweight, const uint16_t* scales_f16, int64_t group_size,
+                        const void* bias, void* C, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream, tq_path path);
+
+/*
+ * w4a16_gemm_workspace_bytes - workspace w4a16_gemm_ws needs for its fastest
+ * schedule of this shape on the current device (0 when none is used, or for
+ * invalid arguments).
+ */
+size_t w4a16_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, tq_dtype dt, int64_t group_size);
 
 /* ------------------------------------------------------------------ misc */
 

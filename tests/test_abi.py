@@ -44,9 +44,9 @@ def test_binding_declares_nothing_extra():
 
 
 def test_version_and_status_strings(lib):
-    assert lib.tq_abi_version() == 2
+    assert lib.tq_abi_version() == 3
     src = open(HEADER).read()
-    assert "#define TQ_ABI_VERSION 2" in src
+    assert "#define TQ_ABI_VERSION 3" in src
     for code, name in _lib.STATUS_NAMES.items():
         assert re.search(rf"\b{name}\s*=\s*{code}\b", src), name
         s = lib.tq_status_str(code)
@@ -120,6 +120,32 @@ def test_tq_gemm_ws_host_checks(lib):
     assert name[st] == "TQ_ERR_PATH"
     st = lib.tq_gemm_ws(None, 0, 32, 64, 64, FAKE, FAKE, None, FAKE, None, 0, None, 0)
     assert name[st] == "TQ_ERR_NULL"
+
+
+def test_w4_workspace_query():
+    """W4A16 split-K workspace (fp16, 3 <= M <= 16): S fp32 partials of
+    [M, N] when the plan splits the K groups; none at M < 3, for bf16, or
+    when one pass over K is cheapest.  Off the GPU the compute-unit count
+    defaults to 256."""
+    wb = _lib.w4a16_gemm_workspace_bytes
+    assert wb(16, 4096, 14336) == 8 * 16 * 4096 * 4       # 112 groups -> 8 splits of 14
+    assert wb(16, 57344, 8192) == 4 * 16 * 57344 * 4
+    assert wb(16, 28672, 4096) == 0 and wb(16, 4096, 4096) == 0
+    assert wb(1, 4096, 14336) == 0 and wb(2, 4096, 14336) == 0
+    assert wb(16, 4096, 14336, "bf16") == 0
+    assert wb(16, 4096, 14336, group_size=64) == 0
+    assert wb(40, 4096, 14336) == 8 * 16 * 4096 * 4      # blocks of 16 rows, the largest block's need
+    assert wb(16, 4096, 200) == 0                         # K % 128 != 0
+
+
+def test_w4a16_gemm_ws_host_checks(lib):
+    name = _lib.STATUS_NAMES
+    st = lib.w4a16_gemm_ws(FAKE, 0, 4, 64, 128, FAKE, FAKE, 128, None, FAKE, MIS, 1024, None, 0)
+    assert name[st] == "TQ_ERR_ALIGN"
+    st = lib.w4a16_gemm_ws(FAKE, 0, 4, 64, 128, FAKE, FAKE, 128, None, FAKE, None, 0, None, 2)
+    assert name[st] == "TQ_ERR_PATH"
+    st = lib.w4a16_gemm_ws(FAKE, 0, 4, 64, 128, FAKE, FAKE, 64, None, FAKE, None, 0, None, 0)
+    assert name[st] == "TQ_ERR_GROUP"
 
 
 def test_tq_gemm_ex_bad_path(lib):

@@ -292,6 +292,38 @@ def test_w4_ragged_shapes(M, N, K):
     check_close(C, A, wdq, bias=bias, label=f"w4 ragged {M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("M,N,K", [(16, 4096, 14336), (5, 1000, 14336), (12, 8192, 28672), (3, 4100, 8192),
+                                   (16, 28672, 4096), (40, 4096, 14336)])
+def test_w4_split_k(M, N, K):
+    """W4A16 streaming kernel with the K groups split across workgroups
+    (workspace from torch) and without a workspace: both within the tolerance
+    on sampled output columns, ragged N, with bias; M > 16 runs blocks of 16
+    rows through one workspace; a repeated call is bit-identical."""
+    import torch
+    import bit_weight_only_tq_amd as tq
+    dev = require_gpu()
+    nbytes = tq.w4a16_gemm_workspace_bytes(M, N, K)
+    log(f"w4 split-K M={M} N={N} K={K} workspace={nbytes}")
+    W = synth.weights_device(N, K, synth.seed_for("w4sk", N, K), dev)
+    q, s = tq.w4a16_pack(W)
+    cols = np.sort(np.random.default_rng(N + K + 2).choice(N, min(N, 160), replace=False))
+    idx = torch.from_numpy(cols).to(dev)
+    rq, rs = OW.w4_pack(W.index_select(0, idx).cpu().numpy())
+    np.testing.assert_array_equal(q.index_select(0, idx).cpu().numpy(), rq)
+    del W
+    wdq = OW.w4_dequant(rq, rs, K)
+    A = synth.activations(M, K, synth.seed_for("w4ska", M, K), "f16")
+    bias = synth.activations(1, N, synth.seed_for("w4skb", N), "f16")[0]
+    outs = []
+    for ws in ("auto", None):
+        C = tq.w4a16_gemm(A.to(dev), q, s, bias=bias.to(dev), workspace=ws)
+        check_close(C.index_select(1, idx), A, wdq, bias=bias[torch.from_numpy(cols)],
+                    label=f"w4 split {M}x{N}x{K} ws={ws}")
+        outs.append(C)
+    C2 = tq.w4a16_gemm(A.to(dev), q, s, bias=bias.to(dev))
+    assert torch.equal(outs[0].view(torch.int16), C2.view(torch.int16))
+
+
 def test_w4_one_hot_bit_exact():
     """A = rows of the identity: C[m, n] = wdq[n, k_m] exactly (the group's
     value (q - 8) * s rounded once to fp16); pins nibble order and pairing."""
