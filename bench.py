@@ -33,7 +33,7 @@ Also reported in the same JSON line:
     timed on the host on a bounded sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--mode MODE]
-  --mode full (default) | decode | decodem | decode70b | w4 | medium | prefill | calib
+  --mode full (default) | decode | decodem | decode70b | w4 | medium | prefill | attrib | calib
   (plain copy of known size, for scaling hardware byte counters)
 """
 
@@ -62,7 +62,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--layers", type=int, default=32)
     ap.add_argument("--mode", default="full",
-                    choices=["full", "decode", "decodem", "decode70b", "w4", "medium", "prefill", "calib"])
+                    choices=["full", "decode", "decodem", "decode70b", "w4", "medium", "prefill", "attrib", "calib"])
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
     ap.add_argument("--unfused", action="store_true", help="decode mode: q,k,v,gate,up as separate calls")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -112,18 +112,34 @@ def build_decode(layers, dev, fused, model="8b"):
     return mats
 
 
-def time_region(fn, steps, stream):
-    """Seconds for `steps` calls of fn, from HIP events on `stream`."""
+def time_region(fn, steps, stream, per_step=None):
+    """Seconds for `steps` calls of fn, from HIP events on `stream`.  With a
+    list as `per_step`, an event is also recorded after every call and the
+    per-call milliseconds are appended to it (the total is unchanged: it is
+    still read from the first and last event)."""
     import torch
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps - 1)] if per_step is not None else []
     torch.cuda.synchronize()
     start.record(stream)
-    for _ in range(steps):
+    for i in range(steps):
         fn()
+        if per_step is not None and i < steps - 1:
+            marks[i].record(stream)
     end.record(stream)
     end.synchronize()
+    if per_step is not None:
+        edges = [start] + marks + [end]
+        per_step.extend(a.elapsed_time(b) for a, b in zip(edges[:-1], edges[1:]))
     return start.elapsed_time(end) / 1e3
+
+
+def percentiles(ms):
+    """p10 / p50 / p90 of a list of per-step milliseconds."""
+    v = sorted(ms)
+    pick = lambda f: v[min(len(v) - 1, int(round(f * (len(v) - 1))))]  # noqa: E731
+    return {"p10": round(pick(0.1), 4), "p50": round(pick(0.5), 4), "p90": round(pick(0.9), 4)}
 
 
 def run_decode(args, dev, fused, graph, model="8b", layers=None, steps=None, M=1):
@@ -156,7 +172,8 @@ def run_decode(args, dev, fused, graph, model="8b", layers=None, steps=None, M=1
     for _ in range(args.warmup):
         run()
     torch.cuda.synchronize()
-    t = time_region(run, steps, stream)
+    step_ms = []
+    t = time_region(run, steps, stream, per_step=step_ms)
     packed = sum(m[3].numel() for m in mats)
     alg = sum(ternary_bytes(M, m[1], m[2]) for m in mats)
     res = {
@@ -164,6 +181,7 @@ def run_decode(args, dev, fused, graph, model="8b", layers=None, steps=None, M=1
         "ms_per_step": t / steps * 1e3, "packed_gbs": packed * steps / t / 1e9,
         "alg_gbs": alg * steps / t / 1e9,
         "avg_launch_us": t / steps / len(mats) * 1e6, "alg_bytes_per_launch": alg / len(mats),
+        "step_ms": percentiles(step_ms),
     }
     del mats, xs, outs
     if graph:
@@ -268,8 +286,75 @@ def run_decode_m(args, dev, graph, Ms=(4, 16)):
     for M in Ms:
         d = run_decode(args, dev, True, graph, M=M)
         res[f"M{M}"] = {"value": round(d["packed_gbs"], 1), "frac_of_peak": round(d["packed_gbs"] / HBM_PEAK_GBS, 4),
-                        "ms_per_step": round(d["ms_per_step"], 4), "avg_launch_us": round(d["avg_launch_us"], 3),
-                        "alg_gbs": round(d["alg_gbs"], 1)}
+                        "ms_per_step": round(d["ms_per_step"], 4), "step_ms_percentiles": d["step_ms"],
+                        "avg_launch_us": round(d["avg_launch_us"], 3), "alg_gbs": round(d["alg_gbs"], 1)}
+    return res
+
+
+def capture(fn, stream):
+    """fn's launches recorded into a HIP graph (warmed up once on a side
+    stream first); returns the graph's replay."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        fn()
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        fn()
+    return g
+
+
+def run_attrib(dev, reps=8):
+    """Where a decode GEMV's time goes (M = 1, Llama-3-8B fused shapes), from
+    real runs only, each a graph of back-to-back calls:
+      hbm_us       the kernel streaming its weights from HBM (copies cycled
+                   over >= 2 GiB, 8x the 256 MB last-level cache);
+      resident_us  the same kernel on one copy, which the last-level cache
+                   then serves (launch + unpack + MAC + on-chip reads);
+      launch_floor the kernel on a 16 x 256 matrix.
+    on_chip_us = resident_us - launch floor; hbm_exposed_us = hbm_us -
+    resident_us."""
+    import torch
+    import bit_weight_only_tq_amd as tq
+    import synth
+    stream = torch.cuda.current_stream()
+    res = {"metric": "decode GEMV time split, Llama-3-8B shapes, M=1 (us per call)"}
+    x_small = synth.activations_device(1, 256, synth.seed_for("attr_s"), "f16", dev)
+    cs, ss = tq.tq_pack(synth.weights_device(16, 256, synth.seed_for("attr_w"), dev))
+    out_s = torch.empty((1, 16), dtype=torch.float16, device=dev)
+    g = capture(lambda: [tq.tq_gemm(x_small, cs, ss, out=out_s) for _ in range(64)], stream)
+    g.replay()
+    res["launch_floor_us"] = round(time_region(g.replay, reps, stream) / (reps * 64) * 1e6, 2)
+    del g
+    for name, (N, K) in layer_shapes(True):
+        W = synth.weights_device(N, K, synth.seed_for("attr", N, K), dev)
+        codes, scale = tq.tq_pack(W)
+        del W
+        nb = codes.numel()
+        copies = max(2, -(-(2 << 30) // nb))
+        buf = torch.empty((copies * nb,), dtype=torch.uint8, device=dev)
+        views = [buf[i * nb:(i + 1) * nb].view(N, K // 4) for i in range(copies)]
+        for v in views:
+            v.copy_(codes)
+        x = synth.activations_device(1, K, synth.seed_for("attrx", K), "f16", dev)
+        out = torch.empty((1, N), dtype=torch.float16, device=dev)
+        g_hbm = capture(lambda: [tq.tq_gemm(x, v, scale, out=out) for v in views], stream)
+        g_res = capture(lambda: [tq.tq_gemm(x, views[0], scale, out=out) for _ in range(64)], stream)
+        g_hbm.replay()
+        g_res.replay()
+        t_hbm = time_region(g_hbm.replay, 2, stream) / (2 * copies)
+        t_res = time_region(g_res.replay, reps, stream) / (reps * 64)
+        res[f"{name}_{N}x{K}"] = {
+            "hbm_us": round(t_hbm * 1e6, 2), "resident_us": round(t_res * 1e6, 2),
+            "hbm_gbs": round(nb / t_hbm / 1e9, 1),
+            "on_chip_us": round(t_res * 1e6 - res["launch_floor_us"], 2),
+            "hbm_exposed_us": round((t_hbm - t_res) * 1e6, 2),
+        }
+        del g_hbm, g_res, views, buf, codes, scale
+        torch.cuda.empty_cache()
     return res
 
 
@@ -280,6 +365,7 @@ def run_decode_70b(args, dev):
                    steps=max(2, args.steps // 2))
     return {"metric": "HBM GB/s ternary GEMV at M=1, Llama-3-70B decode (80 layers resident)",
             "value": round(d["packed_gbs"], 1), "unit": "GB/s", "frac_of_peak": round(d["packed_gbs"] / HBM_PEAK_GBS, 4),
+            "step_ms_percentiles": d["step_ms"],
             "ms_per_step": round(d["ms_per_step"], 4), "launches_per_step": d["launches"],
             "packed_bytes_per_step": d["packed_bytes"], "avg_launch_us": round(d["avg_launch_us"], 3),
             "workload": "80 layers x {qkv (10240x8192), o (8192x8192), gate_up (57344x8192), down (8192x28672)}, "
@@ -413,6 +499,9 @@ def main():
     if args.mode == "prefill":
         print(json.dumps({"secondary": run_prefill(dev)}), flush=True)
         return
+    if args.mode == "attrib":
+        print(json.dumps({"attribution": run_attrib(dev)}), flush=True)
+        return
     if args.mode == "decodem":
         print(json.dumps({"decode_m": run_decode_m(args, dev, not args.no_graph)}), flush=True)
         return
@@ -440,6 +529,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(d["ms_per_step"], 4),
+        "step_ms_percentiles": d["step_ms"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -469,6 +559,8 @@ def main():
                                      "avg_launch_us": round(u["avg_launch_us"], 3)}
         log("decode, M = 4 and 16")
         out["decode_m"] = run_decode_m(args, dev, graph)
+        log("decode time split")
+        out["attribution"] = run_attrib(dev)
         log("decode, Llama-3-70B, 80 layers")
         out["decode_70b"] = run_decode_70b(args, dev)
         log("W4A16 decode")
