@@ -25,6 +25,8 @@ Modules:
                 3.1-3.2, section 4 naive kernel).
 * ``w4``      - W4A16 symmetric int4 pack / unpack / dequant ([P2] sections
                 4.2 and 5).
+* ``w4asym``  - W4A16 with per-group zero points and activation-order groups
+                (g_idx): pack / unpack / dequant ([P2] section 5 (0) and (3)).
 * ``gemm``    - fp64 reference product with the dequantized weights and the
                 per-element magnitude bound used by the tolerance.
 * ``check``   - the tolerance verdict and the ``quant_check`` statistics of

@@ -520,4 +520,160 @@ def pin_tolerance_check(o):
     assert qc == {"ok": False, "max_abs": 0.5, "mean_abs": 0.25, "finite": True}
 
 
+# ------------------------------------------- W4A16, zero points and act-order
+
+def pin_w4a_format_from_pages(o):
+    """Bits, group size, per-group zero point and optional g_idx (golden fixture)."""
+    kv = dict(_golden_lines("w4a16_asym_format.txt"))
+    assert int(kv["bits"]) == o.w4asym.BITS == 4
+    assert int(kv["group_size"]) == o.w4asym.GROUP == 128
+    assert int(kv["packed_factor"]) == o.w4asym.PER_WORD == 8
+    assert kv["zero_point"] == "per_group" and kv["g_idx"] == "optional"
+
+
+def _w4a_words_from_codes(codes):
+    """Words of one row from its codes, nibble i of word j = column 8j + i."""
+    words = []
+    for j in range(len(codes) // 8):
+        w = 0
+        for i in range(8):
+            w |= codes[8 * j + i] << (4 * i)
+        words.append(w)
+    return np.array(words, dtype=np.uint32).view(np.int32)
+
+
+def pin_w4a_hand_example(o):
+    """Hand-derived, K = 384 (three groups), every scale exactly 2^-4:
+    group 0: -0.25, 0.6875, 0.1, 0.03125, 0.09375, -0.03125, then zeros:
+      range [-0.25, 0.6875] -> s = 0.9375/15 = 0.0625, z = 0.25/s = 4;
+      codes 0, 15, rint(1.6)+4 = 6, rint(0.5)+4 = 4 (tie to even),
+      rint(1.5)+4 = 6, rint(-0.5)+4 = 4, and 4 for each zero;
+    group 1: 0.9375, 0.5, then 0.25 x 126 (all positive: the range widens
+      to include 0): s = 0.0625, z = 0; codes 15, 8, 4 ...;
+    group 2: -0.9375, then -0.25 x 127 (all negative): s = 0.0625, z = 15;
+      codes 0, then rint(-4)+15 = 11."""
+    w = np.zeros((1, 384), dtype=np.float32)
+    w[0, :6] = [-0.25, 0.6875, 0.1, 0.03125, 0.09375, -0.03125]
+    w[0, 128:256] = 0.25
+    w[0, 128], w[0, 129] = 0.9375, 0.5
+    w[0, 256:] = -0.25
+    w[0, 256] = -0.9375
+    codes = [0, 15, 6, 4, 6, 4] + [4] * 122 + [15, 8] + [4] * 126 + [0] + [11] * 127
+    for q, sb, z, perm in (o.w4asym.w4a_pack(w), [np.array(x) for x in o.w4asym.w4a_pack_loop(w.tolist())]):
+        assert np.array_equal(np.asarray(sb).reshape(-1), [0x2C00] * 3)
+        assert np.array_equal(np.asarray(z).reshape(-1), [4, 0, 15])
+        words = np.asarray(q).reshape(-1).astype(np.int64) & 0xFFFFFFFF
+        assert np.array_equal(words, _w4a_words_from_codes(codes).view(np.uint32).astype(np.int64))
+        assert np.array_equal(np.asarray(perm).reshape(-1), np.arange(384))
+    q, sb, z, perm = o.w4asym.w4a_pack(w)
+    d = o.w4asym.w4a_dequant(q, sb, z, 384, perm)[0]
+    assert d[0] == -0.25 and d[1] == 0.6875 and d[2] == 0.125 and d[3] == 0.0 and d[5] == 0.0
+    assert d[128] == 0.9375 and d[129] == 0.5 and d[130] == 0.25 and d[256] == -0.9375 and d[300] == -0.25
+
+
+def _w4a_expected(cols, group_vals):
+    """Exact-rational quantization of one group (independent RNE scan):
+    returns (scale bits, zero point, {column: code})."""
+    fr = [Fraction(v) for v in group_vals]
+    lo = min([Fraction(0)] + fr)
+    hi = max([Fraction(0)] + fr)
+    sb = _round_to_grid_f16((hi - lo) / 15)
+    s = _f16_frac(sb)
+    if s == 0:
+        return sb, 0, {c: 0 for c in cols}
+    z = min(max(round(-lo / s), 0), 15)         # Fraction rounds half to even
+    return sb, z, {c: min(max(round(f / s) + z, 0), 15) for c, f in zip(cols, fr)}
+
+
+def pin_w4a_vs_fraction(o):
+    """Scales, zero points and codes equal the exact-rational definition, with
+    and without a random g_idx (groups of 8), both tiers; dequant in the input
+    column order equals (q - z) * s of each column's own group."""
+    rng = random.Random(11)
+    for trial in range(40):
+        N, group = 3, 8
+        K = group * rng.choice([1, 2, 3])
+        G = K // group
+        scale = rng.choice([1e-3, 0.02, 1.0, 300.0])
+        w = np.array([[rng.gauss(0, scale) if rng.random() > 0.1 else 0.0 for _ in range(K)] for _ in range(N)],
+                     dtype=np.float32)
+        if trial % 5 == 0:
+            w[0] = np.abs(w[0])
+        if trial % 7 == 0:
+            w[1] = 0.0
+        g_idx = None
+        if trial % 2:
+            lab = [k // group for k in range(K)]
+            rng.shuffle(lab)
+            g_idx = np.array(lab, dtype=np.int32)
+        q, sb, z, perm = o.w4asym.w4a_pack(w, g_idx, group=group)
+        ql, sbl, zl, perml = o.w4asym.w4a_pack_loop(w.tolist(), None if g_idx is None else g_idx.tolist(), group=group)
+        assert np.array_equal(np.array(ql, dtype=np.uint32).view(np.int32), q)
+        assert np.array_equal(np.array(sbl, dtype=np.uint16), sb) and np.array_equal(np.array(zl, dtype=np.uint8), z)
+        assert np.array_equal(np.array(perml), perm)
+        codes = o.w4asym.w4a_unpack(q, K)
+        d = o.w4asym.w4a_dequant(q, sb, z, K, perm, group=group)
+        dl = o.w4asym.w4a_dequant_loop(ql, sbl, zl, perml, K, group=group)
+        labels = [k // group for k in range(K)] if g_idx is None else g_idx.tolist()
+        for n in range(N):
+            for g in range(G):
+                cols = [k for k in range(K) if labels[k] == g]       # membership, not the sort
+                esb, ez, ecode = _w4a_expected(cols, [float(w[n, k]) for k in cols])
+                s = _f16_frac(esb)
+                for k in cols:
+                    i = int(np.nonzero(perm == k)[0][0])             # where column k was packed
+                    assert i // group == g, "a column left its group"
+                    assert codes[n, i] == ecode[k], (trial, n, k)
+                    assert sb[n, g] == esb and z[n, g] == ez, (trial, n, g)
+                    assert Fraction(d[n, k]) == (ecode[k] - ez) * s
+                    assert Fraction(dl[n][k]) == (ecode[k] - ez) * s
+        if g_idx is not None:
+            assert np.all(np.diff(np.array(labels)[perm]) >= 0)
+            for g in range(G):
+                ks = perm[g * group:(g + 1) * group]
+                assert np.all(np.diff(ks) > 0), "columns of a group not in ascending order"
+
+
+def pin_w4a_bounds_and_zero(o):
+    """Zero dequantizes to exactly 0; the group's minimum gets code 0; every
+    error is at most half a step plus the scale's rounding over 15 steps."""
+    rng = np.random.default_rng(5)
+    w = (rng.standard_normal((64, 1024)) * 0.02).astype(np.float32)
+    w[:, ::17] = 0.0
+    q, sb, z, perm = o.w4asym.w4a_pack(w)
+    d = o.w4asym.w4a_dequant(q, sb, z, 1024, perm)
+    assert np.all(d[:, ::17] == 0.0)
+    g = w.reshape(64, 8, 128).astype(np.float64)
+    lo = np.minimum(g.min(axis=2), 0)
+    hi = np.maximum(g.max(axis=2), 0)
+    s = o.rne.f16_values(sb)
+    bound = 0.5 * s + 15 * np.abs(s - (hi - lo) / 15) + 1e-12
+    err = np.abs(d - w.astype(np.float64)).reshape(64, 8, 128).max(axis=2)
+    assert np.all(err <= bound)
+    codes = o.w4asym.w4a_unpack(q, 1024).reshape(64, 8, 128)
+    amin = g.argmin(axis=2)
+    neg = g.min(axis=2) < 0
+    got = np.take_along_axis(codes, amin[:, :, None], axis=2)[:, :, 0]
+    assert np.all(got[neg] == 0)
+
+
+def pin_w4a_errors_and_identity_order(o):
+    """g_idx with a group of the wrong size or out of range is a GROUP error;
+    g_idx = k // 128 gives the identity order and the results without it."""
+    w = (np.random.default_rng(2).standard_normal((4, 256)) * 0.02).astype(np.float32)
+    ident = np.arange(256) // 128
+    a = o.w4asym.w4a_pack(w)
+    b = o.w4asym.w4a_pack(w, ident)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+    for bad in (np.zeros(256, dtype=np.int32), np.full(256, 2), np.r_[np.zeros(129), np.ones(127)]):
+        for fn in (o.w4asym.w4a_pack, lambda W, g: o.w4asym.w4a_pack_loop(W.tolist(), g.tolist())):
+            try:
+                fn(w, bad)
+            except o.errors.OracleError as e:
+                assert e.kind == "GROUP"
+            else:
+                raise AssertionError("bad g_idx accepted")
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -47,6 +47,20 @@ MUTATIONS = [
     ("w4.py", "np.clip(r, QMIN, QMAX)", "np.clip(r, -7, 7)"),
     ("w4.py", "s = np.repeat(f16_values(scale_bits), group, axis=1)", "s = np.tile(f16_values(scale_bits), (1, group))"),
     ("w4.py", "rv = int(_round_half_even(v / s))", "rv = int(v / s)"),
+    ("w4asym.py", "lo = np.minimum(w.min(axis=2), 0.0)", "lo = w.min(axis=2)"),
+    ("w4asym.py", "hi = np.maximum(w.max(axis=2), 0.0)", "hi = w.max(axis=2)"),
+    ("w4asym.py", "sb = f16_bits((hi - lo) / 15.0)", "sb = f16_bits((hi - lo) / 16.0)"),
+    ("w4asym.py", "np.clip(np.rint(-lo / s), 0, QMAX)", "np.clip(np.floor(-lo / s), 0, QMAX)"),
+    ("w4asym.py", "q = np.rint(w / s[:, :, None]) + z[:, :, None]", "q = np.rint(w / s[:, :, None]) - z[:, :, None]"),
+    ("w4asym.py", "np.clip(q, 0, QMAX))", "np.clip(q, 0, 14))"),
+    ("w4asym.py", 'return np.argsort(g, kind="stable")', 'return np.argsort(-g, kind="stable")'),
+    ("w4asym.py", "packed = (q - z) * s", "packed = (q + z) * s"),
+    ("w4asym.py", "out[:, np.asarray(perm)] = packed", "out = packed[:, np.asarray(perm)]"),
+    ("w4asym.py", "word |= q[:, :, i] << np.uint32(BITS * i)", "word |= q[:, :, 7 - i] << np.uint32(BITS * i)"),
+    ("w4asym.py", "z = int(min(max(_rint(-lo / s), 0), QMAX))", "z = int(min(max(_rint(lo / s), 0), QMAX))"),
+    ("w4asym.py", "                if v < lo:", "                if v > lo:"),
+    ("w4asym.py", "if np.any(np.bincount(g, minlength=G) != group):", "if False:"),
+    ("w4asym.py", "row[perm[i]] = (q - z_row[g]) * f16_value_exact(s_row[g])", "row[i] = (q - z_row[g]) * f16_value_exact(s_row[g])"),
     ("gemm.py", "out = A64 @ wdq64.T", "out = A64 @ wdq64[::-1].T"),
     ("gemm.py", "mag = np.abs(A64) @ np.abs(wdq64).T", "mag = np.abs(A64 @ wdq64.T)"),
     ("gemm.py", "mag = mag + np.abs(b)[None, :]", "mag = mag + b[None, :]"),
@@ -70,7 +84,7 @@ def _load_mutant(tmp_path, idx, fname, old, new):
     sys.path.insert(0, str(tmp_path))
     try:
         pkg = importlib.import_module(name)
-        for sub in ("rne", "ternary", "w4", "gemm", "check"):
+        for sub in ("errors", "rne", "ternary", "w4", "w4asym", "gemm", "check"):
             importlib.import_module(f"{name}.{sub}")
     finally:
         sys.path.remove(str(tmp_path))

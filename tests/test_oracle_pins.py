@@ -6,7 +6,9 @@ import oracle.check
 import oracle.gemm
 import oracle.rne
 import oracle.ternary
+import oracle.errors
 import oracle.w4
+import oracle.w4asym
 from oracle_pins import ALL_PINS
 
 
