@@ -62,7 +62,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--layers", type=int, default=32)
     ap.add_argument("--mode", default="full",
-                    choices=["full", "decode", "decodem", "decode70b", "w4", "medium", "prefill", "attrib", "calib"])
+                    choices=["full", "decode", "decodem", "decode70b", "w4", "w4act", "medium", "prefill", "attrib",
+                             "calib"])
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
     ap.add_argument("--unfused", action="store_true", help="decode mode: q,k,v,gate,up as separate calls")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -195,8 +196,16 @@ def w4_bytes(M, N, K):
     return N * K // 2 + 2 * N * (K // 128) + 2 * M * K + 2 * M * N
 
 
-def run_w4_decode(args, dev, Ms=(1, 4, 16)):
-    """Llama-3-8B decode step with W4A16 weights, fused layout, graph replay."""
+def w4_act_bytes(M, N, K):
+    """Algorithmic bytes of one W4A16 call with zero points and activation
+    order: codes + group scales + zero points + A + the gathered A (written
+    once, read once) + C."""
+    return w4_bytes(M, N, K) + N * (K // 128) + 4 * M * K
+
+
+def run_w4_decode(args, dev, Ms=(1, 4, 16), act_order=False):
+    """Llama-3-8B decode step with W4A16 weights, fused layout, graph replay;
+    act_order: zero points and activation-order groups (gather + kernel)."""
     import torch
     import bit_weight_only_tq_amd as tq
     import synth
@@ -205,20 +214,32 @@ def run_w4_decode(args, dev, Ms=(1, 4, 16)):
     for layer in range(args.layers):
         for name, (N, K) in layer_shapes(True):
             W = synth.weights_device(N, K, synth.seed_for("benchw4", layer, name), dev)
-            q, sc = tq.w4a16_pack(W)
+            if act_order:
+                gi = torch.from_numpy(synth.group_index(K, synth.seed_for("benchw4g", layer, name))).to(dev)
+                q, sc, zp, perm = tq.w4a16_pack_asym(W, gi)
+            else:
+                (q, sc), zp, perm = tq.w4a16_pack(W), None, None
             del W
-            mats.append((N, K, q, sc))
+            mats.append((N, K, q, sc, zp, perm))
     torch.cuda.synchronize()
-    packed = sum(m[2].numel() * 4 + m[3].numel() * 2 for m in mats)
-    res = {"metric": "HBM GB/s W4A16 GEMV, Llama-3-8B decode (32 layers, fused qkv / gate_up)",
+    packed = sum(m[2].numel() * 4 + m[3].numel() * 2 + (m[4].numel() if act_order else 0) for m in mats)
+    what = "W4A16 with zero points and activation order" if act_order else "W4A16"
+    res = {"metric": f"HBM GB/s {what} GEMV, Llama-3-8B decode (32 layers, fused qkv / gate_up)",
            "unit": "GB/s", "packed_bytes_per_step": packed, "launches_per_step": len(mats)}
     for M in Ms:
         xs = {K: synth.activations_device(M, K, synth.seed_for("benchw4x", K, M), "f16", dev) for K in {m[1] for m in mats}}
         outs = [torch.empty((M, m[0]), dtype=torch.float16, device=dev) for m in mats]
+        ws = None
+        if act_order:  # one workspace for every call: they run in order on one stream
+            nb = max(tq.w4a16_gemm_asym_workspace_bytes(M, m[0], m[1], with_perm=True) for m in mats)
+            ws = torch.empty((nb,), dtype=torch.uint8, device=dev)
 
         def step():
-            for i, (N, K, q, sc) in enumerate(mats):
-                tq.w4a16_gemm(xs[K], q, sc, out=outs[i])
+            for i, (N, K, q, sc, zp, perm) in enumerate(mats):
+                if act_order:
+                    tq.w4a16_gemm(xs[K], q, sc, out=outs[i], zeros=zp, perm=perm, workspace=ws)
+                else:
+                    tq.w4a16_gemm(xs[K], q, sc, out=outs[i])
 
         g = torch.cuda.CUDAGraph()
         side = torch.cuda.Stream()
@@ -232,13 +253,13 @@ def run_w4_decode(args, dev, Ms=(1, 4, 16)):
         for _ in range(args.warmup):
             g.replay()
         t = time_region(g.replay, args.steps, stream)
-        alg = sum(w4_bytes(M, m[0], m[1]) for m in mats)
+        alg = sum((w4_act_bytes if act_order else w4_bytes)(M, m[0], m[1]) for m in mats)
         res[f"M{M}"] = {"value": round(packed * args.steps / t / 1e9, 1),
                         "frac_of_peak": round(packed * args.steps / t / 1e9 / HBM_PEAK_GBS, 4),
                         "ms_per_step": round(t / args.steps * 1e3, 4),
                         "avg_launch_us": round(t / args.steps / len(mats) * 1e6, 3),
                         "alg_gbs": round(alg * args.steps / t / 1e9, 1)}
-        del g, xs, outs
+        del g, xs, outs, ws
     del mats
     torch.cuda.empty_cache()
     return res
@@ -511,6 +532,9 @@ def main():
     if args.mode == "w4":
         print(json.dumps({"w4a16_decode": run_w4_decode(args, dev)}), flush=True)
         return
+    if args.mode == "w4act":
+        print(json.dumps({"w4a16_act_decode": run_w4_decode(args, dev, act_order=True)}), flush=True)
+        return
     if args.mode == "medium":
         print(json.dumps({"medium_m": run_medium(dev)}), flush=True)
         return
@@ -565,6 +589,8 @@ def main():
         out["decode_70b"] = run_decode_70b(args, dev)
         log("W4A16 decode")
         out["w4a16_decode"] = run_w4_decode(args, dev)
+        log("W4A16 decode, zero points and activation order")
+        out["w4a16_act_decode"] = run_w4_decode(args, dev, act_order=True)
         log("medium M")
         out["medium_m"] = run_medium(dev)
         log("prefill GEMM M=4096")

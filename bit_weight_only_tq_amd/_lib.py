@@ -39,6 +39,11 @@ SIGNATURES = {
     "w4a16_gemm_ex": (_i32, [_vp, _i32, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _vp, _i32]),
     "w4a16_gemm_ws": (_i32, [_vp, _i32, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp, _i32]),
     "w4a16_gemm_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32, _i64]),
+    "w4a16_pack_asym": (_i32, [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "w4a16_unpack_asym": (_i32, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp]),
+    "w4a16_gemm_asym": (_i32, [_vp, _i32, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp,
+                               _i32]),
+    "w4a16_gemm_asym_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32, _i64, _i32]),
     "tq_select_path": (_i32, [_i32, _i64, _i64, _i64, _i32]),
     "tq_status_str": (ctypes.c_char_p, [_i32]),
     "tq_abi_version": (_i32, []),
@@ -65,6 +70,11 @@ def load(path: str = LIB_PATH):
     if not os.path.exists(path):
         raise RuntimeError(f"libtq.so not built: {path} is missing "
                            "(run `python -m bit_weight_only_tq_amd.build`)")
+    # torch ships its own HIP runtime under another file name; loading it
+    # first makes libtq.so bind to that copy.  Loaded the other way round the
+    # process would hold two runtimes, and torch's device pointers and
+    # streams would be foreign to the library's.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(path)
     for name, (res, args) in SIGNATURES.items():
         f = getattr(lib, name)
@@ -155,6 +165,39 @@ def w4a16_unpack(qweight, scales, K: int, group_size: int = 128, want_q: bool = 
     return q, w
 
 
+def w4a16_pack_asym(W, g_idx=None, group_size: int = 128):
+    """fp32 [N, K] (+ g_idx int32 [K]) -> (qweight int32 [N, K/8], scales fp16 [N, G],
+    zeros uint8 [N, G], perm int32 [K] or None); columns packed in group order."""
+    import torch
+    _need_cuda(W, g_idx)
+    if W.dtype != torch.float32 or W.dim() != 2:
+        raise TypeError("W must be a 2-D float32 tensor")
+    if g_idx is not None and (g_idx.dtype != torch.int32 or g_idx.numel() != W.shape[1]):
+        raise TypeError("g_idx must be an int32 tensor of K entries")
+    N, K = W.shape
+    G = max(K // max(group_size, 1), 1)
+    q = torch.empty((N, K // 8), dtype=torch.int32, device=W.device)
+    s = torch.empty((N, G), dtype=torch.float16, device=W.device)
+    z = torch.empty((N, G), dtype=torch.uint8, device=W.device)
+    perm = torch.empty((K,), dtype=torch.int32, device=W.device) if g_idx is not None else None
+    _check("w4a16_pack_asym", load().w4a16_pack_asym(_ptr(W), N, K, group_size, _ptr(g_idx), _ptr(q), _ptr(s),
+                                                     _ptr(z), _ptr(perm), _stream(W.device)))
+    return q, s, z, perm
+
+
+def w4a16_unpack_asym(qweight, scales, zeros, K: int, perm=None, group_size: int = 128, want_q: bool = True,
+                      want_wdq: bool = True):
+    """-> (q uint8 [N, K] packed order or None, wdq fp16 [N, K] input order or None)."""
+    import torch
+    _need_cuda(qweight, scales, zeros, perm)
+    N = qweight.shape[0]
+    q = torch.empty((N, K), dtype=torch.uint8, device=qweight.device) if want_q else None
+    w = torch.empty((N, K), dtype=torch.float16, device=qweight.device) if want_wdq else None
+    _check("w4a16_unpack_asym", load().w4a16_unpack_asym(_ptr(qweight), _ptr(scales), _ptr(zeros), _ptr(perm), N,
+                                                         K, group_size, _ptr(q), _ptr(w), _stream(qweight.device)))
+    return q, w
+
+
 # -------------------------------------------------------------------- apply
 
 def tq_gemm_workspace_bytes(M: int, N: int, K: int, dtype: str = "f16", path: str = "auto") -> int:
@@ -193,24 +236,42 @@ def w4a16_gemm_workspace_bytes(M: int, N: int, K: int, dtype: str = "f16", group
     return int(load().w4a16_gemm_workspace_bytes(M, N, K, d, group_size))
 
 
-def w4a16_gemm(A, qweight, scales, bias=None, out=None, group_size: int = 128, path: str = "auto",
-               workspace="auto"):
-    """C = A @ dequant(qweight, scales)^T (+ bias); A [M, K] fp16/bf16.
+def w4a16_gemm_asym_workspace_bytes(M: int, N: int, K: int, dtype: str = "f16", group_size: int = 128,
+                                    with_perm: bool = False) -> int:
+    """Bytes of workspace w4a16_gemm_asym uses for its fastest schedule."""
+    d = {"f16": TQ_F16, "bf16": TQ_BF16}[dtype]
+    return int(load().w4a16_gemm_asym_workspace_bytes(M, N, K, d, group_size, 1 if with_perm else 0))
 
+
+def w4a16_gemm(A, qweight, scales, bias=None, out=None, group_size: int = 128, path: str = "auto",
+               workspace="auto", zeros=None, perm=None):
+    """C = A @ dequant(qweight, scales[, zeros])^T (+ bias); A [M, K] fp16/bf16.
+
+    zeros / perm: the zero points and column order of w4a16_pack_asym (both
+    optional); with either, the zero-point entry point runs.
     workspace: as for tq_gemm ("auto", None or a contiguous device tensor)."""
     import torch
-    _need_cuda(A, qweight, scales, bias)
+    _need_cuda(A, qweight, scales, bias, zeros, perm)
     M, K = A.shape
     N = qweight.shape[0]
     dt = _dtype_enum(A)
     C = out if out is not None else torch.empty((M, N), dtype=A.dtype, device=A.device)
+    asym = zeros is not None or perm is not None
     if isinstance(workspace, str):
-        nbytes = int(load().w4a16_gemm_workspace_bytes(M, N, K, dt, group_size))
+        if asym:
+            nbytes = int(load().w4a16_gemm_asym_workspace_bytes(M, N, K, dt, group_size, 1 if perm is not None else 0))
+        else:
+            nbytes = int(load().w4a16_gemm_workspace_bytes(M, N, K, dt, group_size))
         workspace = torch.empty((nbytes,), dtype=torch.uint8, device=A.device) if nbytes else None
     ws_bytes = 0
     if workspace is not None:
         _need_cuda(workspace)
         ws_bytes = workspace.numel() * workspace.element_size()
+    if asym:
+        _check("w4a16_gemm_asym", load().w4a16_gemm_asym(
+            _ptr(A), dt, M, N, K, _ptr(qweight), _ptr(scales), _ptr(zeros), _ptr(perm), group_size, _ptr(bias),
+            _ptr(C), _ptr(workspace), ws_bytes, _stream(A.device), PATHS[path]))
+        return C
     _check("w4a16_gemm", load().w4a16_gemm_ws(_ptr(A), dt, M, N, K, _ptr(qweight), _ptr(scales), group_size,
                                                _ptr(bias), _ptr(C), _ptr(workspace), ws_bytes, _stream(A.device),
                                                PATHS[path]))

@@ -244,6 +244,95 @@ tq_status w4a16_gemm_ex(const void* A, tq_dtype dt, int64_t M, int64_t N, int64_
     return w4a16_gemm_ws(A, dt, M, N, K, qweight, scales_f16, group_size, bias, C, nullptr, 0, stream, path);
 }
 
+// ------------------------------------------- W4A16, zero points and act order
+
+tq_status w4a16_pack_asym(const float* W, int64_t N, int64_t K, int64_t group_size, const int32_t* g_idx,
+                          int32_t* qweight, uint16_t* scales_f16, uint8_t* zeros, int32_t* perm,
+                          hipStream_t stream) {
+    if (!W || !qweight || !scales_f16 || !zeros) return TQ_ERR_NULL;
+    if (g_idx && !perm) return TQ_ERR_NULL;
+    if (group_size != 128) return TQ_ERR_GROUP;
+    if (N <= 0 || K <= 0 || (K % 128) != 0) return TQ_ERR_SHAPE;
+    if ((reinterpret_cast<uintptr_t>(W) & 3u) || (reinterpret_cast<uintptr_t>(qweight) & 3u) ||
+        (reinterpret_cast<uintptr_t>(scales_f16) & 1u) || (reinterpret_cast<uintptr_t>(g_idx) & 3u) ||
+        (reinterpret_cast<uintptr_t>(perm) & 3u))
+        return TQ_ERR_ALIGN;
+    StatusWord st;
+    tq_status r = st.init(stream);
+    if (r != TQ_OK) return r;
+    int flags[4];
+    if (tq::launch_finite_scan(W, N * K, st.dev, stream) != hipSuccess) return TQ_ERR_HIP;
+    if ((r = st.read(stream, flags)) != TQ_OK) return r;
+    if (flags[0]) return TQ_ERR_NONFINITE;
+    if (g_idx) {
+        if (tq::launch_w4a_order(g_idx, K, perm, st.dev, stream) != hipSuccess) return TQ_ERR_HIP;
+        if ((r = st.read(stream, flags)) != TQ_OK) return r;
+        if (flags[3]) return TQ_ERR_GROUP;
+    }
+    if (tq::launch_w4a_pack(W, N, K, g_idx ? perm : nullptr, qweight, scales_f16, zeros, st.dev, stream) != hipSuccess)
+        return TQ_ERR_HIP;
+    if ((r = st.read(stream, flags)) != TQ_OK) return r;
+    if (flags[1]) return TQ_ERR_RANGE;
+    return TQ_OK;
+}
+
+tq_status w4a16_unpack_asym(const int32_t* qweight, const uint16_t* scales_f16, const uint8_t* zeros,
+                            const int32_t* perm, int64_t N, int64_t K, int64_t group_size, uint8_t* q_out,
+                            uint16_t* wdq_f16_out, hipStream_t stream) {
+    if (!qweight || !scales_f16 || !zeros) return TQ_ERR_NULL;
+    if (group_size != 128) return TQ_ERR_GROUP;
+    if (N <= 0 || K <= 0 || (K % 128) != 0) return TQ_ERR_SHAPE;
+    if ((reinterpret_cast<uintptr_t>(qweight) & 3u) || (reinterpret_cast<uintptr_t>(scales_f16) & 1u) ||
+        (reinterpret_cast<uintptr_t>(perm) & 3u) || (reinterpret_cast<uintptr_t>(wdq_f16_out) & 1u))
+        return TQ_ERR_ALIGN;
+    if (tq::launch_w4a_unpack(qweight, scales_f16, zeros, perm, N, K, q_out, wdq_f16_out, stream) != hipSuccess)
+        return TQ_ERR_HIP;
+    return from_hip(hipStreamSynchronize(stream));
+}
+
+namespace {
+// Workspace of the act-order gather: the activations in packed column order.
+size_t gather_bytes(int64_t M, int64_t K) { return ((size_t)M * (size_t)K * 2 + 255) & ~(size_t)255; }
+}  // namespace
+
+size_t w4a16_gemm_asym_workspace_bytes(int64_t M, int64_t N, int64_t K, tq_dtype dt, int64_t group_size,
+                                       int with_perm) {
+    if (M <= 0 || N <= 0 || K <= 0 || K % 128 != 0 || group_size != 128) return 0;
+    return (with_perm ? gather_bytes(M, K) : 0) + w4a16_gemm_workspace_bytes(M, N, K, dt, group_size);
+}
+
+tq_status w4a16_gemm_asym(const void* A, tq_dtype dt, int64_t M, int64_t N, int64_t K, const int32_t* qweight,
+                          const uint16_t* scales_f16, const uint8_t* zeros, const int32_t* perm, int64_t group_size,
+                          const void* bias, void* C, void* workspace, size_t workspace_bytes, hipStream_t stream,
+                          tq_path path) {
+    tq_status r = check_gemm_common(A, dt, M, N, K, qweight, scales_f16, C);
+    if (r != TQ_OK) return r;
+    if (group_size != 128) return TQ_ERR_GROUP;
+    if (K % 128 != 0) return TQ_ERR_SHAPE;
+    if (bias && (reinterpret_cast<uintptr_t>(bias) & 1u)) return TQ_ERR_ALIGN;
+    if (perm && (reinterpret_cast<uintptr_t>(perm) & 3u)) return TQ_ERR_ALIGN;
+    if (workspace && !aligned16(workspace)) return TQ_ERR_ALIGN;
+    if (path == TQ_PATH_AUTO) path = tq_select_path(1, M, N, K, dt);
+    if (path != TQ_PATH_GEMV) return TQ_ERR_PATH;
+    const uint16_t* a_eff = static_cast<const uint16_t*>(A);
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    size_t wsb = workspace ? workspace_bytes : 0;
+    if (perm) {  // gather the activations into packed column order, at the front of the workspace
+        const size_t gb = gather_bytes(M, K);
+        if (wsb < gb) return TQ_ERR_SHAPE;
+        if (tq::launch_gather_columns(a_eff, perm, M, K, reinterpret_cast<uint16_t*>(ws), stream) != hipSuccess)
+            return TQ_ERR_HIP;
+        a_eff = reinterpret_cast<const uint16_t*>(ws);
+        ws += gb;
+        wsb -= gb;
+    }
+    tq::GemmArgs a{a_eff, dt == TQ_BF16 ? 1 : 0, M, N, K, qweight, scales_f16,
+                   static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(C), zeros};
+    void* rest = wsb ? ws : nullptr;
+    if (M > kGemvMaxM) return from_hip(tq::launch_w4_gemm(a, rest, wsb, stream));
+    return from_hip(tq::launch_w4_gemv(a, rest, wsb, stream));
+}
+
 tq_status w4a16_gemm(const void* A, tq_dtype dt, int64_t M, int64_t N, int64_t K, const int32_t* qweight,
                      const uint16_t* scales_f16, int64_t group_size, const void* bias, void* C, hipStream_t stream) {
     return w4a16_gemm_ex(A, dt, M, N, K, qweight, scales_f16, group_size, bias, C, stream, TQ_PATH_AUTO);

@@ -11,6 +11,8 @@
 // W4A16 (page "Model quantization - vLLM runtime quantization architecture",
 // section 5): value = q - 8 with a per-(row, 128-column group) fp16 scale.
 
+#include <type_traits>
+
 #include "tq_device.h"
 #include "tq_internal.h"
 
@@ -81,6 +83,7 @@ __global__ __launch_bounds__(kGemvWaves * kWave) void w4_gemv_kernel(GemmArgs p)
     const int64_t chunks = K / 32;
     const uint4* wrow = reinterpret_cast<const uint4*>(static_cast<const int32_t*>(p.wq) + row * (K / 8));
     const uint16_t* srow = p.scale + row * (K / 128);
+    const uint8_t* zrow = p.zeros ? p.zeros + row * (K / 128) : nullptr;
     float acc[MT];
 #pragma unroll
     for (int m = 0; m < MT; ++m) acc[m] = 0.0f;
@@ -89,6 +92,7 @@ __global__ __launch_bounds__(kGemvWaves * kWave) void w4_gemv_kernel(GemmArgs p)
         const uint4 q = wrow[c];
         const uint32_t qw[4] = {q.x, q.y, q.z, q.w};
         const float s = f16_bits_to_f32(srow[c >> 2]);
+        const int zp = zrow ? (int)zrow[c >> 2] : 8;
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
             if (m < p.M) {
@@ -101,7 +105,7 @@ __global__ __launch_bounds__(kGemvWaves * kWave) void w4_gemv_kernel(GemmArgs p)
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
                         const uint16_t h = (uint16_t)(aw[e >> 1] >> (16 * (e & 1)));
-                        const float v = (float)((int)((qw[d] >> (4 * e)) & 15u) - 8);
+                        const float v = (float)((int)((qw[d] >> (4 * e)) & 15u) - zp);
                         part = fmaf(v, T::to_f32(h), part);
                     }
                 }
@@ -829,11 +833,18 @@ __global__ __launch_bounds__(W * kWave) void w4_gemv_mfma_kernel(GemmArgs p) {
 // one vmcnt wait for the DMA only.  With S = gridDim.y > 1 splits of the groups
 // the workgroup stores fp32 partials (group scales applied) for
 // launch_splitk_reduce.
+// ASYM: per-(row, group) zero points z instead of 8.  A group's start term
+// then depends on the row: sum_k a' (1024 + 16^s q) - sum_k a' (1024 +
+// 16^s z) = acc - 1024 sum a' - z sum a.  So each wave also contracts the
+// group's operand with the constant -1024 pattern (D) and with (1, 16, 1, 16)
+// (sum a, the same for every weight row), and each row-block subtracts z
+// times the latter from its group sum.  The zero points are loaded with the
+// scales, before the DMA.
 __host__ __device__ constexpr int w4_stream_wave_lds(int gsw, int mr, int t) {  // bytes of one wave's LDS area
     return t * 1024 > gsw * mr * 256 ? t * 1024 : gsw * mr * 256;
 }
 
-template <int GSW, int T, int MR>
+template <int GSW, int T, int MR, bool ASYM>
 __global__ __launch_bounds__(1024) void w4_gemv_stream_kernel(SplitArgs sa) {
     const GemmArgs& p = sa.g;
     extern __shared__ uint4 smem[];
@@ -867,15 +878,29 @@ __global__ __launch_bounds__(1024) void w4_gemv_stream_kernel(SplitArgs sa) {
         const int64_t nc = n < N ? n : N - 1;
         bi_bits = (p.bias ? p.bias : p.scale)[nc];
     }
-    // group scales of all row-blocks, first: the codes are waited for in
-    // order, so scales issued after them would hold up row-block 0
-    uint16_t sc[T][GSW];
+    // group scales (and zero points) of all row-blocks, first: the codes are
+    // waited for in order, so loads issued after them would hold up
+    // row-block 0.  Each such load costs the address unit about as much as a
+    // code load (one lane per row, so 64 cache lines), hence few of them: one
+    // load serves four row-blocks (lane 16 j + r fetches row r of row-block
+    // 4 c + j; rows past the workgroup's are clamped and unused) and, with
+    // two groups per wave, both groups (a dword of scales, a halfword of zero
+    // points: the plan takes two groups per wave only when G and the groups
+    // per split are even and the arrays aligned, so g0 is even and the pair
+    // lies in the row).  After the wait, lane shuffles hand each value to the
+    // lanes that use it.
+    static_assert(GSW == 1 || GSW == 2, "one or two groups per wave");
+    using ScaleT = std::conditional_t<GSW == 2, uint32_t, uint16_t>;
+    using ZeroT = std::conditional_t<GSW == 2, uint16_t, uint8_t>;
+    constexpr int TC = (T + 3) / 4;
+    ScaleT scl[TC];
+    ZeroT zpl[TC];
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
-        const int64_t n = n_base + 16 * t + i16;
-        const uint16_t* srow = p.scale + (n < N ? n : N - 1) * G;
-#pragma unroll
-        for (int s = 0; s < GSW; ++s) sc[t][s] = srow[(s < cnt) ? g0 + s : g0];
+    for (int c = 0; c < TC; ++c) {
+        const int64_t n = n_base + 16 * (4 * c + h) + i16;
+        const int64_t o = (n < N ? n : N - 1) * G + g0;
+        scl[c] = *reinterpret_cast<const ScaleT*>(p.scale + o);
+        if constexpr (ASYM) zpl[c] = *reinterpret_cast<const ZeroT*>(p.zeros + o);
     }
     // 1. activation slices -> LDS by DMA (rows past M re-read row M-1)
 #pragma unroll
@@ -910,12 +935,16 @@ __global__ __launch_bounds__(1024) void w4_gemv_stream_kernel(SplitArgs sa) {
     asm volatile("s_waitcnt vmcnt(%0)" :: "n"(T * GSW) : "memory");
     const int rd_row = i16 & (MR - 1);
     const f16x2 sixteenth = f16x2{(_Float16)0.0625f, (_Float16)0.0625f};
-    const uint4 negp = make_uint4(kW4Neg0, kW4Neg1, kW4Neg0, kW4Neg1);
+    // symmetric: -(1024 + 8 * 16^s); ASYM: -1024, and the (1, 16) pattern for sum a
+    const uint4 negp = ASYM ? make_uint4(0xE400E400u, 0xE400E400u, 0xE400E400u, 0xE400E400u)
+                            : make_uint4(kW4Neg0, kW4Neg1, kW4Neg0, kW4Neg1);
+    const uint4 sump = make_uint4(0x3C003C00u, 0x4C004C00u, 0x3C003C00u, 0x4C004C00u);
     uint4 aop[GSW][4];
-    f32x4 dacc[GSW];
+    f32x4 dacc[GSW], sacc[GSW];
 #pragma unroll
     for (int s = 0; s < GSW; ++s) {
         dacc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+        sacc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
             const uint4 v = *reinterpret_cast<const uint4*>(area + s * MR * 256 + rd_row * 256 +
@@ -926,6 +955,33 @@ __global__ __launch_bounds__(1024) void w4_gemv_stream_kernel(SplitArgs sa) {
             const uint32_t p3 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(v.w, v.y, 0x07060302u)) * sixteenth);
             aop[s][d] = make_uint4(p0, p1, p2, p3);
             dacc[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, aop[s][d]), __builtin_bit_cast(f16x8, negp), dacc[s], 0, 0, 0);
+            if constexpr (ASYM)
+                sacc[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, aop[s][d]), __builtin_bit_cast(f16x8, sump), sacc[s], 0, 0, 0);
+        }
+    }
+
+    // the empty asm statements keep the compiler from consuming the loaded
+    // values, with a wait of their own, before the wait above
+    int sc[T][GSW], zp[T][GSW];
+#pragma unroll
+    for (int c = 0; c < TC; ++c) {
+        int sv = (int)scl[c];
+        asm volatile("" : "+v"(sv));
+        int zv = 0;
+        if constexpr (ASYM) {
+            zv = (int)zpl[c];
+            asm volatile("" : "+v"(zv));
+        }
+#pragma unroll
+        for (int j = 0; j < 4 && 4 * c + j < T; ++j) {
+            const int t = 4 * c + j;
+            const int sx = __shfl(sv, 16 * j + i16);
+            const int zx = ASYM ? __shfl(zv, 16 * j + i16) : 0;
+#pragma unroll
+            for (int s = 0; s < GSW; ++s) {
+                sc[t][s] = (sx >> (16 * s)) & 0xFFFF;
+                zp[t][s] = (zx >> (8 * s)) & 0xFF;
+            }
         }
     }
 
@@ -947,7 +1003,12 @@ __global__ __launch_bounds__(1024) void w4_gemv_stream_kernel(SplitArgs sa) {
                                                 (y & sgpr_const<0x000F000Fu>()) | magic_v, (y & sgpr_const<0x00F000F0u>()) | magic_v);
                     ag = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, aop[s][d]), __builtin_bit_cast(f16x8, bw), ag, 0, 0, 0);
                 }
-                const float sv = f16_bits_to_f32(sc[t][s]);
+                if constexpr (ASYM) {
+                    const float z = (float)zp[t][s];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) ag[i] = fmaf(-z, sacc[s][i], ag[i]);
+                }
+                const float sv = f16_bits_to_f32((uint16_t)sc[t][s]);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) a4[i] = fmaf(sv, ag[i], a4[i]);
             }
@@ -1264,6 +1325,15 @@ struct W4StreamPlan {
     size_t lds;
 };
 
+// Two groups per wave read their scales and zero points in pairs: the pair
+// offset row * G + g0 must be even (G and the groups per split even, so g0 is
+// too) and the arrays aligned to the pair's size.
+static bool w4_pairs_ok(const GemmArgs& a, int S) {
+    const int64_t g_all = a.K / 128;
+    return g_all % 2 == 0 && (g_all / S) % 2 == 0 && (reinterpret_cast<uintptr_t>(a.scale) & 3u) == 0 &&
+           (reinterpret_cast<uintptr_t>(a.zeros) & 1u) == 0;
+}
+
 static bool w4_stream_geometry(const GemmArgs& a, int S, int64_t cus, W4StreamPlan* pl) {
     const int64_t g_all = a.K / 128;
     if (S < 1 || g_all % S != 0) return false;
@@ -1271,6 +1341,7 @@ static bool w4_stream_geometry(const GemmArgs& a, int S, int64_t cus, W4StreamPl
     if (gs > 32 || (S > 1 && gs < 4)) return false;
     pl->S = S;
     pl->gsw = gs <= 16 ? 1 : 2;
+    if (pl->gsw == 2 && !w4_pairs_ok(a, S)) return false;
     pl->waves = (int)((gs + pl->gsw - 1) / pl->gsw);
     pl->mr = a.M <= 4 ? 4 : a.M <= 8 ? 8 : 16;
     const int64_t nrb = (a.N + 15) / 16;
@@ -1315,17 +1386,23 @@ size_t w4_gemv_workspace_bytes(const GemmArgs& a) {
     return (size_t)pl.S * (size_t)a.M * (size_t)a.N * sizeof(float);
 }
 
-template <int GSW, int T, int MR>
-static hipError_t launch_w4_stream(const SplitArgs& sa, const W4StreamPlan& pl, hipStream_t s) {
+template <int GSW, int T, int MR, bool ASYM>
+static hipError_t launch_w4_stream_k(const SplitArgs& sa, const W4StreamPlan& pl, hipStream_t s) {
     static DeviceFlags lds_limit_set;
-    hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(&w4_gemv_stream_kernel<GSW, T, MR>),
+    hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(&w4_gemv_stream_kernel<GSW, T, MR, ASYM>),
                                    kGemvLdsMaxBytes, lds_limit_set);
     if (e != hipSuccess) return e;
     if (pl.lds != (size_t)pl.waves * w4_stream_wave_lds(GSW, MR, T)) return hipErrorInvalidValue;
+    if (GSW == 2 && !w4_pairs_ok(sa.g, sa.S)) return hipErrorInvalidValue;
     const dim3 grid((unsigned)((sa.g.N + 16 * T - 1) / (16 * T)), (unsigned)sa.S);
-    w4_gemv_stream_kernel<GSW, T, MR><<<grid, dim3(pl.waves * kWave), pl.lds, s>>>(sa);
+    w4_gemv_stream_kernel<GSW, T, MR, ASYM><<<grid, dim3(pl.waves * kWave), pl.lds, s>>>(sa);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     return sa.S > 1 ? launch_splitk_reduce(sa, s) : hipSuccess;
+}
+
+template <int GSW, int T, int MR>
+static hipError_t launch_w4_stream(const SplitArgs& sa, const W4StreamPlan& pl, hipStream_t s) {
+    return sa.g.zeros ? launch_w4_stream_k<GSW, T, MR, true>(sa, pl, s) : launch_w4_stream_k<GSW, T, MR, false>(sa, pl, s);
 }
 
 template <int MR>
@@ -1357,11 +1434,31 @@ hipError_t launch_w4_gemv(const GemmArgs& a, void* workspace, size_t workspace_b
     W4StreamPlan sp;
     if (w4_stream_plan(a, workspace ? workspace_bytes : 0, &sp))
         return launch_w4_stream_t(SplitArgs{a, static_cast<float*>(workspace), sp.S, 1}, sp, s);
-    if (!a.bf16 && a.M >= 3 && a.M <= kGemvMaxM) {
+    if (!a.bf16 && a.M >= 3 && a.M <= kGemvMaxM && !a.zeros) {  // zero point 8 only
         const int64_t nrb = (a.N + 15) / 16;
         return nrb >= 1024 ? launch_w4_mfma_w<2>(a, s) : launch_w4_mfma_w<1>(a, s);
     }
     return launch_w4_gemv_simple(a, s);
+}
+
+// A_perm[m, i] = A[m, perm[i]]: one thread per element (the index is clamped
+// into [0, K), so any perm contents stay in bounds).
+__global__ __launch_bounds__(256) void gather_columns_kernel(const uint16_t* __restrict__ A,
+                                                             const int32_t* __restrict__ perm, int64_t M,
+                                                             int64_t K, uint16_t* __restrict__ out) {
+    const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (e >= M * K) return;
+    const int64_t m = e / K, i = e % K;
+    int64_t k = perm[i];
+    k = k < 0 || k >= K ? i : k;
+    out[e] = A[m * K + k];
+}
+
+hipError_t launch_gather_columns(const uint16_t* A, const int32_t* perm, int64_t M, int64_t K, uint16_t* out,
+                                 hipStream_t s) {
+    const int64_t n = M * K;
+    gather_columns_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(A, perm, M, K, out);
+    return hipGetLastError();
 }
 
 hipError_t launch_w4_gemv_simple(const GemmArgs& a, hipStream_t s) {

@@ -7,7 +7,8 @@
 //
 // W4A16 (page "Model quantization - vLLM runtime quantization architecture",
 // section 5): symmetric int4, group of 128 along K, eight codes per int32,
-// fp16 group scales.
+// fp16 group scales; and the variant with per-group zero points and an
+// optional activation order (g_idx) that section 5 (0) and (3) name.
 //
 // These results must be reproducible bit for bit, so every sum that decides
 // a code is fp64 and runs sequentially in ascending column order in a single
@@ -25,6 +26,7 @@ namespace tq {
 constexpr int kFlagNonFinite = 0;
 constexpr int kFlagRange = 1;
 constexpr int kFlagBadCode = 2;
+constexpr int kFlagGroup = 3;
 
 // ------------------------------------------------------------------ scans
 
@@ -216,6 +218,116 @@ __global__ __launch_bounds__(256) void w4_unpack_kernel(const int32_t* __restric
     }
 }
 
+// ------------------------------------------ W4A16, zero points and g_idx
+
+// Packed column order from g_idx: thread g scans the columns in ascending
+// order and places the ones of group g at 128g, 128g + 1, ... (a stable sort
+// by group, every group holding exactly 128 columns).  Any other g_idx sets
+// flags[kFlagGroup].
+__global__ __launch_bounds__(64) void w4a_order_kernel(const int32_t* __restrict__ g_idx, int64_t K,
+                                                       int32_t* __restrict__ perm, int* __restrict__ flags) {
+    const int64_t G = K / 128;
+    const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (g >= G) return;
+    int64_t cnt = 0;
+    bool bad = false;
+    for (int64_t k = 0; k < K; ++k) {
+        const int32_t gk = g_idx[k];
+        if (g == 0 && (gk < 0 || (int64_t)gk >= G)) bad = true;
+        if ((int64_t)gk == g) {
+            if (cnt < 128) perm[128 * g + cnt] = (int32_t)k;
+            ++cnt;
+        }
+    }
+    if (bad || cnt != 128) flags[kFlagGroup] = 1;
+}
+
+// One thread per output word (eight consecutive packed columns, gathered
+// through perm when given); the 16 threads of a group share its minimum and
+// maximum through lane shuffles (exact: order does not matter).  Range
+// [min(0, lo), max(0, hi)], s = fp16((hi - lo) / 15), z = clamp(rint(-lo /
+// s), 0, 15), q = clamp(rint(w / s) + z, 0, 15), all in fp64.
+__global__ __launch_bounds__(256) void w4a_pack_kernel(const float* __restrict__ W, int64_t N, int64_t K,
+                                                       const int32_t* __restrict__ perm,
+                                                       int32_t* __restrict__ qweight,
+                                                       uint16_t* __restrict__ scales,
+                                                       uint8_t* __restrict__ zeros,
+                                                       int* __restrict__ flags) {
+    const int64_t words = N * (K / 8);
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const bool live = i < words;
+    float w[8];
+    float lo = 0.0f, hi = 0.0f;
+    if (live) {
+        const int64_t row = i / (K / 8);
+        const int64_t c0 = (i % (K / 8)) * 8;
+        const float* wr = W + row * K;
+        for (int k = 0; k < 8; ++k) {
+            w[k] = wr[perm ? (int64_t)perm[c0 + k] : c0 + k];
+            lo = fminf(lo, w[k]);
+            hi = fmaxf(hi, w[k]);
+        }
+    } else {
+        for (int k = 0; k < 8; ++k) w[k] = 0.0f;
+    }
+    for (int off = 8; off >= 1; off >>= 1) {
+        lo = fminf(lo, __shfl_xor(lo, off, 16));
+        hi = fmaxf(hi, __shfl_xor(hi, off, 16));
+    }
+    if (!live) return;
+    const uint16_t sb = f64_to_f16_rne(((double)hi - (double)lo) / 15.0);
+    if ((sb & 0x7FFFu) == 0x7C00u) flags[kFlagRange] = 1;
+    const double s = f16_bits_to_f64(sb);
+    int z = 0;
+    if (s != 0.0) {
+        double zz = rint(-(double)lo / s);
+        zz = zz < 0.0 ? 0.0 : (zz > 15.0 ? 15.0 : zz);
+        z = (int)zz;
+    }
+    uint32_t word = 0u;
+    for (int k = 0; k < 8; ++k) {
+        int q = 0;
+        if (s != 0.0) {
+            double qq = rint((double)w[k] / s) + (double)z;  // IEEE divide, round half to even
+            qq = qq < 0.0 ? 0.0 : (qq > 15.0 ? 15.0 : qq);
+            q = (int)qq;
+        }
+        word |= (uint32_t)q << (4 * k);
+    }
+    qweight[i] = (int32_t)word;
+    if ((i & 15) == 0) {  // group index = word index / 16
+        scales[i >> 4] = sb;
+        zeros[i >> 4] = (uint8_t)z;
+    }
+}
+
+// One thread per word: codes in packed order; dequant (q - z) * s is exact in
+// fp32, rounded once to binary16 and stored at the input column perm[i].
+__global__ __launch_bounds__(256) void w4a_unpack_kernel(const int32_t* __restrict__ qweight,
+                                                         const uint16_t* __restrict__ scales,
+                                                         const uint8_t* __restrict__ zeros,
+                                                         const int32_t* __restrict__ perm, int64_t N, int64_t K,
+                                                         uint8_t* __restrict__ q_out,
+                                                         uint16_t* __restrict__ wdq_out) {
+    const int64_t words = N * (K / 8);
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= words) return;
+    const uint32_t word = (uint32_t)qweight[i];
+    const float s = f16_bits_to_f32(scales[i >> 4]);
+    const int z = zeros[i >> 4];
+    const int64_t row = i / (K / 8);
+    const int64_t c0 = (i % (K / 8)) * 8;
+    for (int k = 0; k < 8; ++k) {
+        const uint32_t q = (word >> (4 * k)) & 15u;
+        if (q_out) q_out[8 * i + k] = (uint8_t)q;
+        if (wdq_out) {
+            int64_t col = perm ? (int64_t)perm[c0 + k] : c0 + k;
+            col = col < 0 || col >= K ? c0 + k : col;  // memory-safe for any perm contents
+            wdq_out[row * K + col] = f32_to_f16_rne((float)((int)q - z) * s);
+        }
+    }
+}
+
 // ------------------------------------------------------------- launchers
 
 static int grid_for(int64_t items, int block) {
@@ -253,6 +365,24 @@ hipError_t launch_w4_pack(const float* W, int64_t N, int64_t K, int32_t* qweight
 hipError_t launch_w4_unpack(const int32_t* qweight, const uint16_t* scales, int64_t N, int64_t K,
                             uint8_t* q_out, uint16_t* wdq_out, hipStream_t s) {
     w4_unpack_kernel<<<grid_for(N * (K / 8), 256), 256, 0, s>>>(qweight, scales, N, K, q_out, wdq_out);
+    return hipGetLastError();
+}
+
+hipError_t launch_w4a_order(const int32_t* g_idx, int64_t K, int32_t* perm, int* flags, hipStream_t s) {
+    w4a_order_kernel<<<grid_for(K / 128, 64), 64, 0, s>>>(g_idx, K, perm, flags);
+    return hipGetLastError();
+}
+
+hipError_t launch_w4a_pack(const float* W, int64_t N, int64_t K, const int32_t* perm, int32_t* qweight,
+                           uint16_t* scales, uint8_t* zeros, int* flags, hipStream_t s) {
+    w4a_pack_kernel<<<grid_for(N * (K / 8), 256), 256, 0, s>>>(W, N, K, perm, qweight, scales, zeros, flags);
+    return hipGetLastError();
+}
+
+hipError_t launch_w4a_unpack(const int32_t* qweight, const uint16_t* scales, const uint8_t* zeros,
+                             const int32_t* perm, int64_t N, int64_t K, uint8_t* q_out, uint16_t* wdq_out,
+                             hipStream_t s) {
+    w4a_unpack_kernel<<<grid_for(N * (K / 8), 256), 256, 0, s>>>(qweight, scales, zeros, perm, N, K, q_out, wdq_out);
     return hipGetLastError();
 }
 

@@ -18,6 +18,17 @@ hipError_t launch_w4_pack(const float* W, int64_t N, int64_t K, int32_t* qweight
                           int* flags, hipStream_t s);
 hipError_t launch_w4_unpack(const int32_t* qweight, const uint16_t* scales, int64_t N, int64_t K,
                             uint8_t* q_out, uint16_t* wdq_out, hipStream_t s);
+// W4A16 with zero points and activation order: the packed column order from
+// g_idx (flags[3] on a malformed g_idx), then pack / unpack in that order.
+hipError_t launch_w4a_order(const int32_t* g_idx, int64_t K, int32_t* perm, int* flags, hipStream_t s);
+hipError_t launch_w4a_pack(const float* W, int64_t N, int64_t K, const int32_t* perm, int32_t* qweight,
+                           uint16_t* scales, uint8_t* zeros, int* flags, hipStream_t s);
+hipError_t launch_w4a_unpack(const int32_t* qweight, const uint16_t* scales, const uint8_t* zeros,
+                             const int32_t* perm, int64_t N, int64_t K, uint8_t* q_out, uint16_t* wdq_out,
+                             hipStream_t s);
+// gemv.hip: A_perm[m, i] = A[m, perm[i]] (activation order), fp16/bf16 bits.
+hipError_t launch_gather_columns(const uint16_t* A, const int32_t* perm, int64_t M, int64_t K, uint16_t* out,
+                                 hipStream_t s);
 
 // One bit per device ordinal (0..63): whether a per-function setting has been
 // applied on that device.
@@ -48,6 +59,7 @@ struct GemmArgs {
     const uint16_t* scale;  // ternary [N]; W4 [N, K/128]
     const uint16_t* bias;   // [N] or nullptr
     uint16_t* C;            // [M, N]
+    const uint8_t* zeros = nullptr;  // W4A16 zero points [N, K/128] (nullptr: symmetric, zero point 8)
 };
 
 // A call whose K range is split S ways: split z writes its fp32 partial sums

@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define TQ_ABI_VERSION 3
+#define TQ_ABI_VERSION 4
 
 typedef enum tq_status {
     TQ_OK = 0,
@@ -238,6 +238,76 @@ tq_status w4a16_gemm_ws(const void* A, tq_dtype dt, int64_t M, int64_t N, int64_
  * invalid arguments).
  */
 size_t w4a16_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, tq_dtype dt, int64_t group_size);
+
+/* ----------------------- W4A16 with zero points and activation order (ABI 4)
+ *
+ * The variant the page "Model quantization - vLLM runtime quantization
+ * architecture" names in section 5, steps (0) and (3): a per-group zero
+ * point beside the group scale, and optionally g_idx, the group of each
+ * input column (activation ordering).  The quantizer is asymmetric
+ * min-max over each group's range widened to include 0:
+ *   s = fp16((max(0, hi) - min(0, lo)) / 15), z = clamp(rint(-min(0, lo) / s), 0, 15),
+ *   q = clamp(rint(w / s) + z, 0, 15), dequantized weight (q - z) * s,
+ * in fp64 with round-half-even (a zero scale gives z = 0 and q = 0).
+ */
+
+/*
+ * w4a16_pack_asym - pack W [N, K] fp32 (device) with zero points.
+ *   g_idx      int32 [K] or NULL: input column k belongs to group g_idx[k];
+ *              every group must hold exactly 128 columns (else TQ_ERR_GROUP).
+ *              The packed matrix stores the columns sorted by group, stably
+ *              (ascending column within a group), so groups are contiguous.
+ *   qweight    int32 [N, K/8], nibble i of word j = packed column 8j + i.
+ *   scales_f16 [N, K/128]; zeros uint8 [N, K/128] (values 0..15).
+ *   perm       int32 [K], required with g_idx: packed column i is input
+ *              column perm[i] (not written without g_idx; the order is then
+ *              the identity).
+ * Synchronous.  Errors: TQ_ERR_NULL, TQ_ERR_GROUP (group_size != 128 or a
+ * malformed g_idx), TQ_ERR_SHAPE (K % 128 != 0), TQ_ERR_ALIGN (W, qweight,
+ * g_idx, perm 4-byte aligned; scales 2-byte), TQ_ERR_NONFINITE, TQ_ERR_RANGE.
+ */
+tq_status w4a16_pack_asym(const float* W, int64_t N, int64_t K, int64_t group_size, const int32_t* g_idx,
+                          int32_t* qweight, uint16_t* scales_f16, uint8_t* zeros, int32_t* perm,
+                          hipStream_t stream);
+
+/*
+ * w4a16_unpack_asym - codes q_out [N, K] in packed column order (nullable)
+ * and dequantized weights wdq_f16_out [N, K] in the input column order
+ * (nullable; (q - z) * s rounded once to fp16, placed at column perm[i], or
+ * i without perm).  Synchronous.
+ */
+tq_status w4a16_unpack_asym(const int32_t* qweight, const uint16_t* scales_f16, const uint8_t* zeros,
+                            const int32_t* perm, int64_t N, int64_t K, int64_t group_size, uint8_t* q_out,
+                            uint16_t* wdq_f16_out, hipStream_t stream);
+
+/*
+ * w4a16_gemm_asym - C = A * dequant(qweight, scales, zeros)^T (+ bias), the
+ * packed weights of w4a16_pack_asym.
+ *   zeros  uint8 [N, K/128] or NULL (then the symmetric zero point 8).
+ *   perm   int32 [K] or NULL: with it, A is first gathered into packed
+ *          column order, A[:, perm], at the front of the workspace, which is
+ *          then required: at least w4a16_gemm_asym_workspace_bytes(..., 1)
+ *          bytes for the fastest schedule, never less than the gathered
+ *          activations (M * K * 2 bytes rounded up to 256; TQ_ERR_SHAPE
+ *          otherwise).  perm must be the array the pack wrote; any other
+ *          contents give unspecified results (indices are clamped into
+ *          [0, K), so memory stays in bounds).
+ *   path   TQ_PATH_AUTO or TQ_PATH_GEMV (TQ_ERR_PATH otherwise).
+ * The rest of the workspace serves the split-K schedule of w4a16_gemm_ws.
+ * Asynchronous; allocates nothing; graph-capturable.
+ */
+tq_status w4a16_gemm_asym(const void* A, tq_dtype dt, int64_t M, int64_t N, int64_t K, const int32_t* qweight,
+                          const uint16_t* scales_f16, const uint8_t* zeros, const int32_t* perm, int64_t group_size,
+                          const void* bias, void* C, void* workspace, size_t workspace_bytes, hipStream_t stream,
+                          tq_path path);
+
+/*
+ * w4a16_gemm_asym_workspace_bytes - workspace of w4a16_gemm_asym's fastest
+ * schedule: the gathered activations when with_perm, plus the split-K
+ * partials (0 for invalid arguments).
+ */
+size_t w4a16_gemm_asym_workspace_bytes(int64_t M, int64_t N, int64_t K, tq_dtype dt, int64_t group_size,
+                                       int with_perm);
 
 /* ------------------------------------------------------------------ misc */
 

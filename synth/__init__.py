@@ -15,6 +15,8 @@ Recipe
 * Activations: A[M, K] ~ N(0, 1), drawn in fp64 with
   ``default_rng(seed).standard_normal`` then rounded to fp16 by numpy, or to
   bf16 by torch from the fp32 value.
+* Activation-order groups (``group_index``): a seeded random permutation
+  ranks the input columns and group g takes ranks 128g .. 128g + 127.
 * Seeds: the smallest case (256 x 256, M = 1) uses seed 0 for both, weights
   drawn first.  Every other tensor gets ``seed_for(*names)``, a CRC-32 of its
   name, so a weight matrix is shared by every M it is used with.
@@ -92,6 +94,15 @@ def smallest_case():
     W = rng.normal(0.0, SIGMA, (256, 256)).astype(np.float32)
     a = rng.standard_normal((1, 256))
     return W, _to_torch(a, "f16")
+
+
+def group_index(K: int, seed: int, group: int = 128) -> np.ndarray:
+    """Activation-order group of each input column, int32 [K]: the columns
+    take a seeded random rank (a stand-in for an ordering by importance) and
+    consecutive ranks form the groups, so every group holds ``group``
+    columns scattered over the row."""
+    rank = np.random.default_rng(seed).permutation(K)
+    return (rank // group).astype(np.int32)
 
 
 def weights_device(N: int, K: int, seed: int, device, sigma: float = SIGMA):

@@ -29,7 +29,8 @@ def lib():
 
 def test_header_declares_the_boundary():
     names = _declared_functions()
-    for required in ("tq_pack", "tq_gemm", "w4a16_gemm", "tq_unpack", "w4a16_pack", "w4a16_unpack"):
+    for required in ("tq_pack", "tq_gemm", "w4a16_gemm", "tq_unpack", "w4a16_pack", "w4a16_unpack",
+                     "w4a16_pack_asym", "w4a16_unpack_asym", "w4a16_gemm_asym"):
         assert required in names
 
 
@@ -43,10 +44,23 @@ def test_binding_declares_nothing_extra():
     assert set(_lib.SIGNATURES) == set(_declared_functions())
 
 
+def test_one_hip_runtime_per_process():
+    """Loading the library before anything imports torch still leaves one HIP
+    runtime mapped (the binding loads torch's first)."""
+    import subprocess
+    import sys
+    code = ("from bit_weight_only_tq_amd import _lib; _lib.load(); "
+            "print(sorted({l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}))")
+    out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=300)
+    assert out.returncode == 0, out.stderr
+    paths = eval(out.stdout.strip().splitlines()[-1])
+    assert len(paths) == 1, paths
+
+
 def test_version_and_status_strings(lib):
-    assert lib.tq_abi_version() == 3
+    assert lib.tq_abi_version() == 4
     src = open(HEADER).read()
-    assert "#define TQ_ABI_VERSION 3" in src
+    assert "#define TQ_ABI_VERSION 4" in src
     for code, name in _lib.STATUS_NAMES.items():
         assert re.search(rf"\b{name}\s*=\s*{code}\b", src), name
         s = lib.tq_status_str(code)
@@ -146,6 +160,45 @@ def test_w4a16_gemm_ws_host_checks(lib):
     assert name[st] == "TQ_ERR_PATH"
     st = lib.w4a16_gemm_ws(FAKE, 0, 4, 64, 128, FAKE, FAKE, 64, None, FAKE, None, 0, None, 0)
     assert name[st] == "TQ_ERR_GROUP"
+
+
+def test_w4a16_asym_workspace_query():
+    """With a column order the gathered activations (M * K * 2 bytes, rounded
+    up to 256) come first, then the split partials of the symmetric query."""
+    wb = _lib.w4a16_gemm_asym_workspace_bytes
+    sym = _lib.w4a16_gemm_workspace_bytes
+    assert wb(16, 4096, 14336) == sym(16, 4096, 14336) == 8 * 16 * 4096 * 4
+    assert wb(16, 4096, 14336, with_perm=True) == 16 * 14336 * 2 + 8 * 16 * 4096 * 4
+    assert wb(1, 4096, 4096, with_perm=True) == 8192 and wb(1, 4096, 4096) == 0
+    assert wb(3, 64, 128, "bf16", with_perm=True) == 768                 # 3 * 128 * 2 = 768
+    assert wb(1, 64, 384, with_perm=True) == 768                          # 768 already a multiple of 256
+    assert wb(1, 64, 256, with_perm=True) == 512
+    assert wb(5, 64, 128, with_perm=True) == 1280
+    assert wb(1, 64, 200, with_perm=True) == 0 and wb(1, 64, 256, group_size=64, with_perm=True) == 0
+
+
+def test_w4a16_asym_host_checks(lib):
+    name = _lib.STATUS_NAMES
+    g = lib.w4a16_gemm_asym
+    # act order needs a workspace at least as large as the gathered activations
+    assert name[g(FAKE, 0, 4, 64, 128, FAKE, FAKE, FAKE, FAKE, 128, None, FAKE, None, 0, None, 0)] == "TQ_ERR_SHAPE"
+    assert name[g(FAKE, 0, 4, 64, 128, FAKE, FAKE, FAKE, FAKE, 128, None, FAKE, FAKE, 1023, None, 0)] == "TQ_ERR_SHAPE"
+    assert name[g(FAKE, 0, 4, 64, 128, FAKE, FAKE, None, MIS, 128, None, FAKE, FAKE, 4096, None, 0)] == "TQ_ERR_ALIGN"
+    assert name[g(FAKE, 0, 4, 64, 128, FAKE, FAKE, FAKE, None, 64, None, FAKE, None, 0, None, 0)] == "TQ_ERR_GROUP"
+    assert name[g(FAKE, 0, 4, 64, 192, FAKE, FAKE, FAKE, None, 128, None, FAKE, None, 0, None, 0)] == "TQ_ERR_SHAPE"
+    assert name[g(FAKE, 0, 4, 64, 128, FAKE, FAKE, FAKE, None, 128, None, FAKE, None, 0, None, 2)] == "TQ_ERR_PATH"
+    assert name[g(None, 0, 4, 64, 128, FAKE, FAKE, FAKE, None, 128, None, FAKE, None, 0, None, 0)] == "TQ_ERR_NULL"
+    p = lib.w4a16_pack_asym
+    assert name[p(FAKE, 4, 128, 128, FAKE, FAKE, FAKE, FAKE, None, None)] == "TQ_ERR_NULL"   # g_idx without perm
+    assert name[p(FAKE, 4, 128, 128, None, FAKE, FAKE, None, None, None)] == "TQ_ERR_NULL"   # no zeros
+    assert name[p(FAKE, 4, 128, 64, None, FAKE, FAKE, FAKE, None, None)] == "TQ_ERR_GROUP"
+    assert name[p(FAKE, 4, 100, 128, None, FAKE, FAKE, FAKE, None, None)] == "TQ_ERR_SHAPE"
+    assert name[p(MIS, 4, 128, 128, None, FAKE, FAKE, FAKE, None, None)] == "TQ_ERR_ALIGN"
+    u = lib.w4a16_unpack_asym
+    assert name[u(FAKE, FAKE, None, None, 4, 128, 128, None, None, None)] == "TQ_ERR_NULL"
+    assert name[u(FAKE, FAKE, FAKE, None, 4, 128, 64, None, None, None)] == "TQ_ERR_GROUP"
+    assert name[u(FAKE, FAKE, FAKE, None, 4, 100, 128, None, None, None)] == "TQ_ERR_SHAPE"
+    assert name[u(FAKE, FAKE, FAKE, MIS, 4, 128, 128, None, None, None)] == "TQ_ERR_ALIGN"
 
 
 def test_tq_gemm_ex_bad_path(lib):

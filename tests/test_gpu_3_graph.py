@@ -13,6 +13,7 @@ pytestmark = pytest.mark.gpu
     ("ternary", 512, 1024, 4096), ("ternary", 2048, 14336, 4096),  # large M: split K (two kernels), one pass
     ("ternary", 40, 1024, 4096), ("ternary", 200, 2048, 1024),  # medium path: split K, two kernels
     ("w4a16", 4, 1024, 4096), ("w4a16", 16, 4096, 14336),  # W4: one pass; split K (two kernels)
+    ("w4a16_act", 1, 4096, 4096), ("w4a16_act", 16, 4096, 14336),  # zero points + column order: gather first
 ])
 def test_graph_replay_matches_eager(fmt, M, N, K):
     import torch
@@ -23,9 +24,13 @@ def test_graph_replay_matches_eager(fmt, M, N, K):
     if fmt == "ternary":
         wq, sc = tq.tq_pack(W)
         fn = lambda a, out: tq.tq_gemm(a, wq, sc, out=out)  # noqa: E731
-    else:
+    elif fmt == "w4a16":
         wq, sc = tq.w4a16_pack(W)
         fn = lambda a, out: tq.w4a16_gemm(a, wq, sc, out=out)  # noqa: E731
+    else:
+        gi = torch.from_numpy(synth.group_index(K, synth.seed_for("gg", K))).to(dev)
+        wq, sc, zp, perm = tq.w4a16_pack_asym(W, gi)
+        fn = lambda a, out: tq.w4a16_gemm(a, wq, sc, out=out, zeros=zp, perm=perm)  # noqa: E731
     A = synth.activations(M, K, synth.seed_for("ga", M), "f16").to(dev)
     eager = fn(A, None)
     torch.cuda.synchronize()
