@@ -1362,7 +1362,7 @@ static int64_t w4_stream_cost(const GemmArgs& a, const W4StreamPlan& pl, int64_t
 }
 
 static bool w4_stream_plan(const GemmArgs& a, size_t ws_bytes, W4StreamPlan* pl) {
-    if (a.bf16 || a.M < 3 || a.M > kGemvMaxM || a.K % 128 != 0) return false;
+    if (a.bf16 || a.M < 1 || a.M > kGemvMaxM || a.K % 128 != 0) return false;
     const int64_t cus = compute_units();
     bool found = false;
     int64_t best = 0;
@@ -1380,9 +1380,21 @@ static bool w4_stream_plan(const GemmArgs& a, size_t ws_bytes, W4StreamPlan* pl)
     return found;
 }
 
+// Whether the streaming kernel serves this call, and with which plan.  At
+// M = 1 the per-lane kernel (one wave per row) fills the chip on its own; the
+// streaming kernel wins there only without a K split (whose reduction is a
+// second launch) and with a workgroup for every compute unit, so M = 1 never
+// uses a workspace.  From M = 2 on it wins whenever it has a plan.
+static bool w4_use_stream(const GemmArgs& a, size_t ws_bytes, W4StreamPlan* sp) {
+    if (!w4_stream_plan(a, a.M == 1 ? 0 : ws_bytes, sp)) return false;
+    if (a.M >= 2) return true;
+    const int64_t nrb = (a.N + 15) / 16;
+    return sp->S == 1 && (nrb + sp->t - 1) / sp->t >= compute_units();
+}
+
 size_t w4_gemv_workspace_bytes(const GemmArgs& a) {
     W4StreamPlan pl;
-    if (!w4_stream_plan(a, SIZE_MAX, &pl) || pl.S == 1) return 0;
+    if (a.M == 1 || !w4_stream_plan(a, SIZE_MAX, &pl) || pl.S == 1) return 0;
     return (size_t)pl.S * (size_t)a.M * (size_t)a.N * sizeof(float);
 }
 
@@ -1432,7 +1444,7 @@ hipError_t launch_w4_gemv(const GemmArgs& a, hipStream_t s) { return launch_w4_g
 
 hipError_t launch_w4_gemv(const GemmArgs& a, void* workspace, size_t workspace_bytes, hipStream_t s) {
     W4StreamPlan sp;
-    if (w4_stream_plan(a, workspace ? workspace_bytes : 0, &sp))
+    if (w4_use_stream(a, workspace ? workspace_bytes : 0, &sp))
         return launch_w4_stream_t(SplitArgs{a, static_cast<float*>(workspace), sp.S, 1}, sp, s);
     if (!a.bf16 && a.M >= 3 && a.M <= kGemvMaxM && !a.zeros) {  // zero point 8 only
         const int64_t nrb = (a.N + 15) / 16;

@@ -137,15 +137,16 @@ def test_tq_gemm_ws_host_checks(lib):
 
 
 def test_w4_workspace_query():
-    """W4A16 split-K workspace (fp16, 3 <= M <= 16): S fp32 partials of
-    [M, N] when the plan splits the K groups; none at M < 3, for bf16, or
+    """W4A16 split-K workspace (fp16, 2 <= M <= 16): S fp32 partials of
+    [M, N] when the plan splits the K groups; none at M = 1, for bf16, or
     when one pass over K is cheapest.  Off the GPU the compute-unit count
     defaults to 256."""
     wb = _lib.w4a16_gemm_workspace_bytes
     assert wb(16, 4096, 14336) == 8 * 16 * 4096 * 4       # 112 groups -> 8 splits of 14
     assert wb(16, 57344, 8192) == 4 * 16 * 57344 * 4
     assert wb(16, 28672, 4096) == 0 and wb(16, 4096, 4096) == 0
-    assert wb(1, 4096, 14336) == 0 and wb(2, 4096, 14336) == 0
+    assert wb(1, 4096, 14336) == 0                       # M = 1 never splits
+    assert wb(2, 4096, 14336) == 8 * 2 * 4096 * 4        # M = 2 streams: 112 groups -> 8 splits of 14
     assert wb(16, 4096, 14336, "bf16") == 0
     assert wb(16, 4096, 14336, group_size=64) == 0
     assert wb(40, 4096, 14336) == 8 * 16 * 4096 * 4      # blocks of 16 rows, the largest block's need

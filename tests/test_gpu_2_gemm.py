@@ -293,7 +293,8 @@ def test_w4_ragged_shapes(M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K", [(16, 4096, 14336), (5, 1000, 14336), (12, 8192, 28672), (3, 4100, 8192),
-                                   (16, 28672, 4096), (40, 4096, 14336)])
+                                   (16, 28672, 4096), (40, 4096, 14336), (1, 28672, 4096), (1, 4100, 4096),
+                                   (2, 4096, 14336), (2, 300, 1024)])
 def test_w4_split_k(M, N, K):
     """W4A16 streaming kernel with the K groups split across workgroups
     (workspace from torch) and without a workspace: both within the tolerance

@@ -209,6 +209,7 @@ def test_w4a_order_without_zeros():
 
 @pytest.mark.parametrize("M,N,K", [
     (1, 4096, 14336), (4, 4096, 14336), (16, 4096, 14336), (1, 14336, 4096), (16, 28672, 4096), (40, 1024, 4096),
+    (1, 28672, 4096), (2, 4096, 14336), (2, 6144, 4096),
 ])
 def test_w4a_decode_shapes(M, N, K):
     """Llama-3-8B shapes with activation order: the workspace the query asks
