@@ -500,8 +500,16 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(SplitArgs sa) {
     const float b = p.bias ? T::to_f32(p.bias[n]) : 0.0f;
     for (int64_t m = blockIdx.y; m < p.M; m += gridDim.y) {
         const float* src = sa.ws + m * p.N + n;
+        // eight partials in flight at a time, summed in split order z = 0, 1, ...
         float s = 0.0f;
-        for (int z = 0; z < sa.S; ++z) s += src[z * MN];
+        for (int z0 = 0; z0 < sa.S; z0 += 8) {
+            float v[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[j] = z0 + j < sa.S ? src[(int64_t)(z0 + j) * MN] : 0.0f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (z0 + j < sa.S) s += v[j];
+        }
         p.C[m * p.N + n] = T::from_f32_fast(s * sc + b);
     }
 }

@@ -220,26 +220,45 @@ __global__ __launch_bounds__(256) void w4_unpack_kernel(const int32_t* __restric
 
 // ------------------------------------------ W4A16, zero points and g_idx
 
-// Packed column order from g_idx: thread g scans the columns in ascending
-// order and places the ones of group g at 128g, 128g + 1, ... (a stable sort
-// by group, every group holding exactly 128 columns).  Any other g_idx sets
-// flags[kFlagGroup].
-__global__ __launch_bounds__(64) void w4a_order_kernel(const int32_t* __restrict__ g_idx, int64_t K,
-                                                       int32_t* __restrict__ perm, int* __restrict__ flags) {
+// Packed column order from g_idx: workgroup g places the columns of group g
+// at 128g, 128g + 1, ... in ascending column order (a stable sort by group).
+// Thread t counts the matches in its contiguous segment of the columns, an
+// exclusive prefix sum over the threads gives each segment's first slot, and
+// a second pass writes the columns.  Any other g_idx (an index out of range,
+// a group without exactly 128 columns) sets flags[kFlagGroup]; slots past
+// 128 are never written.
+__global__ __launch_bounds__(256) void w4a_order_kernel(const int32_t* __restrict__ g_idx, int64_t K,
+                                                        int32_t* __restrict__ perm, int* __restrict__ flags) {
+    __shared__ int scan[256];
     const int64_t G = K / 128;
-    const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (g >= G) return;
-    int64_t cnt = 0;
+    const int64_t g = blockIdx.x;
+    const int t = threadIdx.x;
+    const int64_t seg = (K + 255) / 256;
+    const int64_t k0 = t * seg < K ? t * seg : K;
+    const int64_t k1 = k0 + seg < K ? k0 + seg : K;
+    int c = 0;
     bool bad = false;
-    for (int64_t k = 0; k < K; ++k) {
+    for (int64_t k = k0; k < k1; ++k) {
         const int32_t gk = g_idx[k];
-        if (g == 0 && (gk < 0 || (int64_t)gk >= G)) bad = true;
-        if ((int64_t)gk == g) {
-            if (cnt < 128) perm[128 * g + cnt] = (int32_t)k;
-            ++cnt;
+        bad |= gk < 0 || (int64_t)gk >= G;
+        c += (int64_t)gk == g;
+    }
+    scan[t] = c;
+    __syncthreads();
+    for (int d = 1; d < 256; d <<= 1) {  // inclusive Hillis-Steele scan
+        const int v = t >= d ? scan[t - d] : 0;
+        __syncthreads();
+        scan[t] += v;
+        __syncthreads();
+    }
+    int slot = scan[t] - c;
+    for (int64_t k = k0; k < k1; ++k) {
+        if ((int64_t)g_idx[k] == g) {
+            if (slot < 128) perm[128 * g + slot] = (int32_t)k;
+            ++slot;
         }
     }
-    if (bad || cnt != 128) flags[kFlagGroup] = 1;
+    if (bad || (t == 255 && scan[255] != 128)) flags[kFlagGroup] = 1;
 }
 
 // One thread per output word (eight consecutive packed columns, gathered
@@ -369,7 +388,7 @@ hipError_t launch_w4_unpack(const int32_t* qweight, const uint16_t* scales, int6
 }
 
 hipError_t launch_w4a_order(const int32_t* g_idx, int64_t K, int32_t* perm, int* flags, hipStream_t s) {
-    w4a_order_kernel<<<grid_for(K / 128, 64), 64, 0, s>>>(g_idx, K, perm, flags);
+    w4a_order_kernel<<<(unsigned)(K / 128), 256, 0, s>>>(g_idx, K, perm, flags);
     return hipGetLastError();
 }
 
