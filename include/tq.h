@@ -174,8 +174,9 @@ tq_status tq_gemm_ex(const void* A, tq_dtype dt, int64_t M, int64_t N, int64_t K
  *                    `stream` is done.  Calls that may overlap must use
  *                    different workspaces.
  *   workspace_bytes  at least tq_gemm_workspace_bytes(M, N, K, dt, path)
- *                    for the split-K schedule of TQ_PATH_STREAM_MFMA and
- *                    TQ_PATH_GEMM; with less (or NULL) those paths run one
+ *                    for the split-K schedule of the decode kernels
+ *                    (3 <= M <= 16, long K), TQ_PATH_STREAM_MFMA and
+ *                    TQ_PATH_GEMM; with less (or NULL) they run one
  *                    workgroup per output tile over all of K - correct,
  *                    slower when the output tiles leave compute units idle.
  *   path             TQ_PATH_AUTO or a forced kernel family (TQ_ERR_PATH if
