@@ -65,7 +65,7 @@ __global__ __launch_bounds__(kGemvWaves * kWave) void ternary_gemv_kernel(GemmAr
     for (int m = 0; m < MT; ++m) {
         if (m < p.M) {
             const float v = wave_sum(acc[m]);
-            if (lane == 0) p.C[m * p.N + row] = T::from_f32(v * s + b);
+            if (lane == 0) p.C[m * p.N + row] = T::from_f32_fast(v * s + b);
         }
     }
 }
@@ -118,7 +118,7 @@ __global__ __launch_bounds__(kGemvWaves * kWave) void w4_gemv_kernel(GemmArgs p)
     for (int m = 0; m < MT; ++m) {
         if (m < p.M) {
             const float v = wave_sum(acc[m]);
-            if (lane == 0) p.C[m * p.N + row] = T::from_f32(v + b);
+            if (lane == 0) p.C[m * p.N + row] = T::from_f32_fast(v + b);
         }
     }
 }
@@ -254,7 +254,7 @@ __global__ __launch_bounds__(W * kWave) void ternary_gemv_mfma_kernel(GemmArgs p
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int m = 4 * (l >> 4) + i;
-            if (m < M) p.C[(int64_t)m * N + n] = F16::from_f32(s[i] * sc + b);
+            if (m < M) p.C[(int64_t)m * N + n] = F16::from_f32_fast(s[i] * sc + b);
         }
     }
 }
@@ -467,7 +467,7 @@ __global__ __launch_bounds__(1024) void ternary_gemv_lds_kernel(GemmArgs p) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int m = 4 * (l >> 4) + i;
-                if (m < M) p.C[(int64_t)m * N + n] = F16::from_f32(sum[i] * sc_e + bi_e);
+                if (m < M) p.C[(int64_t)m * N + n] = F16::from_f32_fast(sum[i] * sc_e + bi_e);
             }
         }
     }
@@ -678,7 +678,7 @@ __global__ __launch_bounds__(1024) void ternary_gemv_stream_kernel(SplitArgs sa)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int m = 4 * (l >> 4) + i;
-                if (m < M) p.C[(int64_t)m * N + n] = F16::from_f32(sum[i] * sc_e + bi_e);
+                if (m < M) p.C[(int64_t)m * N + n] = F16::from_f32_fast(sum[i] * sc_e + bi_e);
             }
         }
     }
@@ -815,7 +815,7 @@ __global__ __launch_bounds__(W * kWave) void w4_gemv_mfma_kernel(GemmArgs p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int m = 4 * (l >> 4) + i;
-            if (m < M) p.C[(int64_t)m * N + n] = F16::from_f32(sum[i] + b);
+            if (m < M) p.C[(int64_t)m * N + n] = F16::from_f32_fast(sum[i] + b);
         }
     }
 }
@@ -1039,7 +1039,7 @@ __global__ __launch_bounds__(1024) void w4_gemv_stream_kernel(SplitArgs sa) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int m = 4 * (l >> 4) + i;
-                if (m < M) p.C[(int64_t)m * N + n] = F16::from_f32(sum[i] + b);
+                if (m < M) p.C[(int64_t)m * N + n] = F16::from_f32_fast(sum[i] + b);
             }
         }
     }

@@ -114,8 +114,9 @@ __device__ __forceinline__ uint4 opaque_uint4() {
 // Activation element type tags.
 // from_f32 rounds in software (mode-independent); from_f32_fast uses the
 // hardware conversion, which rounds to nearest even under the default mode
-// register and keeps fp16 subnormals - used where a result only has to meet
-// a tolerance.
+// register and keeps fp16 subnormals.  The output stores use the latter:
+// the software rounding cost about 15 instructions per value in epilogues
+// that one wave runs while the others wait.
 struct F16 {
     static __device__ __forceinline__ float to_f32(uint16_t h) { return f16_bits_to_f32(h); }
     static __device__ __forceinline__ uint16_t from_f32(float x) { return f32_to_f16_rne(x); }
