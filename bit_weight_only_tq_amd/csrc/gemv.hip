@@ -473,6 +473,135 @@ __global__ __launch_bounds__(1024) void ternary_gemv_lds_kernel(GemmArgs p) {
     }
 }
 
+// M = 1 form of the kernel above (fp16, K a multiple of 256 CSW, N a
+// multiple of 16 R, W = K / (256 CSW) waves).  With one activation row:
+// * unit c (16 columns) of a wave's a' area is 32 contiguous bytes at 32 c,
+//   and only lanes 16g (row 0 of the matrix-core operand) read it back;
+// * the constant term D of a wave is a single number, subtracted from its
+//   partials before the cross-wave sum;
+// * every global address is a wave-uniform base plus a 32-bit lane offset
+//   and a compile-time displacement, and no count depends on M at run time.
+// The bias is read from a valid address whether or not one is given, so the
+// load needs no branch (a branch there makes the compiler wait for every
+// outstanding load, codes included, before it).
+template <int R, int CSW>
+__global__ __launch_bounds__(1024) void ternary_gemv_m1_kernel(GemmArgs p) {
+    extern __shared__ uint4 smem[];
+    constexpr int U = CSW / 4;  // 16-column activation units per lane
+    uint8_t* lds = reinterpret_cast<uint8_t*>(smem);
+    const int W = blockDim.x >> 6;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const int g = lane >> 4;
+    const int i16 = lane & 15;
+    const uint32_t rb = (uint32_t)(p.K / 4);
+    const int64_t n_base = (int64_t)blockIdx.x * (16 * R);
+    const int cs0 = wave * CSW;
+    uint8_t* aps = lds + wave * (CSW * 512);                              // this wave's a'
+    float* red = reinterpret_cast<float*>(lds + W * (CSW * 512));       // [W][R][16]
+
+    // 1. loads in the order they are consumed: activations, row scale and
+    //    bias of the output this thread may finish, then all codes
+    const uint8_t* abase = reinterpret_cast<const uint8_t*>(p.A) + (int64_t)cs0 * 512;
+    uint4 av[U][8];
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+        const uint8_t* src = abase + 2048 * j + (uint64_t)(uint32_t)(32 * lane);
+        av[j][0] = *reinterpret_cast<const uint4*>(src);
+        av[j][1] = *reinterpret_cast<const uint4*>(src + 16);
+    }
+    const int64_t n_e = n_base + (threadIdx.x & (16 * R - 1));
+    const uint16_t* bsrc = p.bias ? p.bias : p.scale;
+    const uint16_t sc_bits = p.scale[n_e];
+    const uint16_t bi_bits = bsrc[n_e];
+    const uint8_t* cbase = static_cast<const uint8_t*>(p.wq) + n_base * rb + (int64_t)cs0 * 64;
+    const uint32_t lo = (uint32_t)i16 * rb + 16u * (uint32_t)g;
+    uint4 q[CSW][R];
+#pragma unroll
+    for (int s = 0; s < CSW; ++s) {
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            q[s][r] = *reinterpret_cast<const uint4*>(cbase + (int64_t)r * 16 * rb + 64 * s + (uint64_t)lo);
+    }
+
+    // 2. a' of this wave's columns to LDS, and the wave's D
+    float dp = 0.0f;
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+        const uint4 w0 = make_uint4(a_pair<0, 0>(av[j]), a_pair<0, 1>(av[j]), a_pair<0, 2>(av[j]), a_pair<0, 3>(av[j]));
+        const uint4 w1 = make_uint4(a_pair<0, 4>(av[j]), a_pair<0, 5>(av[j]), a_pair<0, 6>(av[j]), a_pair<0, 7>(av[j]));
+        dp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w0.x), __builtin_bit_cast(f16x2, one_pattern<0>()), dp, false);
+        dp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w0.y), __builtin_bit_cast(f16x2, one_pattern<1>()), dp, false);
+        dp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w0.z), __builtin_bit_cast(f16x2, one_pattern<2>()), dp, false);
+        dp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w0.w), __builtin_bit_cast(f16x2, one_pattern<3>()), dp, false);
+        dp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w1.x), __builtin_bit_cast(f16x2, one_pattern<4>()), dp, false);
+        dp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w1.y), __builtin_bit_cast(f16x2, one_pattern<5>()), dp, false);
+        dp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w1.z), __builtin_bit_cast(f16x2, one_pattern<6>()), dp, false);
+        dp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w1.w), __builtin_bit_cast(f16x2, one_pattern<7>()), dp, false);
+        uint4* dst = reinterpret_cast<uint4*>(aps + 32 * (lane + 64 * j));
+        dst[0] = w0;
+        dst[1] = w1;
+    }
+    dp = row16_sum(dp);
+    const float dw = (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(dp), 0)) +
+                      __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dp), 16))) +
+                     (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(dp), 32)) +
+                      __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dp), 48)));
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's LDS writes are complete
+
+    // 3. contract; lanes 16g read the operand's row 0, the others keep an
+    //    arbitrary value (their output rows are never stored)
+    f32x4 acc[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const uint32_t magic_v = vgpr_const<kMagic2>();
+#pragma unroll
+    for (int s = 0; s < CSW; ++s) {
+        uint4 aw[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) aw[e] = opaque_uint4();
+        if (i16 == 0) {
+            const uint4* arow = reinterpret_cast<const uint4*>(aps + (4 * s + g) * 128);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) aw[e] = arow[e];
+        }
+#define TQ_MFMA_1(D, I0)                                                                              \
+    {                                                                                                 \
+        const f16x8 aop = __builtin_bit_cast(f16x8, aw[2 * (D) + (I0) / 4]);                          \
+        _Pragma("unroll") for (int r = 0; r < R; ++r) {                                               \
+            const uint32_t x = dword_of(q[s][r], D);                                                  \
+            const uint32_t y = x >> 10;                                                               \
+            const uint4 bw = make_uint4(field_pair<I0>(x, y, magic_v), field_pair<I0 + 1>(x, y, magic_v), \
+                                        field_pair<I0 + 2>(x, y, magic_v), field_pair<I0 + 3>(x, y, magic_v)); \
+            acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, __builtin_bit_cast(f16x8, bw), acc[r], 0, 0, 0); \
+        }                                                                                             \
+    }
+        TQ_MFMA_1(0, 0)
+        TQ_MFMA_1(0, 4)
+        TQ_MFMA_1(1, 0)
+        TQ_MFMA_1(1, 4)
+        TQ_MFMA_1(2, 0)
+        TQ_MFMA_1(2, 4)
+        TQ_MFMA_1(3, 0)
+        TQ_MFMA_1(3, 4)
+#undef TQ_MFMA_1
+    }
+
+    // 4. row 0 of each wave's partials (D removed) -> LDS; fixed-order sum
+    if (g == 0) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) red[(wave * R + r) * 16 + i16] = acc[r][0] - dw;
+    }
+    __syncthreads();
+    if ((int)threadIdx.x < 16 * R) {
+        const int t = (int)threadIdx.x;
+        float sum = red[t];
+        for (int w = 1; w < W; ++w) sum += red[w * (16 * R) + t];
+        const float bi = p.bias ? F16::to_f32(bi_bits) : 0.0f;
+        p.C[n_e] = F16::from_f32_fast(sum * f16_bits_to_f32(sc_bits) + bi);
+    }
+}
+
 // Same arithmetic, streaming schedule (fp16, M <= 16, K / 256 <= 16 CSW).
 //
 // One workgroup per compute unit walks T consecutive 16-row blocks.  Wave w
@@ -1120,6 +1249,40 @@ static hipError_t launch_gemv_lds_upt(const GemmArgs& a, const GemvPlan& pl, hip
     }
 }
 
+// Shape rule for the M = 1 kernel: CSW = 4 chunk-sets per wave (8 when that
+// would need more than 16 waves), every wave a full share of K, at least 4
+// waves; two 16-row blocks per workgroup on the same very tall matrices as
+// the LDS kernel.  Anything else runs the LDS kernel.
+struct GemvM1Plan {
+    int csw, waves, rows16;
+    size_t lds;
+};
+
+static bool gemv_m1_plan(const GemmArgs& a, GemvM1Plan* pl) {
+    if (a.bf16 || a.M != 1 || a.K % 1024 != 0 || a.N % 16 != 0) return false;
+    const int64_t cs = a.K / 256;
+    const int c = cs > 64 ? 8 : 4;
+    if (cs % c != 0 || cs / c < 4 || cs / c > 16) return false;
+    pl->csw = c;
+    pl->waves = (int)(cs / c);
+    const int64_t nrb = a.N / 16;
+    pl->rows16 = (c == 4 && nrb >= 3072 && nrb % 2 == 0) ? 2 : 1;
+    pl->lds = (size_t)pl->waves * c * 512 + (size_t)pl->waves * pl->rows16 * 64;
+    return pl->lds <= (size_t)kGemvLdsMaxBytes;
+}
+
+template <int R, int CSW>
+static hipError_t launch_gemv_m1(const GemmArgs& a, const GemvM1Plan& pl, hipStream_t s) {
+    static DeviceFlags lds_limit_set;
+    hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(&ternary_gemv_m1_kernel<R, CSW>),
+                                   kGemvLdsMaxBytes, lds_limit_set);
+    if (e != hipSuccess) return e;
+    if (a.N % (16 * R) != 0 || a.K != (int64_t)pl.waves * CSW * 256) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)(a.N / (16 * R)));
+    ternary_gemv_m1_kernel<R, CSW><<<grid, dim3(pl.waves * kWave), pl.lds, s>>>(a);
+    return hipGetLastError();
+}
+
 // Streaming kernel: fp16, 3 <= M <= 16, at most 32 chunk-sets (8192
 // columns) per workgroup (one or two per wave, at most 16 waves); for M <= 2
 // the LDS kernel is faster, its per-wave activation prep being cheaper than
@@ -1252,6 +1415,11 @@ hipError_t launch_ternary_gemv(const GemmArgs& a, void* workspace, size_t worksp
     StreamPlan sp;
     if (gemv_stream_plan(a, workspace ? workspace_bytes : 0, &sp))
         return launch_gemv_stream_t(SplitArgs{a, static_cast<float*>(workspace), sp.S}, sp, s);
+    GemvM1Plan m1;
+    if (gemv_m1_plan(a, &m1)) {
+        if (m1.csw == 8) return launch_gemv_m1<1, 8>(a, m1, s);
+        return m1.rows16 == 2 ? launch_gemv_m1<2, 4>(a, m1, s) : launch_gemv_m1<1, 4>(a, m1, s);
+    }
     GemvPlan pl;
     if (gemv_lds_plan(a, &pl)) {
         if (pl.rows16 == 2) {

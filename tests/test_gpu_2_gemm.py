@@ -87,6 +87,34 @@ def test_w4_decode(N, K, M):
     check_close(C, A, wdq, label=f"w4 {N}x{K} M={M}")
 
 
+# Shapes of the M = 1 decode kernel: 4 waves of 4 chunk-sets, 14 waves of 4,
+# 14 waves of 8, and two 16-row blocks per workgroup (from 3072 row-blocks).
+M1_SHAPES = [(320, 4096), (4096, 14336), (1024, 28672), (49152, 4096)]
+
+
+@pytest.mark.parametrize("N,K", M1_SHAPES)
+def test_m1_one_hot_and_bias(N, K):
+    """The M = 1 decode kernel: a one-hot row e_k gives C[0, n] = wdq[n, k]
+    bit for bit, for columns k in the first and last chunk of several waves
+    and at every code-field position; a dense row with a bias is within the
+    tolerance."""
+    import torch
+    import bit_weight_only_tq_amd as tq
+    dev = require_gpu()
+    log(f"M=1 kernel one-hot and bias N={N} K={K}")
+    codes, scale, rc, rs, wdq = _ternary(N, K, dev)
+    ks = sorted({0, 5, 9, 14, 255, 256 + 77, 1023, 1024 + 130, 2048 + 3, K // 2 + 31, K - 257, K - 8, K - 1})
+    for k in ks:
+        A = torch.zeros((1, K), dtype=torch.float16)
+        A[0, k] = 1.0
+        C = tq.tq_gemm(A.to(dev), codes, scale, path="gemv")
+        np.testing.assert_array_equal(bits16(C)[0], OR.f16_bits(wdq[:, k]), err_msg=f"k={k}")
+    A = synth.activations(1, K, synth.seed_for("m1", N, K), "f16")
+    bias = synth.activations(1, N, synth.seed_for("m1b", N, K), "f16")[0]
+    C = tq.tq_gemm(A.to(dev), codes, scale, bias=bias.to(dev))
+    check_close(C, A, wdq, bias=bias, label=f"M=1 kernel {N}x{K} with bias")
+
+
 @pytest.mark.parametrize("N,K", [(14336, 4096), (4096, 14336)])
 @pytest.mark.parametrize("dt", ["bf16", "f16"])
 def test_ternary_prefill_full(N, K, dt):
