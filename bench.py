@@ -570,7 +570,7 @@ def main():
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-            "kernel": "ternary_gemv_lds_kernel", "avg_launch_us": round(d["avg_launch_us"], 3),
+            "kernel": "ternary_gemv_m1_kernel", "avg_launch_us": round(d["avg_launch_us"], 3),
             "alg_bytes_per_launch": round(d["alg_bytes_per_launch"]),
         },
     }

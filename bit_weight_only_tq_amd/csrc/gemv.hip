@@ -1258,6 +1258,11 @@ struct GemvM1Plan {
     size_t lds;
 };
 
+#ifndef TQ_M1_R2_MIN
+#define TQ_M1_R2_MIN 3072
+#endif
+constexpr int64_t kM1TwoBlockRows16 = TQ_M1_R2_MIN;  // 16-row blocks from which R = 2
+
 static bool gemv_m1_plan(const GemmArgs& a, GemvM1Plan* pl) {
     if (a.bf16 || a.M != 1 || a.K % 1024 != 0 || a.N % 16 != 0) return false;
     const int64_t cs = a.K / 256;
@@ -1266,7 +1271,7 @@ static bool gemv_m1_plan(const GemmArgs& a, GemvM1Plan* pl) {
     pl->csw = c;
     pl->waves = (int)(cs / c);
     const int64_t nrb = a.N / 16;
-    pl->rows16 = (c == 4 && nrb >= 3072 && nrb % 2 == 0) ? 2 : 1;
+    pl->rows16 = (c == 4 && nrb >= kM1TwoBlockRows16 && nrb % 2 == 0) ? 2 : 1;
     pl->lds = (size_t)pl->waves * c * 512 + (size_t)pl->waves * pl->rows16 * 64;
     return pl->lds <= (size_t)kGemvLdsMaxBytes;
 }
