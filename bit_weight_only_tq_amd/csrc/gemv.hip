@@ -1291,10 +1291,10 @@ static hipError_t launch_gemv_m1(const GemmArgs& a, const GemvM1Plan& pl, hipStr
 // Streaming kernel: fp16, 3 <= M <= 16, at most 32 chunk-sets (8192
 // columns) per workgroup (one or two per wave, at most 16 waves); for M <= 2
 // the LDS kernel is faster, its per-wave activation prep being cheaper than
-// building the operand in every wave.  T row-blocks per workgroup: the fewest
-// that keep the grid within one workgroup per compute unit (at most 8; at most
-// 4 with two chunk-sets per wave, for registers; at most the wave count, which
-// the final reduction needs).  The waves' LDS areas must fit the compute
+// building the operand in every wave.  T row-blocks per workgroup: the
+// fewest (any count from 1) that keep the grid within one workgroup per
+// compute unit (at most 8; at most 4 with two chunk-sets per wave, for
+// registers; at most the wave count, which the final reduction needs).  The waves' LDS areas must fit the compute
 // unit's LDS, which rules out two chunk-sets per wave for M > 8.  S splits of
 // K when a workspace allows.
 struct StreamPlan {
@@ -1315,6 +1315,18 @@ int compute_units() {
 
 // Geometry of the streaming kernel with K split S ways (false if it does not
 // fit: S must divide the chunk-sets, a split keeps at least four).
+// Row-blocks per workgroup for the streaming kernels: the fewest that keep
+// the grid (S splits) within one workgroup per compute unit, at most tmax
+// (registers) and at most the wave count (the final reduction).  Any count
+// from 1 to tmax is instantiated, so that e.g. 1792 row-blocks take 7 per
+// workgroup and fill 256 compute units instead of 224 with 8.
+static int stream_rows_per_wg(int64_t nrb, int S, int64_t cus, int tmax, int waves) {
+    const int cap = tmax < waves ? tmax : waves;
+    int t = 1;
+    while (t < cap && (nrb + t - 1) / t * S > cus) ++t;
+    return t;
+}
+
 static bool stream_geometry(const GemmArgs& a, int S, int64_t cus, StreamPlan* pl) {
     const int64_t cs_all = a.K / 256;
     if (S < 1 || cs_all % S != 0) return false;
@@ -1325,11 +1337,8 @@ static bool stream_geometry(const GemmArgs& a, int S, int64_t cus, StreamPlan* p
     pl->waves = (int)((cs + pl->csw - 1) / pl->csw);
     const int64_t nrb = (a.N + 15) / 16;
     pl->mr = a.M <= 4 ? 4 : a.M <= 8 ? 8 : 16;
-    const int tmax = pl->csw == 1 ? 8 : 4;
-    int t = 1;
-    while (t < tmax && 2 * t <= pl->waves && (nrb + t - 1) / t * S > cus) t *= 2;
-    pl->t = t;
-    pl->lds = (size_t)pl->waves * stream_wave_lds(pl->csw, pl->mr, t);
+    pl->t = stream_rows_per_wg(nrb, S, cus, pl->csw == 1 ? 8 : 4, pl->waves);
+    pl->lds = (size_t)pl->waves * stream_wave_lds(pl->csw, pl->mr, pl->t);
     return pl->lds <= (size_t)kGemvLdsMaxBytes;
 }
 
@@ -1393,7 +1402,11 @@ static hipError_t launch_gemv_stream_mr(const SplitArgs& sa, const StreamPlan& s
         switch (sp.t) {
             case 1: return launch_gemv_stream<1, 1, MR>(sa, sp, s);
             case 2: return launch_gemv_stream<1, 2, MR>(sa, sp, s);
+            case 3: return launch_gemv_stream<1, 3, MR>(sa, sp, s);
             case 4: return launch_gemv_stream<1, 4, MR>(sa, sp, s);
+            case 5: return launch_gemv_stream<1, 5, MR>(sa, sp, s);
+            case 6: return launch_gemv_stream<1, 6, MR>(sa, sp, s);
+            case 7: return launch_gemv_stream<1, 7, MR>(sa, sp, s);
             default: return launch_gemv_stream<1, 8, MR>(sa, sp, s);
         }
     }
@@ -1403,6 +1416,7 @@ static hipError_t launch_gemv_stream_mr(const SplitArgs& sa, const StreamPlan& s
         switch (sp.t) {
             case 1: return launch_gemv_stream<2, 1, MR>(sa, sp, s);
             case 2: return launch_gemv_stream<2, 2, MR>(sa, sp, s);
+            case 3: return launch_gemv_stream<2, 3, MR>(sa, sp, s);
             default: return launch_gemv_stream<2, 4, MR>(sa, sp, s);
         }
     }
@@ -1518,11 +1532,8 @@ static bool w4_stream_geometry(const GemmArgs& a, int S, int64_t cus, W4StreamPl
     pl->waves = (int)((gs + pl->gsw - 1) / pl->gsw);
     pl->mr = a.M <= 4 ? 4 : a.M <= 8 ? 8 : 16;
     const int64_t nrb = (a.N + 15) / 16;
-    const int tmax = pl->gsw == 1 ? 8 : 4;
-    int t = 1;
-    while (t < tmax && 2 * t <= pl->waves && (nrb + t - 1) / t * S > cus) t *= 2;
-    pl->t = t;
-    pl->lds = (size_t)pl->waves * w4_stream_wave_lds(pl->gsw, pl->mr, t);
+    pl->t = stream_rows_per_wg(nrb, S, cus, pl->gsw == 1 ? 8 : 4, pl->waves);
+    pl->lds = (size_t)pl->waves * w4_stream_wave_lds(pl->gsw, pl->mr, pl->t);
     return pl->lds <= (size_t)kGemvLdsMaxBytes;
 }
 
@@ -1596,13 +1607,18 @@ static hipError_t launch_w4_stream_mr(const SplitArgs& sa, const W4StreamPlan& p
         switch (pl.t) {
             case 1: return launch_w4_stream<1, 1, MR>(sa, pl, s);
             case 2: return launch_w4_stream<1, 2, MR>(sa, pl, s);
+            case 3: return launch_w4_stream<1, 3, MR>(sa, pl, s);
             case 4: return launch_w4_stream<1, 4, MR>(sa, pl, s);
+            case 5: return launch_w4_stream<1, 5, MR>(sa, pl, s);
+            case 6: return launch_w4_stream<1, 6, MR>(sa, pl, s);
+            case 7: return launch_w4_stream<1, 7, MR>(sa, pl, s);
             default: return launch_w4_stream<1, 8, MR>(sa, pl, s);
         }
     }
     switch (pl.t) {
         case 1: return launch_w4_stream<2, 1, MR>(sa, pl, s);
         case 2: return launch_w4_stream<2, 2, MR>(sa, pl, s);
+        case 3: return launch_w4_stream<2, 3, MR>(sa, pl, s);
         default: return launch_w4_stream<2, 4, MR>(sa, pl, s);
     }
 }

@@ -115,6 +115,30 @@ def test_m1_one_hot_and_bias(N, K):
     check_close(C, A, wdq, bias=bias, label=f"M=1 kernel {N}x{K} with bias")
 
 
+# Streaming decode kernels with 3, 5, 6 and 7 row-blocks per workgroup: the
+# fewest that put at most one workgroup on each of 256 compute units
+# (768, 1280, 1536 and 1792 row-blocks of 16 at K = 4096, no K split).
+STREAM_T_SHAPES = [(12288, 4096), (20480, 4096), (24576, 4096), (28672, 4096)]
+
+
+@pytest.mark.parametrize("N,K", STREAM_T_SHAPES)
+@pytest.mark.parametrize("M", [4, 16])
+@pytest.mark.parametrize("fmt", ["ternary", "w4"])
+def test_stream_row_blocks(N, K, M, fmt):
+    import bit_weight_only_tq_amd as tq
+    dev = require_gpu()
+    log(f"stream row-blocks {fmt} N={N} K={K} M={M}")
+    A = synth.activations(M, K, synth.seed_for("st", fmt, N, K, M), "f16")
+    bias = synth.activations(1, N, synth.seed_for("stb", fmt, N, K), "f16")[0]
+    if fmt == "ternary":
+        codes, scale, rc, rs, wdq = _ternary(N, K, dev)
+        C = tq.tq_gemm(A.to(dev), codes, scale, bias=bias.to(dev))
+    else:
+        q, s, rq, rs, wdq = _w4(N, K, dev)
+        C = tq.w4a16_gemm(A.to(dev), q, s, bias=bias.to(dev))
+    check_close(C, A, wdq, bias=bias, label=f"stream {fmt} {N}x{K} M={M}")
+
+
 @pytest.mark.parametrize("N,K", [(14336, 4096), (4096, 14336)])
 @pytest.mark.parametrize("dt", ["bf16", "f16"])
 def test_ternary_prefill_full(N, K, dt):
