@@ -1252,7 +1252,8 @@ static hipError_t launch_gemv_lds_upt(const GemmArgs& a, const GemvPlan& pl, hip
 // Shape rule for the M = 1 kernel: CSW = 4 chunk-sets per wave (8 when that
 // would need more than 16 waves), every wave a full share of K, at least 4
 // waves; two 16-row blocks per workgroup on the same very tall matrices as
-// the LDS kernel.  Anything else runs the LDS kernel.
+// the LDS kernel, and with CSW = 8 once that still fills the compute units.
+// Anything else runs the LDS kernel.
 struct GemvM1Plan {
     int csw, waves, rows16;
     size_t lds;
@@ -1272,6 +1273,10 @@ static bool gemv_m1_plan(const GemmArgs& a, GemvM1Plan* pl) {
     pl->waves = (int)(cs / c);
     const int64_t nrb = a.N / 16;
     pl->rows16 = (c == 4 && nrb >= kM1TwoBlockRows16 && nrb % 2 == 0) ? 2 : 1;
+    // Eight chunk-sets per wave take 78 VGPRs (6 waves per SIMD), so only one
+    // 14-wave workgroup fits a compute unit; with two row-blocks each, one
+    // round of workgroups covers the grid when it has at least 2 per CU.
+    if (c == 8 && nrb % 2 == 0 && nrb >= 2 * (int64_t)compute_units()) pl->rows16 = 2;
     pl->lds = (size_t)pl->waves * c * 512 + (size_t)pl->waves * pl->rows16 * 64;
     return pl->lds <= (size_t)kGemvLdsMaxBytes;
 }
@@ -1436,6 +1441,7 @@ hipError_t launch_ternary_gemv(const GemmArgs& a, void* workspace, size_t worksp
         return launch_gemv_stream_t(SplitArgs{a, static_cast<float*>(workspace), sp.S}, sp, s);
     GemvM1Plan m1;
     if (gemv_m1_plan(a, &m1)) {
+        if (m1.csw == 8 && m1.rows16 == 2) return launch_gemv_m1<2, 8>(a, m1, s);
         if (m1.csw == 8) return launch_gemv_m1<1, 8>(a, m1, s);
         return m1.rows16 == 2 ? launch_gemv_m1<2, 4>(a, m1, s) : launch_gemv_m1<1, 4>(a, m1, s);
     }

@@ -68,3 +68,22 @@ def test_ternary_70b_fused(N, K, M):
     A = synth.activations(M, K, synth.seed_for("a70bf", N, K, M), "f16")
     C = tq.tq_gemm(A.to(dev), codes, scale)
     check_close(C.index_select(1, torch.from_numpy(rows).to(dev)), A, wdq, label=f"70b fused {N}x{K} M={M}")
+
+
+@pytest.mark.parametrize("N,K", [(8192, 28672), (57344, 8192)])
+def test_70b_m1_one_hot(N, K):
+    """The M = 1 decode kernel with two row-blocks per workgroup (down with
+    eight chunk-sets per wave, and the stacked gate/up): a one-hot row e_k
+    gives C[0, n] = wdq[n, k] bit for bit on the sampled rows."""
+    import torch
+    import oracle.rne as OR
+    import bit_weight_only_tq_amd as tq
+    dev = require_gpu()
+    log(f"70b M=1 one-hot N={N} K={K}")
+    codes, scale, rows, wdq = _packed(N, K, dev)
+    idx = torch.from_numpy(rows).to(dev)
+    for k in sorted({0, 7, 2047, 2048 + 5, K // 2 + 13, K - 129, K - 1}):
+        A = torch.zeros((1, K), dtype=torch.float16)
+        A[0, k] = 1.0
+        C = tq.tq_gemm(A.to(dev), codes, scale)
+        np.testing.assert_array_equal(bits16(C.index_select(1, idx))[0], OR.f16_bits(wdq[:, k]), err_msg=f"k={k}")
