@@ -949,6 +949,137 @@ __global__ __launch_bounds__(W * kWave) void w4_gemv_mfma_kernel(GemmArgs p) {
     }
 }
 
+// W4A16 at M = 1 (fp16, symmetric zero point 8, K = 128 G with GSW in {4, 8}
+// groups per wave and 4 <= W = G / GSW <= 16 waves, N a multiple of 16 R),
+// in the form of ternary_gemv_m1_kernel:
+// * wave w owns groups g0 = w GSW .. g0 + GSW - 1.  Lane l = 16h + i loads 16
+//   bytes (group columns 32h .. 32h + 31) of row i of each group, and MFMA d
+//   of a group contracts code word d of every lane (columns 32h + 8d ..);
+// * unit u (8 columns) of the wave's columns is word u % 4 of lane slot
+//   (u / 4) % 4 of group u / 16, so lane l preps units l + 64 j: four a'
+//   pairs (a_0, a_4), (a_1, a_5) / 16, (a_2, a_6), (a_3, a_7) / 16, 16 bytes
+//   at 16 u of the wave's LDS area, and its share of the group's constant
+//   sum a' (1024 + 8 16^s); a 16-lane row sum gives each group's constant;
+// * each group's four MFMAs start from zero, and the group's fp32 sum less
+//   its constant is scaled by s[n, g] into the row result (scales of a wave
+//   are GSW consecutive halves of a row: GSW / 4 8-byte loads);
+// * row 0 of the wave results meets in LDS; one barrier, a fixed-order sum.
+template <int R, int GSW>
+__global__ __launch_bounds__(1024) void w4_gemv_m1_kernel(GemmArgs p) {
+    extern __shared__ uint4 smem[];
+    constexpr int U = GSW / 4;  // 8-column units per lane
+    uint8_t* lds = reinterpret_cast<uint8_t*>(smem);
+    const int W = blockDim.x >> 6;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const int h = lane >> 4;
+    const int i16 = lane & 15;
+    const uint32_t rb = (uint32_t)(p.K / 2);         // code bytes per row
+    const int64_t G = p.K / 128;
+    const int64_t n_base = (int64_t)blockIdx.x * (16 * R);
+    const int g0 = wave * GSW;
+    uint8_t* aps = lds + wave * (GSW * 256);                            // this wave's a'
+    float* red = reinterpret_cast<float*>(lds + W * (GSW * 256));      // [W][R][16]
+
+    // 1. loads in the order they are consumed: activations, scales, bias of
+    //    the output this thread may finish, codes
+    const uint8_t* abase = reinterpret_cast<const uint8_t*>(p.A) + (int64_t)g0 * 256;
+    uint4 av[U];
+#pragma unroll
+    for (int j = 0; j < U; ++j) av[j] = *reinterpret_cast<const uint4*>(abase + 1024 * j + (uint64_t)(uint32_t)(16 * lane));
+    uint2 scw[R][U];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const uint16_t* srow = p.scale + (n_base + 16 * r + i16) * G + g0;
+#pragma unroll
+        for (int j = 0; j < U; ++j) scw[r][j] = *reinterpret_cast<const uint2*>(srow + 4 * j);
+    }
+    const int64_t n_e = n_base + (threadIdx.x & (16 * R - 1));
+    const uint16_t bi_bits = (p.bias ? p.bias : p.scale)[n_e];
+    const uint8_t* cbase = static_cast<const uint8_t*>(p.wq) + n_base * rb + (int64_t)g0 * 64;
+    const uint32_t lo = (uint32_t)i16 * rb + 16u * (uint32_t)h;
+    uint4 q[GSW][R];
+#pragma unroll
+    for (int gi = 0; gi < GSW; ++gi) {
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            q[gi][r] = *reinterpret_cast<const uint4*>(cbase + (int64_t)r * 16 * rb + 64 * gi + (uint64_t)lo);
+    }
+
+    // 2. a' pairs of this lane's units to LDS, and the groups' constants
+    float dpu[U];
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+        const uint4 a = av[j];
+        const f16x2 s16 = f16x2{(_Float16)0.0625f, (_Float16)0.0625f};
+        const uint32_t p0 = __builtin_amdgcn_perm(a.z, a.x, 0x05040100u);
+        const uint32_t p1 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(a.z, a.x, 0x07060302u)) * s16);
+        const uint32_t p2 = __builtin_amdgcn_perm(a.w, a.y, 0x05040100u);
+        const uint32_t p3 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(a.w, a.y, 0x07060302u)) * s16);
+        float dp = 0.0f;
+        dp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, p0), __builtin_bit_cast(f16x2, 0x64086408u), dp, false);
+        dp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, p1), __builtin_bit_cast(f16x2, 0x64806480u), dp, false);
+        dp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, p2), __builtin_bit_cast(f16x2, 0x64086408u), dp, false);
+        dp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, p3), __builtin_bit_cast(f16x2, 0x64806480u), dp, false);
+        dpu[j] = row16_sum(dp);  // DPP row r: the constant of group 4 j + r
+        *reinterpret_cast<uint4*>(aps + 16 * (lane + 64 * j)) = make_uint4(p0, p1, p2, p3);
+    }
+    float dg[GSW];
+#pragma unroll
+    for (int gi = 0; gi < GSW; ++gi)
+        dg[gi] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dpu[gi / 4]), 16 * (gi % 4)));
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's LDS writes are complete
+
+    // 3. contract group by group; lanes 16h read the operand's row 0, the
+    //    others keep an arbitrary value (their output rows are never stored)
+    float res[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) res[r] = 0.0f;
+    const uint32_t magic_v = vgpr_const<kMagic2>();
+    const uint32_t m0 = sgpr_const<0x000F000Fu>();
+    const uint32_t m1 = sgpr_const<0x00F000F0u>();
+#pragma unroll
+    for (int gi = 0; gi < GSW; ++gi) {
+        uint4 aw[4];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) aw[d] = opaque_uint4();
+        if (i16 == 0) {
+            const uint4* arow = reinterpret_cast<const uint4*>(aps + 16 * (16 * gi + 4 * h));
+#pragma unroll
+            for (int d = 0; d < 4; ++d) aw[d] = arow[d];
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            f32x4 ag = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const uint32_t x = dword_of(q[gi][r], d);
+                const uint32_t y = x >> 8;
+                const uint4 bw = make_uint4((x & m0) | magic_v, (x & m1) | magic_v, (y & m0) | magic_v, (y & m1) | magic_v);
+                ag = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, aw[d]), __builtin_bit_cast(f16x8, bw), ag, 0, 0, 0);
+            }
+            const uint2 sw = scw[r][gi / 4];
+            const uint32_t sd = (gi % 4) < 2 ? sw.x : sw.y;
+            const float s = f16_bits_to_f32((uint16_t)(sd >> (16 * (gi % 2))));
+            res[r] = fmaf(s, ag[0] - dg[gi], res[r]);
+        }
+    }
+
+    // 4. row 0 of the wave results -> LDS; fixed-order sum over the waves
+    if (h == 0) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) red[(wave * R + r) * 16 + i16] = res[r];
+    }
+    __syncthreads();
+    if ((int)threadIdx.x < 16 * R) {
+        const int t = (int)threadIdx.x;
+        float sum = red[t];
+        for (int w = 1; w < W; ++w) sum += red[w * (16 * R) + t];
+        const float bi = p.bias ? F16::to_f32(bi_bits) : 0.0f;
+        p.C[n_e] = F16::from_f32_fast(sum + bi);
+    }
+}
+
 // W4A16, streaming schedule (fp16, 3 <= M <= 16): the arithmetic above with
 // the work split of the ternary streaming kernel.  One workgroup walks T
 // consecutive 16-row blocks; wave w owns groups w*GSW .. w*GSW + GSW-1 (128
@@ -1637,7 +1768,49 @@ static hipError_t launch_w4_stream_t(const SplitArgs& sa, const W4StreamPlan& pl
 
 hipError_t launch_w4_gemv(const GemmArgs& a, hipStream_t s) { return launch_w4_gemv(a, nullptr, 0, s); }
 
+// Shape rule for the W4A16 M = 1 kernel: GSW = 4 groups per wave (8 when
+// that would need more than 16 waves), every wave a full share of K, at
+// least 4 waves, scales 8-byte aligned (a wave reads GSW / 4 aligned
+// 8-byte runs of them); two 16-row blocks per workgroup when one-block
+// workgroups would hold more than 8 waves per SIMD.  Zero points, bf16 and
+// other shapes take the kernels below.
+struct W4M1Plan {
+    int gsw, waves, rows16;
+    size_t lds;
+};
+
+static bool w4_m1_plan(const GemmArgs& a, W4M1Plan* pl) {
+    if (a.bf16 || a.M != 1 || a.zeros || a.K % 512 != 0 || a.N % 16 != 0) return false;
+    if ((reinterpret_cast<uintptr_t>(a.scale) & 7u) != 0) return false;
+    const int64_t G = a.K / 128;
+    const int c = G > 64 ? 8 : 4;
+    if (G % c != 0 || G / c < 4 || G / c > 16) return false;
+    pl->gsw = c;
+    pl->waves = (int)(G / c);
+    const int64_t nrb = a.N / 16;
+    pl->rows16 = (nrb % 2 == 0 && nrb * pl->waves > 32 * (int64_t)compute_units()) ? 2 : 1;
+    pl->lds = (size_t)pl->waves * c * 256 + (size_t)pl->waves * pl->rows16 * 64;
+    return pl->lds <= (size_t)kGemvLdsMaxBytes;
+}
+
+template <int R, int GSW>
+static hipError_t launch_w4_m1(const GemmArgs& a, const W4M1Plan& pl, hipStream_t s) {
+    static DeviceFlags lds_limit_set;
+    hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(&w4_gemv_m1_kernel<R, GSW>),
+                                   kGemvLdsMaxBytes, lds_limit_set);
+    if (e != hipSuccess) return e;
+    if (a.N % (16 * R) != 0 || a.K != (int64_t)pl.waves * GSW * 128) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)(a.N / (16 * R)));
+    w4_gemv_m1_kernel<R, GSW><<<grid, dim3(pl.waves * kWave), pl.lds, s>>>(a);
+    return hipGetLastError();
+}
+
 hipError_t launch_w4_gemv(const GemmArgs& a, void* workspace, size_t workspace_bytes, hipStream_t s) {
+    W4M1Plan m1;
+    if (w4_m1_plan(a, &m1)) {
+        if (m1.gsw == 8) return m1.rows16 == 2 ? launch_w4_m1<2, 8>(a, m1, s) : launch_w4_m1<1, 8>(a, m1, s);
+        return m1.rows16 == 2 ? launch_w4_m1<2, 4>(a, m1, s) : launch_w4_m1<1, 4>(a, m1, s);
+    }
     W4StreamPlan sp;
     if (w4_use_stream(a, workspace ? workspace_bytes : 0, &sp))
         return launch_w4_stream_t(SplitArgs{a, static_cast<float*>(workspace), sp.S, 1}, sp, s);

@@ -409,3 +409,33 @@ def test_w4_ragged_and_blocked(M):
     Ab = synth.activations(M, K, synth.seed_for("w4rb", M), "bf16")
     C = tq.w4a16_gemm(Ab.to(dev), q, s)
     check_close(C, Ab, wdq, label=f"w4 ragged bf16 M={M}")
+
+
+# Shapes of the W4A16 M = 1 kernel: 8 waves of 4 groups, 14 waves of 8
+# groups, 16 waves of 4, and two 16-row blocks per workgroup (1792 row-blocks
+# of 8 waves would exceed 8 waves per SIMD on 256 compute units).
+W4_M1_SHAPES = [(320, 4096), (1024, 14336), (512, 8192), (28672, 4096)]
+
+
+@pytest.mark.parametrize("N,K", W4_M1_SHAPES)
+def test_w4_m1_one_hot_and_bias(N, K):
+    """The W4A16 M = 1 kernel: a one-hot row e_k gives C[0, n] = wdq[n, k]
+    bit for bit for k at every nibble position of a word, every word of a
+    lane slot and every slot of a group, in first and last groups of several
+    waves; a dense row with a bias is within the tolerance."""
+    import torch
+    import bit_weight_only_tq_amd as tq
+    dev = require_gpu()
+    log(f"W4 M=1 kernel one-hot and bias N={N} K={K}")
+    q, s, rq, rs, wdq = _w4(N, K, dev)
+    ks = sorted({0, 1, 2, 3, 4, 5, 6, 7, 8, 15, 31, 32, 63, 96 + 7, 127, 128, 640 + 45, 1023, 1024 + 77,
+                 K // 2 + 19, K - 128, K - 33, K - 1})
+    for k in ks:
+        A = torch.zeros((1, K), dtype=torch.float16)
+        A[0, k] = 1.0
+        C = tq.w4a16_gemm(A.to(dev), q, s)
+        np.testing.assert_array_equal(bits16(C)[0], OR.f16_bits(wdq[:, k]), err_msg=f"k={k}")
+    A = synth.activations(1, K, synth.seed_for("w4m1", N, K), "f16")
+    bias = synth.activations(1, N, synth.seed_for("w4m1b", N, K), "f16")[0]
+    C = tq.w4a16_gemm(A.to(dev), q, s, bias=bias.to(dev))
+    check_close(C, A, wdq, bias=bias, label=f"W4 M=1 kernel {N}x{K} with bias")
