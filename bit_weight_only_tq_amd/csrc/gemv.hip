@@ -964,7 +964,10 @@ __global__ __launch_bounds__(W * kWave) void w4_gemv_mfma_kernel(GemmArgs p) {
 //   its constant is scaled by s[n, g] into the row result (scales of a wave
 //   are GSW consecutive halves of a row: GSW / 4 8-byte loads);
 // * row 0 of the wave results meets in LDS; one barrier, a fixed-order sum.
-template <int R, int GSW>
+// ASYM: per-(row, group) zero points z (uint8, [N, K/128]) instead of 8: the
+// group's constant splits into 1024 sum a' and sum a (both row-independent,
+// two row sums), and the group value is acc - 1024 sum a' - z sum a.
+template <int R, int GSW, bool ASYM>
 __global__ __launch_bounds__(1024) void w4_gemv_m1_kernel(GemmArgs p) {
     extern __shared__ uint4 smem[];
     constexpr int U = GSW / 4;  // 8-column units per lane
@@ -994,6 +997,15 @@ __global__ __launch_bounds__(1024) void w4_gemv_m1_kernel(GemmArgs p) {
 #pragma unroll
         for (int j = 0; j < U; ++j) scw[r][j] = *reinterpret_cast<const uint2*>(srow + 4 * j);
     }
+    uint32_t zw[R][U];
+    if constexpr (ASYM) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const uint8_t* zrow = p.zeros + (n_base + 16 * r + i16) * G + g0;
+#pragma unroll
+            for (int j = 0; j < U; ++j) zw[r][j] = *reinterpret_cast<const uint32_t*>(zrow + 4 * j);
+        }
+    }
     const int64_t n_e = n_base + (threadIdx.x & (16 * R - 1));
     const uint16_t bi_bits = (p.bias ? p.bias : p.scale)[n_e];
     const uint8_t* cbase = static_cast<const uint8_t*>(p.wq) + n_base * rb + (int64_t)g0 * 64;
@@ -1007,7 +1019,7 @@ __global__ __launch_bounds__(1024) void w4_gemv_m1_kernel(GemmArgs p) {
     }
 
     // 2. a' pairs of this lane's units to LDS, and the groups' constants
-    float dpu[U];
+    float dpu[U], dsu[U];
 #pragma unroll
     for (int j = 0; j < U; ++j) {
         const uint4 a = av[j];
@@ -1016,18 +1028,32 @@ __global__ __launch_bounds__(1024) void w4_gemv_m1_kernel(GemmArgs p) {
         const uint32_t p1 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(a.z, a.x, 0x07060302u)) * s16);
         const uint32_t p2 = __builtin_amdgcn_perm(a.w, a.y, 0x05040100u);
         const uint32_t p3 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(a.w, a.y, 0x07060302u)) * s16);
+        // symmetric: sum a' (1024 + 8 16^s) = (1032, 1152) patterns; ASYM:
+        // sum a' 1024, and sum a = (1, 16) patterns on the scaled pairs
+        constexpr uint32_t c0 = ASYM ? 0x64006400u : 0x64086408u;
+        constexpr uint32_t c1 = ASYM ? 0x64006400u : 0x64806480u;
         float dp = 0.0f;
-        dp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, p0), __builtin_bit_cast(f16x2, 0x64086408u), dp, false);
-        dp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, p1), __builtin_bit_cast(f16x2, 0x64806480u), dp, false);
-        dp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, p2), __builtin_bit_cast(f16x2, 0x64086408u), dp, false);
-        dp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, p3), __builtin_bit_cast(f16x2, 0x64806480u), dp, false);
+        dp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, p0), __builtin_bit_cast(f16x2, c0), dp, false);
+        dp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, p1), __builtin_bit_cast(f16x2, c1), dp, false);
+        dp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, p2), __builtin_bit_cast(f16x2, c0), dp, false);
+        dp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, p3), __builtin_bit_cast(f16x2, c1), dp, false);
         dpu[j] = row16_sum(dp);  // DPP row r: the constant of group 4 j + r
+        if constexpr (ASYM) {
+            float sa = 0.0f;
+            sa = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, p0), __builtin_bit_cast(f16x2, 0x3C003C00u), sa, false);
+            sa = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, p1), __builtin_bit_cast(f16x2, 0x4C004C00u), sa, false);
+            sa = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, p2), __builtin_bit_cast(f16x2, 0x3C003C00u), sa, false);
+            sa = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, p3), __builtin_bit_cast(f16x2, 0x4C004C00u), sa, false);
+            dsu[j] = row16_sum(sa);
+        }
         *reinterpret_cast<uint4*>(aps + 16 * (lane + 64 * j)) = make_uint4(p0, p1, p2, p3);
     }
-    float dg[GSW];
+    float dg[GSW], sg[GSW];
 #pragma unroll
-    for (int gi = 0; gi < GSW; ++gi)
+    for (int gi = 0; gi < GSW; ++gi) {
         dg[gi] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dpu[gi / 4]), 16 * (gi % 4)));
+        if constexpr (ASYM) sg[gi] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dsu[gi / 4]), 16 * (gi % 4)));
+    }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's LDS writes are complete
 
     // 3. contract group by group; lanes 16h read the operand's row 0, the
@@ -1061,7 +1087,9 @@ __global__ __launch_bounds__(1024) void w4_gemv_m1_kernel(GemmArgs p) {
             const uint2 sw = scw[r][gi / 4];
             const uint32_t sd = (gi % 4) < 2 ? sw.x : sw.y;
             const float s = f16_bits_to_f32((uint16_t)(sd >> (16 * (gi % 2))));
-            res[r] = fmaf(s, ag[0] - dg[gi], res[r]);
+            float v = ag[0] - dg[gi];
+            if constexpr (ASYM) v -= (float)((zw[r][gi / 4] >> (8 * (gi % 4))) & 0xFFu) * sg[gi];
+            res[r] = fmaf(s, v, res[r]);
         }
     }
 
@@ -1770,18 +1798,19 @@ hipError_t launch_w4_gemv(const GemmArgs& a, hipStream_t s) { return launch_w4_g
 
 // Shape rule for the W4A16 M = 1 kernel: GSW = 4 groups per wave (8 when
 // that would need more than 16 waves), every wave a full share of K, at
-// least 4 waves, scales 8-byte aligned (a wave reads GSW / 4 aligned
-// 8-byte runs of them); two 16-row blocks per workgroup when one-block
-// workgroups would hold more than 8 waves per SIMD.  Zero points, bf16 and
-// other shapes take the kernels below.
+// least 4 waves, scales 8-byte and zero points 4-byte aligned (a wave reads
+// aligned runs of them); two 16-row blocks per workgroup when one-block
+// workgroups would hold more than 8 waves per SIMD.  bf16 and other shapes
+// take the kernels below.
 struct W4M1Plan {
     int gsw, waves, rows16;
     size_t lds;
 };
 
 static bool w4_m1_plan(const GemmArgs& a, W4M1Plan* pl) {
-    if (a.bf16 || a.M != 1 || a.zeros || a.K % 512 != 0 || a.N % 16 != 0) return false;
-    if ((reinterpret_cast<uintptr_t>(a.scale) & 7u) != 0) return false;
+    if (a.bf16 || a.M != 1 || a.K % 512 != 0 || a.N % 16 != 0) return false;
+    if ((reinterpret_cast<uintptr_t>(a.scale) & 7u) != 0 || (reinterpret_cast<uintptr_t>(a.zeros) & 3u) != 0)
+        return false;
     const int64_t G = a.K / 128;
     const int c = G > 64 ? 8 : 4;
     if (G % c != 0 || G / c < 4 || G / c > 16) return false;
@@ -1793,16 +1822,21 @@ static bool w4_m1_plan(const GemmArgs& a, W4M1Plan* pl) {
     return pl->lds <= (size_t)kGemvLdsMaxBytes;
 }
 
-template <int R, int GSW>
-static hipError_t launch_w4_m1(const GemmArgs& a, const W4M1Plan& pl, hipStream_t s) {
+template <int R, int GSW, bool ASYM>
+static hipError_t launch_w4_m1_k(const GemmArgs& a, const W4M1Plan& pl, hipStream_t s) {
     static DeviceFlags lds_limit_set;
-    hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(&w4_gemv_m1_kernel<R, GSW>),
+    hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(&w4_gemv_m1_kernel<R, GSW, ASYM>),
                                    kGemvLdsMaxBytes, lds_limit_set);
     if (e != hipSuccess) return e;
     if (a.N % (16 * R) != 0 || a.K != (int64_t)pl.waves * GSW * 128) return hipErrorInvalidValue;
     const dim3 grid((unsigned)(a.N / (16 * R)));
-    w4_gemv_m1_kernel<R, GSW><<<grid, dim3(pl.waves * kWave), pl.lds, s>>>(a);
+    w4_gemv_m1_kernel<R, GSW, ASYM><<<grid, dim3(pl.waves * kWave), pl.lds, s>>>(a);
     return hipGetLastError();
+}
+
+template <int R, int GSW>
+static hipError_t launch_w4_m1(const GemmArgs& a, const W4M1Plan& pl, hipStream_t s) {
+    return a.zeros ? launch_w4_m1_k<R, GSW, true>(a, pl, s) : launch_w4_m1_k<R, GSW, false>(a, pl, s);
 }
 
 hipError_t launch_w4_gemv(const GemmArgs& a, void* workspace, size_t workspace_bytes, hipStream_t s) {
