@@ -949,47 +949,60 @@ __global__ __launch_bounds__(W * kWave) void w4_gemv_mfma_kernel(GemmArgs p) {
     }
 }
 
-// W4A16 at M = 1 (fp16, symmetric zero point 8, K = 128 G with GSW in {4, 8}
-// groups per wave and 4 <= W = G / GSW <= 16 waves, N a multiple of 16 R),
-// in the form of ternary_gemv_m1_kernel:
+// W4A16 at M <= 4 (fp16, K = 128 G with GSW in {4, 8} groups per wave and
+// 4 <= W = G / GSW <= 16 waves, N a multiple of 16 R), in the form of
+// ternary_gemv_m1_kernel; MT in {1, 2, 4} activation rows are held, rows
+// M .. MT-1 re-read row M-1 and are never stored:
 // * wave w owns groups g0 = w GSW .. g0 + GSW - 1.  Lane l = 16h + i loads 16
 //   bytes (group columns 32h .. 32h + 31) of row i of each group, and MFMA d
 //   of a group contracts code word d of every lane (columns 32h + 8d ..);
 // * unit u (8 columns) of the wave's columns is word u % 4 of lane slot
-//   (u / 4) % 4 of group u / 16, so lane l preps units l + 64 j: four a'
-//   pairs (a_0, a_4), (a_1, a_5) / 16, (a_2, a_6), (a_3, a_7) / 16, 16 bytes
-//   at 16 u of the wave's LDS area, and its share of the group's constant
-//   sum a' (1024 + 8 16^s); a 16-lane row sum gives each group's constant;
-// * each group's four MFMAs start from zero, and the group's fp32 sum less
-//   its constant is scaled by s[n, g] into the row result (scales of a wave
-//   are GSW consecutive halves of a row: GSW / 4 8-byte loads);
-// * row 0 of the wave results meets in LDS; one barrier, a fixed-order sum.
+//   (u / 4) % 4 of group u / 16, so lane l preps units l + 64 j of every
+//   activation row m: four a' pairs (a_0, a_4), (a_1, a_5) / 16, (a_2, a_6),
+//   (a_3, a_7) / 16, 16 bytes at 16 u of row m's part of the wave's LDS
+//   area, and its share of the group's constant sum a' (1024 + 8 16^s); a
+//   16-lane row sum gives each (row, group) constant;
+// * lanes 16h + m (m < M) read row m's operand back; each group's four MFMAs
+//   start from zero, and component i (activation row i) of the group's fp32
+//   sum less row i's constant is scaled by s[n, g] into the row result
+//   (scales of a wave are GSW consecutive halves of a row: GSW / 4 8-byte
+//   loads);
+// * rows 0 .. MT-1 of the wave results meet in LDS; one barrier, a
+//   fixed-order sum.
 // ASYM: per-(row, group) zero points z (uint8, [N, K/128]) instead of 8: the
-// group's constant splits into 1024 sum a' and sum a (both row-independent,
-// two row sums), and the group value is acc - 1024 sum a' - z sum a.
-template <int R, int GSW, bool ASYM>
+// group's constant splits into 1024 sum a' and sum a (both independent of
+// the weight row, two row sums), and the group value is
+// acc - 1024 sum a' - z sum a.
+template <int R, int GSW, bool ASYM, int MT>
 __global__ __launch_bounds__(1024) void w4_gemv_m1_kernel(GemmArgs p) {
     extern __shared__ uint4 smem[];
-    constexpr int U = GSW / 4;  // 8-column units per lane
+    constexpr int U = GSW / 4;            // 8-column units per lane and row
+    constexpr int kRowLds = GSW * 256;    // a' bytes of one activation row
     uint8_t* lds = reinterpret_cast<uint8_t*>(smem);
     const int W = blockDim.x >> 6;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
     const int h = lane >> 4;
     const int i16 = lane & 15;
+    const int M = (int)p.M;
     const uint32_t rb = (uint32_t)(p.K / 2);         // code bytes per row
     const int64_t G = p.K / 128;
     const int64_t n_base = (int64_t)blockIdx.x * (16 * R);
     const int g0 = wave * GSW;
-    uint8_t* aps = lds + wave * (GSW * 256);                            // this wave's a'
-    float* red = reinterpret_cast<float*>(lds + W * (GSW * 256));      // [W][R][16]
+    uint8_t* aps = lds + wave * (MT * kRowLds);                           // this wave's a'
+    float* red = reinterpret_cast<float*>(lds + W * (MT * kRowLds));      // [W][R][MT][16]
 
-    // 1. loads in the order they are consumed: activations, scales, bias of
-    //    the output this thread may finish, codes
+    // 1. loads in the order they are consumed: activations, scales, zero
+    //    points, bias of the output this thread may finish, codes
     const uint8_t* abase = reinterpret_cast<const uint8_t*>(p.A) + (int64_t)g0 * 256;
-    uint4 av[U];
+    uint4 av[MT][U];
 #pragma unroll
-    for (int j = 0; j < U; ++j) av[j] = *reinterpret_cast<const uint4*>(abase + 1024 * j + (uint64_t)(uint32_t)(16 * lane));
+    for (int m = 0; m < MT; ++m) {
+        const int mr = m < M ? m : M - 1;
+        const uint8_t* arow = abase + (int64_t)mr * (p.K * 2);
+#pragma unroll
+        for (int j = 0; j < U; ++j) av[m][j] = *reinterpret_cast<const uint4*>(arow + 1024 * j + (uint64_t)(uint32_t)(16 * lane));
+    }
     uint2 scw[R][U];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -1006,7 +1019,10 @@ __global__ __launch_bounds__(1024) void w4_gemv_m1_kernel(GemmArgs p) {
             for (int j = 0; j < U; ++j) zw[r][j] = *reinterpret_cast<const uint32_t*>(zrow + 4 * j);
         }
     }
-    const int64_t n_e = n_base + (threadIdx.x & (16 * R - 1));
+    // output of thread t (< 16 R MT) in step 4: row-block t / (16 MT),
+    // activation row (t / 16) % MT, weight row n_base + 16 (t / (16 MT)) + t % 16
+    const int te = (int)threadIdx.x % (16 * R * MT);
+    const int64_t n_e = n_base + 16 * (te / (16 * MT)) + (te & 15);
     const uint16_t bi_bits = (p.bias ? p.bias : p.scale)[n_e];
     const uint8_t* cbase = static_cast<const uint8_t*>(p.wq) + n_base * rb + (int64_t)g0 * 64;
     const uint32_t lo = (uint32_t)i16 * rb + 16u * (uint32_t)h;
@@ -1018,59 +1034,66 @@ __global__ __launch_bounds__(1024) void w4_gemv_m1_kernel(GemmArgs p) {
             q[gi][r] = *reinterpret_cast<const uint4*>(cbase + (int64_t)r * 16 * rb + 64 * gi + (uint64_t)lo);
     }
 
-    // 2. a' pairs of this lane's units to LDS, and the groups' constants
-    float dpu[U], dsu[U];
+    // 2. a' pairs of this lane's units to LDS, and the (row, group) constants
+    float dg[MT][GSW], sg[MT][GSW];
 #pragma unroll
-    for (int j = 0; j < U; ++j) {
-        const uint4 a = av[j];
-        const f16x2 s16 = f16x2{(_Float16)0.0625f, (_Float16)0.0625f};
-        const uint32_t p0 = __builtin_amdgcn_perm(a.z, a.x, 0x05040100u);
-        const uint32_t p1 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(a.z, a.x, 0x07060302u)) * s16);
-        const uint32_t p2 = __builtin_amdgcn_perm(a.w, a.y, 0x05040100u);
-        const uint32_t p3 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(a.w, a.y, 0x07060302u)) * s16);
-        // symmetric: sum a' (1024 + 8 16^s) = (1032, 1152) patterns; ASYM:
-        // sum a' 1024, and sum a = (1, 16) patterns on the scaled pairs
-        constexpr uint32_t c0 = ASYM ? 0x64006400u : 0x64086408u;
-        constexpr uint32_t c1 = ASYM ? 0x64006400u : 0x64806480u;
-        float dp = 0.0f;
-        dp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, p0), __builtin_bit_cast(f16x2, c0), dp, false);
-        dp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, p1), __builtin_bit_cast(f16x2, c1), dp, false);
-        dp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, p2), __builtin_bit_cast(f16x2, c0), dp, false);
-        dp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, p3), __builtin_bit_cast(f16x2, c1), dp, false);
-        dpu[j] = row16_sum(dp);  // DPP row r: the constant of group 4 j + r
-        if constexpr (ASYM) {
-            float sa = 0.0f;
-            sa = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, p0), __builtin_bit_cast(f16x2, 0x3C003C00u), sa, false);
-            sa = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, p1), __builtin_bit_cast(f16x2, 0x4C004C00u), sa, false);
-            sa = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, p2), __builtin_bit_cast(f16x2, 0x3C003C00u), sa, false);
-            sa = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, p3), __builtin_bit_cast(f16x2, 0x4C004C00u), sa, false);
-            dsu[j] = row16_sum(sa);
+    for (int m = 0; m < MT; ++m) {
+        float dpu[U], dsu[U];
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+            const uint4 a = av[m][j];
+            const f16x2 s16 = f16x2{(_Float16)0.0625f, (_Float16)0.0625f};
+            const uint32_t p0 = __builtin_amdgcn_perm(a.z, a.x, 0x05040100u);
+            const uint32_t p1 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(a.z, a.x, 0x07060302u)) * s16);
+            const uint32_t p2 = __builtin_amdgcn_perm(a.w, a.y, 0x05040100u);
+            const uint32_t p3 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(a.w, a.y, 0x07060302u)) * s16);
+            // symmetric: sum a' (1024 + 8 16^s) = (1032, 1152) patterns; ASYM:
+            // sum a' 1024, and sum a = (1, 16) patterns on the scaled pairs
+            constexpr uint32_t c0 = ASYM ? 0x64006400u : 0x64086408u;
+            constexpr uint32_t c1 = ASYM ? 0x64006400u : 0x64806480u;
+            float dp = 0.0f;
+            dp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, p0), __builtin_bit_cast(f16x2, c0), dp, false);
+            dp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, p1), __builtin_bit_cast(f16x2, c1), dp, false);
+            dp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, p2), __builtin_bit_cast(f16x2, c0), dp, false);
+            dp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, p3), __builtin_bit_cast(f16x2, c1), dp, false);
+            dpu[j] = row16_sum(dp);  // DPP row r: the constant of group 4 j + r
+            if constexpr (ASYM) {
+                float sa = 0.0f;
+                sa = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, p0), __builtin_bit_cast(f16x2, 0x3C003C00u), sa, false);
+                sa = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, p1), __builtin_bit_cast(f16x2, 0x4C004C00u), sa, false);
+                sa = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, p2), __builtin_bit_cast(f16x2, 0x3C003C00u), sa, false);
+                sa = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, p3), __builtin_bit_cast(f16x2, 0x4C004C00u), sa, false);
+                dsu[j] = row16_sum(sa);
+            }
+            *reinterpret_cast<uint4*>(aps + m * kRowLds + 16 * (lane + 64 * j)) = make_uint4(p0, p1, p2, p3);
         }
-        *reinterpret_cast<uint4*>(aps + 16 * (lane + 64 * j)) = make_uint4(p0, p1, p2, p3);
-    }
-    float dg[GSW], sg[GSW];
 #pragma unroll
-    for (int gi = 0; gi < GSW; ++gi) {
-        dg[gi] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dpu[gi / 4]), 16 * (gi % 4)));
-        if constexpr (ASYM) sg[gi] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dsu[gi / 4]), 16 * (gi % 4)));
+        for (int gi = 0; gi < GSW; ++gi) {
+            dg[m][gi] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dpu[gi / 4]), 16 * (gi % 4)));
+            if constexpr (ASYM) sg[m][gi] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dsu[gi / 4]), 16 * (gi % 4)));
+        }
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's LDS writes are complete
 
-    // 3. contract group by group; lanes 16h read the operand's row 0, the
-    //    others keep an arbitrary value (their output rows are never stored)
-    float res[R];
+    // 3. contract group by group; lanes 16h + m (m < M) read row m's operand,
+    //    the others keep an arbitrary value (their output rows are never
+    //    stored)
+    float res[R][MT];
 #pragma unroll
-    for (int r = 0; r < R; ++r) res[r] = 0.0f;
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int i = 0; i < MT; ++i) res[r][i] = 0.0f;
     const uint32_t magic_v = vgpr_const<kMagic2>();
     const uint32_t m0 = sgpr_const<0x000F000Fu>();
     const uint32_t m1 = sgpr_const<0x00F000F0u>();
+    const bool a_live = MT == 1 ? i16 == 0 : i16 < M;
 #pragma unroll
     for (int gi = 0; gi < GSW; ++gi) {
         uint4 aw[4];
 #pragma unroll
         for (int d = 0; d < 4; ++d) aw[d] = opaque_uint4();
-        if (i16 == 0) {
-            const uint4* arow = reinterpret_cast<const uint4*>(aps + 16 * (16 * gi + 4 * h));
+        if (a_live) {
+            const uint4* arow = reinterpret_cast<const uint4*>(aps + (MT == 1 ? 0 : i16 * kRowLds) + 16 * (16 * gi + 4 * h));
 #pragma unroll
             for (int d = 0; d < 4; ++d) aw[d] = arow[d];
         }
@@ -1087,24 +1110,32 @@ __global__ __launch_bounds__(1024) void w4_gemv_m1_kernel(GemmArgs p) {
             const uint2 sw = scw[r][gi / 4];
             const uint32_t sd = (gi % 4) < 2 ? sw.x : sw.y;
             const float s = f16_bits_to_f32((uint16_t)(sd >> (16 * (gi % 2))));
-            float v = ag[0] - dg[gi];
-            if constexpr (ASYM) v -= (float)((zw[r][gi / 4] >> (8 * (gi % 4))) & 0xFFu) * sg[gi];
-            res[r] = fmaf(s, v, res[r]);
+            float zf = 0.0f;
+            if constexpr (ASYM) zf = (float)((zw[r][gi / 4] >> (8 * (gi % 4))) & 0xFFu);
+#pragma unroll
+            for (int i = 0; i < MT; ++i) {
+                float v = ag[i] - dg[i][gi];
+                if constexpr (ASYM) v -= zf * sg[i][gi];
+                res[r][i] = fmaf(s, v, res[r][i]);
+            }
         }
     }
 
-    // 4. row 0 of the wave results -> LDS; fixed-order sum over the waves
+    // 4. rows 0 .. MT-1 of the wave results -> LDS; fixed-order sum
     if (h == 0) {
 #pragma unroll
-        for (int r = 0; r < R; ++r) red[(wave * R + r) * 16 + i16] = res[r];
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int i = 0; i < MT; ++i) red[((wave * R + r) * MT + i) * 16 + i16] = res[r][i];
     }
     __syncthreads();
-    if ((int)threadIdx.x < 16 * R) {
+    if ((int)threadIdx.x < 16 * R * MT) {
         const int t = (int)threadIdx.x;
+        const int i = (t / 16) % MT;
         float sum = red[t];
-        for (int w = 1; w < W; ++w) sum += red[w * (16 * R) + t];
+        for (int w = 1; w < W; ++w) sum += red[w * (16 * R * MT) + t];
         const float bi = p.bias ? F16::to_f32(bi_bits) : 0.0f;
-        p.C[n_e] = F16::from_f32_fast(sum + bi);
+        if (i < M) p.C[(int64_t)i * p.N + n_e] = F16::from_f32_fast(sum + bi);
     }
 }
 
@@ -1803,12 +1834,16 @@ hipError_t launch_w4_gemv(const GemmArgs& a, hipStream_t s) { return launch_w4_g
 // workgroups would hold more than 8 waves per SIMD.  bf16 and other shapes
 // take the kernels below.
 struct W4M1Plan {
-    int gsw, waves, rows16;
+    int gsw, waves, rows16, mt;
     size_t lds;
 };
+#ifndef TQ_W4_SMALL_MAX_M
+#define TQ_W4_SMALL_MAX_M 4
+#endif
+constexpr int64_t kW4SmallMaxM = TQ_W4_SMALL_MAX_M;  // largest M the small-M kernel takes
 
 static bool w4_m1_plan(const GemmArgs& a, W4M1Plan* pl) {
-    if (a.bf16 || a.M != 1 || a.K % 512 != 0 || a.N % 16 != 0) return false;
+    if (a.bf16 || a.M < 1 || a.M > kW4SmallMaxM || a.K % 512 != 0 || a.N % 16 != 0) return false;
     if ((reinterpret_cast<uintptr_t>(a.scale) & 7u) != 0 || (reinterpret_cast<uintptr_t>(a.zeros) & 3u) != 0)
         return false;
     const int64_t G = a.K / 128;
@@ -1818,25 +1853,33 @@ static bool w4_m1_plan(const GemmArgs& a, W4M1Plan* pl) {
     pl->waves = (int)(G / c);
     const int64_t nrb = a.N / 16;
     pl->rows16 = (nrb % 2 == 0 && nrb * pl->waves > 32 * (int64_t)compute_units()) ? 2 : 1;
-    pl->lds = (size_t)pl->waves * c * 256 + (size_t)pl->waves * pl->rows16 * 64;
+    pl->mt = a.M == 1 ? 1 : a.M == 2 ? 2 : 4;
+    pl->lds = (size_t)pl->waves * pl->mt * c * 256 + (size_t)pl->waves * pl->rows16 * pl->mt * 64;
     return pl->lds <= (size_t)kGemvLdsMaxBytes;
 }
 
-template <int R, int GSW, bool ASYM>
+template <int R, int GSW, bool ASYM, int MT>
 static hipError_t launch_w4_m1_k(const GemmArgs& a, const W4M1Plan& pl, hipStream_t s) {
     static DeviceFlags lds_limit_set;
-    hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(&w4_gemv_m1_kernel<R, GSW, ASYM>),
+    hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(&w4_gemv_m1_kernel<R, GSW, ASYM, MT>),
                                    kGemvLdsMaxBytes, lds_limit_set);
     if (e != hipSuccess) return e;
-    if (a.N % (16 * R) != 0 || a.K != (int64_t)pl.waves * GSW * 128) return hipErrorInvalidValue;
+    if (a.N % (16 * R) != 0 || a.K != (int64_t)pl.waves * GSW * 128 || a.M > MT) return hipErrorInvalidValue;
     const dim3 grid((unsigned)(a.N / (16 * R)));
-    w4_gemv_m1_kernel<R, GSW, ASYM><<<grid, dim3(pl.waves * kWave), pl.lds, s>>>(a);
+    w4_gemv_m1_kernel<R, GSW, ASYM, MT><<<grid, dim3(pl.waves * kWave), pl.lds, s>>>(a);
     return hipGetLastError();
+}
+
+template <int R, int GSW, bool ASYM>
+static hipError_t launch_w4_m1_mt(const GemmArgs& a, const W4M1Plan& pl, hipStream_t s) {
+    if (pl.mt == 1) return launch_w4_m1_k<R, GSW, ASYM, 1>(a, pl, s);
+    if (pl.mt == 2) return launch_w4_m1_k<R, GSW, ASYM, 2>(a, pl, s);
+    return launch_w4_m1_k<R, GSW, ASYM, 4>(a, pl, s);
 }
 
 template <int R, int GSW>
 static hipError_t launch_w4_m1(const GemmArgs& a, const W4M1Plan& pl, hipStream_t s) {
-    return a.zeros ? launch_w4_m1_k<R, GSW, true>(a, pl, s) : launch_w4_m1_k<R, GSW, false>(a, pl, s);
+    return a.zeros ? launch_w4_m1_mt<R, GSW, true>(a, pl, s) : launch_w4_m1_mt<R, GSW, false>(a, pl, s);
 }
 
 hipError_t launch_w4_gemv(const GemmArgs& a, void* workspace, size_t workspace_bytes, hipStream_t s) {
