@@ -473,44 +473,56 @@ __global__ __launch_bounds__(1024) void ternary_gemv_lds_kernel(GemmArgs p) {
     }
 }
 
-// M = 1 form of the kernel above (fp16, K a multiple of 256 CSW, N a
-// multiple of 16 R, W = K / (256 CSW) waves).  With one activation row:
-// * unit c (16 columns) of a wave's a' area is 32 contiguous bytes at 32 c,
-//   and only lanes 16g (row 0 of the matrix-core operand) read it back;
-// * the constant term D of a wave is a single number, subtracted from its
-//   partials before the cross-wave sum;
+// Small-M form of the kernel above (fp16, M <= 4, K a multiple of 256 CSW,
+// N a multiple of 16 R, W = K / (256 CSW) waves), with MT in {1, 2, 4}
+// activation rows held at compile time (rows M .. MT-1 re-read row M-1 and
+// are never stored):
+// * unit c (16 columns) of row m's part of a wave's a' area is 32
+//   contiguous bytes at 32 c, and only lanes 16g + m (m < M: row m of the
+//   matrix-core operand) read it back;
+// * the constant term D of a wave is one number per activation row,
+//   subtracted from its partials before the cross-wave sum;
 // * every global address is a wave-uniform base plus a 32-bit lane offset
 //   and a compile-time displacement, and no count depends on M at run time.
 // The bias is read from a valid address whether or not one is given, so the
 // load needs no branch (a branch there makes the compiler wait for every
 // outstanding load, codes included, before it).
-template <int R, int CSW>
+template <int R, int CSW, int MT>
 __global__ __launch_bounds__(1024) void ternary_gemv_m1_kernel(GemmArgs p) {
     extern __shared__ uint4 smem[];
-    constexpr int U = CSW / 4;  // 16-column activation units per lane
+    constexpr int U = CSW / 4;            // 16-column activation units per lane and row
+    constexpr int kRowLds = CSW * 512;    // a' bytes of one activation row
     uint8_t* lds = reinterpret_cast<uint8_t*>(smem);
     const int W = blockDim.x >> 6;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
     const int g = lane >> 4;
     const int i16 = lane & 15;
+    const int M = (int)p.M;
     const uint32_t rb = (uint32_t)(p.K / 4);
     const int64_t n_base = (int64_t)blockIdx.x * (16 * R);
     const int cs0 = wave * CSW;
-    uint8_t* aps = lds + wave * (CSW * 512);                              // this wave's a'
-    float* red = reinterpret_cast<float*>(lds + W * (CSW * 512));       // [W][R][16]
+    uint8_t* aps = lds + wave * (MT * kRowLds);                           // this wave's a'
+    float* red = reinterpret_cast<float*>(lds + W * (MT * kRowLds));      // [W][R][MT][16]
 
     // 1. loads in the order they are consumed: activations, row scale and
     //    bias of the output this thread may finish, then all codes
     const uint8_t* abase = reinterpret_cast<const uint8_t*>(p.A) + (int64_t)cs0 * 512;
-    uint4 av[U][8];
+    uint4 av[MT][U][8];
 #pragma unroll
-    for (int j = 0; j < U; ++j) {
-        const uint8_t* src = abase + 2048 * j + (uint64_t)(uint32_t)(32 * lane);
-        av[j][0] = *reinterpret_cast<const uint4*>(src);
-        av[j][1] = *reinterpret_cast<const uint4*>(src + 16);
+    for (int m = 0; m < MT; ++m) {
+        const int mr = m < M ? m : M - 1;
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+            const uint8_t* src = abase + (int64_t)mr * (p.K * 2) + 2048 * j + (uint64_t)(uint32_t)(32 * lane);
+            av[m][j][0] = *reinterpret_cast<const uint4*>(src);
+            av[m][j][1] = *reinterpret_cast<const uint4*>(src + 16);
+        }
     }
-    const int64_t n_e = n_base + (threadIdx.x & (16 * R - 1));
+    // output of thread t (< 16 R MT) in step 4: row-block t / (16 MT),
+    // activation row (t / 16) % MT, weight row n_base + 16 (t / (16 MT)) + t % 16
+    const int te = (int)threadIdx.x % (16 * R * MT);
+    const int64_t n_e = n_base + 16 * (te / (16 * MT)) + (te & 15);
     const uint16_t* bsrc = p.bias ? p.bias : p.scale;
     const uint16_t sc_bits = p.scale[n_e];
     const uint16_t bi_bits = bsrc[n_e];
@@ -524,44 +536,49 @@ __global__ __launch_bounds__(1024) void ternary_gemv_m1_kernel(GemmArgs p) {
             q[s][r] = *reinterpret_cast<const uint4*>(cbase + (int64_t)r * 16 * rb + 64 * s + (uint64_t)lo);
     }
 
-    // 2. a' of this wave's columns to LDS, and the wave's D
-    float dp = 0.0f;
+    // 2. a' of this wave's columns to LDS, and the wave's D per row
+    float dw[MT];
 #pragma unroll
-    for (int j = 0; j < U; ++j) {
-        const uint4 w0 = make_uint4(a_pair<0, 0>(av[j]), a_pair<0, 1>(av[j]), a_pair<0, 2>(av[j]), a_pair<0, 3>(av[j]));
-        const uint4 w1 = make_uint4(a_pair<0, 4>(av[j]), a_pair<0, 5>(av[j]), a_pair<0, 6>(av[j]), a_pair<0, 7>(av[j]));
-        dp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w0.x), __builtin_bit_cast(f16x2, one_pattern<0>()), dp, false);
-        dp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w0.y), __builtin_bit_cast(f16x2, one_pattern<1>()), dp, false);
-        dp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w0.z), __builtin_bit_cast(f16x2, one_pattern<2>()), dp, false);
-        dp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w0.w), __builtin_bit_cast(f16x2, one_pattern<3>()), dp, false);
-        dp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w1.x), __builtin_bit_cast(f16x2, one_pattern<4>()), dp, false);
-        dp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w1.y), __builtin_bit_cast(f16x2, one_pattern<5>()), dp, false);
-        dp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w1.z), __builtin_bit_cast(f16x2, one_pattern<6>()), dp, false);
-        dp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w1.w), __builtin_bit_cast(f16x2, one_pattern<7>()), dp, false);
-        uint4* dst = reinterpret_cast<uint4*>(aps + 32 * (lane + 64 * j));
-        dst[0] = w0;
-        dst[1] = w1;
+    for (int m = 0; m < MT; ++m) {
+        float dp = 0.0f;
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+            const uint4 w0 = make_uint4(a_pair<0, 0>(av[m][j]), a_pair<0, 1>(av[m][j]), a_pair<0, 2>(av[m][j]), a_pair<0, 3>(av[m][j]));
+            const uint4 w1 = make_uint4(a_pair<0, 4>(av[m][j]), a_pair<0, 5>(av[m][j]), a_pair<0, 6>(av[m][j]), a_pair<0, 7>(av[m][j]));
+            dp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w0.x), __builtin_bit_cast(f16x2, one_pattern<0>()), dp, false);
+            dp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w0.y), __builtin_bit_cast(f16x2, one_pattern<1>()), dp, false);
+            dp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w0.z), __builtin_bit_cast(f16x2, one_pattern<2>()), dp, false);
+            dp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w0.w), __builtin_bit_cast(f16x2, one_pattern<3>()), dp, false);
+            dp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w1.x), __builtin_bit_cast(f16x2, one_pattern<4>()), dp, false);
+            dp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w1.y), __builtin_bit_cast(f16x2, one_pattern<5>()), dp, false);
+            dp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w1.z), __builtin_bit_cast(f16x2, one_pattern<6>()), dp, false);
+            dp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w1.w), __builtin_bit_cast(f16x2, one_pattern<7>()), dp, false);
+            uint4* dst = reinterpret_cast<uint4*>(aps + m * kRowLds + 32 * (lane + 64 * j));
+            dst[0] = w0;
+            dst[1] = w1;
+        }
+        dp = row16_sum(dp);
+        dw[m] = (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(dp), 0)) +
+                 __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dp), 16))) +
+                (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(dp), 32)) +
+                 __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dp), 48)));
     }
-    dp = row16_sum(dp);
-    const float dw = (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(dp), 0)) +
-                      __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dp), 16))) +
-                     (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(dp), 32)) +
-                      __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dp), 48)));
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's LDS writes are complete
 
-    // 3. contract; lanes 16g read the operand's row 0, the others keep an
-    //    arbitrary value (their output rows are never stored)
+    // 3. contract; lanes 16g + m (m < M) read row m of the operand, the
+    //    others keep an arbitrary value (their output rows are never stored)
     f32x4 acc[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
     const uint32_t magic_v = vgpr_const<kMagic2>();
+    const bool a_live = MT == 1 ? i16 == 0 : i16 < M;
 #pragma unroll
     for (int s = 0; s < CSW; ++s) {
         uint4 aw[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) aw[e] = opaque_uint4();
-        if (i16 == 0) {
-            const uint4* arow = reinterpret_cast<const uint4*>(aps + (4 * s + g) * 128);
+        if (a_live) {
+            const uint4* arow = reinterpret_cast<const uint4*>(aps + (MT == 1 ? 0 : i16 * kRowLds) + (4 * s + g) * 128);
 #pragma unroll
             for (int e = 0; e < 8; ++e) aw[e] = arow[e];
         }
@@ -587,18 +604,22 @@ __global__ __launch_bounds__(1024) void ternary_gemv_m1_kernel(GemmArgs p) {
 #undef TQ_MFMA_1
     }
 
-    // 4. row 0 of each wave's partials (D removed) -> LDS; fixed-order sum
+    // 4. rows 0 .. MT-1 of each wave's partials (D removed) -> LDS;
+    //    fixed-order sum (component i of lane i16 < 16: activation row i)
     if (g == 0) {
 #pragma unroll
-        for (int r = 0; r < R; ++r) red[(wave * R + r) * 16 + i16] = acc[r][0] - dw;
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int i = 0; i < MT; ++i) red[((wave * R + r) * MT + i) * 16 + i16] = acc[r][i] - dw[i];
     }
     __syncthreads();
-    if ((int)threadIdx.x < 16 * R) {
+    if ((int)threadIdx.x < 16 * R * MT) {
         const int t = (int)threadIdx.x;
+        const int i = (t / 16) % MT;
         float sum = red[t];
-        for (int w = 1; w < W; ++w) sum += red[w * (16 * R) + t];
+        for (int w = 1; w < W; ++w) sum += red[w * (16 * R * MT) + t];
         const float bi = p.bias ? F16::to_f32(bi_bits) : 0.0f;
-        p.C[n_e] = F16::from_f32_fast(sum * f16_bits_to_f32(sc_bits) + bi);
+        if (i < M) p.C[(int64_t)i * p.N + n_e] = F16::from_f32_fast(sum * f16_bits_to_f32(sc_bits) + bi);
     }
 }
 
@@ -1445,9 +1466,13 @@ static hipError_t launch_gemv_lds_upt(const GemmArgs& a, const GemvPlan& pl, hip
 // the LDS kernel, and with CSW = 8 once that still fills the compute units.
 // Anything else runs the LDS kernel.
 struct GemvM1Plan {
-    int csw, waves, rows16;
+    int csw, waves, rows16, mt;
     size_t lds;
 };
+#ifndef TQ_TERNARY_SMALL_MAX_M
+#define TQ_TERNARY_SMALL_MAX_M 4
+#endif
+constexpr int64_t kTernarySmallMaxM = TQ_TERNARY_SMALL_MAX_M;  // largest M the small-M kernel takes
 
 #ifndef TQ_M1_R2_MIN
 #define TQ_M1_R2_MIN 3072
@@ -1455,7 +1480,7 @@ struct GemvM1Plan {
 constexpr int64_t kM1TwoBlockRows16 = TQ_M1_R2_MIN;  // 16-row blocks from which R = 2
 
 static bool gemv_m1_plan(const GemmArgs& a, GemvM1Plan* pl) {
-    if (a.bf16 || a.M != 1 || a.K % 1024 != 0 || a.N % 16 != 0) return false;
+    if (a.bf16 || a.M < 1 || a.M > kTernarySmallMaxM || a.K % 1024 != 0 || a.N % 16 != 0) return false;
     const int64_t cs = a.K / 256;
     const int c = cs > 64 ? 8 : 4;
     if (cs % c != 0 || cs / c < 4 || cs / c > 16) return false;
@@ -1467,20 +1492,33 @@ static bool gemv_m1_plan(const GemmArgs& a, GemvM1Plan* pl) {
     // 14-wave workgroup fits a compute unit; with two row-blocks each, one
     // round of workgroups covers the grid when it has at least 2 per CU.
     if (c == 8 && nrb % 2 == 0 && nrb >= 2 * (int64_t)compute_units()) pl->rows16 = 2;
-    pl->lds = (size_t)pl->waves * c * 512 + (size_t)pl->waves * pl->rows16 * 64;
+    pl->mt = a.M == 1 ? 1 : a.M == 2 ? 2 : 4;
+    // With four rows held a wave carries ~390 VALU instructions instead of
+    // ~250: it wins where the grid has few waves per SIMD (Llama-3-8B o and
+    // qkv, and down, which the streaming kernel must split along K) and loses
+    // where it has many (gate_up: 7 per SIMD, 14.0 against 10.3 us).
+    if (a.M >= 3 && nrb / pl->rows16 * pl->waves > 16 * (int64_t)compute_units()) return false;
+    pl->lds = (size_t)pl->waves * pl->mt * c * 512 + (size_t)pl->waves * pl->rows16 * pl->mt * 64;
     return pl->lds <= (size_t)kGemvLdsMaxBytes;
+}
+
+template <int R, int CSW, int MT>
+static hipError_t launch_gemv_m1_k(const GemmArgs& a, const GemvM1Plan& pl, hipStream_t s) {
+    static DeviceFlags lds_limit_set;
+    hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(&ternary_gemv_m1_kernel<R, CSW, MT>),
+                                   kGemvLdsMaxBytes, lds_limit_set);
+    if (e != hipSuccess) return e;
+    if (a.N % (16 * R) != 0 || a.K != (int64_t)pl.waves * CSW * 256 || a.M > MT) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)(a.N / (16 * R)));
+    ternary_gemv_m1_kernel<R, CSW, MT><<<grid, dim3(pl.waves * kWave), pl.lds, s>>>(a);
+    return hipGetLastError();
 }
 
 template <int R, int CSW>
 static hipError_t launch_gemv_m1(const GemmArgs& a, const GemvM1Plan& pl, hipStream_t s) {
-    static DeviceFlags lds_limit_set;
-    hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(&ternary_gemv_m1_kernel<R, CSW>),
-                                   kGemvLdsMaxBytes, lds_limit_set);
-    if (e != hipSuccess) return e;
-    if (a.N % (16 * R) != 0 || a.K != (int64_t)pl.waves * CSW * 256) return hipErrorInvalidValue;
-    const dim3 grid((unsigned)(a.N / (16 * R)));
-    ternary_gemv_m1_kernel<R, CSW><<<grid, dim3(pl.waves * kWave), pl.lds, s>>>(a);
-    return hipGetLastError();
+    if (pl.mt == 1) return launch_gemv_m1_k<R, CSW, 1>(a, pl, s);
+    if (pl.mt == 2) return launch_gemv_m1_k<R, CSW, 2>(a, pl, s);
+    return launch_gemv_m1_k<R, CSW, 4>(a, pl, s);
 }
 
 // Streaming kernel: fp16, 3 <= M <= 16, at most 32 chunk-sets (8192
@@ -1573,6 +1611,8 @@ static bool gemv_stream_plan(const GemmArgs& a, size_t ws_bytes, StreamPlan* pl)
 }
 
 size_t gemv_workspace_bytes(const GemmArgs& a) {
+    GemvM1Plan m1;
+    if (gemv_m1_plan(a, &m1)) return 0;  // the small-M kernel never splits K
     StreamPlan pl;
     if (!gemv_stream_plan(a, SIZE_MAX, &pl) || pl.S == 1) return 0;
     return (size_t)pl.S * (size_t)a.M * (size_t)a.N * sizeof(float);
@@ -1626,15 +1666,15 @@ static hipError_t launch_gemv_stream_t(const SplitArgs& sa, const StreamPlan& sp
 hipError_t launch_ternary_gemv(const GemmArgs& a, hipStream_t s) { return launch_ternary_gemv(a, nullptr, 0, s); }
 
 hipError_t launch_ternary_gemv(const GemmArgs& a, void* workspace, size_t workspace_bytes, hipStream_t s) {
-    StreamPlan sp;
-    if (gemv_stream_plan(a, workspace ? workspace_bytes : 0, &sp))
-        return launch_gemv_stream_t(SplitArgs{a, static_cast<float*>(workspace), sp.S}, sp, s);
     GemvM1Plan m1;
     if (gemv_m1_plan(a, &m1)) {
         if (m1.csw == 8 && m1.rows16 == 2) return launch_gemv_m1<2, 8>(a, m1, s);
         if (m1.csw == 8) return launch_gemv_m1<1, 8>(a, m1, s);
         return m1.rows16 == 2 ? launch_gemv_m1<2, 4>(a, m1, s) : launch_gemv_m1<1, 4>(a, m1, s);
     }
+    StreamPlan sp;
+    if (gemv_stream_plan(a, workspace ? workspace_bytes : 0, &sp))
+        return launch_gemv_stream_t(SplitArgs{a, static_cast<float*>(workspace), sp.S}, sp, s);
     GemvPlan pl;
     if (gemv_lds_plan(a, &pl)) {
         if (pl.rows16 == 2) {
@@ -1772,11 +1812,6 @@ static bool w4_use_stream(const GemmArgs& a, size_t ws_bytes, W4StreamPlan* sp) 
     return sp->S == 1 && (nrb + sp->t - 1) / sp->t >= compute_units();
 }
 
-size_t w4_gemv_workspace_bytes(const GemmArgs& a) {
-    W4StreamPlan pl;
-    if (a.M == 1 || !w4_stream_plan(a, SIZE_MAX, &pl) || pl.S == 1) return 0;
-    return (size_t)pl.S * (size_t)a.M * (size_t)a.N * sizeof(float);
-}
 
 template <int GSW, int T, int MR, bool ASYM>
 static hipError_t launch_w4_stream_k(const SplitArgs& sa, const W4StreamPlan& pl, hipStream_t s) {
@@ -1880,6 +1915,14 @@ static hipError_t launch_w4_m1_mt(const GemmArgs& a, const W4M1Plan& pl, hipStre
 template <int R, int GSW>
 static hipError_t launch_w4_m1(const GemmArgs& a, const W4M1Plan& pl, hipStream_t s) {
     return a.zeros ? launch_w4_m1_mt<R, GSW, true>(a, pl, s) : launch_w4_m1_mt<R, GSW, false>(a, pl, s);
+}
+
+size_t w4_gemv_workspace_bytes(const GemmArgs& a) {
+    W4M1Plan m1;
+    if (w4_m1_plan(a, &m1)) return 0;  // the small-M kernel never splits K
+    W4StreamPlan pl;
+    if (a.M == 1 || !w4_stream_plan(a, SIZE_MAX, &pl) || pl.S == 1) return 0;
+    return (size_t)pl.S * (size_t)a.M * (size_t)a.N * sizeof(float);
 }
 
 hipError_t launch_w4_gemv(const GemmArgs& a, void* workspace, size_t workspace_bytes, hipStream_t s) {

@@ -101,6 +101,10 @@ def test_workspace_query():
     assert wb(300, 1000, 1024) == 0                     # 16 K-steps: nothing to split
     assert wb(64, 8192, 8192, path="gemm") == 8 * 64 * 8192 * 4
     assert wb(4, 8192, 8192, path="gemv") == 0
+    # decode (M <= 16): the small-M kernel (M <= 2, and M <= 4 with few waves
+    # per SIMD) never splits; the streaming kernel may
+    assert wb(4, 4096, 14336) == 0 and wb(2, 4096, 14336) == 0
+    assert wb(5, 4096, 14336) == 7 * 5 * 4096 * 4 and wb(16, 4096, 14336) == 7 * 16 * 4096 * 4
 
 
 V = ctypes.c_void_p
@@ -138,15 +142,17 @@ def test_tq_gemm_ws_host_checks(lib):
 
 def test_w4_workspace_query():
     """W4A16 split-K workspace (fp16, 2 <= M <= 16): S fp32 partials of
-    [M, N] when the plan splits the K groups; none at M = 1, for bf16, or
-    when one pass over K is cheapest.  Off the GPU the compute-unit count
+    [M, N] when the plan splits the K groups; none where the small-M kernel
+    runs (M <= 4 on its shapes), for bf16, or when one pass over K is
+    cheapest.  Off the GPU the compute-unit count
     defaults to 256."""
     wb = _lib.w4a16_gemm_workspace_bytes
     assert wb(16, 4096, 14336) == 8 * 16 * 4096 * 4       # 112 groups -> 8 splits of 14
     assert wb(16, 57344, 8192) == 4 * 16 * 57344 * 4
     assert wb(16, 28672, 4096) == 0 and wb(16, 4096, 4096) == 0
     assert wb(1, 4096, 14336) == 0                       # M = 1 never splits
-    assert wb(2, 4096, 14336) == 8 * 2 * 4096 * 4        # M = 2 streams: 112 groups -> 8 splits of 14
+    assert wb(2, 4096, 14336) == 0                       # M = 2: the small-M kernel, no split
+    assert wb(5, 4096, 14336) == 8 * 5 * 4096 * 4        # M = 5 streams: 112 groups -> 8 splits of 14
     assert wb(16, 4096, 14336, "bf16") == 0
     assert wb(16, 4096, 14336, group_size=64) == 0
     assert wb(40, 4096, 14336) == 8 * 16 * 4096 * 4      # blocks of 16 rows, the largest block's need
