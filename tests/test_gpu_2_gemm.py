@@ -467,3 +467,32 @@ def test_w4_small_m_one_hot_and_bias(N, K, M):
     bias = synth.activations(1, N, synth.seed_for("w4smb", N, K), "f16")[0]
     C = tq.w4a16_gemm(A.to(dev), q, s, bias=bias.to(dev))
     check_close(C, A, wdq, bias=bias, label=f"W4 small-M kernel M={M} {N}x{K} with bias")
+
+
+@pytest.mark.parametrize("N,K", [(320, 4096), (4096, 14336), (1024, 28672)])
+@pytest.mark.parametrize("M", [2, 3, 4])
+def test_ternary_small_m_one_hot_and_bias(N, K, M):
+    """The ternary small-M kernel at M = 2..4 (two or four activation rows
+    held; at M = 3 the fourth re-reads the third and is not stored; K = 28672
+    holds four rows only within the LDS at M = 2, so M = 3, 4 stream): one-hot
+    rows give C[m, n] = wdq[n, k_m] bit for bit; dense rows with a bias are
+    within the tolerance; nothing is written past row M - 1."""
+    import torch
+    import bit_weight_only_tq_amd as tq
+    dev = require_gpu()
+    log(f"ternary small-M one-hot and bias M={M} N={N} K={K}")
+    codes, scale, rc, rs, wdq = _ternary(N, K, dev)
+    sets = [[0, 9, 130, K - 1], [5, 255, 1024 + 33, K // 2 + 7], [2, 64 + 3, 2048 + 100, K - 200]]
+    for ks in sets:
+        ks = ks[:M]
+        A = torch.zeros((M, K), dtype=torch.float16)
+        for m, k in enumerate(ks):
+            A[m, k] = 1.0
+        buf = torch.full((M + 1, N), -7.0, dtype=torch.float16, device=dev)
+        C = tq.tq_gemm(A.to(dev), codes, scale, out=buf[:M])
+        np.testing.assert_array_equal(bits16(C), OR.f16_bits(wdq[:, ks].T), err_msg=f"ks={ks}")
+        assert bool((buf[M] == -7.0).all())
+    A = synth.activations(M, K, synth.seed_for("tsm", M, N, K), "f16")
+    bias = synth.activations(1, N, synth.seed_for("tsmb", N, K), "f16")[0]
+    C = tq.tq_gemm(A.to(dev), codes, scale, bias=bias.to(dev))
+    check_close(C, A, wdq, bias=bias, label=f"ternary small-M M={M} {N}x{K} with bias")
