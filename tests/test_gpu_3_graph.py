@@ -10,6 +10,7 @@ pytestmark = pytest.mark.gpu
 
 @pytest.mark.parametrize("fmt,M,N,K", [
     ("ternary", 1, 4096, 4096), ("ternary", 16, 1024, 4096),
+    ("ternary", 2, 1024, 4096), ("ternary", 4, 4096, 14336),  # small-M kernel, two and four rows held
     ("ternary", 512, 1024, 4096), ("ternary", 2048, 14336, 4096),  # large M: split K (two kernels), one pass
     ("ternary", 40, 1024, 4096), ("ternary", 200, 2048, 1024),  # medium path: split K, two kernels
     ("w4a16", 4, 1024, 4096), ("w4a16", 16, 4096, 14336),  # W4: one pass; split K (two kernels)
