@@ -76,26 +76,40 @@ __device__ __forceinline__ void stage_barrier() {
 // stored straight from the accumulators instead.
 namespace v3 {
 
-constexpr int BM = 256;
 constexpr int BN = 256;
 constexpr int BK = 64;
 constexpr int kThreads = 512;
-constexpr int WM = 128, WN = 64;
-constexpr int TM = WM / 16, TN = WN / 16;
+constexpr int WN = 64;
+constexpr int TN = WN / 16;
 constexpr int kStages = 3;
-constexpr int kABytes = BM * BK * 2;                // 32 KB, unpadded (swizzled)
 constexpr int kBBytes = BN * BK / 4;                // 4 KB of codes
-constexpr int kStageBytes = kABytes + kBBytes;
 constexpr int kEpiLd = WN + 8;                      // epilogue staging row (halves)
 constexpr int kEpiRows = 32;
 constexpr int kEpiBytesPerWave = kEpiRows * kEpiLd * 2;
-constexpr size_t kLdsBytes = (size_t)kStages * kStageBytes;
-static_assert(8 * kEpiBytesPerWave + BM * 4 <= (int)kLdsBytes, "epilogue staging must fit in the ring");
 
-template <class T>
+// Block tile height: 256 rows (two waves of 128 along M), or 128 (two of 64)
+// for the last round of a grid that does not fill whole rounds.
+template <int BM_>
+struct Tile {
+    static constexpr int BM = BM_;
+    static constexpr int WM = BM / 2;               // rows per wave
+    static constexpr int TM = WM / 16;              // m-tiles per wave
+    static constexpr int AU = BM / 64;              // 1-KB activation DMA blocks per wave and stage
+    static constexpr int RS = TM / 4;               // m-tiles per wave in the row sums
+    static constexpr int kABytes = BM * BK * 2;     // unpadded (swizzled)
+    static constexpr int kStageBytes = kABytes + kBBytes;
+    static constexpr size_t kLdsBytes = (size_t)kStages * kStageBytes;
+    static_assert(8 * kEpiBytesPerWave + BM * 4 <= (int)kLdsBytes, "epilogue staging must fit in the ring");
+};
+
+template <class T, int BMT>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(SplitArgs sa) {
     typedef typename Mfma<T>::vec vec;
+    typedef Tile<BMT> G;
+    constexpr int BM = G::BM, WM = G::WM, TM = G::TM, AU = G::AU, RS = G::RS;
+    constexpr int kABytes = G::kABytes, kStageBytes = G::kStageBytes;
     const GemmArgs& p = sa.g;
+    const int64_t ldc = sa.ldc ? sa.ldc : p.N;       // row stride of C
     extern __shared__ uint4 smem_v3[];
     uint8_t* lds = reinterpret_cast<uint8_t*>(smem_v3);
     const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)smem_v3;
@@ -114,14 +128,14 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(SplitArgs sa) {
     const uint32_t mask3 = sgpr_const<0x00030003u>();
     const uint32_t mask33 = sgpr_const<0x33333333u>();
 
-    // Activation DMA: wave w fills 1-KB blocks 4w .. 4w+3 of a stage (8 rows
-    // each); lane l lands at chunk l % 8 of row l / 8, so it fetches global
-    // chunk (l % 8) ^ (l / 8) of that row.  Rows past M re-read row M-1.
+    // Activation DMA: wave w fills 1-KB blocks AU w .. AU w + AU-1 of a stage
+    // (8 rows each); lane l lands at chunk l % 8 of row l / 8, so it fetches
+    // global chunk (l % 8) ^ (l / 8) of that row.  Rows past M re-read row M-1.
     const uint16_t* a_blk = p.A + m0 * K;
-    uint32_t a_off[4];
+    uint32_t a_off[AU];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        int64_t r = 8 * (4 * wave + u) + (lane >> 3);
+    for (int u = 0; u < AU; ++u) {
+        int64_t r = 8 * (AU * wave + u) + (lane >> 3);
         if (m0 + r >= M) r = M - 1 - m0;
         a_off[u] = (uint32_t)(r * K + 8 * ((lane & 7) ^ (lane >> 3)));
     }
@@ -137,15 +151,15 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(SplitArgs sa) {
     const bool b_issuer = wave < 4;
     auto issue = [&](int kstep, int stage) {
         const int64_t k0 = (int64_t)kstep * BK;
-        const uint32_t dst = lds_base + (uint32_t)(stage * kStageBytes + 4096 * wave);
+        const uint32_t dst = lds_base + (uint32_t)(stage * kStageBytes + 1024 * AU * wave);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) dma16(a_blk + k0 + a_off[u], dst + 1024u * u);
+        for (int u = 0; u < AU; ++u) dma16(a_blk + k0 + a_off[u], dst + 1024u * u);
         if (b_issuer) dma16(b_blk + k0 / 4 + b_off, lds_base + (uint32_t)(stage * kStageBytes + kABytes + 1024 * wave));
     };
     // the stage issued before the last one has landed (per-wave DMA counts)
     auto wait_prev_stage = [&]() {
-        if (b_issuer) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
-        else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+        if (b_issuer) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(AU + 1) : "memory");
+        else asm volatile("s_waitcnt vmcnt(%0)" :: "n"(AU) : "memory");
     };
 
     f32x4 acc[TM][TN];
@@ -153,7 +167,9 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(SplitArgs sa) {
     for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float rsum[2] = {0.f, 0.f};  // row sums for m-tiles wn and wn + 4
+    float rsum[RS];  // row sums for m-tiles wn (and wn + 4 when TM = 8)
+#pragma unroll
+    for (int t = 0; t < RS; ++t) rsum[t] = 0.f;
 
     // fragment row R = wm*128 + 16i + i16 (R % 8 == i16 % 8): chunk c at
     // byte R*128 + 16*(c ^ (i16 & 7)) of a stage
@@ -198,7 +214,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(SplitArgs sa) {
                                     ((y >> 8) & mask3) | magic_v, ((y >> 12) & mask3) | magic_v);
             }
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {  // this wave's share of the row sums: m-tiles wn, wn + 4
+            for (int t = 0; t < RS; ++t) {  // this wave's share of the row sums: m-tiles wn (, wn + 4)
                 const uint4 v = *reinterpret_cast<const uint4*>(sbase + frag_base + (wn + 4 * t) * 16 * (BK * 2) + 16 * chunk);
                 float r = rsum[t];
                 r = Mfma<T>::dot2(v.x, Mfma<T>::kOnePair, r);
@@ -223,7 +239,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(SplitArgs sa) {
     // row sums -> LDS
     float* rs_lds = reinterpret_cast<float*>(lds + 8 * kEpiBytesPerWave);
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < RS; ++t) {
         float r = rsum[t];
         r += __shfl_xor(r, 16, kWave);
         r += __shfl_xor(r, 32, kWave);
@@ -260,7 +276,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(SplitArgs sa) {
         sc[j] = f16_bits_to_f32(p.scale[nc]);
         bi[j] = p.bias ? T::to_f32(p.bias[nc]) : 0.0f;
     }
-    const bool vec_ok = (N % 8) == 0;
+    const bool vec_ok = ((N | ldc) % 8) == 0;
 #pragma unroll
     for (int slab = 0; slab < TM / 2; ++slab) {
 #pragma unroll
@@ -285,12 +301,12 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(SplitArgs sa) {
             if (m >= M) continue;
             const uint4 v = *reinterpret_cast<const uint4*>(stg + row * kEpiLd + col);
             if (vec_ok && n + 8 <= N) {
-                *reinterpret_cast<uint4*>(p.C + m * N + n) = v;
+                *reinterpret_cast<uint4*>(p.C + m * ldc + n) = v;
             } else {
                 const uint16_t h[8] = {(uint16_t)v.x, (uint16_t)(v.x >> 16), (uint16_t)v.y, (uint16_t)(v.y >> 16),
                                        (uint16_t)v.z, (uint16_t)(v.z >> 16), (uint16_t)v.w, (uint16_t)(v.w >> 16)};
                 for (int e = 0; e < 8; ++e)
-                    if (n + e < N) p.C[m * N + n + e] = h[e];
+                    if (n + e < N) p.C[m * ldc + n + e] = h[e];
             }
         }
     }
@@ -950,17 +966,54 @@ hipError_t launch_splitk_reduce(const SplitArgs& sa, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <class T>
+template <class T, int BM>
 static hipError_t launch_v3(const SplitArgs& sa, hipStream_t s) {
+    typedef v3::Tile<BM> G;
     static DeviceFlags lds_limit_set;
-    hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(&v3::gemm_kernel<T>), (int)v3::kLdsBytes, lds_limit_set);
+    hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(&v3::gemm_kernel<T, BM>), (int)G::kLdsBytes, lds_limit_set);
     if (e != hipSuccess) return e;
     const GemmArgs& a = sa.g;
-    const dim3 grid((unsigned)((a.N + v3::BN - 1) / v3::BN), (unsigned)((a.M + v3::BM - 1) / v3::BM), (unsigned)sa.S);
-    v3::gemm_kernel<T><<<grid, v3::kThreads, v3::kLdsBytes, s>>>(sa);
+    const dim3 grid((unsigned)((a.N + v3::BN - 1) / v3::BN), (unsigned)((a.M + BM - 1) / BM), (unsigned)sa.S);
+    v3::gemm_kernel<T, BM><<<grid, v3::kThreads, G::kLdsBytes, s>>>(sa);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (sa.S > 1) e = launch_splitk_reduce(sa, s);
     return e;
+}
+
+// One pass over K whose 256 x 256 tiles leave the last round of workgroups
+// partly filled: the first n1 columns of 256-row tiles make whole rounds,
+// and the other columns run as 128 x 256 tiles in a second launch, which
+// writes its own columns of C (row stride N).  Returns the column split n1
+// (a multiple of 256), or 0 when the grid already fills whole rounds, the
+// remainder is more than half a round, or the shape is too small.
+int64_t gemm_tail_split(int64_t M, int64_t N, int compute_units) {
+    const int64_t cus = compute_units > 0 ? compute_units : 1;
+    const int64_t mt = (M + 255) / 256, nt = (N + v3::BN - 1) / v3::BN;
+    const int64_t tiles = mt * nt;
+    const int64_t full = tiles / cus * cus;
+    if (tiles <= cus || tiles == full || (tiles - full) * 2 > cus) return 0;
+    const int64_t n1 = full / mt;  // whole columns of tiles within the full rounds
+    if (n1 <= 0 || n1 >= nt) return 0;
+    return n1 * v3::BN;
+}
+
+template <class T>
+static hipError_t launch_v3_auto(const SplitArgs& sa, int compute_units, hipStream_t s) {
+    const GemmArgs& a = sa.g;
+    const int64_t n1 = sa.S == 1 ? gemm_tail_split(a.M, a.N, compute_units) : 0;
+    if (n1 == 0) return launch_v3<T, 256>(sa, s);
+    SplitArgs head = sa, tail = sa;
+    head.g.N = n1;
+    head.ldc = a.N;
+    tail.g.N = a.N - n1;
+    tail.ldc = a.N;
+    tail.g.wq = static_cast<const uint8_t*>(a.wq) + n1 * (a.K / 4);
+    tail.g.scale = a.scale + n1;
+    tail.g.bias = a.bias ? a.bias + n1 : nullptr;
+    tail.g.C = a.C + n1;
+    hipError_t e = launch_v3<T, 256>(head, s);
+    if (e != hipSuccess) return e;
+    return launch_v3<T, 128>(tail, s);
 }
 
 // K split of the large-M kernel.  One 256 x 256 workgroup fills a compute
@@ -972,7 +1025,7 @@ static hipError_t launch_v3(const SplitArgs& sa, hipStream_t s) {
 // 256 x 256 x 64 step at about 1 PFLOP/s over the whole chip) and the
 // partials moving at 4 TB/s; each split keeps at least 16 K-steps.
 int gemm_splits(int64_t M, int64_t N, int64_t K, int compute_units) {
-    const int64_t tiles = ((N + v3::BN - 1) / v3::BN) * ((M + v3::BM - 1) / v3::BM);
+    const int64_t tiles = ((N + v3::BN - 1) / v3::BN) * ((M + v3::Tile<256>::BM - 1) / v3::Tile<256>::BM);
     const int64_t nk = K / v3::BK;
     const int64_t cus = compute_units > 0 ? compute_units : 1;
     const double step_us = 1.5, partial_bytes_per_us = 4.0e6, launch_us = 3.0;
@@ -998,7 +1051,7 @@ hipError_t launch_ternary_gemm(const GemmArgs& a, void* workspace, size_t worksp
     // the C ABI guarantees K % 64 == 0 (whole 16-byte code chunks per row)
     SplitArgs sa{a, static_cast<float*>(workspace), gemm_splits(a.M, a.N, a.K, compute_units)};
     if (sa.S > 1 && (!workspace || workspace_bytes < gemm_workspace_bytes(a.M, a.N, a.K, compute_units))) sa.S = 1;
-    return a.bf16 ? launch_v3<BF16>(sa, s) : launch_v3<F16>(sa, s);
+    return a.bf16 ? launch_v3_auto<BF16>(sa, compute_units, s) : launch_v3_auto<F16>(sa, compute_units, s);
 }
 
 // Split count of the medium-M kernels.

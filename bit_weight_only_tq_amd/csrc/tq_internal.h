@@ -71,6 +71,7 @@ struct SplitArgs {
     float* ws;  // [S][M][N] fp32 partials, unused when S == 1
     int S;
     int scaled;  // 1: the partials already carry the weight scales (W4A16), the reduction adds only the bias
+    int64_t ldc = 0;  // row stride of C in elements (0: N); the large-M kernel's column-split launches set it
 };
 hipError_t launch_splitk_reduce(const SplitArgs& sa, hipStream_t s);  // gemm.hip
 

@@ -496,3 +496,25 @@ def test_ternary_small_m_one_hot_and_bias(N, K, M):
     bias = synth.activations(1, N, synth.seed_for("tsmb", N, K), "f16")[0]
     C = tq.tq_gemm(A.to(dev), codes, scale, bias=bias.to(dev))
     check_close(C, A, wdq, bias=bias, label=f"ternary small-M M={M} {N}x{K} with bias")
+
+
+@pytest.mark.parametrize("M,N,K,dt", [(2560, 7168, 256, "f16"), (2500, 7000, 320, "bf16"), (4096, 14336, 256, "f16")])
+def test_prefill_tail_split(M, N, K, dt):
+    """Large M whose 256 x 256 tiles leave the last round of workgroups at
+    most half full (280 and 896 tiles on 256 compute units): the first
+    columns run as 256-row tiles and the rest as 128-row tiles in a second
+    launch that writes its own columns of C; every output against the
+    oracle, with a bias, ragged M, N and K steps, and the rows past M and
+    columns past N untouched."""
+    import torch
+    import bit_weight_only_tq_amd as tq
+    dev = require_gpu()
+    log(f"prefill tail split M={M} N={N} K={K} {dt}")
+    codes, scale, rc, rs, wdq = _ternary(N, K, dev)
+    A = synth.activations(M, K, synth.seed_for("pts", M, N, K, dt), dt)
+    bias = synth.activations(1, N, synth.seed_for("ptsb", N, dt), dt)[0]
+    tdt = torch.float16 if dt == "f16" else torch.bfloat16
+    buf = torch.full((M * N + 4096,), -3.0, dtype=tdt, device=dev)
+    C = tq.tq_gemm(A.to(dev), codes, scale, bias=bias.to(dev), out=buf[:M * N].view(M, N))
+    assert bool((buf[M * N:] == -3.0).all())
+    check_close(C, A, wdq, bias=bias, label=f"prefill tail split {M}x{N}x{K} {dt}")
