@@ -1,9 +1,14 @@
-// Small-M (decode) kernels: every packed weight byte is read from HBM exactly
-// once per call and unpacked in registers; activations (a few KB) come from
-// the L2 cache.  One wave owns one output row at a time; its 64 lanes split K
-// into 16-byte chunks of packed codes, and the lane partials are combined by
-// a wave-wide reduction (DPP + lane shuffles).  No atomics, no split-K
-// across waves: results are deterministic.
+// Small-M (decode, M <= 16) kernels: every packed weight byte is read from
+// HBM exactly once per call and unpacked in registers; activations (a few KB
+// to a few hundred KB) come from the L2 cache.  The matrix-core kernels give
+// each wave a fixed share of K for 16-row blocks of weights and sum the wave
+// partials in LDS in a fixed order; the streaming kernels may also split K
+// across workgroups (with a caller workspace), and a second kernel then sums
+// the partials in a fixed order.  No atomics: results are deterministic for
+// a given shape, path and workspace size.  Dispatch: the small-M kernels for
+// M <= 2 (ternary; M <= 4 where the grid has few waves per SIMD) and M <= 4
+// (W4A16), the streaming kernels above that, the per-lane FMA kernels for
+// bf16 and shapes the others cannot take.
 //
 // Ternary layer arithmetic (page "Ternary quantized models in vLLM ...",
 // section 4): value = code - 1, out = sum_k a_k * value_k, then the row

@@ -174,8 +174,9 @@ tq_status tq_gemm_ex(const void* A, tq_dtype dt, int64_t M, int64_t N, int64_t K
  *                    `stream` is done.  Calls that may overlap must use
  *                    different workspaces.
  *   workspace_bytes  at least tq_gemm_workspace_bytes(M, N, K, dt, path)
- *                    for the split-K schedule of the decode kernels
- *                    (3 <= M <= 16, long K), TQ_PATH_STREAM_MFMA and
+ *                    for the split-K schedule of the decode streaming
+ *                    kernel (3 <= M <= 16, long K, where the small-M kernel
+ *                    does not run; the query then reports 0), TQ_PATH_STREAM_MFMA and
  *                    TQ_PATH_GEMM; with less (or NULL) they run one
  *                    workgroup per output tile over all of K - correct,
  *                    slower when the output tiles leave compute units idle.
@@ -221,10 +222,11 @@ tq_status w4a16_gemm_ex(const void* A, tq_dtype dt, int64_t M, int64_t N, int64_
  * choice (ABI 3).  The workspace rules are those of tq_gemm_ws: 16-byte
  * aligned device memory of workspace_bytes bytes or NULL, overwritten by
  * the call, not shared by calls that may overlap.  With at least
- * w4a16_gemm_workspace_bytes() bytes the fp16 small-M kernel may split the
- * K groups across workgroups (fp32 partials with the group scales applied,
- * summed in order by a second kernel, bias added there); with less it makes
- * one pass over K.  M > 16 runs as successive blocks of 16 rows that reuse
+ * w4a16_gemm_workspace_bytes() bytes the fp16 streaming kernel (M above 4,
+ * or shapes the M <= 4 kernel cannot take) may split the K groups across
+ * workgroups (fp32 partials with the group scales applied, summed in order
+ * by a second kernel, bias added there); with less it makes one pass over
+ * K.  The M <= 4 kernel never splits, and the query reports 0 for it.  M > 16 runs as successive blocks of 16 rows that reuse
  * the workspace in stream order.  Other arguments, results and errors as
  * w4a16_gemm; TQ_ERR_ALIGN for a misaligned workspace.
  */
