@@ -1560,8 +1560,12 @@ int compute_units() {
 // workgroup and fill 256 compute units instead of 224 with 8.
 static int stream_rows_per_wg(int64_t nrb, int S, int64_t cus, int tmax, int waves) {
     const int cap = tmax < waves ? tmax : waves;
+    for (int t = 1; t <= cap; ++t)
+        if ((nrb + t - 1) / t * S <= cus) return t;
+    // No count fits one round: the largest power of two within the cap (a
+    // capped count in between would only make each of the rounds longer).
     int t = 1;
-    while (t < cap && (nrb + t - 1) / t * S > cus) ++t;
+    while (2 * t <= cap) t *= 2;
     return t;
 }
 
@@ -1744,7 +1748,8 @@ static hipError_t launch_w4_mfma_w(const GemmArgs& a, hipStream_t s) {
 // W4A16 streaming plan: as the ternary one, over 128-column groups.  S
 // divides the groups, a workgroup takes at most 32 (one or two per wave, at
 // most 16 waves), a split keeps at least four; T row-blocks per workgroup
-// (at most 8 with one group per wave, 4 with two; at most the wave count);
+// (at most 8, 6 with two groups per wave and zero points; at most the wave
+// count);
 // the waves' LDS areas must fit.  The cost is the same estimate of bytes per
 // compute unit: activations (M * K/S * 2), codes, split partials, plus
 // 160 KB for the reduction launch.
@@ -1773,7 +1778,9 @@ static bool w4_stream_geometry(const GemmArgs& a, int S, int64_t cus, W4StreamPl
     pl->waves = (int)((gs + pl->gsw - 1) / pl->gsw);
     pl->mr = a.M <= 4 ? 4 : a.M <= 8 ? 8 : 16;
     const int64_t nrb = (a.N + 15) / 16;
-    pl->t = stream_rows_per_wg(nrb, S, cus, pl->gsw == 1 ? 8 : 4, pl->waves);
+    // registers: with two groups per wave and zero points, 7 or more
+    // row-blocks spill (126 VGPRs and 20 bytes of scratch at 7)
+    pl->t = stream_rows_per_wg(nrb, S, cus, (pl->gsw == 2 && a.zeros) ? 6 : 8, pl->waves);
     pl->lds = (size_t)pl->waves * w4_stream_wave_lds(pl->gsw, pl->mr, pl->t);
     return pl->lds <= (size_t)kGemvLdsMaxBytes;
 }
@@ -1820,16 +1827,20 @@ static bool w4_use_stream(const GemmArgs& a, size_t ws_bytes, W4StreamPlan* sp) 
 
 template <int GSW, int T, int MR, bool ASYM>
 static hipError_t launch_w4_stream_k(const SplitArgs& sa, const W4StreamPlan& pl, hipStream_t s) {
-    static DeviceFlags lds_limit_set;
-    hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(&w4_gemv_stream_kernel<GSW, T, MR, ASYM>),
-                                   kGemvLdsMaxBytes, lds_limit_set);
-    if (e != hipSuccess) return e;
-    if (pl.lds != (size_t)pl.waves * w4_stream_wave_lds(GSW, MR, T)) return hipErrorInvalidValue;
-    if (GSW == 2 && !w4_pairs_ok(sa.g, sa.S)) return hipErrorInvalidValue;
-    const dim3 grid((unsigned)((sa.g.N + 16 * T - 1) / (16 * T)), (unsigned)sa.S);
-    w4_gemv_stream_kernel<GSW, T, MR, ASYM><<<grid, dim3(pl.waves * kWave), pl.lds, s>>>(sa);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    return sa.S > 1 ? launch_splitk_reduce(sa, s) : hipSuccess;
+    if constexpr (ASYM && GSW == 2 && T > 6) {
+        return hipErrorInvalidValue;  // the plan never asks for it (registers)
+    } else {
+        static DeviceFlags lds_limit_set;
+        hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(&w4_gemv_stream_kernel<GSW, T, MR, ASYM>),
+                                       kGemvLdsMaxBytes, lds_limit_set);
+        if (e != hipSuccess) return e;
+        if (pl.lds != (size_t)pl.waves * w4_stream_wave_lds(GSW, MR, T)) return hipErrorInvalidValue;
+        if (GSW == 2 && !w4_pairs_ok(sa.g, sa.S)) return hipErrorInvalidValue;
+        const dim3 grid((unsigned)((sa.g.N + 16 * T - 1) / (16 * T)), (unsigned)sa.S);
+        w4_gemv_stream_kernel<GSW, T, MR, ASYM><<<grid, dim3(pl.waves * kWave), pl.lds, s>>>(sa);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        return sa.S > 1 ? launch_splitk_reduce(sa, s) : hipSuccess;
+    }
 }
 
 template <int GSW, int T, int MR>
@@ -1855,7 +1866,11 @@ static hipError_t launch_w4_stream_mr(const SplitArgs& sa, const W4StreamPlan& p
         case 1: return launch_w4_stream<2, 1, MR>(sa, pl, s);
         case 2: return launch_w4_stream<2, 2, MR>(sa, pl, s);
         case 3: return launch_w4_stream<2, 3, MR>(sa, pl, s);
-        default: return launch_w4_stream<2, 4, MR>(sa, pl, s);
+        case 4: return launch_w4_stream<2, 4, MR>(sa, pl, s);
+        case 5: return launch_w4_stream<2, 5, MR>(sa, pl, s);
+        case 6: return launch_w4_stream<2, 6, MR>(sa, pl, s);
+        case 7: return launch_w4_stream<2, 7, MR>(sa, pl, s);
+        default: return launch_w4_stream<2, 8, MR>(sa, pl, s);
     }
 }
 
