@@ -16,6 +16,8 @@
 // and the row sums of A are accumulated alongside with dot2, so the
 // correction is one FMA per output.
 
+#include <type_traits>
+
 #include "tq_device.h"
 #include "tq_internal.h"
 
@@ -66,10 +68,13 @@ __device__ __forceinline__ void stage_barrier() {
 // Codes are unpacked in registers into natural-order fp16 / bf16 pairs
 // (f_2j, f_2j+1):  E = x & 0x33333333 (even fields), O = (x >> 2) & 0x33333333
 // (odd fields), Y = byte-merge(E, O) per half dword, pair j = ((Y >> 4j) &
-// 0x00030003) | MAGIC.  Block tile 256 x 256, K-step 64, eight waves (2 x 4)
-// of 128 x 64 outputs; MFMA s of a K-step (s = 0, 1) takes 8-column chunk
-// 2g + s for lane group g.  Row sums of A for the bias correction are split
-// over the four waves sharing a row block (m-tiles wn and wn + 4).  The
+// 0x00030003) | MAGIC; in fp16 one packed subtract of 1025 then gives the
+// ternary value c - 1 itself.  Block tile 256 x 256 (128 x 256 for the
+// last round of an unbalanced grid), K-step 64, eight waves (2 x 4) of
+// 128 x 64 (64 x 64) outputs; MFMA s of a K-step (s = 0, 1) takes 8-column
+// chunk 2g + s for lane group g.  In bf16 the row sums of A for the MAGIC
+// correction are split over the four waves sharing a row block (m-tiles wn
+// and wn + 4).  The
 // epilogue stages each wave's outputs through LDS so that every lane stores
 // 16 contiguous bytes.  With a K split (blockIdx.z = split z of S, K-steps
 // [z*nk/S, (z+1)*nk/S)) the fp32 partials (row-sum correction applied) are
@@ -110,6 +115,17 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(SplitArgs sa) {
     constexpr int kABytes = G::kABytes, kStageBytes = G::kStageBytes;
     const GemmArgs& p = sa.g;
     const int64_t ldc = sa.ldc ? sa.ldc : p.N;       // row stride of C
+    // fp16: the operand holds the ternary value itself, (1024 + c) - 1025 =
+    // c - 1 in one packed fp16 subtract per pair (exact), so no row sums and
+    // no correction are needed, and the matrix multipliers see +-1 and 0
+    // instead of 1024 + c (less switching on a power-limited part, and no
+    // cancellation of 1025 sum a in fp32).  bf16 keeps MAGIC + c and the
+    // row-sum correction.
+    constexpr bool kExactB = std::is_same<T, F16>::value;
+    auto bfix = [](uint32_t v) -> uint32_t {
+        if constexpr (kExactB) return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, v) + __builtin_bit_cast(f16x2, 0xE401E401u));
+        else return v;
+    };
     extern __shared__ uint4 smem_v3[];
     uint8_t* lds = reinterpret_cast<uint8_t*>(smem_v3);
     const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)smem_v3;
@@ -210,11 +226,11 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(SplitArgs sa) {
 #pragma unroll
             for (int j = 0; j < TN; ++j) {
                 const uint32_t y = __builtin_amdgcn_perm(O[j], E[j], s ? 0x07060302u : 0x05040100u);
-                bop[j] = make_uint4((y & mask3) | magic_v, ((y >> 4) & mask3) | magic_v,
-                                    ((y >> 8) & mask3) | magic_v, ((y >> 12) & mask3) | magic_v);
+                bop[j] = make_uint4(bfix((y & mask3) | magic_v), bfix(((y >> 4) & mask3) | magic_v),
+                                    bfix(((y >> 8) & mask3) | magic_v), bfix(((y >> 12) & mask3) | magic_v));
             }
 #pragma unroll
-            for (int t = 0; t < RS; ++t) {  // this wave's share of the row sums: m-tiles wn (, wn + 4)
+            for (int t = 0; t < (kExactB ? 0 : RS); ++t) {  // this wave's share of the row sums: m-tiles wn (, wn + 4)
                 const uint4 v = *reinterpret_cast<const uint4*>(sbase + frag_base + (wn + 4 * t) * 16 * (BK * 2) + 16 * chunk);
                 float r = rsum[t];
                 r = Mfma<T>::dot2(v.x, Mfma<T>::kOnePair, r);
@@ -256,7 +272,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(SplitArgs sa) {
                 const int row = wm * WM + 16 * i + 4 * g + r;
                 const int64_t m = m0 + row;
                 if (m >= M) continue;
-                const float rs = Mfma<T>::kBias * rs_lds[row];
+                const float rs = kExactB ? 0.0f : Mfma<T>::kBias * rs_lds[row];
 #pragma unroll
                 for (int j = 0; j < TN; ++j) {
                     const int64_t n = n0 + wn * WN + 16 * j + i16;
@@ -288,7 +304,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(SplitArgs sa) {
                 const float rs = rs_lds[wm * WM + 16 * i + 4 * g + r];
 #pragma unroll
                 for (int j = 0; j < TN; ++j)
-                    stg[row * kEpiLd + 16 * j + i16] = T::from_f32_fast((acc[i][j][r] - Mfma<T>::kBias * rs) * sc[j] + bi[j]);
+                    stg[row * kEpiLd + 16 * j + i16] = T::from_f32_fast((acc[i][j][r] - (kExactB ? 0.0f : Mfma<T>::kBias * rs)) * sc[j] + bi[j]);
             }
         }
         // each lane stores 16 contiguous bytes: row lane/8 + 8q, columns 8*(lane%8) .. +7
