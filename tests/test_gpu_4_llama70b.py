@@ -44,7 +44,7 @@ def _packed(N, K, dev):
 
 
 @pytest.mark.parametrize("N,K", SHAPES_70B)
-@pytest.mark.parametrize("M", [1, 32, 64])
+@pytest.mark.parametrize("M", [1, 2, 32, 64])
 def test_ternary_70b(N, K, M):
     import torch
     import bit_weight_only_tq_amd as tq
