@@ -143,7 +143,7 @@ def percentiles(ms):
     return {"p10": round(pick(0.1), 4), "p50": round(pick(0.5), 4), "p90": round(pick(0.9), 4)}
 
 
-def run_decode(args, dev, fused, graph, model="8b", layers=None, steps=None, M=1):
+def run_decode(args, dev, fused, graph, model="8b", layers=None, steps=None, M=1, dt="f16"):
     import torch
     import bit_weight_only_tq_amd as tq
     import synth
@@ -151,8 +151,9 @@ def run_decode(args, dev, fused, graph, model="8b", layers=None, steps=None, M=1
     layers = args.layers if layers is None else layers
     steps = args.steps if steps is None else steps
     mats = build_decode(layers, dev, fused, model)
-    xs = {K: synth.activations_device(M, K, synth.seed_for("benchx", K, M), "f16", dev) for K in {m[2] for m in mats}}
-    outs = [torch.empty((M, m[1]), dtype=torch.float16, device=dev) for m in mats]
+    xs = {K: synth.activations_device(M, K, synth.seed_for("benchx", K, M), dt, dev) for K in {m[2] for m in mats}}
+    odt = torch.float16 if dt == "f16" else torch.bfloat16
+    outs = [torch.empty((M, m[1]), dtype=odt, device=dev) for m in mats]
 
     def step():
         for i, (name, N, K, codes, scale) in enumerate(mats):
@@ -300,12 +301,13 @@ def run_medium(dev, copies=8, iters=16):
     return res
 
 
-def run_decode_m(args, dev, graph, Ms=(4, 16)):
+def run_decode_m(args, dev, graph, Ms=(4, 16), dt="f16"):
     """Llama-3-8B ternary decode step (32 layers, fused qkv / gate_up) at
     several activation rows M."""
-    res = {"metric": "HBM GB/s ternary GEMV, Llama-3-8B decode (32 layers, fused qkv / gate_up)", "unit": "GB/s"}
+    res = {"metric": f"HBM GB/s ternary GEMV, Llama-3-8B decode (32 layers, fused qkv / gate_up), {dt} activations",
+           "unit": "GB/s"}
     for M in Ms:
-        d = run_decode(args, dev, True, graph, M=M)
+        d = run_decode(args, dev, True, graph, M=M, dt=dt)
         res[f"M{M}"] = {"value": round(d["packed_gbs"], 1), "frac_of_peak": round(d["packed_gbs"] / HBM_PEAK_GBS, 4),
                         "ms_per_step": round(d["ms_per_step"], 4), "step_ms_percentiles": d["step_ms"],
                         "avg_launch_us": round(d["avg_launch_us"], 3), "alg_gbs": round(d["alg_gbs"], 1)}
@@ -524,7 +526,8 @@ def main():
         print(json.dumps({"attribution": run_attrib(dev)}), flush=True)
         return
     if args.mode == "decodem":
-        print(json.dumps({"decode_m": run_decode_m(args, dev, not args.no_graph)}), flush=True)
+        print(json.dumps({"decode_m": run_decode_m(args, dev, not args.no_graph),
+                          "decode_bf16": run_decode_m(args, dev, not args.no_graph, Ms=(1, 2), dt="bf16")}), flush=True)
         return
     if args.mode == "decode70b":
         print(json.dumps({"decode_70b": run_decode_70b(args, dev)}), flush=True)
@@ -583,6 +586,8 @@ def main():
                                      "avg_launch_us": round(u["avg_launch_us"], 3)}
         log("decode, M = 4 and 16")
         out["decode_m"] = run_decode_m(args, dev, graph)
+        log("decode, bf16 activations, M = 1 and 2")
+        out["decode_bf16"] = run_decode_m(args, dev, graph, Ms=(1, 2), dt="bf16")
         log("decode time split")
         out["attribution"] = run_attrib(dev)
         log("decode, Llama-3-70B, 80 layers")

@@ -6,9 +6,9 @@
 // across workgroups (with a caller workspace), and a second kernel then sums
 // the partials in a fixed order.  No atomics: results are deterministic for
 // a given shape, path and workspace size.  Dispatch: the small-M kernels for
-// M <= 2 (ternary; M <= 4 where the grid has few waves per SIMD) and M <= 4
-// (W4A16), the streaming kernels above that, the per-lane FMA kernels for
-// bf16 and shapes the others cannot take.
+// M <= 2 (ternary; M <= 4 where the grid has few waves per SIMD, and always
+// for bf16) and M <= 4 (W4A16, fp16), the streaming kernels above that (fp16),
+// the per-lane FMA kernels for the shapes the others cannot take.
 //
 // Ternary layer arithmetic (page "Ternary quantized models in vLLM ...",
 // section 4): value = code - 1, out = sum_k a_k * value_k, then the row
@@ -478,7 +478,80 @@ __global__ __launch_bounds__(1024) void ternary_gemv_lds_kernel(GemmArgs p) {
     }
 }
 
-// Small-M form of the kernel above (fp16, M <= 4, K a multiple of 256 CSW,
+// bf16 form of the a' unpack for the small-M kernel below.  bf16 has 7
+// fraction bits, so three 2-bit fields fit the mantissa of 128.0 (0x4300,
+// unit in the last place 1): fields 0..2 of a code dword x are masked in
+// place, fields 3..5 from x >> 6 and fields 6, 7 from x >> 12, each at bits
+// 2s of its source with s = I, I - 3 or I - 6 and so scaled by 4^s (the
+// partner field I + 8 sits 16 bits higher); the activations are paired and
+// pre-scaled by 1 / 4^s to match.  There is no packed bf16 multiply, so the
+// pre-scale goes through fp32 (exact: a power of two) and back.
+constexpr uint32_t kMagicBf2 = 0x43004300u;  // (128.0, 128.0) as bf16
+
+template <int I> constexpr int bf_shift() { return I < 3 ? I : I < 6 ? I - 3 : I - 6; }
+
+template <int I>
+__device__ __forceinline__ uint32_t bf_field_pair(uint32_t x, uint32_t y, uint32_t z, uint32_t magic_v) {
+    constexpr uint32_t mask = 0x00030003u << (2 * bf_shift<I>());
+    if constexpr (I < 3) return (x & sgpr_const<mask>()) | magic_v;
+    else if constexpr (I < 6) return (y & sgpr_const<mask>()) | magic_v;
+    else return (z & sgpr_const<mask>()) | magic_v;
+}
+
+// a' pair for field I: (a[I], a[I+8]) / 4^s(I), bf16 bits, from the 16
+// columns of one unit (av[0]: columns 0..7, av[1]: 8..15).
+template <int I>
+__device__ __forceinline__ uint32_t bf_a_pair(const uint4 av[8]) {
+    constexpr int c = I / 2;
+    const uint32_t lo = c == 0 ? av[0].x : c == 1 ? av[0].y : c == 2 ? av[0].z : av[0].w;
+    const uint32_t hi = c == 0 ? av[1].x : c == 1 ? av[1].y : c == 2 ? av[1].z : av[1].w;
+    const uint32_t pr = __builtin_amdgcn_perm(hi, lo, (I & 1) ? 0x07060302u : 0x05040100u);
+    constexpr int s = bf_shift<I>();
+    if constexpr (s == 0) {
+        return pr;
+    } else {
+        constexpr float f = 1.0f / (float)(1 << (2 * s));
+        const float a0 = __uint_as_float(pr << 16) * f;
+        const float a1 = __uint_as_float(pr & 0xFFFF0000u) * f;
+        return __builtin_bit_cast(uint32_t, bf16x2{(__bf16)a0, (__bf16)a1});
+    }
+}
+
+// (128 + 4^s) in both bf16 halves: the code-01 value of field I
+template <int I>
+__device__ __forceinline__ constexpr uint32_t bf_one_pattern() {
+    constexpr uint32_t v = 0x4300u + (1u << (2 * bf_shift<I>()));
+    return v | (v << 16);
+}
+
+// Field pair, a' pair, code-01 dot product and matrix-core step of the
+// small-M kernel for activation type T.
+template <class T, int I>
+__device__ __forceinline__ uint32_t sm_field_pair(uint32_t x, uint32_t y, uint32_t z, uint32_t magic_v) {
+    if constexpr (std::is_same<T, F16>::value) return field_pair<I>(x, y, magic_v);
+    else return bf_field_pair<I>(x, y, z, magic_v);
+}
+template <class T, int I>
+__device__ __forceinline__ uint32_t sm_a_pair(const uint4 av[8]) {
+    if constexpr (std::is_same<T, F16>::value) return a_pair<0, I>(av);
+    else return bf_a_pair<I>(av);
+}
+template <class T, int I>
+__device__ __forceinline__ float sm_dot_one(uint32_t pair, float acc) {
+    if constexpr (std::is_same<T, F16>::value)
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pair), __builtin_bit_cast(f16x2, one_pattern<I>()), acc, false);
+    else
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), __builtin_bit_cast(bf16x2, bf_one_pattern<I>()), acc, false);
+}
+template <class T>
+__device__ __forceinline__ f32x4 sm_mma(uint4 a, uint4 b, f32x4 c) {
+    if constexpr (std::is_same<T, F16>::value)
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// Small-M form of the kernel above (fp16 or bf16, M <= 4, K a multiple of 256 CSW,
 // N a multiple of 16 R, W = K / (256 CSW) waves), with MT in {1, 2, 4}
 // activation rows held at compile time (rows M .. MT-1 re-read row M-1 and
 // are never stored):
@@ -492,7 +565,7 @@ __global__ __launch_bounds__(1024) void ternary_gemv_lds_kernel(GemmArgs p) {
 // The bias is read from a valid address whether or not one is given, so the
 // load needs no branch (a branch there makes the compiler wait for every
 // outstanding load, codes included, before it).
-template <int R, int CSW, int MT>
+template <class T, int R, int CSW, int MT>
 __global__ __launch_bounds__(1024) void ternary_gemv_m1_kernel(GemmArgs p) {
     extern __shared__ uint4 smem[];
     constexpr int U = CSW / 4;            // 16-column activation units per lane and row
@@ -548,16 +621,16 @@ __global__ __launch_bounds__(1024) void ternary_gemv_m1_kernel(GemmArgs p) {
         float dp = 0.0f;
 #pragma unroll
         for (int j = 0; j < U; ++j) {
-            const uint4 w0 = make_uint4(a_pair<0, 0>(av[m][j]), a_pair<0, 1>(av[m][j]), a_pair<0, 2>(av[m][j]), a_pair<0, 3>(av[m][j]));
-            const uint4 w1 = make_uint4(a_pair<0, 4>(av[m][j]), a_pair<0, 5>(av[m][j]), a_pair<0, 6>(av[m][j]), a_pair<0, 7>(av[m][j]));
-            dp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w0.x), __builtin_bit_cast(f16x2, one_pattern<0>()), dp, false);
-            dp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w0.y), __builtin_bit_cast(f16x2, one_pattern<1>()), dp, false);
-            dp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w0.z), __builtin_bit_cast(f16x2, one_pattern<2>()), dp, false);
-            dp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w0.w), __builtin_bit_cast(f16x2, one_pattern<3>()), dp, false);
-            dp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w1.x), __builtin_bit_cast(f16x2, one_pattern<4>()), dp, false);
-            dp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w1.y), __builtin_bit_cast(f16x2, one_pattern<5>()), dp, false);
-            dp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w1.z), __builtin_bit_cast(f16x2, one_pattern<6>()), dp, false);
-            dp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w1.w), __builtin_bit_cast(f16x2, one_pattern<7>()), dp, false);
+            const uint4 w0 = make_uint4(sm_a_pair<T, 0>(av[m][j]), sm_a_pair<T, 1>(av[m][j]), sm_a_pair<T, 2>(av[m][j]), sm_a_pair<T, 3>(av[m][j]));
+            const uint4 w1 = make_uint4(sm_a_pair<T, 4>(av[m][j]), sm_a_pair<T, 5>(av[m][j]), sm_a_pair<T, 6>(av[m][j]), sm_a_pair<T, 7>(av[m][j]));
+            dp = sm_dot_one<T, 0>(w0.x, dp);
+            dp = sm_dot_one<T, 1>(w0.y, dp);
+            dp = sm_dot_one<T, 2>(w0.z, dp);
+            dp = sm_dot_one<T, 3>(w0.w, dp);
+            dp = sm_dot_one<T, 4>(w1.x, dp);
+            dp = sm_dot_one<T, 5>(w1.y, dp);
+            dp = sm_dot_one<T, 6>(w1.z, dp);
+            dp = sm_dot_one<T, 7>(w1.w, dp);
             uint4* dst = reinterpret_cast<uint4*>(aps + m * kRowLds + 32 * (lane + 64 * j));
             dst[0] = w0;
             dst[1] = w1;
@@ -575,7 +648,8 @@ __global__ __launch_bounds__(1024) void ternary_gemv_m1_kernel(GemmArgs p) {
     f32x4 acc[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const uint32_t magic_v = vgpr_const<kMagic2>();
+    constexpr bool kBf = std::is_same<T, BF16>::value;
+    const uint32_t magic_v = vgpr_const<kBf ? kMagicBf2 : kMagic2>();
     const bool a_live = MT == 1 ? i16 == 0 : i16 < M;
 #pragma unroll
     for (int s = 0; s < CSW; ++s) {
@@ -589,13 +663,14 @@ __global__ __launch_bounds__(1024) void ternary_gemv_m1_kernel(GemmArgs p) {
         }
 #define TQ_MFMA_1(D, I0)                                                                              \
     {                                                                                                 \
-        const f16x8 aop = __builtin_bit_cast(f16x8, aw[2 * (D) + (I0) / 4]);                          \
+        const uint4 aop = aw[2 * (D) + (I0) / 4];                                                     \
         _Pragma("unroll") for (int r = 0; r < R; ++r) {                                               \
             const uint32_t x = dword_of(q[s][r], D);                                                  \
-            const uint32_t y = x >> 10;                                                               \
-            const uint4 bw = make_uint4(field_pair<I0>(x, y, magic_v), field_pair<I0 + 1>(x, y, magic_v), \
-                                        field_pair<I0 + 2>(x, y, magic_v), field_pair<I0 + 3>(x, y, magic_v)); \
-            acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, __builtin_bit_cast(f16x8, bw), acc[r], 0, 0, 0); \
+            const uint32_t y = x >> (kBf ? 6 : 10);                                                   \
+            const uint32_t z = x >> 12;                                                               \
+            const uint4 bw = make_uint4(sm_field_pair<T, I0>(x, y, z, magic_v), sm_field_pair<T, I0 + 1>(x, y, z, magic_v), \
+                                        sm_field_pair<T, I0 + 2>(x, y, z, magic_v), sm_field_pair<T, I0 + 3>(x, y, z, magic_v)); \
+            acc[r] = sm_mma<T>(aop, bw, acc[r]);                                                      \
         }                                                                                             \
     }
         TQ_MFMA_1(0, 0)
@@ -623,8 +698,8 @@ __global__ __launch_bounds__(1024) void ternary_gemv_m1_kernel(GemmArgs p) {
         const int i = (t / 16) % MT;
         float sum = red[t];
         for (int w = 1; w < W; ++w) sum += red[w * (16 * R * MT) + t];
-        const float bi = p.bias ? F16::to_f32(bi_bits) : 0.0f;
-        if (i < M) p.C[(int64_t)i * p.N + n_e] = F16::from_f32_fast(sum * f16_bits_to_f32(sc_bits) + bi);
+        const float bi = p.bias ? T::to_f32(bi_bits) : 0.0f;
+        if (i < M) p.C[(int64_t)i * p.N + n_e] = T::from_f32_fast(sum * f16_bits_to_f32(sc_bits) + bi);
     }
 }
 
@@ -1485,7 +1560,7 @@ constexpr int64_t kTernarySmallMaxM = TQ_TERNARY_SMALL_MAX_M;  // largest M the 
 constexpr int64_t kM1TwoBlockRows16 = TQ_M1_R2_MIN;  // 16-row blocks from which R = 2
 
 static bool gemv_m1_plan(const GemmArgs& a, GemvM1Plan* pl) {
-    if (a.bf16 || a.M < 1 || a.M > kTernarySmallMaxM || a.K % 1024 != 0 || a.N % 16 != 0) return false;
+    if (a.M < 1 || a.M > kTernarySmallMaxM || a.K % 1024 != 0 || a.N % 16 != 0) return false;
     const int64_t cs = a.K / 256;
     const int c = cs > 64 ? 8 : 4;
     if (cs % c != 0 || cs / c < 4 || cs / c > 16) return false;
@@ -1502,28 +1577,35 @@ static bool gemv_m1_plan(const GemmArgs& a, GemvM1Plan* pl) {
     // ~250: it wins where the grid has few waves per SIMD (Llama-3-8B o and
     // qkv, and down, which the streaming kernel must split along K) and loses
     // where it has many (gate_up: 7 per SIMD, 14.0 against 10.3 us).
-    if (a.M >= 3 && nrb / pl->rows16 * pl->waves > 16 * (int64_t)compute_units()) return false;
+    // (bf16 has no streaming kernel: there the alternative is the per-lane
+    // FMA kernel, so the small-M kernel takes every M <= 4)
+    if (!a.bf16 && a.M >= 3 && nrb / pl->rows16 * pl->waves > 16 * (int64_t)compute_units()) return false;
     pl->lds = (size_t)pl->waves * pl->mt * c * 512 + (size_t)pl->waves * pl->rows16 * pl->mt * 64;
     return pl->lds <= (size_t)kGemvLdsMaxBytes;
 }
 
-template <int R, int CSW, int MT>
+template <class T, int R, int CSW, int MT>
 static hipError_t launch_gemv_m1_k(const GemmArgs& a, const GemvM1Plan& pl, hipStream_t s) {
     static DeviceFlags lds_limit_set;
-    hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(&ternary_gemv_m1_kernel<R, CSW, MT>),
+    hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(&ternary_gemv_m1_kernel<T, R, CSW, MT>),
                                    kGemvLdsMaxBytes, lds_limit_set);
     if (e != hipSuccess) return e;
     if (a.N % (16 * R) != 0 || a.K != (int64_t)pl.waves * CSW * 256 || a.M > MT) return hipErrorInvalidValue;
     const dim3 grid((unsigned)(a.N / (16 * R)));
-    ternary_gemv_m1_kernel<R, CSW, MT><<<grid, dim3(pl.waves * kWave), pl.lds, s>>>(a);
+    ternary_gemv_m1_kernel<T, R, CSW, MT><<<grid, dim3(pl.waves * kWave), pl.lds, s>>>(a);
     return hipGetLastError();
+}
+
+template <class T, int R, int CSW>
+static hipError_t launch_gemv_m1_t(const GemmArgs& a, const GemvM1Plan& pl, hipStream_t s) {
+    if (pl.mt == 1) return launch_gemv_m1_k<T, R, CSW, 1>(a, pl, s);
+    if (pl.mt == 2) return launch_gemv_m1_k<T, R, CSW, 2>(a, pl, s);
+    return launch_gemv_m1_k<T, R, CSW, 4>(a, pl, s);
 }
 
 template <int R, int CSW>
 static hipError_t launch_gemv_m1(const GemmArgs& a, const GemvM1Plan& pl, hipStream_t s) {
-    if (pl.mt == 1) return launch_gemv_m1_k<R, CSW, 1>(a, pl, s);
-    if (pl.mt == 2) return launch_gemv_m1_k<R, CSW, 2>(a, pl, s);
-    return launch_gemv_m1_k<R, CSW, 4>(a, pl, s);
+    return a.bf16 ? launch_gemv_m1_t<BF16, R, CSW>(a, pl, s) : launch_gemv_m1_t<F16, R, CSW>(a, pl, s);
 }
 
 // Streaming kernel: fp16, 3 <= M <= 16, at most 32 chunk-sets (8192

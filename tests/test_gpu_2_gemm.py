@@ -93,26 +93,30 @@ M1_SHAPES = [(320, 4096), (4096, 14336), (1024, 28672), (49152, 4096)]
 
 
 @pytest.mark.parametrize("N,K", M1_SHAPES)
-def test_m1_one_hot_and_bias(N, K):
-    """The M = 1 decode kernel: a one-hot row e_k gives C[0, n] = wdq[n, k]
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_m1_one_hot_and_bias(N, K, dt):
+    """The M = 1 decode kernel (fp16 and bf16 forms: fields masked into the
+    mantissa of 1024 or of 128): a one-hot row e_k gives C[0, n] = wdq[n, k]
     bit for bit, for columns k in the first and last chunk of several waves
     and at every code-field position; a dense row with a bias is within the
     tolerance."""
     import torch
     import bit_weight_only_tq_amd as tq
     dev = require_gpu()
-    log(f"M=1 kernel one-hot and bias N={N} K={K}")
+    log(f"M=1 kernel one-hot and bias N={N} K={K} {dt}")
     codes, scale, rc, rs, wdq = _ternary(N, K, dev)
+    tdt = torch.float16 if dt == "f16" else torch.bfloat16
+    to_bits = OR.f16_bits if dt == "f16" else OR.bf16_bits
     ks = sorted({0, 5, 9, 14, 255, 256 + 77, 1023, 1024 + 130, 2048 + 3, K // 2 + 31, K - 257, K - 8, K - 1})
     for k in ks:
-        A = torch.zeros((1, K), dtype=torch.float16)
+        A = torch.zeros((1, K), dtype=tdt)
         A[0, k] = 1.0
         C = tq.tq_gemm(A.to(dev), codes, scale, path="gemv")
-        np.testing.assert_array_equal(bits16(C)[0], OR.f16_bits(wdq[:, k]), err_msg=f"k={k}")
-    A = synth.activations(1, K, synth.seed_for("m1", N, K), "f16")
-    bias = synth.activations(1, N, synth.seed_for("m1b", N, K), "f16")[0]
+        np.testing.assert_array_equal(bits16(C)[0], to_bits(wdq[:, k]), err_msg=f"k={k}")
+    A = synth.activations(1, K, synth.seed_for("m1", N, K, dt), dt)
+    bias = synth.activations(1, N, synth.seed_for("m1b", N, K, dt), dt)[0]
     C = tq.tq_gemm(A.to(dev), codes, scale, bias=bias.to(dev))
-    check_close(C, A, wdq, bias=bias, label=f"M=1 kernel {N}x{K} with bias")
+    check_close(C, A, wdq, bias=bias, label=f"M=1 kernel {N}x{K} {dt} with bias")
 
 
 # Streaming decode kernels with 3, 5, 6 and 7 row-blocks per workgroup: the
@@ -471,31 +475,35 @@ def test_w4_small_m_one_hot_and_bias(N, K, M):
 
 @pytest.mark.parametrize("N,K", [(320, 4096), (4096, 14336), (1024, 28672)])
 @pytest.mark.parametrize("M", [2, 3, 4])
-def test_ternary_small_m_one_hot_and_bias(N, K, M):
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_ternary_small_m_one_hot_and_bias(N, K, M, dt):
     """The ternary small-M kernel at M = 2..4 (two or four activation rows
     held; at M = 3 the fourth re-reads the third and is not stored; K = 28672
-    holds four rows only within the LDS at M = 2, so M = 3, 4 stream): one-hot
+    holds four rows only within the LDS at M = 2, so M = 3, 4 stream in fp16;
+    bf16 has no streaming kernel and stays on the small-M kernel): one-hot
     rows give C[m, n] = wdq[n, k_m] bit for bit; dense rows with a bias are
     within the tolerance; nothing is written past row M - 1."""
     import torch
     import bit_weight_only_tq_amd as tq
     dev = require_gpu()
-    log(f"ternary small-M one-hot and bias M={M} N={N} K={K}")
+    log(f"ternary small-M one-hot and bias M={M} N={N} K={K} {dt}")
     codes, scale, rc, rs, wdq = _ternary(N, K, dev)
+    tdt = torch.float16 if dt == "f16" else torch.bfloat16
+    to_bits = OR.f16_bits if dt == "f16" else OR.bf16_bits
     sets = [[0, 9, 130, K - 1], [5, 255, 1024 + 33, K // 2 + 7], [2, 64 + 3, 2048 + 100, K - 200]]
     for ks in sets:
         ks = ks[:M]
-        A = torch.zeros((M, K), dtype=torch.float16)
+        A = torch.zeros((M, K), dtype=tdt)
         for m, k in enumerate(ks):
             A[m, k] = 1.0
-        buf = torch.full((M + 1, N), -7.0, dtype=torch.float16, device=dev)
+        buf = torch.full((M + 1, N), -7.0, dtype=tdt, device=dev)
         C = tq.tq_gemm(A.to(dev), codes, scale, out=buf[:M])
-        np.testing.assert_array_equal(bits16(C), OR.f16_bits(wdq[:, ks].T), err_msg=f"ks={ks}")
+        np.testing.assert_array_equal(bits16(C), to_bits(wdq[:, ks].T), err_msg=f"ks={ks}")
         assert bool((buf[M] == -7.0).all())
-    A = synth.activations(M, K, synth.seed_for("tsm", M, N, K), "f16")
-    bias = synth.activations(1, N, synth.seed_for("tsmb", N, K), "f16")[0]
+    A = synth.activations(M, K, synth.seed_for("tsm", M, N, K, dt), dt)
+    bias = synth.activations(1, N, synth.seed_for("tsmb", N, K, dt), dt)[0]
     C = tq.tq_gemm(A.to(dev), codes, scale, bias=bias.to(dev))
-    check_close(C, A, wdq, bias=bias, label=f"ternary small-M M={M} {N}x{K} with bias")
+    check_close(C, A, wdq, bias=bias, label=f"ternary small-M M={M} {N}x{K} {dt} with bias")
 
 
 @pytest.mark.parametrize("M,N,K,dt", [(2560, 7168, 256, "f16"), (2500, 7000, 320, "bf16"), (4096, 14336, 256, "f16")])
