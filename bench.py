@@ -204,7 +204,7 @@ def w4_act_bytes(M, N, K):
     return w4_bytes(M, N, K) + N * (K // 128) + 4 * M * K
 
 
-def run_w4_decode(args, dev, Ms=(1, 4, 16), act_order=False):
+def run_w4_decode(args, dev, Ms=(1, 4, 16), act_order=False, dt="f16"):
     """Llama-3-8B decode step with W4A16 weights, fused layout, graph replay;
     act_order: zero points and activation-order groups (gather + kernel)."""
     import torch
@@ -225,11 +225,13 @@ def run_w4_decode(args, dev, Ms=(1, 4, 16), act_order=False):
     torch.cuda.synchronize()
     packed = sum(m[2].numel() * 4 + m[3].numel() * 2 + (m[4].numel() if act_order else 0) for m in mats)
     what = "W4A16 with zero points and activation order" if act_order else "W4A16"
+    what += ", bf16 activations" if dt == "bf16" else ""
     res = {"metric": f"HBM GB/s {what} GEMV, Llama-3-8B decode (32 layers, fused qkv / gate_up)",
            "unit": "GB/s", "packed_bytes_per_step": packed, "launches_per_step": len(mats)}
     for M in Ms:
-        xs = {K: synth.activations_device(M, K, synth.seed_for("benchw4x", K, M), "f16", dev) for K in {m[1] for m in mats}}
-        outs = [torch.empty((M, m[0]), dtype=torch.float16, device=dev) for m in mats]
+        xs = {K: synth.activations_device(M, K, synth.seed_for("benchw4x", K, M), dt, dev) for K in {m[1] for m in mats}}
+        odt = torch.float16 if dt == "f16" else torch.bfloat16
+        outs = [torch.empty((M, m[0]), dtype=odt, device=dev) for m in mats]
         ws = None
         if act_order:  # one workspace for every call: they run in order on one stream
             nb = max(tq.w4a16_gemm_asym_workspace_bytes(M, m[0], m[1], with_perm=True) for m in mats)
@@ -533,7 +535,8 @@ def main():
         print(json.dumps({"decode_70b": run_decode_70b(args, dev)}), flush=True)
         return
     if args.mode == "w4":
-        print(json.dumps({"w4a16_decode": run_w4_decode(args, dev)}), flush=True)
+        print(json.dumps({"w4a16_decode": run_w4_decode(args, dev),
+                          "w4a16_decode_bf16": run_w4_decode(args, dev, Ms=(1, 4), dt="bf16")}), flush=True)
         return
     if args.mode == "w4act":
         print(json.dumps({"w4a16_act_decode": run_w4_decode(args, dev, act_order=True)}), flush=True)
@@ -594,6 +597,8 @@ def main():
         out["decode_70b"] = run_decode_70b(args, dev)
         log("W4A16 decode")
         out["w4a16_decode"] = run_w4_decode(args, dev)
+        log("W4A16 decode, bf16 activations")
+        out["w4a16_decode_bf16"] = run_w4_decode(args, dev, Ms=(1, 4), dt="bf16")
         log("W4A16 decode, zero points and activation order")
         out["w4a16_act_decode"] = run_w4_decode(args, dev, act_order=True)
         log("medium M")

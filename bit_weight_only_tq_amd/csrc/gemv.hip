@@ -7,7 +7,7 @@
 // the partials in a fixed order.  No atomics: results are deterministic for
 // a given shape, path and workspace size.  Dispatch: the small-M kernels for
 // M <= 2 (ternary; M <= 4 where the grid has few waves per SIMD, and always
-// for bf16) and M <= 4 (W4A16, fp16), the streaming kernels above that (fp16),
+// for bf16) and M <= 4 (W4A16), the streaming kernels above that (fp16),
 // the per-lane FMA kernels for the shapes the others cannot take.
 //
 // Ternary layer arithmetic (page "Ternary quantized models in vLLM ...",
@@ -1050,7 +1050,7 @@ __global__ __launch_bounds__(W * kWave) void w4_gemv_mfma_kernel(GemmArgs p) {
     }
 }
 
-// W4A16 at M <= 4 (fp16, K = 128 G with GSW in {4, 8} groups per wave and
+// W4A16 at M <= 4 (fp16 or bf16, K = 128 G with GSW in {4, 8} groups per wave and
 // 4 <= W = G / GSW <= 16 waves, N a multiple of 16 R), in the form of
 // ternary_gemv_m1_kernel; MT in {1, 2, 4} activation rows are held, rows
 // M .. MT-1 re-read row M-1 and are never stored:
@@ -1074,8 +1074,14 @@ __global__ __launch_bounds__(W * kWave) void w4_gemv_mfma_kernel(GemmArgs p) {
 // group's constant splits into 1024 sum a' and sum a (both independent of
 // the weight row, two row sums), and the group value is
 // acc - 1024 sum a' - z sum a.
-template <int R, int GSW, bool ASYM, int MT>
+// bf16: 7 fraction bits hold a nibble at bits 0..3 (value 128 + q over the
+// bf16 constant 128.0) or at bits 3..6 (128 + 8 q), so the odd nibbles are
+// shifted down one bit before masking (x >> 1 and x >> 9), the odd a' pairs
+// are pre-scaled by 1/8 instead of 1/16 (through fp32: gfx950 has no packed
+// bf16 multiply), and the constants become a' (128 + 8 8^s) and 128 sum a'.
+template <class T, int R, int GSW, bool ASYM, int MT>
 __global__ __launch_bounds__(1024) void w4_gemv_m1_kernel(GemmArgs p) {
+    constexpr bool kBf = std::is_same<T, BF16>::value;
     extern __shared__ uint4 smem[];
     constexpr int U = GSW / 4;            // 8-column units per lane and row
     constexpr int kRowLds = GSW * 256;    // a' bytes of one activation row
@@ -1143,27 +1149,47 @@ __global__ __launch_bounds__(1024) void w4_gemv_m1_kernel(GemmArgs p) {
 #pragma unroll
         for (int j = 0; j < U; ++j) {
             const uint4 a = av[m][j];
-            const f16x2 s16 = f16x2{(_Float16)0.0625f, (_Float16)0.0625f};
             const uint32_t p0 = __builtin_amdgcn_perm(a.z, a.x, 0x05040100u);
-            const uint32_t p1 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(a.z, a.x, 0x07060302u)) * s16);
             const uint32_t p2 = __builtin_amdgcn_perm(a.w, a.y, 0x05040100u);
-            const uint32_t p3 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(a.w, a.y, 0x07060302u)) * s16);
-            // symmetric: sum a' (1024 + 8 16^s) = (1032, 1152) patterns; ASYM:
-            // sum a' 1024, and sum a = (1, 16) patterns on the scaled pairs
-            constexpr uint32_t c0 = ASYM ? 0x64006400u : 0x64086408u;
-            constexpr uint32_t c1 = ASYM ? 0x64006400u : 0x64806480u;
+            uint32_t p1 = __builtin_amdgcn_perm(a.z, a.x, 0x07060302u);
+            uint32_t p3 = __builtin_amdgcn_perm(a.w, a.y, 0x07060302u);
+            if constexpr (kBf) {
+                auto eighth = [](uint32_t v) {
+                    const float lo = __uint_as_float(v << 16) * 0.125f, hi = __uint_as_float(v & 0xFFFF0000u) * 0.125f;
+                    return __builtin_bit_cast(uint32_t, bf16x2{(__bf16)lo, (__bf16)hi});
+                };
+                p1 = eighth(p1);
+                p3 = eighth(p3);
+            } else {
+                const f16x2 s16 = f16x2{(_Float16)0.0625f, (_Float16)0.0625f};
+                p1 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, p1) * s16);
+                p3 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, p3) * s16);
+            }
+            // symmetric: sum a' (1024 + 8 16^s) = (1032, 1152) patterns (bf16:
+            // 128 + 8 8^s = 136, 192); ASYM: sum a' 1024 (128), and sum a =
+            // (1, 16) patterns (bf16: (1, 8)) on the scaled pairs
+            constexpr uint32_t c0 = kBf ? (ASYM ? 0x43004300u : 0x43084308u) : (ASYM ? 0x64006400u : 0x64086408u);
+            constexpr uint32_t c1 = kBf ? (ASYM ? 0x43004300u : 0x43404340u) : (ASYM ? 0x64006400u : 0x64806480u);
+            constexpr uint32_t e0 = kBf ? 0x3F803F80u : 0x3C003C00u;
+            constexpr uint32_t e1 = kBf ? 0x41004100u : 0x4C004C00u;
+            auto dot2 = [](uint32_t x, uint32_t c, float acc) {
+                if constexpr (kBf)
+                    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x), __builtin_bit_cast(bf16x2, c), acc, false);
+                else
+                    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, x), __builtin_bit_cast(f16x2, c), acc, false);
+            };
             float dp = 0.0f;
-            dp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, p0), __builtin_bit_cast(f16x2, c0), dp, false);
-            dp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, p1), __builtin_bit_cast(f16x2, c1), dp, false);
-            dp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, p2), __builtin_bit_cast(f16x2, c0), dp, false);
-            dp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, p3), __builtin_bit_cast(f16x2, c1), dp, false);
+            dp = dot2(p0, c0, dp);
+            dp = dot2(p1, c1, dp);
+            dp = dot2(p2, c0, dp);
+            dp = dot2(p3, c1, dp);
             dpu[j] = row16_sum(dp);  // DPP row r: the constant of group 4 j + r
             if constexpr (ASYM) {
                 float sa = 0.0f;
-                sa = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, p0), __builtin_bit_cast(f16x2, 0x3C003C00u), sa, false);
-                sa = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, p1), __builtin_bit_cast(f16x2, 0x4C004C00u), sa, false);
-                sa = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, p2), __builtin_bit_cast(f16x2, 0x3C003C00u), sa, false);
-                sa = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, p3), __builtin_bit_cast(f16x2, 0x4C004C00u), sa, false);
+                sa = dot2(p0, e0, sa);
+                sa = dot2(p1, e1, sa);
+                sa = dot2(p2, e0, sa);
+                sa = dot2(p3, e1, sa);
                 dsu[j] = row16_sum(sa);
             }
             *reinterpret_cast<uint4*>(aps + m * kRowLds + 16 * (lane + 64 * j)) = make_uint4(p0, p1, p2, p3);
@@ -1184,9 +1210,9 @@ __global__ __launch_bounds__(1024) void w4_gemv_m1_kernel(GemmArgs p) {
     for (int r = 0; r < R; ++r)
 #pragma unroll
         for (int i = 0; i < MT; ++i) res[r][i] = 0.0f;
-    const uint32_t magic_v = vgpr_const<kMagic2>();
+    const uint32_t magic_v = vgpr_const<kBf ? kMagicBf2 : kMagic2>();
     const uint32_t m0 = sgpr_const<0x000F000Fu>();
-    const uint32_t m1 = sgpr_const<0x00F000F0u>();
+    const uint32_t m1 = sgpr_const<kBf ? 0x00780078u : 0x00F000F0u>();
     const bool a_live = MT == 1 ? i16 == 0 : i16 < M;
 #pragma unroll
     for (int gi = 0; gi < GSW; ++gi) {
@@ -1205,8 +1231,10 @@ __global__ __launch_bounds__(1024) void w4_gemv_m1_kernel(GemmArgs p) {
             for (int d = 0; d < 4; ++d) {
                 const uint32_t x = dword_of(q[gi][r], d);
                 const uint32_t y = x >> 8;
-                const uint4 bw = make_uint4((x & m0) | magic_v, (x & m1) | magic_v, (y & m0) | magic_v, (y & m1) | magic_v);
-                ag = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, aw[d]), __builtin_bit_cast(f16x8, bw), ag, 0, 0, 0);
+                const uint32_t x1 = kBf ? x >> 1 : x;
+                const uint32_t y1 = kBf ? x >> 9 : y;
+                const uint4 bw = make_uint4((x & m0) | magic_v, (x1 & m1) | magic_v, (y & m0) | magic_v, (y1 & m1) | magic_v);
+                ag = sm_mma<T>(aw[d], bw, ag);
             }
             const uint2 sw = scw[r][gi / 4];
             const uint32_t sd = (gi % 4) < 2 ? sw.x : sw.y;
@@ -1235,8 +1263,8 @@ __global__ __launch_bounds__(1024) void w4_gemv_m1_kernel(GemmArgs p) {
         const int i = (t / 16) % MT;
         float sum = red[t];
         for (int w = 1; w < W; ++w) sum += red[w * (16 * R * MT) + t];
-        const float bi = p.bias ? F16::to_f32(bi_bits) : 0.0f;
-        if (i < M) p.C[(int64_t)i * p.N + n_e] = F16::from_f32_fast(sum + bi);
+        const float bi = p.bias ? T::to_f32(bi_bits) : 0.0f;
+        if (i < M) p.C[(int64_t)i * p.N + n_e] = T::from_f32_fast(sum + bi);
     }
 }
 
@@ -1968,8 +1996,8 @@ hipError_t launch_w4_gemv(const GemmArgs& a, hipStream_t s) { return launch_w4_g
 // that would need more than 16 waves), every wave a full share of K, at
 // least 4 waves, scales 8-byte and zero points 4-byte aligned (a wave reads
 // aligned runs of them); two 16-row blocks per workgroup when one-block
-// workgroups would hold more than 8 waves per SIMD.  bf16 and other shapes
-// take the kernels below.
+// workgroups would hold more than 8 waves per SIMD.  Other shapes take the
+// kernels below.
 struct W4M1Plan {
     int gsw, waves, rows16, mt;
     size_t lds;
@@ -1980,7 +2008,7 @@ struct W4M1Plan {
 constexpr int64_t kW4SmallMaxM = TQ_W4_SMALL_MAX_M;  // largest M the small-M kernel takes
 
 static bool w4_m1_plan(const GemmArgs& a, W4M1Plan* pl) {
-    if (a.bf16 || a.M < 1 || a.M > kW4SmallMaxM || a.K % 512 != 0 || a.N % 16 != 0) return false;
+    if (a.M < 1 || a.M > kW4SmallMaxM || a.K % 512 != 0 || a.N % 16 != 0) return false;
     if ((reinterpret_cast<uintptr_t>(a.scale) & 7u) != 0 || (reinterpret_cast<uintptr_t>(a.zeros) & 3u) != 0)
         return false;
     const int64_t G = a.K / 128;
@@ -1995,28 +2023,33 @@ static bool w4_m1_plan(const GemmArgs& a, W4M1Plan* pl) {
     return pl->lds <= (size_t)kGemvLdsMaxBytes;
 }
 
-template <int R, int GSW, bool ASYM, int MT>
+template <class T, int R, int GSW, bool ASYM, int MT>
 static hipError_t launch_w4_m1_k(const GemmArgs& a, const W4M1Plan& pl, hipStream_t s) {
     static DeviceFlags lds_limit_set;
-    hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(&w4_gemv_m1_kernel<R, GSW, ASYM, MT>),
+    hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(&w4_gemv_m1_kernel<T, R, GSW, ASYM, MT>),
                                    kGemvLdsMaxBytes, lds_limit_set);
     if (e != hipSuccess) return e;
     if (a.N % (16 * R) != 0 || a.K != (int64_t)pl.waves * GSW * 128 || a.M > MT) return hipErrorInvalidValue;
     const dim3 grid((unsigned)(a.N / (16 * R)));
-    w4_gemv_m1_kernel<R, GSW, ASYM, MT><<<grid, dim3(pl.waves * kWave), pl.lds, s>>>(a);
+    w4_gemv_m1_kernel<T, R, GSW, ASYM, MT><<<grid, dim3(pl.waves * kWave), pl.lds, s>>>(a);
     return hipGetLastError();
 }
 
-template <int R, int GSW, bool ASYM>
+template <class T, int R, int GSW, bool ASYM>
 static hipError_t launch_w4_m1_mt(const GemmArgs& a, const W4M1Plan& pl, hipStream_t s) {
-    if (pl.mt == 1) return launch_w4_m1_k<R, GSW, ASYM, 1>(a, pl, s);
-    if (pl.mt == 2) return launch_w4_m1_k<R, GSW, ASYM, 2>(a, pl, s);
-    return launch_w4_m1_k<R, GSW, ASYM, 4>(a, pl, s);
+    if (pl.mt == 1) return launch_w4_m1_k<T, R, GSW, ASYM, 1>(a, pl, s);
+    if (pl.mt == 2) return launch_w4_m1_k<T, R, GSW, ASYM, 2>(a, pl, s);
+    return launch_w4_m1_k<T, R, GSW, ASYM, 4>(a, pl, s);
+}
+
+template <class T, int R, int GSW>
+static hipError_t launch_w4_m1_t(const GemmArgs& a, const W4M1Plan& pl, hipStream_t s) {
+    return a.zeros ? launch_w4_m1_mt<T, R, GSW, true>(a, pl, s) : launch_w4_m1_mt<T, R, GSW, false>(a, pl, s);
 }
 
 template <int R, int GSW>
 static hipError_t launch_w4_m1(const GemmArgs& a, const W4M1Plan& pl, hipStream_t s) {
-    return a.zeros ? launch_w4_m1_mt<R, GSW, true>(a, pl, s) : launch_w4_m1_mt<R, GSW, false>(a, pl, s);
+    return a.bf16 ? launch_w4_m1_t<BF16, R, GSW>(a, pl, s) : launch_w4_m1_t<F16, R, GSW>(a, pl, s);
 }
 
 size_t w4_gemv_workspace_bytes(const GemmArgs& a) {

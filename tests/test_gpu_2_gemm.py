@@ -422,32 +422,37 @@ W4_M1_SHAPES = [(320, 4096), (1024, 14336), (512, 8192), (28672, 4096)]
 
 
 @pytest.mark.parametrize("N,K", W4_M1_SHAPES)
-def test_w4_m1_one_hot_and_bias(N, K):
-    """The W4A16 M = 1 kernel: a one-hot row e_k gives C[0, n] = wdq[n, k]
-    bit for bit for k at every nibble position of a word, every word of a
-    lane slot and every slot of a group, in first and last groups of several
-    waves; a dense row with a bias is within the tolerance."""
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_w4_m1_one_hot_and_bias(N, K, dt):
+    """The W4A16 M = 1 kernel (fp16, and bf16 with the odd nibbles shifted to
+    bits 3..6): a one-hot row e_k gives C[0, n] = wdq[n, k] bit for bit for
+    k at every nibble position of a word, every word of a lane slot and
+    every slot of a group, in first and last groups of several waves; a
+    dense row with a bias is within the tolerance."""
     import torch
     import bit_weight_only_tq_amd as tq
     dev = require_gpu()
-    log(f"W4 M=1 kernel one-hot and bias N={N} K={K}")
+    log(f"W4 M=1 kernel one-hot and bias N={N} K={K} {dt}")
     q, s, rq, rs, wdq = _w4(N, K, dev)
+    tdt = torch.float16 if dt == "f16" else torch.bfloat16
+    to_bits = OR.f16_bits if dt == "f16" else OR.bf16_bits
     ks = sorted({0, 1, 2, 3, 4, 5, 6, 7, 8, 15, 31, 32, 63, 96 + 7, 127, 128, 640 + 45, 1023, 1024 + 77,
                  K // 2 + 19, K - 128, K - 33, K - 1})
     for k in ks:
-        A = torch.zeros((1, K), dtype=torch.float16)
+        A = torch.zeros((1, K), dtype=tdt)
         A[0, k] = 1.0
         C = tq.w4a16_gemm(A.to(dev), q, s)
-        np.testing.assert_array_equal(bits16(C)[0], OR.f16_bits(wdq[:, k]), err_msg=f"k={k}")
-    A = synth.activations(1, K, synth.seed_for("w4m1", N, K), "f16")
-    bias = synth.activations(1, N, synth.seed_for("w4m1b", N, K), "f16")[0]
+        np.testing.assert_array_equal(bits16(C)[0], to_bits(wdq[:, k]), err_msg=f"k={k}")
+    A = synth.activations(1, K, synth.seed_for("w4m1", N, K, dt), dt)
+    bias = synth.activations(1, N, synth.seed_for("w4m1b", N, K, dt), dt)[0]
     C = tq.w4a16_gemm(A.to(dev), q, s, bias=bias.to(dev))
-    check_close(C, A, wdq, bias=bias, label=f"W4 M=1 kernel {N}x{K} with bias")
+    check_close(C, A, wdq, bias=bias, label=f"W4 M=1 kernel {N}x{K} {dt} with bias")
 
 
 @pytest.mark.parametrize("N,K", [(320, 4096), (1024, 14336), (28672, 4096)])
 @pytest.mark.parametrize("M", [2, 3, 4])
-def test_w4_small_m_one_hot_and_bias(N, K, M):
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_w4_small_m_one_hot_and_bias(N, K, M, dt):
     """The W4A16 small-M kernel at M = 2..4 (two or four activation rows
     held; at M = 3 the fourth re-reads the third and is not stored): one-hot
     rows give C[m, n] = wdq[n, k_m] bit for bit; dense rows with a bias are
@@ -455,22 +460,24 @@ def test_w4_small_m_one_hot_and_bias(N, K, M):
     import torch
     import bit_weight_only_tq_amd as tq
     dev = require_gpu()
-    log(f"W4 small-M kernel one-hot and bias M={M} N={N} K={K}")
+    log(f"W4 small-M kernel one-hot and bias M={M} N={N} K={K} {dt}")
     q, s, rq, rs, wdq = _w4(N, K, dev)
+    tdt = torch.float16 if dt == "f16" else torch.bfloat16
+    to_bits = OR.f16_bits if dt == "f16" else OR.bf16_bits
     sets = [[0, 9, 130, K - 1], [5, 127, 1024 + 33, K // 2 + 7], [2, 64 + 3, 2048 + 100, K - 200]]
     for ks in sets:
         ks = ks[:M]
-        A = torch.zeros((M, K), dtype=torch.float16)
+        A = torch.zeros((M, K), dtype=tdt)
         for m, k in enumerate(ks):
             A[m, k] = 1.0
-        buf = torch.full((M + 1, N), -7.0, dtype=torch.float16, device=dev)
+        buf = torch.full((M + 1, N), -7.0, dtype=tdt, device=dev)
         C = tq.w4a16_gemm(A.to(dev), q, s, out=buf[:M])
-        np.testing.assert_array_equal(bits16(C), OR.f16_bits(wdq[:, ks].T), err_msg=f"ks={ks}")
+        np.testing.assert_array_equal(bits16(C), to_bits(wdq[:, ks].T), err_msg=f"ks={ks}")
         assert bool((buf[M] == -7.0).all())
-    A = synth.activations(M, K, synth.seed_for("w4sm", M, N, K), "f16")
-    bias = synth.activations(1, N, synth.seed_for("w4smb", N, K), "f16")[0]
+    A = synth.activations(M, K, synth.seed_for("w4sm", M, N, K, dt), dt)
+    bias = synth.activations(1, N, synth.seed_for("w4smb", N, K, dt), dt)[0]
     C = tq.w4a16_gemm(A.to(dev), q, s, bias=bias.to(dev))
-    check_close(C, A, wdq, bias=bias, label=f"W4 small-M kernel M={M} {N}x{K} with bias")
+    check_close(C, A, wdq, bias=bias, label=f"W4 small-M kernel M={M} {N}x{K} {dt} with bias")
 
 
 @pytest.mark.parametrize("N,K", [(320, 4096), (4096, 14336), (1024, 28672)])

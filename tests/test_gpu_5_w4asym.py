@@ -286,7 +286,8 @@ def test_w4_pair_fallbacks(case):
 
 
 @pytest.mark.parametrize("N,K,order", [(320, 4096, True), (320, 4096, False), (160, 14336, True)])
-def test_w4a_m1_kernel_one_hot(N, K, order):
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_w4a_m1_kernel_one_hot(N, K, order, dt):
     """The W4A16 M = 1 kernel with zero points (4 and 8 groups per wave): a
     one-hot row gives C[0, n] = wdq[n, k] bit for bit, (q - z) * s rounded
     once, at columns in every nibble position and in first and last groups
@@ -295,10 +296,11 @@ def test_w4a_m1_kernel_one_hot(N, K, order):
     import torch
     import bit_weight_only_tq_amd as tq
     dev = require_gpu()
-    log(f"w4a M=1 kernel one-hot N={N} K={K} order={order}")
+    log(f"w4a M=1 kernel one-hot N={N} K={K} order={order} {dt}")
     (q, s, z, perm), wdq = _packed(N, K, order, dev)
+    to_bits = OR.f16_bits if dt == "f16" else OR.bf16_bits
     for k in sorted({0, 1, 3, 4, 7, 9, 31, 33, 127, 128, 517, 1023, 2048 + 70, K - 129, K - 1}):
-        A = torch.zeros((1, K), dtype=torch.float16)
+        A = torch.zeros((1, K), dtype=torch.float16 if dt == "f16" else torch.bfloat16)
         A[0, k] = 1.0
         C = tq.w4a16_gemm(A.to(dev), q, s, zeros=z, perm=perm if order else None)
-        np.testing.assert_array_equal(bits16(C)[0], OR.f16_bits(wdq[:, k]), err_msg=f"k={k}")
+        np.testing.assert_array_equal(bits16(C)[0], to_bits(wdq[:, k]), err_msg=f"k={k}")
