@@ -529,7 +529,7 @@ def main():
         return
     if args.mode == "decodem":
         print(json.dumps({"decode_m": run_decode_m(args, dev, not args.no_graph),
-                          "decode_bf16": run_decode_m(args, dev, not args.no_graph, Ms=(1, 2), dt="bf16")}), flush=True)
+                          "decode_bf16": run_decode_m(args, dev, not args.no_graph, Ms=(1, 2, 16), dt="bf16")}), flush=True)
         return
     if args.mode == "decode70b":
         print(json.dumps({"decode_70b": run_decode_70b(args, dev)}), flush=True)
@@ -589,8 +589,8 @@ def main():
                                      "avg_launch_us": round(u["avg_launch_us"], 3)}
         log("decode, M = 4 and 16")
         out["decode_m"] = run_decode_m(args, dev, graph)
-        log("decode, bf16 activations, M = 1 and 2")
-        out["decode_bf16"] = run_decode_m(args, dev, graph, Ms=(1, 2), dt="bf16")
+        log("decode, bf16 activations, M = 1, 2 and 16")
+        out["decode_bf16"] = run_decode_m(args, dev, graph, Ms=(1, 2, 16), dt="bf16")
         log("decode time split")
         out["attribution"] = run_attrib(dev)
         log("decode, Llama-3-70B, 80 layers")

@@ -513,6 +513,25 @@ def test_ternary_small_m_one_hot_and_bias(N, K, M, dt):
     check_close(C, A, wdq, bias=bias, label=f"ternary small-M M={M} {N}x{K} {dt} with bias")
 
 
+@pytest.mark.parametrize("M,N,K", [(5, 4096, 4096), (16, 28672, 4096), (9, 4096, 14336), (16, 1000, 4160)])
+def test_bf16_decode_m_auto(M, N, K):
+    """bf16 at M = 5..16 is dispatched to the medium path (its bf16
+    matrix-core kernel, K split with the queried workspace): every output
+    against the oracle, with a bias; the rows past M untouched."""
+    import torch
+    import bit_weight_only_tq_amd as tq
+    dev = require_gpu()
+    log(f"bf16 decode-size M auto M={M} N={N} K={K}")
+    assert tq.tq_select_path("ternary", M, N, K, "bf16") == "stream_mfma"
+    codes, scale, rc, rs, wdq = _ternary(N, K, dev)
+    A = synth.activations(M, K, synth.seed_for("bfm", M, N, K), "bf16")
+    bias = synth.activations(1, N, synth.seed_for("bfmb", N, K), "bf16")[0]
+    buf = torch.full((M + 1, N), -7.0, dtype=torch.bfloat16, device=dev)
+    C = tq.tq_gemm(A.to(dev), codes, scale, bias=bias.to(dev), out=buf[:M])
+    check_close(C, A, wdq, bias=bias, label=f"bf16 auto M={M} {N}x{K}")
+    assert bool((buf[M] == -7.0).all())
+
+
 @pytest.mark.parametrize("M,N,K,dt", [(2560, 7168, 256, "f16"), (2500, 7000, 320, "bf16"), (4096, 14336, 256, "f16")])
 def test_prefill_tail_split(M, N, K, dt):
     """Large M whose 256 x 256 tiles leave the last round of workgroups at
