@@ -536,7 +536,7 @@ def main():
         return
     if args.mode == "w4":
         print(json.dumps({"w4a16_decode": run_w4_decode(args, dev),
-                          "w4a16_decode_bf16": run_w4_decode(args, dev, Ms=(1, 4), dt="bf16")}), flush=True)
+                          "w4a16_decode_bf16": run_w4_decode(args, dev, Ms=(1, 4, 16), dt="bf16")}), flush=True)
         return
     if args.mode == "w4act":
         print(json.dumps({"w4a16_act_decode": run_w4_decode(args, dev, act_order=True)}), flush=True)
@@ -598,7 +598,7 @@ def main():
         log("W4A16 decode")
         out["w4a16_decode"] = run_w4_decode(args, dev)
         log("W4A16 decode, bf16 activations")
-        out["w4a16_decode_bf16"] = run_w4_decode(args, dev, Ms=(1, 4), dt="bf16")
+        out["w4a16_decode_bf16"] = run_w4_decode(args, dev, Ms=(1, 4, 16), dt="bf16")
         log("W4A16 decode, zero points and activation order")
         out["w4a16_act_decode"] = run_w4_decode(args, dev, act_order=True)
         log("medium M")

@@ -16,6 +16,7 @@
 // W4A16 (page "Model quantization - vLLM runtime quantization architecture",
 // section 5): value = q - 8 with a per-(row, 128-column group) fp16 scale.
 
+#include <algorithm>
 #include <type_traits>
 
 #include "tq_device.h"
@@ -2060,11 +2061,32 @@ size_t w4_gemv_workspace_bytes(const GemmArgs& a) {
     return (size_t)pl.S * (size_t)a.M * (size_t)a.N * sizeof(float);
 }
 
+static hipError_t launch_w4_m1_plan(const GemmArgs& a, const W4M1Plan& m1, hipStream_t s) {
+    if (m1.gsw == 8) return m1.rows16 == 2 ? launch_w4_m1<2, 8>(a, m1, s) : launch_w4_m1<1, 8>(a, m1, s);
+    return m1.rows16 == 2 ? launch_w4_m1<2, 4>(a, m1, s) : launch_w4_m1<1, 4>(a, m1, s);
+}
+
 hipError_t launch_w4_gemv(const GemmArgs& a, void* workspace, size_t workspace_bytes, hipStream_t s) {
     W4M1Plan m1;
-    if (w4_m1_plan(a, &m1)) {
-        if (m1.gsw == 8) return m1.rows16 == 2 ? launch_w4_m1<2, 8>(a, m1, s) : launch_w4_m1<1, 8>(a, m1, s);
-        return m1.rows16 == 2 ? launch_w4_m1<2, 4>(a, m1, s) : launch_w4_m1<1, 4>(a, m1, s);
+    if (w4_m1_plan(a, &m1)) return launch_w4_m1_plan(a, m1, s);
+    // bf16 has no streaming kernel: past the small-M kernel's rows it runs
+    // that kernel over blocks of kW4SmallMaxM rows, reading the weights once
+    // per block, which still beats the per-lane FMA kernel several times over
+    if (a.bf16 && a.M > kW4SmallMaxM) {
+        GemmArgs b = a;
+        b.M = kW4SmallMaxM;
+        if (w4_m1_plan(b, &m1)) {
+            for (int64_t m0 = 0; m0 < a.M; m0 += kW4SmallMaxM) {
+                b.A = a.A + m0 * a.K;
+                b.C = a.C + m0 * a.N;
+                b.M = std::min<int64_t>(kW4SmallMaxM, a.M - m0);
+                W4M1Plan pb;
+                if (!w4_m1_plan(b, &pb)) return hipErrorInvalidValue;
+                const hipError_t e = launch_w4_m1_plan(b, pb, s);
+                if (e != hipSuccess) return e;
+            }
+            return hipSuccess;
+        }
     }
     W4StreamPlan sp;
     if (w4_use_stream(a, workspace ? workspace_bytes : 0, &sp))

@@ -449,6 +449,31 @@ def test_w4_m1_one_hot_and_bias(N, K, dt):
     check_close(C, A, wdq, bias=bias, label=f"W4 M=1 kernel {N}x{K} {dt} with bias")
 
 
+@pytest.mark.parametrize("M,N,K", [(5, 4096, 4096), (16, 28672, 4096), (11, 1024, 14336), (40, 320, 4096)])
+def test_w4_bf16_row_blocks(M, N, K):
+    """bf16 W4A16 past four rows: the small-M kernel over blocks of four rows
+    (inside blocks of 16 when M > 16), the last block ragged; one-hot rows
+    give C[m, n] = wdq[n, k_m] bit for bit, dense rows with a bias are within
+    the tolerance, the row past M is untouched."""
+    import torch
+    import bit_weight_only_tq_amd as tq
+    dev = require_gpu()
+    log(f"W4 bf16 row blocks M={M} N={N} K={K}")
+    q, s, rq, rs, wdq = _w4(N, K, dev)
+    ks = [(37 * m + 5) % K for m in range(M)]
+    A = torch.zeros((M, K), dtype=torch.bfloat16)
+    for m, k in enumerate(ks):
+        A[m, k] = 1.0
+    C = tq.w4a16_gemm(A.to(dev), q, s)
+    np.testing.assert_array_equal(bits16(C), OR.bf16_bits(wdq[:, ks].T))
+    A = synth.activations(M, K, synth.seed_for("w4bfr", M, N, K), "bf16")
+    bias = synth.activations(1, N, synth.seed_for("w4bfrb", N, K), "bf16")[0]
+    buf = torch.full((M + 1, N), -7.0, dtype=torch.bfloat16, device=dev)
+    C = tq.w4a16_gemm(A.to(dev), q, s, bias=bias.to(dev), out=buf[:M])
+    check_close(C, A, wdq, bias=bias, label=f"W4 bf16 row blocks M={M} {N}x{K}")
+    assert bool((buf[M] == -7.0).all())
+
+
 @pytest.mark.parametrize("N,K", [(320, 4096), (1024, 14336), (28672, 4096)])
 @pytest.mark.parametrize("M", [2, 3, 4])
 @pytest.mark.parametrize("dt", ["f16", "bf16"])
