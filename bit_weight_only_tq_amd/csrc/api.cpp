@@ -21,7 +21,6 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // cores; in between, 64-row tiles with K split across workgroups.
 constexpr int64_t kGemvMaxM = tq::kGemvMaxM;
 constexpr int64_t kMediumMaxM = 256;  // M < 256: medium path
-constexpr int64_t kTernaryBf16GemvMaxM = 4;  // bf16 ternary: decode kernels up to here
 
 // Device status word for the synchronous prepare calls.
 struct StatusWord {
@@ -77,11 +76,7 @@ const char* tq_status_str(tq_status s) {
 }
 
 tq_path tq_select_path(int format, int64_t M, int64_t N, int64_t K, tq_dtype dt) {
-    (void)N; (void)K;
-    // ternary bf16 past the small-M kernel's rows has only the per-lane FMA
-    // decode kernel; the medium path's bf16 matrix-core kernel beats it
-    // 9-19x on the Llama shapes at M = 5..16
-    if (format == 0 && dt == TQ_BF16 && M > kTernaryBf16GemvMaxM && M <= kGemvMaxM) return TQ_PATH_STREAM_MFMA;
+    (void)N; (void)K; (void)dt;
     if (M <= kGemvMaxM) return TQ_PATH_GEMV;
     if (format == 1) return TQ_PATH_GEMV;  // W4A16: small-M kernel over blocks of rows
     if (M < kMediumMaxM) return TQ_PATH_STREAM_MFMA;

@@ -537,6 +537,11 @@ __device__ __forceinline__ uint32_t sm_a_pair(const uint4 av[8]) {
     if constexpr (std::is_same<T, F16>::value) return a_pair<0, I>(av);
     else return bf_a_pair<I>(av);
 }
+template <class T, int D, int I>
+__device__ __forceinline__ uint32_t sm_a_pair_d(const uint4 av[8]) {  // unit D of av
+    if constexpr (std::is_same<T, F16>::value) return a_pair<D, I>(av);
+    else return bf_a_pair<I>(av + 2 * D);
+}
 template <class T, int I>
 __device__ __forceinline__ float sm_dot_one(uint32_t pair, float acc) {
     if constexpr (std::is_same<T, F16>::value)
@@ -704,7 +709,8 @@ __global__ __launch_bounds__(1024) void ternary_gemv_m1_kernel(GemmArgs p) {
     }
 }
 
-// Same arithmetic, streaming schedule (fp16, M <= 16, K / 256 <= 16 CSW).
+// Same arithmetic, streaming schedule (fp16 or bf16 activations AT, M <= 16,
+// K / 256 <= 16 CSW).
 //
 // One workgroup per compute unit walks T consecutive 16-row blocks.  Wave w
 // owns chunk-sets w*CSW .. w*CSW + CSW-1 (256 columns each) of all of them,
@@ -734,8 +740,9 @@ __host__ __device__ constexpr int stream_wave_lds(int csw, int mr, int t) {  // 
     return t * 1024 > csw * mr * 512 ? t * 1024 : csw * mr * 512;
 }
 
-template <int CSW, int T, int MR>
+template <class AT, int CSW, int T, int MR>
 __global__ __launch_bounds__(1024) void ternary_gemv_stream_kernel(SplitArgs sa) {
+    constexpr bool kBf = std::is_same<AT, BF16>::value;
     const GemmArgs& p = sa.g;
     extern __shared__ uint4 smem[];
     constexpr int kArea = stream_wave_lds(CSW, MR, T);
@@ -818,8 +825,10 @@ __global__ __launch_bounds__(1024) void ternary_gemv_stream_kernel(SplitArgs sa)
 #pragma unroll
     for (int s = 0; s < CSW; ++s) {
 #define TQ_APREP(D)                                                                                  \
-        aw[s][2 * (D)] = make_uint4(a_pair<D, 0>(av[s]), a_pair<D, 1>(av[s]), a_pair<D, 2>(av[s]), a_pair<D, 3>(av[s])); \
-        aw[s][2 * (D) + 1] = make_uint4(a_pair<D, 4>(av[s]), a_pair<D, 5>(av[s]), a_pair<D, 6>(av[s]), a_pair<D, 7>(av[s]));
+        aw[s][2 * (D)] = make_uint4(sm_a_pair_d<AT, D, 0>(av[s]), sm_a_pair_d<AT, D, 1>(av[s]),       \
+                                    sm_a_pair_d<AT, D, 2>(av[s]), sm_a_pair_d<AT, D, 3>(av[s]));      \
+        aw[s][2 * (D) + 1] = make_uint4(sm_a_pair_d<AT, D, 4>(av[s]), sm_a_pair_d<AT, D, 5>(av[s]),   \
+                                        sm_a_pair_d<AT, D, 6>(av[s]), sm_a_pair_d<AT, D, 7>(av[s]));
         TQ_APREP(0)
         TQ_APREP(1)
         TQ_APREP(2)
@@ -829,14 +838,14 @@ __global__ __launch_bounds__(1024) void ternary_gemv_stream_kernel(SplitArgs sa)
 #pragma unroll
             for (int d = 0; d < 4; ++d) {
                 const uint4 lo = aw[s][2 * d], hi = aw[s][2 * d + 1];
-                dl = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, lo.x), __builtin_bit_cast(f16x2, one_pattern<0>()), dl, false);
-                dl = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, lo.y), __builtin_bit_cast(f16x2, one_pattern<1>()), dl, false);
-                dl = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, lo.z), __builtin_bit_cast(f16x2, one_pattern<2>()), dl, false);
-                dl = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, lo.w), __builtin_bit_cast(f16x2, one_pattern<3>()), dl, false);
-                dl = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, hi.x), __builtin_bit_cast(f16x2, one_pattern<4>()), dl, false);
-                dl = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, hi.y), __builtin_bit_cast(f16x2, one_pattern<5>()), dl, false);
-                dl = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, hi.z), __builtin_bit_cast(f16x2, one_pattern<6>()), dl, false);
-                dl = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, hi.w), __builtin_bit_cast(f16x2, one_pattern<7>()), dl, false);
+                dl = sm_dot_one<AT, 0>(lo.x, dl);
+                dl = sm_dot_one<AT, 1>(lo.y, dl);
+                dl = sm_dot_one<AT, 2>(lo.z, dl);
+                dl = sm_dot_one<AT, 3>(lo.w, dl);
+                dl = sm_dot_one<AT, 4>(hi.x, dl);
+                dl = sm_dot_one<AT, 5>(hi.y, dl);
+                dl = sm_dot_one<AT, 6>(hi.z, dl);
+                dl = sm_dot_one<AT, 7>(hi.w, dl);
             }
         }
     }
@@ -849,7 +858,7 @@ __global__ __launch_bounds__(1024) void ternary_gemv_stream_kernel(SplitArgs sa)
     for (int i = 0; i < 4; ++i) dsub[i] = __shfl(dl, 4 * g + i, kWave);
 
     // 4. contract each row-block as its codes land
-    const uint32_t magic_v = vgpr_const<kMagic2>();
+    const uint32_t magic_v = vgpr_const<kBf ? kMagicBf2 : kMagic2>();
     f32x4 acc[T];
 #pragma unroll
     for (int t = 0; t < T; ++t) {
@@ -860,11 +869,11 @@ __global__ __launch_bounds__(1024) void ternary_gemv_stream_kernel(SplitArgs sa)
 #define TQ_MFMA_S(D, I0)                                                                              \
     {                                                                                                 \
         const uint32_t x = dword_of(q[t][s], D);                                                      \
-        const uint32_t y = x >> 10;                                                                   \
-        const uint4 bw = make_uint4(field_pair<I0>(x, y, magic_v), field_pair<I0 + 1>(x, y, magic_v), \
-                                    field_pair<I0 + 2>(x, y, magic_v), field_pair<I0 + 3>(x, y, magic_v)); \
-        a4 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, aw[s][2 * (D) + (I0) / 4]), \
-                                                    __builtin_bit_cast(f16x8, bw), a4, 0, 0, 0);      \
+        const uint32_t y = x >> (kBf ? 6 : 10);                                                       \
+        const uint32_t z = x >> 12;                                                                   \
+        const uint4 bw = make_uint4(sm_field_pair<AT, I0>(x, y, z, magic_v), sm_field_pair<AT, I0 + 1>(x, y, z, magic_v), \
+                                    sm_field_pair<AT, I0 + 2>(x, y, z, magic_v), sm_field_pair<AT, I0 + 3>(x, y, z, magic_v)); \
+        a4 = sm_mma<AT>(aw[s][2 * (D) + (I0) / 4], bw, a4);                                           \
     }
                 TQ_MFMA_S(0, 0)
                 TQ_MFMA_S(0, 4)
@@ -905,11 +914,11 @@ __global__ __launch_bounds__(1024) void ternary_gemv_stream_kernel(SplitArgs sa)
             }
         } else if (n < N) {
             const float sc_e = f16_bits_to_f32(sc_bits);
-            const float bi_e = p.bias ? F16::to_f32(bi_bits) : 0.0f;
+            const float bi_e = p.bias ? AT::to_f32(bi_bits) : 0.0f;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int m = 4 * (l >> 4) + i;
-                if (m < M) p.C[(int64_t)m * N + n] = F16::from_f32_fast(sum[i] * sc_e + bi_e);
+                if (m < M) p.C[(int64_t)m * N + n] = AT::from_f32_fast(sum[i] * sc_e + bi_e);
             }
         }
     }
@@ -1606,9 +1615,7 @@ static bool gemv_m1_plan(const GemmArgs& a, GemvM1Plan* pl) {
     // ~250: it wins where the grid has few waves per SIMD (Llama-3-8B o and
     // qkv, and down, which the streaming kernel must split along K) and loses
     // where it has many (gate_up: 7 per SIMD, 14.0 against 10.3 us).
-    // (bf16 has no streaming kernel: there the alternative is the per-lane
-    // FMA kernel, so the small-M kernel takes every M <= 4)
-    if (!a.bf16 && a.M >= 3 && nrb / pl->rows16 * pl->waves > 16 * (int64_t)compute_units()) return false;
+    if (a.M >= 3 && nrb / pl->rows16 * pl->waves > 16 * (int64_t)compute_units()) return false;
     pl->lds = (size_t)pl->waves * pl->mt * c * 512 + (size_t)pl->waves * pl->rows16 * pl->mt * 64;
     return pl->lds <= (size_t)kGemvLdsMaxBytes;
 }
@@ -1712,7 +1719,7 @@ static int64_t stream_cost(const GemmArgs& a, const StreamPlan& pl, int64_t cus)
 
 // Cheapest streaming plan whose split fits `ws_bytes` of workspace.
 static bool gemv_stream_plan(const GemmArgs& a, size_t ws_bytes, StreamPlan* pl) {
-    if (a.bf16 || a.M < 3 || a.M > kGemvMaxM || a.K % 256 != 0) return false;
+    if (a.M < 3 || a.M > kGemvMaxM || a.K % 256 != 0) return false;
     const int64_t cus = compute_units();
     bool found = false;
     int64_t best = 0;
@@ -1738,17 +1745,22 @@ size_t gemv_workspace_bytes(const GemmArgs& a) {
     return (size_t)pl.S * (size_t)a.M * (size_t)a.N * sizeof(float);
 }
 
-template <int CSW, int T, int MR>
-static hipError_t launch_gemv_stream(const SplitArgs& sa, const StreamPlan& pl, hipStream_t s) {
+template <class AT, int CSW, int T, int MR>
+static hipError_t launch_gemv_stream_at(const SplitArgs& sa, const StreamPlan& pl, hipStream_t s) {
     static DeviceFlags lds_limit_set;
-    hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(&ternary_gemv_stream_kernel<CSW, T, MR>),
+    hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(&ternary_gemv_stream_kernel<AT, CSW, T, MR>),
                                    kGemvLdsMaxBytes, lds_limit_set);
     if (e != hipSuccess) return e;
     if (pl.lds != (size_t)pl.waves * stream_wave_lds(CSW, MR, T)) return hipErrorInvalidValue;
     const dim3 grid((unsigned)((sa.g.N + 16 * T - 1) / (16 * T)), (unsigned)sa.S);
-    ternary_gemv_stream_kernel<CSW, T, MR><<<grid, dim3(pl.waves * kWave), pl.lds, s>>>(sa);
+    ternary_gemv_stream_kernel<AT, CSW, T, MR><<<grid, dim3(pl.waves * kWave), pl.lds, s>>>(sa);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     return sa.S > 1 ? launch_splitk_reduce(sa, s) : hipSuccess;
+}
+
+template <int CSW, int T, int MR>
+static hipError_t launch_gemv_stream(const SplitArgs& sa, const StreamPlan& pl, hipStream_t s) {
+    return sa.g.bf16 ? launch_gemv_stream_at<BF16, CSW, T, MR>(sa, pl, s) : launch_gemv_stream_at<F16, CSW, T, MR>(sa, pl, s);
 }
 
 template <int MR>

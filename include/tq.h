@@ -321,8 +321,7 @@ size_t w4a16_gemm_asym_workspace_bytes(int64_t M, int64_t N, int64_t K, tq_dtype
  *   dense contraction for the matrix cores (the decode / prefill split of
  *   the quantization decision tree on page "10.6 Quantization choice and vLLM
  *   in practice", section 10.6.1); ternary M in 17 .. 255 takes the medium
- *   path, 64-row tiles with K split across workgroups, and so does ternary
- *   bf16 at M = 5 .. 16 (its decode kernels past M = 4 are per-lane FMA).
+ *   path, 64-row tiles with K split across workgroups.
  */
 tq_path tq_select_path(int format, int64_t M, int64_t N, int64_t K, tq_dtype dt);
 

@@ -78,13 +78,11 @@ def test_dispatcher_by_m():
         assert sel("w4a16", M, 8192, 8192) == "gemv"
     for M in (256, 2048, 4096, 8192):
         assert sel("ternary", M, 14336, 4096, "bf16") == "gemm"
-    # bf16 ternary: decode kernels up to M = 4, the medium path's bf16
-    # matrix-core kernel for 5 .. 255; W4A16 keeps its decode kernels
-    for M in (1, 4):
+    # bf16 follows the same split (its decode kernels match fp16's)
+    for M in (1, 4, 5, 16):
         assert sel("ternary", M, 4096, 4096, "bf16") == "gemv"
-    for M in (5, 16, 17):
-        assert sel("ternary", M, 4096, 4096, "bf16") == "stream_mfma"
         assert sel("w4a16", M, 4096, 4096, "bf16") == "gemv"
+    assert sel("ternary", 17, 4096, 4096, "bf16") == "stream_mfma"
 
 
 def test_workspace_query():
@@ -93,7 +91,7 @@ def test_workspace_query():
     Off the GPU the compute-unit count defaults to 256."""
     wb = _lib.tq_gemm_workspace_bytes
     assert wb(1, 4096, 4096) == 0 and wb(4096, 4096, 4096) == 0
-    assert wb(8, 4096, 4096, "bf16") == wb(8, 4096, 4096, "bf16", "stream_mfma") > 0  # bf16 M = 5..16: medium path
+    assert wb(16, 4096, 14336, "bf16") == wb(16, 4096, 14336) > 0  # bf16 streaming kernel: same K split as fp16
     assert wb(64, 8192, 8192) == 8 * 64 * 8192 * 4      # 32 tiles -> 8 splits
     assert wb(32, 1024, 8192) == 16 * 32 * 1024 * 4     # 4 tiles: capped at 16 splits
     assert wb(40, 10240, 8192) == 6 * 40 * 10240 * 4    # 40 tiles: 6 splits keep one round on 256 CUs
