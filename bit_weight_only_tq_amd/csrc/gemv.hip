@@ -1302,8 +1302,9 @@ __host__ __device__ constexpr int w4_stream_wave_lds(int gsw, int mr, int t) {  
     return t * 1024 > gsw * mr * 256 ? t * 1024 : gsw * mr * 256;
 }
 
-template <int GSW, int T, int MR, bool ASYM>
+template <class AT, int GSW, int T, int MR, bool ASYM>
 __global__ __launch_bounds__(1024) void w4_gemv_stream_kernel(SplitArgs sa) {
+    constexpr bool kBf = std::is_same<AT, BF16>::value;  // bf16: the small-M kernel's bf16 unpack
     const GemmArgs& p = sa.g;
     extern __shared__ uint4 smem[];
     constexpr int kArea = w4_stream_wave_lds(GSW, MR, T);
@@ -1393,10 +1394,22 @@ __global__ __launch_bounds__(1024) void w4_gemv_stream_kernel(SplitArgs sa) {
     asm volatile("s_waitcnt vmcnt(%0)" :: "n"(T * GSW) : "memory");
     const int rd_row = i16 & (MR - 1);
     const f16x2 sixteenth = f16x2{(_Float16)0.0625f, (_Float16)0.0625f};
-    // symmetric: -(1024 + 8 * 16^s); ASYM: -1024, and the (1, 16) pattern for sum a
-    const uint4 negp = ASYM ? make_uint4(0xE400E400u, 0xE400E400u, 0xE400E400u, 0xE400E400u)
-                            : make_uint4(kW4Neg0, kW4Neg1, kW4Neg0, kW4Neg1);
-    const uint4 sump = make_uint4(0x3C003C00u, 0x4C004C00u, 0x3C003C00u, 0x4C004C00u);
+    // symmetric: -(1024 + 8 * 16^s); ASYM: -1024, and the (1, 16) pattern for
+    // sum a (bf16: -(128 + 8 * 8^s), -128, (1, 8))
+    constexpr uint32_t n0 = kBf ? (ASYM ? 0xC300C300u : 0xC308C308u) : (ASYM ? 0xE400E400u : kW4Neg0);
+    constexpr uint32_t n1 = kBf ? (ASYM ? 0xC300C300u : 0xC340C340u) : (ASYM ? 0xE400E400u : kW4Neg1);
+    constexpr uint32_t e0 = kBf ? 0x3F803F80u : 0x3C003C00u;
+    constexpr uint32_t e1 = kBf ? 0x41004100u : 0x4C004C00u;
+    const uint4 negp = make_uint4(n0, n1, n0, n1);
+    const uint4 sump = make_uint4(e0, e1, e0, e1);
+    auto odd_pair = [&](uint32_t v) -> uint32_t {  // (a_i, a_i+4) / 16, bf16: / 8
+        if constexpr (kBf) {
+            const float lo = __uint_as_float(v << 16) * 0.125f, hi = __uint_as_float(v & 0xFFFF0000u) * 0.125f;
+            return __builtin_bit_cast(uint32_t, bf16x2{(__bf16)lo, (__bf16)hi});
+        } else {
+            return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, v) * sixteenth);
+        }
+    };
     uint4 aop[GSW][4];
     f32x4 dacc[GSW], sacc[GSW];
 #pragma unroll
@@ -1408,13 +1421,12 @@ __global__ __launch_bounds__(1024) void w4_gemv_stream_kernel(SplitArgs sa) {
             const uint4 v = *reinterpret_cast<const uint4*>(area + s * MR * 256 + rd_row * 256 +
                                                             16 * ((4 * h + d) ^ (rd_row & 15)));
             const uint32_t p0 = __builtin_amdgcn_perm(v.z, v.x, 0x05040100u);
-            const uint32_t p1 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(v.z, v.x, 0x07060302u)) * sixteenth);
+            const uint32_t p1 = odd_pair(__builtin_amdgcn_perm(v.z, v.x, 0x07060302u));
             const uint32_t p2 = __builtin_amdgcn_perm(v.w, v.y, 0x05040100u);
-            const uint32_t p3 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(v.w, v.y, 0x07060302u)) * sixteenth);
+            const uint32_t p3 = odd_pair(__builtin_amdgcn_perm(v.w, v.y, 0x07060302u));
             aop[s][d] = make_uint4(p0, p1, p2, p3);
-            dacc[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, aop[s][d]), __builtin_bit_cast(f16x8, negp), dacc[s], 0, 0, 0);
-            if constexpr (ASYM)
-                sacc[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, aop[s][d]), __builtin_bit_cast(f16x8, sump), sacc[s], 0, 0, 0);
+            dacc[s] = sm_mma<AT>(aop[s][d], negp, dacc[s]);
+            if constexpr (ASYM) sacc[s] = sm_mma<AT>(aop[s][d], sump, sacc[s]);
         }
     }
 
@@ -1444,7 +1456,7 @@ __global__ __launch_bounds__(1024) void w4_gemv_stream_kernel(SplitArgs sa) {
     }
 
     // 4. contract each row-block as its codes land
-    const uint32_t magic_v = vgpr_const<kMagic2>();
+    const uint32_t magic_v = vgpr_const<kBf ? kMagicBf2 : kMagic2>();
     f32x4 acc[T];
 #pragma unroll
     for (int t = 0; t < T; ++t) {
@@ -1457,9 +1469,12 @@ __global__ __launch_bounds__(1024) void w4_gemv_stream_kernel(SplitArgs sa) {
                 for (int d = 0; d < 4; ++d) {
                     const uint32_t x = dword_of(q[t][s], d);
                     const uint32_t y = x >> 8;
-                    const uint4 bw = make_uint4((x & sgpr_const<0x000F000Fu>()) | magic_v, (x & sgpr_const<0x00F000F0u>()) | magic_v,
-                                                (y & sgpr_const<0x000F000Fu>()) | magic_v, (y & sgpr_const<0x00F000F0u>()) | magic_v);
-                    ag = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, aop[s][d]), __builtin_bit_cast(f16x8, bw), ag, 0, 0, 0);
+                    const uint32_t x1 = kBf ? x >> 1 : x;
+                    const uint32_t y1 = kBf ? x >> 9 : y;
+                    constexpr uint32_t m1 = kBf ? 0x00780078u : 0x00F000F0u;
+                    const uint4 bw = make_uint4((x & sgpr_const<0x000F000Fu>()) | magic_v, (x1 & sgpr_const<m1>()) | magic_v,
+                                                (y & sgpr_const<0x000F000Fu>()) | magic_v, (y1 & sgpr_const<m1>()) | magic_v);
+                    ag = sm_mma<AT>(aop[s][d], bw, ag);
                 }
                 if constexpr (ASYM) {
                     const float z = (float)zp[t][s];
@@ -1493,11 +1508,11 @@ __global__ __launch_bounds__(1024) void w4_gemv_stream_kernel(SplitArgs sa) {
                 if (m < M) part[(int64_t)m * N + n] = sum[i];
             }
         } else if (n < N) {
-            const float b = p.bias ? F16::to_f32(bi_bits) : 0.0f;
+            const float b = p.bias ? AT::to_f32(bi_bits) : 0.0f;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int m = 4 * (l >> 4) + i;
-                if (m < M) p.C[(int64_t)m * N + n] = F16::from_f32_fast(sum[i] + b);
+                if (m < M) p.C[(int64_t)m * N + n] = AT::from_f32_fast(sum[i] + b);
             }
         }
     }
@@ -1917,7 +1932,7 @@ static int64_t w4_stream_cost(const GemmArgs& a, const W4StreamPlan& pl, int64_t
 }
 
 static bool w4_stream_plan(const GemmArgs& a, size_t ws_bytes, W4StreamPlan* pl) {
-    if (a.bf16 || a.M < 1 || a.M > kGemvMaxM || a.K % 128 != 0) return false;
+    if (a.M < 1 || a.M > kGemvMaxM || a.K % 128 != 0) return false;
     const int64_t cus = compute_units();
     bool found = false;
     int64_t best = 0;
@@ -1948,22 +1963,28 @@ static bool w4_use_stream(const GemmArgs& a, size_t ws_bytes, W4StreamPlan* sp) 
 }
 
 
-template <int GSW, int T, int MR, bool ASYM>
-static hipError_t launch_w4_stream_k(const SplitArgs& sa, const W4StreamPlan& pl, hipStream_t s) {
+template <class AT, int GSW, int T, int MR, bool ASYM>
+static hipError_t launch_w4_stream_at(const SplitArgs& sa, const W4StreamPlan& pl, hipStream_t s) {
     if constexpr (ASYM && GSW == 2 && T > 6) {
         return hipErrorInvalidValue;  // the plan never asks for it (registers)
     } else {
         static DeviceFlags lds_limit_set;
-        hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(&w4_gemv_stream_kernel<GSW, T, MR, ASYM>),
+        hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(&w4_gemv_stream_kernel<AT, GSW, T, MR, ASYM>),
                                        kGemvLdsMaxBytes, lds_limit_set);
         if (e != hipSuccess) return e;
         if (pl.lds != (size_t)pl.waves * w4_stream_wave_lds(GSW, MR, T)) return hipErrorInvalidValue;
         if (GSW == 2 && !w4_pairs_ok(sa.g, sa.S)) return hipErrorInvalidValue;
         const dim3 grid((unsigned)((sa.g.N + 16 * T - 1) / (16 * T)), (unsigned)sa.S);
-        w4_gemv_stream_kernel<GSW, T, MR, ASYM><<<grid, dim3(pl.waves * kWave), pl.lds, s>>>(sa);
+        w4_gemv_stream_kernel<AT, GSW, T, MR, ASYM><<<grid, dim3(pl.waves * kWave), pl.lds, s>>>(sa);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         return sa.S > 1 ? launch_splitk_reduce(sa, s) : hipSuccess;
     }
+}
+
+template <int GSW, int T, int MR, bool ASYM>
+static hipError_t launch_w4_stream_k(const SplitArgs& sa, const W4StreamPlan& pl, hipStream_t s) {
+    return sa.g.bf16 ? launch_w4_stream_at<BF16, GSW, T, MR, ASYM>(sa, pl, s)
+                     : launch_w4_stream_at<F16, GSW, T, MR, ASYM>(sa, pl, s);
 }
 
 template <int GSW, int T, int MR>
@@ -2081,9 +2102,12 @@ static hipError_t launch_w4_m1_plan(const GemmArgs& a, const W4M1Plan& m1, hipSt
 hipError_t launch_w4_gemv(const GemmArgs& a, void* workspace, size_t workspace_bytes, hipStream_t s) {
     W4M1Plan m1;
     if (w4_m1_plan(a, &m1)) return launch_w4_m1_plan(a, m1, s);
-    // bf16 has no streaming kernel: past the small-M kernel's rows it runs
-    // that kernel over blocks of kW4SmallMaxM rows, reading the weights once
-    // per block, which still beats the per-lane FMA kernel several times over
+    W4StreamPlan sp;
+    if (w4_use_stream(a, workspace ? workspace_bytes : 0, &sp))
+        return launch_w4_stream_t(SplitArgs{a, static_cast<float*>(workspace), sp.S, 1}, sp, s);
+    // bf16 shapes the streaming kernel cannot take: the small-M kernel over
+    // blocks of kW4SmallMaxM rows, reading the weights once per block, which
+    // still beats the per-lane FMA kernel several times over
     if (a.bf16 && a.M > kW4SmallMaxM) {
         GemmArgs b = a;
         b.M = kW4SmallMaxM;
@@ -2100,9 +2124,6 @@ hipError_t launch_w4_gemv(const GemmArgs& a, void* workspace, size_t workspace_b
             return hipSuccess;
         }
     }
-    W4StreamPlan sp;
-    if (w4_use_stream(a, workspace ? workspace_bytes : 0, &sp))
-        return launch_w4_stream_t(SplitArgs{a, static_cast<float*>(workspace), sp.S, 1}, sp, s);
     if (!a.bf16 && a.M >= 3 && a.M <= kGemvMaxM && !a.zeros) {  // zero point 8 only
         const int64_t nrb = (a.N + 15) / 16;
         return nrb >= 1024 ? launch_w4_mfma_w<2>(a, s) : launch_w4_mfma_w<1>(a, s);

@@ -451,10 +451,10 @@ def test_w4_m1_one_hot_and_bias(N, K, dt):
 
 @pytest.mark.parametrize("M,N,K", [(5, 4096, 4096), (16, 28672, 4096), (11, 1024, 14336), (40, 320, 4096)])
 def test_w4_bf16_row_blocks(M, N, K):
-    """bf16 W4A16 past four rows: the small-M kernel over blocks of four rows
-    (inside blocks of 16 when M > 16), the last block ragged; one-hot rows
-    give C[m, n] = wdq[n, k_m] bit for bit, dense rows with a bias are within
-    the tolerance, the row past M is untouched."""
+    """bf16 W4A16 past four rows: the streaming kernel's bf16 form (inside
+    blocks of 16 rows when M > 16, the last block ragged); one-hot rows give
+    C[m, n] = wdq[n, k_m] bit for bit, dense rows with a bias are within the
+    tolerance, the row past M is untouched."""
     import torch
     import bit_weight_only_tq_amd as tq
     dev = require_gpu()
