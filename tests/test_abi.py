@@ -159,7 +159,7 @@ def test_w4_workspace_query():
     assert wb(1, 4096, 14336) == 0                       # M = 1 never splits
     assert wb(2, 4096, 14336) == 0                       # M = 2: the small-M kernel, no split
     assert wb(5, 4096, 14336) == 8 * 5 * 4096 * 4        # M = 5 streams: 112 groups -> 8 splits of 14
-    assert wb(16, 4096, 14336, "bf16") == 0
+    assert wb(16, 4096, 14336, "bf16") == wb(16, 4096, 14336)  # bf16 streams like fp16
     assert wb(16, 4096, 14336, group_size=64) == 0
     assert wb(40, 4096, 14336) == 8 * 16 * 4096 * 4      # blocks of 16 rows, the largest block's need
     assert wb(16, 4096, 200) == 0                         # K % 128 != 0
