@@ -112,6 +112,53 @@ def _need_cuda(*ts):
     for t in ts:
         if t is not None and (not t.is_cuda or not t.is_contiguous()):
             raise ValueError("tensors must be contiguous device tensors")
+    devs = {t.device for t in ts if t is not None}
+    if len(devs) > 1:
+        raise ValueError(f"tensors must live on one device, got {sorted(str(d) for d in devs)}")
+
+
+# Shape and dtype checks before any call: the C ABI takes bare pointers and
+# cannot check buffer sizes, so a mismatched tensor would make a kernel read
+# or write out of bounds.
+
+def _check_activations(A):
+    import torch
+    if A.dim() != 2:
+        raise ValueError(f"A must be 2-D [M, K], got shape {tuple(A.shape)}")
+    if A.dtype not in (torch.float16, torch.bfloat16):
+        raise TypeError(f"activations must be float16 or bfloat16, got {A.dtype}")
+    return A.shape
+
+
+def _check_out_bias(A, N, bias, out):
+    M = A.shape[0]
+    if bias is not None and (bias.dtype != A.dtype or tuple(bias.shape) != (N,)):
+        raise ValueError(f"bias must be {A.dtype} ({N},), got {bias.dtype} {tuple(bias.shape)}")
+    if out is not None and (out.dtype != A.dtype or tuple(out.shape) != (M, N)):
+        raise ValueError(f"out must be {A.dtype} ({M}, {N}), got {out.dtype} {tuple(out.shape)}")
+
+
+def _ternary_layout(codes, scale, K):
+    from .layout import TernaryLayout
+    if codes.dim() != 2:
+        raise ValueError(f"codes must be 2-D [N, ceil(K/4)], got shape {tuple(codes.shape)}")
+    lay = TernaryLayout(int(codes.shape[0]), int(K))
+    lay.validate(codes, scale)
+    return lay
+
+
+def _w4_layout(qweight, scales, K, group_size, zeros=None, perm=None):
+    import torch
+    from .layout import W4Layout
+    if qweight.dim() != 2:
+        raise ValueError(f"qweight must be 2-D [N, K/8], got shape {tuple(qweight.shape)}")
+    lay = W4Layout(int(qweight.shape[0]), int(K), int(group_size))
+    lay.validate(qweight, scales)
+    if zeros is not None and (zeros.dtype != torch.uint8 or tuple(zeros.shape) != lay.scales_shape):
+        raise ValueError(f"zeros must be uint8 {lay.scales_shape}, got {zeros.dtype} {tuple(zeros.shape)}")
+    if perm is not None and (perm.dtype != torch.int32 or tuple(perm.shape) != (lay.K,)):
+        raise ValueError(f"perm must be int32 ({lay.K},), got {perm.dtype} {tuple(perm.shape)}")
+    return lay
 
 
 # ------------------------------------------------------------------ prepare
@@ -132,8 +179,8 @@ def tq_pack(W):
 def tq_unpack(codes, scale, K: int, want_t: bool = True, want_wdq: bool = True):
     """-> (t int8 [N, K] or None, wdq fp16 [N, K] or None)."""
     import torch
+    N = _ternary_layout(codes, scale, K).N
     _need_cuda(codes, scale)
-    N = codes.shape[0]
     t = torch.empty((N, K), dtype=torch.int8, device=codes.device) if want_t else None
     w = torch.empty((N, K), dtype=torch.float16, device=codes.device) if want_wdq else None
     _check("tq_unpack", load().tq_unpack(_ptr(codes), _ptr(scale), N, K, _ptr(t), _ptr(w), _stream(codes.device)))
@@ -156,8 +203,8 @@ def w4a16_pack(W, group_size: int = 128):
 def w4a16_unpack(qweight, scales, K: int, group_size: int = 128, want_q: bool = True, want_wdq: bool = True):
     """-> (q uint8 [N, K] or None, wdq fp16 [N, K] or None)."""
     import torch
+    N = _w4_layout(qweight, scales, K, group_size).N
     _need_cuda(qweight, scales)
-    N = qweight.shape[0]
     q = torch.empty((N, K), dtype=torch.uint8, device=qweight.device) if want_q else None
     w = torch.empty((N, K), dtype=torch.float16, device=qweight.device) if want_wdq else None
     _check("w4a16_unpack", load().w4a16_unpack(_ptr(qweight), _ptr(scales), N, K, group_size,
@@ -189,8 +236,10 @@ def w4a16_unpack_asym(qweight, scales, zeros, K: int, perm=None, group_size: int
                       want_wdq: bool = True):
     """-> (q uint8 [N, K] packed order or None, wdq fp16 [N, K] input order or None)."""
     import torch
+    if zeros is None:
+        raise ValueError("zeros are required")
+    N = _w4_layout(qweight, scales, K, group_size, zeros, perm).N
     _need_cuda(qweight, scales, zeros, perm)
-    N = qweight.shape[0]
     q = torch.empty((N, K), dtype=torch.uint8, device=qweight.device) if want_q else None
     w = torch.empty((N, K), dtype=torch.float16, device=qweight.device) if want_wdq else None
     _check("w4a16_unpack_asym", load().w4a16_unpack_asym(_ptr(qweight), _ptr(scales), _ptr(zeros), _ptr(perm), N,
@@ -213,9 +262,10 @@ def tq_gemm(A, codes, scale, bias=None, out=None, path: str = "auto", workspace=
     torch's allocator (stream-ordered, so overlapping calls never share it);
     None runs without one; or a contiguous device tensor."""
     import torch
-    _need_cuda(A, codes, scale, bias)
-    M, K = A.shape
-    N = codes.shape[0]
+    M, K = _check_activations(A)
+    N = _ternary_layout(codes, scale, K).N
+    _check_out_bias(A, N, bias, out)
+    _need_cuda(A, codes, scale, bias, out)
     dt = _dtype_enum(A)
     C = out if out is not None else torch.empty((M, N), dtype=A.dtype, device=A.device)
     if isinstance(workspace, str):
@@ -223,7 +273,7 @@ def tq_gemm(A, codes, scale, bias=None, out=None, path: str = "auto", workspace=
         workspace = torch.empty((nbytes,), dtype=torch.uint8, device=A.device) if nbytes else None
     ws_bytes = 0
     if workspace is not None:
-        _need_cuda(workspace)
+        _need_cuda(A, workspace)
         ws_bytes = workspace.numel() * workspace.element_size()
     _check("tq_gemm", load().tq_gemm_ws(_ptr(A), dt, M, N, K, _ptr(codes), _ptr(scale), _ptr(bias), _ptr(C),
                                          _ptr(workspace), ws_bytes, _stream(A.device), PATHS[path]))
@@ -251,9 +301,10 @@ def w4a16_gemm(A, qweight, scales, bias=None, out=None, group_size: int = 128, p
     optional); with either, the zero-point entry point runs.
     workspace: as for tq_gemm ("auto", None or a contiguous device tensor)."""
     import torch
-    _need_cuda(A, qweight, scales, bias, zeros, perm)
-    M, K = A.shape
-    N = qweight.shape[0]
+    M, K = _check_activations(A)
+    N = _w4_layout(qweight, scales, K, group_size, zeros, perm).N
+    _check_out_bias(A, N, bias, out)
+    _need_cuda(A, qweight, scales, bias, zeros, perm, out)
     dt = _dtype_enum(A)
     C = out if out is not None else torch.empty((M, N), dtype=A.dtype, device=A.device)
     asym = zeros is not None or perm is not None
@@ -265,7 +316,7 @@ def w4a16_gemm(A, qweight, scales, bias=None, out=None, group_size: int = 128, p
         workspace = torch.empty((nbytes,), dtype=torch.uint8, device=A.device) if nbytes else None
     ws_bytes = 0
     if workspace is not None:
-        _need_cuda(workspace)
+        _need_cuda(A, workspace)
         ws_bytes = workspace.numel() * workspace.element_size()
     if asym:
         _check("w4a16_gemm_asym", load().w4a16_gemm_asym(

@@ -76,7 +76,11 @@ const char* tq_status_str(tq_status s) {
 }
 
 tq_path tq_select_path(int format, int64_t M, int64_t N, int64_t K, tq_dtype dt) {
-    (void)N; (void)K; (void)dt;
+    (void)N; (void)dt;
+    // Ternary rows that are not whole 256-column chunk-sets leave the decode
+    // kernels only their per-lane FMA form; from three activation rows the
+    // medium path's matrix-core tiles (any K % 64 == 0) are faster.
+    if (format == 0 && M >= 3 && M <= kGemvMaxM && K % 256 != 0) return TQ_PATH_STREAM_MFMA;
     if (M <= kGemvMaxM) return TQ_PATH_GEMV;
     if (format == 1) return TQ_PATH_GEMV;  // W4A16: small-M kernel over blocks of rows
     if (M < kMediumMaxM) return TQ_PATH_STREAM_MFMA;

@@ -7,14 +7,15 @@
 // asynchronous weight staging through shared memory).  Tiles here are sized
 // for gfx950 (64-wide waves, 160 KB LDS), not for the page's 32x32 blocks.
 //
-// Unpacking codes into matrix-core operands costs about one VALU op per
-// code: a pair of 2-bit fields is masked straight into the low mantissa bits
-// of the constant MAGIC (1024.0 in fp16, 128.0 in bf16, whose unit in the
-// last place is 1), giving the exact values MAGIC + c for c in {0, 1, 2}.
-// Since t = c - 1,
-//   sum_k a_k t_k = sum_k a_k (MAGIC + c_k) - (MAGIC + 1) sum_k a_k,
-// and the row sums of A are accumulated alongside with dot2, so the
-// correction is one FMA per output.
+// Unpacking codes into matrix-core operands: a pair of 2-bit fields is
+// masked straight into the low mantissa bits of the fp16 constant 1024
+// (unit in the last place 1), giving the exact values 1024 + c for c in
+// {0, 1, 2}, and one packed fp16 subtract of 1025 leaves the ternary value
+// t = c - 1 itself (exact).  The matrix units therefore multiply every
+// activation by -1, 0 or +1 and the fp32 sums hold only the terms of the
+// result, so the error of an output scales with its own sum_k |a_k t_k|.
+// bf16 activations take the same operand bits, which read as bf16 are
+// -2^-7, 0, +2^-7; those kernels multiply their sums by 128 (exact).
 
 #include <type_traits>
 
@@ -28,28 +29,29 @@ namespace {
 template <class T> struct Mfma;
 template <> struct Mfma<F16> {
     typedef f16x8 vec;
-    static constexpr uint32_t kMagicPair = 0x64006400u;  // 1024.0 in both halves
-    static constexpr float kBias = 1025.0f;              // MAGIC + 1
+    static constexpr float kUnit = 1.0f;  // value of the operand bits of +1
     static __device__ __forceinline__ f32x4 mma(vec a, vec b, f32x4 c) {
         return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
     }
-    static __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
-        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), c, false);
-    }
-    static constexpr uint32_t kOnePair = 0x3C003C00u;     // (1.0, 1.0)
 };
 template <> struct Mfma<BF16> {
     typedef bf16x8 vec;
-    static constexpr uint32_t kMagicPair = 0x43004300u;  // 128.0 in both halves
-    static constexpr float kBias = 129.0f;
+    static constexpr float kUnit = kBf16TernaryUnit;  // the operand bits of +1 read as bf16 are 2^-7
     static __device__ __forceinline__ f32x4 mma(vec a, vec b, f32x4 c) {
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
     }
-    static __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
-        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
-    }
-    static constexpr uint32_t kOnePair = 0x3F803F80u;
 };
+
+// Natural-order operand pair j of a half dword of fields (see v3 below):
+// (1024 + c) - 1025 = c - 1, exact in fp16.
+__device__ __forceinline__ uint32_t nat_pair(uint32_t y, int j, uint32_t mask3, uint32_t magic_v) {
+    const uint32_t v = ((y >> (4 * j)) & mask3) | magic_v;
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, v) + __builtin_bit_cast(f16x2, 0xE401E401u));
+}
+__device__ __forceinline__ uint4 nat_quad(uint32_t y, uint32_t mask3, uint32_t magic_v) {
+    return make_uint4(nat_pair(y, 0, mask3, magic_v), nat_pair(y, 1, mask3, magic_v), nat_pair(y, 2, mask3, magic_v),
+                      nat_pair(y, 3, mask3, magic_v));
+}
 
 // Bare workgroup barrier: __syncthreads() would add a release fence that
 // waits for every outstanding DMA, including the stage issued ahead.
@@ -65,20 +67,17 @@ __device__ __forceinline__ void stage_barrier() {
 //  - activations: 256 rows x 64 columns per stage, natural column order,
 //    16-byte chunks XOR-swizzled (chunk c of row r at position c ^ (r % 8));
 //  - codes: 256 weight rows x 16 bytes (64 columns) per stage.
-// Codes are unpacked in registers into natural-order fp16 / bf16 pairs
-// (f_2j, f_2j+1):  E = x & 0x33333333 (even fields), O = (x >> 2) & 0x33333333
-// (odd fields), Y = byte-merge(E, O) per half dword, pair j = ((Y >> 4j) &
-// 0x00030003) | MAGIC; in fp16 one packed subtract of 1025 then gives the
-// ternary value c - 1 itself.  Block tile 256 x 256 (128 x 256 for the
-// last round of an unbalanced grid), K-step 64, eight waves (2 x 4) of
-// 128 x 64 (64 x 64) outputs; MFMA s of a K-step (s = 0, 1) takes 8-column
-// chunk 2g + s for lane group g.  In bf16 the row sums of A for the MAGIC
-// correction are split over the four waves sharing a row block (m-tiles wn
-// and wn + 4).  The
-// epilogue stages each wave's outputs through LDS so that every lane stores
-// 16 contiguous bytes.  With a K split (blockIdx.z = split z of S, K-steps
-// [z*nk/S, (z+1)*nk/S)) the fp32 partials (row-sum correction applied) are
-// stored straight from the accumulators instead.
+// Codes are unpacked in registers into natural-order pairs (f_2j, f_2j+1):
+// E = x & 0x33333333 (even fields), O = (x >> 2) & 0x33333333 (odd fields),
+// Y = byte-merge(E, O) per half dword, pair j = ((Y >> 4j) & 0x00030003) |
+// 1024.0, and one packed fp16 subtract of 1025 gives the ternary value c - 1
+// itself (nat_pair).  Block tile 256 x 256 (128 x 256 for the last round of
+// an unbalanced grid), K-step 64, eight waves (2 x 4) of 128 x 64 (64 x 64)
+// outputs; MFMA s of a K-step (s = 0, 1) takes 8-column chunk 2g + s for
+// lane group g.  The epilogue stages each wave's outputs through LDS so that
+// every lane stores 16 contiguous bytes.  With a K split (blockIdx.z = split
+// z of S, K-steps [z*nk/S, (z+1)*nk/S)) the fp32 partials (in units of the
+// result) are stored straight from the accumulators instead.
 namespace v3 {
 
 constexpr int BN = 256;
@@ -100,32 +99,20 @@ struct Tile {
     static constexpr int WM = BM / 2;               // rows per wave
     static constexpr int TM = WM / 16;              // m-tiles per wave
     static constexpr int AU = BM / 64;              // 1-KB activation DMA blocks per wave and stage
-    static constexpr int RS = TM / 4;               // m-tiles per wave in the row sums
     static constexpr int kABytes = BM * BK * 2;     // unpadded (swizzled)
     static constexpr int kStageBytes = kABytes + kBBytes;
     static constexpr size_t kLdsBytes = (size_t)kStages * kStageBytes;
-    static_assert(8 * kEpiBytesPerWave + BM * 4 <= (int)kLdsBytes, "epilogue staging must fit in the ring");
+    static_assert(8 * kEpiBytesPerWave <= (int)kLdsBytes, "epilogue staging must fit in the ring");
 };
 
 template <class T, int BMT>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(SplitArgs sa) {
     typedef typename Mfma<T>::vec vec;
     typedef Tile<BMT> G;
-    constexpr int BM = G::BM, WM = G::WM, TM = G::TM, AU = G::AU, RS = G::RS;
+    constexpr int BM = G::BM, WM = G::WM, TM = G::TM, AU = G::AU;
     constexpr int kABytes = G::kABytes, kStageBytes = G::kStageBytes;
     const GemmArgs& p = sa.g;
     const int64_t ldc = sa.ldc ? sa.ldc : p.N;       // row stride of C
-    // fp16: the operand holds the ternary value itself, (1024 + c) - 1025 =
-    // c - 1 in one packed fp16 subtract per pair (exact), so no row sums and
-    // no correction are needed, and the matrix multipliers see +-1 and 0
-    // instead of 1024 + c (less switching on a power-limited part, and no
-    // cancellation of 1025 sum a in fp32).  bf16 keeps MAGIC + c and the
-    // row-sum correction.
-    constexpr bool kExactB = std::is_same<T, F16>::value;
-    auto bfix = [](uint32_t v) -> uint32_t {
-        if constexpr (kExactB) return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, v) + __builtin_bit_cast(f16x2, 0xE401E401u));
-        else return v;
-    };
     extern __shared__ uint4 smem_v3[];
     uint8_t* lds = reinterpret_cast<uint8_t*>(smem_v3);
     const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)smem_v3;
@@ -140,7 +127,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(SplitArgs sa) {
     const int64_t n0 = (int64_t)blockIdx.x * BN;
     const int64_t M = p.M, N = p.N, K = p.K;
     const int64_t rb = K / 4;
-    const uint32_t magic_v = vgpr_const<Mfma<T>::kMagicPair>();
+    const uint32_t magic_v = vgpr_const<kMagic2>();
     const uint32_t mask3 = sgpr_const<0x00030003u>();
     const uint32_t mask33 = sgpr_const<0x33333333u>();
 
@@ -183,9 +170,6 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(SplitArgs sa) {
     for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float rsum[RS];  // row sums for m-tiles wn (and wn + 4 when TM = 8)
-#pragma unroll
-    for (int t = 0; t < RS; ++t) rsum[t] = 0.f;
 
     // fragment row R = wm*128 + 16i + i16 (R % 8 == i16 % 8): chunk c at
     // byte R*128 + 16*(c ^ (i16 & 7)) of a stage
@@ -224,21 +208,8 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(SplitArgs sa) {
                 af[i] = __builtin_bit_cast(vec, *reinterpret_cast<const uint4*>(sbase + frag_base + i * 16 * (BK * 2) + 16 * chunk));
             uint4 bop[TN];
 #pragma unroll
-            for (int j = 0; j < TN; ++j) {
-                const uint32_t y = __builtin_amdgcn_perm(O[j], E[j], s ? 0x07060302u : 0x05040100u);
-                bop[j] = make_uint4(bfix((y & mask3) | magic_v), bfix(((y >> 4) & mask3) | magic_v),
-                                    bfix(((y >> 8) & mask3) | magic_v), bfix(((y >> 12) & mask3) | magic_v));
-            }
-#pragma unroll
-            for (int t = 0; t < (kExactB ? 0 : RS); ++t) {  // this wave's share of the row sums: m-tiles wn (, wn + 4)
-                const uint4 v = *reinterpret_cast<const uint4*>(sbase + frag_base + (wn + 4 * t) * 16 * (BK * 2) + 16 * chunk);
-                float r = rsum[t];
-                r = Mfma<T>::dot2(v.x, Mfma<T>::kOnePair, r);
-                r = Mfma<T>::dot2(v.y, Mfma<T>::kOnePair, r);
-                r = Mfma<T>::dot2(v.z, Mfma<T>::kOnePair, r);
-                r = Mfma<T>::dot2(v.w, Mfma<T>::kOnePair, r);
-                rsum[t] = r;
-            }
+            for (int j = 0; j < TN; ++j)
+                bop[j] = nat_quad(__builtin_amdgcn_perm(O[j], E[j], s ? 0x07060302u : 0x05040100u), mask3, magic_v);
 #pragma unroll
             for (int j = 0; j < TN; ++j) {
                 const vec bf = __builtin_bit_cast(vec, bop[j]);
@@ -252,17 +223,6 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(SplitArgs sa) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();        // the ring is idle from here on
 
-    // row sums -> LDS
-    float* rs_lds = reinterpret_cast<float*>(lds + 8 * kEpiBytesPerWave);
-#pragma unroll
-    for (int t = 0; t < RS; ++t) {
-        float r = rsum[t];
-        r += __shfl_xor(r, 16, kWave);
-        r += __shfl_xor(r, 32, kWave);
-        if (g == 0) rs_lds[wm * WM + 16 * (wn + 4 * t) + i16] = r;
-    }
-    __syncthreads();
-
     if (sa.S > 1) {  // fp32 partial of this split: 16 lanes store 64 contiguous bytes per row
         float* ws = sa.ws + (int64_t)blockIdx.z * M * N;
 #pragma unroll
@@ -272,11 +232,10 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(SplitArgs sa) {
                 const int row = wm * WM + 16 * i + 4 * g + r;
                 const int64_t m = m0 + row;
                 if (m >= M) continue;
-                const float rs = kExactB ? 0.0f : Mfma<T>::kBias * rs_lds[row];
 #pragma unroll
                 for (int j = 0; j < TN; ++j) {
                     const int64_t n = n0 + wn * WN + 16 * j + i16;
-                    if (n < N) ws[m * N + n] = acc[i][j][r] - rs;
+                    if (n < N) ws[m * N + n] = acc[i][j][r] * Mfma<T>::kUnit;
                 }
             }
         return;
@@ -289,7 +248,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(SplitArgs sa) {
     for (int j = 0; j < TN; ++j) {
         const int64_t n = n0 + wn * WN + 16 * j + i16;
         const int64_t nc = n < N ? n : N - 1;
-        sc[j] = f16_bits_to_f32(p.scale[nc]);
+        sc[j] = f16_bits_to_f32(p.scale[nc]) * Mfma<T>::kUnit;
         bi[j] = p.bias ? T::to_f32(p.bias[nc]) : 0.0f;
     }
     const bool vec_ok = ((N | ldc) % 8) == 0;
@@ -301,10 +260,9 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(SplitArgs sa) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int row = 16 * ii + 4 * g + r;
-                const float rs = rs_lds[wm * WM + 16 * i + 4 * g + r];
 #pragma unroll
                 for (int j = 0; j < TN; ++j)
-                    stg[row * kEpiLd + 16 * j + i16] = T::from_f32_fast((acc[i][j][r] - (kExactB ? 0.0f : Mfma<T>::kBias * rs)) * sc[j] + bi[j]);
+                    stg[row * kEpiLd + 16 * j + i16] = T::from_f32_fast(acc[i][j][r] * sc[j] + bi[j]);
             }
         }
         // each lane stores 16 contiguous bytes: row lane/8 + 8q, columns 8*(lane%8) .. +7
@@ -349,7 +307,7 @@ constexpr int kAhead = kStages - 1;
 constexpr int kBBytes = BN * BK / 4;  // 4 KB of codes per stage
 template <int TM> constexpr int a_bytes() { return 16 * TM * BK * 2; }
 template <int TM> constexpr int stage_bytes() { return a_bytes<TM>() + kBBytes; }
-template <int TM> constexpr size_t lds_bytes() { return (size_t)kStages * stage_bytes<TM>() + 16 * TM * 4; }
+template <int TM> constexpr size_t lds_bytes() { return (size_t)kStages * stage_bytes<TM>(); }
 
 template <class T, int TM>
 __global__ __launch_bounds__(kThreads) void tile_kernel(SplitArgs sa) {
@@ -375,7 +333,7 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(SplitArgs sa) {
     const int nk = (int)(K / BK);
     const int ks0 = (int)((int64_t)nk * z / sa.S);
     const int ks1 = (int)((int64_t)nk * (z + 1) / sa.S);  // > ks0: S <= nk
-    const uint32_t magic_v = vgpr_const<Mfma<T>::kMagicPair>();
+    const uint32_t magic_v = vgpr_const<kMagic2>();
     const uint32_t mask3 = sgpr_const<0x00030003u>();
     const uint32_t mask33 = sgpr_const<0x33333333u>();
 
@@ -419,8 +377,6 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(SplitArgs sa) {
     for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float rsum = 0.0f;  // row sums of m-tile (wave % TM), kept by waves 0 .. TM-1
-    const int rs_tile = wave % TM;
     const int swz = i16 & 7;
     const int frag_base = i16 * (BK * 2);
     const int b_frag = kABytes + (32 * wave + i16) * 16 + 4 * g;
@@ -450,21 +406,8 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(SplitArgs sa) {
                 af[i] = __builtin_bit_cast(vec, *reinterpret_cast<const uint4*>(sbase + frag_base + i * 16 * (BK * 2) + 16 * chunk));
             uint4 bop[TN];
 #pragma unroll
-            for (int j = 0; j < TN; ++j) {
-                const uint32_t y = __builtin_amdgcn_perm(O[j], E[j], s ? 0x07060302u : 0x05040100u);
-                bop[j] = make_uint4((y & mask3) | magic_v, ((y >> 4) & mask3) | magic_v,
-                                    ((y >> 8) & mask3) | magic_v, ((y >> 12) & mask3) | magic_v);
-            }
-#pragma unroll
-            for (int i = 0; i < TM; ++i) {
-                if (i == rs_tile) {  // wave-uniform
-                    const uint4 v = __builtin_bit_cast(uint4, af[i]);
-                    rsum = Mfma<T>::dot2(v.x, Mfma<T>::kOnePair, rsum);
-                    rsum = Mfma<T>::dot2(v.y, Mfma<T>::kOnePair, rsum);
-                    rsum = Mfma<T>::dot2(v.z, Mfma<T>::kOnePair, rsum);
-                    rsum = Mfma<T>::dot2(v.w, Mfma<T>::kOnePair, rsum);
-                }
-            }
+            for (int j = 0; j < TN; ++j)
+                bop[j] = nat_quad(__builtin_amdgcn_perm(O[j], E[j], s ? 0x07060302u : 0x05040100u), mask3, magic_v);
 #pragma unroll
             for (int j = 0; j < TN; ++j) {
                 const vec bf = __builtin_bit_cast(vec, bop[j]);
@@ -476,16 +419,6 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(SplitArgs sa) {
         stage_barrier();    // ... for every wave, and nobody reads stage kt any more
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-
-    float* rs_lds = reinterpret_cast<float*>(lds + kStages * kStageBytes);
-    {
-        float r = rsum;
-        r += __shfl_xor(r, 16, kWave);
-        r += __shfl_xor(r, 32, kWave);
-        if (wave < TM && g == 0) rs_lds[16 * wave + i16] = r;
-    }
-    __syncthreads();
 
     const bool final_out = sa.S == 1;
     float sc[TN], bi[TN];
@@ -504,12 +437,11 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(SplitArgs sa) {
             const int row = 16 * i + 4 * g + r;
             const int64_t m = m0 + row;
             if (m >= M) continue;
-            const float corr = Mfma<T>::kBias * rs_lds[row];
 #pragma unroll
             for (int j = 0; j < TN; ++j) {
                 const int64_t n = n0 + 32 * wave + 16 * j + i16;
                 if (n >= N) continue;
-                const float v = acc[i][j][r] - corr;
+                const float v = acc[i][j][r] * Mfma<T>::kUnit;
                 if (final_out) p.C[m * N + n] = T::from_f32_fast(v * sc[j] + bi[j]);
                 else wsz[m * N + n] = v;
             }
@@ -548,220 +480,28 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(SplitArgs sa) {
 
 }  // namespace mm
 
+
 // ------------------------------------------------------------------------
-// Medium M, K % 256 == 0: the tile of the kernel above (16TM activation rows
-// x 256 weight rows, eight waves of 32 weight rows each, optional K split)
-// with 256-column K-steps in a 3-slot LDS ring filled two steps ahead, so
-// that each barrier covers 8TM MFMAs per wave and every DMA instruction
-// reads whole row segments:
+// Medium M, K % 256 == 0 (fp16 or bf16): 16TM activation rows x 256 weight
+// rows per workgroup, eight waves of 32 weight rows each, optional K split,
+// with 256-column K-steps in an LDS ring filled R - 1 steps ahead, so that
+// each barrier covers 8TM MFMAs per wave and every DMA instruction reads
+// whole row segments:
 //  - codes: 256 rows x 64 bytes per step, 16 rows per instruction (lane l:
 //    row l/4, 16-byte chunk l%4); chunk c of row r sits at c ^ ((r/4) % 4)
 //    so that the 64 lanes' dword reads of a fragment hit 64 different banks;
 //  - activations: 16TM rows x 512 bytes per step, 2 rows per instruction
 //    (lane l: row l/32, chunk l%32); chunk c of row r at c ^ (r % 16).
-// Within a step, sub-step u (0..3) covers columns 64u .. 64u+63 exactly as
-// one K-step of the kernel above: MFMA s of lane group g takes the 8 columns
-// 64u + 16g + 8s .., codes dword u of the row segment, unpacked the same way.
-namespace mm2 {
-
-constexpr int BN = 256;
-constexpr int BK = 256;
-constexpr int kThreads = 512;
-constexpr int TN = 2;
-constexpr int kStages = 3;
-constexpr int kBBytes = BN * (BK / 4);  // 16 KB of codes per step
-template <int TM> constexpr int a_bytes() { return 16 * TM * BK * 2; }
-template <int TM> constexpr int stage_bytes() { return a_bytes<TM>() + kBBytes; }
-template <int TM> constexpr size_t lds_bytes() { return (size_t)kStages * stage_bytes<TM>() + 16 * TM * 4; }
-
-template <class T, int TM>
-__global__ __launch_bounds__(kThreads) void tile_kernel(SplitArgs sa) {
-    typedef typename Mfma<T>::vec vec;
-    constexpr int BM = 16 * TM;
-    constexpr int kABytes = a_bytes<TM>();
-    constexpr int kStageBytes = stage_bytes<TM>();
-    const GemmArgs& p = sa.g;
-    extern __shared__ uint4 smem_mm2[];
-    uint8_t* lds = reinterpret_cast<uint8_t*>(smem_mm2);
-    const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)smem_mm2;
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int g = lane >> 4;
-    const int i16 = lane & 15;
-    const int64_t n0 = (int64_t)blockIdx.x * BN;
-    const int64_t m0 = (int64_t)blockIdx.y * BM;
-    const int z = blockIdx.z;
-    const int64_t M = p.M, N = p.N, K = p.K;
-    const int64_t rb = K / 4;
-    const int nk = (int)(K / BK);
-    const int ks0 = (int)((int64_t)nk * z / sa.S);
-    const int ks1 = (int)((int64_t)nk * (z + 1) / sa.S);  // > ks0: S <= nk
-    const uint32_t magic_v = vgpr_const<Mfma<T>::kMagicPair>();
-    const uint32_t mask3 = sgpr_const<0x00030003u>();
-    const uint32_t mask33 = sgpr_const<0x33333333u>();
-
-    // DMA sources.  Activations: wave w issues instructions w*TM .. w*TM+TM-1
-    // (rows 2i, 2i+1 of the tile; rows past M re-read row M-1).  Codes: wave w
-    // issues instructions 2w, 2w+1 (rows 16j .. 16j+15; rows past N re-read
-    // row N-1).  Offsets are relative to the K-step's first column.
-    const uint16_t* a_src[TM];
-#pragma unroll
-    for (int u = 0; u < TM; ++u) {
-        const int r = 2 * (wave * TM + u) + (lane >> 5);
-        const int64_t m = m0 + r < M ? m0 + r : M - 1;
-        a_src[u] = p.A + m * K + 8 * ((lane & 31) ^ (r & 15));
-    }
-    const uint8_t* b_src[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int r = 16 * (2 * wave + u) + (lane >> 2);
-        const int64_t n = n0 + r < N ? n0 + r : N - 1;
-        b_src[u] = static_cast<const uint8_t*>(p.wq) + n * rb + 16 * ((lane & 3) ^ ((r >> 2) & 3));
-    }
-    auto issue = [&](int kstep, int stage) {
-        const uint32_t st = lds_base + (uint32_t)(stage * kStageBytes);
-#pragma unroll
-        for (int u = 0; u < TM; ++u) dma16(a_src[u] + (int64_t)kstep * BK, st + 1024u * (wave * TM + u));
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-            dma16(b_src[u] + (int64_t)kstep * (BK / 4), st + kABytes + 1024u * (2 * wave + u));
-    };
-    // the older of the two K-steps in flight has landed (in-order completion:
-    // only the newer step's TM + 2 DMAs of this wave may remain)
-    auto wait_older = [&]() {
-        if constexpr (TM == 2) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-        else asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
-    };
-    static_assert(TM == 2 || TM == 4, "wait counts above assume TM + 2 DMAs per step");
-
-    f32x4 acc[TM][TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float rsum = 0.0f;  // row sums of m-tile `wave`, kept by waves 0 .. TM-1
-    int b_row[TN], b_swz[TN];
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-        b_row[j] = 32 * wave + 16 * j + i16;
-        b_swz[j] = (b_row[j] >> 2) & 3;
-    }
-
-    issue(ks0, 0);
-    issue(ks0 + 1 < ks1 ? ks0 + 1 : ks1 - 1, 1);
-    wait_older();
-    stage_barrier();
-    for (int kt = ks0; kt < ks1; ++kt) {
-        const int it = kt - ks0;
-        // Unconditional so the per-wave counts stay exact: past the end the DMA
-        // re-reads the last K-step into the slot nobody reads any more.
-        issue(kt + 2 < ks1 ? kt + 2 : ks1 - 1, (it + 2) % kStages);
-        const uint8_t* sbase = lds + (it % kStages) * kStageBytes;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            uint32_t E[TN], O[TN];
-#pragma unroll
-            for (int j = 0; j < TN; ++j) {
-                const uint32_t x = *reinterpret_cast<const uint32_t*>(sbase + kABytes + b_row[j] * 64 +
-                                                                      16 * (u ^ b_swz[j]) + 4 * g);
-                E[j] = x & mask33;
-                O[j] = (x >> 2) & mask33;
-            }
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                const int c = 8 * u + 2 * g + s;
-                vec af[TM];
-#pragma unroll
-                for (int i = 0; i < TM; ++i)
-                    af[i] = __builtin_bit_cast(vec, *reinterpret_cast<const uint4*>(sbase + (16 * i + i16) * 512 +
-                                                                                   16 * (c ^ i16)));
-                uint4 bop[TN];
-#pragma unroll
-                for (int j = 0; j < TN; ++j) {
-                    const uint32_t y = __builtin_amdgcn_perm(O[j], E[j], s ? 0x07060302u : 0x05040100u);
-                    bop[j] = make_uint4((y & mask3) | magic_v, ((y >> 4) & mask3) | magic_v,
-                                        ((y >> 8) & mask3) | magic_v, ((y >> 12) & mask3) | magic_v);
-                }
-#pragma unroll
-                for (int i = 0; i < TM; ++i) {
-                    if (i == wave) {  // wave-uniform
-                        const uint4 v = __builtin_bit_cast(uint4, af[i]);
-                        rsum = Mfma<T>::dot2(v.x, Mfma<T>::kOnePair, rsum);
-                        rsum = Mfma<T>::dot2(v.y, Mfma<T>::kOnePair, rsum);
-                        rsum = Mfma<T>::dot2(v.z, Mfma<T>::kOnePair, rsum);
-                        rsum = Mfma<T>::dot2(v.w, Mfma<T>::kOnePair, rsum);
-                    }
-                }
-#pragma unroll
-                for (int j = 0; j < TN; ++j) {
-                    const vec bf = __builtin_bit_cast(vec, bop[j]);
-#pragma unroll
-                    for (int i = 0; i < TM; ++i) acc[i][j] = Mfma<T>::mma(af[i], bf, acc[i][j]);
-                }
-            }
-        }
-        wait_older();       // K-step kt + 1 has landed
-        stage_barrier();    // ... for every wave, and nobody reads step kt any more
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-
-    float* rs_lds = reinterpret_cast<float*>(lds + kStages * kStageBytes);
-    {
-        float r = rsum;
-        r += __shfl_xor(r, 16, kWave);
-        r += __shfl_xor(r, 32, kWave);
-        if (wave < TM && g == 0) rs_lds[16 * wave + i16] = r;
-    }
-    __syncthreads();
-
-    const bool final_out = sa.S == 1;
-    float sc[TN], bi[TN];
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-        const int64_t n = n0 + 32 * wave + 16 * j + i16;
-        const int64_t nc = n < N ? n : N - 1;
-        sc[j] = f16_bits_to_f32(p.scale[nc]);
-        bi[j] = p.bias ? T::to_f32(p.bias[nc]) : 0.0f;
-    }
-    float* wsz = final_out ? nullptr : sa.ws + (int64_t)z * M * N;
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int row = 16 * i + 4 * g + r;
-            const int64_t m = m0 + row;
-            if (m >= M) continue;
-            const float corr = Mfma<T>::kBias * rs_lds[row];
-#pragma unroll
-            for (int j = 0; j < TN; ++j) {
-                const int64_t n = n0 + 32 * wave + 16 * j + i16;
-                if (n >= N) continue;
-                const float v = acc[i][j][r] - corr;
-                if (final_out) p.C[m * N + n] = T::from_f32_fast(v * sc[j] + bi[j]);
-                else wsz[m * N + n] = v;
-            }
-        }
-    }
-}
-
-}  // namespace mm2
-
-// ------------------------------------------------------------------------
-// Medium M, fp16, K % 256 == 0: the tiles, DMA layouts and split of mm2, but
-// the codes are unpacked with the fp16 a' scheme (one v_and_or_b32 per
-// operand register instead of about two and a half).  That needs the
-// activations paired and pre-scaled by 1/4^s, which is done once per K-step
-// for the whole workgroup, in place in the ring slot: thread t owns the
-// 16-column groups (row t/16 + 32p, group t%16) and rewrites each group's two
-// 16-byte chunks (columns 16G..16G+7 and 16G+8..) as its a' pairs for fields
-// 0..3 and 4..7, keeping the chunk positions (c ^ (r % 16)); it also sums
-// its share of D[m] = sum_k a'_k (1024 + 4^s(k)), the term the accumulators
-// carry on top of sum_k a_k t_k.  The prep of step k+1 shares a phase with
-// the MFMAs of step k, so one barrier per step still suffices:
-//   issue DMA of step k + R - 1; prep step k + 1; contract step k;
+// Codes are unpacked with the in-place field scheme of the decode kernels
+// (tern_pair: one v_and_or_b32 and one packed fp16 fma per operand
+// register).  That needs the activations paired to match the fields, which
+// is done once per K-step for the whole workgroup, in place in the ring
+// slot: thread t owns the 16-column groups (row t/16 + 32p, group t%16) and
+// rewrites each group's two 16-byte chunks (columns 16G..16G+7 and 16G+8..)
+// as its pairs for fields 0..3 and 4..7, keeping the chunk positions
+// (c ^ (r % 16)).  The pairing of step k+1 shares a phase with the MFMAs of
+// step k, so one barrier per step still suffices:
+//   issue DMA of step k + R - 1; pair step k + 1; contract step k;
 //   wait for the DMA of step k + 2; barrier,
 // with R = 4 ring slots for 32 activation rows and 3 for 64 (LDS).
 // Sub-step u, half h of a K-step: lane group g contracts 16-column group
@@ -776,32 +516,22 @@ constexpr int kBBytes = BN * (BK / 4);  // 16 KB of codes per step
 template <int TM> constexpr int a_bytes() { return 16 * TM * BK * 2; }
 template <int TM> constexpr int stage_bytes() { return a_bytes<TM>() + kBBytes; }
 template <int TM> constexpr int slots() { return TM == 2 ? 4 : 3; }
-template <int TM> constexpr size_t lds_bytes() { return (size_t)slots<TM>() * stage_bytes<TM>() + 16 * TM * 4; }
+template <int TM> constexpr size_t lds_bytes() { return (size_t)slots<TM>() * stage_bytes<TM>(); }
 
-// In-place a' prep of one 16-column group of one activation row; returns
-// its share of D.
-__device__ __forceinline__ float prep_group(uint8_t* row, int G, int swz) {
+// In-place pairing of one 16-column group of one activation row.
+__device__ __forceinline__ void prep_group(uint8_t* row, int G, int swz) {
     uint4* p0 = reinterpret_cast<uint4*>(row + 16 * ((2 * G) ^ swz));
     uint4* p1 = reinterpret_cast<uint4*>(row + 16 * ((2 * G + 1) ^ swz));
     uint4 av[2] = {*p0, *p1};  // columns 16G .. 16G+7, 16G+8 .. 16G+15
-    const uint4 f03 = make_uint4(a_pair<0, 0>(av), a_pair<0, 1>(av), a_pair<0, 2>(av), a_pair<0, 3>(av));
-    const uint4 f47 = make_uint4(a_pair<0, 4>(av), a_pair<0, 5>(av), a_pair<0, 6>(av), a_pair<0, 7>(av));
+    uint4 f03, f47;
+    act_pairs16<0>(av, f03, f47);
     *p0 = f03;
     *p1 = f47;
-    float d = 0.0f;
-    d = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, f03.x), __builtin_bit_cast(f16x2, one_pattern<0>()), d, false);
-    d = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, f03.y), __builtin_bit_cast(f16x2, one_pattern<1>()), d, false);
-    d = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, f03.z), __builtin_bit_cast(f16x2, one_pattern<2>()), d, false);
-    d = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, f03.w), __builtin_bit_cast(f16x2, one_pattern<3>()), d, false);
-    d = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, f47.x), __builtin_bit_cast(f16x2, one_pattern<4>()), d, false);
-    d = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, f47.y), __builtin_bit_cast(f16x2, one_pattern<5>()), d, false);
-    d = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, f47.z), __builtin_bit_cast(f16x2, one_pattern<6>()), d, false);
-    d = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, f47.w), __builtin_bit_cast(f16x2, one_pattern<7>()), d, false);
-    return d;
 }
 
-template <int TM>
+template <class T, int TM>
 __global__ __launch_bounds__(kThreads) void tile_kernel(SplitArgs sa) {
+    typedef typename Mfma<T>::vec vec;
     constexpr int BM = 16 * TM;
     constexpr int kABytes = a_bytes<TM>();
     constexpr int kStageBytes = stage_bytes<TM>();
@@ -851,15 +581,12 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(SplitArgs sa) {
     };
     auto clamp_step = [&](int k) { return k < ks1 ? k : ks1 - 1; };
 
-    // prep units of this thread: row tid/16 + 32q, group tid%16
-    float dsum[TM / 2];
-#pragma unroll
-    for (int q = 0; q < TM / 2; ++q) dsum[q] = 0.0f;
+    // pairing units of this thread: row tid/16 + 32q, group tid%16
     auto prep = [&](int slot) {
 #pragma unroll
         for (int q = 0; q < TM / 2; ++q) {
             const int r = (tid >> 4) + 32 * q;
-            dsum[q] += prep_group(lds + slot * kStageBytes + r * 512, tid & 15, r & 15);
+            prep_group(lds + slot * kStageBytes + r * 512, tid & 15, r & 15);
         }
     };
 
@@ -895,30 +622,23 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(SplitArgs sa) {
         const uint8_t* sbase = lds + (it % R) * kStageBytes;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            uint32_t x[TN], y[TN];
+            uint32_t x[TN];
 #pragma unroll
-            for (int j = 0; j < TN; ++j) {
-                x[j] = *reinterpret_cast<const uint32_t*>(sbase + b_off[j] + 16 * (u ^ b_swz[j]));
-                y[j] = x[j] >> 10;
-            }
+            for (int j = 0; j < TN; ++j) x[j] = *reinterpret_cast<const uint32_t*>(sbase + b_off[j] + 16 * (u ^ b_swz[j]));
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const int q = 2 * (4 * u + g) + h;
-                f16x8 af[TM];
+                vec af[TM];
 #pragma unroll
                 for (int i = 0; i < TM; ++i)
-                    af[i] = __builtin_bit_cast(f16x8, *reinterpret_cast<const uint4*>(sbase + (16 * i + i16) * 512 +
-                                                                                     16 * (q ^ i16)));
+                    af[i] = __builtin_bit_cast(vec, *reinterpret_cast<const uint4*>(sbase + (16 * i + i16) * 512 +
+                                                                                   16 * (q ^ i16)));
 #pragma unroll
                 for (int j = 0; j < TN; ++j) {
-                    const uint4 bw = h == 0 ? make_uint4(field_pair<0>(x[j], y[j], magic_v), field_pair<1>(x[j], y[j], magic_v),
-                                                         field_pair<2>(x[j], y[j], magic_v), field_pair<3>(x[j], y[j], magic_v))
-                                            : make_uint4(field_pair<4>(x[j], y[j], magic_v), field_pair<5>(x[j], y[j], magic_v),
-                                                         field_pair<6>(x[j], y[j], magic_v), field_pair<7>(x[j], y[j], magic_v));
-                    const f16x8 bf = __builtin_bit_cast(f16x8, bw);
+                    const uint4 bw = h == 0 ? tern_quad<0>(x[j], magic_v) : tern_quad<4>(x[j], magic_v);
+                    const vec bf = __builtin_bit_cast(vec, bw);
 #pragma unroll
-                    for (int i = 0; i < TM; ++i)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf, acc[i][j], 0, 0, 0);
+                    for (int i = 0; i < TM; ++i) acc[i][j] = Mfma<T>::mma(af[i], bf, acc[i][j]);
                 }
             }
         }
@@ -928,16 +648,6 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(SplitArgs sa) {
         stage_barrier();
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-
-    // D[m]: the 16 groups of a row sit on 16 neighbouring lanes, summed in a fixed order
-    float* d_lds = reinterpret_cast<float*>(lds + R * kStageBytes);
-#pragma unroll
-    for (int q = 0; q < TM / 2; ++q) {
-        const float d = row16_sum(dsum[q]);
-        if ((tid & 15) == 0) d_lds[(tid >> 4) + 32 * q] = d;
-    }
-    __syncthreads();
 
     const bool final_out = sa.S == 1;
     float sc[TN], bi[TN];
@@ -946,7 +656,7 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(SplitArgs sa) {
         const int64_t n = n0 + 32 * wave + 16 * j + i16;
         const int64_t nc = n < N ? n : N - 1;
         sc[j] = f16_bits_to_f32(p.scale[nc]);
-        bi[j] = p.bias ? F16::to_f32(p.bias[nc]) : 0.0f;
+        bi[j] = p.bias ? T::to_f32(p.bias[nc]) : 0.0f;
     }
     float* wsz = final_out ? nullptr : sa.ws + (int64_t)z * M * N;
 #pragma unroll
@@ -956,13 +666,12 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(SplitArgs sa) {
             const int row = 16 * i + 4 * g + r;
             const int64_t m = m0 + row;
             if (m >= M) continue;
-            const float corr = d_lds[row];
 #pragma unroll
             for (int j = 0; j < TN; ++j) {
                 const int64_t n = n0 + 32 * wave + 16 * j + i16;
                 if (n >= N) continue;
-                const float v = acc[i][j][r] - corr;
-                if (final_out) p.C[m * N + n] = F16::from_f32_fast(v * sc[j] + bi[j]);
+                const float v = acc[i][j][r] * Mfma<T>::kUnit;
+                if (final_out) p.C[m * N + n] = T::from_f32_fast(v * sc[j] + bi[j]);
                 else wsz[m * N + n] = v;
             }
         }
@@ -1071,7 +780,7 @@ hipError_t launch_ternary_gemm(const GemmArgs& a, void* workspace, size_t worksp
 }
 
 // Split count of the medium-M kernels.
-//  K % 256 == 0 (mm2): one workgroup fills a compute unit (the ring takes
+//  K % 256 == 0 (mm3): one workgroup fills a compute unit (the ring takes
 //  96 or 144 KB of LDS), so the split count is the largest that keeps the
 //  T tiles x S splits within one round on the compute units (at most 16,
 //  each split keeping two K-steps); measured on the Llama-3-70B shapes at
@@ -1084,9 +793,9 @@ int medium_m_splits(int64_t M, int64_t N, int64_t K, int compute_units) {
     const int64_t tm = M <= 32 ? 2 : 4;
     const int64_t tiles = ((N + mm::BN - 1) / mm::BN) * ((M + 16 * tm - 1) / (16 * tm));
     const int64_t cus = compute_units > 0 ? compute_units : 1;
-    if (K % mm2::BK == 0) {
+    if (K % mm3::BK == 0) {
         int64_t S = cus / tiles;
-        const int64_t nk = K / mm2::BK;
+        const int64_t nk = K / mm3::BK;
         if (S > 16) S = 16;
         if (S > nk / 2) S = nk / 2;
         return S < 1 ? 1 : (int)S;
@@ -1118,30 +827,15 @@ static hipError_t launch_mm(const SplitArgs& sa, hipStream_t s) {
 }
 
 template <class T, int TM>
-static hipError_t launch_mm2(const SplitArgs& sa, hipStream_t s) {
-    static DeviceFlags lds_limit_set;
-    hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(&mm2::tile_kernel<T, TM>), (int)mm2::lds_bytes<TM>(),
-                                   lds_limit_set);
-    if (e != hipSuccess) return e;
-    const GemmArgs& a = sa.g;
-    if (sa.S < 1 || sa.S > a.K / mm2::BK) return hipErrorInvalidValue;
-    const dim3 grid((unsigned)((a.N + mm2::BN - 1) / mm2::BN), (unsigned)((a.M + 16 * TM - 1) / (16 * TM)), (unsigned)sa.S);
-    mm2::tile_kernel<T, TM><<<grid, mm2::kThreads, mm2::lds_bytes<TM>(), s>>>(sa);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    if (sa.S > 1) e = launch_splitk_reduce(sa, s);
-    return e;
-}
-
-template <int TM>
 static hipError_t launch_mm3(const SplitArgs& sa, hipStream_t s) {
     static DeviceFlags lds_limit_set;
-    hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(&mm3::tile_kernel<TM>), (int)mm3::lds_bytes<TM>(),
+    hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(&mm3::tile_kernel<T, TM>), (int)mm3::lds_bytes<TM>(),
                                    lds_limit_set);
     if (e != hipSuccess) return e;
     const GemmArgs& a = sa.g;
     if (sa.S < 1 || sa.S > a.K / mm3::BK) return hipErrorInvalidValue;
     const dim3 grid((unsigned)((a.N + mm3::BN - 1) / mm3::BN), (unsigned)((a.M + 16 * TM - 1) / (16 * TM)), (unsigned)sa.S);
-    mm3::tile_kernel<TM><<<grid, mm3::kThreads, mm3::lds_bytes<TM>(), s>>>(sa);
+    mm3::tile_kernel<T, TM><<<grid, mm3::kThreads, mm3::lds_bytes<TM>(), s>>>(sa);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (sa.S > 1) e = launch_splitk_reduce(sa, s);
     return e;
@@ -1159,9 +853,9 @@ hipError_t launch_ternary_medium(const GemmArgs& a, void* workspace, size_t work
 hipError_t launch_ternary_medium_split(const SplitArgs& sa, hipStream_t s) {
     const GemmArgs& a = sa.g;
     const bool small = a.M <= 32;
-    if (a.K % mm2::BK == 0) {
-        if (a.bf16) return small ? launch_mm2<BF16, 2>(sa, s) : launch_mm2<BF16, 4>(sa, s);
-        return small ? launch_mm3<2>(sa, s) : launch_mm3<4>(sa, s);
+    if (a.K % mm3::BK == 0) {
+        if (a.bf16) return small ? launch_mm3<BF16, 2>(sa, s) : launch_mm3<BF16, 4>(sa, s);
+        return small ? launch_mm3<F16, 2>(sa, s) : launch_mm3<F16, 4>(sa, s);
     }
     if (a.bf16) return small ? launch_mm<BF16, 2>(sa, s) : launch_mm<BF16, 4>(sa, s);
     return small ? launch_mm<F16, 2>(sa, s) : launch_mm<F16, 4>(sa, s);

@@ -133,20 +133,19 @@ __global__ __launch_bounds__(kGemvWaves * kWave) void w4_gemv_kernel(GemmArgs p)
 //
 // fp16 activations, M <= 16, K % 256 == 0.  The multiply-accumulates run on
 // v_mfma_f32_16x16x32_f16 with M padded to 16 rows, so every M up to 16
-// costs the same; the VALU only unpacks codes, at about one op per code.
+// costs the same; the VALU only unpacks codes, at two ops per pair of codes.
 //
 // Unpack: a code dword x holds fields f_0..f_15 (f_j at bits 2j, column j of
 // its 16).  Masking one field of each 16-bit half into the mantissa of the
 // fp16 constant 1024 (0x6400, unit in the last place 1) gives, in one
 // v_and_or_b32, the pair P_i = (1024 + 4^s f_i, 1024 + 4^s f_{i+8}) with
 // s = i for fields in bits 0..9 (i = 0..4); fields in bits 10..15 are shifted
-// down by 10 first (s = i - 5).  The activations are pre-scaled once per
-// 256 columns to a'_k = a_k / 4^s(k) and paired the same way, so
-//   sum_k a'_k (1024 + 4^s c_k) = sum_k a_k c_k + sum_k a'_k 1024,
-// and since t = c - 1, sum_k a_k t_k = that minus sum_k a'_k (1024 + 4^s).
-// The subtracted term does not depend on the weight row: one extra MFMA of
-// the same a' against the constant pattern -(1024 + 4^s) per eight MFMAs
-// accumulates it for all rows at once.
+// down by 10 first (s = i - 5).  One packed fp16 fma, P_i * 4^-s - (1024 /
+// 4^s + 1), then gives the ternary values (t_i, t_{i+8}) = f - 1 exactly
+// (tern_pair).  The activations are paired the same way, (a_i, a_{i+8}), and
+// not scaled, so every product a_k t_k is exact and the fp32 sums hold only
+// the terms of the result: the error of a row scales with its own
+// sum_k |a_k t_k| however few codes are nonzero.
 //
 // Work split: a block owns 16R weight rows (R blocks of 16, one per MFMA
 // column tile) and all of K; its W waves take every W-th 256-column
@@ -184,7 +183,6 @@ __global__ __launch_bounds__(W * kWave) void ternary_gemv_mfma_kernel(GemmArgs p
     f32x4 acc[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
-    f32x4 dacc = f32x4{0.f, 0.f, 0.f, 0.f};
     const uint32_t magic_v = vgpr_const<kMagic2>();
 
     uint4 q[R], qn[R];
@@ -216,17 +214,11 @@ __global__ __launch_bounds__(W * kWave) void ternary_gemv_mfma_kernel(GemmArgs p
         }
 #define TQ_MFMA_J(D, I0)                                                                              \
     {                                                                                                 \
-        const uint4 aw = make_uint4(a_pair<D, I0>(av), a_pair<D, I0 + 1>(av), a_pair<D, I0 + 2>(av),  \
-                                    a_pair<D, I0 + 3>(av));                                           \
+        const uint4 aw = make_uint4(act_pair<D, I0>(av), act_pair<D, I0 + 1>(av), act_pair<D, I0 + 2>(av), \
+                                    act_pair<D, I0 + 3>(av));                                         \
         const f16x8 aop = __builtin_bit_cast(f16x8, aw);                                              \
-        const uint4 nw = make_uint4(neg_one_pattern<I0>(), neg_one_pattern<I0 + 1>(),                 \
-                                    neg_one_pattern<I0 + 2>(), neg_one_pattern<I0 + 3>());            \
-        dacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, __builtin_bit_cast(f16x8, nw), dacc, 0, 0, 0); \
         _Pragma("unroll") for (int r = 0; r < R; ++r) {                                               \
-            const uint32_t x = dword_of(q[r], D);                                                     \
-            const uint32_t y = x >> 10;                                                               \
-            const uint4 bw = make_uint4(field_pair<I0>(x, y, magic_v), field_pair<I0 + 1>(x, y, magic_v), \
-                                        field_pair<I0 + 2>(x, y, magic_v), field_pair<I0 + 3>(x, y, magic_v)); \
+            const uint4 bw = tern_quad<I0>(dword_of(q[r], D), magic_v);                               \
             acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, __builtin_bit_cast(f16x8, bw), acc[r], 0, 0, 0); \
         }                                                                                             \
     }
@@ -245,7 +237,7 @@ __global__ __launch_bounds__(W * kWave) void ternary_gemv_mfma_kernel(GemmArgs p
         }
     }
 #pragma unroll
-    for (int r = 0; r < R; ++r) red[wave][r][lane] = acc[r] + dacc;
+    for (int r = 0; r < R; ++r) red[wave][r][lane] = acc[r];
     __syncthreads();
     for (int e = threadIdx.x; e < R * kWave; e += W * kWave) {
         const int r = e / kWave;
@@ -269,7 +261,7 @@ __global__ __launch_bounds__(W * kWave) void ternary_gemv_mfma_kernel(GemmArgs p
 //
 // Block = W waves over 16R weight rows and all of K; wave w owns chunk-sets
 // w*CSW .. w*CSW + CSW-1 (256 columns each) of every row.  Waves are
-// independent until the final reduction: each preps the activations of its
+// independent until the final reduction: each pairs the activations of its
 // own columns in a private LDS area, so no barrier sits between the code
 // loads and the contraction.
 // 1. Each lane loads the activations of its prep units first (16 columns of
@@ -277,29 +269,25 @@ __global__ __launch_bounds__(W * kWave) void ternary_gemv_mfma_kernel(GemmArgs p
 //    issues all its code loads in the order step 3 consumes them.  Every
 //    load is unconditional (addresses clamped, surplus results discarded):
 //    the compiler keeps this issue order, and the in-order completion
-//    counter lets each use wait only for the loads it needs - the prep waits
-//    for the activations only.  The epilogue's row scale and bias are loaded
-//    here too.
-// 2. While the codes are in flight the wave writes its scaled, paired a'
-//    values to its LDS area in MFMA operand order - dword
-//    ((m * 4 CSW + chunk) * 32 + 8 d + i) = pair (d, i) of row m - and sums
-//    its share of D[m] = sum_k a'_k (1024 + 4^s(k)): dot2 partials per 16
-//    columns, reduced over each 16-lane row (256 columns of one activation
-//    row) and over the wave's chunk-sets in a fixed order.
+//    counter lets each use wait only for the loads it needs - the pairing
+//    waits for the activations only.  The epilogue's row scale and bias are
+//    loaded here too.
+// 2. While the codes are in flight the wave writes its paired activations
+//    to its LDS area in MFMA operand order - dword
+//    ((m * 4 CSW + chunk) * 32 + 8 d + i) = pair (d, i) of row m.
 // 3. The wave contracts its chunk-sets as their codes land.  Lanes of
 //    activation rows m >= M skip the LDS read (their output rows are never
-//    stored).  Its D share is subtracted from its partials.
+//    stored).
 // 4. Wave partials meet in LDS; after one barrier a fixed-order sum, then the
 //    row scale and bias.
 
-// LDS layout of the kernel below (byte offsets): per wave, a' [M][4 CSW
-// chunks][128 bytes] then D partials [M][CSW floats, padded to 16 bytes];
-// after the W wave areas, the wave partials [W][R][64 lanes][16 bytes].
+// LDS layout of the kernel below (byte offsets): per wave, paired
+// activations [M][4 CSW chunks][128 bytes]; after the W wave areas, the wave
+// partials [W][R][64 lanes][16 bytes].
 struct GemvLds {
-    int64_t wave_bytes, dpart, red, total;
+    int64_t wave_bytes, red, total;
     __host__ __device__ GemvLds(int64_t M, int csw, int W, int R) {
-        dpart = M * csw * 512;
-        wave_bytes = dpart + ((M * csw * 4 + 15) / 16) * 16;
+        wave_bytes = M * csw * 512;
         red = W * wave_bytes;
         total = red + (int64_t)W * R * 64 * 16;
     }
@@ -324,8 +312,7 @@ __global__ __launch_bounds__(1024) void ternary_gemv_lds_kernel(GemmArgs p) {
     const int cs0 = wave * CSW;
     const int cnt = CS - cs0 < CSW ? CS - cs0 : CSW;  // >= 1 for every wave of the launch
     const GemvLds L(M, CSW, W, R);
-    uint32_t* aps = reinterpret_cast<uint32_t*>(lds + wave * L.wave_bytes);   // this wave's a'
-    float* dpart = reinterpret_cast<float*>(lds + wave * L.wave_bytes + L.dpart);
+    uint32_t* aps = reinterpret_cast<uint32_t*>(lds + wave * L.wave_bytes);   // this wave's pairs
     f32x4* red = reinterpret_cast<f32x4*>(lds + L.red);                      // [W][R][64]
 
     // 1a. activation loads: unit u = lane + 64 j covers columns
@@ -369,7 +356,7 @@ __global__ __launch_bounds__(1024) void ternary_gemv_lds_kernel(GemmArgs p) {
         sc_e = f16_bits_to_f32(p.scale[nc]);
         bi_e = p.bias ? F16::to_f32(p.bias[nc]) : 0.0f;
     }
-    // 2. a' and D partials of this wave's columns to its LDS area
+    // 2. paired activations of this wave's columns to its LDS area
 #pragma unroll
     for (int j = 0; j < UPT; ++j) {
         const int u = lane + j * kWave;
@@ -377,38 +364,15 @@ __global__ __launch_bounds__(1024) void ternary_gemv_lds_kernel(GemmArgs p) {
         const int uc = live ? u : units - 1;
         const int m = (uc >= per) + (uc >= 2 * per) + (uc >= 3 * per);
         const int c = uc - m * per;
-        const uint4 w0 = make_uint4(a_pair<0, 0>(av[j]), a_pair<0, 1>(av[j]), a_pair<0, 2>(av[j]), a_pair<0, 3>(av[j]));
-        const uint4 w1 = make_uint4(a_pair<0, 4>(av[j]), a_pair<0, 5>(av[j]), a_pair<0, 6>(av[j]), a_pair<0, 7>(av[j]));
-        float dp = 0.0f;
-        dp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w0.x), __builtin_bit_cast(f16x2, one_pattern<0>()), dp, false);
-        dp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w0.y), __builtin_bit_cast(f16x2, one_pattern<1>()), dp, false);
-        dp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w0.z), __builtin_bit_cast(f16x2, one_pattern<2>()), dp, false);
-        dp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w0.w), __builtin_bit_cast(f16x2, one_pattern<3>()), dp, false);
-        dp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w1.x), __builtin_bit_cast(f16x2, one_pattern<4>()), dp, false);
-        dp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w1.y), __builtin_bit_cast(f16x2, one_pattern<5>()), dp, false);
-        dp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w1.z), __builtin_bit_cast(f16x2, one_pattern<6>()), dp, false);
-        dp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w1.w), __builtin_bit_cast(f16x2, one_pattern<7>()), dp, false);
-        dp = row16_sum(dp);  // 16 units of one row: 256 columns (one chunk-set) of activation row m
+        uint4 w0, w1;
+        act_pairs16<0>(av[j], w0, w1);
         if (live) {
             uint4* dst = reinterpret_cast<uint4*>(aps + ((int64_t)(m * 4 * CSW + (c >> 2)) * 32 + 8 * (c & 3)));
             dst[0] = w0;
             dst[1] = w1;
-            if ((c & 15) == 0) dpart[m * CSW + (c >> 4)] = dp;
         }
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's LDS writes are complete
-
-    // this lane's share of D for its output rows m = 4 (lane / 16) + i
-    float dsub[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int m = 4 * g + i;
-        float t = 0.0f;
-        if (m < M) {
-            for (int q2 = 0; q2 < cnt; ++q2) t += dpart[m * CSW + q2];
-        }
-        dsub[i] = t;
-    }
 
     // 3. contract
     f32x4 acc[R];
@@ -434,10 +398,7 @@ __global__ __launch_bounds__(1024) void ternary_gemv_lds_kernel(GemmArgs p) {
     {                                                                                                 \
         const f16x8 aop = __builtin_bit_cast(f16x8, aw[2 * (D) + (I0) / 4]);                          \
         _Pragma("unroll") for (int r = 0; r < R; ++r) {                                               \
-            const uint32_t x = dword_of(q[s][r], D);                                                  \
-            const uint32_t y = x >> 10;                                                               \
-            const uint4 bw = make_uint4(field_pair<I0>(x, y, magic_v), field_pair<I0 + 1>(x, y, magic_v), \
-                                        field_pair<I0 + 2>(x, y, magic_v), field_pair<I0 + 3>(x, y, magic_v)); \
+            const uint4 bw = tern_quad<I0>(dword_of(q[s][r], D), magic_v);                            \
             acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, __builtin_bit_cast(f16x8, bw), acc[r], 0, 0, 0); \
         }                                                                                             \
     }
@@ -453,14 +414,9 @@ __global__ __launch_bounds__(1024) void ternary_gemv_lds_kernel(GemmArgs p) {
         }
     }
 
-    // 4. wave partials (D share removed) -> LDS, fixed-order sum
+    // 4. wave partials -> LDS, fixed-order sum
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-        f32x4 v = acc[r];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] -= dsub[i];
-        red[(wave * R + r) * kWave + lane] = v;
-    }
+    for (int r = 0; r < R; ++r) red[(wave * R + r) * kWave + lane] = acc[r];
     __syncthreads();
     if ((int)threadIdx.x < R * kWave) {  // R <= W
         const int e = (int)threadIdx.x;
@@ -479,76 +435,10 @@ __global__ __launch_bounds__(1024) void ternary_gemv_lds_kernel(GemmArgs p) {
     }
 }
 
-// bf16 form of the a' unpack for the small-M kernel below.  bf16 has 7
-// fraction bits, so three 2-bit fields fit the mantissa of 128.0 (0x4300,
-// unit in the last place 1): fields 0..2 of a code dword x are masked in
-// place, fields 3..5 from x >> 6 and fields 6, 7 from x >> 12, each at bits
-// 2s of its source with s = I, I - 3 or I - 6 and so scaled by 4^s (the
-// partner field I + 8 sits 16 bits higher); the activations are paired and
-// pre-scaled by 1 / 4^s to match.  There is no packed bf16 multiply, so the
-// pre-scale goes through fp32 (exact: a power of two) and back.
-constexpr uint32_t kMagicBf2 = 0x43004300u;  // (128.0, 128.0) as bf16
-
-template <int I> constexpr int bf_shift() { return I < 3 ? I : I < 6 ? I - 3 : I - 6; }
-
-template <int I>
-__device__ __forceinline__ uint32_t bf_field_pair(uint32_t x, uint32_t y, uint32_t z, uint32_t magic_v) {
-    constexpr uint32_t mask = 0x00030003u << (2 * bf_shift<I>());
-    if constexpr (I < 3) return (x & sgpr_const<mask>()) | magic_v;
-    else if constexpr (I < 6) return (y & sgpr_const<mask>()) | magic_v;
-    else return (z & sgpr_const<mask>()) | magic_v;
-}
-
-// a' pair for field I: (a[I], a[I+8]) / 4^s(I), bf16 bits, from the 16
-// columns of one unit (av[0]: columns 0..7, av[1]: 8..15).
-template <int I>
-__device__ __forceinline__ uint32_t bf_a_pair(const uint4 av[8]) {
-    constexpr int c = I / 2;
-    const uint32_t lo = c == 0 ? av[0].x : c == 1 ? av[0].y : c == 2 ? av[0].z : av[0].w;
-    const uint32_t hi = c == 0 ? av[1].x : c == 1 ? av[1].y : c == 2 ? av[1].z : av[1].w;
-    const uint32_t pr = __builtin_amdgcn_perm(hi, lo, (I & 1) ? 0x07060302u : 0x05040100u);
-    constexpr int s = bf_shift<I>();
-    if constexpr (s == 0) {
-        return pr;
-    } else {
-        constexpr float f = 1.0f / (float)(1 << (2 * s));
-        const float a0 = __uint_as_float(pr << 16) * f;
-        const float a1 = __uint_as_float(pr & 0xFFFF0000u) * f;
-        return __builtin_bit_cast(uint32_t, bf16x2{(__bf16)a0, (__bf16)a1});
-    }
-}
-
-// (128 + 4^s) in both bf16 halves: the code-01 value of field I
-template <int I>
-__device__ __forceinline__ constexpr uint32_t bf_one_pattern() {
-    constexpr uint32_t v = 0x4300u + (1u << (2 * bf_shift<I>()));
-    return v | (v << 16);
-}
-
-// Field pair, a' pair, code-01 dot product and matrix-core step of the
-// small-M kernel for activation type T.
-template <class T, int I>
-__device__ __forceinline__ uint32_t sm_field_pair(uint32_t x, uint32_t y, uint32_t z, uint32_t magic_v) {
-    if constexpr (std::is_same<T, F16>::value) return field_pair<I>(x, y, magic_v);
-    else return bf_field_pair<I>(x, y, z, magic_v);
-}
-template <class T, int I>
-__device__ __forceinline__ uint32_t sm_a_pair(const uint4 av[8]) {
-    if constexpr (std::is_same<T, F16>::value) return a_pair<0, I>(av);
-    else return bf_a_pair<I>(av);
-}
-template <class T, int D, int I>
-__device__ __forceinline__ uint32_t sm_a_pair_d(const uint4 av[8]) {  // unit D of av
-    if constexpr (std::is_same<T, F16>::value) return a_pair<D, I>(av);
-    else return bf_a_pair<I>(av + 2 * D);
-}
-template <class T, int I>
-__device__ __forceinline__ float sm_dot_one(uint32_t pair, float acc) {
-    if constexpr (std::is_same<T, F16>::value)
-        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pair), __builtin_bit_cast(f16x2, one_pattern<I>()), acc, false);
-    else
-        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), __builtin_bit_cast(bf16x2, bf_one_pattern<I>()), acc, false);
-}
+// Matrix-core step and output unit for activation type T.  Both types
+// take the same exact ternary operand (tern_pair): fp16 reads it as -1, 0,
+// +1; bf16 reads the same bits as -2^-7, 0, +2^-7, so a bf16 kernel's fp32
+// sums are 2^-7 times the result and kUnit (128) restores it exactly.
 template <class T>
 __device__ __forceinline__ f32x4 sm_mma(uint4 a, uint4 b, f32x4 c) {
     if constexpr (std::is_same<T, F16>::value)
@@ -556,16 +446,16 @@ __device__ __forceinline__ f32x4 sm_mma(uint4 a, uint4 b, f32x4 c) {
     else
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
+template <class T>
+constexpr float ternary_unit() { return std::is_same<T, F16>::value ? 1.0f : kBf16TernaryUnit; }
 
 // Small-M form of the kernel above (fp16 or bf16, M <= 4, K a multiple of 256 CSW,
 // N a multiple of 16 R, W = K / (256 CSW) waves), with MT in {1, 2, 4}
 // activation rows held at compile time (rows M .. MT-1 re-read row M-1 and
 // are never stored):
-// * unit c (16 columns) of row m's part of a wave's a' area is 32
+// * unit c (16 columns) of row m's part of a wave's pair area is 32
 //   contiguous bytes at 32 c, and only lanes 16g + m (m < M: row m of the
 //   matrix-core operand) read it back;
-// * the constant term D of a wave is one number per activation row,
-//   subtracted from its partials before the cross-wave sum;
 // * every global address is a wave-uniform base plus a 32-bit lane offset
 //   and a compile-time displacement, and no count depends on M at run time.
 // The bias is read from a valid address whether or not one is given, so the
@@ -575,7 +465,7 @@ template <class T, int R, int CSW, int MT>
 __global__ __launch_bounds__(1024) void ternary_gemv_m1_kernel(GemmArgs p) {
     extern __shared__ uint4 smem[];
     constexpr int U = CSW / 4;            // 16-column activation units per lane and row
-    constexpr int kRowLds = CSW * 512;    // a' bytes of one activation row
+    constexpr int kRowLds = CSW * 512;    // pair bytes of one activation row
     uint8_t* lds = reinterpret_cast<uint8_t*>(smem);
     const int W = blockDim.x >> 6;
     const int lane = threadIdx.x & (kWave - 1);
@@ -586,7 +476,7 @@ __global__ __launch_bounds__(1024) void ternary_gemv_m1_kernel(GemmArgs p) {
     const uint32_t rb = (uint32_t)(p.K / 4);
     const int64_t n_base = (int64_t)blockIdx.x * (16 * R);
     const int cs0 = wave * CSW;
-    uint8_t* aps = lds + wave * (MT * kRowLds);                           // this wave's a'
+    uint8_t* aps = lds + wave * (MT * kRowLds);                           // this wave's pairs
     float* red = reinterpret_cast<float*>(lds + W * (MT * kRowLds));      // [W][R][MT][16]
 
     // 1. loads in the order they are consumed: activations, row scale and
@@ -620,32 +510,17 @@ __global__ __launch_bounds__(1024) void ternary_gemv_m1_kernel(GemmArgs p) {
             q[s][r] = *reinterpret_cast<const uint4*>(cbase + (int64_t)r * 16 * rb + 64 * s + (uint64_t)lo);
     }
 
-    // 2. a' of this wave's columns to LDS, and the wave's D per row
-    float dw[MT];
+    // 2. paired activations of this wave's columns to LDS
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
-        float dp = 0.0f;
 #pragma unroll
         for (int j = 0; j < U; ++j) {
-            const uint4 w0 = make_uint4(sm_a_pair<T, 0>(av[m][j]), sm_a_pair<T, 1>(av[m][j]), sm_a_pair<T, 2>(av[m][j]), sm_a_pair<T, 3>(av[m][j]));
-            const uint4 w1 = make_uint4(sm_a_pair<T, 4>(av[m][j]), sm_a_pair<T, 5>(av[m][j]), sm_a_pair<T, 6>(av[m][j]), sm_a_pair<T, 7>(av[m][j]));
-            dp = sm_dot_one<T, 0>(w0.x, dp);
-            dp = sm_dot_one<T, 1>(w0.y, dp);
-            dp = sm_dot_one<T, 2>(w0.z, dp);
-            dp = sm_dot_one<T, 3>(w0.w, dp);
-            dp = sm_dot_one<T, 4>(w1.x, dp);
-            dp = sm_dot_one<T, 5>(w1.y, dp);
-            dp = sm_dot_one<T, 6>(w1.z, dp);
-            dp = sm_dot_one<T, 7>(w1.w, dp);
+            uint4 w0, w1;
+            act_pairs16<0>(av[m][j], w0, w1);
             uint4* dst = reinterpret_cast<uint4*>(aps + m * kRowLds + 32 * (lane + 64 * j));
             dst[0] = w0;
             dst[1] = w1;
         }
-        dp = row16_sum(dp);
-        dw[m] = (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(dp), 0)) +
-                 __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dp), 16))) +
-                (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(dp), 32)) +
-                 __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dp), 48)));
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's LDS writes are complete
 
@@ -654,8 +529,7 @@ __global__ __launch_bounds__(1024) void ternary_gemv_m1_kernel(GemmArgs p) {
     f32x4 acc[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
-    constexpr bool kBf = std::is_same<T, BF16>::value;
-    const uint32_t magic_v = vgpr_const<kBf ? kMagicBf2 : kMagic2>();
+    const uint32_t magic_v = vgpr_const<kMagic2>();
     const bool a_live = MT == 1 ? i16 == 0 : i16 < M;
 #pragma unroll
     for (int s = 0; s < CSW; ++s) {
@@ -671,11 +545,7 @@ __global__ __launch_bounds__(1024) void ternary_gemv_m1_kernel(GemmArgs p) {
     {                                                                                                 \
         const uint4 aop = aw[2 * (D) + (I0) / 4];                                                     \
         _Pragma("unroll") for (int r = 0; r < R; ++r) {                                               \
-            const uint32_t x = dword_of(q[s][r], D);                                                  \
-            const uint32_t y = x >> (kBf ? 6 : 10);                                                   \
-            const uint32_t z = x >> 12;                                                               \
-            const uint4 bw = make_uint4(sm_field_pair<T, I0>(x, y, z, magic_v), sm_field_pair<T, I0 + 1>(x, y, z, magic_v), \
-                                        sm_field_pair<T, I0 + 2>(x, y, z, magic_v), sm_field_pair<T, I0 + 3>(x, y, z, magic_v)); \
+            const uint4 bw = tern_quad<I0>(dword_of(q[s][r], D), magic_v);                            \
             acc[r] = sm_mma<T>(aop, bw, acc[r]);                                                      \
         }                                                                                             \
     }
@@ -690,13 +560,13 @@ __global__ __launch_bounds__(1024) void ternary_gemv_m1_kernel(GemmArgs p) {
 #undef TQ_MFMA_1
     }
 
-    // 4. rows 0 .. MT-1 of each wave's partials (D removed) -> LDS;
-    //    fixed-order sum (component i of lane i16 < 16: activation row i)
+    // 4. rows 0 .. MT-1 of each wave's partials -> LDS; fixed-order sum
+    //    (component i of lane i16 < 16: activation row i)
     if (g == 0) {
 #pragma unroll
         for (int r = 0; r < R; ++r)
 #pragma unroll
-            for (int i = 0; i < MT; ++i) red[((wave * R + r) * MT + i) * 16 + i16] = acc[r][i] - dw[i];
+            for (int i = 0; i < MT; ++i) red[((wave * R + r) * MT + i) * 16 + i16] = acc[r][i];
     }
     __syncthreads();
     if ((int)threadIdx.x < 16 * R * MT) {
@@ -705,7 +575,8 @@ __global__ __launch_bounds__(1024) void ternary_gemv_m1_kernel(GemmArgs p) {
         float sum = red[t];
         for (int w = 1; w < W; ++w) sum += red[w * (16 * R * MT) + t];
         const float bi = p.bias ? T::to_f32(bi_bits) : 0.0f;
-        if (i < M) p.C[(int64_t)i * p.N + n_e] = T::from_f32_fast(sum * f16_bits_to_f32(sc_bits) + bi);
+        const float sc = f16_bits_to_f32(sc_bits) * ternary_unit<T>();
+        if (i < M) p.C[(int64_t)i * p.N + n_e] = T::from_f32_fast(sum * sc + bi);
     }
 }
 
@@ -716,11 +587,11 @@ __global__ __launch_bounds__(1024) void ternary_gemv_m1_kernel(GemmArgs p) {
 // owns chunk-sets w*CSW .. w*CSW + CSW-1 (256 columns each) of all of them,
 // so the activation operand of its MFMAs never changes: it is built once, in
 // registers, from the activations of its columns (lane 16g + i: row i,
-// chunk 4cs + g), together with the wave's share of D[m].  The wave issues
-// its activation loads, then the code loads of all T row-blocks, then builds
-// the operand while the codes are in flight, and contracts each row-block as
-// its codes land (in-order completion), one accumulator per row-block.  Wave
-// partials meet in LDS once, at the end, and are summed in a fixed order.
+// chunk 4cs + g).  The wave issues its activation loads, then the code loads
+// of all T row-blocks, then builds the operand while the codes are in
+// flight, and contracts each row-block as its codes land (in-order
+// completion), one accumulator per row-block.  Wave partials meet in LDS
+// once, at the end, and are summed in a fixed order.
 //
 // The operand layout puts 16 activation rows on neighbouring lanes, so
 // loading it directly would touch a different 128-byte line with every lane.
@@ -742,7 +613,6 @@ __host__ __device__ constexpr int stream_wave_lds(int csw, int mr, int t) {  // 
 
 template <class AT, int CSW, int T, int MR>
 __global__ __launch_bounds__(1024) void ternary_gemv_stream_kernel(SplitArgs sa) {
-    constexpr bool kBf = std::is_same<AT, BF16>::value;
     const GemmArgs& p = sa.g;
     extern __shared__ uint4 smem[];
     constexpr int kArea = stream_wave_lds(CSW, MR, T);
@@ -808,57 +678,26 @@ __global__ __launch_bounds__(1024) void ternary_gemv_stream_kernel(SplitArgs sa)
 
     // 3. wait for the activation DMA only (the T * CSW code loads issued after
     //    it may still be in flight: completion is in order), read the operand
-    //    rows, then operands a' (pair (d, i) of a chunk in dword 8 d + i) and
-    //    the D share
+    //    rows and pair them (pair (d, i) of a chunk in dword 8 d + i)
     static_assert(T * CSW <= 63, "vmcnt range");
     asm volatile("s_waitcnt vmcnt(%0)" :: "n"(T * CSW) : "memory");
     const int rd_row = i16 & (MR - 1);
-    uint4 av[CSW][8];
-#pragma unroll
-    for (int s = 0; s < CSW; ++s)
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-            av[s][e] = *reinterpret_cast<const uint4*>(area + s * MR * 512 + rd_row * 512 +
-                                                       16 * ((8 * g + e) ^ (rd_row & 15)));
     uint4 aw[CSW][8];
-    float dl = 0.0f;
 #pragma unroll
     for (int s = 0; s < CSW; ++s) {
-#define TQ_APREP(D)                                                                                  \
-        aw[s][2 * (D)] = make_uint4(sm_a_pair_d<AT, D, 0>(av[s]), sm_a_pair_d<AT, D, 1>(av[s]),       \
-                                    sm_a_pair_d<AT, D, 2>(av[s]), sm_a_pair_d<AT, D, 3>(av[s]));      \
-        aw[s][2 * (D) + 1] = make_uint4(sm_a_pair_d<AT, D, 4>(av[s]), sm_a_pair_d<AT, D, 5>(av[s]),   \
-                                        sm_a_pair_d<AT, D, 6>(av[s]), sm_a_pair_d<AT, D, 7>(av[s]));
-        TQ_APREP(0)
-        TQ_APREP(1)
-        TQ_APREP(2)
-        TQ_APREP(3)
-#undef TQ_APREP
-        if (s < cnt) {
+        uint4 av[8];
 #pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                const uint4 lo = aw[s][2 * d], hi = aw[s][2 * d + 1];
-                dl = sm_dot_one<AT, 0>(lo.x, dl);
-                dl = sm_dot_one<AT, 1>(lo.y, dl);
-                dl = sm_dot_one<AT, 2>(lo.z, dl);
-                dl = sm_dot_one<AT, 3>(lo.w, dl);
-                dl = sm_dot_one<AT, 4>(hi.x, dl);
-                dl = sm_dot_one<AT, 5>(hi.y, dl);
-                dl = sm_dot_one<AT, 6>(hi.z, dl);
-                dl = sm_dot_one<AT, 7>(hi.w, dl);
-            }
-        }
+        for (int e = 0; e < 8; ++e)
+            av[e] = *reinterpret_cast<const uint4*>(area + s * MR * 512 + rd_row * 512 +
+                                                    16 * ((8 * g + e) ^ (rd_row & 15)));
+        act_pairs16<0>(av, aw[s][0], aw[s][1]);
+        act_pairs16<1>(av, aw[s][2], aw[s][3]);
+        act_pairs16<2>(av, aw[s][4], aw[s][5]);
+        act_pairs16<3>(av, aw[s][6], aw[s][7]);
     }
-    // D share of operand row i16, summed over the four lane groups; output
-    // element i of this lane belongs to row 4g + i
-    dl += __shfl_xor(dl, 16, kWave);
-    dl += __shfl_xor(dl, 32, kWave);
-    float dsub[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) dsub[i] = __shfl(dl, 4 * g + i, kWave);
 
     // 4. contract each row-block as its codes land
-    const uint32_t magic_v = vgpr_const<kBf ? kMagicBf2 : kMagic2>();
+    const uint32_t magic_v = vgpr_const<kMagic2>();
     f32x4 acc[T];
 #pragma unroll
     for (int t = 0; t < T; ++t) {
@@ -868,11 +707,7 @@ __global__ __launch_bounds__(1024) void ternary_gemv_stream_kernel(SplitArgs sa)
             if (s < cnt) {
 #define TQ_MFMA_S(D, I0)                                                                              \
     {                                                                                                 \
-        const uint32_t x = dword_of(q[t][s], D);                                                      \
-        const uint32_t y = x >> (kBf ? 6 : 10);                                                       \
-        const uint32_t z = x >> 12;                                                                   \
-        const uint4 bw = make_uint4(sm_field_pair<AT, I0>(x, y, z, magic_v), sm_field_pair<AT, I0 + 1>(x, y, z, magic_v), \
-                                    sm_field_pair<AT, I0 + 2>(x, y, z, magic_v), sm_field_pair<AT, I0 + 3>(x, y, z, magic_v)); \
+        const uint4 bw = tern_quad<I0>(dword_of(q[t][s], D), magic_v);                                \
         a4 = sm_mma<AT>(aw[s][2 * (D) + (I0) / 4], bw, a4);                                           \
     }
                 TQ_MFMA_S(0, 0)
@@ -889,14 +724,10 @@ __global__ __launch_bounds__(1024) void ternary_gemv_stream_kernel(SplitArgs sa)
         acc[t] = a4;
     }
 
-    // 5. wave partials (D share removed) -> LDS, fixed-order sum
+    // 5. wave partials -> LDS, fixed-order sum; split partials carry the
+    //    bf16 unit, so the reduction treats both types alike
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
-        f32x4 v = acc[t];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] -= dsub[i];
-        red[wave * (kArea / 16) + t * kWave + lane] = v;
-    }
+    for (int t = 0; t < T; ++t) red[wave * (kArea / 16) + t * kWave + lane] = acc[t];
     __syncthreads();
     if ((int)threadIdx.x < T * kWave) {  // T <= W
         const int e = (int)threadIdx.x;
@@ -910,10 +741,10 @@ __global__ __launch_bounds__(1024) void ternary_gemv_stream_kernel(SplitArgs sa)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int m = 4 * (l >> 4) + i;
-                if (m < M) part[(int64_t)m * N + n] = sum[i];
+                if (m < M) part[(int64_t)m * N + n] = sum[i] * ternary_unit<AT>();
             }
         } else if (n < N) {
-            const float sc_e = f16_bits_to_f32(sc_bits);
+            const float sc_e = f16_bits_to_f32(sc_bits) * ternary_unit<AT>();
             const float bi_e = p.bias ? AT::to_f32(bi_bits) : 0.0f;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -934,15 +765,13 @@ __global__ __launch_bounds__(1024) void ternary_gemv_stream_kernel(SplitArgs sa)
 //   (x & 0x000F000F) | magic = (1024 + q_0, 1024 + q_4),
 //   (x & 0x00F000F0) | magic = (1024 + 16 q_1, 1024 + 16 q_5),
 // and with y = x >> 8 the pairs (q_2, q_6) and (16 q_3, 16 q_7) the same way.
-// The activations are paired to match - (a_0, a_4), (a_1, a_5) / 16, (a_2,
-// a_6), (a_3, a_7) / 16 - so one MFMA contracts one word of each of 16 rows:
-//   sum a' (1024 + 16^s q) = sum a q + sum a' 1024.
-// The weight value is q - 8 (zero point 8), so a group's sum is that minus
-// sum a' (1024 + 8 * 16^s), which is the same for every weight row: MFMAs of
-// the group's activation operand against that constant pattern, negated,
-// give every group accumulator its starting value.  The group scale
-// s[n, g] then multiplies the group's fp32 sum (page "Model quantization -
-// vLLM runtime quantization architecture", section 5: group_size 128).
+// One packed fp16 add of -(1024 + 8), or fma by 1/16 with -(64 + 8), leaves
+// the weight values q - 8 exactly (zero point 8; w4_quad), and the
+// activations are paired to match - (a_0, a_4), (a_1, a_5), (a_2, a_6),
+// (a_3, a_7) - so one MFMA contracts one word of each of 16 rows with exact
+// products and no offset in the sums.  The group scale s[n, g] then
+// multiplies the group's fp32 sum (page "Model quantization - vLLM runtime
+// quantization architecture", section 5: group_size 128).
 //
 // Work split: a block owns 16R weight rows and all of K; its W waves take
 // every W-th 128-column group.  Lane l = 16h + i loads 16 bytes (32 codes,
@@ -951,8 +780,6 @@ __global__ __launch_bounds__(1024) void ternary_gemv_stream_kernel(SplitArgs sa)
 // code word d of every lane.  The next group's loads are issued before the
 // current group is contracted.  Wave partials meet in LDS and are summed in
 // a fixed order.
-constexpr uint32_t kW4Neg0 = 0xE408E408u;  // -(1024 + 8), both halves
-constexpr uint32_t kW4Neg1 = 0xE480E480u;  // -(1024 + 128), both halves
 
 template <int R, int W>
 __global__ __launch_bounds__(W * kWave) void w4_gemv_mfma_kernel(GemmArgs p) {
@@ -997,8 +824,7 @@ __global__ __launch_bounds__(W * kWave) void w4_gemv_mfma_kernel(GemmArgs p) {
 #pragma unroll
     for (int r = 0; r < R; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
     const uint32_t magic_v = vgpr_const<kMagic2>();
-    const f16x2 sixteenth = f16x2{(_Float16)0.0625f, (_Float16)0.0625f};
-    const uint4 negp = make_uint4(kW4Neg0, kW4Neg1, kW4Neg0, kW4Neg1);
+    const f16x2 k0 = __builtin_bit_cast(f16x2, kW4Sub0Sym), k1 = __builtin_bit_cast(f16x2, kW4Sub1Sym);
 
     uint4 q[R], qn[R], av[4], avn[4];
     uint16_t sc[R], scn[R];
@@ -1007,28 +833,15 @@ __global__ __launch_bounds__(W * kWave) void w4_gemv_mfma_kernel(GemmArgs p) {
     for (; gi < G; gi += W) {
         const int gn = gi + W < G ? gi + W : gi;  // past the end: re-read, unused
         load(gn, qn, scn, avn);
-        // activation operands of the four code words, and the group's start
-        uint4 aop[4];
-        f32x4 dacc = f32x4{0.f, 0.f, 0.f, 0.f};
+        uint4 aop[4];  // activation operands of the four code words
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
-            const uint4 v = av[d];  // columns 8d .. 8d+7 of this lane's 32
-            const uint32_t p0 = __builtin_amdgcn_perm(v.z, v.x, 0x05040100u);
-            const uint32_t p1 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(v.z, v.x, 0x07060302u)) * sixteenth);
-            const uint32_t p2 = __builtin_amdgcn_perm(v.w, v.y, 0x05040100u);
-            const uint32_t p3 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(v.w, v.y, 0x07060302u)) * sixteenth);
-            aop[d] = make_uint4(p0, p1, p2, p3);
-            dacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, aop[d]), __builtin_bit_cast(f16x8, negp), dacc, 0, 0, 0);
-        }
+        for (int d = 0; d < 4; ++d) aop[d] = w4_act_quad(av[d]);  // columns 8d .. 8d+7 of this lane's 32
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            f32x4 ag = dacc;
+            f32x4 ag = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int d = 0; d < 4; ++d) {
-                const uint32_t x = dword_of(q[r], d);
-                const uint32_t y = x >> 8;
-                const uint4 bw = make_uint4((x & sgpr_const<0x000F000Fu>()) | magic_v, (x & sgpr_const<0x00F000F0u>()) | magic_v,
-                                            (y & sgpr_const<0x000F000Fu>()) | magic_v, (y & sgpr_const<0x00F000F0u>()) | magic_v);
+                const uint4 bw = w4_quad(dword_of(q[r], d), magic_v, k0, k1);
                 ag = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, aop[d]), __builtin_bit_cast(f16x8, bw), ag, 0, 0, 0);
             }
             const float s = f16_bits_to_f32(sc[r]);
@@ -1068,33 +881,25 @@ __global__ __launch_bounds__(W * kWave) void w4_gemv_mfma_kernel(GemmArgs p) {
 //   bytes (group columns 32h .. 32h + 31) of row i of each group, and MFMA d
 //   of a group contracts code word d of every lane (columns 32h + 8d ..);
 // * unit u (8 columns) of the wave's columns is word u % 4 of lane slot
-//   (u / 4) % 4 of group u / 16, so lane l preps units l + 64 j of every
-//   activation row m: four a' pairs (a_0, a_4), (a_1, a_5) / 16, (a_2, a_6),
-//   (a_3, a_7) / 16, 16 bytes at 16 u of row m's part of the wave's LDS
-//   area, and its share of the group's constant sum a' (1024 + 8 16^s); a
-//   16-lane row sum gives each (row, group) constant;
+//   (u / 4) % 4 of group u / 16, so lane l pairs units l + 64 j of every
+//   activation row m: (a_0, a_4), (a_1, a_5), (a_2, a_6), (a_3, a_7), 16
+//   bytes at 16 u of row m's part of the wave's LDS area;
 // * lanes 16h + m (m < M) read row m's operand back; each group's four MFMAs
-//   start from zero, and component i (activation row i) of the group's fp32
-//   sum less row i's constant is scaled by s[n, g] into the row result
-//   (scales of a wave are GSW consecutive halves of a row: GSW / 4 8-byte
-//   loads);
+//   start from zero on exact weight values q - z (w4_quad), and component i
+//   (activation row i) of the group's fp32 sum is scaled by s[n, g] into the
+//   row result (scales of a wave are GSW consecutive halves of a row: GSW / 4
+//   8-byte loads);
 // * rows 0 .. MT-1 of the wave results meet in LDS; one barrier, a
 //   fixed-order sum.
 // ASYM: per-(row, group) zero points z (uint8, [N, K/128]) instead of 8: the
-// group's constant splits into 1024 sum a' and sum a (both independent of
-// the weight row, two row sums), and the group value is
-// acc - 1024 sum a' - z sum a.
-// bf16: 7 fraction bits hold a nibble at bits 0..3 (value 128 + q over the
-// bf16 constant 128.0) or at bits 3..6 (128 + 8 q), so the odd nibbles are
-// shifted down one bit before masking (x >> 1 and x >> 9), the odd a' pairs
-// are pre-scaled by 1/8 instead of 1/16 (through fp32: gfx950 has no packed
-// bf16 multiply), and the constants become a' (128 + 8 8^s) and 128 sum a'.
+// packed constants -(1024 + z), -(64 + z) are built per row and group.
+// bf16: the exact fp16 integers are converted to bf16 (w4_quad_bf16).
 template <class T, int R, int GSW, bool ASYM, int MT>
 __global__ __launch_bounds__(1024) void w4_gemv_m1_kernel(GemmArgs p) {
     constexpr bool kBf = std::is_same<T, BF16>::value;
     extern __shared__ uint4 smem[];
     constexpr int U = GSW / 4;            // 8-column units per lane and row
-    constexpr int kRowLds = GSW * 256;    // a' bytes of one activation row
+    constexpr int kRowLds = GSW * 256;    // pair bytes of one activation row
     uint8_t* lds = reinterpret_cast<uint8_t*>(smem);
     const int W = blockDim.x >> 6;
     const int lane = threadIdx.x & (kWave - 1);
@@ -1106,7 +911,7 @@ __global__ __launch_bounds__(1024) void w4_gemv_m1_kernel(GemmArgs p) {
     const int64_t G = p.K / 128;
     const int64_t n_base = (int64_t)blockIdx.x * (16 * R);
     const int g0 = wave * GSW;
-    uint8_t* aps = lds + wave * (MT * kRowLds);                           // this wave's a'
+    uint8_t* aps = lds + wave * (MT * kRowLds);                           // this wave's pairs
     float* red = reinterpret_cast<float*>(lds + W * (MT * kRowLds));      // [W][R][MT][16]
 
     // 1. loads in the order they are consumed: activations, scales, zero
@@ -1151,64 +956,12 @@ __global__ __launch_bounds__(1024) void w4_gemv_m1_kernel(GemmArgs p) {
             q[gi][r] = *reinterpret_cast<const uint4*>(cbase + (int64_t)r * 16 * rb + 64 * gi + (uint64_t)lo);
     }
 
-    // 2. a' pairs of this lane's units to LDS, and the (row, group) constants
-    float dg[MT][GSW], sg[MT][GSW];
+    // 2. activation pairs of this lane's units to LDS
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
-        float dpu[U], dsu[U];
 #pragma unroll
-        for (int j = 0; j < U; ++j) {
-            const uint4 a = av[m][j];
-            const uint32_t p0 = __builtin_amdgcn_perm(a.z, a.x, 0x05040100u);
-            const uint32_t p2 = __builtin_amdgcn_perm(a.w, a.y, 0x05040100u);
-            uint32_t p1 = __builtin_amdgcn_perm(a.z, a.x, 0x07060302u);
-            uint32_t p3 = __builtin_amdgcn_perm(a.w, a.y, 0x07060302u);
-            if constexpr (kBf) {
-                auto eighth = [](uint32_t v) {
-                    const float lo = __uint_as_float(v << 16) * 0.125f, hi = __uint_as_float(v & 0xFFFF0000u) * 0.125f;
-                    return __builtin_bit_cast(uint32_t, bf16x2{(__bf16)lo, (__bf16)hi});
-                };
-                p1 = eighth(p1);
-                p3 = eighth(p3);
-            } else {
-                const f16x2 s16 = f16x2{(_Float16)0.0625f, (_Float16)0.0625f};
-                p1 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, p1) * s16);
-                p3 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, p3) * s16);
-            }
-            // symmetric: sum a' (1024 + 8 16^s) = (1032, 1152) patterns (bf16:
-            // 128 + 8 8^s = 136, 192); ASYM: sum a' 1024 (128), and sum a =
-            // (1, 16) patterns (bf16: (1, 8)) on the scaled pairs
-            constexpr uint32_t c0 = kBf ? (ASYM ? 0x43004300u : 0x43084308u) : (ASYM ? 0x64006400u : 0x64086408u);
-            constexpr uint32_t c1 = kBf ? (ASYM ? 0x43004300u : 0x43404340u) : (ASYM ? 0x64006400u : 0x64806480u);
-            constexpr uint32_t e0 = kBf ? 0x3F803F80u : 0x3C003C00u;
-            constexpr uint32_t e1 = kBf ? 0x41004100u : 0x4C004C00u;
-            auto dot2 = [](uint32_t x, uint32_t c, float acc) {
-                if constexpr (kBf)
-                    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x), __builtin_bit_cast(bf16x2, c), acc, false);
-                else
-                    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, x), __builtin_bit_cast(f16x2, c), acc, false);
-            };
-            float dp = 0.0f;
-            dp = dot2(p0, c0, dp);
-            dp = dot2(p1, c1, dp);
-            dp = dot2(p2, c0, dp);
-            dp = dot2(p3, c1, dp);
-            dpu[j] = row16_sum(dp);  // DPP row r: the constant of group 4 j + r
-            if constexpr (ASYM) {
-                float sa = 0.0f;
-                sa = dot2(p0, e0, sa);
-                sa = dot2(p1, e1, sa);
-                sa = dot2(p2, e0, sa);
-                sa = dot2(p3, e1, sa);
-                dsu[j] = row16_sum(sa);
-            }
-            *reinterpret_cast<uint4*>(aps + m * kRowLds + 16 * (lane + 64 * j)) = make_uint4(p0, p1, p2, p3);
-        }
-#pragma unroll
-        for (int gi = 0; gi < GSW; ++gi) {
-            dg[m][gi] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dpu[gi / 4]), 16 * (gi % 4)));
-            if constexpr (ASYM) sg[m][gi] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dsu[gi / 4]), 16 * (gi % 4)));
-        }
+        for (int j = 0; j < U; ++j)
+            *reinterpret_cast<uint4*>(aps + m * kRowLds + 16 * (lane + 64 * j)) = w4_act_quad(av[m][j]);
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's LDS writes are complete
 
@@ -1220,9 +973,7 @@ __global__ __launch_bounds__(1024) void w4_gemv_m1_kernel(GemmArgs p) {
     for (int r = 0; r < R; ++r)
 #pragma unroll
         for (int i = 0; i < MT; ++i) res[r][i] = 0.0f;
-    const uint32_t magic_v = vgpr_const<kBf ? kMagicBf2 : kMagic2>();
-    const uint32_t m0 = sgpr_const<0x000F000Fu>();
-    const uint32_t m1 = sgpr_const<kBf ? 0x00780078u : 0x00F000F0u>();
+    const uint32_t magic_v = vgpr_const<kMagic2>();
     const bool a_live = MT == 1 ? i16 == 0 : i16 < M;
 #pragma unroll
     for (int gi = 0; gi < GSW; ++gi) {
@@ -1236,27 +987,20 @@ __global__ __launch_bounds__(1024) void w4_gemv_m1_kernel(GemmArgs p) {
         }
 #pragma unroll
         for (int r = 0; r < R; ++r) {
+            W4Sub k{__builtin_bit_cast(f16x2, kW4Sub0Sym), __builtin_bit_cast(f16x2, kW4Sub1Sym)};
+            if constexpr (ASYM) k = w4_sub((zw[r][gi / 4] >> (8 * (gi % 4))) & 0xFFu);
             f32x4 ag = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int d = 0; d < 4; ++d) {
                 const uint32_t x = dword_of(q[gi][r], d);
-                const uint32_t y = x >> 8;
-                const uint32_t x1 = kBf ? x >> 1 : x;
-                const uint32_t y1 = kBf ? x >> 9 : y;
-                const uint4 bw = make_uint4((x & m0) | magic_v, (x1 & m1) | magic_v, (y & m0) | magic_v, (y1 & m1) | magic_v);
+                const uint4 bw = kBf ? w4_quad_bf16(x, magic_v, k.k0, k.k1) : w4_quad(x, magic_v, k.k0, k.k1);
                 ag = sm_mma<T>(aw[d], bw, ag);
             }
             const uint2 sw = scw[r][gi / 4];
             const uint32_t sd = (gi % 4) < 2 ? sw.x : sw.y;
             const float s = f16_bits_to_f32((uint16_t)(sd >> (16 * (gi % 2))));
-            float zf = 0.0f;
-            if constexpr (ASYM) zf = (float)((zw[r][gi / 4] >> (8 * (gi % 4))) & 0xFFu);
 #pragma unroll
-            for (int i = 0; i < MT; ++i) {
-                float v = ag[i] - dg[i][gi];
-                if constexpr (ASYM) v -= zf * sg[i][gi];
-                res[r][i] = fmaf(s, v, res[r][i]);
-            }
+            for (int i = 0; i < MT; ++i) res[r][i] = fmaf(s, ag[i], res[r][i]);
         }
     }
 
@@ -1278,11 +1022,11 @@ __global__ __launch_bounds__(1024) void w4_gemv_m1_kernel(GemmArgs p) {
     }
 }
 
-// W4A16, streaming schedule (fp16, 3 <= M <= 16): the arithmetic above with
+// W4A16, streaming schedule (fp16 or bf16, 3 <= M <= 16): the arithmetic above with
 // the work split of the ternary streaming kernel.  One workgroup walks T
 // consecutive 16-row blocks; wave w owns groups w*GSW .. w*GSW + GSW-1 (128
-// columns each) of its K range, so it builds the activation operands and the
-// groups' constant terms once and contracts every row-block against them.
+// columns each) of its K range, so it builds the activation operands once
+// and contracts every row-block against them.
 // Activations reach the wave's LDS area by DMA, four 256-byte row slices per
 // instruction (lane l: row 4e + l/16, 16-byte slot l%16, slot q of row r at
 // q ^ (r % 16)), MR/4 instructions for the MR >= M rows; each lane then reads
@@ -1291,20 +1035,16 @@ __global__ __launch_bounds__(1024) void w4_gemv_m1_kernel(GemmArgs p) {
 // one vmcnt wait for the DMA only.  With S = gridDim.y > 1 splits of the groups
 // the workgroup stores fp32 partials (group scales applied) for
 // launch_splitk_reduce.
-// ASYM: per-(row, group) zero points z instead of 8.  A group's start term
-// then depends on the row: sum_k a' (1024 + 16^s q) - sum_k a' (1024 +
-// 16^s z) = acc - 1024 sum a' - z sum a.  So each wave also contracts the
-// group's operand with the constant -1024 pattern (D) and with (1, 16, 1, 16)
-// (sum a, the same for every weight row), and each row-block subtracts z
-// times the latter from its group sum.  The zero points are loaded with the
-// scales, before the DMA.
+// ASYM: per-(row, group) zero points z instead of 8, loaded with the scales
+// before the DMA; each row-block builds its packed constants -(1024 + z),
+// -(64 + z) per group, so the operand is q - z exactly.
 __host__ __device__ constexpr int w4_stream_wave_lds(int gsw, int mr, int t) {  // bytes of one wave's LDS area
     return t * 1024 > gsw * mr * 256 ? t * 1024 : gsw * mr * 256;
 }
 
 template <class AT, int GSW, int T, int MR, bool ASYM>
 __global__ __launch_bounds__(1024) void w4_gemv_stream_kernel(SplitArgs sa) {
-    constexpr bool kBf = std::is_same<AT, BF16>::value;  // bf16: the small-M kernel's bf16 unpack
+    constexpr bool kBf = std::is_same<AT, BF16>::value;  // bf16: exact integers converted to bf16
     const GemmArgs& p = sa.g;
     extern __shared__ uint4 smem[];
     constexpr int kArea = w4_stream_wave_lds(GSW, MR, T);
@@ -1389,45 +1129,16 @@ __global__ __launch_bounds__(1024) void w4_gemv_stream_kernel(SplitArgs sa) {
     }
 
     // 3. wait for the DMA only (completion is in order), build the operands
-    //    and each group's constant term
     static_assert(T * GSW <= 63, "vmcnt range");
     asm volatile("s_waitcnt vmcnt(%0)" :: "n"(T * GSW) : "memory");
     const int rd_row = i16 & (MR - 1);
-    const f16x2 sixteenth = f16x2{(_Float16)0.0625f, (_Float16)0.0625f};
-    // symmetric: -(1024 + 8 * 16^s); ASYM: -1024, and the (1, 16) pattern for
-    // sum a (bf16: -(128 + 8 * 8^s), -128, (1, 8))
-    constexpr uint32_t n0 = kBf ? (ASYM ? 0xC300C300u : 0xC308C308u) : (ASYM ? 0xE400E400u : kW4Neg0);
-    constexpr uint32_t n1 = kBf ? (ASYM ? 0xC300C300u : 0xC340C340u) : (ASYM ? 0xE400E400u : kW4Neg1);
-    constexpr uint32_t e0 = kBf ? 0x3F803F80u : 0x3C003C00u;
-    constexpr uint32_t e1 = kBf ? 0x41004100u : 0x4C004C00u;
-    const uint4 negp = make_uint4(n0, n1, n0, n1);
-    const uint4 sump = make_uint4(e0, e1, e0, e1);
-    auto odd_pair = [&](uint32_t v) -> uint32_t {  // (a_i, a_i+4) / 16, bf16: / 8
-        if constexpr (kBf) {
-            const float lo = __uint_as_float(v << 16) * 0.125f, hi = __uint_as_float(v & 0xFFFF0000u) * 0.125f;
-            return __builtin_bit_cast(uint32_t, bf16x2{(__bf16)lo, (__bf16)hi});
-        } else {
-            return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, v) * sixteenth);
-        }
-    };
     uint4 aop[GSW][4];
-    f32x4 dacc[GSW], sacc[GSW];
 #pragma unroll
     for (int s = 0; s < GSW; ++s) {
-        dacc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
-        sacc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
-            const uint4 v = *reinterpret_cast<const uint4*>(area + s * MR * 256 + rd_row * 256 +
-                                                            16 * ((4 * h + d) ^ (rd_row & 15)));
-            const uint32_t p0 = __builtin_amdgcn_perm(v.z, v.x, 0x05040100u);
-            const uint32_t p1 = odd_pair(__builtin_amdgcn_perm(v.z, v.x, 0x07060302u));
-            const uint32_t p2 = __builtin_amdgcn_perm(v.w, v.y, 0x05040100u);
-            const uint32_t p3 = odd_pair(__builtin_amdgcn_perm(v.w, v.y, 0x07060302u));
-            aop[s][d] = make_uint4(p0, p1, p2, p3);
-            dacc[s] = sm_mma<AT>(aop[s][d], negp, dacc[s]);
-            if constexpr (ASYM) sacc[s] = sm_mma<AT>(aop[s][d], sump, sacc[s]);
-        }
+        for (int d = 0; d < 4; ++d)
+            aop[s][d] = w4_act_quad(*reinterpret_cast<const uint4*>(area + s * MR * 256 + rd_row * 256 +
+                                                                    16 * ((4 * h + d) ^ (rd_row & 15))));
     }
 
     // the empty asm statements keep the compiler from consuming the loaded
@@ -1456,7 +1167,7 @@ __global__ __launch_bounds__(1024) void w4_gemv_stream_kernel(SplitArgs sa) {
     }
 
     // 4. contract each row-block as its codes land
-    const uint32_t magic_v = vgpr_const<kBf ? kMagicBf2 : kMagic2>();
+    const uint32_t magic_v = vgpr_const<kMagic2>();
     f32x4 acc[T];
 #pragma unroll
     for (int t = 0; t < T; ++t) {
@@ -1464,22 +1175,14 @@ __global__ __launch_bounds__(1024) void w4_gemv_stream_kernel(SplitArgs sa) {
 #pragma unroll
         for (int s = 0; s < GSW; ++s) {
             if (s < cnt) {
-                f32x4 ag = dacc[s];
+                W4Sub k{__builtin_bit_cast(f16x2, kW4Sub0Sym), __builtin_bit_cast(f16x2, kW4Sub1Sym)};
+                if constexpr (ASYM) k = w4_sub((uint32_t)zp[t][s]);
+                f32x4 ag = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int d = 0; d < 4; ++d) {
                     const uint32_t x = dword_of(q[t][s], d);
-                    const uint32_t y = x >> 8;
-                    const uint32_t x1 = kBf ? x >> 1 : x;
-                    const uint32_t y1 = kBf ? x >> 9 : y;
-                    constexpr uint32_t m1 = kBf ? 0x00780078u : 0x00F000F0u;
-                    const uint4 bw = make_uint4((x & sgpr_const<0x000F000Fu>()) | magic_v, (x1 & sgpr_const<m1>()) | magic_v,
-                                                (y & sgpr_const<0x000F000Fu>()) | magic_v, (y1 & sgpr_const<m1>()) | magic_v);
+                    const uint4 bw = kBf ? w4_quad_bf16(x, magic_v, k.k0, k.k1) : w4_quad(x, magic_v, k.k0, k.k1);
                     ag = sm_mma<AT>(aop[s][d], bw, ag);
-                }
-                if constexpr (ASYM) {
-                    const float z = (float)zp[t][s];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) ag[i] = fmaf(-z, sacc[s][i], ag[i]);
                 }
                 const float sv = f16_bits_to_f32((uint16_t)sc[t][s]);
 #pragma unroll

@@ -128,13 +128,22 @@ struct BF16 {
     static __device__ __forceinline__ uint16_t from_f32_fast(float x) { return f32_to_bf16_rne(x); }
 };
 
-// ---- fp16 a' unpack of ternary codes (the scheme is laid out at the
-// matrix-core GEMV in gemv.hip): field I of a code dword x, masked into the
-// mantissa of 1024.0, is the pair (1024 + 4^s c_I, 1024 + 4^s c_{I+8}),
-// s = I for I < 5 and I - 5 (after x >> 10) otherwise; the activations of
-// the same columns are paired and pre-scaled by 1 / 4^s to match.
+// ---- exact ternary operands for the matrix cores (the scheme is laid out
+// at the matrix-core GEMV in gemv.hip).  Field I of a code dword x, masked
+// into the mantissa of 1024.0, is the pair (1024 + 4^s c_I, 1024 + 4^s
+// c_{I+8}), s = I for I < 5 and I - 5 (after x >> 10) otherwise.  One packed
+// fp16 fma, v * 4^-s - (1024 / 4^s + 1), turns each half into c - 1, the
+// ternary value itself, without rounding: v * 4^-s = 1024 / 4^s + c is exact
+// and so is the difference.  The activations of the same columns are paired
+// to match but not scaled, so the matrix units multiply a_k by -1, 0 or +1
+// and the fp32 sums carry no offset that would later cancel.
+//
+// Read as bfloat16, the fp16 bit patterns of -1, 0 and +1 (0xBC00, 0, 0x3C00)
+// are -2^-7, 0 and +2^-7: the same operand feeds the bf16 matrix cores, and
+// the bf16 kernels multiply their fp32 sums by 128 (exact).
 
 constexpr uint32_t kMagic2 = 0x64006400u;  // (1024.0, 1024.0) as fp16
+constexpr float kBf16TernaryUnit = 128.0f;  // 1 / (bf16 value of the fp16 pattern of +1)
 
 template <int I>
 __device__ __forceinline__ uint32_t field_pair(uint32_t x, uint32_t y, uint32_t magic_v) {
@@ -142,42 +151,99 @@ __device__ __forceinline__ uint32_t field_pair(uint32_t x, uint32_t y, uint32_t 
     else return (y & sgpr_const<(0x00030003u << (2 * (I - 5)))>()) | magic_v;
 }
 
-// 1 / 4^s for field I, as an fp16 pair.
+// (t_I, t_{I+8}) of code dword x (y = x >> 10) as exact fp16 values.
 template <int I>
-__device__ __forceinline__ f16x2 inv_mult() {
+__device__ __forceinline__ uint32_t tern_pair(uint32_t x, uint32_t y, uint32_t magic_v) {
     constexpr int s = I < 5 ? I : I - 5;
-    const _Float16 v = (_Float16)(1.0f / (float)(1 << (2 * s)));
-    return f16x2{v, v};
+    constexpr float kAdd = -(float)((1024 >> (2 * s)) + 1);
+    constexpr float kMul = 1.0f / (float)(1 << (2 * s));
+    const f16x2 v = __builtin_bit_cast(f16x2, field_pair<I>(x, y, magic_v));
+    const f16x2 add = f16x2{(_Float16)kAdd, (_Float16)kAdd};
+    if constexpr (s == 0) {
+        return __builtin_bit_cast(uint32_t, v + add);
+    } else {
+        const f16x2 mul = f16x2{(_Float16)kMul, (_Float16)kMul};
+        return __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(v, mul, add));
+    }
 }
 
-// -(1024 + 4^s) for field I in both halves (the code-01 pattern, negated).
-template <int I>
-__device__ __forceinline__ constexpr uint32_t neg_one_pattern() {
-    constexpr int s = I < 5 ? I : I - 5;
-    return 0xE400E400u | (0x00010001u << (2 * s));
+// Four exact operand dwords of code dword x for fields I0 .. I0+3.
+template <int I0>
+__device__ __forceinline__ uint4 tern_quad(uint32_t x, uint32_t magic_v) {
+    const uint32_t y = x >> 10;
+    return make_uint4(tern_pair<I0>(x, y, magic_v), tern_pair<I0 + 1>(x, y, magic_v),
+                      tern_pair<I0 + 2>(x, y, magic_v), tern_pair<I0 + 3>(x, y, magic_v));
 }
 
-// a' pair for field I of code dword D: (a[16D+I], a[16D+I+8]) / 4^s(I).
+// Activation pair matching field I of code dword D: (a[16D+I], a[16D+I+8]),
+// 16-bit patterns (fp16 or bf16) of 16 consecutive columns per two uint4.
 template <int D, int I>
-__device__ __forceinline__ uint32_t a_pair(const uint4 av[8]) {
+__device__ __forceinline__ uint32_t act_pair(const uint4 av[8]) {
     const uint4& lo4 = av[2 * D];
     const uint4& hi4 = av[2 * D + 1];
     constexpr int c = I / 2;
     const uint32_t lo = c == 0 ? lo4.x : c == 1 ? lo4.y : c == 2 ? lo4.z : lo4.w;
     const uint32_t hi = c == 0 ? hi4.x : c == 1 ? hi4.y : c == 2 ? hi4.z : hi4.w;
-    const uint32_t pr = __builtin_amdgcn_perm(hi, lo, (I & 1) ? 0x07060302u : 0x05040100u);
-    const f16x2 v = __builtin_bit_cast(f16x2, pr) * inv_mult<I>();
-    return __builtin_bit_cast(uint32_t, v);
+    return __builtin_amdgcn_perm(hi, lo, (I & 1) ? 0x07060302u : 0x05040100u);
+}
+
+// The eight activation pairs of 16 columns (fields 0..3, then 4..7).
+template <int D>
+__device__ __forceinline__ void act_pairs16(const uint4 av[8], uint4& f03, uint4& f47) {
+    f03 = make_uint4(act_pair<D, 0>(av), act_pair<D, 1>(av), act_pair<D, 2>(av), act_pair<D, 3>(av));
+    f47 = make_uint4(act_pair<D, 4>(av), act_pair<D, 5>(av), act_pair<D, 6>(av), act_pair<D, 7>(av));
 }
 
 __device__ __forceinline__ uint32_t dword_of(const uint4& q, int d) {
     return d == 0 ? q.x : d == 1 ? q.y : d == 2 ? q.z : q.w;
 }
 
-template <int I>
-__device__ __forceinline__ constexpr uint32_t one_pattern() {  // (1024 + 4^s) in both halves
-    constexpr int s = I < 5 ? I : I - 5;
-    return 0x64006400u | (0x00010001u << (2 * s));
+// ---- exact W4A16 operands.  Nibble q_i of a code word x sits at bits 4i;
+// masked into the mantissa of 1024.0, (x & 0x000F000F) | magic = (1024 + q_0,
+// 1024 + q_4) and (x & 0x00F000F0) | magic = (1024 + 16 q_1, 1024 + 16 q_5),
+// and with x >> 8 the pairs (q_2, q_6) and (q_3, q_7).  One packed fp16
+// add or fma per pair subtracts 1024 + z (or scales by 1/16 and subtracts
+// 64 + z), leaving q - z exactly (integers of magnitude <= 15).  The
+// activations are paired to match: (a_0, a_4), (a_1, a_5), (a_2, a_6),
+// (a_3, a_7).
+struct W4Sub {
+    f16x2 k0, k1;  // -(1024 + z), -(64 + z) in both halves
+};
+__device__ __forceinline__ W4Sub w4_sub(uint32_t z) {  // z in 0..15
+    // -(1024 + z): sign, exponent 10, fraction z; -(64 + z): exponent 6,
+    // fraction 16 z (unit in the last place 1/16)
+    const uint32_t a = 0xE400u + z, b = 0xD400u + 16u * z;
+    return W4Sub{__builtin_bit_cast(f16x2, a | (a << 16)), __builtin_bit_cast(f16x2, b | (b << 16))};
+}
+constexpr uint32_t kW4Sub0Sym = 0xE408E408u;  // -(1024 + 8), both halves
+constexpr uint32_t kW4Sub1Sym = 0xD480D480u;  // -(64 + 8), both halves
+
+__device__ __forceinline__ uint4 w4_quad(uint32_t x, uint32_t magic_v, f16x2 k0, f16x2 k1) {
+    const uint32_t y = x >> 8;
+    const f16x2 sixteenth = f16x2{(_Float16)0.0625f, (_Float16)0.0625f};
+    const f16x2 v0 = __builtin_bit_cast(f16x2, (x & sgpr_const<0x000F000Fu>()) | magic_v);
+    const f16x2 v1 = __builtin_bit_cast(f16x2, (x & sgpr_const<0x00F000F0u>()) | magic_v);
+    const f16x2 v2 = __builtin_bit_cast(f16x2, (y & sgpr_const<0x000F000Fu>()) | magic_v);
+    const f16x2 v3 = __builtin_bit_cast(f16x2, (y & sgpr_const<0x00F000F0u>()) | magic_v);
+    return make_uint4(__builtin_bit_cast(uint32_t, v0 + k0), __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(v1, sixteenth, k1)),
+                      __builtin_bit_cast(uint32_t, v2 + k0), __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(v3, sixteenth, k1)));
+}
+
+// bf16 form: the exact fp16 integers converted to bf16 through fp32 (every
+// integer of magnitude <= 15 is exact in all three formats).
+__device__ __forceinline__ uint32_t f16x2_to_bf16x2(uint32_t v) {
+    const f16x2 h = __builtin_bit_cast(f16x2, v);
+    return __builtin_bit_cast(uint32_t, bf16x2{(__bf16)(float)h.x, (__bf16)(float)h.y});
+}
+__device__ __forceinline__ uint4 w4_quad_bf16(uint32_t x, uint32_t magic_v, f16x2 k0, f16x2 k1) {
+    const uint4 h = w4_quad(x, magic_v, k0, k1);
+    return make_uint4(f16x2_to_bf16x2(h.x), f16x2_to_bf16x2(h.y), f16x2_to_bf16x2(h.z), f16x2_to_bf16x2(h.w));
+}
+
+// Activation pairs of one code word's eight columns (v: columns 8d .. 8d+7).
+__device__ __forceinline__ uint4 w4_act_quad(const uint4& v) {
+    return make_uint4(__builtin_amdgcn_perm(v.z, v.x, 0x05040100u), __builtin_amdgcn_perm(v.z, v.x, 0x07060302u),
+                      __builtin_amdgcn_perm(v.w, v.y, 0x05040100u), __builtin_amdgcn_perm(v.w, v.y, 0x07060302u));
 }
 
 // 16 bytes per lane, global -> LDS at M0 + 16 * lane (M0 must be wave-uniform).

@@ -123,3 +123,83 @@ def activations_device(M: int, K: int, seed: int, dtype: str, device):
     g.manual_seed(seed)
     a = torch.randn((M, K), generator=g, device=device, dtype=torch.float32)
     return a.to(torch.float16 if dtype == "f16" else torch.bfloat16)
+
+
+# ---------------------------------------------------------------- edge cases
+#
+# Inputs that stress the accumulation rather than the pack rule: weight rows
+# with very few nonzero values and scales across the binary16 range, next to
+# dense rows, and activations with outliers or of tiny magnitude.
+
+EDGE_SCALES = (1.0, 0.5, 3.0e-3, 6.0e4, 1.0e-4, 7.3, 1.5e3, 0.02)
+ACT_REGIMES = ("dense", "outlier", "tiny")
+
+
+def sparse_ternary_weights(N: int, K: int, seed: int) -> np.ndarray:
+    """fp32 [N, K] whose rows cycle through: all zero; one kept entry (+s or
+    -s); 2 .. 8 kept entries of random sign; dense N(0, 0.02); dense with a
+    large spread (N(0, 2e4)).  A row of k entries of magnitude s and zeros
+    elsewhere keeps exactly those k entries (s > 0.7 k s / K) with scale s;
+    s cycles through EDGE_SCALES."""
+    rng = np.random.default_rng(seed)
+    W = np.zeros((N, K), dtype=np.float32)
+    kinds = 12
+    for n in range(N):
+        kind = n % kinds
+        s = EDGE_SCALES[(n // kinds) % len(EDGE_SCALES)]
+        if kind == 0:
+            continue
+        if kind in (1, 2):
+            W[n, rng.integers(K)] = s if kind == 1 else -s
+        elif kind <= 9:
+            k = kind - 1  # 2 .. 8 entries
+            cols = rng.choice(K, size=k, replace=False)
+            W[n, cols] = np.where(rng.integers(2, size=k) == 0, -s, s)
+        elif kind == 10:
+            W[n] = rng.normal(0.0, SIGMA, K)
+        else:
+            W[n] = rng.normal(0.0, 2.0e4, K)
+    return W
+
+
+def sparse_w4_weights(N: int, K: int, seed: int) -> np.ndarray:
+    """fp32 [N, K] with 128-column groups of these kinds, cycling over rows
+    and groups: all zero; one nonzero value (magnitudes from EDGE_SCALES); one
+    large value among values 1e-3 times smaller (which quantize to zero);
+    dense N(0, 0.02); dense N(0, 0.02) shifted by a per-group offset (zero
+    points spread over 0 .. 15 in the asymmetric format)."""
+    rng = np.random.default_rng(seed)
+    G = K // 128
+    W = np.zeros((N, K), dtype=np.float32)
+    for n in range(N):
+        for g in range(G):
+            kind = (n + 3 * g) % 5
+            s = EDGE_SCALES[(n + g) % len(EDGE_SCALES)]
+            blk = W[n, 128 * g:128 * (g + 1)]
+            if kind == 1:
+                blk[rng.integers(128)] = s * (1 if rng.integers(2) else -1)
+            elif kind == 2:
+                blk[:] = rng.normal(0.0, 1.0e-3 * s, 128)
+                blk[rng.integers(128)] = s
+            elif kind == 3:
+                blk[:] = rng.normal(0.0, SIGMA, 128)
+            elif kind == 4:
+                blk[:] = rng.normal(0.0, SIGMA, 128) + rng.uniform(-0.03, 0.03)
+    return W
+
+
+def activations_regime(M: int, K: int, seed: int, regime: str, dtype: str = "f16"):
+    """torch CPU tensor [M, K]: "dense" N(0, 1); "outlier" N(0, 1) with eight
+    entries per row replaced by +-U(200, 1000); "tiny" N(0, 1) * 2^-12 (a
+    few values fall into the binary16 subnormal range)."""
+    rng = np.random.default_rng(seed)
+    a = rng.standard_normal((M, K))
+    if regime == "outlier":
+        for m in range(M):
+            cols = rng.choice(K, size=min(8, K), replace=False)
+            a[m, cols] = rng.uniform(200.0, 1000.0, len(cols)) * np.where(rng.integers(2, size=len(cols)) == 0, -1, 1)
+    elif regime == "tiny":
+        a = a * 2.0 ** -12
+    elif regime != "dense":
+        raise ValueError(f"unknown activation regime {regime!r}")
+    return _to_torch(a, dtype)

@@ -520,6 +520,72 @@ def pin_tolerance_check(o):
     assert qc == {"ok": False, "max_abs": 0.5, "mean_abs": 0.25, "finite": True}
 
 
+def pin_ternary_dequant_loop(o):
+    """The loop tier's dequant: s16 * t for every row of every sign pattern
+    (brute force over 3^6 rows of K = 6, scales 0.25, 3 and a subnormal),
+    the same values as the numpy tier, and IEEE zeros of the form +0."""
+    import itertools
+    K = 6
+    for s in (0.25, 3.0, 2.0 ** -20):
+        rows = np.array(list(itertools.product((-1, 0, 1), repeat=K)), dtype=np.float64)
+        rows = rows[np.any(rows != 0, axis=1)]
+        W = (rows * s).astype(np.float32)
+        codes, sb = o.ternary.ternary_pack(W)
+        loop = np.array(o.ternary.ternary_dequant_loop(codes.tolist(), sb.tolist(), K))
+        s16 = o.rne.f16_value_exact(int(sb[0]))
+        assert np.all(sb == sb[0]) and s16 == float(np.float16(s))
+        assert np.array_equal(loop, rows * s16)
+        assert np.array_equal(loop, o.ternary.ternary_dequant(codes, sb, K))
+        assert not np.any(np.signbit(loop[rows == 0]))
+
+
+def pin_bf16_values_exhaustive(o):
+    """Both bf16 decoders on all 65536 bit patterns against torch's own
+    bfloat16 -> float32 conversion (NaNs as NaNs), plus hand values."""
+    import torch
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).float().double().numpy()
+    vec = o.rne.bf16_values(bits)
+    loop = np.array([o.rne.bf16_value_exact(int(b)) for b in bits])
+    for got in (vec, loop):
+        nan = np.isnan(ref)
+        assert np.array_equal(np.isnan(got), nan)
+        assert np.array_equal(got[~nan], ref[~nan])
+        assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+    assert o.rne.bf16_value_exact(0x3F80) == 1.0
+    assert o.rne.bf16_value_exact(0x0001) == 2.0 ** -133
+    assert o.rne.bf16_value_exact(0x7F7F) == (2.0 - 2.0 ** -7) * 2.0 ** 127
+    assert o.rne.bf16_value_exact(0xC040) == -3.0
+
+
+def pin_tolerance_overflow(o):
+    """An infinite output passes only with the sign of the reference and only
+    when some value within the bound of it rounds to that infinity: binary16
+    rounds magnitudes from 65504 + 16 = 65520 up to infinity (65519.99 rounds
+    down to 65504), bfloat16 from (2 - 2^-8) 2^127 up (checked against numpy's
+    and torch's own conversions)."""
+    import torch
+    assert np.float16(65519.99) == 65504.0 and np.isinf(np.float16(65520.0))
+    assert o.check.F16_OVERFLOW == 65520.0
+    x32 = np.float32(o.check.BF16_OVERFLOW)
+    assert float(x32) == o.check.BF16_OVERFLOW  # exact in fp32 (9 significant bits)
+    bf = torch.tensor([x32, np.nextafter(x32, np.float32(0))], dtype=torch.float32).to(torch.bfloat16).float()
+    assert np.isinf(bf[0].item()) and np.isfinite(bf[1].item())
+    inf = np.inf
+    # reference 70000 (rounds to +inf in binary16): +inf passes, -inf and a finite value do not
+    ok, st = o.check.tolerance_ok(np.array([[inf]]), np.array([[70000.0]]), np.array([[70000.0]]))
+    assert ok and not st["finite"], st
+    assert not o.check.tolerance_ok(np.array([[-inf]]), np.array([[70000.0]]), np.array([[70000.0]]))[0]
+    assert not o.check.tolerance_ok(np.array([[65504.0]]), np.array([[70000.0]]), np.array([[70000.0]]))[0]
+    # reference 65500 with magnitude sum 65500: bound 131 reaches past 65520, so +inf passes;
+    # with magnitude sum 0 (bound 1e-3) it does not
+    assert o.check.tolerance_ok(np.array([[inf]]), np.array([[65500.0]]), np.array([[65500.0]]))[0]
+    assert not o.check.tolerance_ok(np.array([[inf]]), np.array([[65500.0]]), np.array([[0.0]]))[0]
+    # bf16: 1e38 never rounds to infinity; 3.4e38 with a loose bound does
+    assert not o.check.tolerance_ok(np.array([[inf]]), np.array([[1e38]]), np.array([[1e38]]), out_dtype="bf16")[0]
+    assert o.check.tolerance_ok(np.array([[-inf]]), np.array([[-3.4e38]]), np.array([[3.4e38]]), out_dtype="bf16")[0]
+
+
 # ------------------------------------------- W4A16, zero points and act-order
 
 def pin_w4a_format_from_pages(o):

@@ -83,6 +83,12 @@ def test_dispatcher_by_m():
         assert sel("ternary", M, 4096, 4096, "bf16") == "gemv"
         assert sel("w4a16", M, 4096, 4096, "bf16") == "gemv"
     assert sel("ternary", 17, 4096, 4096, "bf16") == "stream_mfma"
+    # rows that are not whole 256-column chunk-sets: the medium path's tiles
+    # from three activation rows, the decode path below that
+    for M in (3, 8, 16):
+        assert sel("ternary", M, 4096, 4160) == "stream_mfma"
+    for M in (1, 2):
+        assert sel("ternary", M, 4096, 4160) == "gemv"
 
 
 def test_workspace_query():

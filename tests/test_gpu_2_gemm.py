@@ -128,19 +128,20 @@ STREAM_T_SHAPES = [(12288, 4096), (20480, 4096), (24576, 4096), (28672, 4096)]
 @pytest.mark.parametrize("N,K", STREAM_T_SHAPES)
 @pytest.mark.parametrize("M", [4, 16])
 @pytest.mark.parametrize("fmt", ["ternary", "w4"])
-def test_stream_row_blocks(N, K, M, fmt):
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_stream_row_blocks(N, K, M, fmt, dt):
     import bit_weight_only_tq_amd as tq
     dev = require_gpu()
-    log(f"stream row-blocks {fmt} N={N} K={K} M={M}")
-    A = synth.activations(M, K, synth.seed_for("st", fmt, N, K, M), "f16")
-    bias = synth.activations(1, N, synth.seed_for("stb", fmt, N, K), "f16")[0]
+    log(f"stream row-blocks {fmt} N={N} K={K} M={M} {dt}")
+    A = synth.activations(M, K, synth.seed_for("st", fmt, N, K, M), dt)
+    bias = synth.activations(1, N, synth.seed_for("stb", fmt, N, K), dt)[0]
     if fmt == "ternary":
         codes, scale, rc, rs, wdq = _ternary(N, K, dev)
         C = tq.tq_gemm(A.to(dev), codes, scale, bias=bias.to(dev))
     else:
         q, s, rq, rs, wdq = _w4(N, K, dev)
         C = tq.w4a16_gemm(A.to(dev), q, s, bias=bias.to(dev))
-    check_close(C, A, wdq, bias=bias, label=f"stream {fmt} {N}x{K} M={M}")
+    check_close(C, A, wdq, bias=bias, label=f"stream {fmt} {N}x{K} M={M} {dt}")
 
 
 @pytest.mark.parametrize("N,K", [(14336, 4096), (4096, 14336)])

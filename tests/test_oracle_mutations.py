@@ -69,6 +69,15 @@ MUTATIONS = [
     ("check.py", '"mean_abs": float(diff.mean())', '"mean_abs": float(diff.max())'),
     ("check.py", "BF16_UNIT_ROUNDOFF = 2.0 ** -8", "BF16_UNIT_ROUNDOFF = 2.0 ** -6"),
     ("check.py", 'if out_dtype == "bf16":', 'if out_dtype == "never":'),
+    ("check.py", "(np.sign(C64) == np.sign(out64))", "(np.sign(C64) != 0)"),
+    ("check.py", "(np.abs(out64) + bound >= overflow)", "(np.abs(out64) >= 0)"),
+    ("check.py", "F16_OVERFLOW = 65504.0 + 16.0", "F16_OVERFLOW = 65504.0"),
+    ("ternary.py", "return [[tv * f16_value_exact(sb) for tv in row] for row, sb in zip(t, scale_bits)]",
+     "return [[tv * f16_value_exact(sb) for tv in row[::-1]] for row, sb in zip(t, scale_bits)]"),
+    ("ternary.py", "t = ternary_unpack_loop(codes, K)\n    return", "t = [[-v for v in r] for r in ternary_unpack_loop(codes, K)]\n    return"),
+    ("rne.py", "        return s * f * 2.0 ** -133", "        return s * f * 2.0 ** -126"),
+    ("rne.py", "    return s * (128 + f) * 2.0 ** (e - 134)", "    return s * (128 + f) * 2.0 ** (e - 133)"),
+    ("rne.py", "    u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16", "    u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 15"),
 ]
 
 
