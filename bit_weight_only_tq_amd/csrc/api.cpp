@@ -10,7 +10,16 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "tq_internal.h"
+
+// Status flags of the synchronous prepare calls, in the library's own device
+// memory (one copy per device), so that a prepare call allocates nothing.
+// Their address is looked up per device; prepare calls on one device share
+// the flags and are therefore serialized by a per-device host mutex.
+static __device__ __align__(16) int prepare_flags[4];
 
 namespace {
 
@@ -22,11 +31,40 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 constexpr int64_t kGemvMaxM = tq::kGemvMaxM;
 constexpr int64_t kMediumMaxM = 256;  // M < 256: medium path
 
-// Device status word for the synchronous prepare calls.
+constexpr int kMaxDevices = 64;
+
+// Device address of a file-scope __device__ symbol on the current device,
+// looked up once per device (the symbol's name in host code is only a
+// host-side stand-in, never a device address).
+template <class T>
+tq_status symbol_address(const T& sym, std::atomic<void*> (&cache)[kMaxDevices], void** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return TQ_ERR_HIP;
+    void* p = cache[dev].load(std::memory_order_acquire);
+    if (!p) {
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(sym)) != hipSuccess || !p) return TQ_ERR_HIP;
+        cache[dev].store(p, std::memory_order_release);
+    }
+    *out = p;
+    return TQ_OK;
+}
+
+std::atomic<void*> prepare_flags_ptr[kMaxDevices];
+std::mutex prepare_mutex[kMaxDevices];
+
+// Status flags of one synchronous prepare call: holds the device's prepare
+// mutex for the call's duration.
 struct StatusWord {
+    std::unique_lock<std::mutex> lock;
     int* dev = nullptr;
     tq_status init(hipStream_t s) {
-        if (hipMalloc(&dev, 4 * sizeof(int)) != hipSuccess) { dev = nullptr; return TQ_ERR_HIP; }
+        int d = 0;
+        if (hipGetDevice(&d) != hipSuccess || d < 0 || d >= kMaxDevices) return TQ_ERR_HIP;
+        lock = std::unique_lock<std::mutex>(prepare_mutex[d]);
+        void* p = nullptr;
+        const tq_status r = symbol_address(prepare_flags, prepare_flags_ptr, &p);
+        if (r != TQ_OK) return r;
+        dev = static_cast<int*>(p);
         if (hipMemsetAsync(dev, 0, 4 * sizeof(int), s) != hipSuccess) return TQ_ERR_HIP;
         return TQ_OK;
     }
@@ -34,9 +72,6 @@ struct StatusWord {
         if (hipMemcpyAsync(out, dev, 4 * sizeof(int), hipMemcpyDeviceToHost, s) != hipSuccess) return TQ_ERR_HIP;
         if (hipStreamSynchronize(s) != hipSuccess) return TQ_ERR_HIP;
         return TQ_OK;
-    }
-    ~StatusWord() {
-        if (dev) (void)hipFree(dev);
     }
 };
 

@@ -35,8 +35,9 @@
  *    TQ_ERR_PATH.  A failed launch or HIP call returns TQ_ERR_HIP.
  *  - Prepare calls (pack / unpack) are SYNCHRONOUS: they wait for `stream`
  *    and report data errors (TQ_ERR_NONFINITE, TQ_ERR_RANGE,
- *    TQ_ERR_BAD_CODE).  They allocate a small device status word for the
- *    duration of the call.
+ *    TQ_ERR_BAD_CODE).  They allocate nothing: their status flags live in
+ *    the library's own device memory, one copy per device, so prepare calls
+ *    on one device are serialized by a host mutex.
  *  - Apply calls (tq_gemm, tq_gemm_ws, w4a16_gemm) are ASYNCHRONOUS on
  *    `stream`, allocate nothing, never synchronize and are safe to capture in
  *    a HIP graph.  Faults during execution surface at the caller's next sync.
