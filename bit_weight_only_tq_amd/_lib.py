@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(HERE, "libtq.so")
 STATUS_NAMES = {
     0: "TQ_OK", 1: "TQ_ERR_NULL", 2: "TQ_ERR_SHAPE", 3: "TQ_ERR_ALIGN", 4: "TQ_ERR_DTYPE",
     5: "TQ_ERR_GROUP", 6: "TQ_ERR_NONFINITE", 7: "TQ_ERR_RANGE", 8: "TQ_ERR_BAD_CODE",
-    9: "TQ_ERR_HIP", 10: "TQ_ERR_PATH",
+    9: "TQ_ERR_HIP", 10: "TQ_ERR_PATH", 11: "TQ_ERR_SCRATCH",
 }
 # tq_dtype
 TQ_F16, TQ_BF16 = 0, 1
@@ -35,6 +35,8 @@ SIGNATURES = {
     "tq_gemm_ex": (_i32, [_vp, _i32, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _i32]),
     "tq_gemm_ws": (_i32, [_vp, _i32, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _sz, _vp, _i32]),
     "tq_gemm_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32, _i32]),
+    "tq_gemm_noalloc": (_i32, [_vp, _i32, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _i32]),
+    "tq_gemm_noalloc_scratch_bytes": (_sz, []),
     "w4a16_gemm": (_i32, [_vp, _i32, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _vp]),
     "w4a16_gemm_ex": (_i32, [_vp, _i32, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _vp, _i32]),
     "w4a16_gemm_ws": (_i32, [_vp, _i32, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp, _i32]),
@@ -277,6 +279,21 @@ def tq_gemm(A, codes, scale, bias=None, out=None, path: str = "auto", workspace=
         ws_bytes = workspace.numel() * workspace.element_size()
     _check("tq_gemm", load().tq_gemm_ws(_ptr(A), dt, M, N, K, _ptr(codes), _ptr(scale), _ptr(bias), _ptr(C),
                                          _ptr(workspace), ws_bytes, _stream(A.device), PATHS[path]))
+    return C
+
+
+def tq_gemm_noalloc(A, codes, scale, bias=None, out=None, path: str = "auto"):
+    """tq_gemm through the entry point that allocates nothing (its split-K
+    partials go to the library's per-device scratch; see include/tq.h)."""
+    import torch
+    M, K = _check_activations(A)
+    N = _ternary_layout(codes, scale, K).N
+    _check_out_bias(A, N, bias, out)
+    _need_cuda(A, codes, scale, bias, out)
+    dt = _dtype_enum(A)
+    C = out if out is not None else torch.empty((M, N), dtype=A.dtype, device=A.device)
+    _check("tq_gemm_noalloc", load().tq_gemm_noalloc(_ptr(A), dt, M, N, K, _ptr(codes), _ptr(scale), _ptr(bias),
+                                                     _ptr(C), _stream(A.device), PATHS[path]))
     return C
 
 

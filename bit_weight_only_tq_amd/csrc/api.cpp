@@ -21,6 +21,12 @@
 // the flags and are therefore serialized by a per-device host mutex.
 static __device__ __align__(16) int prepare_flags[4];
 
+// Scratch memory of tq_gemm_noalloc: the split-K partials of the apply
+// kernels, for callers that cannot allocate.  One copy per device, held
+// until the process ends; every call on a device shares it.
+constexpr size_t kScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
 namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -50,6 +56,7 @@ tq_status symbol_address(const T& sym, std::atomic<void*> (&cache)[kMaxDevices],
 }
 
 std::atomic<void*> prepare_flags_ptr[kMaxDevices];
+std::atomic<void*> scratch_ptr[kMaxDevices];
 std::mutex prepare_mutex[kMaxDevices];
 
 // Status flags of one synchronous prepare call: holds the device's prepare
@@ -106,6 +113,7 @@ const char* tq_status_str(tq_status s) {
         case TQ_ERR_BAD_CODE: return "packed code field 0b11 (unused) found";
         case TQ_ERR_HIP: return "HIP runtime error or kernel launch failure";
         case TQ_ERR_PATH: return "forced kernel path cannot run this shape";
+        case TQ_ERR_SCRATCH: return "the call needs more scratch memory than tq_gemm_noalloc holds";
     }
     return "unknown status";
 }
@@ -239,6 +247,20 @@ tq_status tq_gemm_ex(const void* A, tq_dtype dt, int64_t M, int64_t N, int64_t K
 tq_status tq_gemm(const void* A, tq_dtype dt, int64_t M, int64_t N, int64_t K, const uint8_t* codes,
                   const uint16_t* scale_f16, const void* bias, void* C, hipStream_t stream) {
     return tq_gemm_ws(A, dt, M, N, K, codes, scale_f16, bias, C, nullptr, 0, stream, TQ_PATH_AUTO);
+}
+
+size_t tq_gemm_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+tq_status tq_gemm_noalloc(const void* A, tq_dtype dt, int64_t M, int64_t N, int64_t K, const uint8_t* codes,
+                          const uint16_t* scale_f16, const void* bias, void* C, hipStream_t stream, tq_path path) {
+    tq_status r = check_gemm_common(A, dt, M, N, K, codes, scale_f16, C);
+    if (r != TQ_OK) return r;
+    if (K % 64 != 0) return TQ_ERR_SHAPE;
+    const size_t need = tq_gemm_workspace_bytes(M, N, K, dt, path);
+    if (need > kScratchBytes) return TQ_ERR_SCRATCH;
+    void* ws = nullptr;
+    if (need > 0 && (r = symbol_address(scratch, scratch_ptr, &ws)) != TQ_OK) return r;
+    return tq_gemm_ws(A, dt, M, N, K, codes, scale_f16, bias, C, ws, need, stream, path);
 }
 
 tq_status w4a16_gemm_ws(const void* A, tq_dtype dt, int64_t M, int64_t N, int64_t K, const int32_t* qweight,

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define TQ_ABI_VERSION 4
+#define TQ_ABI_VERSION 5
 
 typedef enum tq_status {
     TQ_OK = 0,
@@ -68,7 +68,8 @@ typedef enum tq_status {
     TQ_ERR_RANGE = 7,      /* pack: a scale rounds to infinity in fp16 */
     TQ_ERR_BAD_CODE = 8,   /* unpack: a 2-bit field holds the unused 0b11 */
     TQ_ERR_HIP = 9,        /* a HIP runtime call or kernel launch failed */
-    TQ_ERR_PATH = 10       /* a forced kernel path cannot run this shape */
+    TQ_ERR_PATH = 10,      /* a forced kernel path cannot run this shape */
+    TQ_ERR_SCRATCH = 11    /* tq_gemm_noalloc: the schedule needs more than its scratch */
 } tq_status;
 
 typedef enum tq_dtype {
@@ -192,6 +193,29 @@ tq_status tq_gemm_ws(const void* A, tq_dtype dt, int64_t M, int64_t N, int64_t K
                      const uint8_t* codes, const uint16_t* scale_f16, const void* bias,
                      void* C, void* workspace, size_t workspace_bytes,
                      hipStream_t stream, tq_path path);
+
+/*
+ * tq_gemm_noalloc - tq_gemm_ws for callers that cannot allocate memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Instead of a caller workspace it uses a scratch array in the
+ * library's own device memory: tq_gemm_noalloc_scratch_bytes() bytes
+ * (16 MiB) per device, held until the process ends.  The call takes the
+ * schedule tq_gemm_ws would take with tq_gemm_workspace_bytes(M, N, K, dt,
+ * path) bytes of workspace, and so gives bit-identical results; when that
+ * schedule needs more than the scratch holds it returns TQ_ERR_SCRATCH with
+ * nothing launched.  It calls no allocating routine.  Every call on a device
+ * shares that device's scratch (the split partials are fully rewritten by
+ * each call, nothing needs clearing): calls that may overlap on one device
+ * (different streams, or threads) race and must be serialized by the
+ * caller; calls in one stream's order are safe.  Other arguments, results
+ * and errors as tq_gemm_ws.
+ */
+tq_status tq_gemm_noalloc(const void* A, tq_dtype dt, int64_t M, int64_t N, int64_t K,
+                          const uint8_t* codes, const uint16_t* scale_f16, const void* bias,
+                          void* C, hipStream_t stream, tq_path path);
+
+/* Bytes of the per-device scratch of tq_gemm_noalloc. */
+size_t tq_gemm_noalloc_scratch_bytes(void);
 
 /*
  * tq_gemm_workspace_bytes - workspace tq_gemm_ws needs for its fastest

@@ -58,9 +58,9 @@ def test_one_hip_runtime_per_process():
 
 
 def test_version_and_status_strings(lib):
-    assert lib.tq_abi_version() == 4
+    assert lib.tq_abi_version() == 5
     src = open(HEADER).read()
-    assert "#define TQ_ABI_VERSION 4" in src
+    assert "#define TQ_ABI_VERSION 5" in src
     for code, name in _lib.STATUS_NAMES.items():
         assert re.search(rf"\b{name}\s*=\s*{code}\b", src), name
         s = lib.tq_status_str(code)
@@ -248,3 +248,19 @@ def test_prepare_host_checks(lib):
     assert name[lib.w4a16_pack(FAKE, 4, 100, 128, FAKE, FAKE, None)] == "TQ_ERR_SHAPE"
     assert name[lib.w4a16_pack(MIS, 4, 128, 128, FAKE, FAKE, None)] == "TQ_ERR_ALIGN"
     assert name[lib.w4a16_unpack(FAKE, FAKE, 4, 128, 64, None, None, None)] == "TQ_ERR_GROUP"
+
+
+def test_noalloc_rejects_schedules_beyond_its_scratch(lib):
+    """tq_gemm_noalloc: a schedule whose split partials exceed the 16 MiB
+    scratch (prefill 2048 x 4096 x 14336: two splits, 64 MiB) returns
+    TQ_ERR_SCRATCH from the host check, before any HIP call; argument errors
+    come first, as in tq_gemm_ws."""
+    assert lib.tq_gemm_noalloc_scratch_bytes() == 16 << 20
+    FAKE = 1 << 20
+    assert _lib.tq_gemm_workspace_bytes(2048, 4096, 14336) > 16 << 20
+    st = lib.tq_gemm_noalloc(FAKE, 0, 2048, 4096, 14336, FAKE, FAKE, None, FAKE, None, 0)
+    assert _lib.STATUS_NAMES[st] == "TQ_ERR_SCRATCH"
+    st = lib.tq_gemm_noalloc(FAKE, 0, 2048, 4096, 14336, None, FAKE, None, FAKE, None, 0)
+    assert _lib.STATUS_NAMES[st] == "TQ_ERR_NULL"
+    st = lib.tq_gemm_noalloc(FAKE, 0, 16, 4096, 4160 + 1, FAKE, FAKE, None, FAKE, None, 0)
+    assert _lib.STATUS_NAMES[st] == "TQ_ERR_SHAPE"
