@@ -46,6 +46,8 @@ SIGNATURES = {
     "w4a16_gemm_asym": (_i32, [_vp, _i32, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp,
                                _i32]),
     "w4a16_gemm_asym_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32, _i64, _i32]),
+    "tq_diag_stream_read": (_i32, [_vp, _sz, _vp, _i64, _vp]),
+    "tq_diag_gemv": (_i32, [_vp, _i32, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _i32]),
     "tq_select_path": (_i32, [_i32, _i64, _i64, _i64, _i32]),
     "tq_status_str": (ctypes.c_char_p, [_i32]),
     "tq_abi_version": (_i32, []),
@@ -351,6 +353,33 @@ def tq_select_path(fmt: str, M: int, N: int, K: int, dtype: str = "f16") -> str:
     f = {"ternary": 0, "w4a16": 1}[fmt]
     d = {"f16": TQ_F16, "bf16": TQ_BF16}[dtype]
     return PATH_NAMES[load().tq_select_path(f, M, N, K, d)]
+
+
+def tq_diag_stream_read(src, blocks: int, sink=None):
+    """Launch the plain streaming read over all of `src` (a contiguous
+    device tensor); returns the sink tensor it may write."""
+    import torch
+    _need_cuda(src)
+    nbytes = src.numel() * src.element_size()
+    if sink is None:
+        sink = torch.empty((blocks,), dtype=torch.int32, device=src.device)
+    _check("tq_diag_stream_read", load().tq_diag_stream_read(_ptr(src), nbytes, _ptr(sink), blocks,
+                                                             _stream(src.device)))
+    return sink
+
+
+def tq_diag_gemv(A, codes, scale, variant: int, out=None):
+    """The M = 1 decode kernel in measurement form (0 as tq_gemm, 1 codes
+    from the cache, 2 codes from the cache without the multiply)."""
+    import torch
+    M, K = _check_activations(A)
+    N = _ternary_layout(codes, scale, K).N
+    _check_out_bias(A, N, None, out)
+    _need_cuda(A, codes, scale, out)
+    C = out if out is not None else torch.empty((M, N), dtype=A.dtype, device=A.device)
+    _check("tq_diag_gemv", load().tq_diag_gemv(_ptr(A), _dtype_enum(A), M, N, K, _ptr(codes), _ptr(scale), None,
+                                               _ptr(C), _stream(A.device), variant))
+    return C
 
 
 def tq_abi_version() -> int:

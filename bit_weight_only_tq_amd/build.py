@@ -27,6 +27,7 @@ SOURCES = {
     "pack.hip": ["-ffp-contract=off"],
     "gemv.hip": [],
     "gemm.hip": [],
+    "diag.hip": [],
     "api.cpp": ["-x", "hip"],
 }
 

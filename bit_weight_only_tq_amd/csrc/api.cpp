@@ -399,4 +399,26 @@ tq_status w4a16_gemm(const void* A, tq_dtype dt, int64_t M, int64_t N, int64_t K
     return w4a16_gemm_ex(A, dt, M, N, K, qweight, scales_f16, group_size, bias, C, stream, TQ_PATH_AUTO);
 }
 
+// ------------------------------------------------------------ measurement
+
+tq_status tq_diag_stream_read(const void* src, size_t bytes, uint32_t* sink, int64_t blocks, hipStream_t stream) {
+    if (!src || !sink) return TQ_ERR_NULL;
+    if (bytes == 0 || bytes % 16 != 0 || blocks <= 0 || (int64_t)(bytes / 16) < blocks) return TQ_ERR_SHAPE;
+    if (!aligned16(src) || (reinterpret_cast<uintptr_t>(sink) & 3u)) return TQ_ERR_ALIGN;
+    return from_hip(tq::launch_stream_read(src, bytes, sink, blocks, stream));
+}
+
+tq_status tq_diag_gemv(const void* A, tq_dtype dt, int64_t M, int64_t N, int64_t K, const uint8_t* codes,
+                       const uint16_t* scale_f16, const void* bias, void* C, hipStream_t stream, int variant) {
+    tq_status r = check_gemm_common(A, dt, M, N, K, codes, scale_f16, C);
+    if (r != TQ_OK) return r;
+    if (K % 64 != 0) return TQ_ERR_SHAPE;
+    if (bias && (reinterpret_cast<uintptr_t>(bias) & 1u)) return TQ_ERR_ALIGN;
+    if (variant < 0 || variant > 2) return TQ_ERR_PATH;
+    tq::GemmArgs a{static_cast<const uint16_t*>(A), dt == TQ_BF16 ? 1 : 0, M, N, K, codes, scale_f16,
+                   static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(C)};
+    const hipError_t e = tq::launch_ternary_gemv_variant(a, variant, stream);
+    return e == hipErrorInvalidValue ? TQ_ERR_PATH : from_hip(e);
+}
+
 }  // extern "C"

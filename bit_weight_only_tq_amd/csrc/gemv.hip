@@ -461,7 +461,13 @@ constexpr float ternary_unit() { return std::is_same<T, F16>::value ? 1.0f : kBf
 // The bias is read from a valid address whether or not one is given, so the
 // load needs no branch (a branch there makes the compiler wait for every
 // outstanding load, codes included, before it).
-template <class T, int R, int CSW, int MT>
+//
+// VAR selects a measurement variant (the dispatcher always runs VAR = 0):
+// 1 reads row-block 0's codes in every workgroup, so the codes come from the
+// cache instead of HBM; 2 does that and also drops the matrix-core step
+// (the unpacked operands are kept alive but not multiplied).  Their outputs
+// are meaningless; they split a call's time into HBM, unpack and MAC parts.
+template <class T, int R, int CSW, int MT, int VAR = 0>
 __global__ __launch_bounds__(1024) void ternary_gemv_m1_kernel(GemmArgs p) {
     extern __shared__ uint4 smem[];
     constexpr int U = CSW / 4;            // 16-column activation units per lane and row
@@ -500,7 +506,8 @@ __global__ __launch_bounds__(1024) void ternary_gemv_m1_kernel(GemmArgs p) {
     const uint16_t* bsrc = p.bias ? p.bias : p.scale;
     const uint16_t sc_bits = p.scale[n_e];
     const uint16_t bi_bits = bsrc[n_e];
-    const uint8_t* cbase = static_cast<const uint8_t*>(p.wq) + n_base * rb + (int64_t)cs0 * 64;
+    const int64_t n_codes = VAR == 0 ? n_base : 0;
+    const uint8_t* cbase = static_cast<const uint8_t*>(p.wq) + n_codes * rb + (int64_t)cs0 * 64;
     const uint32_t lo = (uint32_t)i16 * rb + 16u * (uint32_t)g;
     uint4 q[CSW][R];
 #pragma unroll
@@ -546,7 +553,8 @@ __global__ __launch_bounds__(1024) void ternary_gemv_m1_kernel(GemmArgs p) {
         const uint4 aop = aw[2 * (D) + (I0) / 4];                                                     \
         _Pragma("unroll") for (int r = 0; r < R; ++r) {                                               \
             const uint4 bw = tern_quad<I0>(dword_of(q[s][r], D), magic_v);                            \
-            acc[r] = sm_mma<T>(aop, bw, acc[r]);                                                      \
+            if constexpr (VAR == 2) asm volatile("" :: "v"(bw.x), "v"(bw.y), "v"(bw.z), "v"(bw.w), "v"(aop.x)); \
+            else acc[r] = sm_mma<T>(aop, bw, acc[r]);                                                 \
         }                                                                                             \
     }
         TQ_MFMA_1(0, 0)
@@ -1338,28 +1346,48 @@ static bool gemv_m1_plan(const GemmArgs& a, GemvM1Plan* pl) {
     return pl->lds <= (size_t)kGemvLdsMaxBytes;
 }
 
-template <class T, int R, int CSW, int MT>
+template <class T, int R, int CSW, int MT, int VAR>
 static hipError_t launch_gemv_m1_k(const GemmArgs& a, const GemvM1Plan& pl, hipStream_t s) {
     static DeviceFlags lds_limit_set;
-    hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(&ternary_gemv_m1_kernel<T, R, CSW, MT>),
+    hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(&ternary_gemv_m1_kernel<T, R, CSW, MT, VAR>),
                                    kGemvLdsMaxBytes, lds_limit_set);
     if (e != hipSuccess) return e;
     if (a.N % (16 * R) != 0 || a.K != (int64_t)pl.waves * CSW * 256 || a.M > MT) return hipErrorInvalidValue;
     const dim3 grid((unsigned)(a.N / (16 * R)));
-    ternary_gemv_m1_kernel<T, R, CSW, MT><<<grid, dim3(pl.waves * kWave), pl.lds, s>>>(a);
+    ternary_gemv_m1_kernel<T, R, CSW, MT, VAR><<<grid, dim3(pl.waves * kWave), pl.lds, s>>>(a);
     return hipGetLastError();
 }
 
-template <class T, int R, int CSW>
+template <class T, int R, int CSW, int VAR>
 static hipError_t launch_gemv_m1_t(const GemmArgs& a, const GemvM1Plan& pl, hipStream_t s) {
-    if (pl.mt == 1) return launch_gemv_m1_k<T, R, CSW, 1>(a, pl, s);
-    if (pl.mt == 2) return launch_gemv_m1_k<T, R, CSW, 2>(a, pl, s);
-    return launch_gemv_m1_k<T, R, CSW, 4>(a, pl, s);
+    if (pl.mt == 1) return launch_gemv_m1_k<T, R, CSW, 1, VAR>(a, pl, s);
+    if (VAR != 0) return hipErrorInvalidValue;  // measurement variants: M = 1 only
+    if (pl.mt == 2) return launch_gemv_m1_k<T, R, CSW, 2, 0>(a, pl, s);
+    return launch_gemv_m1_k<T, R, CSW, 4, 0>(a, pl, s);
 }
 
-template <int R, int CSW>
+template <int R, int CSW, int VAR = 0>
 static hipError_t launch_gemv_m1(const GemmArgs& a, const GemvM1Plan& pl, hipStream_t s) {
-    return a.bf16 ? launch_gemv_m1_t<BF16, R, CSW>(a, pl, s) : launch_gemv_m1_t<F16, R, CSW>(a, pl, s);
+    return a.bf16 ? launch_gemv_m1_t<BF16, R, CSW, VAR>(a, pl, s) : launch_gemv_m1_t<F16, R, CSW, VAR>(a, pl, s);
+}
+
+template <int VAR>
+static hipError_t launch_gemv_m1_plan(const GemmArgs& a, const GemvM1Plan& m1, hipStream_t s) {
+    if (m1.csw == 8 && m1.rows16 == 2) return launch_gemv_m1<2, 8, VAR>(a, m1, s);
+    if (m1.csw == 8) return launch_gemv_m1<1, 8, VAR>(a, m1, s);
+    return m1.rows16 == 2 ? launch_gemv_m1<2, 4, VAR>(a, m1, s) : launch_gemv_m1<1, 4, VAR>(a, m1, s);
+}
+
+// Measurement variants of the M = 1 kernel (see ternary_gemv_m1_kernel):
+// variant 0 is the kernel the dispatcher runs, 1 reads cached codes, 2 also
+// skips the matrix-core step.  Shapes the M = 1 kernel does not take fail.
+hipError_t launch_ternary_gemv_variant(const GemmArgs& a, int variant, hipStream_t s) {
+    GemvM1Plan m1;
+    if (a.M != 1 || !gemv_m1_plan(a, &m1)) return hipErrorInvalidValue;
+    if (variant == 0) return launch_gemv_m1_plan<0>(a, m1, s);
+    if (variant == 1) return launch_gemv_m1_plan<1>(a, m1, s);
+    if (variant == 2) return launch_gemv_m1_plan<2>(a, m1, s);
+    return hipErrorInvalidValue;
 }
 
 // Streaming kernel: fp16, 3 <= M <= 16, at most 32 chunk-sets (8192
@@ -1517,11 +1545,7 @@ hipError_t launch_ternary_gemv(const GemmArgs& a, hipStream_t s) { return launch
 
 hipError_t launch_ternary_gemv(const GemmArgs& a, void* workspace, size_t workspace_bytes, hipStream_t s) {
     GemvM1Plan m1;
-    if (gemv_m1_plan(a, &m1)) {
-        if (m1.csw == 8 && m1.rows16 == 2) return launch_gemv_m1<2, 8>(a, m1, s);
-        if (m1.csw == 8) return launch_gemv_m1<1, 8>(a, m1, s);
-        return m1.rows16 == 2 ? launch_gemv_m1<2, 4>(a, m1, s) : launch_gemv_m1<1, 4>(a, m1, s);
-    }
+    if (gemv_m1_plan(a, &m1)) return launch_gemv_m1_plan<0>(a, m1, s);
     StreamPlan sp;
     if (gemv_stream_plan(a, workspace ? workspace_bytes : 0, &sp))
         return launch_gemv_stream_t(SplitArgs{a, static_cast<float*>(workspace), sp.S}, sp, s);

@@ -84,6 +84,14 @@ hipError_t launch_ternary_gemv(const GemmArgs& a, void* workspace, size_t worksp
 hipError_t launch_ternary_gemv(const GemmArgs& a, hipStream_t s);         // picks the fastest eligible kernel
 hipError_t launch_ternary_gemv_simple(const GemmArgs& a, hipStream_t s);  // any dtype, any K % 64 == 0
 bool ternary_gemv_mfma_ok(const GemmArgs& a);                             // fp16, K % 256 == 0
+// Measurement variants of the M = 1 kernel: 0 as dispatched, 1 codes read
+// from the cache (every workgroup reads row-block 0), 2 as 1 without the
+// matrix-core step.  hipErrorInvalidValue where the M = 1 kernel does not run.
+hipError_t launch_ternary_gemv_variant(const GemmArgs& a, int variant, hipStream_t s);
+// diag.hip: a plain streaming read of `bytes` (a multiple of 16) by `blocks`
+// workgroups; sink[b] (blocks entries) is written only if workgroup b's
+// XOR of the data equals an improbable value.
+hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, int64_t blocks, hipStream_t s);
 // W4A16 small M: with a workspace of w4_gemv_workspace_bytes() the streaming
 // kernel may split K; without one it never does.
 size_t w4_gemv_workspace_bytes(const GemmArgs& a);

@@ -337,6 +337,37 @@ tq_status w4a16_gemm_asym(const void* A, tq_dtype dt, int64_t M, int64_t N, int6
 size_t w4a16_gemm_asym_workspace_bytes(int64_t M, int64_t N, int64_t K, tq_dtype dt, int64_t group_size,
                                        int with_perm);
 
+/* ----------------------------------------------------------- measurement
+ *
+ * Instruments for the benchmark, not part of the layer: they measure the
+ * device, not compute a result.
+ */
+
+/*
+ * tq_diag_stream_read - a plain streaming read of `bytes` bytes at `src`
+ * (device, 16-byte aligned, bytes a positive multiple of 16) by at most
+ * `blocks` workgroups of 256 lanes, each reading a contiguous share.  The
+ * data are folded with XOR and nothing is stored unless a workgroup's fold
+ * equals an improbable value; `sink` (device, at least `blocks` uint32)
+ * takes those stores.  This is the HBM read ceiling one launch of that size
+ * reaches.  Asynchronous.  TQ_ERR_SHAPE if blocks exceeds bytes / 16.
+ */
+tq_status tq_diag_stream_read(const void* src, size_t bytes, uint32_t* sink, int64_t blocks, hipStream_t stream);
+
+/*
+ * tq_diag_gemv - the M = 1 decode kernel of tq_gemm in a measurement form
+ * (page "Ternary quantized models in vLLM ...", section 5.7: attributing
+ * kernel time to unpacking).  variant 0 runs the kernel tq_gemm runs (same
+ * result); 1 makes every workgroup read the codes of rows 0..15, so the
+ * codes come from the cache, not HBM; 2 is 1 without the matrix-core
+ * multiply (codes are loaded and unpacked only).  Outputs of variants 1 and
+ * 2 are unspecified (C is still written, in bounds).  Arguments as tq_gemm;
+ * TQ_ERR_PATH if M != 1 or the M = 1 kernel does not take the shape.
+ */
+tq_status tq_diag_gemv(const void* A, tq_dtype dt, int64_t M, int64_t N, int64_t K,
+                       const uint8_t* codes, const uint16_t* scale_f16, const void* bias,
+                       void* C, hipStream_t stream, int variant);
+
 /* ------------------------------------------------------------------ misc */
 
 /*

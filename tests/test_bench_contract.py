@@ -33,3 +33,26 @@ def test_algorithmic_bytes():
     import bench
     # codes N*K/4 + fp16 scales + fp16 activations + fp16 outputs
     assert bench.ternary_bytes(1, 4096, 4096) == 4096 * 1024 + 2 * 4096 + 2 * 4096 + 2 * 4096
+
+
+def test_sample_verdicts():
+    """The CPU leg's parity check: an output equal to the oracle's product
+    rounded to fp16 passes, one pushed past the bound fails, per line."""
+    import numpy as np
+    sys.path.insert(0, ROOT)
+    import bench
+    import oracle.gemm as OG
+    import oracle.ternary as OT
+    import synth
+    W = synth.weights(32, 256, 5)
+    codes, sb = OT.ternary_pack(W)
+    A = synth.activations(2, 256, 6).double().numpy()
+    out, mag = OG.gemm_ref64(A, OT.ternary_dequant(codes, sb, 256))
+    good = out.astype(np.float16).astype(np.float64)
+    bad = good.copy()
+    bad[1, 3] += 2e-3 * mag[1, 3] + 2e-3
+    smp = lambda line, C: {"line": line, "kind": "ternary", "K": 256, "dtype": "f16", "codes": codes,  # noqa: E731
+                            "scale": sb, "A": A, "C": C}
+    v = bench.check_samples([smp("a", good), smp("b", bad), smp("a", good)])
+    assert v["lines"]["a"]["ok"] and v["lines"]["a"]["outputs"] == 2 * 2 * 32
+    assert not v["lines"]["b"]["ok"] and not v["ok"]

@@ -542,14 +542,14 @@ def test_ternary_small_m_one_hot_and_bias(N, K, M, dt):
 @pytest.mark.parametrize("M,N,K", [(5, 4096, 4096), (16, 28672, 4096), (9, 4096, 14336), (16, 1000, 4160)])
 def test_bf16_decode_m_auto(M, N, K):
     """bf16 at M = 5..16 through the dispatcher: the streaming kernel's bf16
-    form (K split with the queried workspace on long K), or the per-lane
-    kernel where K % 256 != 0; every output against the oracle, with a bias;
+    form (K split with the queried workspace on long K), or the medium path's
+    tiles where K % 256 != 0; every output against the oracle, with a bias;
     the rows past M untouched."""
     import torch
     import bit_weight_only_tq_amd as tq
     dev = require_gpu()
     log(f"bf16 decode-size M auto M={M} N={N} K={K}")
-    assert tq.tq_select_path("ternary", M, N, K, "bf16") == "gemv"
+    assert tq.tq_select_path("ternary", M, N, K, "bf16") == ("gemv" if K % 256 == 0 else "stream_mfma")
     codes, scale, rc, rs, wdq = _ternary(N, K, dev)
     A = synth.activations(M, K, synth.seed_for("bfm", M, N, K), "bf16")
     bias = synth.activations(1, N, synth.seed_for("bfmb", N, K), "bf16")[0]
