@@ -125,7 +125,12 @@ tq_path tq_select_path(int format, int64_t M, int64_t N, int64_t K, tq_dtype dt)
     // medium path's matrix-core tiles (any K % 64 == 0) are faster.
     if (format == 0 && M >= 3 && M <= kGemvMaxM && K % 256 != 0) return TQ_PATH_STREAM_MFMA;
     if (M <= kGemvMaxM) return TQ_PATH_GEMV;
-    if (format == 1) return TQ_PATH_GEMV;  // W4A16: small-M kernel over blocks of rows
+    if (format == 1) {
+        // W4A16: the prefill GEMM from 256 rows where it takes the shape (at
+        // most 128 groups), else the small-M kernels over blocks of 16 rows
+        const tq::GemmArgs a{nullptr, dt == TQ_BF16 ? 1 : 0, M, N, K, nullptr, nullptr, nullptr, nullptr};
+        return (M >= kMediumMaxM && tq::w4_prefill_ok(a)) ? TQ_PATH_GEMM : TQ_PATH_GEMV;
+    }
     if (M < kMediumMaxM) return TQ_PATH_STREAM_MFMA;
     return TQ_PATH_GEMM;
 }
@@ -280,6 +285,9 @@ tq_status w4a16_gemm_ws(const void* A, tq_dtype dt, int64_t M, int64_t N, int64_
         case TQ_PATH_GEMV:
             if (M > kGemvMaxM) return from_hip(tq::launch_w4_gemm(a, workspace, wsb, stream));
             return from_hip(tq::launch_w4_gemv(a, workspace, wsb, stream));
+        case TQ_PATH_GEMM:
+            if (!tq::w4_prefill_ok(a)) return TQ_ERR_PATH;
+            return from_hip(tq::launch_w4_prefill(a, stream));
         default:
             return TQ_ERR_PATH;
     }
@@ -287,6 +295,7 @@ tq_status w4a16_gemm_ws(const void* A, tq_dtype dt, int64_t M, int64_t N, int64_
 
 size_t w4a16_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, tq_dtype dt, int64_t group_size) {
     if (M <= 0 || N <= 0 || K <= 0 || K % 128 != 0 || group_size != 128) return 0;
+    if (tq_select_path(1, M, N, K, dt) == TQ_PATH_GEMM) return 0;  // the prefill kernel needs none
     const tq::GemmArgs a{nullptr, dt == TQ_BF16 ? 1 : 0, M < kGemvMaxM ? M : kGemvMaxM, N, K,
                          nullptr, nullptr, nullptr, nullptr};
     size_t b = tq::w4_gemv_workspace_bytes(a);
@@ -374,7 +383,11 @@ tq_status w4a16_gemm_asym(const void* A, tq_dtype dt, int64_t M, int64_t N, int6
     if (perm && (reinterpret_cast<uintptr_t>(perm) & 3u)) return TQ_ERR_ALIGN;
     if (workspace && !aligned16(workspace)) return TQ_ERR_ALIGN;
     if (path == TQ_PATH_AUTO) path = tq_select_path(1, M, N, K, dt);
-    if (path != TQ_PATH_GEMV) return TQ_ERR_PATH;
+    if (path != TQ_PATH_GEMV && path != TQ_PATH_GEMM) return TQ_ERR_PATH;
+    {
+        const tq::GemmArgs probe{nullptr, dt == TQ_BF16 ? 1 : 0, M, N, K, nullptr, nullptr, nullptr, nullptr};
+        if (path == TQ_PATH_GEMM && !tq::w4_prefill_ok(probe)) return TQ_ERR_PATH;
+    }
     const uint16_t* a_eff = static_cast<const uint16_t*>(A);
     uint8_t* ws = static_cast<uint8_t*>(workspace);
     size_t wsb = workspace ? workspace_bytes : 0;
@@ -390,6 +403,7 @@ tq_status w4a16_gemm_asym(const void* A, tq_dtype dt, int64_t M, int64_t N, int6
     tq::GemmArgs a{a_eff, dt == TQ_BF16 ? 1 : 0, M, N, K, qweight, scales_f16,
                    static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(C), zeros};
     void* rest = wsb ? ws : nullptr;
+    if (path == TQ_PATH_GEMM) return from_hip(tq::launch_w4_prefill(a, stream));
     if (M > kGemvMaxM) return from_hip(tq::launch_w4_gemm(a, rest, wsb, stream));
     return from_hip(tq::launch_w4_gemv(a, rest, wsb, stream));
 }

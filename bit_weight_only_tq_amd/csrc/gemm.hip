@@ -251,7 +251,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(SplitArgs sa) {
         sc[j] = f16_bits_to_f32(p.scale[nc]) * Mfma<T>::kUnit;
         bi[j] = p.bias ? T::to_f32(p.bias[nc]) : 0.0f;
     }
-    const bool vec_ok = ((N | ldc) % 8) == 0;
+    const bool vec_ok = ((N | ldc) % 8) == 0 && (reinterpret_cast<uintptr_t>(p.C) & 15u) == 0;
 #pragma unroll
     for (int slab = 0; slab < TM / 2; ++slab) {
 #pragma unroll
@@ -681,6 +681,253 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(SplitArgs sa) {
 }  // namespace mm3
 
 
+// ------------------------------------------------------------------------
+// W4A16 at large M (prefill): the DMA ring of v3 with int4 codes.
+//
+// C[m, n] = sum_g s[n, g] * sum_{k in g} A[m, k] (q[n, k] - z[n, g]) (+ bias)
+// (page "Model quantization - vLLM runtime quantization architecture",
+// section 5: INT4 weights, fp16 group scales of 128 columns, and a GEMM
+// kernel consuming them; page "10.6 Quantization choice ...", section
+// 10.6.1: prefill is the compute-bound GEMM regime).
+//
+// Block tile 256 x 128, K-step 64 (half a group), eight waves (2 x 4) of
+// 128 x 32 outputs (8 x 2 tiles of v_mfma_f32_16x16x32).  Per stage the ring
+// holds 256 activation rows x 64 columns (natural order, 16-byte chunks
+// XOR-swizzled as in v3) and 128 weight rows x 32 bytes of codes (8 words).
+// A code word holds 8 consecutive columns, one MFMA operand: byte d of the
+// word is moved to both halves of a dword (v_perm), its two nibbles masked
+// into the mantissa of 1024 (1024 + q, 1024 + 16 q), and one packed fma by
+// (1, 1/16) with -(1024 + z, 64 + z) leaves (q_2d - z, q_2d+1 - z) exactly -
+// natural order, so the activations need no pairing.  bf16 activations take
+// the same exact integers converted to bf16.  The MFMAs of a group run into
+// group accumulators that start from zero; at the group's end each is
+// scaled by s[n, g] (fp32) into the output accumulators, so every product is
+// exact and the scale is applied once per group, as the format defines.
+// The block's scales (and zero points) are copied to LDS once, before the
+// K loop, so the loop's only global traffic is the DMA whose per-wave counts
+// the stage waits rely on; that bounds K at 128 groups (16384 columns).
+namespace w4p {
+
+constexpr int BM = 256;
+constexpr int BN = 128;
+constexpr int BK = 64;
+constexpr int kThreads = 512;
+constexpr int WM = 128, WN = 32;
+constexpr int TM = WM / 16, TN = WN / 16;
+constexpr int AU = BM / 64;                 // 1-KB activation DMA blocks per wave and stage
+constexpr int kStages = 3;
+constexpr int kABytes = BM * BK * 2;        // 32 KB
+constexpr int kBBytes = BN * BK / 2;        // 4 KB: 128 rows x 32 bytes
+constexpr int kStageBytes = kABytes + kBBytes;
+constexpr int kRingBytes = kStages * kStageBytes;
+constexpr int kMaxGroups = 128;
+constexpr int kEpiLd = WN + 8;              // epilogue staging row (halves)
+constexpr int kEpiBytesPerWave = 32 * kEpiLd * 2;
+static_assert(8 * kEpiBytesPerWave <= kRingBytes, "epilogue staging must fit in the ring");
+
+__host__ __device__ constexpr size_t lds_bytes(int64_t G, bool asym) {
+    return (size_t)kRingBytes + (size_t)BN * G * 2 + (asym ? (size_t)BN * G : 0);
+}
+
+// (q_2d - z, q_2d+1 - z) of code word x as exact fp16, natural order.
+template <int D>
+__device__ __forceinline__ uint32_t nat_w4_pair(uint32_t x, uint32_t mask_v, uint32_t magic_v, f16x2 mul, f16x2 add) {
+    const uint32_t y = __builtin_amdgcn_perm(x, x, 0x0C000C00u | (uint32_t)D | ((uint32_t)D << 16));
+    const f16x2 v = __builtin_bit_cast(f16x2, (y & mask_v) | magic_v);
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(v, mul, add));
+}
+
+template <class T>
+__device__ __forceinline__ uint4 nat_w4_quad(uint32_t x, uint32_t mask_v, uint32_t magic_v, f16x2 mul, f16x2 add) {
+    const uint4 h = make_uint4(nat_w4_pair<0>(x, mask_v, magic_v, mul, add), nat_w4_pair<1>(x, mask_v, magic_v, mul, add),
+                               nat_w4_pair<2>(x, mask_v, magic_v, mul, add), nat_w4_pair<3>(x, mask_v, magic_v, mul, add));
+    if constexpr (std::is_same<T, F16>::value) return h;
+    else return make_uint4(f16x2_to_bf16x2(h.x), f16x2_to_bf16x2(h.y), f16x2_to_bf16x2(h.z), f16x2_to_bf16x2(h.w));
+}
+
+// -(1024 + z) in the low half, -(64 + z) in the high half
+__device__ __forceinline__ f16x2 w4_nat_sub(uint32_t z) {
+    return __builtin_bit_cast(f16x2, (0xE400u + z) | ((0xD400u + 16u * z) << 16));
+}
+
+template <class T, bool ASYM>
+__global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
+    typedef typename Mfma<T>::vec vec;
+    extern __shared__ uint4 smem_w4p[];
+    uint8_t* lds = reinterpret_cast<uint8_t*>(smem_w4p);
+    const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)smem_w4p;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 2, wn = wave & 3;
+    const int g = lane >> 4;
+    const int i16 = lane & 15;
+    const int64_t m0 = (int64_t)blockIdx.y * BM;
+    const int64_t n0 = (int64_t)blockIdx.x * BN;
+    const int64_t M = p.M, N = p.N, K = p.K;
+    const int G = (int)(K / 128);
+    const int64_t rowb = K / 2;  // code bytes per weight row
+    uint16_t* sc_lds = reinterpret_cast<uint16_t*>(lds + kRingBytes);   // [BN][G]
+    uint8_t* zp_lds = lds + kRingBytes + (size_t)BN * G * 2;             // [BN][G]
+
+    // the block's group scales (and zero points) -> LDS; rows past N re-read row N-1
+    for (int e = tid; e < BN * G; e += kThreads) {
+        const int r = e / G, gi = e - r * G;
+        const int64_t n = n0 + r < N ? n0 + r : N - 1;
+        sc_lds[e] = p.scale[n * G + gi];
+        if constexpr (ASYM) zp_lds[e] = p.zeros[n * G + gi];
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+    // Activation DMA: as v3, wave w fills 1-KB blocks AU w .. AU w + AU-1 of a
+    // stage (8 rows each), lane l at chunk l % 8 of row l / 8, fetching global
+    // chunk (l % 8) ^ (l / 8).  Rows past M re-read row M-1.
+    const uint16_t* a_blk = p.A + m0 * K;
+    uint32_t a_off[AU];
+#pragma unroll
+    for (int u = 0; u < AU; ++u) {
+        int64_t r = 8 * (AU * wave + u) + (lane >> 3);
+        if (m0 + r >= M) r = M - 1 - m0;
+        a_off[u] = (uint32_t)(r * K + 8 * ((lane & 7) ^ (lane >> 3)));
+    }
+    // Code DMA (waves 0..3, 256 lanes): lane L = 64 w + l fetches bytes
+    // 16 (L % 2) .. +15 of the K-step's 32 bytes of weight row n0 + L / 2,
+    // landing at 32 (L / 2) + 16 (L % 2).  Rows past N re-read row N-1.
+    const uint8_t* b_blk = static_cast<const uint8_t*>(p.wq);
+    const bool b_issuer = wave < 4;
+    int64_t b_off;
+    {
+        const int L = 64 * (wave & 3) + lane;
+        const int64_t n = n0 + (L >> 1) < N ? n0 + (L >> 1) : N - 1;
+        b_off = n * rowb + 16 * (L & 1);
+    }
+    auto issue = [&](int kstep, int stage) {
+        const int64_t k0 = (int64_t)kstep * BK;
+        const uint32_t dst = lds_base + (uint32_t)(stage * kStageBytes + 1024 * AU * wave);
+#pragma unroll
+        for (int u = 0; u < AU; ++u) dma16(a_blk + k0 + a_off[u], dst + 1024u * u);
+        if (b_issuer) dma16(b_blk + b_off + k0 / 2, lds_base + (uint32_t)(stage * kStageBytes + kABytes + 1024 * wave));
+    };
+    auto wait_prev_stage = [&]() {
+        if (b_issuer) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(AU + 1) : "memory");
+        else asm volatile("s_waitcnt vmcnt(%0)" :: "n"(AU) : "memory");
+    };
+
+    f32x4 acc[TM][TN], accg[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            accg[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    const int frag_base = (wm * WM + i16) * (BK * 2);
+    const int swz = i16 & 7;
+    int nloc[TN];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) nloc[j] = wn * WN + 16 * j + i16;
+    const uint32_t magic_v = vgpr_const<kMagic2>();
+    const uint32_t mask_v = sgpr_const<0x00F0000Fu>();
+    const f16x2 mul = __builtin_bit_cast(f16x2, 0x2C003C00u);  // (1, 1/16)
+    f16x2 add[TN];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) add[j] = w4_nat_sub(8u);
+
+    const int nk = (int)(K / BK);  // even: K % 128 == 0
+    issue(0, 0);
+    issue(nk > 1 ? 1 : 0, 1);
+    wait_prev_stage();
+    __syncthreads();  // the scales in LDS and stage 0, for every wave
+    for (int kt = 0; kt < nk; ++kt) {
+        const int stage = kt % kStages;
+        issue(kt + 2 < nk ? kt + 2 : nk - 1, (kt + 2) % kStages);
+        const int gi = kt >> 1;
+        if constexpr (ASYM) {
+            if ((kt & 1) == 0) {
+#pragma unroll
+                for (int j = 0; j < TN; ++j) add[j] = w4_nat_sub(zp_lds[nloc[j] * G + gi]);
+            }
+        }
+        const uint8_t* sbase = lds + stage * kStageBytes;
+        uint2 bw[TN];
+#pragma unroll
+        for (int j = 0; j < TN; ++j) bw[j] = *reinterpret_cast<const uint2*>(sbase + kABytes + nloc[j] * 32 + 8 * g);
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const int chunk = (2 * g + s) ^ swz;
+            vec af[TM];
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+                af[i] = __builtin_bit_cast(vec, *reinterpret_cast<const uint4*>(sbase + frag_base + i * 16 * (BK * 2) + 16 * chunk));
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const vec bf = __builtin_bit_cast(vec, nat_w4_quad<T>(s ? bw[j].y : bw[j].x, mask_v, magic_v, mul, add[j]));
+#pragma unroll
+                for (int i = 0; i < TM; ++i) accg[i][j] = Mfma<T>::mma(af[i], bf, accg[i][j]);
+            }
+        }
+        if (kt & 1) {  // end of group gi: scale into the outputs
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const float sc = f16_bits_to_f32(sc_lds[nloc[j] * G + gi]);
+#pragma unroll
+                for (int i = 0; i < TM; ++i) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) acc[i][j][r] = fmaf(sc, accg[i][j][r], acc[i][j][r]);
+                    accg[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+                }
+            }
+        }
+        wait_prev_stage();  // stage kt + 1 has landed
+        stage_barrier();    // ... for every wave, and nobody reads stage kt any more
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();        // the ring is idle from here on
+
+    // epilogue: per wave, slabs of 32 rows x 32 columns through a private LDS area
+    uint16_t* stg = reinterpret_cast<uint16_t*>(lds + wave * kEpiBytesPerWave);
+    float bi[TN];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+        const int64_t n = n0 + nloc[j];
+        bi[j] = p.bias ? T::to_f32(p.bias[n < N ? n : N - 1]) : 0.0f;
+    }
+    const bool vec_ok = (N % 8) == 0 && (reinterpret_cast<uintptr_t>(p.C) & 15u) == 0;
+#pragma unroll
+    for (int slab = 0; slab < TM / 2; ++slab) {
+#pragma unroll
+        for (int ii = 0; ii < 2; ++ii) {
+            const int i = 2 * slab + ii;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 16 * ii + 4 * g + r;
+#pragma unroll
+                for (int j = 0; j < TN; ++j) stg[row * kEpiLd + 16 * j + i16] = T::from_f32_fast(acc[i][j][r] + bi[j]);
+            }
+        }
+        // each lane stores 16 contiguous bytes: row lane/4 + 16q, columns 8 (lane % 4) .. +7
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int row = (lane >> 2) + 16 * q;
+            const int col = 8 * (lane & 3);
+            const int64_t m = m0 + wm * WM + 32 * slab + row;
+            const int64_t n = n0 + wn * WN + col;
+            if (m >= M) continue;
+            const uint4 v = *reinterpret_cast<const uint4*>(stg + row * kEpiLd + col);
+            if (vec_ok && n + 8 <= N) {
+                *reinterpret_cast<uint4*>(p.C + m * N + n) = v;
+            } else {
+                const uint16_t h[8] = {(uint16_t)v.x, (uint16_t)(v.x >> 16), (uint16_t)v.y, (uint16_t)(v.y >> 16),
+                                       (uint16_t)v.z, (uint16_t)(v.z >> 16), (uint16_t)v.w, (uint16_t)(v.w >> 16)};
+                for (int e = 0; e < 8; ++e)
+                    if (n + e < N) p.C[m * N + n + e] = h[e];
+            }
+        }
+    }
+}
+
+}  // namespace w4p
+
 }  // namespace
 
 hipError_t launch_splitk_reduce(const SplitArgs& sa, hipStream_t s) {
@@ -861,7 +1108,29 @@ hipError_t launch_ternary_medium_split(const SplitArgs& sa, hipStream_t s) {
     return small ? launch_mm<F16, 2>(sa, s) : launch_mm<F16, 4>(sa, s);
 }
 
-// W4A16 at large M: run the small-M kernels on successive blocks of 16
+template <class T, bool ASYM>
+static hipError_t launch_w4p(const GemmArgs& a, hipStream_t s) {
+    static DeviceFlags lds_limit_set;
+    const int64_t G = a.K / 128;
+    hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(&w4p::gemm_kernel<T, ASYM>),
+                                   (int)w4p::lds_bytes(w4p::kMaxGroups, ASYM), lds_limit_set);
+    if (e != hipSuccess) return e;
+    if (G < 1 || G > w4p::kMaxGroups || a.K % 128 != 0) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)((a.N + w4p::BN - 1) / w4p::BN), (unsigned)((a.M + w4p::BM - 1) / w4p::BM));
+    w4p::gemm_kernel<T, ASYM><<<grid, w4p::kThreads, w4p::lds_bytes(G, ASYM), s>>>(a);
+    return hipGetLastError();
+}
+
+bool w4_prefill_ok(const GemmArgs& a) { return a.K % 128 == 0 && a.K / 128 <= w4p::kMaxGroups; }
+
+hipError_t launch_w4_prefill(const GemmArgs& a, hipStream_t s) {
+    if (!w4_prefill_ok(a)) return hipErrorInvalidValue;
+    if (a.zeros) return a.bf16 ? launch_w4p<BF16, true>(a, s) : launch_w4p<F16, true>(a, s);
+    return a.bf16 ? launch_w4p<BF16, false>(a, s) : launch_w4p<F16, false>(a, s);
+}
+
+// W4A16 at large M where the prefill kernel does not take the shape (more
+// than 128 groups): the small-M kernels on successive blocks of 16
 // activation rows (weights are re-read once per block).
 hipError_t launch_w4_gemm(const GemmArgs& a, void* workspace, size_t workspace_bytes, hipStream_t s) {
     for (int64_t m = 0; m < a.M; m += kGemvMaxM) {

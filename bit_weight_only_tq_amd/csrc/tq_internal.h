@@ -116,5 +116,8 @@ hipError_t launch_ternary_medium_split(const SplitArgs& sa, hipStream_t s);  // 
 // Compute units of the current device (cached per device ordinal).
 int compute_units();
 hipError_t launch_w4_gemm(const GemmArgs& a, void* workspace, size_t workspace_bytes, hipStream_t s);
+// gemm.hip: W4A16 prefill GEMM (any M, K % 128 == 0, at most 128 groups).
+bool w4_prefill_ok(const GemmArgs& a);
+hipError_t launch_w4_prefill(const GemmArgs& a, hipStream_t s);
 
 }  // namespace tq

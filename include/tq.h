@@ -231,7 +231,9 @@ size_t tq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, tq_dtype dt, tq_
  *   w4a16_pack; group_size must be 128; K % 128 == 0.
  * C[m, n] = sum_g s[n, g] * sum_{k in g} A[m, k] * (q[n, k] - 8) + bias[n]:
  * the group scale multiplies each group's fp32 partial sum.  Other arguments
- * as tq_gemm.  Asynchronous; allocates nothing; graph-capturable.
+ * as tq_gemm.  From M = 256 (or with TQ_PATH_GEMM) a prefill GEMM runs on the
+ * matrix cores when K / 128 <= 128; other shapes run the decode kernels over
+ * blocks of 16 rows.  Asynchronous; allocates nothing; graph-capturable.
  */
 tq_status w4a16_gemm(const void* A, tq_dtype dt, int64_t M, int64_t N, int64_t K,
                      const int32_t* qweight, const uint16_t* scales_f16, int64_t group_size,
@@ -320,7 +322,8 @@ tq_status w4a16_unpack_asym(const int32_t* qweight, const uint16_t* scales_f16, 
  *          otherwise).  perm must be the array the pack wrote; any other
  *          contents give unspecified results (indices are clamped into
  *          [0, K), so memory stays in bounds).
- *   path   TQ_PATH_AUTO or TQ_PATH_GEMV (TQ_ERR_PATH otherwise).
+ *   path   TQ_PATH_AUTO, TQ_PATH_GEMV or TQ_PATH_GEMM (the prefill GEMM; needs
+ *          K / 128 <= 128; TQ_ERR_PATH otherwise).
  * The rest of the workspace serves the split-K schedule of w4a16_gemm_ws.
  * Asynchronous; allocates nothing; graph-capturable.
  */
@@ -376,8 +379,9 @@ tq_status tq_diag_gemv(const void* A, tq_dtype dt, int64_t M, int64_t N, int64_t
  *   weights (they dominate the bytes moved); prefill-sized M (>= 256) is a
  *   dense contraction for the matrix cores (the decode / prefill split of
  *   the quantization decision tree on page "10.6 Quantization choice and vLLM
- *   in practice", section 10.6.1); ternary M in 17 .. 255 takes the medium
- *   path, 64-row tiles with K split across workgroups.
+ *   in practice", section 10.6.1; W4A16 when K / 128 <= 128); ternary M in
+ *   17 .. 255, and ternary M in 3 .. 16 with K % 256 != 0, take the medium
+ *   path, 32- or 64-row tiles with K split across workgroups.
  */
 tq_path tq_select_path(int format, int64_t M, int64_t N, int64_t K, tq_dtype dt);
 

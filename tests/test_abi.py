@@ -78,6 +78,9 @@ def test_dispatcher_by_m():
         assert sel("w4a16", M, 8192, 8192) == "gemv"
     for M in (256, 2048, 4096, 8192):
         assert sel("ternary", M, 14336, 4096, "bf16") == "gemm"
+        assert sel("w4a16", M, 14336, 4096, "bf16") == "gemm"
+        assert sel("w4a16", M, 4096, 16384) == "gemm"
+        assert sel("w4a16", M, 4096, 16384 + 128) == "gemv"  # past 128 groups: decode kernels over row blocks
     # bf16 follows the same split (its decode kernels match fp16's)
     for M in (1, 4, 5, 16):
         assert sel("ternary", M, 4096, 4096, "bf16") == "gemv"
