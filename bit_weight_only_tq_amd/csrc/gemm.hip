@@ -53,10 +53,15 @@ __device__ __forceinline__ uint4 nat_quad(uint32_t y, uint32_t mask3, uint32_t m
                       nat_pair(y, 3, mask3, magic_v));
 }
 
-// Bare workgroup barrier: __syncthreads() would add a release fence that
-// waits for every outstanding DMA, including the stage issued ahead.
+// Workgroup barrier without a release fence: __syncthreads() would wait for
+// every outstanding DMA, including the stages issued ahead.  LDS reads and
+// writes issued before it are waited for here (the hardware barrier does not
+// wait for them, and the compiler may place register-only work, with the
+// waits that feed it, after the barrier): a slot read before the barrier may
+// be refilled by another wave's DMA right after it, and pairs written before
+// it are read by other waves after it.
 __device__ __forceinline__ void stage_barrier() {
-    asm volatile("" ::: "memory");
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
 }
