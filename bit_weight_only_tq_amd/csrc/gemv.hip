@@ -1858,23 +1858,50 @@ hipError_t launch_w4_gemv(const GemmArgs& a, void* workspace, size_t workspace_b
     return launch_w4_gemv_simple(a, s);
 }
 
-// A_perm[m, i] = A[m, perm[i]]: one thread per element (the index is clamped
-// into [0, K), so any perm contents stay in bounds).
+// A_perm[m, i] = A[m, perm[i]], the index clamped into [0, K) (an index out
+// of range takes column i), so any perm contents stay in bounds.  K % 8 == 0
+// and a 16-byte aligned output.  Thread t of block (x, y) owns columns
+// 8c .. 8c+7, c = 256 x + t: it loads their eight indices once and gathers
+// them from rows y R, y R + gridDim.y R, ... (R consecutive rows each: 1
+// while M is small, so that the grid still has M blocks per 2048 columns),
+// storing each row's eight values as one 16-byte write.  A row of A is at
+// most a few tens of KB, so the scattered 2-byte reads of a row hit the
+// cache after the first.
+
 __global__ __launch_bounds__(256) void gather_columns_kernel(const uint16_t* __restrict__ A,
                                                              const int32_t* __restrict__ perm, int64_t M,
-                                                             int64_t K, uint16_t* __restrict__ out) {
-    const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (e >= M * K) return;
-    const int64_t m = e / K, i = e % K;
-    int64_t k = perm[i];
-    k = k < 0 || k >= K ? i : k;
-    out[e] = A[m * K + k];
+                                                             int64_t K, int R, uint16_t* __restrict__ out) {
+    const int64_t c0 = 8 * ((int64_t)blockIdx.x * 256 + threadIdx.x);
+    if (c0 >= K) return;
+    int64_t k[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int64_t v = perm[c0 + j];
+        k[j] = v < 0 || v >= K ? c0 + j : v;
+    }
+    for (int64_t m0 = (int64_t)blockIdx.y * R; m0 < M; m0 += (int64_t)gridDim.y * R) {
+        for (int r = 0; r < R; ++r) {
+            const int64_t m = m0 + r;
+            if (m >= M) break;
+            const uint16_t* src = A + m * K;
+            uint16_t v[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[j] = src[k[j]];
+            *reinterpret_cast<uint4*>(out + m * K + c0) =
+                make_uint4(v[0] | ((uint32_t)v[1] << 16), v[2] | ((uint32_t)v[3] << 16), v[4] | ((uint32_t)v[5] << 16),
+                           v[6] | ((uint32_t)v[7] << 16));
+        }
+    }
 }
 
 hipError_t launch_gather_columns(const uint16_t* A, const int32_t* perm, int64_t M, int64_t K, uint16_t* out,
                                  hipStream_t s) {
-    const int64_t n = M * K;
-    gather_columns_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(A, perm, M, K, out);
+    if (K % 8 != 0 || (reinterpret_cast<uintptr_t>(out) & 15u) != 0) return hipErrorInvalidValue;
+    if (M <= 0 || K <= 0) return hipSuccess;
+    const int R = M <= 64 ? 1 : 8;
+    const int64_t gy = (M + R - 1) / R;
+    const dim3 grid((unsigned)((K / 8 + 255) / 256), (unsigned)(gy < 65535 ? gy : 65535));
+    gather_columns_kernel<<<grid, 256, 0, s>>>(A, perm, M, K, R, out);
     return hipGetLastError();
 }
 
