@@ -705,9 +705,11 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(SplitArgs sa) {
 // (1, 1/16) with -(1024 + z, 64 + z) leaves (q_2d - z, q_2d+1 - z) exactly -
 // natural order, so the activations need no pairing.  bf16 activations take
 // the same exact integers converted to bf16.  The MFMAs of a group run into
-// group accumulators that start from zero; at the group's end each is
-// scaled by s[n, g] (fp32) into the output accumulators, so every product is
-// exact and the scale is applied once per group, as the format defines.
+// group accumulators whose first MFMA takes zero as its accumulator input
+// (no reset instructions; the loop walks a whole group, two K-steps, per
+// iteration); at the group's end each is scaled by s[n, g] (fp32) into the
+// output accumulators, so every product is exact and the scale is applied
+// once per group, as the format defines.
 // The block's scales (and zero points) are copied to LDS once, before the
 // K loop, so the loop's only global traffic is the DMA whose per-wave counts
 // the stage waits rely on; that bounds K at 128 groups (16384 columns).
@@ -818,14 +820,11 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
         else asm volatile("s_waitcnt vmcnt(%0)" :: "n"(AU) : "memory");
     };
 
-    f32x4 acc[TM][TN], accg[TM][TN];
+    f32x4 acc[TM][TN], accg[TM][TN];  // accg: each group's first MFMA starts from zero
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-            accg[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
+        for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int frag_base = (wm * WM + i16) * (BK * 2);
     const int swz = i16 & 7;
     int nloc[TN];
@@ -843,48 +842,51 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
     issue(nk > 1 ? 1 : 0, 1);
     wait_prev_stage();
     __syncthreads();  // the scales in LDS and stage 0, for every wave
-    for (int kt = 0; kt < nk; ++kt) {
-        const int stage = kt % kStages;
-        issue(kt + 2 < nk ? kt + 2 : nk - 1, (kt + 2) % kStages);
+    const f32x4 zero4 = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int kt = 0; kt < nk; kt += 2) {  // group gi = kt / 2: K-steps kt and kt + 1
         const int gi = kt >> 1;
         if constexpr (ASYM) {
-            if ((kt & 1) == 0) {
 #pragma unroll
-                for (int j = 0; j < TN; ++j) add[j] = w4_nat_sub(zp_lds[nloc[j] * G + gi]);
-            }
+            for (int j = 0; j < TN; ++j) add[j] = w4_nat_sub(zp_lds[nloc[j] * G + gi]);
         }
-        const uint8_t* sbase = lds + stage * kStageBytes;
-        uint2 bw[TN];
 #pragma unroll
-        for (int j = 0; j < TN; ++j) bw[j] = *reinterpret_cast<const uint2*>(sbase + kABytes + nloc[j] * 32 + 8 * g);
+        for (int h = 0; h < 2; ++h) {
+            const int k = kt + h;
+            const int stage = k % kStages;
+            issue(k + 2 < nk ? k + 2 : nk - 1, (k + 2) % kStages);
+            const uint8_t* sbase = lds + stage * kStageBytes;
+            uint2 bw[TN];
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            const int chunk = (2 * g + s) ^ swz;
-            vec af[TM];
+            for (int j = 0; j < TN; ++j) bw[j] = *reinterpret_cast<const uint2*>(sbase + kABytes + nloc[j] * 32 + 8 * g);
 #pragma unroll
-            for (int i = 0; i < TM; ++i)
-                af[i] = __builtin_bit_cast(vec, *reinterpret_cast<const uint4*>(sbase + frag_base + i * 16 * (BK * 2) + 16 * chunk));
+            for (int s = 0; s < 2; ++s) {
+                const int chunk = (2 * g + s) ^ swz;
+                vec af[TM];
 #pragma unroll
-            for (int j = 0; j < TN; ++j) {
-                const vec bf = __builtin_bit_cast(vec, nat_w4_quad<T>(s ? bw[j].y : bw[j].x, mask_v, magic_v, mul, add[j]));
+                for (int i = 0; i < TM; ++i)
+                    af[i] = __builtin_bit_cast(vec, *reinterpret_cast<const uint4*>(sbase + frag_base + i * 16 * (BK * 2) + 16 * chunk));
 #pragma unroll
-                for (int i = 0; i < TM; ++i) accg[i][j] = Mfma<T>::mma(af[i], bf, accg[i][j]);
-            }
-        }
-        if (kt & 1) {  // end of group gi: scale into the outputs
+                for (int j = 0; j < TN; ++j) {
+                    const vec bf = __builtin_bit_cast(vec, nat_w4_quad<T>(s ? bw[j].y : bw[j].x, mask_v, magic_v, mul, add[j]));
+                    // the group's first MFMA starts from zero (an inline operand, no reset)
 #pragma unroll
-            for (int j = 0; j < TN; ++j) {
-                const float sc = f16_bits_to_f32(sc_lds[nloc[j] * G + gi]);
-#pragma unroll
-                for (int i = 0; i < TM; ++i) {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) acc[i][j][r] = fmaf(sc, accg[i][j][r], acc[i][j][r]);
-                    accg[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    for (int i = 0; i < TM; ++i)
+                        accg[i][j] = Mfma<T>::mma(af[i], bf, h == 0 && s == 0 ? zero4 : accg[i][j]);
                 }
             }
+            if (h == 1) {  // end of group gi: scale into the outputs
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    const float sc = f16_bits_to_f32(sc_lds[nloc[j] * G + gi]);
+#pragma unroll
+                    for (int i = 0; i < TM; ++i)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) acc[i][j][r] = fmaf(sc, accg[i][j][r], acc[i][j][r]);
+                }
+            }
+            wait_prev_stage();  // stage k + 1 has landed
+            stage_barrier();    // ... for every wave, and nobody reads stage k any more
         }
-        wait_prev_stage();  // stage kt + 1 has landed
-        stage_barrier();    // ... for every wave, and nobody reads stage kt any more
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();        // the ring is idle from here on
