@@ -654,33 +654,38 @@ __global__ __launch_bounds__(1024) void ternary_gemv_stream_kernel(SplitArgs sa)
         sc_bits = p.scale[nc];
         bi_bits = (p.bias ? p.bias : p.scale)[nc];
     }
+    // Global addresses are a wave-uniform base plus a 32-bit lane offset (the
+    // plan keeps 16 T rows of codes and 16 rows of activations below 4 GiB).
     // 1. activation slices -> the wave's LDS area by DMA, two rows per
     //    instruction (rows past M re-read row M-1; operand rows m >= M only
     //    feed outputs that are never stored)
+    const uint8_t* a_base = reinterpret_cast<const uint8_t*>(p.A);
 #pragma unroll
     for (int s = 0; s < CSW; ++s) {
-        const int cs = (s < cnt) ? cs0 + s : cs0;
+        const int cs = (s == 0 || s < cnt) ? cs0 + s : cs0;
+        const uint8_t* a_cs = a_base + (int64_t)cs * 512;
 #pragma unroll
         for (int e = 0; e < MR / 2; ++e) {
             const int r0 = 2 * e + (lane >> 5);
             const int r = r0 < M ? r0 : M - 1;
             const int piece = (lane & 31) ^ (r0 & 15);
-            dma16(p.A + (int64_t)r * K + (int64_t)cs * 256 + 8 * piece,
-                  area_lds + (uint32_t)(s * MR * 512 + e * 1024));
+            const uint32_t off = (uint32_t)r * (uint32_t)(2 * K) + 16u * (uint32_t)piece;
+            dma16(a_cs + off, area_lds + (uint32_t)(s * MR * 512 + e * 1024));
         }
     }
     // 2. code loads of all row-blocks, in the order step 4 consumes them (rows
     //    past N re-read row N-1, chunk-sets past the wave's share re-read its
     //    first one; both are ignored)
+    const uint8_t* c_blk = codes + n_base * rb;
     uint4 q[T][CSW];
 #pragma unroll
     for (int t = 0; t < T; ++t) {
         const int64_t n = n_base + 16 * t + i16;
-        const uint8_t* crow = codes + (n < N ? n : N - 1) * rb;
+        const uint32_t roff = (uint32_t)((n < N ? n : N - 1) - n_base) * (uint32_t)rb + 16u * (uint32_t)g;
 #pragma unroll
         for (int s = 0; s < CSW; ++s) {
-            const int cs = (s < cnt) ? cs0 + s : cs0;
-            q[t][s] = *reinterpret_cast<const uint4*>(crow + (int64_t)(4 * cs + g) * 16);
+            const int cs = (s == 0 || s < cnt) ? cs0 + s : cs0;
+            q[t][s] = *reinterpret_cast<const uint4*>(c_blk + (int64_t)cs * 64 + roff);
         }
     }
 
@@ -712,7 +717,7 @@ __global__ __launch_bounds__(1024) void ternary_gemv_stream_kernel(SplitArgs sa)
         f32x4 a4 = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < CSW; ++s) {
-            if (s < cnt) {
+            if (s == 0 || s < cnt) {  // cnt >= 1: the first chunk-set is unconditional
 #define TQ_MFMA_S(D, I0)                                                                              \
     {                                                                                                 \
         const uint4 bw = tern_quad<I0>(dword_of(q[t][s], D), magic_v);                                \
@@ -1109,30 +1114,35 @@ __global__ __launch_bounds__(1024) void w4_gemv_stream_kernel(SplitArgs sa) {
         scl[c] = *reinterpret_cast<const ScaleT*>(p.scale + o);
         if constexpr (ASYM) zpl[c] = *reinterpret_cast<const ZeroT*>(p.zeros + o);
     }
+    // Global addresses are a wave-uniform base plus a 32-bit lane offset (the
+    // plan keeps 16 T rows of codes and 16 rows of activations below 4 GiB).
     // 1. activation slices -> LDS by DMA (rows past M re-read row M-1)
+    const uint8_t* a_base = reinterpret_cast<const uint8_t*>(p.A);
 #pragma unroll
     for (int s = 0; s < GSW; ++s) {
-        const int gi = (s < cnt) ? g0 + s : g0;
+        const int gi = (s == 0 || s < cnt) ? g0 + s : g0;
+        const uint8_t* a_g = a_base + (int64_t)gi * 256;
 #pragma unroll
         for (int e = 0; e < MR / 4; ++e) {
             const int r0 = 4 * e + (lane >> 4);
             const int r = r0 < M ? r0 : M - 1;
             const int piece = (lane & 15) ^ (r0 & 15);
-            dma16(p.A + (int64_t)r * K + (int64_t)gi * 128 + 8 * piece,
-                  area_lds + (uint32_t)(s * MR * 256 + e * 1024));
+            const uint32_t off = (uint32_t)r * (uint32_t)(2 * K) + 16u * (uint32_t)piece;
+            dma16(a_g + off, area_lds + (uint32_t)(s * MR * 256 + e * 1024));
         }
     }
     // 2. code words of all row-blocks (rows past N re-read row N-1, groups
     //    past the wave's share re-read its first; both ignored)
+    const uint8_t* c_blk = codes + n_base * rowb;
     uint4 q[T][GSW];
 #pragma unroll
     for (int t = 0; t < T; ++t) {
         const int64_t n = n_base + 16 * t + i16;
-        const uint8_t* crow = codes + (n < N ? n : N - 1) * rowb + 16 * h;
+        const uint32_t roff = (uint32_t)((n < N ? n : N - 1) - n_base) * (uint32_t)rowb + 16u * (uint32_t)h;
 #pragma unroll
         for (int s = 0; s < GSW; ++s) {
-            const int gi = (s < cnt) ? g0 + s : g0;
-            q[t][s] = *reinterpret_cast<const uint4*>(crow + (int64_t)gi * 64);
+            const int gi = (s == 0 || s < cnt) ? g0 + s : g0;
+            q[t][s] = *reinterpret_cast<const uint4*>(c_blk + (int64_t)gi * 64 + roff);
         }
     }
 
@@ -1182,7 +1192,7 @@ __global__ __launch_bounds__(1024) void w4_gemv_stream_kernel(SplitArgs sa) {
         f32x4 a4 = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < GSW; ++s) {
-            if (s < cnt) {
+            if (s == 0 || s < cnt) {  // cnt >= 1: the first group is unconditional
                 W4Sub k{__builtin_bit_cast(f16x2, kW4Sub0Sym), __builtin_bit_cast(f16x2, kW4Sub1Sym)};
                 if constexpr (ASYM) k = w4_sub((uint32_t)zp[t][s]);
                 f32x4 ag = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1465,7 +1475,9 @@ static int64_t stream_cost(const GemmArgs& a, const StreamPlan& pl, int64_t cus)
 
 // Cheapest streaming plan whose split fits `ws_bytes` of workspace.
 static bool gemv_stream_plan(const GemmArgs& a, size_t ws_bytes, StreamPlan* pl) {
-    if (a.M < 3 || a.M > kGemvMaxM || a.K % 256 != 0) return false;
+    // K <= 2^20 keeps the kernel's 32-bit lane offsets in range (the
+    // geometry already bounds K far lower)
+    if (a.M < 3 || a.M > kGemvMaxM || a.K % 256 != 0 || a.K > (int64_t(1) << 20)) return false;
     const int64_t cus = compute_units();
     bool found = false;
     int64_t best = 0;
@@ -1659,7 +1671,9 @@ static int64_t w4_stream_cost(const GemmArgs& a, const W4StreamPlan& pl, int64_t
 }
 
 static bool w4_stream_plan(const GemmArgs& a, size_t ws_bytes, W4StreamPlan* pl) {
-    if (a.M < 1 || a.M > kGemvMaxM || a.K % 128 != 0) return false;
+    // K <= 2^20 keeps the kernel's 32-bit lane offsets in range (the
+    // geometry already bounds K far lower)
+    if (a.M < 1 || a.M > kGemvMaxM || a.K % 128 != 0 || a.K > (int64_t(1) << 20)) return false;
     const int64_t cus = compute_units();
     bool found = false;
     int64_t best = 0;
