@@ -304,3 +304,24 @@ def test_w4a_m1_kernel_one_hot(N, K, order, dt):
         A[0, k] = 1.0
         C = tq.w4a16_gemm(A.to(dev), q, s, zeros=z, perm=perm if order else None)
         np.testing.assert_array_equal(bits16(C)[0], to_bits(wdq[:, k]), err_msg=f"k={k}")
+
+
+@pytest.mark.parametrize("M", [1, 16, 300])
+def test_w4a_perm_out_of_range_clamped(M):
+    """A perm that is not the pack's (entries below 0, at K and far past it):
+    the gather clamps such an index to its own column, so an identity perm
+    with bad entries gives exactly the product without perm, on the decode
+    kernels and on the prefill GEMM, with no access outside A."""
+    import torch
+    import bit_weight_only_tq_amd as tq
+    dev = require_gpu()
+    N, K = 200, 1024
+    log(f"w4 perm out of range M={M}")
+    W = synth.weights(N, K, synth.seed_for("w4pbad", N, K))
+    q, s = tq.w4a16_pack(torch.from_numpy(W).to(dev))
+    perm = np.arange(K, dtype=np.int32)
+    perm[[3, 100, 640, K - 1]] = [-5, K, K + 7, 2 ** 31 - 1]
+    A = synth.activations(M, K, synth.seed_for("w4pbada", M, K), "f16").to(dev)
+    ref = tq.w4a16_gemm(A, q, s)
+    C = tq.w4a16_gemm(A, q, s, perm=torch.from_numpy(perm).to(dev))
+    np.testing.assert_array_equal(bits16(C), bits16(ref))
