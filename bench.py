@@ -333,7 +333,8 @@ def run_medium(dev, copies=8, iters=16, samples=None):
     import synth
     stream = torch.cuda.current_stream()
     res = {"metric": "ternary medium-M path (K split across workgroups), one Llama-3-70B layer",
-           "kernel": "mm3::tile_kernel (fp16, K % 256 == 0) + mm::splitk_reduce_kernel"}
+           "kernel": "mm3::tile_kernel (fp16, K % 256 == 0) + mm::splitk_reduce_kernel; "
+                     "mm3::pair_activations_kernel first where N K >= 200 * 2^20"}
     for name, (N, K) in layer_shapes(True, "70b"):
         W = synth.weights_device(N, K, synth.seed_for("benchmm", name), dev)
         codes, scale = tq.tq_pack(W)
@@ -343,6 +344,9 @@ def run_medium(dev, copies=8, iters=16, samples=None):
             A = synth.activations_device(M, K, synth.seed_for("benchmma", N, K, M), "f16", dev)
             C = torch.empty((M, N), dtype=torch.float16, device=dev)
             nbytes = tq.tq_gemm_workspace_bytes(M, N, K)
+            # the library pairs the activations once per call into the
+            # workspace (after the split partials) when N K >= 200 * 2^20
+            pair_b = M * K * 2 if K % 256 == 0 and N * K >= (200 << 20) else 0
             ws = torch.empty((max(nbytes, 16),), dtype=torch.uint8, device=dev)
             calls = [lambda c=c, s_=s_: tq.tq_gemm(A, c, s_, out=C, workspace=ws) for c, s_ in reps]
             for c in calls:
@@ -358,7 +362,8 @@ def run_medium(dev, copies=8, iters=16, samples=None):
             res[f"{name}_{N}x{K}_M{M}"] = {"us": round(t * 1e6, 2), "tflops": round(flops / t / 1e12, 1),
                                            "packed_gbs": round(codes.numel() / t / 1e9, 1),
                                            "roof_us": round(roof_s * 1e6, 2), "frac_of_roof": round(roof_s / t, 4),
-                                           "splits": nbytes // (4 * M * N) if nbytes else 1}
+                                           "splits": max(1, (nbytes - pair_b) // (4 * M * N)),
+                                           "paired_activations": pair_b > 0}
             del A, C, ws
         del reps, codes, scale
     torch.cuda.empty_cache()

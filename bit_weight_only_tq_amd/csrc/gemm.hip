@@ -534,7 +534,25 @@ __device__ __forceinline__ void prep_group(uint8_t* row, int G, int swz) {
     *p1 = f47;
 }
 
-template <class T, int TM>
+// PAIRED: A already holds the pairs (pair_activations_kernel), so the
+// in-place pairing of every K-step is skipped.
+// The in-place pairing of prep_group, once per call for the whole of A:
+// thread e pairs 16-column group e % (K / 16) of row e / (K / 16) (K % 16
+// == 0, A and out 16-byte aligned).
+__global__ __launch_bounds__(256) void pair_activations_kernel(const uint16_t* __restrict__ A, int64_t M, int64_t K,
+                                                               uint16_t* __restrict__ out) {
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (e >= M * (K / 16)) return;
+    const uint4* src = reinterpret_cast<const uint4*>(A) + 2 * e;
+    uint4 av[2] = {src[0], src[1]};
+    uint4 f03, f47;
+    act_pairs16<0>(av, f03, f47);
+    uint4* dst = reinterpret_cast<uint4*>(out) + 2 * e;
+    dst[0] = f03;
+    dst[1] = f47;
+}
+
+template <class T, int TM, bool PAIRED>
 __global__ __launch_bounds__(kThreads) void tile_kernel(SplitArgs sa) {
     typedef typename Mfma<T>::vec vec;
     constexpr int BM = 16 * TM;
@@ -614,7 +632,7 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(SplitArgs sa) {
     if constexpr (R == 4) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * P) : "memory");
     else asm volatile("s_waitcnt vmcnt(%0)" :: "n"(P) : "memory");
     stage_barrier();
-    prep(0);
+    if constexpr (!PAIRED) prep(0);
     if constexpr (R == 4) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(P) : "memory");
     else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     stage_barrier();
@@ -623,7 +641,9 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(SplitArgs sa) {
         // Unconditional so the per-wave counts stay exact: past the end the DMA
         // re-reads the last K-step into a slot nobody reads any more.
         issue(clamp_step(kt + R - 1), (it + R - 1) % R);
-        if (kt + 1 < ks1) prep((it + 1) % R);
+        if constexpr (!PAIRED) {
+            if (kt + 1 < ks1) prep((it + 1) % R);
+        }
         const uint8_t* sbase = lds + (it % R) * kStageBytes;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
@@ -1061,9 +1081,25 @@ int medium_m_splits(int64_t M, int64_t N, int64_t K, int compute_units) {
     return S < 1 ? 1 : (int)S;
 }
 
-size_t medium_m_workspace_bytes(int64_t M, int64_t N, int64_t K, int compute_units) {
+// With a workspace, large shapes pair the activations once per call
+// (pair_activations_kernel, into the workspace after the split partials)
+// instead of in every workgroup's K-steps: the pairing costs each of the
+// (N / 256) x (K / 256) workgroup K-steps about a microsecond per thousand,
+// the extra launch about 2.5 us, so it pays from N K ~ 2e8 (Llama-3-70B
+// gate_up and down, not qkv and o).
+constexpr int64_t kMediumPairMinNK = int64_t(200) << 20;
+
+static bool medium_paired(int64_t N, int64_t K) { return K % mm3::BK == 0 && N * K >= kMediumPairMinNK; }
+
+static size_t medium_partial_bytes(int64_t M, int64_t N, int64_t K, int compute_units) {
     const int S = medium_m_splits(M, N, K, compute_units);
     return S > 1 ? (size_t)S * (size_t)M * (size_t)N * sizeof(float) : 0;
+}
+
+size_t medium_m_workspace_bytes(int64_t M, int64_t N, int64_t K, int compute_units) {
+    const size_t part = medium_partial_bytes(M, N, K, compute_units);
+    if (!medium_paired(N, K)) return part;
+    return ((part + 255) & ~size_t(255)) + (size_t)M * (size_t)K * 2;
 }
 
 template <class T, int TM>
@@ -1080,16 +1116,16 @@ static hipError_t launch_mm(const SplitArgs& sa, hipStream_t s) {
     return e;
 }
 
-template <class T, int TM>
+template <class T, int TM, bool PAIRED>
 static hipError_t launch_mm3(const SplitArgs& sa, hipStream_t s) {
     static DeviceFlags lds_limit_set;
-    hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(&mm3::tile_kernel<T, TM>), (int)mm3::lds_bytes<TM>(),
-                                   lds_limit_set);
+    hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(&mm3::tile_kernel<T, TM, PAIRED>),
+                                   (int)mm3::lds_bytes<TM>(), lds_limit_set);
     if (e != hipSuccess) return e;
     const GemmArgs& a = sa.g;
     if (sa.S < 1 || sa.S > a.K / mm3::BK) return hipErrorInvalidValue;
     const dim3 grid((unsigned)((a.N + mm3::BN - 1) / mm3::BN), (unsigned)((a.M + 16 * TM - 1) / (16 * TM)), (unsigned)sa.S);
-    mm3::tile_kernel<T, TM><<<grid, mm3::kThreads, mm3::lds_bytes<TM>(), s>>>(sa);
+    mm3::tile_kernel<T, TM, PAIRED><<<grid, mm3::kThreads, mm3::lds_bytes<TM>(), s>>>(sa);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (sa.S > 1) e = launch_splitk_reduce(sa, s);
     return e;
@@ -1100,16 +1136,31 @@ static hipError_t launch_mm3(const SplitArgs& sa, hipStream_t s) {
 hipError_t launch_ternary_medium(const GemmArgs& a, void* workspace, size_t workspace_bytes, int compute_units,
                                  hipStream_t s) {
     SplitArgs sa{a, static_cast<float*>(workspace), medium_m_splits(a.M, a.N, a.K, compute_units)};
-    if (sa.S > 1 && (!workspace || workspace_bytes < medium_m_workspace_bytes(a.M, a.N, a.K, compute_units))) sa.S = 1;
-    return launch_ternary_medium_split(sa, s);
+    const size_t part = medium_partial_bytes(a.M, a.N, a.K, compute_units);
+    const bool paired = medium_paired(a.N, a.K) && workspace &&
+                        workspace_bytes >= medium_m_workspace_bytes(a.M, a.N, a.K, compute_units);
+    if (sa.S > 1 && (!workspace || workspace_bytes < part)) sa.S = 1;
+    if (paired) {
+        uint16_t* pa = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(workspace) + ((part + 255) & ~size_t(255)));
+        const int64_t n = a.M * (a.K / 16);
+        mm3::pair_activations_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(a.A, a.M, a.K, pa);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        sa.g.A = pa;
+    }
+    return launch_ternary_medium_split(sa, paired, s);
 }
 
-hipError_t launch_ternary_medium_split(const SplitArgs& sa, hipStream_t s) {
+hipError_t launch_ternary_medium_split(const SplitArgs& sa, bool paired, hipStream_t s) {
     const GemmArgs& a = sa.g;
     const bool small = a.M <= 32;
     if (a.K % mm3::BK == 0) {
-        if (a.bf16) return small ? launch_mm3<BF16, 2>(sa, s) : launch_mm3<BF16, 4>(sa, s);
-        return small ? launch_mm3<F16, 2>(sa, s) : launch_mm3<F16, 4>(sa, s);
+        if (paired) {
+            if (a.bf16) return small ? launch_mm3<BF16, 2, true>(sa, s) : launch_mm3<BF16, 4, true>(sa, s);
+            return small ? launch_mm3<F16, 2, true>(sa, s) : launch_mm3<F16, 4, true>(sa, s);
+        }
+        if (a.bf16) return small ? launch_mm3<BF16, 2, false>(sa, s) : launch_mm3<BF16, 4, false>(sa, s);
+        return small ? launch_mm3<F16, 2, false>(sa, s) : launch_mm3<F16, 4, false>(sa, s);
     }
     if (a.bf16) return small ? launch_mm<BF16, 2>(sa, s) : launch_mm<BF16, 4>(sa, s);
     return small ? launch_mm<F16, 2>(sa, s) : launch_mm<F16, 4>(sa, s);

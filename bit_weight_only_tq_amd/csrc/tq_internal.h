@@ -112,7 +112,7 @@ int medium_m_splits(int64_t M, int64_t N, int64_t K, int compute_units);
 size_t medium_m_workspace_bytes(int64_t M, int64_t N, int64_t K, int compute_units);
 hipError_t launch_ternary_medium(const GemmArgs& a, void* workspace, size_t workspace_bytes, int compute_units,
                                  hipStream_t s);
-hipError_t launch_ternary_medium_split(const SplitArgs& sa, hipStream_t s);  // a given split count
+hipError_t launch_ternary_medium_split(const SplitArgs& sa, bool paired, hipStream_t s);  // a given split count; paired: A holds pairs
 // Compute units of the current device (cached per device ordinal).
 int compute_units();
 hipError_t launch_w4_gemm(const GemmArgs& a, void* workspace, size_t workspace_bytes, hipStream_t s);

@@ -185,9 +185,14 @@ tq_status tq_gemm_ex(const void* A, tq_dtype dt, int64_t M, int64_t N, int64_t K
  *   path             TQ_PATH_AUTO or a forced kernel family (TQ_ERR_PATH if
  *                    it cannot run the shape: TQ_PATH_GEMV needs M <= 16).
  * With S > 1 splits the kernel writes S fp32 partials [S][M][N] into the
- * workspace and a second kernel sums them in order z = 0 .. S-1.  Other
- * arguments, results and errors as tq_gemm; TQ_ERR_ALIGN for a misaligned
- * workspace.  Asynchronous; allocates nothing; graph-capturable.
+ * workspace and a second kernel sums them in order z = 0 .. S-1.  On
+ * TQ_PATH_STREAM_MFMA with K % 256 == 0 and N * K >= 200 * 2^20 the
+ * workspace also holds the activations in the kernel's pair order (M * K * 2
+ * bytes after the partials, written by a first kernel of the call); with a
+ * workspace too small for both, the pairs are made inside the tiles, as
+ * without a workspace.  Other arguments, results and errors as tq_gemm;
+ * TQ_ERR_ALIGN for a misaligned workspace.  Asynchronous; allocates nothing;
+ * graph-capturable.
  */
 tq_status tq_gemm_ws(const void* A, tq_dtype dt, int64_t M, int64_t N, int64_t K,
                      const uint8_t* codes, const uint16_t* scale_f16, const void* bias,

@@ -96,7 +96,8 @@ def test_dispatcher_by_m():
 
 def test_workspace_query():
     """Split-K workspace: S fp32 partials of [M, N] for the medium and large-M
-    paths, none for the GEMV path or when the output tiles fill the device.
+    paths, none for the GEMV path or when the output tiles fill the device;
+    the medium path adds the paired activations on large shapes.
     Off the GPU the compute-unit count defaults to 256."""
     wb = _lib.tq_gemm_workspace_bytes
     assert wb(1, 4096, 4096) == 0 and wb(4096, 4096, 4096) == 0
@@ -106,7 +107,11 @@ def test_workspace_query():
     assert wb(40, 10240, 8192) == 6 * 40 * 10240 * 4    # 40 tiles: 6 splits keep one round on 256 CUs
     assert wb(100, 2000, 1024) == 2 * 100 * 2000 * 4    # 4 K-steps of 256: two per split
     assert wb(100, 2000, 4160) == 8 * 100 * 2000 * 4    # K % 256 != 0: 64-column kernel, >= 8 K-steps per split
-    assert wb(64, 57344, 8192) == 0                     # 224 tiles: no split
+    # N K >= 2e8: the activations are paired once per call, into the
+    # workspace after the split partials (256-byte aligned)
+    assert wb(64, 57344, 8192) == 64 * 8192 * 2         # 224 tiles: no split, pairs only
+    assert wb(32, 8192, 28672) == 8 * 32 * 8192 * 4 + 32 * 28672 * 2
+    assert wb(32, 8192, 28672, path="stream_mfma") == wb(32, 8192, 28672)
     assert wb(64, 8192, 96) == 0                        # K % 64 != 0
     # large M: 256 x 256 tiles, one per compute unit, >= 16 K-steps per split
     assert wb(2048, 4096, 14336) == 2 * 2048 * 4096 * 4  # 128 tiles: two splits fill the device
