@@ -126,10 +126,14 @@ tq_path tq_select_path(int format, int64_t M, int64_t N, int64_t K, tq_dtype dt)
     if (format == 0 && M >= 3 && M <= kGemvMaxM && K % 256 != 0) return TQ_PATH_STREAM_MFMA;
     if (M <= kGemvMaxM) return TQ_PATH_GEMV;
     if (format == 1) {
-        // W4A16: the prefill GEMM from 256 rows where it takes the shape (at
-        // most 128 groups), else the small-M kernels over blocks of 16 rows
-        const tq::GemmArgs a{nullptr, dt == TQ_BF16 ? 1 : 0, M, N, K, nullptr, nullptr, nullptr, nullptr};
-        return (M >= kMediumMaxM && tq::w4_prefill_ok(a)) ? TQ_PATH_GEMM : TQ_PATH_GEMV;
+        // W4A16: the matrix-core GEMM (64-row tiles below 256 rows, 256-row
+        // tiles above) from 33 rows, and from 17 where K >= 8192; the small-M
+        // kernels over blocks of 16 rows below that, where two passes over
+        // short-K weights beat the GEMM's K loop (Llama-3-8B gate_up at
+        // M = 17..32: 27-29 against 34 us).  A call whose K needs a split the
+        // workspace cannot hold also takes the row blocks (w4a16_gemm_ws).
+        if (K % 128 != 0 || (M <= 32 && K < 8192)) return TQ_PATH_GEMV;
+        return TQ_PATH_GEMM;
     }
     if (M < kMediumMaxM) return TQ_PATH_STREAM_MFMA;
     return TQ_PATH_GEMM;
@@ -268,6 +272,28 @@ tq_status tq_gemm_noalloc(const void* A, tq_dtype dt, int64_t M, int64_t N, int6
     return tq_gemm_ws(A, dt, M, N, K, codes, scale_f16, bias, C, ws, need, stream, path);
 }
 
+namespace {
+// The W4A16 kernels for a resolved path.  TQ_PATH_GEMM that the workspace
+// cannot serve (K long enough to need a split) falls back to the small-M
+// kernels over blocks of 16 rows when the dispatcher chose it, and is
+// refused when the caller forced it.
+tq_status launch_w4_path(const tq::GemmArgs& a, tq_path path, bool chosen, void* workspace, size_t wsb,
+                         hipStream_t stream) {
+    switch (path) {
+        case TQ_PATH_GEMV:
+            if (a.M > kGemvMaxM) return from_hip(tq::launch_w4_gemm(a, workspace, wsb, stream));
+            return from_hip(tq::launch_w4_gemv(a, workspace, wsb, stream));
+        case TQ_PATH_GEMM:
+            if (tq::w4_prefill_ok(a, wsb)) return from_hip(tq::launch_w4_prefill(a, workspace, wsb, stream));
+            if (!chosen) return TQ_ERR_PATH;
+            if (a.M > kGemvMaxM) return from_hip(tq::launch_w4_gemm(a, workspace, wsb, stream));
+            return from_hip(tq::launch_w4_gemv(a, workspace, wsb, stream));
+        default:
+            return TQ_ERR_PATH;
+    }
+}
+}  // namespace
+
 tq_status w4a16_gemm_ws(const void* A, tq_dtype dt, int64_t M, int64_t N, int64_t K, const int32_t* qweight,
                         const uint16_t* scales_f16, int64_t group_size, const void* bias, void* C, void* workspace,
                         size_t workspace_bytes, hipStream_t stream, tq_path path) {
@@ -277,25 +303,17 @@ tq_status w4a16_gemm_ws(const void* A, tq_dtype dt, int64_t M, int64_t N, int64_
     if (K % 128 != 0) return TQ_ERR_SHAPE;
     if (bias && (reinterpret_cast<uintptr_t>(bias) & 1u)) return TQ_ERR_ALIGN;
     if (workspace && !aligned16(workspace)) return TQ_ERR_ALIGN;
-    if (path == TQ_PATH_AUTO) path = tq_select_path(1, M, N, K, dt);
+    const bool chosen = path == TQ_PATH_AUTO;
+    if (chosen) path = tq_select_path(1, M, N, K, dt);
     tq::GemmArgs a{static_cast<const uint16_t*>(A), dt == TQ_BF16 ? 1 : 0, M, N, K, qweight, scales_f16,
                    static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(C)};
     const size_t wsb = workspace ? workspace_bytes : 0;
-    switch (path) {
-        case TQ_PATH_GEMV:
-            if (M > kGemvMaxM) return from_hip(tq::launch_w4_gemm(a, workspace, wsb, stream));
-            return from_hip(tq::launch_w4_gemv(a, workspace, wsb, stream));
-        case TQ_PATH_GEMM:
-            if (!tq::w4_prefill_ok(a)) return TQ_ERR_PATH;
-            return from_hip(tq::launch_w4_prefill(a, stream));
-        default:
-            return TQ_ERR_PATH;
-    }
+    return launch_w4_path(a, path, chosen, workspace, wsb, stream);
 }
 
 size_t w4a16_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, tq_dtype dt, int64_t group_size) {
     if (M <= 0 || N <= 0 || K <= 0 || K % 128 != 0 || group_size != 128) return 0;
-    if (tq_select_path(1, M, N, K, dt) == TQ_PATH_GEMM) return 0;  // the prefill kernel needs none
+    if (tq_select_path(1, M, N, K, dt) == TQ_PATH_GEMM) return tq::w4_gemm_workspace_bytes(M, N, K, tq::compute_units());
     const tq::GemmArgs a{nullptr, dt == TQ_BF16 ? 1 : 0, M < kGemvMaxM ? M : kGemvMaxM, N, K,
                          nullptr, nullptr, nullptr, nullptr};
     size_t b = tq::w4_gemv_workspace_bytes(a);
@@ -382,15 +400,17 @@ tq_status w4a16_gemm_asym(const void* A, tq_dtype dt, int64_t M, int64_t N, int6
     if (bias && (reinterpret_cast<uintptr_t>(bias) & 1u)) return TQ_ERR_ALIGN;
     if (perm && (reinterpret_cast<uintptr_t>(perm) & 3u)) return TQ_ERR_ALIGN;
     if (workspace && !aligned16(workspace)) return TQ_ERR_ALIGN;
-    if (path == TQ_PATH_AUTO) path = tq_select_path(1, M, N, K, dt);
+    const bool chosen = path == TQ_PATH_AUTO;
+    if (chosen) path = tq_select_path(1, M, N, K, dt);
     if (path != TQ_PATH_GEMV && path != TQ_PATH_GEMM) return TQ_ERR_PATH;
-    {
-        const tq::GemmArgs probe{nullptr, dt == TQ_BF16 ? 1 : 0, M, N, K, nullptr, nullptr, nullptr, nullptr};
-        if (path == TQ_PATH_GEMM && !tq::w4_prefill_ok(probe)) return TQ_ERR_PATH;
-    }
     const uint16_t* a_eff = static_cast<const uint16_t*>(A);
     uint8_t* ws = static_cast<uint8_t*>(workspace);
     size_t wsb = workspace ? workspace_bytes : 0;
+    {  // a forced GEMM path that cannot run is refused before anything is launched
+        const tq::GemmArgs probe{nullptr, dt == TQ_BF16 ? 1 : 0, M, N, K, nullptr, nullptr, nullptr, nullptr};
+        const size_t gb = perm ? gather_bytes(M, K) : 0;
+        if (path == TQ_PATH_GEMM && !chosen && !tq::w4_prefill_ok(probe, wsb > gb ? wsb - gb : 0)) return TQ_ERR_PATH;
+    }
     if (perm) {  // gather the activations into packed column order, at the front of the workspace
         const size_t gb = gather_bytes(M, K);
         if (wsb < gb) return TQ_ERR_SHAPE;
@@ -403,9 +423,7 @@ tq_status w4a16_gemm_asym(const void* A, tq_dtype dt, int64_t M, int64_t N, int6
     tq::GemmArgs a{a_eff, dt == TQ_BF16 ? 1 : 0, M, N, K, qweight, scales_f16,
                    static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(C), zeros};
     void* rest = wsb ? ws : nullptr;
-    if (path == TQ_PATH_GEMM) return from_hip(tq::launch_w4_prefill(a, stream));
-    if (M > kGemvMaxM) return from_hip(tq::launch_w4_gemm(a, rest, wsb, stream));
-    return from_hip(tq::launch_w4_gemv(a, rest, wsb, stream));
+    return launch_w4_path(a, path, chosen, rest, wsb, stream);
 }
 
 tq_status w4a16_gemm(const void* A, tq_dtype dt, int64_t M, int64_t N, int64_t K, const int32_t* qweight,

@@ -735,25 +735,35 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(SplitArgs sa) {
 // the stage waits rely on; that bounds K at 128 groups (16384 columns).
 namespace w4p {
 
-constexpr int BM = 256;
 constexpr int BN = 128;
 constexpr int BK = 64;
 constexpr int kThreads = 512;
-constexpr int WM = 128, WN = 32;
-constexpr int TM = WM / 16, TN = WN / 16;
-constexpr int AU = BM / 64;                 // 1-KB activation DMA blocks per wave and stage
 constexpr int kStages = 3;
-constexpr int kABytes = BM * BK * 2;        // 32 KB
 constexpr int kBBytes = BN * BK / 2;        // 4 KB: 128 rows x 32 bytes
-constexpr int kStageBytes = kABytes + kBBytes;
-constexpr int kRingBytes = kStages * kStageBytes;
-constexpr int kMaxGroups = 128;
-constexpr int kEpiLd = WN + 8;              // epilogue staging row (halves)
-constexpr int kEpiBytesPerWave = 32 * kEpiLd * 2;
-static_assert(8 * kEpiBytesPerWave <= kRingBytes, "epilogue staging must fit in the ring");
+constexpr int kMaxGroups = 128;             // groups per split (scales held in LDS)
 
-__host__ __device__ constexpr size_t lds_bytes(int64_t G, bool asym) {
-    return (size_t)kRingBytes + (size_t)BN * G * 2 + (asym ? (size_t)BN * G : 0);
+// Block tile BM x 128: BM = 256 (eight waves of 128 x 32) for prefill,
+// BM = 64 (eight waves of 64 x 16) for 17 <= M < 256, where a 256-row tile
+// would mostly multiply padding.
+template <int BM>
+struct Tile {
+    static constexpr int WM = BM == 256 ? 128 : 64;
+    static constexpr int WN = BM == 256 ? 32 : 16;
+    static constexpr int kWaveCols = BN / WN;
+    static constexpr int TM = WM / 16, TN = WN / 16;
+    static constexpr int AU = BM / 64;                  // 1-KB activation DMA blocks per wave and stage
+    static constexpr int kABytes = BM * BK * 2;
+    static constexpr int kStageBytes = kABytes + kBBytes;
+    static constexpr int kRingBytes = kStages * kStageBytes;
+    static constexpr int kEpiLd = WN + 8;               // epilogue staging row (halves)
+    static constexpr int kEpiBytesPerWave = 32 * kEpiLd * 2;
+    static_assert((BM / WM) * kWaveCols == 8, "eight waves");
+    static_assert(8 * kEpiBytesPerWave <= kRingBytes, "epilogue staging must fit in the ring");
+};
+
+template <int BM>
+__host__ __device__ constexpr size_t lds_bytes(int64_t groups, bool asym) {
+    return (size_t)Tile<BM>::kRingBytes + (size_t)BN * groups * 2 + (asym ? (size_t)BN * groups : 0);
 }
 
 // (q_2d - z, q_2d+1 - z) of code word x as exact fp16, natural order.
@@ -777,32 +787,44 @@ __device__ __forceinline__ f16x2 w4_nat_sub(uint32_t z) {
     return __builtin_bit_cast(f16x2, (0xE400u + z) | ((0xD400u + 16u * z) << 16));
 }
 
-template <class T, bool ASYM>
-__global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
+// Split z of S (gridDim.z) covers groups [z G / S, (z + 1) G / S) and, when
+// S > 1, stores fp32 partials (scales applied, no bias) for
+// launch_splitk_reduce; the host keeps every split within kMaxGroups.
+template <class T, bool ASYM, int BM>
+__global__ __launch_bounds__(kThreads) void gemm_kernel(SplitArgs sa) {
     typedef typename Mfma<T>::vec vec;
+    typedef Tile<BM> TL;
+    constexpr int WM = TL::WM, WN = TL::WN, TM = TL::TM, TN = TL::TN, AU = TL::AU;
+    constexpr int kABytes = TL::kABytes, kStageBytes = TL::kStageBytes, kRingBytes = TL::kRingBytes;
+    constexpr int kEpiLd = TL::kEpiLd, kEpiBytesPerWave = TL::kEpiBytesPerWave;
+    const GemmArgs& p = sa.g;
     extern __shared__ uint4 smem_w4p[];
     uint8_t* lds = reinterpret_cast<uint8_t*>(smem_w4p);
     const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)smem_w4p;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 2, wn = wave & 3;
+    const int wm = wave / TL::kWaveCols, wn = wave % TL::kWaveCols;
     const int g = lane >> 4;
     const int i16 = lane & 15;
     const int64_t m0 = (int64_t)blockIdx.y * BM;
     const int64_t n0 = (int64_t)blockIdx.x * BN;
     const int64_t M = p.M, N = p.N, K = p.K;
     const int G = (int)(K / 128);
+    const int z = blockIdx.z;
+    const int g_lo = (int)((int64_t)G * z / sa.S);
+    const int Gs = (int)((int64_t)G * (z + 1) / sa.S) - g_lo;  // groups of this split, 1 .. kMaxGroups
     const int64_t rowb = K / 2;  // code bytes per weight row
-    uint16_t* sc_lds = reinterpret_cast<uint16_t*>(lds + kRingBytes);   // [BN][G]
-    uint8_t* zp_lds = lds + kRingBytes + (size_t)BN * G * 2;             // [BN][G]
+    uint16_t* sc_lds = reinterpret_cast<uint16_t*>(lds + kRingBytes);   // [BN][Gs]
+    uint8_t* zp_lds = lds + kRingBytes + (size_t)BN * Gs * 2;            // [BN][Gs]
 
-    // the block's group scales (and zero points) -> LDS; rows past N re-read row N-1
-    for (int e = tid; e < BN * G; e += kThreads) {
-        const int r = e / G, gi = e - r * G;
+    // the block's group scales (and zero points) of this split -> LDS; rows
+    // past N re-read row N-1
+    for (int e = tid; e < BN * Gs; e += kThreads) {
+        const int r = e / Gs, gl = e - r * Gs;
         const int64_t n = n0 + r < N ? n0 + r : N - 1;
-        sc_lds[e] = p.scale[n * G + gi];
-        if constexpr (ASYM) zp_lds[e] = p.zeros[n * G + gi];
+        sc_lds[e] = p.scale[n * G + g_lo + gl];
+        if constexpr (ASYM) zp_lds[e] = p.zeros[n * G + g_lo + gl];
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
@@ -857,23 +879,23 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) add[j] = w4_nat_sub(8u);
 
-    const int nk = (int)(K / BK);  // even: K % 128 == 0
-    issue(0, 0);
-    issue(nk > 1 ? 1 : 0, 1);
+    const int kb = 2 * g_lo, nk = 2 * Gs;  // this split's K-steps kb .. kb + nk - 1 (nk >= 2)
+    issue(kb, 0);
+    issue(kb + 1, 1);
     wait_prev_stage();
     __syncthreads();  // the scales in LDS and stage 0, for every wave
     const f32x4 zero4 = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int kt = 0; kt < nk; kt += 2) {  // group gi = kt / 2: K-steps kt and kt + 1
-        const int gi = kt >> 1;
+    for (int kt = 0; kt < nk; kt += 2) {  // local group gl = kt / 2: K-steps kt and kt + 1
+        const int gl = kt >> 1;
         if constexpr (ASYM) {
 #pragma unroll
-            for (int j = 0; j < TN; ++j) add[j] = w4_nat_sub(zp_lds[nloc[j] * G + gi]);
+            for (int j = 0; j < TN; ++j) add[j] = w4_nat_sub(zp_lds[nloc[j] * Gs + gl]);
         }
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int k = kt + h;
             const int stage = k % kStages;
-            issue(k + 2 < nk ? k + 2 : nk - 1, (k + 2) % kStages);
+            issue(kb + (k + 2 < nk ? k + 2 : nk - 1), (k + 2) % kStages);
             const uint8_t* sbase = lds + stage * kStageBytes;
             uint2 bw[TN];
 #pragma unroll
@@ -897,7 +919,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
             if (h == 1) {  // end of group gi: scale into the outputs
 #pragma unroll
                 for (int j = 0; j < TN; ++j) {
-                    const float sc = f16_bits_to_f32(sc_lds[nloc[j] * G + gi]);
+                    const float sc = f16_bits_to_f32(sc_lds[nloc[j] * Gs + gl]);
 #pragma unroll
                     for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -911,7 +933,24 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();        // the ring is idle from here on
 
-    // epilogue: per wave, slabs of 32 rows x 32 columns through a private LDS area
+    if (sa.S > 1) {  // fp32 partial of this split: 16 lanes store 64 contiguous bytes per row
+        float* ws = sa.ws + (int64_t)z * M * N;
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int64_t m = m0 + wm * WM + 16 * i + 4 * g + r;
+                if (m >= M) continue;
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    const int64_t n = n0 + nloc[j];
+                    if (n < N) ws[m * N + n] = acc[i][j][r];
+                }
+            }
+        return;
+    }
+
+    // epilogue: per wave, slabs of 32 rows x WN columns through a private LDS area
     uint16_t* stg = reinterpret_cast<uint16_t*>(lds + wave * kEpiBytesPerWave);
     float bi[TN];
 #pragma unroll
@@ -932,11 +971,12 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
                 for (int j = 0; j < TN; ++j) stg[row * kEpiLd + 16 * j + i16] = T::from_f32_fast(acc[i][j][r] + bi[j]);
             }
         }
-        // each lane stores 16 contiguous bytes: row lane/4 + 16q, columns 8 (lane % 4) .. +7
+        // each lane stores 16 contiguous bytes: WN / 8 lanes per row
+        constexpr int kLanesPerRow = WN / 8, kRowsPerPass = 64 / kLanesPerRow;
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const int row = (lane >> 2) + 16 * q;
-            const int col = 8 * (lane & 3);
+        for (int q = 0; q < 32 / kRowsPerPass; ++q) {
+            const int row = lane / kLanesPerRow + kRowsPerPass * q;
+            const int col = 8 * (lane % kLanesPerRow);
             const int64_t m = m0 + wm * WM + 32 * slab + row;
             const int64_t n = n0 + wn * WN + col;
             if (m >= M) continue;
@@ -1166,25 +1206,70 @@ hipError_t launch_ternary_medium_split(const SplitArgs& sa, bool paired, hipStre
     return small ? launch_mm<F16, 2>(sa, s) : launch_mm<F16, 4>(sa, s);
 }
 
-template <class T, bool ASYM>
-static hipError_t launch_w4p(const GemmArgs& a, hipStream_t s) {
-    static DeviceFlags lds_limit_set;
-    const int64_t G = a.K / 128;
-    hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(&w4p::gemm_kernel<T, ASYM>),
-                                   (int)w4p::lds_bytes(w4p::kMaxGroups, ASYM), lds_limit_set);
-    if (e != hipSuccess) return e;
-    if (G < 1 || G > w4p::kMaxGroups || a.K % 128 != 0) return hipErrorInvalidValue;
-    const dim3 grid((unsigned)((a.N + w4p::BN - 1) / w4p::BN), (unsigned)((a.M + w4p::BM - 1) / w4p::BM));
-    w4p::gemm_kernel<T, ASYM><<<grid, w4p::kThreads, w4p::lds_bytes(G, ASYM), s>>>(a);
-    return hipGetLastError();
+// W4A16 GEMM plan: the 256-row tile from M = 256, the 64-row tile below;
+// K split S ways (fp32 partials, launch_splitk_reduce) while the tiles leave
+// compute units idle (at most 16 splits, at least one group each), and at
+// least enough splits that none holds more than kMaxGroups groups' scales.
+static int w4_gemm_bm(int64_t M) { return M >= 256 ? 256 : 64; }
+
+static int w4_gemm_min_splits(int64_t K) {
+    const int64_t G = K / 128;
+    return (int)((G + w4p::kMaxGroups - 1) / w4p::kMaxGroups);
 }
 
-bool w4_prefill_ok(const GemmArgs& a) { return a.K % 128 == 0 && a.K / 128 <= w4p::kMaxGroups; }
+int w4_gemm_splits(int64_t M, int64_t N, int64_t K, int compute_units) {
+    const int64_t G = K / 128;
+    const int bm = w4_gemm_bm(M);
+    const int64_t tiles = ((N + w4p::BN - 1) / w4p::BN) * ((M + bm - 1) / bm);
+    const int64_t cus = compute_units > 0 ? compute_units : 1;
+    int64_t S = cus / tiles;
+    if (S > 16) S = 16;
+    if (S > G) S = G;
+    const int smin = w4_gemm_min_splits(K);
+    if (S < smin) S = smin;
+    return S < 1 ? 1 : (int)S;
+}
 
-hipError_t launch_w4_prefill(const GemmArgs& a, hipStream_t s) {
-    if (!w4_prefill_ok(a)) return hipErrorInvalidValue;
-    if (a.zeros) return a.bf16 ? launch_w4p<BF16, true>(a, s) : launch_w4p<F16, true>(a, s);
-    return a.bf16 ? launch_w4p<BF16, false>(a, s) : launch_w4p<F16, false>(a, s);
+size_t w4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int compute_units) {
+    const int S = w4_gemm_splits(M, N, K, compute_units);
+    return S > 1 ? (size_t)S * (size_t)M * (size_t)N * sizeof(float) : 0;
+}
+
+bool w4_prefill_ok(const GemmArgs& a, size_t workspace_bytes) {
+    if (a.K % 128 != 0 || a.K < 128) return false;
+    const int smin = w4_gemm_min_splits(a.K);
+    return smin == 1 || (smin <= 16 && smin <= a.K / 128 &&
+                         workspace_bytes >= (size_t)smin * (size_t)a.M * (size_t)a.N * sizeof(float));
+}
+
+template <class T, bool ASYM, int BM>
+static hipError_t launch_w4p(const SplitArgs& sa, hipStream_t s) {
+    static DeviceFlags lds_limit_set;
+    hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(&w4p::gemm_kernel<T, ASYM, BM>),
+                                   (int)w4p::lds_bytes<BM>(w4p::kMaxGroups, ASYM), lds_limit_set);
+    if (e != hipSuccess) return e;
+    const GemmArgs& a = sa.g;
+    const int64_t G = a.K / 128;
+    if (a.K % 128 != 0 || sa.S < 1 || sa.S > G || (G + sa.S - 1) / sa.S > w4p::kMaxGroups) return hipErrorInvalidValue;
+    const int64_t gs_max = (G + sa.S - 1) / sa.S;
+    const dim3 grid((unsigned)((a.N + w4p::BN - 1) / w4p::BN), (unsigned)((a.M + BM - 1) / BM), (unsigned)sa.S);
+    w4p::gemm_kernel<T, ASYM, BM><<<grid, w4p::kThreads, w4p::lds_bytes<BM>(gs_max, ASYM), s>>>(sa);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    return sa.S > 1 ? launch_splitk_reduce(sa, s) : hipSuccess;
+}
+
+template <int BM>
+static hipError_t launch_w4p_bm(const SplitArgs& sa, hipStream_t s) {
+    if (sa.g.zeros) return sa.g.bf16 ? launch_w4p<BF16, true, BM>(sa, s) : launch_w4p<F16, true, BM>(sa, s);
+    return sa.g.bf16 ? launch_w4p<BF16, false, BM>(sa, s) : launch_w4p<F16, false, BM>(sa, s);
+}
+
+hipError_t launch_w4_prefill(const GemmArgs& a, void* workspace, size_t workspace_bytes, hipStream_t s) {
+    if (!w4_prefill_ok(a, workspace ? workspace_bytes : 0)) return hipErrorInvalidValue;
+    SplitArgs sa{a, static_cast<float*>(workspace), w4_gemm_splits(a.M, a.N, a.K, compute_units()), 1};
+    const size_t need = (size_t)sa.S * (size_t)a.M * (size_t)a.N * sizeof(float);
+    if (sa.S > 1 && (!workspace || workspace_bytes < need)) sa.S = w4_gemm_min_splits(a.K);  // fits: w4_prefill_ok
+    return w4_gemm_bm(a.M) == 256 ? launch_w4p_bm<256>(sa, s) : launch_w4p_bm<64>(sa, s);
 }
 
 // W4A16 at large M where the prefill kernel does not take the shape (more

@@ -117,7 +117,13 @@ hipError_t launch_ternary_medium_split(const SplitArgs& sa, bool paired, hipStre
 int compute_units();
 hipError_t launch_w4_gemm(const GemmArgs& a, void* workspace, size_t workspace_bytes, hipStream_t s);
 // gemm.hip: W4A16 prefill GEMM (any M, K % 128 == 0, at most 128 groups).
-bool w4_prefill_ok(const GemmArgs& a);
-hipError_t launch_w4_prefill(const GemmArgs& a, hipStream_t s);
+// gemm.hip: W4A16 matrix-core GEMM (17 <= M), K split across workgroups
+// while the tiles leave compute units idle or a split would hold more than
+// 128 groups; w4_prefill_ok tells whether a workspace of the given size lets
+// it run (long K needs at least the minimum split's partials).
+int w4_gemm_splits(int64_t M, int64_t N, int64_t K, int compute_units);
+size_t w4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int compute_units);
+bool w4_prefill_ok(const GemmArgs& a, size_t workspace_bytes);
+hipError_t launch_w4_prefill(const GemmArgs& a, void* workspace, size_t workspace_bytes, hipStream_t s);
 
 }  // namespace tq

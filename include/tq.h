@@ -82,7 +82,7 @@ typedef enum tq_path {
     TQ_PATH_AUTO = 0,        /* let the dispatcher choose */
     TQ_PATH_GEMV = 1,        /* small M: weight-streaming kernel, codes read once per call */
     TQ_PATH_STREAM_MFMA = 2, /* medium M: 64-row tiles, K split across workgroups */
-    TQ_PATH_GEMM = 3         /* large M: LDS-tiled matrix-core GEMM (prefill) */
+    TQ_PATH_GEMM = 3         /* large M: LDS-tiled matrix-core GEMM (prefill; W4A16 also medium M) */
 } tq_path;
 
 /* ---------------------------------------------------------------- prepare */
@@ -236,9 +236,11 @@ size_t tq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, tq_dtype dt, tq_
  *   w4a16_pack; group_size must be 128; K % 128 == 0.
  * C[m, n] = sum_g s[n, g] * sum_{k in g} A[m, k] * (q[n, k] - 8) + bias[n]:
  * the group scale multiplies each group's fp32 partial sum.  Other arguments
- * as tq_gemm.  From M = 256 (or with TQ_PATH_GEMM) a prefill GEMM runs on the
- * matrix cores when K / 128 <= 128; other shapes run the decode kernels over
- * blocks of 16 rows.  Asynchronous; allocates nothing; graph-capturable.
+ * as tq_gemm.  From M = 33 (M = 17 when K >= 8192), or with TQ_PATH_GEMM, a
+ * GEMM runs on the matrix cores (256-row tiles from M = 256, 64-row tiles
+ * below); without a workspace it needs K / 128 <= 128.  Other shapes run the
+ * decode kernels over blocks of 16 rows.  Asynchronous; allocates nothing;
+ * graph-capturable.
  */
 tq_status w4a16_gemm(const void* A, tq_dtype dt, int64_t M, int64_t N, int64_t K,
                      const int32_t* qweight, const uint16_t* scales_f16, int64_t group_size,
@@ -258,8 +260,13 @@ tq_status w4a16_gemm_ex(const void* A, tq_dtype dt, int64_t M, int64_t N, int64_
  * or shapes the M <= 4 kernel cannot take) may split the K groups across
  * workgroups (fp32 partials with the group scales applied, summed in order
  * by a second kernel, bias added there); with less it makes one pass over
- * K.  The M <= 4 kernel never splits, and the query reports 0 for it.  M > 16 runs as successive blocks of 16 rows that reuse
- * the workspace in stream order.  Other arguments, results and errors as
+ * K.  The M <= 4 kernel never splits, and the query reports 0 for it.  The
+ * matrix-core GEMM splits the K groups the same way while its 128-column
+ * tiles leave compute units idle (at most 16 splits) and always when K / 128
+ * > 128 (each split holds at most 128 groups' scales); a shape that needs a
+ * split the workspace cannot hold runs the decode kernels over blocks of 16
+ * rows under TQ_PATH_AUTO and returns TQ_ERR_PATH under TQ_PATH_GEMM.  Row
+ * blocks (M > 16) reuse the workspace in stream order.  Other arguments, results and errors as
  * w4a16_gemm; TQ_ERR_ALIGN for a misaligned workspace.
  */
 tq_status w4a16_gemm_ws(const void* A, tq_dtype dt, int64_t M, int64_t N, int64_t K,
@@ -327,8 +334,9 @@ tq_status w4a16_unpack_asym(const int32_t* qweight, const uint16_t* scales_f16, 
  *          otherwise).  perm must be the array the pack wrote; any other
  *          contents give unspecified results (indices are clamped into
  *          [0, K), so memory stays in bounds).
- *   path   TQ_PATH_AUTO, TQ_PATH_GEMV or TQ_PATH_GEMM (the prefill GEMM; needs
- *          K / 128 <= 128; TQ_ERR_PATH otherwise).
+ *   path   TQ_PATH_AUTO, TQ_PATH_GEMV or TQ_PATH_GEMM (the matrix-core GEMM;
+ *          with K / 128 > 128 it needs the workspace of the K split after
+ *          the gathered activations, TQ_ERR_PATH otherwise).
  * The rest of the workspace serves the split-K schedule of w4a16_gemm_ws.
  * Asynchronous; allocates nothing; graph-capturable.
  */
@@ -384,9 +392,10 @@ tq_status tq_diag_gemv(const void* A, tq_dtype dt, int64_t M, int64_t N, int64_t
  *   weights (they dominate the bytes moved); prefill-sized M (>= 256) is a
  *   dense contraction for the matrix cores (the decode / prefill split of
  *   the quantization decision tree on page "10.6 Quantization choice and vLLM
- *   in practice", section 10.6.1; W4A16 when K / 128 <= 128); ternary M in
- *   17 .. 255, and ternary M in 3 .. 16 with K % 256 != 0, take the medium
- *   path, 32- or 64-row tiles with K split across workgroups.
+ *   in practice", section 10.6.1); ternary M in 17 .. 255, and ternary M in
+ *   3 .. 16 with K % 256 != 0, take the medium path, 32- or 64-row tiles
+ *   with K split across workgroups.  W4A16 takes its matrix-core GEMM from
+ *   M = 33 (M = 17 when K >= 8192), 64-row tiles below 256 rows.
  */
 tq_path tq_select_path(int format, int64_t M, int64_t N, int64_t K, tq_dtype dt);
 

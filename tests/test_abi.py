@@ -75,12 +75,15 @@ def test_dispatcher_by_m():
         assert sel("w4a16", M, 4096, 4096) == "gemv"
     for M in (17, 32, 64, 255):
         assert sel("ternary", M, 8192, 8192) == "stream_mfma"
-        assert sel("w4a16", M, 8192, 8192) == "gemv"
+        assert sel("w4a16", M, 8192, 8192) == "gemm"      # W4A16: the GEMM's 64-row tiles
+    # W4A16 at 17..32 rows with K < 8192: two passes of the decode kernels
+    assert sel("w4a16", 17, 14336, 4096) == sel("w4a16", 32, 14336, 4096) == "gemv"
+    assert sel("w4a16", 33, 14336, 4096) == "gemm"
     for M in (256, 2048, 4096, 8192):
         assert sel("ternary", M, 14336, 4096, "bf16") == "gemm"
         assert sel("w4a16", M, 14336, 4096, "bf16") == "gemm"
         assert sel("w4a16", M, 4096, 16384) == "gemm"
-        assert sel("w4a16", M, 4096, 16384 + 128) == "gemv"  # past 128 groups: decode kernels over row blocks
+        assert sel("w4a16", M, 4096, 16384 + 128) == "gemm"  # past 128 groups: split K (needs a workspace)
     # bf16 follows the same split (its decode kernels match fp16's)
     for M in (1, 4, 5, 16):
         assert sel("ternary", M, 4096, 4096, "bf16") == "gemv"
@@ -161,10 +164,10 @@ def test_tq_gemm_ws_host_checks(lib):
 
 
 def test_w4_workspace_query():
-    """W4A16 split-K workspace (fp16, 2 <= M <= 16): S fp32 partials of
-    [M, N] when the plan splits the K groups; none where the small-M kernel
-    runs (M <= 4 on its shapes), for bf16, or when one pass over K is
-    cheapest.  Off the GPU the compute-unit count
+    """W4A16 split-K workspace: S fp32 partials of [M, N] when the plan splits
+    the K groups (the streaming kernel at 2 <= M <= 16, the matrix-core GEMM
+    above); none where the small-M kernel runs (M <= 4 on its shapes) or when
+    one pass over K is cheapest.  Off the GPU the compute-unit count
     defaults to 256."""
     wb = _lib.w4a16_gemm_workspace_bytes
     assert wb(16, 4096, 14336) == 8 * 16 * 4096 * 4       # 112 groups -> 8 splits of 14
@@ -175,7 +178,15 @@ def test_w4_workspace_query():
     assert wb(5, 4096, 14336) == 8 * 5 * 4096 * 4        # M = 5 streams: 112 groups -> 8 splits of 14
     assert wb(16, 4096, 14336, "bf16") == wb(16, 4096, 14336)  # bf16 streams like fp16
     assert wb(16, 4096, 14336, group_size=64) == 0
-    assert wb(40, 4096, 14336) == 8 * 16 * 4096 * 4      # blocks of 16 rows, the largest block's need
+    assert wb(24, 4096, 4096) == 0                        # blocks of 16 rows, no split on these shapes
+    assert wb(24, 1024, 4096) == wb(16, 1024, 4096)       # ... the largest block's need
+    # the matrix-core GEMM (17 <= M, K >= 8192 or M > 32): split while the
+    # 128-column tiles leave compute units idle, at most 16, >= 1 group each
+    assert wb(40, 4096, 14336) == 8 * 40 * 4096 * 4      # 32 tiles -> 8 splits
+    assert wb(64, 57344, 8192) == 0                       # 448 tiles: one pass
+    assert wb(256, 4096, 14336) == 8 * 256 * 4096 * 4     # 256-row tiles: 32 tiles -> 8 splits
+    assert wb(2048, 4096, 14336) == 0 and wb(4096, 14336, 4096) == 0
+    assert wb(4096, 4096, 16384 + 128) == 2 * 4096 * 4096 * 4  # 129 groups: two splits at least
     assert wb(16, 4096, 200) == 0                         # K % 128 != 0
 
 

@@ -355,8 +355,9 @@ def test_w4_ragged_shapes(M, N, K):
 def test_w4_split_k(M, N, K):
     """W4A16 streaming kernel with the K groups split across workgroups
     (workspace from torch) and without a workspace: both within the tolerance
-    on sampled output columns, ragged N, with bias; M > 16 runs blocks of 16
-    rows through one workspace; a repeated call is bit-identical."""
+    on sampled output columns, ragged N, with bias; a repeated call is
+    bit-identical.  M > 16 takes the matrix-core GEMM (its own K split) and,
+    forced, the decode kernels over blocks of 16 rows through one workspace."""
     import torch
     import bit_weight_only_tq_amd as tq
     dev = require_gpu()
@@ -380,6 +381,11 @@ def test_w4_split_k(M, N, K):
         outs.append(C)
     C2 = tq.w4a16_gemm(A.to(dev), q, s, bias=bias.to(dev))
     assert torch.equal(outs[0].view(torch.int16), C2.view(torch.int16))
+    if M > 16:
+        ws = torch.empty((64 << 20,), dtype=torch.uint8, device=dev)
+        C = tq.w4a16_gemm(A.to(dev), q, s, bias=bias.to(dev), workspace=ws, path="gemv")
+        check_close(C.index_select(1, idx), A, wdq, bias=bias[torch.from_numpy(cols)],
+                    label=f"w4 row blocks {M}x{N}x{K}")
 
 
 def test_w4_one_hot_bit_exact():
@@ -399,8 +405,10 @@ def test_w4_one_hot_bit_exact():
     np.testing.assert_array_equal(bits16(C), OR.f16_bits(wdq[:, ks].T))
 
 
-@pytest.mark.parametrize("M", [1, 40])
+@pytest.mark.parametrize("M", [1, 20, 40])
 def test_w4_ragged_and_blocked(M):
+    """Ragged N = 200 at K = 384: the decode kernels (M = 1), blocks of 16
+    rows (M = 20) and the matrix-core GEMM (M = 40), fp16 and bf16."""
     import torch
     import bit_weight_only_tq_amd as tq
     dev = require_gpu()
@@ -450,12 +458,14 @@ def test_w4_m1_one_hot_and_bias(N, K, dt):
     check_close(C, A, wdq, bias=bias, label=f"W4 M=1 kernel {N}x{K} {dt} with bias")
 
 
-@pytest.mark.parametrize("M,N,K", [(5, 4096, 4096), (16, 28672, 4096), (11, 1024, 14336), (40, 320, 4096)])
-def test_w4_bf16_row_blocks(M, N, K):
+@pytest.mark.parametrize("M,N,K,path", [(5, 4096, 4096, "auto"), (16, 28672, 4096, "auto"), (11, 1024, 14336, "auto"),
+                                        (24, 320, 4096, "auto"), (40, 320, 4096, "gemv"), (40, 320, 4096, "auto")])
+def test_w4_bf16_row_blocks(M, N, K, path):
     """bf16 W4A16 past four rows: the streaming kernel's bf16 form (inside
-    blocks of 16 rows when M > 16, the last block ragged); one-hot rows give
-    C[m, n] = wdq[n, k_m] bit for bit, dense rows with a bias are within the
-    tolerance, the row past M is untouched."""
+    blocks of 16 rows when M > 16, the last block ragged; M = 40 also through
+    the matrix-core GEMM); one-hot rows give C[m, n] = wdq[n, k_m] bit for
+    bit, dense rows with a bias are within the tolerance, the row past M is
+    untouched."""
     import torch
     import bit_weight_only_tq_amd as tq
     dev = require_gpu()
@@ -465,12 +475,12 @@ def test_w4_bf16_row_blocks(M, N, K):
     A = torch.zeros((M, K), dtype=torch.bfloat16)
     for m, k in enumerate(ks):
         A[m, k] = 1.0
-    C = tq.w4a16_gemm(A.to(dev), q, s)
+    C = tq.w4a16_gemm(A.to(dev), q, s, path=path)
     np.testing.assert_array_equal(bits16(C), OR.bf16_bits(wdq[:, ks].T))
     A = synth.activations(M, K, synth.seed_for("w4bfr", M, N, K), "bf16")
     bias = synth.activations(1, N, synth.seed_for("w4bfrb", N, K), "bf16")[0]
     buf = torch.full((M + 1, N), -7.0, dtype=torch.bfloat16, device=dev)
-    C = tq.w4a16_gemm(A.to(dev), q, s, bias=bias.to(dev), out=buf[:M])
+    C = tq.w4a16_gemm(A.to(dev), q, s, bias=bias.to(dev), out=buf[:M], path=path)
     check_close(C, A, wdq, bias=bias, label=f"W4 bf16 row blocks M={M} {N}x{K}")
     assert bool((buf[M] == -7.0).all())
 

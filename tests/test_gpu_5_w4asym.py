@@ -152,10 +152,11 @@ def _packed(N, K, order, dev):
 
 @pytest.mark.parametrize("order", [False, True])
 @pytest.mark.parametrize("dt", ["f16", "bf16"])
-@pytest.mark.parametrize("M", [1, 2, 3, 4, 8, 16, 40])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 8, 16, 24, 40])
 def test_w4a_gemm(M, dt, order):
     """Every kernel the dispatcher picks for 1 <= M <= 40 (streaming,
-    per-lane FMA, blocks of 16 rows), ragged N, with bias."""
+    per-lane FMA, blocks of 16 rows at M = 24, the matrix-core GEMM at
+    M = 40), ragged N, with bias."""
     import bit_weight_only_tq_amd as tq
     dev = require_gpu()
     N, K = 300, 1024

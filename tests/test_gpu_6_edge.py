@@ -123,7 +123,9 @@ W4_CASES = [
     ("matrix-core GEMV", 1024, 16384, 8, "f16", None),
     ("per-lane FMA", 1024, 1024, 1, "f16", "auto"),
     ("per-lane FMA", 1024, 1024, 2, "bf16", "auto"),
-    ("blocks of 16 rows", 1024, 4096, 40, "f16", "auto"),
+    ("blocks of 16 rows", 1024, 4096, 24, "f16", "auto"),
+    ("GEMM 64-row tiles, one pass", 1024, 4096, 40, "f16", None),
+    ("GEMM 64-row tiles split-K", 1024, 8192, 20, "bf16", "auto"),
 ]
 
 

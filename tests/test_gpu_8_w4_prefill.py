@@ -1,4 +1,6 @@
-"""GPU parity of the W4A16 prefill GEMM (M >= 256 on the matrix cores).
+"""GPU parity of the W4A16 matrix-core GEMM (256-row tiles from M = 256,
+64-row tiles below; split K where the tiles leave compute units idle or K
+holds more than 128 groups).
 
 Symmetric (zero point 8) and asymmetric formats, with and without
 activation order, fp16 and bf16 activations: every output at M = 2048 and
@@ -137,16 +139,23 @@ def test_w4_prefill_one_hot(dt, fmt):
     np.testing.assert_array_equal(bits16(C), to_bits(wdq[:, ks].T))
 
 
-def test_w4_prefill_rejects_long_k():
-    """More than 128 groups: the forced prefill path is refused with nothing
-    launched, the dispatcher takes the decode kernels over row blocks."""
+def test_w4_gemm_long_k_splits():
+    """More than 128 groups (the scales one split can hold): with a workspace
+    the GEMM splits K (at least two splits) and stays within the tolerance;
+    forced without one it is refused with nothing launched, and the
+    dispatcher then takes the decode kernels over row blocks."""
     import torch
     import bit_weight_only_tq_amd as tq
     dev = require_gpu()
-    K = 16384 + 128
-    assert tq.tq_select_path("w4a16", 256, 256, K) == "gemv"
-    q = torch.zeros((256, K // 8), dtype=torch.int32, device=dev)
-    s = torch.zeros((256, K // 128), dtype=torch.float16, device=dev)
-    A = torch.zeros((256, K), dtype=torch.float16, device=dev)
+    M, N, K = 300, 256, 16384 + 128
+    assert tq.tq_select_path("w4a16", M, N, K) == "gemm"
+    assert tq.w4a16_gemm_workspace_bytes(M, N, K) >= 2 * M * N * 4
+    log(f"w4 long K M={M} N={N} K={K}")
+    q, s, z, perm, wdq = _packed(N, K, "sym", dev)
+    A = synth.activations(M, K, synth.seed_for("w4lk", M, K), "f16")
+    C = tq.w4a16_gemm(A.to(dev), q, s)
+    check_close(C, A, wdq, label="w4 long K, split")
     with pytest.raises(tq.TQError, match="TQ_ERR_PATH"):
-        tq.w4a16_gemm(A, q, s, path="gemm")
+        tq.w4a16_gemm(A.to(dev), q, s, path="gemm", workspace=None)
+    C = tq.w4a16_gemm(A.to(dev)[:40], q, s, workspace=None)  # auto, no workspace: row blocks
+    check_close(C, A[:40], wdq, label="w4 long K, row blocks")
