@@ -62,7 +62,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--layers", type=int, default=32)
     ap.add_argument("--mode", default="full",
-                    choices=["full", "decode", "decodem", "decode70b", "w4", "w4act", "medium", "prefill", "w4prefill",
+                    choices=["full", "decode", "decodem", "decode70b", "w4", "w4act", "medium", "w4medium", "prefill", "w4prefill",
                              "attrib", "calib"])
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
     ap.add_argument("--unfused", action="store_true", help="decode mode: q,k,v,gate,up as separate calls")
@@ -322,6 +322,52 @@ def run_w4_decode(args, dev, Ms=(1, 4, 16), act_order=False, dt="f16", samples=N
                         "alg_gbs": round(alg * args.steps / t / 1e9, 1)}
         del g, xs, outs, ws
     del mats
+    torch.cuda.empty_cache()
+    return res
+
+
+def run_w4_medium(dev, copies=4, iters=16, samples=None):
+    """W4A16 at medium M on one Llama-3-70B layer, M = 32 and 64 (the
+    matrix-core GEMM's 64-row tiles with split K), and the decode kernels
+    over 16-row blocks beside it for comparison."""
+    import torch
+    import bit_weight_only_tq_amd as tq
+    import synth
+    stream = torch.cuda.current_stream()
+    res = {"metric": "W4A16 medium-M path, one Llama-3-70B layer", "unit": "us per call",
+           "kernel": "w4p::gemm_kernel<T, ASYM, 64> + mm::splitk_reduce_kernel"}
+    ws = torch.empty((64 << 20,), dtype=torch.uint8, device=dev)
+    for name, (N, K) in layer_shapes(True, "70b"):
+        W = synth.weights_device(N, K, synth.seed_for("benchw4m", name), dev)
+        q, s = tq.w4a16_pack(W)
+        del W
+        reps = [(q, s)] + [(q.clone(), s.clone()) for _ in range(copies - 1)]
+        for M in (32, 64):
+            A = synth.activations_device(M, K, synth.seed_for("benchw4ma", N, K, M), "f16", dev)
+            C = torch.empty((M, N), dtype=torch.float16, device=dev)
+            entry = {}
+            for path in ("gemm", "gemv"):
+                calls = [lambda qq=qq, ss=ss: tq.w4a16_gemm(A, qq, ss, out=C, workspace=ws, path=path)
+                         for qq, ss in reps]
+                for c in calls:
+                    c()
+                t = time_region(lambda: [c() for c in calls], iters, stream) / (iters * copies)
+                torch.cuda.synchronize()
+                if path == "gemm":
+                    if samples is not None:  # C holds the last copy's output
+                        samples.append(w4_sample(f"w4_medium_M{M}", A, C, reps[-1][0], reps[-1][1],
+                                                 synth.seed_for("bw4m", name, M)))
+                    flops = 2.0 * M * N * K
+                    alg = w4_bytes(M, N, K)
+                    roof_s = max(alg / (HBM_PEAK_GBS * 1e9), flops / (MFMA_PEAK_TFLOPS * 1e12))
+                    entry.update({"us": round(t * 1e6, 2), "tflops": round(flops / t / 1e12, 1),
+                                  "packed_gbs": round(q.numel() * 4 / t / 1e9, 1), "roof_us": round(roof_s * 1e6, 2),
+                                  "frac_of_roof": round(roof_s / t, 4)})
+                else:
+                    entry["row_blocks_us"] = round(t * 1e6, 2)
+            res[f"{name}_{N}x{K}_M{M}"] = entry
+            del A, C
+        del reps, q, s
     torch.cuda.empty_cache()
     return res
 
@@ -812,6 +858,9 @@ def main():
     if args.mode == "w4prefill":
         print(json.dumps({"w4a16_prefill": run_w4_prefill(dev)}), flush=True)
         return
+    if args.mode == "w4medium":
+        print(json.dumps({"w4a16_medium_m": run_w4_medium(dev)}), flush=True)
+        return
 
     graph = not args.no_graph
     fused = not args.unfused
@@ -893,6 +942,8 @@ def main():
         out["w4a16_act_decode"] = run_w4_decode(args, dev, act_order=True, samples=samples)
         log("medium M")
         out["medium_m"] = run_medium(dev, samples=samples)
+        log("W4A16 medium M")
+        out["w4a16_medium_m"] = run_w4_medium(dev, samples=samples)
         log("prefill GEMM M=4096")
         out["secondary"] = run_prefill(dev, samples=samples)
         log("W4A16 prefill GEMM")
