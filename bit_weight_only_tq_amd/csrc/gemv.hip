@@ -1908,10 +1908,59 @@ __global__ __launch_bounds__(256) void gather_columns_kernel(const uint16_t* __r
     }
 }
 
+// Large M: block b owns rows b R .. b R + R - 1, R = kGatherLdsBytes / (2 K)
+// rows (at most 8): they are copied to LDS with 16-byte loads, then each
+// thread gathers eight columns at a time from LDS (indices loaded once for
+// the block's rows) and stores 16 bytes per row.  The global traffic is the
+// rows read once and written once; the scattered reads stay on chip.  Same
+// index clamp and alignment as above; A 16-byte aligned.
+constexpr int kGatherLdsBytes = 64 << 10;
+
+__global__ __launch_bounds__(256) void gather_columns_lds_kernel(const uint16_t* __restrict__ A,
+                                                                 const int32_t* __restrict__ perm, int64_t M,
+                                                                 int64_t K, int R, uint16_t* __restrict__ out) {
+    extern __shared__ uint4 smem_gather[];
+    const uint16_t* rows = reinterpret_cast<const uint16_t*>(smem_gather);
+    const int64_t m0 = (int64_t)blockIdx.x * R;
+    const int nr = (int)(M - m0 < R ? M - m0 : R);
+    const int64_t chunks = K / 8;  // 16-byte chunks per row
+    const uint4* src = reinterpret_cast<const uint4*>(A + m0 * K);
+    for (int64_t e = threadIdx.x; e < nr * chunks; e += 256) smem_gather[e] = src[e];
+    __syncthreads();
+    for (int64_t c = threadIdx.x; c < chunks; c += 256) {
+        int32_t k[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int64_t v = perm[8 * c + j];
+            k[j] = (int32_t)(v < 0 || v >= K ? 8 * c + j : v);
+        }
+        for (int r = 0; r < nr; ++r) {
+            const uint16_t* row = rows + (int64_t)r * K;
+            uint16_t v[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[j] = row[k[j]];
+            *reinterpret_cast<uint4*>(out + (m0 + r) * K + 8 * c) =
+                make_uint4(v[0] | ((uint32_t)v[1] << 16), v[2] | ((uint32_t)v[3] << 16), v[4] | ((uint32_t)v[5] << 16),
+                           v[6] | ((uint32_t)v[7] << 16));
+        }
+    }
+}
+
 hipError_t launch_gather_columns(const uint16_t* A, const int32_t* perm, int64_t M, int64_t K, uint16_t* out,
                                  hipStream_t s) {
     if (K % 8 != 0 || (reinterpret_cast<uintptr_t>(out) & 15u) != 0) return hipErrorInvalidValue;
     if (M <= 0 || K <= 0) return hipSuccess;
+    if (M > 64 && 2 * K <= kGatherLdsBytes && (reinterpret_cast<uintptr_t>(A) & 15u) == 0) {
+        int64_t R = kGatherLdsBytes / (2 * K);
+        if (R > 8) R = 8;
+        static DeviceFlags lds_limit_set;
+        hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(&gather_columns_lds_kernel), kGatherLdsBytes,
+                                       lds_limit_set);
+        if (e != hipSuccess) return e;
+        const size_t lds = (size_t)R * (size_t)K * 2;
+        gather_columns_lds_kernel<<<(unsigned)((M + R - 1) / R), 256, lds, s>>>(A, perm, M, K, (int)R, out);
+        return hipGetLastError();
+    }
     const int R = M <= 64 ? 1 : 8;
     const int64_t gy = (M + R - 1) / R;
     const dim3 grid((unsigned)((K / 8 + 255) / 256), (unsigned)(gy < 65535 ? gy : 65535));
