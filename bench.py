@@ -800,18 +800,44 @@ def cpu_baseline(min_seconds, samples):
     }, parity
 
 
+def kernel_digest(source, spans, headers=()):
+    """sha256 of the parts of `source` that decide one kernel's HBM traffic
+    and of the headers it includes, so that edits elsewhere in the file do
+    not invalidate a measurement of it.  Each span (first, last) runs from
+    the definition of `first` (with its template line) to the lone closing
+    brace that ends the definition of `last`."""
+    import hashlib
+    lines = open(os.path.join(ROOT, source)).read().split("\n")
+    h = hashlib.sha256()
+    for first, last in spans:
+        start = next(i for i, ln in enumerate(lines) if f" {first}(" in ln and not ln.rstrip().endswith(";"))
+        if start > 0 and lines[start - 1].startswith("template"):
+            start -= 1
+        at = next(i for i in range(start, len(lines)) if f" {last}(" in lines[i])
+        end = next(i for i in range(at, len(lines)) if lines[i] == "}")
+        h.update("\n".join(lines[start:end + 1]).encode())
+    for hdr in headers:
+        h.update(open(os.path.join(ROOT, hdr), "rb").read())
+    return h.hexdigest()
+
+
+# The M = 1 ternary decode kernel: its device helpers and body, and the plan
+# and launch code that fix its grid.
+TRAFFIC_KERNEL = ("bit_weight_only_tq_amd/csrc/gemv.hip",
+                  (("sm_mma", "ternary_gemv_m1_kernel"), ("gemv_m1_plan", "launch_gemv_m1_plan")),
+                  ("bit_weight_only_tq_amd/csrc/tq_device.h",))
+
+
 def load_traffic(path):
     """HBM bytes per GEMV launch from the committed counter summary, or None
-    when it is missing or was measured on a different kernel source."""
-    import hashlib
+    when it is missing or was measured on a different kernel definition."""
     try:
         with open(path) as f:
             tj = json.load(f)
-        with open(os.path.join(ROOT, tj["kernel_source"]), "rb") as f:
-            if hashlib.sha256(f.read()).hexdigest() != tj["kernel_sha256"]:
-                return None
+        if kernel_digest(*TRAFFIC_KERNEL) != tj["kernel_digest"]:
+            return None
         return tj["hbm_bytes_per_launch"]
-    except (OSError, KeyError, ValueError):
+    except (OSError, KeyError, ValueError, StopIteration):
         return None
 
 

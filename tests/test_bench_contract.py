@@ -22,10 +22,27 @@ def test_traffic_summary_matches_kernel_or_is_dropped(tmp_path):
     v = bench.load_traffic(tj)
     assert v is None or v > 0
     bad = json.load(open(tj))
-    bad["kernel_sha256"] = "0" * 64
+    bad["kernel_digest"] = "0" * 64
     p = tmp_path / "t.json"
     p.write_text(json.dumps(bad))
     assert bench.load_traffic(str(p)) is None
+
+
+def test_traffic_digest_covers_only_the_kernel(tmp_path):
+    """The digest changes with the measured kernel's body and not with an
+    edit elsewhere in its source file."""
+    sys.path.insert(0, ROOT)
+    import bench
+    src, spans, hdrs = bench.TRAFFIC_KERNEL
+    text = open(os.path.join(ROOT, src)).read()
+    base = bench.kernel_digest(src, spans, hdrs)
+    rel = os.path.relpath(str(tmp_path / "k.hip"), ROOT)
+    (tmp_path / "k.hip").write_text(text + "\n// appended\n")
+    assert bench.kernel_digest(rel, spans, hdrs) == base
+    body = text.replace("constexpr int kRowLds = CSW * 512;", "constexpr int kRowLds = CSW * 512 ;", 1)
+    assert body != text
+    (tmp_path / "k.hip").write_text(body)
+    assert bench.kernel_digest(rel, spans, hdrs) != base
 
 
 def test_algorithmic_bytes():
