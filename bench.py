@@ -177,6 +177,25 @@ def time_region(fn, steps, stream, per_step=None):
     return start.elapsed_time(end) / 1e3
 
 
+SETTLE_SECONDS = 0.3
+
+
+def settle(fn, seconds=SETTLE_SECONDS):
+    """Untimed calls of fn for at least `seconds` of wall clock, ending with a
+    synchronize.  The part raises its shader clock only after some tens of
+    milliseconds of sustained load: a compute-bound line timed straight after
+    idle host work (packing, the previous line's checks) would catch the
+    ramp and report less than the sustained rate a serving loop sees."""
+    import torch
+    t0 = time.perf_counter()
+    while True:
+        for _ in range(4):
+            fn()
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= seconds:
+            return
+
+
 def percentiles(ms):
     """p10 / p50 / p90 of a list of per-step milliseconds."""
     v = sorted(ms)
@@ -594,8 +613,7 @@ def run_prefill(dev, iters=10, samples=None):
             C = torch.empty((M, N), dtype=A.dtype, device=dev)
             nbytes = tq.tq_gemm_workspace_bytes(M, N, K, dt)
             ws = torch.empty((nbytes,), dtype=torch.uint8, device=dev) if nbytes else None
-            for _ in range(3):
-                tq.tq_gemm(A, codes, scale, out=C, workspace=ws)
+            settle(lambda: tq.tq_gemm(A, codes, scale, out=C, workspace=ws))
             t = time_region(lambda: tq.tq_gemm(A, codes, scale, out=C, workspace=ws), iters, stream) / iters
             torch.cuda.synchronize()
             if samples is not None:
@@ -605,8 +623,7 @@ def run_prefill(dev, iters=10, samples=None):
                      "splits": nbytes // (4 * M * N) if nbytes else 1}
             if M == 4096:
                 Wd = W.to(A.dtype)
-                for _ in range(3):
-                    torch.nn.functional.linear(A, Wd)
+                settle(lambda: torch.nn.functional.linear(A, Wd))
                 td = time_region(lambda: torch.nn.functional.linear(A, Wd), iters, stream) / iters
                 entry["dense_ref_tflops"] = round(2.0 * M * N * K / td / 1e12, 1)
                 del Wd
@@ -650,8 +667,7 @@ def run_w4_prefill(dev, iters=10, samples=None):
                 call = lambda: tq.w4a16_gemm(A, qa, sca, zeros=za, perm=pa, out=C, workspace=ws)  # noqa: E731
             else:
                 call = lambda: tq.w4a16_gemm(A, q, sc, out=C, workspace=None)  # noqa: E731
-            for _ in range(3):
-                call()
+            settle(call)
             t = time_region(call, iters, stream) / iters
             torch.cuda.synchronize()
             if samples is not None:

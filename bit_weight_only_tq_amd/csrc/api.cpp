@@ -86,7 +86,7 @@ tq_status check_gemm_common(const void* A, tq_dtype dt, int64_t M, int64_t N, in
                             const uint16_t* scale, void* C) {
     if (!A || !wq || !scale || !C) return TQ_ERR_NULL;
     if (dt != TQ_F16 && dt != TQ_BF16) return TQ_ERR_DTYPE;
-    if (M <= 0 || N <= 0 || K <= 0) return TQ_ERR_SHAPE;
+    if (M <= 0 || N <= 0 || K <= 0 || K > tq::kMaxK) return TQ_ERR_SHAPE;
     if (!aligned16(A) || !aligned16(wq)) return TQ_ERR_ALIGN;
     if ((reinterpret_cast<uintptr_t>(C) & 1u) || (reinterpret_cast<uintptr_t>(scale) & 1u)) return TQ_ERR_ALIGN;
     return TQ_OK;

@@ -42,15 +42,31 @@ template <> struct Mfma<BF16> {
     }
 };
 
-// Natural-order operand pair j of a half dword of fields (see v3 below):
-// (1024 + c) - 1025 = c - 1, exact in fp16.
-__device__ __forceinline__ uint32_t nat_pair(uint32_t y, int j, uint32_t mask3, uint32_t magic_v) {
-    const uint32_t v = ((y >> (4 * j)) & mask3) | magic_v;
-    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, v) + __builtin_bit_cast(f16x2, 0xE401E401u));
+// Natural-order operand pairs of byte b of a code dword x (fields f_4b ..
+// f_4b+3 at bits 0, 2, 4, 6 of the byte): one byte permute puts the byte in
+// the low byte of both halves, a mask into 1024.0 keeps field 4b (low half)
+// and 4b+1 (high half) at bits 0 and 2, or fields 4b+2 and 4b+3 at bits 4
+// and 6, and one packed fp16 fma per pair scales each half by its own power
+// of 4 and subtracts 1024/4^s + 1: (1024 + 4^s c) / 4^s - (1024/4^s + 1) =
+// c - 1, exact.
+struct NatConsts {
+    f16x2 mul_lo, add_lo, mul_hi, add_hi;
+};
+__device__ __forceinline__ NatConsts nat_consts() {
+    return NatConsts{f16x2{(_Float16)1.0f, (_Float16)0.25f}, f16x2{(_Float16)-1025.0f, (_Float16)-257.0f},
+                     f16x2{(_Float16)0.0625f, (_Float16)0.015625f}, f16x2{(_Float16)-65.0f, (_Float16)-17.0f}};
 }
-__device__ __forceinline__ uint4 nat_quad(uint32_t y, uint32_t mask3, uint32_t magic_v) {
-    return make_uint4(nat_pair(y, 0, mask3, magic_v), nat_pair(y, 1, mask3, magic_v), nat_pair(y, 2, mask3, magic_v),
-                      nat_pair(y, 3, mask3, magic_v));
+__device__ __forceinline__ uint32_t nat_fma(uint32_t v, f16x2 mul, f16x2 add) {
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(__builtin_bit_cast(f16x2, v), mul, add));
+}
+// Operand of fields 8h .. 8h+7 of x (bytes 2h and 2h+1) in natural order.
+template <int H>
+__device__ __forceinline__ uint4 nat_quad(uint32_t x, uint32_t magic_v, const NatConsts& k) {
+    const uint32_t p0 = __builtin_amdgcn_perm(x, x, 0x0C000C00u | (uint32_t)(2 * H) * 0x00010001u);
+    const uint32_t p1 = __builtin_amdgcn_perm(x, x, 0x0C000C00u | (uint32_t)(2 * H + 1) * 0x00010001u);
+    const uint32_t mlo = sgpr_const<0x000C0003u>(), mhi = sgpr_const<0x00C00030u>();
+    return make_uint4(nat_fma((p0 & mlo) | magic_v, k.mul_lo, k.add_lo), nat_fma((p0 & mhi) | magic_v, k.mul_hi, k.add_hi),
+                      nat_fma((p1 & mlo) | magic_v, k.mul_lo, k.add_lo), nat_fma((p1 & mhi) | magic_v, k.mul_hi, k.add_hi));
 }
 
 // Workgroup barrier without a release fence: __syncthreads() would wait for
@@ -72,11 +88,12 @@ __device__ __forceinline__ void stage_barrier() {
 //  - activations: 256 rows x 64 columns per stage, natural column order,
 //    16-byte chunks XOR-swizzled (chunk c of row r at position c ^ (r % 8));
 //  - codes: 256 weight rows x 16 bytes (64 columns) per stage.
-// Codes are unpacked in registers into natural-order pairs (f_2j, f_2j+1):
-// E = x & 0x33333333 (even fields), O = (x >> 2) & 0x33333333 (odd fields),
-// Y = byte-merge(E, O) per half dword, pair j = ((Y >> 4j) & 0x00030003) |
-// 1024.0, and one packed fp16 subtract of 1025 gives the ternary value c - 1
-// itself (nat_pair).  Block tile 256 x 256 (128 x 256 for the last round of
+// Codes are unpacked in registers into natural-order pairs (f_2j, f_2j+1),
+// five VALU instructions per four codes (nat_quad): a byte permute, two
+// masks into 1024.0 and two packed fp16 fmas that leave the ternary values
+// c - 1 themselves.  DMA addresses are the tile's base in SGPRs plus fixed
+// 32-bit lane offsets, so the K loop does no 64-bit address arithmetic.
+// Block tile 256 x 256 (128 x 256 for the last round of
 // an unbalanced grid), K-step 64, eight waves (2 x 4) of 128 x 64 (64 x 64)
 // outputs; MFMA s of a K-step (s = 0, 1) takes 8-column chunk 2g + s for
 // lane group g.  The epilogue stages each wave's outputs through LDS so that
@@ -133,8 +150,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(SplitArgs sa) {
     const int64_t M = p.M, N = p.N, K = p.K;
     const int64_t rb = K / 4;
     const uint32_t magic_v = vgpr_const<kMagic2>();
-    const uint32_t mask3 = sgpr_const<0x00030003u>();
-    const uint32_t mask33 = sgpr_const<0x33333333u>();
+    const NatConsts nk_c = nat_consts();
 
     // Activation DMA: wave w fills 1-KB blocks AU w .. AU w + AU-1 of a stage
     // (8 rows each); lane l lands at chunk l % 8 of row l / 8, so it fetches
@@ -145,7 +161,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(SplitArgs sa) {
     for (int u = 0; u < AU; ++u) {
         int64_t r = 8 * (AU * wave + u) + (lane >> 3);
         if (m0 + r >= M) r = M - 1 - m0;
-        a_off[u] = (uint32_t)(r * K + 8 * ((lane & 7) ^ (lane >> 3)));
+        a_off[u] = (uint32_t)(2 * (r * K + 8 * ((lane & 7) ^ (lane >> 3))));  // bytes
     }
     // Code DMA (waves 0..3): lane l of wave w fetches the 16 bytes of weight
     // row n0 + 64w + l for the K-step.  Rows past N re-read row N-1.
@@ -161,8 +177,8 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(SplitArgs sa) {
         const int64_t k0 = (int64_t)kstep * BK;
         const uint32_t dst = lds_base + (uint32_t)(stage * kStageBytes + 1024 * AU * wave);
 #pragma unroll
-        for (int u = 0; u < AU; ++u) dma16(a_blk + k0 + a_off[u], dst + 1024u * u);
-        if (b_issuer) dma16(b_blk + k0 / 4 + b_off, lds_base + (uint32_t)(stage * kStageBytes + kABytes + 1024 * wave));
+        for (int u = 0; u < AU; ++u) dma16s(a_blk + k0, a_off[u], dst + 1024u * u);
+        if (b_issuer) dma16s(b_blk + k0 / 4, b_off, lds_base + (uint32_t)(stage * kStageBytes + kABytes + 1024 * wave));
     };
     // the stage issued before the last one has landed (per-wave DMA counts)
     auto wait_prev_stage = [&]() {
@@ -197,13 +213,9 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(SplitArgs sa) {
         // re-reads the last K-step into the stage nobody reads any more.
         issue(kb + (kt + 2 < nk ? kt + 2 : nk - 1), (kt + 2) % kStages);
         const uint8_t* sbase = lds + stage * kStageBytes;
-        uint32_t E[TN], O[TN];
+        uint32_t X[TN];
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const uint32_t x = *reinterpret_cast<const uint32_t*>(sbase + b_frag + 16 * 16 * j);
-            E[j] = x & mask33;
-            O[j] = (x >> 2) & mask33;
-        }
+        for (int j = 0; j < TN; ++j) X[j] = *reinterpret_cast<const uint32_t*>(sbase + b_frag + 16 * 16 * j);
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             const int chunk = (2 * g + s) ^ swz;
@@ -214,7 +226,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(SplitArgs sa) {
             uint4 bop[TN];
 #pragma unroll
             for (int j = 0; j < TN; ++j)
-                bop[j] = nat_quad(__builtin_amdgcn_perm(O[j], E[j], s ? 0x07060302u : 0x05040100u), mask3, magic_v);
+                bop[j] = s ? nat_quad<1>(X[j], magic_v, nk_c) : nat_quad<0>(X[j], magic_v, nk_c);
 #pragma unroll
             for (int j = 0; j < TN; ++j) {
                 const vec bf = __builtin_bit_cast(vec, bop[j]);
@@ -339,8 +351,7 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(SplitArgs sa) {
     const int ks0 = (int)((int64_t)nk * z / sa.S);
     const int ks1 = (int)((int64_t)nk * (z + 1) / sa.S);  // > ks0: S <= nk
     const uint32_t magic_v = vgpr_const<kMagic2>();
-    const uint32_t mask3 = sgpr_const<0x00030003u>();
-    const uint32_t mask33 = sgpr_const<0x33333333u>();
+    const NatConsts nk_c = nat_consts();
 
     // Activation DMA: waves 0 .. 2TM-1 fill the 1-KB blocks of a stage (8 rows
     // each); lane l lands at chunk l % 8 of row 8w + l / 8 and fetches global
@@ -350,7 +361,7 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(SplitArgs sa) {
     {
         int64_t r = 8 * (wave % (2 * TM)) + (lane >> 3);
         if (m0 + r >= M) r = M - 1 - m0;
-        a_off = (uint32_t)(r * K + 8 * ((lane & 7) ^ (lane >> 3)));
+        a_off = (uint32_t)(2 * (r * K + 8 * ((lane & 7) ^ (lane >> 3))));  // bytes
     }
     const uint16_t* a_blk = p.A + m0 * K;
     // Code DMA (waves 0..3): lane l of wave w fetches 16 bytes of weight row
@@ -365,8 +376,8 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(SplitArgs sa) {
     }
     auto issue = [&](int kstep, int stage) {
         const int64_t k0 = (int64_t)kstep * BK;
-        if (a_issuer) dma16(a_blk + k0 + a_off, lds_base + (uint32_t)(stage * kStageBytes + 1024 * wave));
-        if (b_issuer) dma16(b_blk + k0 / 4 + b_off, lds_base + (uint32_t)(stage * kStageBytes + kABytes + 1024 * wave));
+        if (a_issuer) dma16s(a_blk + k0, a_off, lds_base + (uint32_t)(stage * kStageBytes + 1024 * wave));
+        if (b_issuer) dma16s(b_blk + k0 / 4, b_off, lds_base + (uint32_t)(stage * kStageBytes + kABytes + 1024 * wave));
     };
     // the oldest stage in flight has landed: at most kAhead - 1 stages of
     // this wave's DMAs remain outstanding
@@ -395,13 +406,9 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(SplitArgs sa) {
         const int stage = it % kStages;
         issue(kt + kAhead < ks1 ? kt + kAhead : ks1 - 1, (it + kAhead) % kStages);
         const uint8_t* sbase = lds + stage * kStageBytes;
-        uint32_t E[TN], O[TN];
+        uint32_t X[TN];
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const uint32_t x = *reinterpret_cast<const uint32_t*>(sbase + b_frag + 16 * 16 * j);
-            E[j] = x & mask33;
-            O[j] = (x >> 2) & mask33;
-        }
+        for (int j = 0; j < TN; ++j) X[j] = *reinterpret_cast<const uint32_t*>(sbase + b_frag + 16 * 16 * j);
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             const int chunk = (2 * g + s) ^ swz;
@@ -412,7 +419,7 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(SplitArgs sa) {
             uint4 bop[TN];
 #pragma unroll
             for (int j = 0; j < TN; ++j)
-                bop[j] = nat_quad(__builtin_amdgcn_perm(O[j], E[j], s ? 0x07060302u : 0x05040100u), mask3, magic_v);
+                bop[j] = s ? nat_quad<1>(X[j], magic_v, nk_c) : nat_quad<0>(X[j], magic_v, nk_c);
 #pragma unroll
             for (int j = 0; j < TN; ++j) {
                 const vec bf = __builtin_bit_cast(vec, bop[j]);
@@ -580,27 +587,31 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(SplitArgs sa) {
     const int ks1 = (int)((int64_t)nk * (z + 1) / sa.S);  // > ks0: S <= nk
     const uint32_t magic_v = vgpr_const<kMagic2>();
 
-    const uint16_t* a_src[TM];
+    // byte offsets of each lane's rows from the tile's first activation row
+    // and first weight row
+    const uint16_t* a_blk = p.A + m0 * K;
+    uint32_t a_dma[TM];
 #pragma unroll
     for (int u = 0; u < TM; ++u) {
         const int r = 2 * (wave * TM + u) + (lane >> 5);
-        const int64_t m = m0 + r < M ? m0 + r : M - 1;
-        a_src[u] = p.A + m * K + 8 * ((lane & 31) ^ (r & 15));
+        const int64_t m = m0 + r < M ? r : M - 1 - m0;
+        a_dma[u] = (uint32_t)(2 * (m * K + 8 * ((lane & 31) ^ (r & 15))));
     }
-    const uint8_t* b_src[2];
+    const uint8_t* b_blk = static_cast<const uint8_t*>(p.wq) + n0 * rb;
+    uint32_t b_dma[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
         const int r = 16 * (2 * wave + u) + (lane >> 2);
-        const int64_t n = n0 + r < N ? n0 + r : N - 1;
-        b_src[u] = static_cast<const uint8_t*>(p.wq) + n * rb + 16 * ((lane & 3) ^ ((r >> 2) & 3));
+        const int64_t n = n0 + r < N ? r : N - 1 - n0;
+        b_dma[u] = (uint32_t)(n * rb + 16 * ((lane & 3) ^ ((r >> 2) & 3)));
     }
     auto issue = [&](int kstep, int slot) {
         const uint32_t st = lds_base + (uint32_t)(slot * kStageBytes);
 #pragma unroll
-        for (int u = 0; u < TM; ++u) dma16(a_src[u] + (int64_t)kstep * BK, st + 1024u * (wave * TM + u));
+        for (int u = 0; u < TM; ++u) dma16s(a_blk + (int64_t)kstep * BK, a_dma[u], st + 1024u * (wave * TM + u));
 #pragma unroll
         for (int u = 0; u < 2; ++u)
-            dma16(b_src[u] + (int64_t)kstep * (BK / 4), st + kABytes + 1024u * (2 * wave + u));
+            dma16s(b_blk + (int64_t)kstep * (BK / 4), b_dma[u], st + kABytes + 1024u * (2 * wave + u));
     };
     auto clamp_step = [&](int k) { return k < ks1 ? k : ks1 - 1; };
 
@@ -837,25 +848,25 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(SplitArgs sa) {
     for (int u = 0; u < AU; ++u) {
         int64_t r = 8 * (AU * wave + u) + (lane >> 3);
         if (m0 + r >= M) r = M - 1 - m0;
-        a_off[u] = (uint32_t)(r * K + 8 * ((lane & 7) ^ (lane >> 3)));
+        a_off[u] = (uint32_t)(2 * (r * K + 8 * ((lane & 7) ^ (lane >> 3))));  // bytes
     }
     // Code DMA (waves 0..3, 256 lanes): lane L = 64 w + l fetches bytes
     // 16 (L % 2) .. +15 of the K-step's 32 bytes of weight row n0 + L / 2,
     // landing at 32 (L / 2) + 16 (L % 2).  Rows past N re-read row N-1.
-    const uint8_t* b_blk = static_cast<const uint8_t*>(p.wq);
+    const uint8_t* b_blk = static_cast<const uint8_t*>(p.wq) + n0 * rowb;
     const bool b_issuer = wave < 4;
-    int64_t b_off;
+    uint32_t b_off;
     {
         const int L = 64 * (wave & 3) + lane;
-        const int64_t n = n0 + (L >> 1) < N ? n0 + (L >> 1) : N - 1;
-        b_off = n * rowb + 16 * (L & 1);
+        const int64_t n = n0 + (L >> 1) < N ? (L >> 1) : N - 1 - n0;
+        b_off = (uint32_t)(n * rowb + 16 * (L & 1));
     }
     auto issue = [&](int kstep, int stage) {
         const int64_t k0 = (int64_t)kstep * BK;
         const uint32_t dst = lds_base + (uint32_t)(stage * kStageBytes + 1024 * AU * wave);
 #pragma unroll
-        for (int u = 0; u < AU; ++u) dma16(a_blk + k0 + a_off[u], dst + 1024u * u);
-        if (b_issuer) dma16(b_blk + b_off + k0 / 2, lds_base + (uint32_t)(stage * kStageBytes + kABytes + 1024 * wave));
+        for (int u = 0; u < AU; ++u) dma16s(a_blk + k0, a_off[u], dst + 1024u * u);
+        if (b_issuer) dma16s(b_blk + k0 / 2, b_off, lds_base + (uint32_t)(stage * kStageBytes + kABytes + 1024 * wave));
     };
     auto wait_prev_stage = [&]() {
         if (b_issuer) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(AU + 1) : "memory");

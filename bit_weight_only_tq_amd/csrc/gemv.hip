@@ -670,7 +670,7 @@ __global__ __launch_bounds__(1024) void ternary_gemv_stream_kernel(SplitArgs sa)
             const int r = r0 < M ? r0 : M - 1;
             const int piece = (lane & 31) ^ (r0 & 15);
             const uint32_t off = (uint32_t)r * (uint32_t)(2 * K) + 16u * (uint32_t)piece;
-            dma16(a_cs + off, area_lds + (uint32_t)(s * MR * 512 + e * 1024));
+            dma16s(a_cs, off, area_lds + (uint32_t)(s * MR * 512 + e * 1024));
         }
     }
     // 2. code loads of all row-blocks, in the order step 4 consumes them (rows
@@ -1128,7 +1128,7 @@ __global__ __launch_bounds__(1024) void w4_gemv_stream_kernel(SplitArgs sa) {
             const int r = r0 < M ? r0 : M - 1;
             const int piece = (lane & 15) ^ (r0 & 15);
             const uint32_t off = (uint32_t)r * (uint32_t)(2 * K) + 16u * (uint32_t)piece;
-            dma16(a_g + off, area_lds + (uint32_t)(s * MR * 256 + e * 1024));
+            dma16s(a_g, off, area_lds + (uint32_t)(s * MR * 256 + e * 1024));
         }
     }
     // 2. code words of all row-blocks (rows past N re-read row N-1, groups

@@ -256,6 +256,12 @@ __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_addr) {
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                  :: "v"(gptr), "s"(lds_addr) : "memory", "m0");
 }
+// The same from a wave-uniform base address (an SGPR pair) plus a 32-bit
+// per-lane byte offset: no 64-bit vector address arithmetic per load.
+__device__ __forceinline__ void dma16s(const void* base, uint32_t off, uint32_t lds_addr) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :: "v"(off), "s"(base), "s"(lds_addr) : "memory", "m0");
+}
 
 // Sum over the 16 lanes of each DPP row (lanes 16r .. 16r+15); every lane of
 // the row receives its row's total.  Steps: swap neighbours, swap pairs,

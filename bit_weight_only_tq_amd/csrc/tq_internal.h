@@ -77,6 +77,9 @@ hipError_t launch_splitk_reduce(const SplitArgs& sa, hipStream_t s);  // gemm.hi
 
 // gemv.hip: small M (<= kGemvMaxM), weights streamed once per call.
 constexpr int kGemvMaxM = 16;
+// Largest K of a product call: the tiled kernels address up to 256 rows of
+// a tile from a uniform base with 32-bit byte offsets (256 * 2K bytes).
+constexpr int64_t kMaxK = (int64_t)1 << 22;
 // With a workspace of gemv_workspace_bytes() the streaming kernel may split
 // K (long-K, short-N shapes); without one it never does.
 size_t gemv_workspace_bytes(const GemmArgs& a);

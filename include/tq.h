@@ -155,7 +155,9 @@ tq_status w4a16_unpack(const int32_t* qweight, const uint16_t* scales_f16,
  *          nearest even; overflow gives +-inf.
  * C[m, n] = scale[n] * sum_k A[m, k] * t[n, k] + bias[n]: the scale is
  * applied after accumulation (ternary page, section 4.2).  Requires
- * K % 64 == 0 (rows are whole 16-byte chunks).  A row of codes containing the
+ * K % 64 == 0 (rows are whole 16-byte chunks) and K <= 2^22 (every product
+ * call: tiles address their rows with 32-bit byte offsets; TQ_ERR_SHAPE
+ * beyond).  A row of codes containing the
  * unused field 0b11 gives an unspecified result.  Asynchronous; allocates
  * nothing; graph-capturable.
  */
@@ -233,7 +235,8 @@ size_t tq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, tq_dtype dt, tq_
 /*
  * w4a16_gemm - C = A * dequant(qweight, scales)^T (+ bias), fp32 accumulation.
  *   qweight [N, K/8] int32 and scales_f16 [N, K/128] as written by
- *   w4a16_pack; group_size must be 128; K % 128 == 0.
+ *   w4a16_pack; group_size must be 128; K % 128 == 0; K <= 2^22 as for
+ *   tq_gemm.
  * C[m, n] = sum_g s[n, g] * sum_{k in g} A[m, k] * (q[n, k] - 8) + bias[n]:
  * the group scale multiplies each group's fp32 partial sum.  Other arguments
  * as tq_gemm.  From M = 33 (M = 17 when K >= 8192), or with TQ_PATH_GEMM, a

@@ -145,6 +145,7 @@ MIS = V(0x10002)           # 2-byte aligned only
     ((FAKE, 0, 1, -5, 64, FAKE, FAKE, None, FAKE, None), "TQ_ERR_SHAPE"),
     ((FAKE, 0, 1, 64, 0, FAKE, FAKE, None, FAKE, None), "TQ_ERR_SHAPE"),
     ((FAKE, 0, 1, 64, 96, FAKE, FAKE, None, FAKE, None), "TQ_ERR_SHAPE"),   # K % 64 != 0
+    ((FAKE, 0, 1, 64, (1 << 22) + 64, FAKE, FAKE, None, FAKE, None), "TQ_ERR_SHAPE"),  # K > 2^22
     ((MIS, 0, 1, 64, 64, FAKE, FAKE, None, FAKE, None), "TQ_ERR_ALIGN"),
     ((FAKE, 0, 1, 64, 64, MIS, FAKE, None, FAKE, None), "TQ_ERR_ALIGN"),
     ((FAKE, 0, 1, 64, 64, FAKE, FAKE, None, V(0x10001), None), "TQ_ERR_ALIGN"),
@@ -249,6 +250,7 @@ def test_tq_gemm_ex_bad_path(lib):
 @pytest.mark.parametrize("args, want", [
     ((FAKE, 0, 1, 64, 128, FAKE, FAKE, 64, None, FAKE, None), "TQ_ERR_GROUP"),
     ((FAKE, 0, 1, 64, 192, FAKE, FAKE, 128, None, FAKE, None), "TQ_ERR_SHAPE"),
+    ((FAKE, 0, 1, 64, (1 << 22) + 128, FAKE, FAKE, 128, None, FAKE, None), "TQ_ERR_SHAPE"),
     ((None, 0, 1, 64, 128, FAKE, FAKE, 128, None, FAKE, None), "TQ_ERR_NULL"),
     ((FAKE, 2, 1, 64, 128, FAKE, FAKE, 128, None, FAKE, None), "TQ_ERR_DTYPE"),
 ])
