@@ -217,10 +217,13 @@ def run_decode(args, dev, fused, graph, model="8b", layers=None, steps=None, M=1
     xs = {K: synth.activations_device(M, K, synth.seed_for("benchx", K, M), dt, dev) for K in {m[2] for m in mats}}
     odt = torch.float16 if dt == "f16" else torch.bfloat16
     outs = [torch.empty((M, m[1]), dtype=odt, device=dev) for m in mats]
+    # one workspace for every call of the step (they run in stream order), its
+    # arrival counters zeroed once, as a serving loop would hold it
+    ws = tq.new_workspace(max(tq.tq_gemm_workspace_bytes(M, m[1], m[2], dt) for m in mats), dev)
 
     def step():
         for i, (name, N, K, codes, scale) in enumerate(mats):
-            tq.tq_gemm(xs[K], codes, scale, out=outs[i])
+            tq.tq_gemm(xs[K], codes, scale, out=outs[i], workspace=ws)
 
     run = step
     if graph:
@@ -303,17 +306,20 @@ def run_w4_decode(args, dev, Ms=(1, 4, 16), act_order=False, dt="f16", samples=N
         xs = {K: synth.activations_device(M, K, synth.seed_for("benchw4x", K, M), dt, dev) for K in {m[1] for m in mats}}
         odt = torch.float16 if dt == "f16" else torch.bfloat16
         outs = [torch.empty((M, m[0]), dtype=odt, device=dev) for m in mats]
-        ws = None
-        if act_order:  # one workspace for every call: they run in order on one stream
-            nb = max(tq.w4a16_gemm_asym_workspace_bytes(M, m[0], m[1], with_perm=True) for m in mats)
-            ws = torch.empty((nb,), dtype=torch.uint8, device=dev)
+        # one workspace for every call (they run in order on one stream), its
+        # arrival counters zeroed once
+        if act_order:
+            nb = max(tq.w4a16_gemm_asym_workspace_bytes(M, m[0], m[1], dt, with_perm=True) for m in mats)
+        else:
+            nb = max(tq.w4a16_gemm_workspace_bytes(M, m[0], m[1], dt) for m in mats)
+        ws = tq.new_workspace(nb, dev)
 
         def step():
             for i, (N, K, q, sc, zp, perm) in enumerate(mats):
                 if act_order:
                     tq.w4a16_gemm(xs[K], q, sc, out=outs[i], zeros=zp, perm=perm, workspace=ws)
                 else:
-                    tq.w4a16_gemm(xs[K], q, sc, out=outs[i])
+                    tq.w4a16_gemm(xs[K], q, sc, out=outs[i], workspace=ws)
 
         g = torch.cuda.CUDAGraph()
         side = torch.cuda.Stream()
@@ -355,7 +361,7 @@ def run_w4_medium(dev, copies=4, iters=16, samples=None):
     stream = torch.cuda.current_stream()
     res = {"metric": "W4A16 medium-M path, one Llama-3-70B layer", "unit": "us per call",
            "kernel": "w4p::gemm_kernel<T, ASYM, 64> + mm::splitk_reduce_kernel"}
-    ws = torch.empty((64 << 20,), dtype=torch.uint8, device=dev)
+    ws = tq.new_workspace(64 << 20, dev)
     for name, (N, K) in layer_shapes(True, "70b"):
         W = synth.weights_device(N, K, synth.seed_for("benchw4m", name), dev)
         q, s = tq.w4a16_pack(W)
@@ -412,7 +418,7 @@ def run_medium(dev, copies=8, iters=16, samples=None):
             # the library pairs the activations once per call into the
             # workspace (after the split partials) when N K >= 200 * 2^20
             pair_b = M * K * 2 if K % 256 == 0 and N * K >= (200 << 20) else 0
-            ws = torch.empty((max(nbytes, 16),), dtype=torch.uint8, device=dev)
+            ws = tq.new_workspace(nbytes, dev)
             calls = [lambda c=c, s_=s_: tq.tq_gemm(A, c, s_, out=C, workspace=ws) for c, s_ in reps]
             for c in calls:
                 c()
@@ -427,7 +433,7 @@ def run_medium(dev, copies=8, iters=16, samples=None):
             res[f"{name}_{N}x{K}_M{M}"] = {"us": round(t * 1e6, 2), "tflops": round(flops / t / 1e12, 1),
                                            "packed_gbs": round(codes.numel() / t / 1e9, 1),
                                            "roof_us": round(roof_s * 1e6, 2), "frac_of_roof": round(roof_s / t, 4),
-                                           "splits": max(1, (nbytes - pair_b) // (4 * M * N)),
+                                           "splits": max(1, (nbytes - tq.TQ_WORKSPACE_FLAG_BYTES - pair_b) // (4 * M * N)),
                                            "paired_activations": pair_b > 0}
             del A, C, ws
         del reps, codes, scale
@@ -612,7 +618,7 @@ def run_prefill(dev, iters=10, samples=None):
             A = synth.activations_device(M, K, synth.seed_for("benchpfa", N, K, dt), dt, dev)
             C = torch.empty((M, N), dtype=A.dtype, device=dev)
             nbytes = tq.tq_gemm_workspace_bytes(M, N, K, dt)
-            ws = torch.empty((nbytes,), dtype=torch.uint8, device=dev) if nbytes else None
+            ws = tq.new_workspace(nbytes, dev)
             settle(lambda: tq.tq_gemm(A, codes, scale, out=C, workspace=ws))
             t = time_region(lambda: tq.tq_gemm(A, codes, scale, out=C, workspace=ws), iters, stream) / iters
             torch.cuda.synchronize()
@@ -620,7 +626,7 @@ def run_prefill(dev, iters=10, samples=None):
                 samples.append(ternary_sample(f"prefill_{dt}_M{M}", A, C, codes, scale,
                                               synth.seed_for("bsp", N, K, M, dt)))
             entry = {"ms": round(t * 1e3, 4), "tflops": round(2.0 * M * N * K / t / 1e12, 1),
-                     "splits": nbytes // (4 * M * N) if nbytes else 1}
+                     "splits": (nbytes - tq.TQ_WORKSPACE_FLAG_BYTES) // (4 * M * N) if nbytes else 1}
             if M == 4096:
                 Wd = W.to(A.dtype)
                 settle(lambda: torch.nn.functional.linear(A, Wd))
@@ -663,7 +669,7 @@ def run_w4_prefill(dev, iters=10, samples=None):
             C = torch.empty((M, N), dtype=A.dtype, device=dev)
             if act:
                 nb = tq.w4a16_gemm_asym_workspace_bytes(M, N, K, dt, with_perm=True)
-                ws = torch.empty((nb,), dtype=torch.uint8, device=dev)
+                ws = tq.new_workspace(nb, dev)
                 call = lambda: tq.w4a16_gemm(A, qa, sca, zeros=za, perm=pa, out=C, workspace=ws)  # noqa: E731
             else:
                 call = lambda: tq.w4a16_gemm(A, q, sc, out=C, workspace=None)  # noqa: E731

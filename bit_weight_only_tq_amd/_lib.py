@@ -253,6 +253,23 @@ def w4a16_unpack_asym(qweight, scales, zeros, K: int, perm=None, group_size: int
 
 # -------------------------------------------------------------------- apply
 
+# Bytes of split arrival counters at the front of every workspace (include/tq.h)
+TQ_WORKSPACE_FLAG_BYTES = 16384
+
+
+def new_workspace(nbytes: int, device):
+    """A device workspace of nbytes bytes from torch's allocator (None for 0)
+    whose arrival counters, the first TQ_WORKSPACE_FLAG_BYTES bytes, are zero
+    (the library leaves them zero after every call, so a reused workspace
+    needs this once)."""
+    import torch
+    if not nbytes:
+        return None
+    ws = torch.empty((nbytes,), dtype=torch.uint8, device=device)
+    ws[:TQ_WORKSPACE_FLAG_BYTES].zero_()
+    return ws
+
+
 def tq_gemm_workspace_bytes(M: int, N: int, K: int, dtype: str = "f16", path: str = "auto") -> int:
     """Bytes of workspace tq_gemm_ws uses for its fastest schedule (0: none)."""
     d = {"f16": TQ_F16, "bf16": TQ_BF16}[dtype]
@@ -263,8 +280,10 @@ def tq_gemm(A, codes, scale, bias=None, out=None, path: str = "auto", workspace=
     """C = A @ dequant(codes, scale)^T (+ bias); A [M, K] fp16/bf16.
 
     workspace: "auto" takes the bytes tq_gemm_workspace_bytes asks for from
-    torch's allocator (stream-ordered, so overlapping calls never share it);
-    None runs without one; or a contiguous device tensor."""
+    torch's allocator (stream-ordered, so overlapping calls never share it)
+    and zeroes its arrival counters; None runs without one; or a contiguous
+    device tensor whose first TQ_WORKSPACE_FLAG_BYTES bytes are zero (see
+    new_workspace)."""
     import torch
     M, K = _check_activations(A)
     N = _ternary_layout(codes, scale, K).N
@@ -274,7 +293,7 @@ def tq_gemm(A, codes, scale, bias=None, out=None, path: str = "auto", workspace=
     C = out if out is not None else torch.empty((M, N), dtype=A.dtype, device=A.device)
     if isinstance(workspace, str):
         nbytes = int(load().tq_gemm_workspace_bytes(M, N, K, dt, PATHS[path]))
-        workspace = torch.empty((nbytes,), dtype=torch.uint8, device=A.device) if nbytes else None
+        workspace = new_workspace(nbytes, A.device)
     ws_bytes = 0
     if workspace is not None:
         _need_cuda(A, workspace)
@@ -332,7 +351,7 @@ def w4a16_gemm(A, qweight, scales, bias=None, out=None, group_size: int = 128, p
             nbytes = int(load().w4a16_gemm_asym_workspace_bytes(M, N, K, dt, group_size, 1 if perm is not None else 0))
         else:
             nbytes = int(load().w4a16_gemm_workspace_bytes(M, N, K, dt, group_size))
-        workspace = torch.empty((nbytes,), dtype=torch.uint8, device=A.device) if nbytes else None
+        workspace = new_workspace(nbytes, A.device)
     ws_bytes = 0
     if workspace is not None:
         _need_cuda(A, workspace)

@@ -94,6 +94,26 @@ tq_status check_gemm_common(const void* A, tq_dtype dt, int64_t M, int64_t N, in
 
 tq_status from_hip(hipError_t e) { return e == hipSuccess ? TQ_OK : TQ_ERR_HIP; }
 
+// A caller workspace: tq::kFlagBytes of split arrival counters at its front
+// (zero when first used; every call leaves them zero), then the bytes for
+// partial sums and staging.  A workspace smaller than the counters counts as
+// none.
+struct Carved {
+    uint32_t* flags = nullptr;
+    void* data = nullptr;
+    size_t bytes = 0;
+};
+Carved carve(void* ws, size_t bytes) {
+    Carved c;
+    if (!ws || bytes < tq::kFlagBytes) return c;
+    c.flags = static_cast<uint32_t*>(ws);
+    c.bytes = bytes - tq::kFlagBytes;
+    if (c.bytes) c.data = static_cast<uint8_t*>(ws) + tq::kFlagBytes;
+    return c;
+}
+// Caller bytes for `data` bytes of partials and staging (0: no workspace).
+size_t with_flags(size_t data) { return data ? tq::kFlagBytes + data : 0; }
+
 }  // namespace
 
 extern "C" {
@@ -140,13 +160,13 @@ tq_path tq_select_path(int format, int64_t M, int64_t N, int64_t K, tq_dtype dt)
 }
 
 size_t tq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, tq_dtype dt, tq_path path) {
-    if (M <= 0 || N <= 0 || K <= 0 || K % 64 != 0) return 0;
+    if (M <= 0 || N <= 0 || K <= 0 || K % 64 != 0 || K > tq::kMaxK) return 0;
     if (path == TQ_PATH_AUTO) path = tq_select_path(0, M, N, K, dt);
-    if (path == TQ_PATH_STREAM_MFMA) return tq::medium_m_workspace_bytes(M, N, K, tq::compute_units());
-    if (path == TQ_PATH_GEMM) return tq::gemm_workspace_bytes(M, N, K, tq::compute_units());
+    if (path == TQ_PATH_STREAM_MFMA) return with_flags(tq::medium_m_workspace_bytes(M, N, K, tq::compute_units()));
+    if (path == TQ_PATH_GEMM) return with_flags(tq::gemm_workspace_bytes(M, N, K, tq::compute_units()));
     if (path == TQ_PATH_GEMV && M <= kGemvMaxM) {
         const tq::GemmArgs a{nullptr, dt == TQ_BF16 ? 1 : 0, M, N, K, nullptr, nullptr, nullptr, nullptr};
-        return tq::gemv_workspace_bytes(a);
+        return with_flags(tq::gemv_workspace_bytes(a));
     }
     return 0;
 }
@@ -233,16 +253,15 @@ tq_status tq_gemm_ws(const void* A, tq_dtype dt, int64_t M, int64_t N, int64_t K
     if (path == TQ_PATH_AUTO) path = tq_select_path(0, M, N, K, dt);
     tq::GemmArgs a{static_cast<const uint16_t*>(A), dt == TQ_BF16 ? 1 : 0, M, N, K, codes, scale_f16,
                    static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(C)};
+    const Carved w = carve(workspace, workspace_bytes);
     switch (path) {
         case TQ_PATH_GEMV:
             if (M > kGemvMaxM) return TQ_ERR_PATH;
-            return from_hip(tq::launch_ternary_gemv(a, workspace, workspace ? workspace_bytes : 0, stream));
+            return from_hip(tq::launch_ternary_gemv(a, w.data, w.bytes, stream, w.flags));
         case TQ_PATH_STREAM_MFMA:
-            return from_hip(tq::launch_ternary_medium(a, workspace, workspace ? workspace_bytes : 0,
-                                                      tq::compute_units(), stream));
+            return from_hip(tq::launch_ternary_medium(a, w.data, w.bytes, tq::compute_units(), stream));
         case TQ_PATH_GEMM:
-            return from_hip(tq::launch_ternary_gemm(a, workspace, workspace ? workspace_bytes : 0,
-                                                    tq::compute_units(), stream));
+            return from_hip(tq::launch_ternary_gemm(a, w.data, w.bytes, tq::compute_units(), stream, w.flags));
         default:
             return TQ_ERR_PATH;
     }
@@ -278,16 +297,16 @@ namespace {
 // kernels over blocks of 16 rows when the dispatcher chose it, and is
 // refused when the caller forced it.
 tq_status launch_w4_path(const tq::GemmArgs& a, tq_path path, bool chosen, void* workspace, size_t wsb,
-                         hipStream_t stream) {
+                         hipStream_t stream, uint32_t* flags) {
     switch (path) {
         case TQ_PATH_GEMV:
-            if (a.M > kGemvMaxM) return from_hip(tq::launch_w4_gemm(a, workspace, wsb, stream));
-            return from_hip(tq::launch_w4_gemv(a, workspace, wsb, stream));
+            if (a.M > kGemvMaxM) return from_hip(tq::launch_w4_gemm(a, workspace, wsb, stream, flags));
+            return from_hip(tq::launch_w4_gemv(a, workspace, wsb, stream, flags));
         case TQ_PATH_GEMM:
             if (tq::w4_prefill_ok(a, wsb)) return from_hip(tq::launch_w4_prefill(a, workspace, wsb, stream));
             if (!chosen) return TQ_ERR_PATH;
-            if (a.M > kGemvMaxM) return from_hip(tq::launch_w4_gemm(a, workspace, wsb, stream));
-            return from_hip(tq::launch_w4_gemv(a, workspace, wsb, stream));
+            if (a.M > kGemvMaxM) return from_hip(tq::launch_w4_gemm(a, workspace, wsb, stream, flags));
+            return from_hip(tq::launch_w4_gemv(a, workspace, wsb, stream, flags));
         default:
             return TQ_ERR_PATH;
     }
@@ -307,12 +326,13 @@ tq_status w4a16_gemm_ws(const void* A, tq_dtype dt, int64_t M, int64_t N, int64_
     if (chosen) path = tq_select_path(1, M, N, K, dt);
     tq::GemmArgs a{static_cast<const uint16_t*>(A), dt == TQ_BF16 ? 1 : 0, M, N, K, qweight, scales_f16,
                    static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(C)};
-    const size_t wsb = workspace ? workspace_bytes : 0;
-    return launch_w4_path(a, path, chosen, workspace, wsb, stream);
+    const Carved w = carve(workspace, workspace_bytes);
+    return launch_w4_path(a, path, chosen, w.data, w.bytes, stream, w.flags);
 }
 
-size_t w4a16_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, tq_dtype dt, int64_t group_size) {
-    if (M <= 0 || N <= 0 || K <= 0 || K % 128 != 0 || group_size != 128) return 0;
+namespace {
+// Bytes of partial sums a W4A16 call uses for its fastest schedule (no counters).
+size_t w4_data_bytes(int64_t M, int64_t N, int64_t K, tq_dtype dt) {
     if (tq_select_path(1, M, N, K, dt) == TQ_PATH_GEMM) return tq::w4_gemm_workspace_bytes(M, N, K, tq::compute_units());
     const tq::GemmArgs a{nullptr, dt == TQ_BF16 ? 1 : 0, M < kGemvMaxM ? M : kGemvMaxM, N, K,
                          nullptr, nullptr, nullptr, nullptr};
@@ -324,6 +344,12 @@ size_t w4a16_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, tq_dtype dt, 
         if (bt > b) b = bt;
     }
     return b;
+}
+}  // namespace
+
+size_t w4a16_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, tq_dtype dt, int64_t group_size) {
+    if (M <= 0 || N <= 0 || K <= 0 || K % 128 != 0 || K > tq::kMaxK || group_size != 128) return 0;
+    return with_flags(w4_data_bytes(M, N, K, dt));
 }
 
 tq_status w4a16_gemm_ex(const void* A, tq_dtype dt, int64_t M, int64_t N, int64_t K, const int32_t* qweight,
@@ -385,8 +411,8 @@ size_t gather_bytes(int64_t M, int64_t K) { return ((size_t)M * (size_t)K * 2 + 
 
 size_t w4a16_gemm_asym_workspace_bytes(int64_t M, int64_t N, int64_t K, tq_dtype dt, int64_t group_size,
                                        int with_perm) {
-    if (M <= 0 || N <= 0 || K <= 0 || K % 128 != 0 || group_size != 128) return 0;
-    return (with_perm ? gather_bytes(M, K) : 0) + w4a16_gemm_workspace_bytes(M, N, K, dt, group_size);
+    if (M <= 0 || N <= 0 || K <= 0 || K % 128 != 0 || K > tq::kMaxK || group_size != 128) return 0;
+    return with_flags((with_perm ? gather_bytes(M, K) : 0) + w4_data_bytes(M, N, K, dt));
 }
 
 tq_status w4a16_gemm_asym(const void* A, tq_dtype dt, int64_t M, int64_t N, int64_t K, const int32_t* qweight,
@@ -404,8 +430,9 @@ tq_status w4a16_gemm_asym(const void* A, tq_dtype dt, int64_t M, int64_t N, int6
     if (chosen) path = tq_select_path(1, M, N, K, dt);
     if (path != TQ_PATH_GEMV && path != TQ_PATH_GEMM) return TQ_ERR_PATH;
     const uint16_t* a_eff = static_cast<const uint16_t*>(A);
-    uint8_t* ws = static_cast<uint8_t*>(workspace);
-    size_t wsb = workspace ? workspace_bytes : 0;
+    const Carved w = carve(workspace, workspace_bytes);  // counters, then [gathered activations][partials]
+    uint8_t* ws = static_cast<uint8_t*>(w.data);
+    size_t wsb = w.bytes;
     {  // a forced GEMM path that cannot run is refused before anything is launched
         const tq::GemmArgs probe{nullptr, dt == TQ_BF16 ? 1 : 0, M, N, K, nullptr, nullptr, nullptr, nullptr};
         const size_t gb = perm ? gather_bytes(M, K) : 0;
@@ -423,7 +450,7 @@ tq_status w4a16_gemm_asym(const void* A, tq_dtype dt, int64_t M, int64_t N, int6
     tq::GemmArgs a{a_eff, dt == TQ_BF16 ? 1 : 0, M, N, K, qweight, scales_f16,
                    static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(C), zeros};
     void* rest = wsb ? ws : nullptr;
-    return launch_w4_path(a, path, chosen, rest, wsb, stream);
+    return launch_w4_path(a, path, chosen, rest, wsb, stream, w.flags);
 }
 
 tq_status w4a16_gemm(const void* A, tq_dtype dt, int64_t M, int64_t N, int64_t K, const int32_t* qweight,

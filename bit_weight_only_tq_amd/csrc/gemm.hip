@@ -252,9 +252,52 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(SplitArgs sa) {
 #pragma unroll
                 for (int j = 0; j < TN; ++j) {
                     const int64_t n = n0 + wn * WN + 16 * j + i16;
-                    if (n < N) ws[m * N + n] = acc[i][j][r] * Mfma<T>::kUnit;
+                    if (n < N) store_partial(ws + m * N + n, acc[i][j][r] * Mfma<T>::kUnit);
                 }
             }
+        // the last split of this tile to finish sums the partials and finishes it
+        if (!sa.flags || !split_last_arrival(sa.flags, blockIdx.y * gridDim.x + blockIdx.x, sa.S,
+                                             reinterpret_cast<uint32_t*>(lds)))
+            return;
+        float scz[TN], biz[TN];
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int64_t n = n0 + wn * WN + 16 * j + i16;
+            const int64_t nc = n < N ? n : N - 1;
+            scz[j] = f16_bits_to_f32(p.scale[nc]);
+            biz[j] = p.bias ? T::to_f32(p.bias[nc]) : 0.0f;
+        }
+        // two m-tiles (32 outputs) per batch, both splits of a batch in flight
+        const float* base = sa.ws + m0 * N + n0;
+        constexpr int IB = TM < 2 ? TM : 2, E = IB * 4 * TN;
+#pragma unroll
+        for (int i0 = 0; i0 < TM; i0 += IB) {
+            uint32_t off[E];
+#pragma unroll
+            for (int ii = 0; ii < IB; ++ii)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+#pragma unroll
+                    for (int j = 0; j < TN; ++j) {
+                        const int64_t m = m0 + wm * WM + 16 * (i0 + ii) + 4 * g + r;
+                        const int64_t n = n0 + wn * WN + 16 * j + i16;
+                        off[(ii * 4 + r) * TN + j] = (uint32_t)(((m < M ? m : M - 1) - m0) * N + ((n < N ? n : N - 1) - n0));
+                    }
+            float sum[E];
+            split_sums<E, 2>(base, M * N, off, sa.S, sum);
+#pragma unroll
+            for (int ii = 0; ii < IB; ++ii)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int64_t m = m0 + wm * WM + 16 * (i0 + ii) + 4 * g + r;
+                    if (m >= M) continue;
+#pragma unroll
+                    for (int j = 0; j < TN; ++j) {
+                        const int64_t n = n0 + wn * WN + 16 * j + i16;
+                        if (n < N) p.C[m * ldc + n] = T::from_f32_fast(sum[(ii * 4 + r) * TN + j] * scz[j] + biz[j]);
+                    }
+                }
+        }
         return;
     }
 
@@ -1024,9 +1067,11 @@ static hipError_t launch_v3(const SplitArgs& sa, hipStream_t s) {
     if (e != hipSuccess) return e;
     const GemmArgs& a = sa.g;
     const dim3 grid((unsigned)((a.N + v3::BN - 1) / v3::BN), (unsigned)((a.M + BM - 1) / BM), (unsigned)sa.S);
-    v3::gemm_kernel<T, BM><<<grid, v3::kThreads, G::kLdsBytes, s>>>(sa);
+    SplitArgs k = sa;
+    k.flags = split_flags(sa.flags, sa.S, (int64_t)grid.x * grid.y);
+    v3::gemm_kernel<T, BM><<<grid, v3::kThreads, G::kLdsBytes, s>>>(k);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    if (sa.S > 1) e = launch_splitk_reduce(sa, s);
+    if (sa.S > 1 && !k.flags) e = launch_splitk_reduce(sa, s);
     return e;
 }
 
@@ -1097,9 +1142,10 @@ size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int compute_units) 
 // Large M with an optional workspace: the split count of gemm_splits when
 // `workspace` holds gemm_workspace_bytes(), a single pass over K otherwise.
 hipError_t launch_ternary_gemm(const GemmArgs& a, void* workspace, size_t workspace_bytes, int compute_units,
-                               hipStream_t s) {
+                               hipStream_t s, uint32_t* flags) {
     // the C ABI guarantees K % 64 == 0 (whole 16-byte code chunks per row)
     SplitArgs sa{a, static_cast<float*>(workspace), gemm_splits(a.M, a.N, a.K, compute_units)};
+    sa.flags = flags;
     if (sa.S > 1 && (!workspace || workspace_bytes < gemm_workspace_bytes(a.M, a.N, a.K, compute_units))) sa.S = 1;
     return a.bf16 ? launch_v3_auto<BF16>(sa, compute_units, s) : launch_v3_auto<F16>(sa, compute_units, s);
 }
@@ -1286,14 +1332,16 @@ hipError_t launch_w4_prefill(const GemmArgs& a, void* workspace, size_t workspac
 // W4A16 at large M where the prefill kernel does not take the shape (more
 // than 128 groups): the small-M kernels on successive blocks of 16
 // activation rows (weights are re-read once per block).
-hipError_t launch_w4_gemm(const GemmArgs& a, void* workspace, size_t workspace_bytes, hipStream_t s) {
+hipError_t launch_w4_gemm(const GemmArgs& a, void* workspace, size_t workspace_bytes, hipStream_t s,
+                          uint32_t* flags) {
     for (int64_t m = 0; m < a.M; m += kGemvMaxM) {
         GemmArgs b = a;
         b.A = a.A + m * a.K;
         b.C = a.C + m * a.N;
         b.M = (a.M - m) < kGemvMaxM ? (a.M - m) : kGemvMaxM;
         // the blocks run in stream order, so they may share one workspace
-        hipError_t e = launch_w4_gemv(b, workspace, workspace_bytes, s);
+        // (each leaves the arrival counters zero for the next)
+        hipError_t e = launch_w4_gemv(b, workspace, workspace_bytes, s, flags);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;

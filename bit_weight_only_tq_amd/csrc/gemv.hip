@@ -754,10 +754,37 @@ __global__ __launch_bounds__(1024) void ternary_gemv_stream_kernel(SplitArgs sa)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int m = 4 * (l >> 4) + i;
-                if (m < M) part[(int64_t)m * N + n] = sum[i] * ternary_unit<AT>();
+                if (m < M) store_partial(part + (int64_t)m * N + n, sum[i] * ternary_unit<AT>());
             }
         } else if (n < N) {
             const float sc_e = f16_bits_to_f32(sc_bits) * ternary_unit<AT>();
+            const float bi_e = p.bias ? AT::to_f32(bi_bits) : 0.0f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int m = 4 * (l >> 4) + i;
+                if (m < M) p.C[(int64_t)m * N + n] = AT::from_f32_fast(sum[i] * sc_e + bi_e);
+            }
+        }
+    }
+    // 6. with a split, the last workgroup of this row block to finish sums
+    //    the S partials in split order and finishes the outputs
+    if (sa.S == 1 || !sa.flags) return;
+    if (!split_last_arrival(sa.flags, blockIdx.x, sa.S, reinterpret_cast<uint32_t*>(smem))) return;
+    if ((int)threadIdx.x < T * kWave) {
+        const int e = (int)threadIdx.x;
+        const int l = e % kWave;
+        const int64_t n = n_base + 16 * (e / kWave) + (l & 15);
+        const int64_t nc = n < N ? n : N - 1;
+        uint32_t off[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int m = 4 * (l >> 4) + i;
+            off[i] = (uint32_t)((m < M ? m : M - 1) * N + nc);
+        }
+        float sum[4];
+        split_sums<4, 4>(sa.ws, (int64_t)M * N, off, sa.S, sum);
+        if (n < N) {
+            const float sc_e = f16_bits_to_f32(sc_bits);
             const float bi_e = p.bias ? AT::to_f32(bi_bits) : 0.0f;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -1226,9 +1253,35 @@ __global__ __launch_bounds__(1024) void w4_gemv_stream_kernel(SplitArgs sa) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int m = 4 * (l >> 4) + i;
-                if (m < M) part[(int64_t)m * N + n] = sum[i];
+                if (m < M) store_partial(part + (int64_t)m * N + n, sum[i]);
             }
         } else if (n < N) {
+            const float b = p.bias ? AT::to_f32(bi_bits) : 0.0f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int m = 4 * (l >> 4) + i;
+                if (m < M) p.C[(int64_t)m * N + n] = AT::from_f32_fast(sum[i] + b);
+            }
+        }
+    }
+    // 6. with a split, the last workgroup of this row block to finish sums
+    //    the S partials (which carry the group scales) in split order
+    if (sa.S == 1 || !sa.flags) return;
+    if (!split_last_arrival(sa.flags, blockIdx.x, sa.S, reinterpret_cast<uint32_t*>(smem))) return;
+    if ((int)threadIdx.x < T * kWave) {
+        const int e = (int)threadIdx.x;
+        const int l = e % kWave;
+        const int64_t n = n_base + 16 * (e / kWave) + (l & 15);
+        const int64_t nc = n < N ? n : N - 1;
+        uint32_t off[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int m = 4 * (l >> 4) + i;
+            off[i] = (uint32_t)((m < M ? m : M - 1) * N + nc);
+        }
+        float sum[4];
+        split_sums<4, 4>(sa.ws, (int64_t)M * N, off, sa.S, sum);
+        if (n < N) {
             const float b = p.bias ? AT::to_f32(bi_bits) : 0.0f;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -1511,9 +1564,11 @@ static hipError_t launch_gemv_stream_at(const SplitArgs& sa, const StreamPlan& p
     if (e != hipSuccess) return e;
     if (pl.lds != (size_t)pl.waves * stream_wave_lds(CSW, MR, T)) return hipErrorInvalidValue;
     const dim3 grid((unsigned)((sa.g.N + 16 * T - 1) / (16 * T)), (unsigned)sa.S);
-    ternary_gemv_stream_kernel<AT, CSW, T, MR><<<grid, dim3(pl.waves * kWave), pl.lds, s>>>(sa);
+    SplitArgs k = sa;
+    k.flags = split_flags(sa.flags, sa.S, grid.x);
+    ternary_gemv_stream_kernel<AT, CSW, T, MR><<<grid, dim3(pl.waves * kWave), pl.lds, s>>>(k);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    return sa.S > 1 ? launch_splitk_reduce(sa, s) : hipSuccess;
+    return sa.S > 1 && !k.flags ? launch_splitk_reduce(sa, s) : hipSuccess;
 }
 
 template <int CSW, int T, int MR>
@@ -1555,12 +1610,13 @@ static hipError_t launch_gemv_stream_t(const SplitArgs& sa, const StreamPlan& sp
 
 hipError_t launch_ternary_gemv(const GemmArgs& a, hipStream_t s) { return launch_ternary_gemv(a, nullptr, 0, s); }
 
-hipError_t launch_ternary_gemv(const GemmArgs& a, void* workspace, size_t workspace_bytes, hipStream_t s) {
+hipError_t launch_ternary_gemv(const GemmArgs& a, void* workspace, size_t workspace_bytes, hipStream_t s,
+                               uint32_t* flags) {
     GemvM1Plan m1;
     if (gemv_m1_plan(a, &m1)) return launch_gemv_m1_plan<0>(a, m1, s);
     StreamPlan sp;
     if (gemv_stream_plan(a, workspace ? workspace_bytes : 0, &sp))
-        return launch_gemv_stream_t(SplitArgs{a, static_cast<float*>(workspace), sp.S}, sp, s);
+        return launch_gemv_stream_t(SplitArgs{a, static_cast<float*>(workspace), sp.S, 0, 0, flags}, sp, s);
     GemvPlan pl;
     if (gemv_lds_plan(a, &pl)) {
         if (pl.rows16 == 2) {
@@ -1716,9 +1772,11 @@ static hipError_t launch_w4_stream_at(const SplitArgs& sa, const W4StreamPlan& p
         if (pl.lds != (size_t)pl.waves * w4_stream_wave_lds(GSW, MR, T)) return hipErrorInvalidValue;
         if (GSW == 2 && !w4_pairs_ok(sa.g, sa.S)) return hipErrorInvalidValue;
         const dim3 grid((unsigned)((sa.g.N + 16 * T - 1) / (16 * T)), (unsigned)sa.S);
-        w4_gemv_stream_kernel<AT, GSW, T, MR, ASYM><<<grid, dim3(pl.waves * kWave), pl.lds, s>>>(sa);
+        SplitArgs k = sa;
+        k.flags = split_flags(sa.flags, sa.S, grid.x);
+        w4_gemv_stream_kernel<AT, GSW, T, MR, ASYM><<<grid, dim3(pl.waves * kWave), pl.lds, s>>>(k);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        return sa.S > 1 ? launch_splitk_reduce(sa, s) : hipSuccess;
+        return sa.S > 1 && !k.flags ? launch_splitk_reduce(sa, s) : hipSuccess;
     }
 }
 
@@ -1840,12 +1898,13 @@ static hipError_t launch_w4_m1_plan(const GemmArgs& a, const W4M1Plan& m1, hipSt
     return m1.rows16 == 2 ? launch_w4_m1<2, 4>(a, m1, s) : launch_w4_m1<1, 4>(a, m1, s);
 }
 
-hipError_t launch_w4_gemv(const GemmArgs& a, void* workspace, size_t workspace_bytes, hipStream_t s) {
+hipError_t launch_w4_gemv(const GemmArgs& a, void* workspace, size_t workspace_bytes, hipStream_t s,
+                          uint32_t* flags) {
     W4M1Plan m1;
     if (w4_m1_plan(a, &m1)) return launch_w4_m1_plan(a, m1, s);
     W4StreamPlan sp;
     if (w4_use_stream(a, workspace ? workspace_bytes : 0, &sp))
-        return launch_w4_stream_t(SplitArgs{a, static_cast<float*>(workspace), sp.S, 1}, sp, s);
+        return launch_w4_stream_t(SplitArgs{a, static_cast<float*>(workspace), sp.S, 1, 0, flags}, sp, s);
     // bf16 shapes the streaming kernel cannot take: the small-M kernel over
     // blocks of kW4SmallMaxM rows, reading the weights once per block, which
     // still beats the per-lane FMA kernel several times over

@@ -263,6 +263,67 @@ __device__ __forceinline__ void dma16s(const void* base, uint32_t off, uint32_t 
                  :: "v"(off), "s"(base), "s"(lds_addr) : "memory", "m0");
 }
 
+// Split-K completion inside the kernel.  Every split workgroup of an output
+// tile stores its fp32 partials (store_partial) and then counts itself in
+// flags[tile]; the one that brings the count to S is the last, resets the
+// counter (every call leaves the counters zero, as the next call needs them)
+// and goes on to sum the S partials in split order (split_sum), the same
+// order and arithmetic as the separate reduction kernel, so the result does
+// not depend on which split finishes last.
+// Coherence across the XCDs (each has its own L2) comes from the accesses
+// themselves, not from fences: the partials are stored and loaded at device
+// scope (write-through stores, loads served from the device's coherence
+// point), the counter is a device-scope atomic, and each wave waits for its
+// partial stores to complete before the barrier that precedes the count.
+// A fence would write back or drop the whole L2 of the XCD instead.
+// Called by every thread of a one-dimensional workgroup after its last use
+// of LDS; `word` is a 32-bit LDS word for the broadcast.  Nothing waits on
+// another workgroup.
+__device__ __forceinline__ void store_partial(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ bool split_last_arrival(uint32_t* flags, uint32_t tile, int S, uint32_t* word) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's partial stores are complete
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t seen = __hip_atomic_fetch_add(flags + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const bool last = seen == (uint32_t)(S - 1);
+        if (last) __hip_atomic_store(flags + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *word = last ? 1u : 0u;
+    }
+    __syncthreads();
+    return *word != 0u;
+}
+
+// Sums of the S partials of E outputs in split order z = 0 .. S-1 (the
+// reduction kernel's arithmetic: 0 + p_0 + p_1 + ...): output e of slab z is
+// base[z * MN + off[e]].  Rounds of R splits issue all R * E loads before
+// using any, so a round costs one memory latency.  Every off[e] must address
+// an element of the slab, also for outputs the caller then drops.
+template <int E, int R>
+__device__ __forceinline__ void split_sums(const float* base, int64_t MN, const uint32_t (&off)[E], int S,
+                                           float (&out)[E]) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) out[e] = 0.0f;
+    for (int z0 = 0; z0 < S; z0 += R) {
+        float v[R][E];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const float* slab = base + (int64_t)(z0 + r < S ? z0 + r : S - 1) * MN;
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                v[r][e] = __hip_atomic_load(slab + off[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            if (z0 + r < S) {
+#pragma unroll
+                for (int e = 0; e < E; ++e) out[e] += v[r][e];
+            }
+    }
+}
+
 // Sum over the 16 lanes of each DPP row (lanes 16r .. 16r+15); every lane of
 // the row receives its row's total.  Steps: swap neighbours, swap pairs,
 // mirror half-rows, mirror rows.  All 64 lanes must be active.

@@ -63,17 +63,32 @@ struct GemmArgs {
 };
 
 // A call whose K range is split S ways: split z writes its fp32 partial sums
-// (no row scale, no bias) to ws[z][M][N]; launch_splitk_reduce then sums
-// the S partials of each output in order z = 0 .. S-1 and applies the row
-// scale and bias, so the result does not depend on scheduling.
+// (no row scale, no bias) to ws[z][M][N], and the S partials of each output
+// are summed in order z = 0 .. S-1 before the row scale and bias, so the
+// result does not depend on scheduling.  With `flags` the summing is done
+// inside the kernel by the last split workgroup of each output tile to
+// finish (a counter per tile, split_last_arrival); without, by a second
+// launch (launch_splitk_reduce).
 struct SplitArgs {
     GemmArgs g;
     float* ws;  // [S][M][N] fp32 partials, unused when S == 1
     int S;
     int scaled;  // 1: the partials already carry the weight scales (W4A16), the reduction adds only the bias
     int64_t ldc = 0;  // row stride of C in elements (0: N); the large-M kernel's column-split launches set it
+    uint32_t* flags = nullptr;  // per-tile arrival counters, zero on entry and on exit (S > 1), or nullptr
 };
 hipError_t launch_splitk_reduce(const SplitArgs& sa, hipStream_t s);  // gemm.hip
+
+// Arrival counters at the front of every caller workspace: kFlagBytes bytes,
+// one 32-bit counter per output tile of a split call (kMaxFlags tiles; a
+// call with more tiles falls back to the reduction launch).  They must be
+// zero when a workspace is first used, and every call leaves them zero.
+constexpr size_t kFlagBytes = 16384;
+constexpr int64_t kMaxFlags = (int64_t)(kFlagBytes / 4);
+// The counters to use for a split grid of `tiles` output tiles, or nullptr.
+inline uint32_t* split_flags(uint32_t* flags, int S, int64_t tiles) {
+    return (flags && S > 1 && tiles <= kMaxFlags) ? flags : nullptr;
+}
 
 // gemv.hip: small M (<= kGemvMaxM), weights streamed once per call.
 constexpr int kGemvMaxM = 16;
@@ -83,7 +98,8 @@ constexpr int64_t kMaxK = (int64_t)1 << 22;
 // With a workspace of gemv_workspace_bytes() the streaming kernel may split
 // K (long-K, short-N shapes); without one it never does.
 size_t gemv_workspace_bytes(const GemmArgs& a);
-hipError_t launch_ternary_gemv(const GemmArgs& a, void* workspace, size_t workspace_bytes, hipStream_t s);
+hipError_t launch_ternary_gemv(const GemmArgs& a, void* workspace, size_t workspace_bytes, hipStream_t s,
+                               uint32_t* flags = nullptr);
 hipError_t launch_ternary_gemv(const GemmArgs& a, hipStream_t s);         // picks the fastest eligible kernel
 hipError_t launch_ternary_gemv_simple(const GemmArgs& a, hipStream_t s);  // any dtype, any K % 64 == 0
 bool ternary_gemv_mfma_ok(const GemmArgs& a);                             // fp16, K % 256 == 0
@@ -98,7 +114,8 @@ hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, int
 // W4A16 small M: with a workspace of w4_gemv_workspace_bytes() the streaming
 // kernel may split K; without one it never does.
 size_t w4_gemv_workspace_bytes(const GemmArgs& a);
-hipError_t launch_w4_gemv(const GemmArgs& a, void* workspace, size_t workspace_bytes, hipStream_t s);
+hipError_t launch_w4_gemv(const GemmArgs& a, void* workspace, size_t workspace_bytes, hipStream_t s,
+                          uint32_t* flags = nullptr);
 hipError_t launch_w4_gemv(const GemmArgs& a, hipStream_t s);         // picks the fastest eligible kernel
 hipError_t launch_w4_gemv_simple(const GemmArgs& a, hipStream_t s);  // any dtype
 
@@ -106,7 +123,7 @@ hipError_t launch_w4_gemv_simple(const GemmArgs& a, hipStream_t s);  // any dtyp
 // Large M: K split S ways (gemm_splits) when `workspace` holds
 // gemm_workspace_bytes(), else one pass over K.
 hipError_t launch_ternary_gemm(const GemmArgs& a, void* workspace, size_t workspace_bytes, int compute_units,
-                               hipStream_t s);
+                               hipStream_t s, uint32_t* flags = nullptr);
 int gemm_splits(int64_t M, int64_t N, int64_t K, int compute_units);
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int compute_units);
 // gemm.hip: medium M (64-row tiles, K split across workgroups when the
@@ -118,7 +135,8 @@ hipError_t launch_ternary_medium(const GemmArgs& a, void* workspace, size_t work
 hipError_t launch_ternary_medium_split(const SplitArgs& sa, bool paired, hipStream_t s);  // a given split count; paired: A holds pairs
 // Compute units of the current device (cached per device ordinal).
 int compute_units();
-hipError_t launch_w4_gemm(const GemmArgs& a, void* workspace, size_t workspace_bytes, hipStream_t s);
+hipError_t launch_w4_gemm(const GemmArgs& a, void* workspace, size_t workspace_bytes, hipStream_t s,
+                          uint32_t* flags = nullptr);
 // gemm.hip: W4A16 prefill GEMM (any M, K % 128 == 0, at most 128 groups).
 // gemm.hip: W4A16 matrix-core GEMM (17 <= M), K split across workgroups
 // while the tiles leave compute units idle or a split would hold more than

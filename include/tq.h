@@ -41,9 +41,18 @@
  *  - Apply calls (tq_gemm, tq_gemm_ws, w4a16_gemm) are ASYNCHRONOUS on
  *    `stream`, allocate nothing, never synchronize and are safe to capture in
  *    a HIP graph.  Faults during execution surface at the caller's next sync.
- *  - All results are deterministic: no atomics; where K is split across
- *    workgroups the partial sums are added in a fixed order.  The same
- *    inputs, path and workspace size give bit-identical outputs.
+ *  - All results are deterministic: where K is split across workgroups the
+ *    fp32 partial sums are added in a fixed order, split 0 first, whichever
+ *    workgroup adds them.  The same inputs, path and workspace size give
+ *    bit-identical outputs.
+ *  - Workspaces (the *_ws and asym calls): the first TQ_WORKSPACE_FLAG_BYTES
+ *    bytes of a workspace are per-tile arrival counters of the K split (the
+ *    last split workgroup of an output tile to finish adds the partials
+ *    itself, instead of a second kernel).  They must be zero before the
+ *    workspace is first used; every call leaves them zero again, so a
+ *    workspace that only this library writes needs clearing once.  The
+ *    *_workspace_bytes queries include them; a workspace smaller than
+ *    TQ_WORKSPACE_FLAG_BYTES counts as none.
  */
 #ifndef TQ_H
 #define TQ_H
@@ -55,7 +64,10 @@
 extern "C" {
 #endif
 
-#define TQ_ABI_VERSION 5
+#define TQ_ABI_VERSION 6
+
+/* Arrival counters at the front of every workspace (see above). */
+#define TQ_WORKSPACE_FLAG_BYTES 16384
 
 typedef enum tq_status {
     TQ_OK = 0,
@@ -173,10 +185,11 @@ tq_status tq_gemm_ex(const void* A, tq_dtype dt, int64_t M, int64_t N, int64_t K
 /*
  * tq_gemm_ws - tq_gemm with a caller-owned workspace and a path choice.
  *   workspace        device buffer (16-byte aligned) of workspace_bytes
- *                    bytes, or NULL; the call may overwrite all of it and
- *                    the caller must not touch it until the work on
- *                    `stream` is done.  Calls that may overlap must use
- *                    different workspaces.
+ *                    bytes, or NULL, whose first TQ_WORKSPACE_FLAG_BYTES
+ *                    are zero (see the workspace rules above); the call may
+ *                    overwrite the rest and the caller must not touch it
+ *                    until the work on `stream` is done.  Calls that may
+ *                    overlap must use different workspaces.
  *   workspace_bytes  at least tq_gemm_workspace_bytes(M, N, K, dt, path)
  *                    for the split-K schedule of the decode streaming
  *                    kernel (3 <= M <= 16, long K, where the small-M kernel
@@ -187,7 +200,11 @@ tq_status tq_gemm_ex(const void* A, tq_dtype dt, int64_t M, int64_t N, int64_t K
  *   path             TQ_PATH_AUTO or a forced kernel family (TQ_ERR_PATH if
  *                    it cannot run the shape: TQ_PATH_GEMV needs M <= 16).
  * With S > 1 splits the kernel writes S fp32 partials [S][M][N] into the
- * workspace and a second kernel sums them in order z = 0 .. S-1.  On
+ * workspace (after the counters), summed in order z = 0 .. S-1: on
+ * TQ_PATH_GEMV and TQ_PATH_GEMM by the last split of each output tile to
+ * finish (for grids of up to TQ_WORKSPACE_FLAG_BYTES / 4 tiles), on
+ * TQ_PATH_STREAM_MFMA by a second kernel, whose launch costs less there than
+ * the tail of one workgroup reading every split of its tile.  On
  * TQ_PATH_STREAM_MFMA with K % 256 == 0 and N * K >= 200 * 2^20 the
  * workspace also holds the activations in the kernel's pair order (M * K * 2
  * bytes after the partials, written by a first kernel of the call); with a
@@ -211,8 +228,10 @@ tq_status tq_gemm_ws(const void* A, tq_dtype dt, int64_t M, int64_t N, int64_t K
  * path) bytes of workspace, and so gives bit-identical results; when that
  * schedule needs more than the scratch holds it returns TQ_ERR_SCRATCH with
  * nothing launched.  It calls no allocating routine.  Every call on a device
- * shares that device's scratch (the split partials are fully rewritten by
- * each call, nothing needs clearing): calls that may overlap on one device
+ * shares that device's scratch: its front holds the split arrival counters,
+ * zero when the library is loaded and left zero by every call, and the
+ * split partials behind them are fully rewritten by each call, so nothing
+ * needs clearing; calls that may overlap on one device
  * (different streams, or threads) race and must be serialized by the
  * caller; calls in one stream's order are safe.  Other arguments, results
  * and errors as tq_gemm_ws.
@@ -257,16 +276,18 @@ tq_status w4a16_gemm_ex(const void* A, tq_dtype dt, int64_t M, int64_t N, int64_
 /*
  * w4a16_gemm_ws - w4a16_gemm with a caller-owned workspace and a path
  * choice (ABI 3).  The workspace rules are those of tq_gemm_ws: 16-byte
- * aligned device memory of workspace_bytes bytes or NULL, overwritten by
- * the call, not shared by calls that may overlap.  With at least
+ * aligned device memory of workspace_bytes bytes or NULL, zero counters at
+ * its front, the rest overwritten by the call, not shared by calls that may
+ * overlap.  With at least
  * w4a16_gemm_workspace_bytes() bytes the fp16 streaming kernel (M above 4,
  * or shapes the M <= 4 kernel cannot take) may split the K groups across
  * workgroups (fp32 partials with the group scales applied, summed in order
- * by a second kernel, bias added there); with less it makes one pass over
+ * by the tile's last split to finish, bias added there); with less it makes one pass over
  * K.  The M <= 4 kernel never splits, and the query reports 0 for it.  The
  * matrix-core GEMM splits the K groups the same way while its 128-column
  * tiles leave compute units idle (at most 16 splits) and always when K / 128
- * > 128 (each split holds at most 128 groups' scales); a shape that needs a
+ * > 128 (each split holds at most 128 groups' scales), summed by a second
+ * kernel; a shape that needs a
  * split the workspace cannot hold runs the decode kernels over blocks of 16
  * rows under TQ_PATH_AUTO and returns TQ_ERR_PATH under TQ_PATH_GEMM.  Row
  * blocks (M > 16) reuse the workspace in stream order.  Other arguments, results and errors as
@@ -330,7 +351,7 @@ tq_status w4a16_unpack_asym(const int32_t* qweight, const uint16_t* scales_f16, 
  * packed weights of w4a16_pack_asym.
  *   zeros  uint8 [N, K/128] or NULL (then the symmetric zero point 8).
  *   perm   int32 [K] or NULL: with it, A is first gathered into packed
- *          column order, A[:, perm], at the front of the workspace, which is
+ *          column order, A[:, perm], in the workspace after its counters, which is
  *          then required: at least w4a16_gemm_asym_workspace_bytes(..., 1)
  *          bytes for the fastest schedule, never less than the gathered
  *          activations (M * K * 2 bytes rounded up to 256; TQ_ERR_SHAPE
@@ -350,8 +371,8 @@ tq_status w4a16_gemm_asym(const void* A, tq_dtype dt, int64_t M, int64_t N, int6
 
 /*
  * w4a16_gemm_asym_workspace_bytes - workspace of w4a16_gemm_asym's fastest
- * schedule: the gathered activations when with_perm, plus the split-K
- * partials (0 for invalid arguments).
+ * schedule: the counters, the gathered activations when with_perm, and the
+ * split-K partials (0 for invalid arguments or when nothing is needed).
  */
 size_t w4a16_gemm_asym_workspace_bytes(int64_t M, int64_t N, int64_t K, tq_dtype dt, int64_t group_size,
                                        int with_perm);

@@ -27,6 +27,9 @@ def lib():
     return _lib.load()
 
 
+F = 16384  # TQ_WORKSPACE_FLAG_BYTES: split arrival counters at the front of a workspace
+
+
 def test_header_declares_the_boundary():
     names = _declared_functions()
     for required in ("tq_pack", "tq_gemm", "w4a16_gemm", "tq_unpack", "w4a16_pack", "w4a16_unpack",
@@ -58,9 +61,9 @@ def test_one_hip_runtime_per_process():
 
 
 def test_version_and_status_strings(lib):
-    assert lib.tq_abi_version() == 5
+    assert lib.tq_abi_version() == 6
     src = open(HEADER).read()
-    assert "#define TQ_ABI_VERSION 5" in src
+    assert "#define TQ_ABI_VERSION 6" in src
     for code, name in _lib.STATUS_NAMES.items():
         assert re.search(rf"\b{name}\s*=\s*{code}\b", src), name
         s = lib.tq_status_str(code)
@@ -98,36 +101,37 @@ def test_dispatcher_by_m():
 
 
 def test_workspace_query():
-    """Split-K workspace: S fp32 partials of [M, N] for the medium and large-M
-    paths, none for the GEMV path or when the output tiles fill the device;
-    the medium path adds the paired activations on large shapes.
+    """Split-K workspace: the arrival counters (F bytes) and S fp32 partials
+    of [M, N] for the medium and large-M paths, none for the GEMV path or
+    when the output tiles fill the device; the medium path adds the paired
+    activations on large shapes.
     Off the GPU the compute-unit count defaults to 256."""
     wb = _lib.tq_gemm_workspace_bytes
     assert wb(1, 4096, 4096) == 0 and wb(4096, 4096, 4096) == 0
     assert wb(16, 4096, 14336, "bf16") == wb(16, 4096, 14336) > 0  # bf16 streaming kernel: same K split as fp16
-    assert wb(64, 8192, 8192) == 8 * 64 * 8192 * 4      # 32 tiles -> 8 splits
-    assert wb(32, 1024, 8192) == 16 * 32 * 1024 * 4     # 4 tiles: capped at 16 splits
-    assert wb(40, 10240, 8192) == 6 * 40 * 10240 * 4    # 40 tiles: 6 splits keep one round on 256 CUs
-    assert wb(100, 2000, 1024) == 2 * 100 * 2000 * 4    # 4 K-steps of 256: two per split
-    assert wb(100, 2000, 4160) == 8 * 100 * 2000 * 4    # K % 256 != 0: 64-column kernel, >= 8 K-steps per split
+    assert wb(64, 8192, 8192) == F + 8 * 64 * 8192 * 4  # 32 tiles -> 8 splits
+    assert wb(32, 1024, 8192) == F + 16 * 32 * 1024 * 4  # 4 tiles: capped at 16 splits
+    assert wb(40, 10240, 8192) == F + 6 * 40 * 10240 * 4  # 40 tiles: 6 splits keep one round on 256 CUs
+    assert wb(100, 2000, 1024) == F + 2 * 100 * 2000 * 4  # 4 K-steps of 256: two per split
+    assert wb(100, 2000, 4160) == F + 8 * 100 * 2000 * 4  # K % 256 != 0: 64-column kernel, >= 8 K-steps per split
     # N K >= 2e8: the activations are paired once per call, into the
     # workspace after the split partials (256-byte aligned)
-    assert wb(64, 57344, 8192) == 64 * 8192 * 2         # 224 tiles: no split, pairs only
-    assert wb(32, 8192, 28672) == 8 * 32 * 8192 * 4 + 32 * 28672 * 2
+    assert wb(64, 57344, 8192) == F + 64 * 8192 * 2  # 224 tiles: no split, pairs only
+    assert wb(32, 8192, 28672) == F + 8 * 32 * 8192 * 4 + 32 * 28672 * 2
     assert wb(32, 8192, 28672, path="stream_mfma") == wb(32, 8192, 28672)
     assert wb(64, 8192, 96) == 0                        # K % 64 != 0
     # large M: 256 x 256 tiles, one per compute unit, >= 16 K-steps per split
-    assert wb(2048, 4096, 14336) == 2 * 2048 * 4096 * 4  # 128 tiles: two splits fill the device
+    assert wb(2048, 4096, 14336) == F + 2 * 2048 * 4096 * 4  # 128 tiles: two splits fill the device
     assert wb(2048, 14336, 4096) == 0                   # 448 tiles: partials cost more than they save
     assert wb(4096, 4096, 14336) == 0 and wb(8192, 4096, 14336) == 0
-    assert wb(300, 1000, 4096) == 4 * 300 * 1000 * 4    # 8 tiles, 64 K-steps -> 4 splits
+    assert wb(300, 1000, 4096) == F + 4 * 300 * 1000 * 4  # 8 tiles, 64 K-steps -> 4 splits
     assert wb(300, 1000, 1024) == 0                     # 16 K-steps: nothing to split
-    assert wb(64, 8192, 8192, path="gemm") == 8 * 64 * 8192 * 4
+    assert wb(64, 8192, 8192, path="gemm") == F + 8 * 64 * 8192 * 4
     assert wb(4, 8192, 8192, path="gemv") == 0
     # decode (M <= 16): the small-M kernel (M <= 2, and M <= 4 with few waves
     # per SIMD) never splits; the streaming kernel may
     assert wb(4, 4096, 14336) == 0 and wb(2, 4096, 14336) == 0
-    assert wb(5, 4096, 14336) == 7 * 5 * 4096 * 4 and wb(16, 4096, 14336) == 7 * 16 * 4096 * 4
+    assert wb(5, 4096, 14336) == F + 7 * 5 * 4096 * 4 and wb(16, 4096, 14336) == F + 7 * 16 * 4096 * 4
 
 
 V = ctypes.c_void_p
@@ -171,23 +175,23 @@ def test_w4_workspace_query():
     one pass over K is cheapest.  Off the GPU the compute-unit count
     defaults to 256."""
     wb = _lib.w4a16_gemm_workspace_bytes
-    assert wb(16, 4096, 14336) == 8 * 16 * 4096 * 4       # 112 groups -> 8 splits of 14
-    assert wb(16, 57344, 8192) == 4 * 16 * 57344 * 4
+    assert wb(16, 4096, 14336) == F + 8 * 16 * 4096 * 4  # 112 groups -> 8 splits of 14
+    assert wb(16, 57344, 8192) == F + 4 * 16 * 57344 * 4
     assert wb(16, 28672, 4096) == 0 and wb(16, 4096, 4096) == 0
     assert wb(1, 4096, 14336) == 0                       # M = 1 never splits
     assert wb(2, 4096, 14336) == 0                       # M = 2: the small-M kernel, no split
-    assert wb(5, 4096, 14336) == 8 * 5 * 4096 * 4        # M = 5 streams: 112 groups -> 8 splits of 14
+    assert wb(5, 4096, 14336) == F + 8 * 5 * 4096 * 4  # M = 5 streams: 112 groups -> 8 splits of 14
     assert wb(16, 4096, 14336, "bf16") == wb(16, 4096, 14336)  # bf16 streams like fp16
     assert wb(16, 4096, 14336, group_size=64) == 0
     assert wb(24, 4096, 4096) == 0                        # blocks of 16 rows, no split on these shapes
     assert wb(24, 1024, 4096) == wb(16, 1024, 4096)       # ... the largest block's need
     # the matrix-core GEMM (17 <= M, K >= 8192 or M > 32): split while the
     # 128-column tiles leave compute units idle, at most 16, >= 1 group each
-    assert wb(40, 4096, 14336) == 8 * 40 * 4096 * 4      # 32 tiles -> 8 splits
+    assert wb(40, 4096, 14336) == F + 8 * 40 * 4096 * 4  # 32 tiles -> 8 splits
     assert wb(64, 57344, 8192) == 0                       # 448 tiles: one pass
-    assert wb(256, 4096, 14336) == 8 * 256 * 4096 * 4     # 256-row tiles: 32 tiles -> 8 splits
+    assert wb(256, 4096, 14336) == F + 8 * 256 * 4096 * 4  # 256-row tiles: 32 tiles -> 8 splits
     assert wb(2048, 4096, 14336) == 0 and wb(4096, 14336, 4096) == 0
-    assert wb(4096, 4096, 16384 + 128) == 2 * 4096 * 4096 * 4  # 129 groups: two splits at least
+    assert wb(4096, 4096, 16384 + 128) == F + 2 * 4096 * 4096 * 4  # 129 groups: two splits at least
     assert wb(16, 4096, 200) == 0                         # K % 128 != 0
 
 
@@ -202,17 +206,18 @@ def test_w4a16_gemm_ws_host_checks(lib):
 
 
 def test_w4a16_asym_workspace_query():
-    """With a column order the gathered activations (M * K * 2 bytes, rounded
-    up to 256) come first, then the split partials of the symmetric query."""
+    """After the arrival counters, with a column order the gathered
+    activations (M * K * 2 bytes, rounded up to 256) come first, then the
+    split partials of the symmetric query."""
     wb = _lib.w4a16_gemm_asym_workspace_bytes
     sym = _lib.w4a16_gemm_workspace_bytes
-    assert wb(16, 4096, 14336) == sym(16, 4096, 14336) == 8 * 16 * 4096 * 4
-    assert wb(16, 4096, 14336, with_perm=True) == 16 * 14336 * 2 + 8 * 16 * 4096 * 4
-    assert wb(1, 4096, 4096, with_perm=True) == 8192 and wb(1, 4096, 4096) == 0
-    assert wb(3, 64, 128, "bf16", with_perm=True) == 768                 # 3 * 128 * 2 = 768
-    assert wb(1, 64, 384, with_perm=True) == 768                          # 768 already a multiple of 256
-    assert wb(1, 64, 256, with_perm=True) == 512
-    assert wb(5, 64, 128, with_perm=True) == 1280
+    assert wb(16, 4096, 14336) == sym(16, 4096, 14336) == F + 8 * 16 * 4096 * 4
+    assert wb(16, 4096, 14336, with_perm=True) == F + 16 * 14336 * 2 + 8 * 16 * 4096 * 4
+    assert wb(1, 4096, 4096, with_perm=True) == F + 8192 and wb(1, 4096, 4096) == 0
+    assert wb(3, 64, 128, "bf16", with_perm=True) == F + 768  # 3 * 128 * 2 = 768
+    assert wb(1, 64, 384, with_perm=True) == F + 768  # 768 already a multiple of 256
+    assert wb(1, 64, 256, with_perm=True) == F + 512
+    assert wb(5, 64, 128, with_perm=True) == F + 1280
     assert wb(1, 64, 200, with_perm=True) == 0 and wb(1, 64, 256, group_size=64, with_perm=True) == 0
 
 

@@ -382,7 +382,7 @@ def test_w4_split_k(M, N, K):
     C2 = tq.w4a16_gemm(A.to(dev), q, s, bias=bias.to(dev))
     assert torch.equal(outs[0].view(torch.int16), C2.view(torch.int16))
     if M > 16:
-        ws = torch.empty((64 << 20,), dtype=torch.uint8, device=dev)
+        ws = tq.new_workspace(64 << 20, dev)
         C = tq.w4a16_gemm(A.to(dev), q, s, bias=bias.to(dev), workspace=ws, path="gemv")
         check_close(C.index_select(1, idx), A, wdq, bias=bias[torch.from_numpy(cols)],
                     label=f"w4 row blocks {M}x{N}x{K}")

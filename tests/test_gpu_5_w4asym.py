@@ -214,9 +214,9 @@ def test_w4a_order_without_zeros():
 ])
 def test_w4a_decode_shapes(M, N, K):
     """Llama-3-8B shapes with activation order: the workspace the query asks
-    for (gather + split partials), exactly the gather (no split) and none
-    (rejected); sampled output columns within the tolerance; a repeated
-    call is bit-identical."""
+    for (counters + gather + split partials), exactly the counters and the
+    gather (no split) and none (rejected); sampled output columns within the
+    tolerance; a repeated call is bit-identical."""
     import torch
     import bit_weight_only_tq_amd as tq
     dev = require_gpu()
@@ -234,10 +234,10 @@ def test_w4a_decode_shapes(M, N, K):
     wdq = OA.w4a_dequant(rq, rs, rz, K, rp)
     A = synth.activations(M, K, synth.seed_for("w4ada", M, K), "f16")
     bias = synth.activations(1, N, synth.seed_for("w4adb", N), "f16")[0]
-    gather = (M * K * 2 + 255) // 256 * 256
+    gather = tq.TQ_WORKSPACE_FLAG_BYTES + (M * K * 2 + 255) // 256 * 256  # counters + gathered activations
     outs = []
     for nbytes in ("auto", gather):
-        ws = nbytes if nbytes == "auto" else torch.empty((nbytes,), dtype=torch.uint8, device=dev)
+        ws = nbytes if nbytes == "auto" else tq.new_workspace(nbytes, dev)
         C = tq.w4a16_gemm(A.to(dev), q, s, bias=bias.to(dev), zeros=z, perm=perm, workspace=ws)
         check_close(C.index_select(1, idx), A, wdq, bias=bias[torch.from_numpy(cols)],
                     label=f"w4a {M}x{N}x{K} ws={nbytes}")

@@ -43,7 +43,7 @@ def _call_ws(lib, A, codes, scale, bias, C, dt):
     M, K = A.shape
     N = codes.shape[0]
     nbytes = lib.tq_gemm_workspace_bytes(M, N, K, dt, 0)
-    ws = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=A.device)
+    ws = torch.zeros((max(nbytes, 1),), dtype=torch.uint8, device=A.device)  # counters zero
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     p = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())  # noqa: E731
     st = lib.tq_gemm_ws(p(A), dt, M, N, K, p(codes), p(scale), p(bias), p(C), p(ws) if nbytes else None, nbytes,
