@@ -68,6 +68,9 @@ def parse():
     ap.add_argument("--unfused", action="store_true", help="decode mode: q,k,v,gate,up as separate calls")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="lower bound on the CPU sample's run time")
+    ap.add_argument("--settle", type=float, default=0.3,
+                    help="seconds of untimed calls before each prefill line (counter passes use less: "
+                         "every call is a profiled dispatch)")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "ternary_gemv_traffic.json"))
     return ap.parse_args()
 
@@ -177,16 +180,17 @@ def time_region(fn, steps, stream, per_step=None):
     return start.elapsed_time(end) / 1e3
 
 
-SETTLE_SECONDS = 0.3
+SETTLE_SECONDS = [0.3]  # set from --settle
 
 
-def settle(fn, seconds=SETTLE_SECONDS):
+def settle(fn, seconds=None):
     """Untimed calls of fn for at least `seconds` of wall clock, ending with a
     synchronize.  The part raises its shader clock only after some tens of
     milliseconds of sustained load: a compute-bound line timed straight after
     idle host work (packing, the previous line's checks) would catch the
     ramp and report less than the sustained rate a serving loop sees."""
     import torch
+    seconds = SETTLE_SECONDS[0] if seconds is None else seconds
     t0 = time.perf_counter()
     while True:
         for _ in range(4):
@@ -865,6 +869,7 @@ def load_traffic(path):
 
 def main():
     args = parse()
+    SETTLE_SECONDS[0] = args.settle
     if args.gpus != 1:
         print(json.dumps({"error": "the benchmark runs on exactly one GPU (no multi-GPU path); --gpus must be 1"}), flush=True)
         sys.exit(2)
