@@ -614,7 +614,9 @@ __global__ __launch_bounds__(1024) void ternary_gemv_m1_kernel(GemmArgs p) {
 // Every workgroup reads the activations of its whole K range (M * K * 2
 // bytes), so for short, wide matrices the grid may also split K: workgroup
 // (x, z) covers chunk-sets z*CS/S .. (z+1)*CS/S - 1 of its row-blocks and
-// stores fp32 partials for launch_splitk_reduce (S = gridDim.y divides CS).
+// stores fp32 partials (S = gridDim.y divides CS); the last split of each
+// row-block to finish sums them (step 6; launch_splitk_reduce instead when
+// no arrival counters are given).
 __host__ __device__ constexpr int stream_wave_lds(int csw, int mr, int t) {  // bytes of one wave's LDS area
     return t * 1024 > csw * mr * 512 ? t * 1024 : csw * mr * 512;
 }
@@ -1073,8 +1075,9 @@ __global__ __launch_bounds__(1024) void w4_gemv_m1_kernel(GemmArgs p) {
 // its four operand chunks (row i, slots 4h .. 4h+3).  Issue order: bias bits
 // and group scales, activation DMA, the code words of all row-blocks, then
 // one vmcnt wait for the DMA only.  With S = gridDim.y > 1 splits of the groups
-// the workgroup stores fp32 partials (group scales applied) for
-// launch_splitk_reduce.
+// the workgroup stores fp32 partials (group scales applied), and the last
+// split of each row-block to finish sums them and adds the bias
+// (launch_splitk_reduce instead when no arrival counters are given).
 // ASYM: per-(row, group) zero points z instead of 8, loaded with the scales
 // before the DMA; each row-block builds its packed constants -(1024 + z),
 // -(64 + z) per group, so the operand is q - z exactly.
