@@ -1115,10 +1115,12 @@ static hipError_t launch_v3_auto(const SplitArgs& sa, int compute_units, hipStre
 // unit (the LDS ring takes 108 KB), so a grid of T tiles runs in
 // ceil(T / CUs) rounds of nk K-steps each.  When T leaves compute units idle,
 // S splits shorten each round to ceil(nk / S) K-steps at the price of
-// writing and re-reading S * M * N fp32 partials plus a second launch.  The
-// split count minimises that estimate, with one K-step taken as 1.5 us (a
-// 256 x 256 x 64 step at about 1 PFLOP/s over the whole chip) and the
-// partials moving at 4 TB/s; each split keeps at least 16 K-steps.
+// writing S * M * N fp32 partials and re-reading them (by the last split of
+// each tile, or a second launch without arrival counters; charged 3 us
+// either way).  The split count minimises that estimate, with one K-step
+// taken as 1.5 us (a 256 x 256 x 64 step at about 1 PFLOP/s over the whole
+// chip) and the partials moving at 4 TB/s; each split keeps at least 16
+// K-steps.
 int gemm_splits(int64_t M, int64_t N, int64_t K, int compute_units) {
     const int64_t tiles = ((N + v3::BN - 1) / v3::BN) * ((M + v3::Tile<256>::BM - 1) / v3::Tile<256>::BM);
     const int64_t nk = K / v3::BK;
